@@ -1,0 +1,163 @@
+"""Plain fp64 CPU oracle for GQA / MQA / MHA / MLA attention over a KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It never imports the
+HIP library (``mha_mla_kv_amd``) and shares no code with it; the two meet only
+through the seeded inputs of ``synth``.
+
+The arithmetic lives in ``oracle.c`` (plain loops, double accumulation, OpenMP
+over independent output rows).  This module compiles it with gcc, marshals
+arrays through ctypes and returns float64 numpy arrays.  ``accounting`` holds
+the KV-cache byte and parameter closed forms.
+
+What each routine computes, and the passage it follows, is stated at the top of
+``oracle.c``.  Parity of every routine is pinned by ``tests/test_oracle_*.py``
+against library routines, closed forms, invariants and the numbers the pages
+print; none is left unpinned.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _SO) -> str:
+    """Compile ``src`` (default: oracle.c) into a shared library at ``out``."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _declare(lib):
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    D = ctypes.c_double
+    lib.oracle_threads.restype = I
+    lib.oracle_threads.argtypes = []
+    lib.oracle_gqa_decode.restype = None
+    lib.oracle_gqa_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, D]
+    lib.oracle_gqa_prefill_causal.restype = None
+    lib.oracle_gqa_prefill_causal.argtypes = [P, P, P, P, I, I, I, I, I, D, P, I]
+    for name in ("oracle_mla_decode_decompressed", "oracle_mla_decode_absorbed"):
+        fn = getattr(lib, name)
+        fn.restype = None
+        fn.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, D, P, I]
+    return lib
+
+
+def load(path: str | None = None):
+    """Load the oracle library (building it first when it is missing or stale)."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            _lib = _declare(ctypes.CDLL(_SO))
+    return _lib
+
+
+def _f32(x) -> np.ndarray:
+    """Any CPU array-like (numpy, or a torch tensor of any float dtype) -> contiguous float32.
+
+    bf16 and fp32 values are exactly representable in float32, so nothing is rounded."""
+    if hasattr(x, "detach"):  # torch tensor, without importing torch here
+        x = x.detach().to("cpu").float().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def _i32(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _p(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check_groups(Hq: int, Hkv: int) -> None:
+    if Hkv <= 0 or Hq <= 0 or Hq % Hkv != 0:
+        raise ValueError(f"Hkv={Hkv} must divide Hq={Hq}")
+
+
+def gqa_decode(q, k, v, cache_lens, softmax_scale: float = 0.0, lib=None) -> np.ndarray:
+    """q [B,Hq,D], k/v [B,T_max,Hkv,D], cache_lens [B] -> out [B,Hq,D] float64."""
+    q, k, v, lens = _f32(q), _f32(k), _f32(v), _i32(cache_lens)
+    B, Hq, D = q.shape
+    _, T_max, Hkv, _ = k.shape
+    _check_groups(Hq, Hkv)
+    assert k.shape == (B, T_max, Hkv, D) and v.shape == k.shape and lens.shape == (B,)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    (lib or load()).oracle_gqa_decode(_p(q), _p(k), _p(v), _p(lens), _p(out), B, Hq, Hkv, D, T_max,
+                                      float(softmax_scale))
+    return out
+
+
+def gqa_prefill_causal(q, k, v, softmax_scale: float = 0.0, rows=None, lib=None) -> np.ndarray:
+    """q [B,S,Hq,D], k/v [B,S,Hkv,D] -> out [B,S,Hq,D] float64.
+
+    ``rows``: optional list of query positions to compute (others stay NaN)."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    _check_groups(Hq, Hkv)
+    assert k.shape == (B, S, Hkv, D) and v.shape == k.shape
+    out = np.full((B, S, Hq, D), np.nan, dtype=np.float64)
+    r = None if rows is None else _i32(rows)
+    (lib or load()).oracle_gqa_prefill_causal(_p(q), _p(k), _p(v), _p(out), B, S, Hq, Hkv, D,
+                                              float(softmax_scale), _p(r),
+                                              0 if r is None else int(r.size))
+    return out
+
+
+def _mla(fn_name, q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, cache_lens, softmax_scale, bh, lib):
+    q_nope, q_rope, w_uk, w_uv = _f32(q_nope), _f32(q_rope), _f32(w_uk), _f32(w_uv)
+    c_kv, k_rope, lens = _f32(c_kv), _f32(k_rope), _i32(cache_lens)
+    B, H, dn = q_nope.shape
+    dR = q_rope.shape[2]
+    _, dv, r = w_uv.shape
+    T_max = c_kv.shape[1]
+    assert q_rope.shape == (B, H, dR) and w_uk.shape == (H, dn, r) and w_uv.shape == (H, dv, r)
+    assert c_kv.shape == (B, T_max, r) and k_rope.shape == (B, T_max, dR) and lens.shape == (B,)
+    out = np.full((B, H, dv), np.nan, dtype=np.float64)
+    bhl = None if bh is None else _i32(bh)
+    getattr(lib or load(), fn_name)(_p(q_nope), _p(q_rope), _p(w_uk), _p(w_uv), _p(c_kv), _p(k_rope),
+                                    _p(lens), _p(out), B, H, dn, dR, dv, r, T_max,
+                                    float(softmax_scale), _p(bhl), 0 if bhl is None else int(bhl.size))
+    return out
+
+
+def mla_decode_decompressed(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, cache_lens,
+                            softmax_scale: float = 0.0, bh=None, lib=None) -> np.ndarray:
+    """MLA decode with keys/values rebuilt from the latent.  w_uk [H,dn,r], w_uv [H,dv,r].
+
+    ``bh``: optional flattened (b*H + h) rows to compute (others stay NaN)."""
+    return _mla("oracle_mla_decode_decompressed", q_nope, q_rope, w_uk, w_uv, c_kv, k_rope,
+                cache_lens, softmax_scale, bh, lib)
+
+
+def mla_decode_absorbed(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, cache_lens,
+                        softmax_scale: float = 0.0, bh=None, lib=None) -> np.ndarray:
+    """MLA decode with W_UK folded into the query and W_UV applied after the weighted sum."""
+    return _mla("oracle_mla_decode_absorbed", q_nope, q_rope, w_uk, w_uv, c_kv, k_rope,
+                cache_lens, softmax_scale, bh, lib)
+
+
+def threads(lib=None) -> int:
+    """OpenMP threads the oracle runs with."""
+    return int((lib or load()).oracle_threads())

@@ -1,0 +1,339 @@
+"""Pins that tie the fp64 oracle to something other than itself.
+
+Each ``pin_*`` function takes an oracle library handle (``oracle.load()`` or a
+deliberately broken build of oracle.c) and raises AssertionError when the
+oracle disagrees with:
+  * a library routine: torch's CPU float64 ``scaled_dot_product_attention``, with
+    K/V expanded to one head per query head by ``repeat_interleave`` along the
+    head axis (the expansion the "MQA & GQA 调研" page's repeat_kv docstring
+    names), and, for MLA, keys/values rebuilt with ``torch.nn.functional.linear``
+    from the up-projection weights exactly as the MultiHeadLatentAttention
+    listing on the qqstock DeepSeek MLA article builds them;
+  * closed forms: one cached token returns its V row; a zero query returns the
+    mean of the V rows; two tokens weight V by logistic functions of the score
+    gap; a saturating one-hot key selects one V row bit-exactly;
+  * invariants: a joint permutation of cached tokens, a constant added to every
+    score, per-head MHA, MQA = every head reading KV head 0, GQA = MHA on K/V
+    expanded by the repeat_kv expand+reshape, MLA absorbed = decompressed;
+  * the empty cache giving zeros (a reading; the pages are silent).
+The tests run them on the real oracle; tests/test_oracle_mutants.py runs them on
+broken copies and requires that each planted mistake trips at least one pin.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+TOL = 1e-12
+
+
+def _rel(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = max(np.max(np.abs(b)), 1e-300)
+    return float(np.max(np.abs(a - b)) / den)
+
+
+def _close(a, b, tol=TOL, what=""):
+    r = _rel(a, b)
+    assert np.all(np.isfinite(a)), f"{what}: non-finite oracle output"
+    assert r <= tol, f"{what}: relative error {r:.3e} > {tol:.1e}"
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(size=shape).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- library routine
+
+def sdpa_decode_ref(q, k, v, lens, scale=None):
+    """torch float64 SDPA, one sequence at a time, K/V expanded per query head."""
+    B, Hq, D = q.shape
+    Hkv = k.shape[2]
+    n_rep = Hq // Hkv
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        L = int(lens[b])
+        if L == 0:
+            continue
+        qb = torch.from_numpy(q[b].astype(np.float64))[None, :, None, :]          # [1,Hq,1,D]
+        kb = torch.from_numpy(k[b, :L].astype(np.float64)).repeat_interleave(n_rep, dim=1)
+        vb = torch.from_numpy(v[b, :L].astype(np.float64)).repeat_interleave(n_rep, dim=1)
+        kb = kb.permute(1, 0, 2)[None]                                              # [1,Hq,L,D]
+        vb = vb.permute(1, 0, 2)[None]
+        o = F.scaled_dot_product_attention(qb, kb, vb, scale=scale)
+        out[b] = o[0, :, 0, :].numpy()
+    return out
+
+
+def sdpa_prefill_ref(q, k, v, scale=None):
+    B, S, Hq, D = q.shape
+    n_rep = Hq // k.shape[2]
+    qt = torch.from_numpy(q.astype(np.float64)).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k.astype(np.float64)).repeat_interleave(n_rep, dim=2).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(v.astype(np.float64)).repeat_interleave(n_rep, dim=2).permute(0, 2, 1, 3)
+    o = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def sdpa_mla_ref(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, lens, scale=None):
+    """Keys [W_UK c , k_rope] and values W_UV c rebuilt with F.linear from the per-head weights
+    viewed as the up-projection Linear weights ([H*dn, r] and [H*dv, r]); k_rope is broadcast to
+    every head; the new token's query sees the whole cache (no causal cut inside the cache)."""
+    B, H, dn = q_nope.shape
+    dR = q_rope.shape[2]
+    dv, r = w_uv.shape[1], w_uv.shape[2]
+    Wk = torch.from_numpy(w_uk.astype(np.float64)).reshape(H * dn, r)
+    Wv = torch.from_numpy(w_uv.astype(np.float64)).reshape(H * dv, r)
+    out = np.zeros((B, H, dv))
+    for b in range(B):
+        L = int(lens[b])
+        if L == 0:
+            continue
+        c = torch.from_numpy(c_kv[b, :L].astype(np.float64))                       # [L, r]
+        k_nope = F.linear(c, Wk).view(L, H, dn).permute(1, 0, 2)                     # [H, L, dn]
+        value = F.linear(c, Wv).view(L, H, dv).permute(1, 0, 2)                      # [H, L, dv]
+        kr = torch.from_numpy(k_rope[b, :L].astype(np.float64))[None].expand(H, L, dR)
+        k_rec = torch.cat([k_nope, kr], dim=-1)[None]                                # [1,H,L,dn+dR]
+        q_rec = torch.cat([torch.from_numpy(q_nope[b].astype(np.float64)),
+                           torch.from_numpy(q_rope[b].astype(np.float64))], dim=-1)[None, :, None, :]
+        o = F.scaled_dot_product_attention(q_rec, k_rec, value[None], scale=scale)
+        out[b] = o[0, :, 0, :].numpy()
+    return out
+
+
+# ----------------------------------------------------------------------------- GQA decode pins
+
+DECODE_SHAPES = [
+    # B, Hq, Hkv, D, T_max, lens
+    (2, 8, 2, 16, 12, [12, 5]),
+    (3, 4, 4, 8, 9, [1, 9, 4]),       # MHA
+    (2, 6, 1, 8, 7, [7, 3]),          # MQA
+    (1, 8, 4, 96, 33, [33]),
+    (2, 32, 8, 128, 20, [17, 20]),
+]
+
+
+def pin_decode_vs_sdpa(lib):
+    for i, (B, Hq, Hkv, D, T, lens) in enumerate(DECODE_SHAPES):
+        rng = _rng(100 + i)
+        q, k, v = _rand(rng, B, Hq, D), _rand(rng, B, T, Hkv, D), _rand(rng, B, T, Hkv, D)
+        lens = np.array(lens, dtype=np.int32)
+        _close(oracle.gqa_decode(q, k, v, lens, lib=lib), sdpa_decode_ref(q, k, v, lens),
+               what=f"decode default scale {B,Hq,Hkv,D}")
+        s = 0.37
+        _close(oracle.gqa_decode(q, k, v, lens, softmax_scale=s, lib=lib),
+               sdpa_decode_ref(q, k, v, lens, scale=s), what="decode explicit scale")
+
+
+def pin_decode_closed_forms(lib):
+    rng = _rng(7)
+    B, Hq, Hkv, D, T = 2, 4, 2, 8, 6
+    q, k, v = _rand(rng, B, Hq, D), _rand(rng, B, T, Hkv, D), _rand(rng, B, T, Hkv, D)
+    n_rep = Hq // Hkv
+    # one cached token: the output is that token's V row, exactly
+    out = oracle.gqa_decode(q, k, v, np.array([1, 1], np.int32), lib=lib)
+    for b in range(B):
+        for h in range(Hq):
+            assert np.array_equal(out[b, h], v[b, 0, h // n_rep].astype(np.float64)), "L=1 != V0"
+    # zero query: uniform weights, the mean of the visible V rows
+    lens = np.array([6, 3], np.int32)
+    out = oracle.gqa_decode(np.zeros_like(q), k, v, lens, lib=lib)
+    for b in range(B):
+        for h in range(Hq):
+            _close(out[b, h], v[b, :lens[b], h // n_rep].astype(np.float64).mean(axis=0), 1e-14,
+                   "q=0 mean")
+    # two tokens: weights sigma(s0-s1), sigma(s1-s0)
+    scale = 1.0 / math.sqrt(D)
+    out = oracle.gqa_decode(q, k, v, np.array([2, 2], np.int32), lib=lib)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // n_rep
+            s0 = scale * float(np.dot(q[b, h].astype(np.float64), k[b, 0, g]))
+            s1 = scale * float(np.dot(q[b, h].astype(np.float64), k[b, 1, g]))
+            w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+            want = w0 * v[b, 0, g].astype(np.float64) + (1.0 - w0) * v[b, 1, g].astype(np.float64)
+            _close(out[b, h], want, 1e-14, "two-token sigmoid")
+    # saturating one-hot selection: q = 8*1, K[t*] = 8*1, other K = 0 -> exactly V[t*]
+    T2 = 40
+    q1 = np.full((1, Hq, D), 8.0, np.float32)
+    k1 = np.zeros((1, T2, Hkv, D), np.float32)
+    v1 = _rand(rng, 1, T2, Hkv, D)
+    for t_star in (0, 17, 39):
+        k1[:] = 0.0
+        k1[0, t_star] = 8.0
+        out = oracle.gqa_decode(q1, k1, v1, np.array([T2], np.int32), lib=lib)
+        for h in range(Hq):
+            assert np.array_equal(out[0, h], v1[0, t_star, h // n_rep].astype(np.float64)), "one-hot"
+
+
+def pin_decode_invariants(lib):
+    rng = _rng(11)
+    B, Hq, Hkv, D, T = 2, 8, 2, 16, 10
+    q, k, v = _rand(rng, B, Hq, D), _rand(rng, B, T, Hkv, D), _rand(rng, B, T, Hkv, D)
+    lens = np.array([10, 10], np.int32)
+    base = oracle.gqa_decode(q, k, v, lens, lib=lib)
+    perm = rng.permutation(T)
+    _close(oracle.gqa_decode(q, k[:, perm], v[:, perm], lens, lib=lib), base, 1e-13, "permutation")
+    # each output coordinate lies between the min and max of the V rows it read
+    n_rep = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            vv = v[b, :, h // n_rep].astype(np.float64)
+            assert np.all(base[b, h] <= vv.max(0) + 1e-12) and np.all(base[b, h] >= vv.min(0) - 1e-12)
+    # a constant added to every score changes nothing: single head, K' = K + c q/|q|^2
+    q1, k1, v1 = _rand(rng, 1, 1, D), _rand(rng, 1, T, 1, D), _rand(rng, 1, T, 1, D)
+    L1 = np.array([T], np.int32)
+    qq = q1[0, 0].astype(np.float64)
+    shift = (3.0 * qq / np.dot(qq, qq)).astype(np.float64)
+    k_shift = (k1.astype(np.float64) + shift[None, None, None, :])
+    a = oracle.gqa_decode(q1, k1, v1, L1, lib=lib)
+    b_ = oracle.gqa_decode(q1, k_shift.astype(np.float32), v1, L1, lib=lib)
+    assert _rel(a, b_) < 1e-5, "score shift"  # k_shift is rounded to float32 once
+    # an empty cache gives zeros; lengths beyond T_max are clamped
+    z = oracle.gqa_decode(q, k, v, np.array([0, 10], np.int32), lib=lib)
+    assert np.all(z[0] == 0.0) and np.all(np.isfinite(z))
+    _close(oracle.gqa_decode(q, k, v, np.array([999, 10], np.int32), lib=lib), base, 0.0, "clamp")
+
+
+def pin_decode_head_structure(lib):
+    rng = _rng(13)
+    B, Hq, D, T = 2, 8, 16, 9
+    lens = np.array([9, 4], np.int32)
+    # MHA (Hkv = Hq) equals single-head attention run independently per head
+    q, k, v = _rand(rng, B, Hq, D), _rand(rng, B, T, Hq, D), _rand(rng, B, T, Hq, D)
+    mha = oracle.gqa_decode(q, k, v, lens, lib=lib)
+    for h in range(Hq):
+        one = oracle.gqa_decode(np.ascontiguousarray(q[:, h:h + 1]), np.ascontiguousarray(k[:, :, h:h + 1]),
+                                np.ascontiguousarray(v[:, :, h:h + 1]), lens, lib=lib)
+        _close(mha[:, h:h + 1], one, 0.0, "MHA per head")
+    # MQA (Hkv = 1) equals MHA with the single K/V head copied to every head
+    k1, v1 = _rand(rng, B, T, 1, D), _rand(rng, B, T, 1, D)
+    mqa = oracle.gqa_decode(q, k1, v1, lens, lib=lib)
+    _close(mqa, oracle.gqa_decode(q, np.repeat(k1, Hq, axis=2), np.repeat(v1, Hq, axis=2), lens, lib=lib),
+           0.0, "MQA")
+    # GQA equals MHA on K/V expanded by repeat_kv: x[:, :, :, None, :] broadcast over n_rep, reshaped
+    for Hkv in (2, 4):
+        n_rep = Hq // Hkv
+        kg, vg = _rand(rng, B, T, Hkv, D), _rand(rng, B, T, Hkv, D)
+
+        def repeat_kv(x):
+            bs, slen, nkv, hd = x.shape
+            return np.broadcast_to(x[:, :, :, None, :], (bs, slen, nkv, n_rep, hd)).reshape(bs, slen, nkv * n_rep, hd)
+
+        ke, ve = repeat_kv(kg), repeat_kv(vg)
+        assert np.array_equal(ke, np.repeat(kg, n_rep, axis=2))  # the docstring's repeat_interleave
+        _close(oracle.gqa_decode(q, kg, vg, lens, lib=lib),
+               oracle.gqa_decode(q, np.ascontiguousarray(ke), np.ascontiguousarray(ve), lens, lib=lib),
+               0.0, f"repeat_kv n_rep={n_rep}")
+
+
+# ----------------------------------------------------------------------------- prefill pins
+
+PREFILL_SHAPES = [(2, 7, 8, 2, 16), (1, 5, 4, 4, 8), (1, 6, 4, 1, 8), (1, 33, 8, 2, 128)]
+
+
+def pin_prefill_vs_sdpa(lib):
+    for i, (B, S, Hq, Hkv, D) in enumerate(PREFILL_SHAPES):
+        rng = _rng(200 + i)
+        q, k, v = _rand(rng, B, S, Hq, D), _rand(rng, B, S, Hkv, D), _rand(rng, B, S, Hkv, D)
+        _close(oracle.gqa_prefill_causal(q, k, v, lib=lib), sdpa_prefill_ref(q, k, v), what="prefill")
+        _close(oracle.gqa_prefill_causal(q, k, v, softmax_scale=0.2, lib=lib),
+               sdpa_prefill_ref(q, k, v, scale=0.2), what="prefill scale")
+
+
+def pin_prefill_rows(lib):
+    rng = _rng(17)
+    B, S, Hq, Hkv, D = 2, 9, 8, 2, 16
+    q, k, v = _rand(rng, B, S, Hq, D), _rand(rng, B, S, Hkv, D), _rand(rng, B, S, Hkv, D)
+    full = oracle.gqa_prefill_causal(q, k, v, lib=lib)
+    n_rep = Hq // Hkv
+    for b in range(B):  # the first query sees only key 0
+        for h in range(Hq):
+            assert np.array_equal(full[b, 0, h], v[b, 0, h // n_rep].astype(np.float64)), "row 0"
+    sub = oracle.gqa_prefill_causal(q, k, v, rows=[8, 3], lib=lib)
+    _close(sub[:, [3, 8]], full[:, [3, 8]], 0.0, "row subset")
+    for i in (3, 8):  # causal row i = decode of query i against the first i+1 cached tokens
+        dec = oracle.gqa_decode(np.ascontiguousarray(q[:, i]), k, v, np.full(B, i + 1, np.int32), lib=lib)
+        _close(full[:, i], dec, 1e-14, f"row {i} vs decode")
+
+
+# ----------------------------------------------------------------------------- MLA pins
+
+MLA_SHAPES = [
+    # B, H, dn, dR, dv, r, T, lens
+    (2, 4, 8, 4, 6, 16, 7, [7, 3]),
+    (1, 8, 96, 48, 96, 128, 12, [12]),
+    (2, 2, 5, 3, 7, 9, 5, [5, 1]),
+]
+
+
+def _mla_inputs(rng, B, H, dn, dR, dv, r, T):
+    return (_rand(rng, B, H, dn), _rand(rng, B, H, dR), _rand(rng, H, dn, r) / np.float32(math.sqrt(r)),
+            _rand(rng, H, dv, r) / np.float32(math.sqrt(r)), _rand(rng, B, T, r), _rand(rng, B, T, dR))
+
+
+def pin_mla_vs_sdpa(lib):
+    for i, (B, H, dn, dR, dv, r, T, lens) in enumerate(MLA_SHAPES):
+        rng = _rng(300 + i)
+        args = _mla_inputs(rng, B, H, dn, dR, dv, r, T)
+        lens = np.array(lens, np.int32)
+        ref = sdpa_mla_ref(*args, lens)
+        _close(oracle.mla_decode_decompressed(*args, lens, lib=lib), ref, what="MLA decompressed")
+        _close(oracle.mla_decode_absorbed(*args, lens, lib=lib), ref, what="MLA absorbed")
+        ref_s = sdpa_mla_ref(*args, lens, scale=0.11)
+        _close(oracle.mla_decode_absorbed(*args, lens, softmax_scale=0.11, lib=lib), ref_s, what="MLA scale")
+
+
+def pin_mla_absorbed_equals_decompressed(lib):
+    rng = _rng(19)
+    B, H, dn, dR, dv, r, T = 3, 8, 96, 48, 96, 128, 20
+    args = _mla_inputs(rng, B, H, dn, dR, dv, r, T)
+    lens = np.array([20, 1, 13], np.int32)
+    a = oracle.mla_decode_absorbed(*args, lens, lib=lib)
+    d = oracle.mla_decode_decompressed(*args, lens, lib=lib)
+    _close(a, d, TOL, "absorbed vs decompressed")
+    sub = oracle.mla_decode_absorbed(*args, lens, bh=[5, 17], lib=lib)
+    flat, fsub = a.reshape(B * H, dv), sub.reshape(B * H, dv)
+    _close(fsub[[5, 17]], flat[[5, 17]], 0.0, "bh subset")
+
+
+def pin_mla_selection(lib):
+    """0/1 selection weights and a saturating score make the output an exact copy of chosen
+    latent coordinates."""
+    H, dn, dR, dv, r, T = 2, 4, 4, 3, 8, 6
+    w_uk = np.zeros((H, dn, r), np.float32)
+    w_uv = np.zeros((H, dv, r), np.float32)
+    for h in range(H):
+        w_uk[h, 0, h] = 1.0              # k_nope[h][0] = c[h]
+        for i in range(dv):
+            w_uv[h, i, (i + 2 * h) % r] = 1.0  # v[h][i] = c[(i + 2h) % r]
+    rng = _rng(23)
+    c = _rand(rng, 1, T, r)
+    t_star = 4
+    for h in range(H):
+        c[0, :, h] = 0.0
+        c[0, t_star, h] = 50.0
+    q_nope = np.zeros((1, H, dn), np.float32)
+    q_nope[0, :, 0] = 50.0
+    q_rope = np.zeros((1, H, dR), np.float32)
+    k_rope = _rand(rng, 1, T, dR)
+    for fn in (oracle.mla_decode_absorbed, oracle.mla_decode_decompressed):
+        out = fn(q_nope, q_rope, w_uk, w_uv, c, k_rope, np.array([T], np.int32), lib=lib)
+        for h in range(H):
+            want = np.array([c[0, t_star, (i + 2 * h) % r] for i in range(dv)], np.float64)
+            assert np.array_equal(out[0, h], want), "MLA selection"
+
+
+ALL_PINS = [pin_decode_vs_sdpa, pin_decode_closed_forms, pin_decode_invariants, pin_decode_head_structure,
+            pin_prefill_vs_sdpa, pin_prefill_rows, pin_mla_vs_sdpa, pin_mla_absorbed_equals_decompressed,
+            pin_mla_selection]
