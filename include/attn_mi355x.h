@@ -1,0 +1,181 @@
+/*
+ * attn_mi355x.h -- C ABI of a small attention library for AMD Instinct MI355X
+ * (gfx950 / CDNA4): grouped-query attention over a KV cache (decode and causal
+ * prefill) and multi-head latent attention (MLA) decode over a latent cache.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *    never allocates, frees or synchronises: it validates its arguments, then
+ *    enqueues kernels on `stream` (a hipStream_t passed as void*, NULL = the
+ *    default stream) and returns.  Results are ready when the stream is.
+ *  - All tensors are dense and row-major (C order) with the shapes given below.
+ *  - Validation runs before any HIP call.  A call that returns an error status
+ *    has enqueued nothing, and attn_last_error() (thread-local) describes why.
+ *    ATTN_ERR_HIP is returned when the HIP runtime itself fails (no device,
+ *    launch failure); no error is ever thrown across the ABI.
+ *  - cache_lens[b] (int32, device memory) is the number of valid cached tokens
+ *    of sequence b, INCLUDING the newest token: decode attends to positions
+ *    t in [0, cache_lens[b]).  Values are clamped to [0, T_max] on the device
+ *    (they are not checked on the host, which would need a synchronisation).
+ *    A length of 0 yields an all-zero output row.  Cache slots at or beyond the
+ *    length are never read, so they may hold anything (including NaN).
+ *  - softmax_scale <= 0 selects the default: 1/sqrt(head_dim) for GQA and
+ *    1/sqrt(nope_head_dim + rope_dim) for MLA.
+ *  - Accumulation is fp32.  bf16 inputs are read as stored; softmax statistics,
+ *    partial results and the merge are fp32.
+ *  - Calls are reentrant; concurrent calls must not share a workspace.
+ *
+ * Head grouping (GQA-G): Hq query heads are split into Hkv = G contiguous
+ * groups of n_rep = Hq/Hkv heads; query head h reads KV head floor(h/n_rep).
+ * Hkv = Hq is MHA and Hkv = 1 is MQA.  Source: the "模型架构｜MQA & GQA 调研"
+ * page (section Grouped-query attention, and the repeat_kv / Attention.forward
+ * listing in its code section, whose expand-then-reshape gives the contiguous
+ * grouping).  A group count that does not divide Hq is an error and is never
+ * rounded ("MHA, MQA và GQA" e-book, third simulator step).
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  ATTN_ERR_SHAPE = 2,       /* a size is <= 0, out of range, or inconsistent     */
+  ATTN_ERR_GROUPS = 3,      /* Hkv does not divide Hq                            */
+  ATTN_ERR_UNSUPPORTED = 4, /* head size / dtype combination not built           */
+  ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required           */
+  ATTN_ERR_HIP = 6          /* the HIP runtime reported an error                 */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Version of this ABI (ATTN_ABI_VERSION of the built library). */
+int attn_abi_version(void);
+
+/* Short static description of a status code. */
+const char* attn_status_string(attn_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* GQA / MQA / MHA decode: one new query token per sequence against its cache.
+ *
+ * Computes, for every sequence b and query head h (g = floor(h / (Hq/Hkv))):
+ *   out[b,h,:] = sum_{t < L_b} softmax_t(scale * q[b,h,:] . k_cache[b,t,g,:]) v_cache[b,t,g,:]
+ * i.e. the score / fp32-softmax / weighted-sum core of Attention.forward on the
+ * "模型架构｜MQA & GQA 调研" page (code section) for one query position, after
+ * the new token has been written to the cache.
+ *
+ *   q          [B, Hq, head_dim]          in_dtype
+ *   k_cache    [B, T_max, Hkv, head_dim]  in_dtype   (the page's cache layout)
+ *   v_cache    [B, T_max, Hkv, head_dim]  in_dtype
+ *   cache_lens [B]                        int32
+ *   out        [B, Hq, head_dim]          out_dtype
+ *
+ * Supported: in_dtype ATTN_BF16 with head_dim in {64, 96, 128} and
+ * Hq/Hkv <= 64; in_dtype ATTN_F32 with head_dim in {64, 96, 128} and
+ * Hq/Hkv <= 16.  out_dtype ATTN_F32 or ATTN_BF16.
+ *
+ * The cache is split into chunks of `split_tokens` positions; every
+ * (chunk, KV head, sequence) is one workgroup that reads its K/V rows once for
+ * all Hq/Hkv query heads of the group, and a second kernel merges the chunks by
+ * their log-sum-exp.  split_tokens = 0 lets the library choose; otherwise it
+ * must be a multiple of 64 in [64, 65536].  The result does not depend on the
+ * split beyond fp32 rounding.
+ *
+ * workspace: device memory of at least attn_decode_gqa_workspace_bytes(...)
+ * bytes for the same arguments, 256-byte aligned, used for the per-chunk
+ * partial outputs.  Its contents need no initialisation.
+ */
+size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int head_dim, int T_max,
+                                       int split_tokens);
+
+attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* cache_lens, void* out, int B, int Hq, int Hkv,
+                            int head_dim, int T_max, float softmax_scale, attn_dtype in_dtype,
+                            attn_dtype out_dtype, int split_tokens, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Causal GQA prefill (no cached prefix): query i attends to keys j <= i.
+ *
+ *   out[b,i,h,:] = sum_{j <= i} softmax_j(scale * q[b,i,h,:] . k[b,j,g,:]) v[b,j,g,:]
+ *
+ * This is Attention.forward on the "模型架构｜MQA & GQA 调研" page with
+ * start_pos = 0 and the additive causal mask, equivalently the
+ * scaled_dot_product_attention(is_causal=True) call of the MultiHeadLatentAttention
+ * listing on the qqstock DeepSeek MLA article.  QK^T and PV run on bf16 MFMA with
+ * fp32 accumulation; the probabilities are rounded to bf16 before PV, as the
+ * page's softmax(...).type_as(xq) does.
+ *
+ *   q   [B, S, Hq, head_dim]   bf16          k, v [B, S, Hkv, head_dim]   bf16
+ *   out [B, S, Hq, head_dim]   out_dtype (ATTN_BF16 or ATTN_F32)
+ *
+ * Supported: in_dtype ATTN_BF16, head_dim 128 (64 also built), any S >= 1,
+ * Hq/Hkv any divisor split.  No workspace.
+ */
+attn_status attn_prefill_gqa_causal(const void* q, const void* k, const void* v, void* out, int B,
+                                    int S, int Hq, int Hkv, int head_dim, float softmax_scale,
+                                    attn_dtype in_dtype, attn_dtype out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* MLA decode, absorbed form, over a latent cache plus one shared RoPE key.
+ *
+ * Source: qqstock DeepSeek MLA article -- sections 1 (only the low-rank latent
+ * c is cached), 2 and 4 (the key up-projection W_UK is folded into the query,
+ * the value up-projection W_UV is applied after attention), 3 (a separate
+ * rotated key part shared by all heads), 6 (values share the latent with the
+ * un-rotated key) -- and its MultiHeadLatentAttention listing, whose
+ * decompress_k_nope / decompress_v_linear weights are w_uk / w_uv here and whose
+ * score width nope+rope sets the default scale.  Per sequence b and head h:
+ *
+ *   q_lat  = [ w_uk[h]^T q_nope[b,h] ,  q_rope[b,h] ]              (r + dR wide)
+ *   s_t    = scale * q_lat . [ c_kv[b,t] , k_rope[b,t] ]            t < L_b
+ *   o_lat  = sum_t softmax(s)_t c_kv[b,t]                           (r wide)
+ *   out[b,h] = w_uv[h] o_lat                                        (dv wide)
+ *
+ * which equals attention with decompressed keys [w_uk[h] c , k_rope] and values
+ * w_uv[h] c.  The cache rows (c_kv, k_rope) are read once per sequence for all H
+ * heads.
+ *
+ *   q_nope [B, H, nope_head_dim]      q_rope [B, H, rope_dim] (already rotated)
+ *   w_uk   [H, nope_head_dim, kv_lora_rank]   (= decompress_k_nope.weight viewed per head)
+ *   w_uv   [H, v_head_dim, kv_lora_rank]      (= decompress_v_linear.weight viewed per head)
+ *   c_kv   [B, T_max, kv_lora_rank]   k_rope [B, T_max, rope_dim] (already rotated)
+ *   cache_lens [B] int32              out [B, H, v_head_dim] out_dtype
+ *   all of q_nope, q_rope, w_uk, w_uv, c_kv, k_rope in in_dtype (ATTN_BF16).
+ *
+ * Supported: in_dtype ATTN_BF16, kv_lora_rank in {64, 128, 256, 512}... see
+ * attn_decode_mla_supported(); rope_dim a multiple of 16 up to 64; H <= 16;
+ * nope_head_dim and v_head_dim in [1, 256].  split_tokens as for attn_decode_gqa.
+ * workspace: at least attn_decode_mla_workspace_bytes(...) bytes.
+ */
+size_t attn_decode_mla_workspace_bytes(int B, int H, int kv_lora_rank, int rope_dim, int T_max,
+                                       int split_tokens);
+
+/* 1 if this (H, kv_lora_rank, rope_dim, in_dtype) combination is built, else 0. */
+int attn_decode_mla_supported(int H, int kv_lora_rank, int rope_dim, attn_dtype in_dtype);
+
+attn_status attn_decode_mla_absorbed(const void* q_nope, const void* q_rope, const void* w_uk,
+                                     const void* w_uv, const void* c_kv, const void* k_rope,
+                                     const int32_t* cache_lens, void* out, int B, int H,
+                                     int nope_head_dim, int rope_dim, int v_head_dim,
+                                     int kv_lora_rank, int T_max, float softmax_scale,
+                                     attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_H */

@@ -1,0 +1,227 @@
+"""Python binding of libattn_mi355x.so: GQA/MQA/MHA decode, causal GQA prefill and MLA
+absorbed decode on AMD MI355X (gfx950).
+
+The functions carry the C entry points' names and do argument marshalling only: they check
+that the torch tensors are CUDA (HIP) tensors of the right dtype, shape and layout, allocate
+the output and workspace with torch when the caller passes none, and call the C ABI on
+torch's current stream.  Every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is missing or fails to load, importing the functions
+raises.
+
+Build the library with ``python -m mha_mla_kv_amd.build`` (hipcc, gfx950).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn_mi355x.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "attn_mi355x.h")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_GROUPS",
+          4: "ATTN_ERR_UNSUPPORTED", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP"}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A non-OK status returned by the library."""
+
+    def __init__(self, status: int, fn: str, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{fn}: {self.name}: {detail}")
+
+
+def _declare(lib):
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_abi_version.restype = I
+    lib.attn_abi_version.argtypes = []
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [I]
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_decode_gqa_workspace_bytes.restype = Z
+    lib.attn_decode_gqa_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.attn_decode_gqa.restype = I
+    lib.attn_decode_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, Z, P]
+    lib.attn_prefill_gqa_causal.restype = I
+    lib.attn_prefill_gqa_causal.argtypes = [P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.attn_decode_mla_workspace_bytes.restype = Z
+    lib.attn_decode_mla_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.attn_decode_mla_supported.restype = I
+    lib.attn_decode_mla_supported.argtypes = [I, I, I, I]
+    lib.attn_decode_mla_absorbed.restype = I
+    lib.attn_decode_mla_absorbed.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, I,
+                                             P, Z, P]
+    return lib
+
+
+def lib():
+    """The loaded ctypes library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(f"{LIB_PATH} is missing: build it with `python -m mha_mla_kv_amd.build`")
+            _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/attn_mi355x.h."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: torch.Tensor, name: str, shape=None, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def _raise_if(status: int, fn: str):
+    if status != 0:
+        raise AttnError(status, fn, lib().attn_last_error().decode())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def attn_decode_gqa_workspace_bytes(B: int, Hq: int, Hkv: int, head_dim: int, T_max: int,
+                                    split_tokens: int = 0) -> int:
+    return int(lib().attn_decode_gqa_workspace_bytes(B, Hq, Hkv, head_dim, T_max, split_tokens))
+
+
+def attn_decode_gqa(q, k_cache, v_cache, cache_lens, out=None, softmax_scale: float = 0.0,
+                    out_dtype=torch.float32, split_tokens: int = 0, workspace=None):
+    """out[b,h] = softmax_t(scale q[b,h].k[b,t,g]) v[b,t,g], t < cache_lens[b], g = h // (Hq/Hkv).
+
+    q [B,Hq,D], k_cache/v_cache [B,T_max,Hkv,D] (same dtype, fp32 or bf16), cache_lens [B] int32,
+    out [B,Hq,D] of out_dtype.  Returns out."""
+    _check(q, "q")
+    B, Hq, D = q.shape
+    _check(k_cache, "k_cache", dtype=q.dtype)
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError(f"k_cache must be [B={B}, T_max, Hkv, {D}] (got {tuple(k_cache.shape)})")
+    T_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _check(v_cache, "v_cache", shape=k_cache.shape, dtype=q.dtype)
+    _check(cache_lens, "cache_lens", shape=(B,), dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    _check(out, "out", shape=(B, Hq, D))
+    need = attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T_max, split_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(workspace, "workspace", dtype=torch.uint8)
+    st = lib().attn_decode_gqa(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens), _ptr(out), B, Hq,
+                               Hkv, D, T_max, float(softmax_scale), _dt(q), _dt(out), int(split_tokens),
+                               _ptr(workspace), workspace.numel(), _stream(q.device))
+    _raise_if(st, "attn_decode_gqa")
+    return out
+
+
+def attn_prefill_gqa_causal(q, k, v, out=None, softmax_scale: float = 0.0, out_dtype=torch.bfloat16):
+    """Causal prefill: out[b,i,h] = softmax_{j<=i}(scale q[b,i,h].k[b,j,g]) v[b,j,g].
+
+    q [B,S,Hq,D], k/v [B,S,Hkv,D] bf16; out [B,S,Hq,D] of out_dtype.  Returns out."""
+    _check(q, "q")
+    B, S, Hq, D = q.shape
+    _check(k, "k", dtype=q.dtype)
+    if k.dim() != 4 or k.shape[0] != B or k.shape[1] != S or k.shape[3] != D:
+        raise ValueError(f"k must be [B={B}, S={S}, Hkv, {D}] (got {tuple(k.shape)})")
+    Hkv = k.shape[2]
+    _check(v, "v", shape=k.shape, dtype=q.dtype)
+    if out is None:
+        out = torch.empty((B, S, Hq, D), dtype=out_dtype, device=q.device)
+    _check(out, "out", shape=(B, S, Hq, D))
+    st = lib().attn_prefill_gqa_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, Hq, Hkv, D,
+                                       float(softmax_scale), _dt(q), _dt(out), _stream(q.device))
+    _raise_if(st, "attn_prefill_gqa_causal")
+    return out
+
+
+def attn_decode_mla_workspace_bytes(B: int, H: int, kv_lora_rank: int, rope_dim: int, T_max: int,
+                                    split_tokens: int = 0) -> int:
+    return int(lib().attn_decode_mla_workspace_bytes(B, H, kv_lora_rank, rope_dim, T_max, split_tokens))
+
+
+def attn_decode_mla_supported(H: int, kv_lora_rank: int, rope_dim: int, dtype=torch.bfloat16) -> bool:
+    return bool(lib().attn_decode_mla_supported(H, kv_lora_rank, rope_dim,
+                                                ATTN_BF16 if dtype == torch.bfloat16 else ATTN_F32))
+
+
+def attn_decode_mla_absorbed(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, cache_lens, out=None,
+                             softmax_scale: float = 0.0, out_dtype=torch.float32, split_tokens: int = 0,
+                             workspace=None):
+    """MLA decode with W_UK absorbed into the query and W_UV applied after the weighted sum.
+
+    q_nope [B,H,dn], q_rope [B,H,dR], w_uk [H,dn,r], w_uv [H,dv,r], c_kv [B,T_max,r],
+    k_rope [B,T_max,dR] (all bf16), cache_lens [B] int32 -> out [B,H,dv] of out_dtype."""
+    _check(q_nope, "q_nope")
+    B, H, dn = q_nope.shape
+    dt = q_nope.dtype
+    _check(q_rope, "q_rope", dtype=dt)
+    if q_rope.dim() != 3 or q_rope.shape[:2] != (B, H):
+        raise ValueError(f"q_rope must be [B={B}, H={H}, rope_dim] (got {tuple(q_rope.shape)})")
+    dR = q_rope.shape[2]
+    _check(w_uk, "w_uk", dtype=dt)
+    if w_uk.dim() != 3 or w_uk.shape[:2] != (H, dn):
+        raise ValueError(f"w_uk must be [H={H}, nope_head_dim={dn}, kv_lora_rank] (got {tuple(w_uk.shape)})")
+    r = w_uk.shape[2]
+    _check(w_uv, "w_uv", dtype=dt)
+    if w_uv.dim() != 3 or w_uv.shape[0] != H or w_uv.shape[2] != r:
+        raise ValueError(f"w_uv must be [H={H}, v_head_dim, kv_lora_rank={r}] (got {tuple(w_uv.shape)})")
+    dv = w_uv.shape[1]
+    _check(c_kv, "c_kv", dtype=dt)
+    if c_kv.dim() != 3 or c_kv.shape[0] != B or c_kv.shape[2] != r:
+        raise ValueError(f"c_kv must be [B={B}, T_max, kv_lora_rank={r}] (got {tuple(c_kv.shape)})")
+    T_max = c_kv.shape[1]
+    _check(k_rope, "k_rope", shape=(B, T_max, dR), dtype=dt)
+    _check(cache_lens, "cache_lens", shape=(B,), dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=out_dtype, device=q_nope.device)
+    _check(out, "out", shape=(B, H, dv))
+    need = attn_decode_mla_workspace_bytes(B, H, r, dR, T_max, split_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_nope.device)
+    _check(workspace, "workspace", dtype=torch.uint8)
+    st = lib().attn_decode_mla_absorbed(_ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(c_kv),
+                                        _ptr(k_rope), _ptr(cache_lens), _ptr(out), B, H, dn, dR, dv, r, T_max,
+                                        float(softmax_scale), _dt(q_nope), _dt(out), int(split_tokens),
+                                        _ptr(workspace), workspace.numel(), _stream(q_nope.device))
+    _raise_if(st, "attn_decode_mla_absorbed")
+    return out
+
+
+__all__ = ["attn_decode_gqa", "attn_decode_gqa_workspace_bytes", "attn_prefill_gqa_causal",
+           "attn_decode_mla_absorbed", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",
+           "AttnError", "lib", "header_functions", "LIB_PATH", "ATTN_F32", "ATTN_BF16"]

@@ -1,0 +1,315 @@
+// C-ABI host layer: argument validation, split planning, workspace carving and
+// kernel launch.  Validation runs before any HIP call, so every error status is
+// reachable (and tested) on a machine without a GPU.
+#include "attn_mi355x.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "attn_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+attn_status fail(attn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+attn_status ok() {
+  g_last_error[0] = '\0';
+  return ATTN_OK;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr size_t kAlign = 256;
+constexpr int kMaxGridYZ = 65535;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(attn_dtype d) { return d == ATTN_F32 || d == ATTN_BF16; }
+
+// Largest power of two <= x (x >= 1).
+int pow2_floor(long long x) {
+  int p = 1;
+  while ((long long)p * 2 <= x && p < (1 << 30)) p *= 2;
+  return p;
+}
+
+// Tokens per decode chunk.  Aim for at least ~8 workgroups per compute unit
+// (256 CUs) when every sequence is full, but keep a chunk long enough that the
+// fp32 partial results (n_rep * D * 4 bytes written and read back per chunk)
+// stay small next to the chunk's cache bytes, and at least one 32-token tile
+// per wave.
+int choose_split(int B, int Hkv, int n_rep, int T_max) {
+  const long long target_wgs = 2048;
+  long long per_pair = (long long)T_max;
+  long long pairs = (long long)B * Hkv;
+  long long want = pairs * per_pair / target_wgs;
+  int split = pow2_floor(want < 1 ? 1 : want);
+  int lo = 128;
+  if (n_rep >= 16) lo = 256;
+  if (n_rep >= 32) lo = 512;
+  if (split < lo) split = lo;
+  if (split > 2048) split = 2048;
+  return split;
+}
+
+bool valid_split(int split) { return split == 0 || (split >= 64 && split <= 65536 && split % 64 == 0); }
+
+struct GqaLayout {
+  int split, n_splits;
+  size_t o_part_off, lse_off, total;
+};
+
+GqaLayout gqa_layout(int B, int Hq, int Hkv, int D, int T_max, int split_tokens) {
+  GqaLayout l;
+  l.split = split_tokens ? split_tokens : choose_split(B, Hkv, Hq / (Hkv > 0 ? Hkv : 1), T_max);
+  l.n_splits = (T_max + l.split - 1) / l.split;
+  const size_t rows = (size_t)B * Hq * l.n_splits;
+  l.o_part_off = 0;
+  l.lse_off = align_up(rows * D * sizeof(float));
+  l.total = l.lse_off + align_up(rows * sizeof(float));
+  return l;
+}
+
+struct MlaLayout {
+  int split, n_splits;
+  size_t q_lat_off, o_part_off, lse_off, total;
+};
+
+MlaLayout mla_layout(int B, int H, int r, int dR, int T_max, int split_tokens) {
+  MlaLayout l;
+  // One (sequence, chunk) workgroup serves all heads, so there are B chunks
+  // rows of work; aim for ~4 workgroups per CU.
+  if (split_tokens) {
+    l.split = split_tokens;
+  } else {
+    long long want = (long long)B * T_max / 1024;
+    int s = pow2_floor(want < 1 ? 1 : want);
+    if (s < 128) s = 128;
+    if (s > 2048) s = 2048;
+    l.split = s;
+  }
+  l.n_splits = (T_max + l.split - 1) / l.split;
+  const size_t rows = (size_t)B * H * l.n_splits;
+  l.q_lat_off = 0;
+  l.o_part_off = align_up((size_t)B * 2 * 16 * (r + dR) * 2);
+  l.lse_off = l.o_part_off + align_up(rows * r * sizeof(float));
+  l.total = l.lse_off + align_up(rows * sizeof(float));
+  return l;
+}
+
+attn_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "null pointer argument";
+    case ATTN_ERR_SHAPE: return "invalid size argument";
+    case ATTN_ERR_GROUPS: return "KV head count does not divide query head count";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head size, dtype or layout";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int head_dim, int T_max,
+                                       int split_tokens) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || head_dim <= 0 || T_max <= 0 || !valid_split(split_tokens))
+    return 0;
+  return gqa_layout(B, Hq, Hkv, head_dim, T_max, split_tokens).total;
+}
+
+attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* cache_lens, void* out, int B, int Hq, int Hkv,
+                            int head_dim, int T_max, float softmax_scale, attn_dtype in_dtype,
+                            attn_dtype out_dtype, int split_tokens, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !cache_lens || !out)
+    return fail(ATTN_ERR_NULL, "attn_decode_gqa: q, k_cache, v_cache, cache_lens and out must be non-NULL");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || head_dim <= 0 || T_max <= 0)
+    return fail(ATTN_ERR_SHAPE, "attn_decode_gqa: sizes must be positive (B=%d Hq=%d Hkv=%d head_dim=%d T_max=%d)",
+                B, Hq, Hkv, head_dim, T_max);
+  if (B > kMaxGridYZ || Hkv > kMaxGridYZ)
+    return fail(ATTN_ERR_SHAPE, "attn_decode_gqa: B and Hkv must be <= %d", kMaxGridYZ);
+  if (Hq % Hkv != 0)
+    return fail(ATTN_ERR_GROUPS, "attn_decode_gqa: Hkv=%d does not divide Hq=%d (remainder %d); not rounded",
+                Hkv, Hq, Hq % Hkv);
+  if (!valid_split(split_tokens))
+    return fail(ATTN_ERR_SHAPE, "attn_decode_gqa: split_tokens=%d must be 0 or a multiple of 64 in [64, 65536]",
+                split_tokens);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_gqa: unknown dtype");
+  const int n_rep = Hq / Hkv;
+  const int in_bf16 = in_dtype == ATTN_BF16;
+  if (!attn::gqa_decode_supported(head_dim, n_rep, in_bf16))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_gqa: head_dim=%d with Hq/Hkv=%d and %s inputs is not built",
+                head_dim, n_rep, in_bf16 ? "bf16" : "fp32");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_gqa: q, caches and out must be 16-byte aligned");
+  const GqaLayout lay = gqa_layout(B, Hq, Hkv, head_dim, T_max, split_tokens);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(ATTN_ERR_WORKSPACE, "attn_decode_gqa: workspace of %zu bytes needed, %zu given%s", lay.total,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(ATTN_ERR_WORKSPACE, "attn_decode_gqa: workspace must be 256-byte aligned");
+
+  attn::GqaDecodeArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.lens = cache_lens;
+  a.out = out;
+  a.o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.o_part_off);
+  a.lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_off);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = head_dim;
+  a.T_max = T_max;
+  a.n_rep = n_rep;
+  a.split = lay.split;
+  a.n_splits = lay.n_splits;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  a.scale_log2e = scale * kLog2e;
+  a.in_bf16 = in_bf16;
+  a.out_bf16 = out_dtype == ATTN_BF16;
+  return hip_status(attn::launch_gqa_decode(a, static_cast<hipStream_t>(stream)), "attn_decode_gqa");
+}
+
+attn_status attn_prefill_gqa_causal(const void* q, const void* k, const void* v, void* out, int B,
+                                    int S, int Hq, int Hkv, int head_dim, float softmax_scale,
+                                    attn_dtype in_dtype, attn_dtype out_dtype, void* stream) {
+  if (!q || !k || !v || !out)
+    return fail(ATTN_ERR_NULL, "attn_prefill_gqa_causal: q, k, v and out must be non-NULL");
+  if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || head_dim <= 0)
+    return fail(ATTN_ERR_SHAPE, "attn_prefill_gqa_causal: sizes must be positive (B=%d S=%d Hq=%d Hkv=%d head_dim=%d)",
+                B, S, Hq, Hkv, head_dim);
+  if (B > kMaxGridYZ || Hq > kMaxGridYZ)
+    return fail(ATTN_ERR_SHAPE, "attn_prefill_gqa_causal: B and Hq must be <= %d", kMaxGridYZ);
+  if (Hq % Hkv != 0)
+    return fail(ATTN_ERR_GROUPS, "attn_prefill_gqa_causal: Hkv=%d does not divide Hq=%d (remainder %d); not rounded",
+                Hkv, Hq, Hq % Hkv);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_gqa_causal: unknown dtype");
+  if (in_dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_gqa_causal: only bf16 inputs are built (MFMA path)");
+  if (!attn::prefill_supported(head_dim))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_gqa_causal: head_dim=%d is not built", head_dim);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_gqa_causal: q, k, v and out must be 16-byte aligned");
+  attn::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.B = B;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = head_dim;
+  a.n_rep = Hq / Hkv;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  a.scale_log2e = scale * kLog2e;
+  a.out_bf16 = out_dtype == ATTN_BF16;
+  return hip_status(attn::launch_prefill(a, static_cast<hipStream_t>(stream)), "attn_prefill_gqa_causal");
+}
+
+size_t attn_decode_mla_workspace_bytes(int B, int H, int kv_lora_rank, int rope_dim, int T_max,
+                                       int split_tokens) {
+  if (B <= 0 || H <= 0 || kv_lora_rank <= 0 || rope_dim < 0 || T_max <= 0 || !valid_split(split_tokens))
+    return 0;
+  return mla_layout(B, H, kv_lora_rank, rope_dim, T_max, split_tokens).total;
+}
+
+int attn_decode_mla_supported(int H, int kv_lora_rank, int rope_dim, attn_dtype in_dtype) {
+  return in_dtype == ATTN_BF16 && attn::mla_decode_supported(H, kv_lora_rank, rope_dim) ? 1 : 0;
+}
+
+attn_status attn_decode_mla_absorbed(const void* q_nope, const void* q_rope, const void* w_uk,
+                                     const void* w_uv, const void* c_kv, const void* k_rope,
+                                     const int32_t* cache_lens, void* out, int B, int H,
+                                     int nope_head_dim, int rope_dim, int v_head_dim,
+                                     int kv_lora_rank, int T_max, float softmax_scale,
+                                     attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q_nope || !q_rope || !w_uk || !w_uv || !c_kv || !k_rope || !cache_lens || !out)
+    return fail(ATTN_ERR_NULL, "attn_decode_mla_absorbed: all tensor pointers must be non-NULL");
+  if (B <= 0 || H <= 0 || nope_head_dim <= 0 || rope_dim <= 0 || v_head_dim <= 0 || kv_lora_rank <= 0 ||
+      T_max <= 0)
+    return fail(ATTN_ERR_SHAPE,
+                "attn_decode_mla_absorbed: sizes must be positive (B=%d H=%d nope=%d rope=%d v=%d rank=%d T_max=%d)",
+                B, H, nope_head_dim, rope_dim, v_head_dim, kv_lora_rank, T_max);
+  if (B > kMaxGridYZ)
+    return fail(ATTN_ERR_SHAPE, "attn_decode_mla_absorbed: B must be <= %d", kMaxGridYZ);
+  if (nope_head_dim > 256 || v_head_dim > 256)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: nope_head_dim and v_head_dim must be <= 256");
+  if (!valid_split(split_tokens))
+    return fail(ATTN_ERR_SHAPE, "attn_decode_mla_absorbed: split_tokens=%d must be 0 or a multiple of 64 in [64, 65536]",
+                split_tokens);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: unknown dtype");
+  if (!attn_decode_mla_supported(H, kv_lora_rank, rope_dim, in_dtype))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: H=%d kv_lora_rank=%d rope_dim=%d %s is not built",
+                H, kv_lora_rank, rope_dim, in_dtype == ATTN_BF16 ? "bf16" : "fp32");
+  if (!aligned16(c_kv) || !aligned16(k_rope) || !aligned16(out))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: c_kv, k_rope and out must be 16-byte aligned");
+  const MlaLayout lay = mla_layout(B, H, kv_lora_rank, rope_dim, T_max, split_tokens);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(ATTN_ERR_WORKSPACE, "attn_decode_mla_absorbed: workspace of %zu bytes needed, %zu given%s",
+                lay.total, workspace_bytes, workspace ? "" : " (NULL)");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(ATTN_ERR_WORKSPACE, "attn_decode_mla_absorbed: workspace must be 256-byte aligned");
+  attn::MlaDecodeArgs a;
+  a.q_nope = q_nope;
+  a.q_rope = q_rope;
+  a.w_uk = w_uk;
+  a.w_uv = w_uv;
+  a.c_kv = c_kv;
+  a.k_rope = k_rope;
+  a.lens = cache_lens;
+  a.out = out;
+  char* ws = static_cast<char*>(workspace);
+  a.q_lat = ws + lay.q_lat_off;
+  a.o_part = reinterpret_cast<float*>(ws + lay.o_part_off);
+  a.lse = reinterpret_cast<float*>(ws + lay.lse_off);
+  a.B = B;
+  a.H = H;
+  a.dn = nope_head_dim;
+  a.dR = rope_dim;
+  a.dv = v_head_dim;
+  a.r = kv_lora_rank;
+  a.T_max = T_max;
+  a.split = lay.split;
+  a.n_splits = lay.n_splits;
+  const float scale =
+      softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)(nope_head_dim + rope_dim));
+  a.scale_log2e = scale * kLog2e;
+  a.out_bf16 = out_dtype == ATTN_BF16;
+  return hip_status(attn::launch_mla_decode(a, static_cast<hipStream_t>(stream)), "attn_decode_mla_absorbed");
+}
+
+}  // extern "C"

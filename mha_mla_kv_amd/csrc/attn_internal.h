@@ -1,0 +1,71 @@
+// Internal interface between the C-ABI host layer (attn_api.cpp) and the HIP
+// kernel translation units.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Tokens per MFMA tile processed by one wave in the decode kernels.
+constexpr int kDecodeTileTokens = 32;
+// Waves per decode workgroup.
+constexpr int kDecodeWaves = 4;
+
+struct GqaDecodeArgs {
+  const void* q;          // [B, Hq, D]
+  const void* k;          // [B, T_max, Hkv, D]
+  const void* v;          // [B, T_max, Hkv, D]
+  const int32_t* lens;    // [B]
+  void* out;              // [B, Hq, D]
+  float* o_part;          // [B, Hq, n_splits, D]   workspace
+  float* lse;             // [B, Hq, n_splits]      workspace (log2 domain)
+  int B, Hq, Hkv, D, T_max, n_rep;
+  int split;              // tokens per chunk (multiple of 64)
+  int n_splits;           // ceil(T_max / split)
+  float scale_log2e;      // softmax scale * log2(e)
+  int in_bf16;            // 1: bf16 inputs, 0: fp32 inputs
+  int out_bf16;           // 1: bf16 output, 0: fp32 output
+};
+
+struct PrefillArgs {
+  const void* q;  // [B, S, Hq, D] bf16
+  const void* k;  // [B, S, Hkv, D] bf16
+  const void* v;  // [B, S, Hkv, D] bf16
+  void* out;      // [B, S, Hq, D]
+  int B, S, Hq, Hkv, D, n_rep;
+  float scale_log2e;
+  int out_bf16;
+};
+
+struct MlaDecodeArgs {
+  const void* q_nope;   // [B, H, dn]
+  const void* q_rope;   // [B, H, dR]
+  const void* w_uk;     // [H, dn, r]
+  const void* w_uv;     // [H, dv, r]
+  const void* c_kv;     // [B, T_max, r]
+  const void* k_rope;   // [B, T_max, dR]
+  const int32_t* lens;  // [B]
+  void* out;            // [B, H, dv]
+  void* q_lat;          // [B, 2, 16, r + dR] bf16 (hi, lo), workspace
+  float* o_part;        // [B, H, n_splits, r]  workspace
+  float* lse;           // [B, H, n_splits]     workspace
+  int B, H, dn, dR, dv, r, T_max;
+  int split, n_splits;
+  float scale_log2e;
+  int out_bf16;
+};
+
+// Each launcher validates nothing (the host layer has done it) and returns the
+// HIP status of its launches.  Returns hipErrorInvalidValue for an
+// unsupported template combination (the host layer checks *_supported first).
+bool gqa_decode_supported(int D, int n_rep, int in_bf16);
+hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t stream);
+
+bool prefill_supported(int D);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+bool mla_decode_supported(int H, int r, int dR);
+hipError_t launch_mla_decode(const MlaDecodeArgs& a, hipStream_t stream);
+
+}  // namespace attn

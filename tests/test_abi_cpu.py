@@ -1,0 +1,125 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects invalid arguments on the host.
+
+Validation runs before any HIP call, so every error status is reachable without a GPU.  The
+calls below pass fake (never dereferenced) device pointers and are each built to fail
+validation; they are skipped where a GPU is visible so that a validation bug can never turn one
+of them into a real launch."""
+import ctypes
+
+import pytest
+import torch
+
+import mha_mla_kv_amd as attn
+
+OK, NULL, SHAPE, GROUPS, UNSUP, WS, HIP = range(7)
+F32, BF16 = attn.ATTN_F32, attn.ATTN_BF16
+FAKE = ctypes.c_void_p(0x100000)      # 256-byte aligned, never dereferenced
+FAKE_MIS = ctypes.c_void_p(0x100008)  # 8-byte aligned only
+
+no_gpu_only = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer validation runs without a GPU")
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = attn.lib()
+    names = attn.header_functions()
+    for required in ("attn_decode_gqa", "attn_prefill_gqa_causal", "attn_decode_mla_absorbed"):
+        assert required in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/attn_mi355x.h but not exported"
+    assert lib.attn_abi_version() == 1
+
+
+def test_status_strings():
+    lib = attn.lib()
+    for s in range(7):
+        assert lib.attn_status_string(s)
+    assert lib.attn_status_string(3) == b"KV head count does not divide query head count"
+
+
+def test_workspace_sizes():
+    # Llama-3-8B decode shape: partials [B, Hq, n_splits, D] fp32 + lse, 256-byte aligned pieces
+    n = attn.attn_decode_gqa_workspace_bytes(32, 32, 8, 128, 8192, 512)
+    splits = 8192 // 512
+    rows = 32 * 32 * splits
+    assert n == rows * 128 * 4 + ((rows * 4 + 255) // 256) * 256
+    assert attn.attn_decode_gqa_workspace_bytes(32, 32, 8, 128, 8192, 0) > 0
+    assert attn.attn_decode_gqa_workspace_bytes(0, 32, 8, 128, 8192, 0) == 0
+    assert attn.attn_decode_gqa_workspace_bytes(1, 32, 8, 128, 8192, 100) == 0  # split not a multiple of 64
+    assert attn.attn_decode_mla_workspace_bytes(64, 8, 128, 48, 4096, 0) > 0
+    assert attn.attn_decode_mla_supported(8, 128, 48)
+    assert not attn.attn_decode_mla_supported(8, 100, 48)
+    assert not attn.attn_decode_mla_supported(8, 128, 48, torch.float32)
+
+
+def _gqa(lib, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, out=FAKE, B=2, Hq=8, Hkv=2, D=128, T=64, scale=0.0,
+         ind=BF16, outd=F32, split=0, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = 1 << 30
+    return lib.attn_decode_gqa(q, k, v, lens, out, B, Hq, Hkv, D, T, scale, ind, outd, split, ws, wsb, None)
+
+
+@no_gpu_only
+def test_decode_gqa_validation():
+    lib = attn.lib()
+    assert _gqa(lib, q=None) == NULL
+    assert _gqa(lib, lens=None) == NULL
+    assert _gqa(lib, B=0) == SHAPE
+    assert _gqa(lib, T=-1) == SHAPE
+    assert _gqa(lib, B=70000) == SHAPE
+    assert _gqa(lib, Hq=32, Hkv=3) == GROUPS      # 32 heads into 3 groups: an error, not rounded
+    assert b"remainder 2" in lib.attn_last_error()
+    assert _gqa(lib, Hq=32, Hkv=6) == GROUPS
+    assert _gqa(lib, split=100) == SHAPE
+    assert _gqa(lib, ind=7) == UNSUP
+    assert _gqa(lib, D=80) == UNSUP
+    assert _gqa(lib, Hq=128, Hkv=1) == UNSUP     # n_rep 128 not built
+    assert _gqa(lib, ind=F32, Hq=64, Hkv=2) == UNSUP  # fp32 path: n_rep <= 16
+    assert _gqa(lib, q=FAKE_MIS) == UNSUP
+    assert _gqa(lib, ws=None) == WS
+    assert _gqa(lib, wsb=16) == WS
+    assert b"workspace" in lib.attn_last_error()
+    assert _gqa(lib, ws=FAKE_MIS) == WS
+
+
+@no_gpu_only
+def test_prefill_validation():
+    lib = attn.lib()
+    f = lambda **kw: lib.attn_prefill_gqa_causal(kw.get("q", FAKE), FAKE, FAKE, kw.get("out", FAKE), kw.get("B", 1),
+                                                 kw.get("S", 16), kw.get("Hq", 8), kw.get("Hkv", 2), kw.get("D", 128),
+                                                 0.0, kw.get("ind", BF16), BF16, None)
+    assert f(q=None) == NULL
+    assert f(S=0) == SHAPE
+    assert f(Hq=8, Hkv=3) == GROUPS
+    assert f(ind=F32) == UNSUP
+    assert f(D=80) == UNSUP
+    assert f(out=FAKE_MIS) == UNSUP
+
+
+@no_gpu_only
+def test_mla_validation():
+    lib = attn.lib()
+
+    def f(**kw):
+        return lib.attn_decode_mla_absorbed(kw.get("qn", FAKE), FAKE, FAKE, FAKE, kw.get("c", FAKE), FAKE, FAKE, FAKE,
+                                            kw.get("B", 2), kw.get("H", 8), kw.get("dn", 96), kw.get("dR", 48),
+                                            kw.get("dv", 96), kw.get("r", 128), kw.get("T", 64), 0.0,
+                                            kw.get("ind", BF16), F32, kw.get("split", 0), kw.get("ws", FAKE),
+                                            kw.get("wsb", 1 << 30), None)
+    assert f(qn=None) == NULL
+    assert f(T=0) == SHAPE
+    assert f(split=65) == SHAPE
+    assert f(H=17) == UNSUP
+    assert f(r=100) == UNSUP
+    assert f(dR=40) == UNSUP
+    assert f(ind=F32) == UNSUP
+    assert f(dn=300) == UNSUP
+    assert f(c=FAKE_MIS) == UNSUP
+    assert f(ws=None) == WS
+    assert f(wsb=10) == WS
+
+
+def test_python_binding_rejects_cpu_tensors():
+    q = torch.zeros(1, 8, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 16, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.attn_decode_gqa(q, k, k, torch.zeros(1, dtype=torch.int32))
