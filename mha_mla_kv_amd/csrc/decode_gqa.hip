@@ -94,7 +94,7 @@ __device__ __forceinline__ int clamp_len(int L, int T_max) { return L < 0 ? 0 : 
 // ---------------------------------------------------------------------------
 // bf16 inputs, MFMA.  HB blocks of 16 query heads (n_rep <= 16 * HB).
 template <int D, int HB>
-__global__ __launch_bounds__(256) void gqa_decode_bf16_partial(GqaDecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HB == 1 ? 4 : 1))) void gqa_decode_bf16_partial(GqaDecodeArgs a) {
   static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
   constexpr int KC = D / 32;           // 32-wide dim chunks (QK contraction)
   constexpr int DW = D / 16;           // 16-wide dim blocks (PV output rows)
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void gqa_decode_bf16_partial(GqaDecodeArgs a) 
   static_assert(2 * kDecodeWaves * HB * 16 * 4 + HB * 16 * D * 4 <= kVtElems * 2, "merge scratch must fit");
   __shared__ __attribute__((aligned(16))) u16 smem[kVtElems];
 
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
   const int L = clamp_len(a.lens[b], a.T_max);
   const int c0 = s * a.split;
   if (c0 >= L) return;  // uniform: the whole chunk is past the cache length
@@ -144,19 +144,26 @@ __global__ __launch_bounds__(256) void gqa_decode_bf16_partial(GqaDecodeArgs a) 
   }
   u16* vt = smem + wave * kDecodeTileTokens * VP;
 
-  for (int t0 = c0 + wave * kDecodeTileTokens; t0 < c1; t0 += kDecodeWaves * kDecodeTileTokens) {
-    // K as the A operand (row = token), V in the same layout (to be transposed).
-    bf16x8 kr[2][KC], vr[2][KC];
+  // K as the A operand (row = token), V in the same layout.  Row indices are
+  // clamped to L - 1: rows past the chunk end re-read a valid row and their
+  // scores are masked.
+  auto load_tile = [&](bf16x8 (&kr)[2][KC], bf16x8 (&vr)[2][KC], int t0) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int tok = min(t0 + 16 * u + row, L - 1);
       const u16* krow = kp + (size_t)tok * tok_stride + 8 * grp;
-      const u16* vrow = vp + (size_t)tok * tok_stride + 8 * grp;
 #pragma unroll
       for (int c = 0; c < KC; ++c) kr[u][c] = load_bf16x8(krow + 32 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tok = min(t0 + 16 * u + row, L - 1);
+      const u16* vrow = vp + (size_t)tok * tok_stride + 8 * grp;
 #pragma unroll
       for (int c = 0; c < KC; ++c) vr[u][c] = load_bf16x8(vrow + 32 * c);
     }
+  };
+  auto process_tile = [&](const bf16x8 (&kr)[2][KC], const bf16x8 (&vr)[2][KC], int t0) {
     // Scores: lane holds S^T[token 16u + 4grp + i][head 16hb + row]
     float sc[HB][2][4];
 #pragma unroll
@@ -220,6 +227,14 @@ __global__ __launch_bounds__(256) void gqa_decode_bf16_partial(GqaDecodeArgs a) 
       for (int hb = 0; hb < HB; ++hb) o[hb][w] = mfma_16x16x32(__builtin_bit_cast(bf16x8, av), pop[hb], o[hb][w]);
     }
     wave_lds_sync();
+  };
+
+  // Tiles of this wave: t0 = c0 + 32*wave + 128*i, one at a time.  (Keeping a
+  // second tile in flight was measured slower: it halves the waves per SIMD.)
+  for (int t0 = c0 + wave * kDecodeTileTokens; t0 < c1; t0 += kDecodeWaves * kDecodeTileTokens) {
+    bf16x8 kA[2][KC], vA[2][KC];
+    load_tile(kA, vA, t0);
+    process_tile(kA, vA, t0);
   }
 
   // ---- merge the four waves of the workgroup ----
@@ -290,7 +305,7 @@ __global__ __launch_bounds__(256) void gqa_decode_f32_partial(GqaDecodeArgs a) {
   __shared__ float mw[kDecodeWaves][NR], lw[kDecodeWaves][NR];
   __shared__ float ob[NR][D];
 
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
   const int L = clamp_len(a.lens[b], a.T_max);
   const int c0 = s * a.split;
   if (c0 >= L) return;
@@ -405,13 +420,18 @@ __global__ __launch_bounds__(256) void gqa_decode_f32_partial(GqaDecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Merge the chunks of every (sequence, query head) by their log2-sum-exp.
-// One wave per row; lanes cover the head dimension.
+// One wave per row.  Lane l covers dims 4*(l % (D/4)) .. +4 of the chunks
+// s = l / (D/4) + k * (64 / (D/4)), so all of a row's partial loads are issued
+// together; the lane groups are then summed with cross-lane shuffles.
+template <int D>
 __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
+  static_assert(D == 64 || D == 128 || D == 96, "head_dim");
+  constexpr int LPR = D / 4;                       // lanes per chunk row (16, 24 or 32)
+  constexpr int G = 64 / LPR;                      // chunk rows per pass (4, 2 or 2)
   const int rowid = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (rowid >= a.B * a.Hq) return;
   const int lane = threadIdx.x & 63;
   const int b = rowid / a.Hq;
-  const int D = a.D;
   const int L = clamp_len(a.lens[b], a.T_max);
   const int n = (L + a.split - 1) / a.split;
   const float* lse = a.lse + (size_t)rowid * a.n_splits;
@@ -419,23 +439,42 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
   float M = kNegInf;
   for (int s = lane; s < n; s += 64) M = fmaxf(M, lse[s]);
   M = wave_max(M);
-  float acc0 = 0.f, acc1 = 0.f, wsum = 0.f;
-  const bool has1 = lane + 64 < D;
-  for (int s = 0; s < n; ++s) {
-    const float w = exp2_fast(lse[s] - M);
-    wsum += w;
-    acc0 = fmaf(w, op[(size_t)s * D + lane], acc0);
-    if (has1) acc1 = fmaf(w, op[(size_t)s * D + lane + 64], acc1);
+  const int gi = lane / LPR, li = lane - gi * LPR;
+  const bool active = gi < G;  // D = 96: lanes 48..63 idle
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (active) {
+    for (int s = gi; s < n; s += G) {
+      const float w = exp2_fast(lse[s] - M);
+      const float4 v = *reinterpret_cast<const float4*>(op + (size_t)s * D + 4 * li);
+      wsum += w;
+      acc.x = fmaf(w, v.x, acc.x);
+      acc.y = fmaf(w, v.y, acc.y);
+      acc.z = fmaf(w, v.z, acc.z);
+      acc.w = fmaf(w, v.w, acc.w);
+    }
   }
+  // add the G chunk groups into group 0 (lanes LPR apart)
+#pragma unroll
+  for (int k = 1; k < G; k <<= 1) {
+    const int src = (lane + k * LPR) & 63;
+    wsum += __shfl(wsum, src);
+    acc.x += __shfl(acc.x, src);
+    acc.y += __shfl(acc.y, src);
+    acc.z += __shfl(acc.z, src);
+    acc.w += __shfl(acc.w, src);
+  }
+  if (gi != 0) return;
   const float inv = n > 0 ? 1.f / wsum : 0.f;
   if (a.out_bf16) {
-    __bf16* out = static_cast<__bf16*>(a.out) + (size_t)rowid * D;
-    if (lane < D) out[lane] = (__bf16)(acc0 * inv);
-    if (has1) out[lane + 64] = (__bf16)(acc1 * inv);
+    __bf16* out = static_cast<__bf16*>(a.out) + (size_t)rowid * D + 4 * li;
+    out[0] = (__bf16)(acc.x * inv);
+    out[1] = (__bf16)(acc.y * inv);
+    out[2] = (__bf16)(acc.z * inv);
+    out[3] = (__bf16)(acc.w * inv);
   } else {
-    float* out = static_cast<float*>(a.out) + (size_t)rowid * D;
-    if (lane < D) out[lane] = acc0 * inv;
-    if (has1) out[lane + 64] = acc1 * inv;
+    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + (size_t)rowid * D + 4 * li) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
 }
 
@@ -471,7 +510,9 @@ bool gqa_decode_supported(int D, int n_rep, int in_bf16) {
 
 hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t st) {
   if (!gqa_decode_supported(a.D, a.n_rep, a.in_bf16)) return hipErrorInvalidValue;
-  const dim3 grid(a.n_splits, a.Hkv, a.B);
+  // KV heads vary fastest so the workgroups of one chunk's heads (interleaved in
+  // memory, one row of Hkv*D per token) are dispatched together.
+  const dim3 grid(a.Hkv, a.n_splits, a.B);
   hipError_t e;
   if (a.in_bf16) {
     e = a.D == 64 ? launch_bf16<64>(a, grid, st) : a.D == 96 ? launch_bf16<96>(a, grid, st) : launch_bf16<128>(a, grid, st);
@@ -479,8 +520,10 @@ hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t st) {
     e = a.D == 64 ? launch_f32<64>(a, grid, st) : a.D == 96 ? launch_f32<96>(a, grid, st) : launch_f32<128>(a, grid, st);
   }
   if (e != hipSuccess) return e;
-  const int rows = a.B * a.Hq;
-  hipLaunchKernelGGL(gqa_decode_merge, dim3((rows + 3) / 4), dim3(256), 0, st, a);
+  const dim3 mgrid((a.B * a.Hq + 3) / 4);
+  if (a.D == 64) hipLaunchKernelGGL(gqa_decode_merge<64>, mgrid, dim3(256), 0, st, a);
+  else if (a.D == 96) hipLaunchKernelGGL(gqa_decode_merge<96>, mgrid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(gqa_decode_merge<128>, mgrid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

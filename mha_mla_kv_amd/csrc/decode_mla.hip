@@ -73,38 +73,42 @@ __device__ __forceinline__ float bf16_to_f32(u16 x) { return __builtin_bit_cast(
 // q_lat[b][hl][h][0:r]     = hi / lo bf16 parts of W_UK[h]^T q_nope[b,h]
 // q_lat[b][0][h][r:r+dR]   = q_rope[b,h];  q_lat[b][1][h][r:r+dR] = 0
 // heads h in [H, 16) are zero.
+// Grid (16, B), block 256: one workgroup per (padded head, sequence); thread j
+// owns latent column j (coalesced reads of W_UK rows), q_nope comes from LDS.
 __global__ __launch_bounds__(256) void mla_absorb(MlaDecodeArgs a) {
-  const int b = blockIdx.x;
+  __shared__ float qs[256];
+  const int h = blockIdx.x, b = blockIdx.y;
   const int RW = a.r + a.dR;
-  const u16* qn = static_cast<const u16*>(a.q_nope) + (size_t)b * a.H * a.dn;
-  const u16* qr = static_cast<const u16*>(a.q_rope) + (size_t)b * a.H * a.dR;
-  const u16* wk = static_cast<const u16*>(a.w_uk);
-  u16* ql = static_cast<u16*>(a.q_lat) + (size_t)b * 2 * kHeadsPad * RW;
-  for (int e = threadIdx.x; e < kHeadsPad * RW; e += 256) {
-    const int h = e / RW, j = e - h * RW;
-    u16 hi = 0, lo = 0;
-    if (h < a.H) {
-      if (j < a.r) {
-        float acc = 0.f;
-        const u16* wcol = wk + (size_t)h * a.dn * a.r + j;
-        const u16* qv = qn + (size_t)h * a.dn;
-        for (int i = 0; i < a.dn; ++i) acc = fmaf(bf16_to_f32(wcol[(size_t)i * a.r]), bf16_to_f32(qv[i]), acc);
-        const __bf16 h16 = (__bf16)acc;
-        const float rem = acc - (float)h16;
-        hi = __builtin_bit_cast(u16, h16);
-        lo = __builtin_bit_cast(u16, (__bf16)rem);
-      } else {
-        hi = qr[(size_t)h * a.dR + (j - a.r)];
-      }
+  u16* ql_hi = static_cast<u16*>(a.q_lat) + ((size_t)b * 2 * kHeadsPad + h) * RW;
+  u16* ql_lo = ql_hi + (size_t)kHeadsPad * RW;
+  if (h >= a.H) {
+    for (int j = threadIdx.x; j < RW; j += 256) {
+      ql_hi[j] = 0;
+      ql_lo[j] = 0;
     }
-    ql[(size_t)h * RW + j] = hi;
-    ql[(size_t)(kHeadsPad + h) * RW + j] = lo;
+    return;
+  }
+  const u16* qn = static_cast<const u16*>(a.q_nope) + ((size_t)b * a.H + h) * a.dn;
+  for (int i = threadIdx.x; i < a.dn; i += 256) qs[i] = bf16_to_f32(qn[i]);
+  __syncthreads();
+  const u16* wk = static_cast<const u16*>(a.w_uk) + (size_t)h * a.dn * a.r;
+  for (int j = threadIdx.x; j < a.r; j += 256) {
+    float acc = 0.f;
+    for (int i = 0; i < a.dn; ++i) acc = fmaf(bf16_to_f32(wk[(size_t)i * a.r + j]), qs[i], acc);
+    const __bf16 h16 = (__bf16)acc;
+    ql_hi[j] = __builtin_bit_cast(u16, h16);
+    ql_lo[j] = __builtin_bit_cast(u16, (__bf16)(acc - (float)h16));
+  }
+  const u16* qr = static_cast<const u16*>(a.q_rope) + ((size_t)b * a.H + h) * a.dR;
+  for (int e = threadIdx.x; e < a.dR; e += 256) {
+    ql_hi[a.r + e] = qr[e];
+    ql_lo[a.r + e] = 0;
   }
 }
 
 // ---------------------------------------------------------------------------
 template <int R, int DR>
-__global__ __launch_bounds__(256) void mla_decode_partial(MlaDecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 128 ? 4 : 1))) void mla_decode_partial(MlaDecodeArgs a) {
   static_assert(R % 32 == 0 && DR % 16 == 0 && DR >= 16 && DR <= 64, "unsupported latent/rope widths");
   constexpr int KC = R / 32;         // 32-wide latent chunks
   constexpr int RC = DR / 32;        // 32-wide rope chunks
@@ -145,9 +149,10 @@ __global__ __launch_bounds__(256) void mla_decode_partial(MlaDecodeArgs a) {
   for (int w = 0; w < DW; ++w) o[w] = f32x4{0.f, 0.f, 0.f, 0.f};
   u16* vt = smem + wave * kDecodeTileTokens * VP;
 
-  for (int t0 = c0 + wave * kDecodeTileTokens; t0 < c1; t0 += kDecodeWaves * kDecodeTileTokens) {
-    bf16x8 cr[2][KC], kr32[2][RC > 0 ? RC : 1];
-    s16x4 kr16[2];
+  constexpr int RCA = RC > 0 ? RC : 1;
+  // Latent rows as the A operand (row = token); indices clamped to L - 1 (rows
+  // past the chunk end re-read a valid row and are masked).
+  auto load_tile = [&](bf16x8 (&cr)[2][KC], bf16x8 (&kr32)[2][RCA], s16x4 (&kr16)[2], int t0) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int tok = min(t0 + 16 * u + row, L - 1);
@@ -159,6 +164,9 @@ __global__ __launch_bounds__(256) void mla_decode_partial(MlaDecodeArgs a) {
       for (int c = 0; c < RC; ++c) kr32[u][c] = load_bf16x8(rrow + 32 * c + 8 * grp);
       if constexpr (R16) kr16[u] = load_s16x4(rrow + 32 * RC + 4 * grp);
     }
+  };
+  auto process_tile = [&](const bf16x8 (&cr)[2][KC], const bf16x8 (&kr32)[2][RCA], const s16x4 (&kr16)[2],
+                          int t0) {
     float sc[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -215,6 +223,13 @@ __global__ __launch_bounds__(256) void mla_decode_partial(MlaDecodeArgs a) {
       o[w] = mfma_16x16x32(__builtin_bit_cast(bf16x8, av), pop, o[w]);
     }
     wave_lds_sync();
+  };
+
+  for (int t0 = c0 + wave * kDecodeTileTokens; t0 < c1; t0 += kDecodeWaves * kDecodeTileTokens) {
+    bf16x8 cA[2][KC], rA[2][RCA];
+    s16x4 sA[2];
+    load_tile(cA, rA, sA, t0);
+    process_tile(cA, rA, sA, t0);
   }
 
   lsum += __shfl_xor(lsum, 16);
@@ -266,43 +281,75 @@ __global__ __launch_bounds__(256) void mla_decode_partial(MlaDecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup per sequence: merge chunks into o_lat[H][r] (LDS), then
-// out[b,h,i] = sum_j W_UV[h][i][j] o_lat[h][j].
+// One workgroup per (head, sequence): merge the chunks into o_lat[r] (LDS),
+// then out[b,h,i] = sum_j W_UV[h][i][j] o_lat[j].  The W_UV product runs one
+// output row per wave step: lanes split the r-long dot product (16-byte loads of
+// the row) and a wave reduction finishes it.
 __global__ __launch_bounds__(256) void mla_merge_wuv(MlaDecodeArgs a) {
-  extern __shared__ float olat[];  // [H][r]
-  const int b = blockIdx.x;
+  __shared__ float olat[256];
+  __shared__ float wts[64];
+  __shared__ float wsum_s;
+  const int h = blockIdx.x, b = blockIdx.y;
   const int L = clamp_len(a.lens[b], a.T_max);
   const int n = (L + a.split - 1) / a.split;
   const int R = a.r;
-  for (int e = threadIdx.x; e < a.H * R; e += 256) {
-    const int h = e / R, j = e - h * R;
-    const float* lse = a.lse + ((size_t)b * a.H + h) * a.n_splits;
-    const float* op = a.o_part + ((size_t)b * a.H + h) * a.n_splits * R + j;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t row = (size_t)b * a.H + h;
+  const float* lse = a.lse + row * a.n_splits;
+  const float* op = a.o_part + row * a.n_splits * R;
+  if (wave == 0) {
+    // chunk weights 2^(lse_s - max); n <= n_splits, read 64 at a time
     float M = kNegInf;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, lse[s]);
-    float acc = 0.f, ws = 0.f;
-    for (int s = 0; s < n; ++s) {
-      const float w = exp2_fast(lse[s] - M);
+    for (int s = lane; s < n; s += 64) M = fmaxf(M, lse[s]);
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float ws = 0.f;
+    for (int s0 = 0; s0 < n; s0 += 64) {
+      const int s = s0 + lane;
+      const float w = s < n ? exp2_fast(lse[s] - M) : 0.f;
       ws += w;
-      acc = fmaf(w, op[(size_t)s * R], acc);
+      if (s0 == 0) wts[lane] = w;
     }
-    olat[e] = n > 0 ? acc / ws : 0.f;
+    for (int off = 32; off >= 1; off >>= 1) ws += __shfl_xor(ws, off);
+    if (lane == 0) wsum_s = ws;
   }
   __syncthreads();
-  const u16* wv = static_cast<const u16*>(a.w_uv);
-  for (int e = threadIdx.x; e < a.H * a.dv; e += 256) {
-    const int h = e / a.dv, i = e - h * a.dv;
-    const u16* wrow = wv + ((size_t)h * a.dv + i) * R;
-    const float* ov = olat + h * R;
+  const float inv = n > 0 ? 1.f / wsum_s : 0.f;
+  for (int j = tid; j < R; j += 256) {
     float acc = 0.f;
-    for (int j = 0; j < R; j += 8) {
+    for (int s = 0; s < n; ++s) {
+      // weights of chunks >= 64 are recomputed (only for very long caches)
+      const float w = s < 64 ? wts[s] : 0.f;
+      acc = fmaf(w, op[(size_t)s * R + j], acc);
+    }
+    olat[j] = acc * inv;
+  }
+  if (n > 64) {
+    // rare: more than 64 chunks; add the rest with recomputed weights
+    __syncthreads();
+    float M = kNegInf;
+    for (int s = 0; s < n; ++s) M = fmaxf(M, lse[s]);
+    for (int j = tid; j < R; j += 256) {
+      float acc = 0.f;
+      for (int s = 64; s < n; ++s) acc = fmaf(exp2_fast(lse[s] - M), op[(size_t)s * R + j], acc);
+      olat[j] += acc * inv;
+    }
+  }
+  __syncthreads();
+  const u16* wv = static_cast<const u16*>(a.w_uv) + (size_t)h * a.dv * R;
+  for (int i = wave; i < a.dv; i += 4) {
+    const u16* wrow = wv + (size_t)i * R;
+    float acc = 0.f;
+    for (int j = 8 * lane; j < R; j += 512) {
       const u16x8 w8 = *reinterpret_cast<const u16x8*>(wrow + j);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc = fmaf(bf16_to_f32(w8[k]), ov[j + k], acc);
+      for (int k = 0; k < 8; ++k) acc = fmaf(bf16_to_f32(w8[k]), olat[j + k], acc);
     }
-    const size_t oi = ((size_t)b * a.H + h) * a.dv + i;
-    if (a.out_bf16) static_cast<__bf16*>(a.out)[oi] = (__bf16)acc;
-    else static_cast<float*>(a.out)[oi] = acc;
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) {
+      const size_t oi = row * a.dv + i;
+      if (a.out_bf16) static_cast<__bf16*>(a.out)[oi] = (__bf16)acc;
+      else static_cast<float*>(a.out)[oi] = acc;
+    }
   }
 }
 
@@ -329,15 +376,14 @@ hipError_t launch_mla_decode(const MlaDecodeArgs& a, hipStream_t st) {
   if (!mla_decode_supported(a.H, a.r, a.dR)) return hipErrorInvalidValue;
   // w_uv rows are read 16 bytes at a time
   if (a.r % 8 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mla_absorb, dim3(a.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(mla_absorb, dim3(kHeadsPad, a.B), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(a.n_splits, a.B);
   e = a.r == 64 ? launch_partial<64>(a, grid, st) : a.r == 128 ? launch_partial<128>(a, grid, st)
                                                                : launch_partial<256>(a, grid, st);
   if (e != hipSuccess) return e;
-  const size_t shmem = (size_t)a.H * a.r * sizeof(float);
-  hipLaunchKernelGGL(mla_merge_wuv, dim3(a.B), dim3(256), shmem, st, a);
+  hipLaunchKernelGGL(mla_merge_wuv, dim3(a.H, a.B), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

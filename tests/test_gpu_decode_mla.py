@@ -32,6 +32,7 @@ CASES = [
     ("h1_r64_dr16", 2, 1, 32, 16, 48, 64, 200, [200, 33], 64),
     ("h16_r256_dr64", 2, 16, 128, 64, 128, 256, 260, [260, 129], 128),
     ("h5_r128_dr32", 2, 5, 64, 32, 80, 128, 150, [150, 64], 64),
+    ("many_chunks", 2, 2, 32, 16, 48, 64, 5000, [5000, 4097], 64),  # more than 64 chunks to merge
 ]
 
 
