@@ -86,16 +86,23 @@ const char* attn_last_error(void);
  * Hq/Hkv <= 64; in_dtype ATTN_F32 with head_dim in {64, 96, 128} and
  * Hq/Hkv <= 16.  out_dtype ATTN_F32 or ATTN_BF16.
  *
- * The cache is split into chunks of `split_tokens` positions; every
- * (chunk, KV head, sequence) is one workgroup that reads its K/V rows once for
- * all Hq/Hkv query heads of the group, and a second kernel merges the chunks by
- * their log-sum-exp.  split_tokens = 0 lets the library choose; otherwise it
- * must be a multiple of 64 in [64, 65536].  The result does not depend on the
- * split beyond fp32 rounding.
+ * Work is cut into pieces of cached positions of one (sequence, KV head); a
+ * workgroup reads a piece's K/V rows once for all Hq/Hkv query heads of the
+ * group, and pieces of one sequence are merged by their log-sum-exp in the same
+ * kernel.  split_tokens = 0 lets the library plan on the device from cache_lens
+ * (equal work per workgroup; batches up to 1024 sequences, else fixed chunks of
+ * its choice); otherwise pieces are fixed chunks of split_tokens positions, a
+ * multiple of 64 in [64, 65536].  The result does not depend on the split
+ * beyond fp32 rounding.
  *
  * workspace: device memory of at least attn_decode_gqa_workspace_bytes(...)
- * bytes for the same arguments, 256-byte aligned, used for the per-chunk
- * partial outputs.  Its contents need no initialisation.
+ * bytes for the same arguments, 256-byte aligned.  Its first B*Hkv int32 are
+ * completion counters: they must be zero before the first call that uses the
+ * workspace (e.g. allocate it zero-filled), and every call leaves them zero, so
+ * later calls with the same B, Hq, Hkv, head_dim, T_max and split_tokens may
+ * reuse it as is.  Zero it again before using it for other sizes (their
+ * counters lie where these sizes keep partial results).  The rest needs no
+ * initialisation.  One workspace per concurrent call.
  */
 size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int head_dim, int T_max,
                                        int split_tokens);

@@ -33,9 +33,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra: list[str], build_dir: str) -> str:
+    os.makedirs(build_dir, exist_ok=True)
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + DEVICE_FLAGS + extra
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
@@ -47,18 +47,19 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build_library(extra: list[str] | None = None, jobs: int = 4) -> str:
-    """Compile every HIP/C++ source for gfx950 and link the shared library. Always rebuilds."""
+def build_library(extra: list[str] | None = None, jobs: int = 4, out: str = LIB,
+                  build_dir: str = BUILD) -> str:
+    """Compile every HIP/C++ source for gfx950 and link the shared library at `out`. Always rebuilds."""
     extra = list(extra or [])
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, extra, build_dir), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -67,20 +68,59 @@ int choose_split(int B, int Hkv, int n_rep, int T_max) {
 
 bool valid_split(int split) { return split == 0 || (split >= 64 && split <= 65536 && split % 64 == 0); }
 
+// Decode schedule and workspace layout.  split_tokens > 0 selects fixed chunks;
+// 0 selects the balanced schedule (equal rows per workgroup, planned on the
+// device from cache_lens) when the batch fits its limits, else library-chosen
+// fixed chunks.  Workspace: [counters B*Hkv int32][lse slots*n_rep][o_part
+// slots*n_rep*D], each piece 256-byte aligned.
+constexpr int kBalancedMaxWgs = 2048;       // slot bound of the balanced schedule
+constexpr unsigned long long kBalancedMaxRows = 1ull << 31;
+
 struct GqaLayout {
+  bool balanced;
   int split, n_splits;
-  size_t o_part_off, lse_off, total;
+  long long slots;
+  size_t cnt_off, lse_off, o_off, total;
 };
+
+bool use_balanced(int B, int Hkv, int T_max, int split_tokens) {
+  return split_tokens == 0 && B <= attn::kBalancedMaxB &&
+         (unsigned long long)B * (unsigned long long)Hkv * (unsigned long long)T_max < kBalancedMaxRows;
+}
 
 GqaLayout gqa_layout(int B, int Hq, int Hkv, int D, int T_max, int split_tokens) {
   GqaLayout l;
-  l.split = split_tokens ? split_tokens : choose_split(B, Hkv, Hq / (Hkv > 0 ? Hkv : 1), T_max);
-  l.n_splits = (T_max + l.split - 1) / l.split;
-  const size_t rows = (size_t)B * Hq * l.n_splits;
-  l.o_part_off = 0;
-  l.lse_off = align_up(rows * D * sizeof(float));
-  l.total = l.lse_off + align_up(rows * sizeof(float));
+  const int n_rep = Hq / (Hkv > 0 ? Hkv : 1);
+  l.balanced = use_balanced(B, Hkv, T_max, split_tokens);
+  if (l.balanced) {
+    l.split = 0;
+    l.n_splits = 0;
+    l.slots = (long long)kBalancedMaxWgs + (long long)B * Hkv;
+  } else {
+    l.split = split_tokens ? split_tokens : choose_split(B, Hkv, n_rep, T_max);
+    l.n_splits = (T_max + l.split - 1) / l.split;
+    l.slots = (long long)B * Hkv * l.n_splits;
+  }
+  l.cnt_off = 0;
+  l.lse_off = align_up((size_t)B * Hkv * sizeof(int));
+  l.o_off = l.lse_off + align_up((size_t)l.slots * n_rep * sizeof(float));
+  l.total = l.o_off + align_up((size_t)l.slots * n_rep * D * sizeof(float));
   return l;
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 struct MlaLayout {
@@ -171,6 +211,11 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_gqa: q, caches and out must be 16-byte aligned");
   const GqaLayout lay = gqa_layout(B, Hq, Hkv, head_dim, T_max, split_tokens);
+  if (!lay.balanced && lay.n_splits > kMaxGridYZ)
+    return fail(ATTN_ERR_SHAPE, "attn_decode_gqa: ceil(T_max/split_tokens)=%d chunks exceed %d", lay.n_splits,
+                kMaxGridYZ);
+  if (lay.slots >= (1ll << 31) / (n_rep > 0 ? n_rep : 1))
+    return fail(ATTN_ERR_SHAPE, "attn_decode_gqa: too many chunks (B*Hkv*ceil(T_max/split_tokens) too large)");
   if (!workspace || workspace_bytes < lay.total)
     return fail(ATTN_ERR_WORKSPACE, "attn_decode_gqa: workspace of %zu bytes needed, %zu given%s", lay.total,
                 workspace_bytes, workspace ? "" : " (NULL)");
@@ -183,16 +228,29 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
   a.v = v_cache;
   a.lens = cache_lens;
   a.out = out;
-  a.o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.o_part_off);
-  a.lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_off);
+  char* ws = static_cast<char*>(workspace);
+  a.counters = reinterpret_cast<int*>(ws + lay.cnt_off);
+  a.lse = reinterpret_cast<float*>(ws + lay.lse_off);
+  a.o_part = reinterpret_cast<float*>(ws + lay.o_off);
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.D = head_dim;
   a.T_max = T_max;
   a.n_rep = n_rep;
+  a.balanced = lay.balanced;
   a.split = lay.split;
   a.n_splits = lay.n_splits;
+  a.grid_wgs = 0;
+  a.min_rows_per_wg = 0;
+  if (lay.balanced) {
+    // four decode workgroups fit on a compute unit (LDS and registers): one round
+    const int cus = device_cus();
+    if (cus <= 0) return fail(ATTN_ERR_HIP, "attn_decode_gqa: cannot query the current device");
+    a.grid_wgs = cus * 4 < kBalancedMaxWgs ? cus * 4 : kBalancedMaxWgs;
+    // keep a piece long against its partial: >= 16*n_rep rows, >= 2 tiles per wave
+    a.min_rows_per_wg = 16 * n_rep > 256 ? 16 * n_rep : 256;
+  }
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   a.scale_log2e = scale * kLog2e;
   a.in_bf16 = in_bf16;

@@ -12,17 +12,25 @@ constexpr int kDecodeTileTokens = 32;
 // Waves per decode workgroup.
 constexpr int kDecodeWaves = 4;
 
+// Largest batch the balanced decode schedule plans for (its per-workgroup
+// prefix sum of lengths lives in LDS); larger batches use fixed chunks.
+constexpr int kBalancedMaxB = 1024;
+
 struct GqaDecodeArgs {
   const void* q;          // [B, Hq, D]
   const void* k;          // [B, T_max, Hkv, D]
   const void* v;          // [B, T_max, Hkv, D]
   const int32_t* lens;    // [B]
   void* out;              // [B, Hq, D]
-  float* o_part;          // [B, Hq, n_splits, D]   workspace
-  float* lse;             // [B, Hq, n_splits]      workspace (log2 domain)
+  int* counters;          // [B, Hkv] completion counters, zero between calls (workspace)
+  float* lse;             // [slots, n_rep] log2-sum-exp of each piece   (workspace)
+  float* o_part;          // [slots, n_rep, D] normalised piece outputs  (workspace)
   int B, Hq, Hkv, D, T_max, n_rep;
-  int split;              // tokens per chunk (multiple of 64)
-  int n_splits;           // ceil(T_max / split)
+  int balanced;           // 1: balanced schedule, 0: fixed chunks
+  int split;              // fixed: positions per chunk (multiple of 64)
+  int n_splits;           // fixed: ceil(T_max / split)
+  int grid_wgs;           // balanced: workgroups launched
+  int min_rows_per_wg;    // balanced: fewest (position, KV head) rows per workgroup
   float scale_log2e;      // softmax scale * log2(e)
   int in_bf16;            // 1: bf16 inputs, 0: fp32 inputs
   int out_bf16;           // 1: bf16 output, 0: fp32 output

@@ -38,6 +38,28 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kHeadsPad = 16;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reductions across the four 16-lane rows of a wave without LDS traffic.
+// v_permlane16_swap_b32 a, b exchanges rows 1 and 3 of a with rows 0 and 2 of b;
+// v_permlane32_swap_b32 a, b the upper half of a with the lower half of b
+// (gfx950).  With a and b both holding x, lane l ends up with x_l and x_(l^16)
+// (resp. x_(l^32)) in a and b.  Written as inline asm (both operands read and
+// written) because the compiler builtin for these instructions loses its second
+// result; the s_nop pairs cover the VALU-write -> permlane-read hazard.
+__device__ __forceinline__ float2 pair_xor16(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return make_float2(a, b);
+}
+__device__ __forceinline__ float2 pair_xor32(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return make_float2(a, b);
+}
+__device__ __forceinline__ float max_xor16(float x) { const float2 p = pair_xor16(x); return fmaxf(p.x, p.y); }
+__device__ __forceinline__ float max_xor32(float x) { const float2 p = pair_xor32(x); return fmaxf(p.x, p.y); }
+__device__ __forceinline__ float sum_xor16(float x) { const float2 p = pair_xor16(x); return p.x + p.y; }
+__device__ __forceinline__ float sum_xor32(float x) { const float2 p = pair_xor32(x); return p.x + p.y; }
 __device__ __forceinline__ float rescale(float m, float M) { return m == kNegInf ? 0.f : exp2_fast(m - M); }
 __device__ __forceinline__ int clamp_len(int L, int T_max) { return L < 0 ? 0 : (L > T_max ? T_max : L); }
 
@@ -190,8 +212,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 128 ? 
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sc[u][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = max_xor16(mt);
+    mt = max_xor32(mt);
     const float mn = fmaxf(m, mt);
     const float alpha = exp2_fast(m - mn);
     m = mn;
@@ -232,8 +254,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 128 ? 
     process_tile(cA, rA, sA, t0);
   }
 
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = sum_xor16(lsum);
+  lsum = sum_xor32(lsum);
   __syncthreads();
   float* mw = reinterpret_cast<float*>(smem);  // [waves][16]
   float* lw = mw + kDecodeWaves * kHeadsPad;   // [waves][16]

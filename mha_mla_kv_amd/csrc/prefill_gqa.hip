@@ -40,6 +40,28 @@ constexpr int kWaves = 4;     // 32 rows each
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions across the four 16-lane rows of a wave without LDS traffic.
+// v_permlane16_swap_b32 a, b exchanges rows 1 and 3 of a with rows 0 and 2 of b;
+// v_permlane32_swap_b32 a, b the upper half of a with the lower half of b
+// (gfx950).  With a and b both holding x, lane l ends up with x_l and x_(l^16)
+// (resp. x_(l^32)) in a and b.  Written as inline asm (both operands read and
+// written) because the compiler builtin for these instructions loses its second
+// result; the s_nop pairs cover the VALU-write -> permlane-read hazard.
+__device__ __forceinline__ float2 pair_xor16(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return make_float2(a, b);
+}
+__device__ __forceinline__ float2 pair_xor32(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return make_float2(a, b);
+}
+__device__ __forceinline__ float max_xor16(float x) { const float2 p = pair_xor16(x); return fmaxf(p.x, p.y); }
+__device__ __forceinline__ float max_xor32(float x) { const float2 p = pair_xor32(x); return fmaxf(p.x, p.y); }
+__device__ __forceinline__ float sum_xor16(float x) { const float2 p = pair_xor16(x); return p.x + p.y; }
+__device__ __forceinline__ float sum_xor32(float x) { const float2 p = pair_xor32(x); return p.x + p.y; }
+
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -163,7 +185,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           sc[j][i] = s;
           mt = fmaxf(mt, s);
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = max_xor32(mt);
       const float mn = fmaxf(m, mt);  // finite: key 0 is visible to every row, in tile 0
       const float alpha = exp2_fast(m - mn);
       m = mn;
@@ -204,7 +226,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
 
   // normalise and store: lane holds O^T[dims 32d + 8(i/4) + 4h2 + (i%4)][row ln]
-  lsum += __shfl_xor(lsum, 32);
+  lsum = sum_xor32(lsum);
   if (my_row < a.S) {
     const float inv = 1.f / lsum;
     const size_t orow = ((size_t)b * a.S + my_row) * a.Hq + h;

@@ -146,3 +146,18 @@ def test_full_size_sampled_rows(name):
         ref = oracle.gqa_decode(inp["q"][sl], inp["k"][sl], inp["v"][sl], inp["cache_lens"][sl])
         tol = TOL_FP32 if spec["dtype"] == "f32" else TOL_BF16
         assert_close_rows(out[sl], ref, tol, f"{name} b={b} L={int(inp['cache_lens'][b])}")
+
+
+def test_workspace_reuse_across_calls_keeps_counters_zero():
+    """Calls that share one zero-filled workspace (same shape) stay correct, also when the
+    lengths change between calls, and leave the completion counters zero."""
+    import mha_mla_kv_amd as attn
+    B, Hq, Hkv, D, T = 6, 16, 4, 128, 3000
+    ws = torch.zeros(attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T, 0), dtype=torch.uint8, device="cuda")
+    for seed, lens in ((1, [3000, 1, 2999, 1500, 64, 0]), (2, [17, 3000, 3000, 2048, 1000, 999]), (3, [0, 0, 5, 3000, 2, 1])):
+        inp = synth.gqa_decode_inputs(B, Hq, Hkv, D, T, lens, seed=seed)
+        out = attn.attn_decode_gqa(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), inp["cache_lens"].cuda(), workspace=ws)
+        torch.cuda.synchronize()
+        assert_close_rows(out, oracle.gqa_decode(inp["q"], inp["k"], inp["v"], inp["cache_lens"]), TOL_BF16,
+                          f"reuse seed {seed}")
+        assert int(ws[:B * Hkv * 4].view(torch.int32).abs().sum()) == 0
