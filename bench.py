@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass over the three C-ABI entry points, each on its own synthetic workload
+(shapes from the pages' configurations, i.i.d. N(0,1) inputs from fixed seeds):
+
+  * attn_decode_gqa           Llama-3-8B-shaped GQA decode: B 32, Hq 32, Hkv 8, head_dim 128,
+                              cache lengths uniform in [1024, 8192] (T_max 8192), bf16 in, fp32 out
+  * attn_decode_mla_absorbed  MiniMind-768 MLA decode: B 64, 8 heads, nope 96, rope 48, v 96,
+                              kv_lora_rank 128, cache 4096, bf16
+  * attn_prefill_gqa_causal   Llama-3-8B-shaped causal prefill: B 4, S 4096, Hq 32, Hkv 8,
+                              head_dim 128, bf16 in / out
+
+The printed `value` is the GQA decode's KV-cache read rate (algorithmic bytes: every cached
+K and V row read once per KV head, 2*Hkv*head_dim*2 bytes per cached position) divided by
+its kernel time, measured with HIP events around each launch on the stream the library
+launches on.  The other two entry points are reported under "parts".  Inputs are resident in
+HBM before the timed region.  `cpu_baseline` times the fp64 CPU oracle (tests' checker, not
+tuned) on the same decode workload on this host.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GQA/MLA decode KV-cache GB/s (% HBM peak) + causal prefill TFLOP/s, 1 MI355X"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published (no sparsity)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gqa_decode_llama3_traffic.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU oracle time")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy per step (for counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mha_mla_kv_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when they were
+    taken on another version of the kernel's source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("source_hash") != src_hash:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): the library is a "
+              "single-GPU kernel set; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mha_mla_kv_amd as attn
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (HIP device)", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    attn.lib()  # fail loudly now if the library is missing
+
+    t_gen = time.time()
+    # ---- workloads (generated on the host from fixed seeds, then moved to HBM) ----
+    dspec = synth.WORKLOADS["llama3_8b_gqa_decode"]
+    dec_cpu = synth.make("llama3_8b_gqa_decode")
+    dec = {k: v.to(dev) for k, v in dec_cpu.items()}
+    B, Hq, D = dec["q"].shape
+    T_max, Hkv = dec["k"].shape[1], dec["k"].shape[2]
+    sum_len = int(dec_cpu["cache_lens"].clamp(0, T_max).sum())
+    dec_bytes = 2 * Hkv * D * 2 * sum_len                      # K and V rows, bf16, once per KV head
+    dec_flops = 4 * Hq * D * sum_len                           # QK^T and PV
+    dec_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    dec_ws = torch.zeros(attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T_max, 0), dtype=torch.uint8,
+                         device=dev)
+
+    mspec = synth.WORKLOADS["minimind768_mla_decode"]
+    mla_cpu = synth.make("minimind768_mla_decode")
+    mla = {k: v.to(dev) for k, v in mla_cpu.items()}
+    MB, H, dn = mla["q_nope"].shape
+    dR = mla["q_rope"].shape[2]
+    dv, r = mla["w_uv"].shape[1], mla["w_uv"].shape[2]
+    MT = mla["c_kv"].shape[1]
+    mla_len = int(mla_cpu["cache_lens"].clamp(0, MT).sum())
+    mla_bytes = (r + dR) * 2 * mla_len                          # one [c_kv, k_rope] row per position
+    mla_flops = H * (2 * (r + dR) + 2 * r) * mla_len
+    mla_out = torch.empty(MB, H, dv, dtype=torch.float32, device=dev)
+    mla_ws = torch.zeros(attn.attn_decode_mla_workspace_bytes(MB, H, r, dR, MT, 0), dtype=torch.uint8, device=dev)
+
+    pspec = synth.WORKLOADS["llama3_8b_gqa_prefill"]
+    pre = {k: v.to(dev) for k, v in synth.make("llama3_8b_gqa_prefill").items()}
+    PB, S, PHq, PD = pre["q"].shape
+    pre_flops = 4 * PB * PHq * PD * S * (S + 1) // 2           # unmasked (i, j <= i) pairs only
+    pre_out = torch.empty_like(pre["q"])
+    copy_src = copy_dst = None
+    if args.copy_calibration:
+        copy_src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        copy_dst = torch.empty_like(copy_src)
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+
+    stream = torch.cuda.current_stream(dev)
+
+    def run_decode():
+        attn.attn_decode_gqa(dec["q"], dec["k"], dec["v"], dec["cache_lens"], out=dec_out, workspace=dec_ws)
+
+    def run_mla():
+        attn.attn_decode_mla_absorbed(mla["q_nope"], mla["q_rope"], mla["w_uk"], mla["w_uv"], mla["c_kv"],
+                                      mla["k_rope"], mla["cache_lens"], out=mla_out, workspace=mla_ws)
+
+    def run_prefill():
+        attn.attn_prefill_gqa_causal(pre["q"], pre["k"], pre["v"], out=pre_out)
+
+    parts = [("gqa_decode", run_decode), ("mla_decode", run_mla), ("prefill", run_prefill)]
+    if args.copy_calibration:
+        parts.append(("copy_1GiB", lambda: copy_dst.copy_(copy_src)))
+
+    for _ in range(args.warmup):
+        for _, fn in parts:
+            fn()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+          for name, _ in parts}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        for name, fn in parts:
+            e0, e1 = ev[name][i]
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {name: float(np.mean([a.elapsed_time(b) for a, b in ev[name]])) for name, _ in parts}
+
+    dec_gbs = dec_bytes / (ms["gqa_decode"] * 1e-3) / 1e9
+    mla_gbs = mla_bytes / (ms["mla_decode"] * 1e-3) / 1e9
+    pre_tfs = pre_flops / (ms["prefill"] * 1e-3) / 1e12
+
+    dec_hash = source_hash("decode_gqa.hip", "attn_internal.h")
+    traffic = measured_traffic("gqa_decode_bf16<128, 1, true>", dec_hash)
+
+    result = {
+        "metric": METRIC,
+        "value": round(dec_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"llama3_8b_gqa_decode: B={B} Hq={Hq} Hkv={Hkv} head_dim={D} T_max={T_max} "
+                         f"cache_lens~U[{dspec['lens'][0]},{dspec['lens'][1]}] (sum {sum_len}) seed={dspec['seed']}, "
+                         "bf16 in, fp32 out, schedule=balanced"),
+            "step": "attn_decode_gqa + attn_decode_mla_absorbed + attn_prefill_gqa_causal, one launch each",
+            "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "prefill": PB * S},
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gqa_decode_bf16<128, 1, true> (attn_decode_gqa, one launch)",
+            "achieved": round(dec_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dec_bytes,
+            "avg_launch_ms": round(ms["gqa_decode"], 5),
+        },
+        "parts": {
+            "gqa_decode": {"ms": round(ms["gqa_decode"], 5), "GB/s": round(dec_gbs, 1),
+                           "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4), "TFLOP/s": round(dec_flops / (ms["gqa_decode"] * 1e-3) / 1e12, 2),
+                           "tokens_per_s": round(B / (ms["gqa_decode"] * 1e-3), 1)},
+            "mla_decode": {"ms": round(ms["mla_decode"], 5), "GB/s": round(mla_gbs, 1),
+                           "hbm_frac": round(mla_gbs / HBM_PEAK_GBS, 4),
+                           "algorithmic_bytes_per_launch": mla_bytes,
+                           "TFLOP/s": round(mla_flops / (ms["mla_decode"] * 1e-3) / 1e12, 2),
+                           "tokens_per_s": round(MB / (ms["mla_decode"] * 1e-3), 1),
+                           "workload": f"minimind768_mla_decode: B={MB} H={H} nope={dn} rope={dR} v={dv} r={r} "
+                                       f"cache={MT} seed={mspec['seed']}"},
+            "prefill": {"ms": round(ms["prefill"], 5), "TFLOP/s": round(pre_tfs, 1),
+                        "mfma_frac": round(pre_tfs / BF16_DENSE_PEAK_TFLOPS, 4),
+                        "algorithmic_flops_per_launch": pre_flops,
+                        "tokens_per_s": round(PB * S / (ms["prefill"] * 1e-3), 1),
+                        "workload": f"llama3_8b_gqa_prefill: B={PB} S={S} Hq={PHq} Hkv={pre['k'].shape[2]} "
+                                    f"head_dim={PD} seed={pspec['seed']} bf16 causal"},
+        },
+        "input_generation_s": round(t_gen, 2),
+    }
+    if args.copy_calibration:
+        result["parts"]["copy_1GiB"] = {"ms": round(ms["copy_1GiB"], 5),
+                                        "GB/s_read+write": round(2 * (1 << 30) / (ms["copy_1GiB"] * 1e-3) / 1e9, 1)}
+
+    if not args.no_cpu_baseline:
+        import oracle
+        # the oracle as it stands, on the same decode workload (all 32 sequences), repeated until
+        # about --cpu-seconds of host time
+        reps, t_cpu = 0, 0.0
+        t_begin = time.perf_counter()
+        while True:
+            t1 = time.perf_counter()
+            oracle.gqa_decode(dec_cpu["q"], dec_cpu["k"], dec_cpu["v"], dec_cpu["cache_lens"])
+            t_cpu += time.perf_counter() - t1
+            reps += 1
+            if time.perf_counter() - t_begin >= args.cpu_seconds or reps >= 50:
+                break
+        result["cpu_baseline"] = {
+            "value": round(dec_bytes * reps / t_cpu / 1e9, 3),
+            "unit": "GB/s",
+            "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": (f"fp64 C oracle (oracle/oracle.c, OpenMP over (sequence, head) rows) on the full "
+                       f"llama3_8b_gqa_decode workload, {reps} run(s) in {t_cpu:.2f} s (float32 copies of the "
+                       f"bf16 inputs; conversion included)"),
+        }
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

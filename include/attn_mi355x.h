@@ -162,10 +162,11 @@ attn_status attn_prefill_gqa_causal(const void* q, const void* k, const void* v,
  *   cache_lens [B] int32              out [B, H, v_head_dim] out_dtype
  *   all of q_nope, q_rope, w_uk, w_uv, c_kv, k_rope in in_dtype (ATTN_BF16).
  *
- * Supported: in_dtype ATTN_BF16, kv_lora_rank in {64, 128, 256, 512}... see
- * attn_decode_mla_supported(); rope_dim a multiple of 16 up to 64; H <= 16;
- * nope_head_dim and v_head_dim in [1, 256].  split_tokens as for attn_decode_gqa.
- * workspace: at least attn_decode_mla_workspace_bytes(...) bytes.
+ * Supported (attn_decode_mla_supported): in_dtype ATTN_BF16, kv_lora_rank in
+ * {64, 128, 256}, rope_dim in {16, 32, 48, 64}, H <= 16; nope_head_dim and
+ * v_head_dim in [1, 256].  split_tokens as for attn_decode_gqa.
+ * workspace: at least attn_decode_mla_workspace_bytes(...) bytes, 256-byte
+ * aligned, zero-filled before its first use with these sizes.
  */
 size_t attn_decode_mla_workspace_bytes(int B, int H, int kv_lora_rank, int rope_dim, int T_max,
                                        int split_tokens);

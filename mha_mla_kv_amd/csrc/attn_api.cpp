@@ -333,8 +333,8 @@ attn_status attn_decode_mla_absorbed(const void* q_nope, const void* q_rope, con
   if (!attn_decode_mla_supported(H, kv_lora_rank, rope_dim, in_dtype))
     return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: H=%d kv_lora_rank=%d rope_dim=%d %s is not built",
                 H, kv_lora_rank, rope_dim, in_dtype == ATTN_BF16 ? "bf16" : "fp32");
-  if (!aligned16(c_kv) || !aligned16(k_rope) || !aligned16(out))
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: c_kv, k_rope and out must be 16-byte aligned");
+  if (!aligned16(c_kv) || !aligned16(k_rope) || !aligned16(w_uv) || !aligned16(out))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: c_kv, k_rope, w_uv and out must be 16-byte aligned");
   const MlaLayout lay = mla_layout(B, H, kv_lora_rank, rope_dim, T_max, split_tokens);
   if (!workspace || workspace_bytes < lay.total)
     return fail(ATTN_ERR_WORKSPACE, "attn_decode_mla_absorbed: workspace of %zu bytes needed, %zu given%s",
