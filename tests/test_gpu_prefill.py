@@ -54,8 +54,10 @@ def test_prefill_first_row_is_v0_and_deterministic():
     assert np.array_equal(a, b)
     v = inp["v"].float().numpy()
     for h in range(8):
-        # query 0 sees only key 0: its output is V[0] up to the fp32 normalisation (p = 1 exactly)
-        assert np.array_equal(a[:, 0, h], v[:, 0, h // 4])
+        # query 0 sees only key 0, so its output is V[0]; the kernel's exp2(s*c - m)
+        # with m rounded gives p = 1 up to one fp32 rounding, hence the 1e-6 slack
+        # (a leak of any other key would show at the 1e-2 level)
+        np.testing.assert_allclose(a[:, 0, h], v[:, 0, h // 4], rtol=1e-6, atol=1e-6)
 
 
 def test_prefill_full_size_sampled_rows():
