@@ -12,18 +12,21 @@
 //    each wave owns 32 rows.  The linear workgroup id is mapped so that all heads
 //    of one KV group of one sequence run on the same XCD (one L2), heaviest
 //    q-tiles (most keys) first.
-//  * K/V tiles of 64 keys go HBM -> LDS with global_load_lds_dwordx4 (no staging
-//    registers, no LDS write instructions), double-buffered, one barrier per
-//    tile.  Key rows are stored unpadded with their 16-byte chunks XOR-swizzled
-//    by key, which keeps the 16-byte K operand reads and the transposed V reads
-//    free of bank conflicts.
+//  * K/V tiles of 64 keys go HBM -> LDS with buffer_load_dwordx4 ... lds (no
+//    staging registers, no LDS write instructions), double-buffered, one barrier
+//    per tile.  The buffer resource ends at the sequence's last key, so keys past
+//    it read as zeros without address clamping.  Key rows are stored unpadded
+//    with their 16-byte chunks XOR-swizzled by key, which keeps the 16-byte K
+//    operand reads and the transposed V reads free of bank conflicts on the
+//    256-byte-per-clock LDS.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: a 32-key K block is the A operand,
 //    the wave's Q^T is the B operand, held in registers for the whole kernel.  The
 //    accumulator gives each lane one query row (lane % 32) and 16 keys.
 //  * O^T += V^T P^T: P stays in the accumulator layout and is the B operand after
 //    a key permutation shared with the A operand; V^T comes from the row-major V
 //    tile through ds_read_b64_tr_b16.
-//  * Online softmax in base 2, scale and max folded into one FMA per score.  The
+//  * Online softmax in base 2, scale and max folded into one FMA per score; the
+//    row sum adds the bf16-rounded probabilities the PV product uses.  The
 //    reference max only moves (and O, l are rescaled) when a tile's max exceeds
 //    it by more than 2^8: probabilities then stay below 256, far inside bf16 and
 //    fp32 range, and most tiles skip the O rescale.
@@ -36,6 +39,7 @@ namespace attn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16;
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
@@ -53,10 +57,11 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // b (gfx950): with a and b both holding x, lane l ends up with x_l and x_(l^32).
 // Inline asm (both operands read and written) because the compiler builtin for
 // this instruction loses its second result; the s_nop pairs cover the
-// VALU-write -> permlane-read hazard.
+// VALU-write -> permlane-read hazard.  Not volatile: it touches no memory, so
+// the scheduler may move loads and other arithmetic across it.
 __device__ __forceinline__ float2 pair_xor32(float x) {
   float a = x, b = x;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
   return make_float2(a, b);
 }
 __device__ __forceinline__ float max_xor32(float x) { const float2 p = pair_xor32(x); return fmaxf(p.x, p.y); }
@@ -75,33 +80,60 @@ __device__ __forceinline__ u16x4 lds_read_tr16(const u16* p) {
   return __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(p)));
 }
 
-// 16-byte chunk c of key row r sits at chunk position c ^ swz(r).  Over 8
-// consecutive keys swz takes 8 distinct values (K operand reads: 8 lanes of one
-// chunk index per LDS cycle), and over 4 consecutive keys an even-aligned chunk
-// pair lands on 4 distinct pairs (transposed V reads: 4 keys x 2 chunks per cycle).
-__device__ __forceinline__ int swz(int r) { return ((r << 1) + (r >> 2)) & 7; }
-
-// HBM -> LDS copy of one 64-key tile of K or V (D/8 chunks per key); every lane
-// of an instruction writes its 16 bytes at LDS base + 16 * lane, so the lane
-// fetches the chunk that belongs at that position.  Keys past the end repeat
-// the last key (masked by causality).
+// 16-byte chunk c of key row r sits at chunk position c ^ swz<D>(r).  gfx950's
+// LDS serves 256 bytes per clock: 16 lanes of a 16-byte read, 32 lanes of an
+// 8-byte read.  K operand reads take one chunk index from 16 consecutive keys,
+// so swz must be a bijection on 16 consecutive keys modulo the 256-byte bank
+// period; transposed V reads take an aligned block of 4 chunks from 4
+// consecutive keys, so those keys must land the block on 4 different blocks.
+// D = 128 (256-byte rows): swz = 4 (r % 4) + (r / 4) % 4.
+// D = 64 (128-byte rows, two per bank period): swz = 4 ((r / 2) % 2) + (r / 4) % 4.
 template <int D>
-__device__ __forceinline__ void load_tile_lds(u16* lds_tile, const u16* src, size_t row_stride, int key0, int S,
-                                              int wave, int lane) {
-  constexpr int kChunks = D / 8;
-  constexpr int kRowsPerInst = 64 / kChunks;
-  constexpr int kInstPerWave = kBN / kRowsPerInst / kWaves;
-#pragma unroll
-  for (int i = 0; i < kInstPerWave; ++i) {
-    const int r0 = (wave * kInstPerWave + i) * kRowsPerInst;
-    const int r = r0 + lane / kChunks;
-    const int p = lane % kChunks;
-    const int key = min(key0 + r, S - 1);
-    const u16* g = src + (size_t)key * row_stride + 8 * (p ^ swz(r));
-    __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)(lds_tile + r0 * D),
-                                     16, 0, 0);
-  }
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
+
+// HBM -> LDS copies of 64-key tiles of K or V (D/8 16-byte chunks per key) with
+// buffer_load_dwordx4 ... lds.  Each lane of an instruction writes its 16 bytes at
+// LDS base + 16 * lane, so the lane fetches the chunk that belongs at that
+// position.  The buffer resource of a tile starts at the tile's first key and
+// ends after the sequence's last key (nothing for a tile outside 0..n_kt-1):
+// reads past it return zeros, so keys beyond the sequence and pipeline fill or
+// drain tiles cost no memory traffic and need no clamping.
+template <int D>
+struct TileCopy {
+  static constexpr int kChunks = D / 8;
+  static constexpr int kRowsPerInst = 64 / kChunks;
+  static constexpr int kInst = kBN / kRowsPerInst / kWaves;  // instructions per wave and tile
+  int voff[kInst];  // per-lane byte offset within the tile
+  int wave;
+
+  __device__ __forceinline__ TileCopy(int wave_, int lane, int row_bytes) : wave(wave_) {
+#pragma unroll
+    for (int i = 0; i < kInst; ++i) {
+      const int r = (wave * kInst + i) * kRowsPerInst + lane / kChunks;
+      voff[i] = r * row_bytes + 16 * ((lane % kChunks) ^ swz<D>(r));
+    }
+  }
+
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const u16* p, int kt, int n_kt, int S, int row_bytes) {
+    const bool ok = kt >= 0 && kt < n_kt;
+    const int key0 = ok ? kt * kBN : 0;
+    const char* base = reinterpret_cast<const char*>(p) + (size_t)key0 * row_bytes;
+    const unsigned long long end = (unsigned long long)(S - 1 - key0) * row_bytes + 2 * D;
+    const unsigned num = ok ? (unsigned)(end < 0xffffffffull ? end : 0xffffffffull) : 0u;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)num, 0x00020000);
+  }
+
+  __device__ __forceinline__ void issue(u16* lds_tile, __amdgpu_buffer_rsrc_t r) const {
+#pragma unroll
+    for (int i = 0; i < kInst; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(lds_tile + (wave * kInst + i) * kRowsPerInst * D), 16,
+          voff[i], 0, 0, 0);
+  }
+};
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 
@@ -136,6 +168,73 @@ __device__ __forceinline__ Tile map_tile(const PrefillArgs& a, int id) {
   return t;
 }
 
+// Per-lane constants of a wave.
+struct Lane {
+  int lane, ln, h2, row0, my_row;
+  float c;  // softmax scale * log2(e)
+};
+
+// LDS element offsets.  swz<D>(key) depends on key only through key % 16 in a way
+// that is the same for keys 32j + ln (j = 0, 1) and for keys 16v + x (v = 0..3),
+// and row r starts at r * D, whose low bits are clear.  So chunk c of key row
+// `key` sits at (key * D + 8 * (h ^ swz)) ^ (16 * c') for c = 2c' + h, and the
+// block of 4 chunks 4d + (0..3) of a transposed read at (...) ^ (32 * d): one
+// per-lane base, XORed with a constant, plus an immediate for the key block.
+struct LdsOffsets {
+  int k;      // K operand read of chunk h2 of key ln
+  int v_lo;   // transposed V read, lower key quad of step 0, dim block 0
+  int v_hi;   // ... upper key quad
+};
+
+template <int D>
+__device__ __forceinline__ LdsOffsets lds_offsets(const Lane& w) {
+  LdsOffsets o;
+  o.k = w.ln * D + 8 * (w.h2 ^ swz<D>(w.ln));
+  const int g16 = (w.lane >> 4) & 1, i16 = w.lane & 15;
+  const int vc = 2 * g16 + ((i16 & 3) >> 1);  // chunk within the dim block
+  const int klo = 4 * w.h2 + (i16 >> 2), khi = klo + 8;
+  o.v_lo = klo * D + 4 * (i16 & 1) + 8 * (vc ^ swz<D>(klo));
+  o.v_hi = khi * D + 4 * (i16 & 1) + 8 * (vc ^ swz<D>(khi));
+  return o;
+}
+
+// S^T of one tile from the K tile kc: lane holds S^T[key 32j + 8(i/4) + 4h2 + i%4][row ln]
+// (keys relative to the tile).  A = 32-key K block, B = the wave's Q^T.
+template <int D>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const u16* kc, const bf16x8 (&qop)[D / 16], int off) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const u16* kr = kc + 32 * j * D + (off ^ (16 * c));
+      acc = mfma_32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(kr)), qop[c], acc);
+    }
+    s[j] = acc;
+  }
+}
+
+// O^T[dims 32d..][rows] += V^T P^T over one tile from the V tile vc.  Step v of the
+// contraction covers keys 16v + 4h2 + (0..3) and 16v + 8 + 4h2 + (0..3); 16-lane
+// group (g16, h2) of a transposed read points at key 16v + 4h2 + (i16 >> 2) (+8),
+// dims 32d + 16g16 + 4(i16 & 3).
+template <int D>
+__device__ __forceinline__ void pv_tile(f32x16 (&o)[D / 32], const u16* vc, const bf16x8 (&p)[4], int off_lo,
+                                        int off_hi) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d) {
+      const u16x4 lo = lds_read_tr16(vc + 16 * v * D + (off_lo ^ (32 * d)));
+      const u16x4 hi = lds_read_tr16(vc + 16 * v * D + (off_hi ^ (32 * d)));
+      const u16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      o[d] = mfma_32x32x16(__builtin_bit_cast(bf16x8, av), p[v], o[d]);
+    }
+  }
+}
+
 // Running state of one wave: O^T accumulators, reference max, partial row sum.
 template <int D>
 struct RowState {
@@ -143,57 +242,37 @@ struct RowState {
   float m, lsum;
 };
 
-// One 64-key tile: issue the copies of tile kt+1 into (kn, vn) if there is one,
-// consume tile kt from (kc, vc) if some row of the wave sees it, then wait for
-// the copies and meet at the barrier.  The four buffers are distinct LDS
-// variables addressed directly, so the compiler can tell the copies in flight
-// from the reads of the current tile and does not wait for them before reading.
+// One 64-key tile: issue the copies of tile kt+1 into (kn, vn), consume tile kt
+// from (kc, vc) if some row of the wave sees it, then wait for the copies and
+// meet at the barrier.  The four buffers are distinct LDS variables addressed
+// directly, so the compiler can tell the copies in flight from the reads of the
+// current tile and does not wait for them before reading.
 template <int D>
 __device__ __forceinline__ void tile_step(RowState<D>& st, const u16* kc, const u16* vc, u16* kn, u16* vn,
-                                          const bf16x8 (&qop)[D / 16], int kt, int n_kt, int last_kt, int row0,
-                                          int my_row, const u16* kp, const u16* vp, size_t kv_row, int S,
-                                          float c_log2, int wave, int lane) {
-  constexpr int KC = D / 16;
-  constexpr int DB = D / 32;
-  const int ln = lane & 31, h2 = lane >> 5;
+                                          const bf16x8 (&qop)[D / 16], int kt, int n_kt, int last_kt,
+                                          const u16* kp, const u16* vp, int row_bytes, int S,
+                                          const TileCopy<D>& cp, const LdsOffsets& off, const Lane& w) {
   if (kt + 1 < n_kt) {  // (kn, vn) were released by the last barrier
-    load_tile_lds<D>(kn, kp, kv_row, (kt + 1) * kBN, S, wave, lane);
-    load_tile_lds<D>(vn, vp, kv_row, (kt + 1) * kBN, S, wave, lane);
+    cp.issue(kn, TileCopy<D>::rsrc(kp, kt + 1, n_kt, S, row_bytes));
+    cp.issue(vn, TileCopy<D>::rsrc(vp, kt + 1, n_kt, S, row_bytes));
   }
   if (kt <= last_kt) {
     const int kv0 = kt * kBN;
-    // S^T blocks: lane holds S^T[key kv0 + 32j + 8(i/4) + 4h2 + i%4][row ln]
     f32x16 sc[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      f32x16 acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-      const int key = 32 * j + ln;
-      const u16* kr = kc + key * D;
-      const int sw = swz(key);
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(kr + 8 * ((2 * c + h2) ^ sw)));
-        acc = mfma_32x32x16(kop, qop[c], acc);
-      }
-      sc[j] = acc;
-    }
-    if (kv0 + kBN - 1 > row0) {  // the tile reaches above the diagonal of some row
+    qk_tile<D>(sc, kc, qop, off.k);
+    if (kv0 + kBN - 1 > w.row0) {  // the tile reaches above the diagonal of some row
+      const int t = w.my_row - kv0 - 4 * w.h2;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + 32 * j + 8 * (i >> 2) + 4 * h2 + (i & 3);
-          sc[j][i] = key <= my_row ? sc[j][i] : kNegInf;
-        }
+        for (int i = 0; i < 16; ++i) sc[j][i] = 32 * j + 8 * (i >> 2) + (i & 3) <= t ? sc[j][i] : kNegInf;
     }
     float mr = kNegInf;  // raw row max; the scale is positive
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mr = fmaxf(mr, sc[j][i]);
-    const float mt = max_xor32(mr) * c_log2;
+    const float mt = max_xor32(mr) * w.c;
     // key 0 is visible to every row, so tile 0 always sets a finite reference
     if (__builtin_amdgcn_ballot_w64(mt > st.m + kRescaleSlack) != 0) {
       const float mn = fmaxf(st.m, mt);
@@ -201,39 +280,27 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, const u16* kc, const 
       st.m = mn;
       st.lsum *= alpha;
 #pragma unroll
-      for (int d = 0; d < DB; ++d) st.o[d] *= alpha;
+      for (int d = 0; d < D / 32; ++d) st.o[d] *= alpha;
     }
     // P^T operand of PV step v: S^T block v/2, values 8(v%2)..+8
     bf16x8 pop[4];
-    float ps = 0.f;
 #pragma unroll
     for (int v = 0; v < 4; ++v)
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const float p = exp2_fast(fmaf(sc[v >> 1][8 * (v & 1) + jj], c_log2, -st.m));
-        ps += p;
-        pop[v][jj] = (__bf16)p;
-      }
-    st.lsum += ps;
-    // O^T[dims 32d..][rows] += V^T P^T.  Step v covers keys 16v + 4h2 + (0..3) and
-    // 16v + 8 + 4h2 + (0..3) of the tile; 16-lane group (g16, h2) of a transposed
-    // read points at key 16v + 4h2 + (i16 >> 2) (+8), dims 32d + 16g16 + 4(i16 & 3).
-    const int g16 = (lane >> 4) & 1, i16 = lane & 15;
-    const int v_chunk = 2 * g16 + ((i16 & 3) >> 1);
+      for (int jj = 0; jj < 8; ++jj) pop[v][jj] = (__bf16)exp2_fast(fmaf(sc[v >> 1][8 * (v & 1) + jj], w.c, -st.m));
+    // row sum of the bf16-rounded probabilities (the ones the PV product uses),
+    // two per v_dot2_f32_bf16 against (1, 1), in four independent chains
+    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+    float ps4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int klo = 16 * v + 4 * h2 + (i16 >> 2), khi = klo + 8;
-      const u16* plo = vc + klo * D + 4 * (i16 & 1);
-      const u16* phi = vc + khi * D + 4 * (i16 & 1);
-      const int swlo = swz(klo), swhi = swz(khi);
+    for (int v = 0; v < 4; ++v)
 #pragma unroll
-      for (int d = 0; d < DB; ++d) {
-        const u16x4 lo = lds_read_tr16(plo + 8 * ((4 * d + v_chunk) ^ swlo));
-        const u16x4 hi = lds_read_tr16(phi + 8 * ((4 * d + v_chunk) ^ swhi));
-        const u16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        st.o[d] = mfma_32x32x16(__builtin_bit_cast(bf16x8, av), pop[v], st.o[d]);
+      for (int q = 0; q < 4; ++q) {
+        const bf16x2 pair = {pop[v][2 * q], pop[v][2 * q + 1]};
+        ps4[q] = __builtin_amdgcn_fdot2_f32_bf16(pair, one, ps4[q], false);
       }
-    }
+    st.lsum += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+    pv_tile<D>(st.o, vc, pop, off.v_lo, off.v_hi);
   }
   wait_vmem();      // this thread's copies of tile kt+1 have landed
   __syncthreads();  // ... and everyone's; nobody reads tile kt any more
@@ -255,12 +322,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int h = tl.h, b = tl.b;
   const int g = h / a.n_rep;
   const int q0 = tl.qt * kBM;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ln = lane & 31, h2 = lane >> 5;
+  Lane w;
+  w.lane = tid & 63;
+  w.ln = w.lane & 31;
+  w.h2 = w.lane >> 5;
+  w.row0 = q0 + wave * 32;
+  w.my_row = w.row0 + w.ln;
+  w.c = a.scale_log2e;
 
   const size_t q_row = (size_t)a.Hq * D;
-  const size_t kv_row = (size_t)a.Hkv * D;
+  const int row_bytes = a.Hkv * D * 2;
   const u16* qp = static_cast<const u16*>(a.q) + ((size_t)b * a.S * a.Hq + h) * D;
   const u16* kp = static_cast<const u16*>(a.k) + ((size_t)b * a.S * a.Hkv + g) * D;
   const u16* vp = static_cast<const u16*>(a.v) + ((size_t)b * a.S * a.Hkv + g) * D;
@@ -269,17 +342,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // visible to some row of this wave
   const int kv_end = min(a.S, q0 + kBM);
   const int n_kt = (kv_end + kBN - 1) / kBN;
-  const int row0 = q0 + wave * 32;
-  const int last_kt = min(n_kt - 1, (row0 + 31) / kBN);
-  const int my_row = row0 + ln;
+  const int last_kt = min(n_kt - 1, (w.row0 + 31) / kBN);
 
-  load_tile_lds<D>(k0, kp, kv_row, 0, a.S, wave, lane);
-  load_tile_lds<D>(v0, vp, kv_row, 0, a.S, wave, lane);
+  const TileCopy<D> cp(wave, w.lane, row_bytes);
+  cp.issue(k0, TileCopy<D>::rsrc(kp, 0, n_kt, a.S, row_bytes));
+  cp.issue(v0, TileCopy<D>::rsrc(vp, 0, n_kt, a.S, row_bytes));
+  const LdsOffsets off = lds_offsets<D>(w);
 
   // Q^T as the B operand: lane holds Q[row ln][16c + 8h2 ..+8]
   bf16x8 qop[KC];
   {
-    const u16* qr = qp + (size_t)min(my_row, a.S - 1) * q_row + 8 * h2;
+    const u16* qr = qp + (size_t)min(w.my_row, a.S - 1) * q_row + 8 * w.h2;
 #pragma unroll
     for (int c = 0; c < KC; ++c) qop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qr + 16 * c));
   }
@@ -291,32 +364,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     for (int i = 0; i < 16; ++i) st.o[d][i] = 0.f;
   st.m = kNegInf;
   st.lsum = 0.f;
-  const float c_log2 = a.scale_log2e;
 
   wait_vmem();
   __syncthreads();
   for (int kt = 0; kt < n_kt; kt += 2) {
-    tile_step<D>(st, k0, v0, k1, v1, qop, kt, n_kt, last_kt, row0, my_row, kp, vp, kv_row, a.S, c_log2, wave, lane);
+    tile_step<D>(st, k0, v0, k1, v1, qop, kt, n_kt, last_kt, kp, vp, row_bytes, a.S, cp, off, w);
     if (kt + 1 < n_kt)
-      tile_step<D>(st, k1, v1, k0, v0, qop, kt + 1, n_kt, last_kt, row0, my_row, kp, vp, kv_row, a.S, c_log2, wave,
-                   lane);
+      tile_step<D>(st, k1, v1, k0, v0, qop, kt + 1, n_kt, last_kt, kp, vp, row_bytes, a.S, cp, off, w);
   }
 
   // normalise and store: lane holds O^T[dims 32d + 8(i/4) + 4h2 + (i%4)][row ln]
   const float lsum = sum_xor32(st.lsum);
-  if (my_row < a.S) {
+  if (w.my_row < a.S) {
     const float inv = 1.f / lsum;
-    const size_t orow = ((size_t)b * a.S + my_row) * a.Hq + h;
+    const size_t orow = ((size_t)b * a.S + w.my_row) * a.Hq + h;
     if (a.out_bf16) {
       u16* op = static_cast<u16*>(a.out) + orow * D;
 #pragma unroll
       for (int d = 0; d < DB; ++d)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          u16x4 w;
+          u16x4 o4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(u16, (__bf16)(st.o[d][4 * q4 + e] * inv));
-          *reinterpret_cast<u16x4*>(op + 32 * d + 8 * q4 + 4 * h2) = w;
+          for (int e = 0; e < 4; ++e) o4[e] = __builtin_bit_cast(u16, (__bf16)(st.o[d][4 * q4 + e] * inv));
+          *reinterpret_cast<u16x4*>(op + 32 * d + 8 * q4 + 4 * w.h2) = o4;
         }
     } else {
       float* op = static_cast<float*>(a.out) + orow * D;
@@ -324,7 +395,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       for (int d = 0; d < DB; ++d)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<float4*>(op + 32 * d + 8 * q4 + 4 * h2) =
+          *reinterpret_cast<float4*>(op + 32 * d + 8 * q4 + 4 * w.h2) =
               make_float4(st.o[d][4 * q4] * inv, st.o[d][4 * q4 + 1] * inv, st.o[d][4 * q4 + 2] * inv,
                           st.o[d][4 * q4 + 3] * inv);
     }
