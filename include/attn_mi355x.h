@@ -164,9 +164,17 @@ attn_status attn_prefill_gqa_causal(const void* q, const void* k, const void* v,
  *
  * Supported (attn_decode_mla_supported): in_dtype ATTN_BF16, kv_lora_rank in
  * {64, 128, 256}, rope_dim in {16, 32, 48, 64}, H <= 16; nope_head_dim and
- * v_head_dim in [1, 256].  split_tokens as for attn_decode_gqa.
+ * v_head_dim in [1, 256].  c_kv, k_rope, w_uk, w_uv and out must be 16-byte
+ * aligned (else ATTN_ERR_UNSUPPORTED).
+ * split_tokens: 0 lets the library choose the chunk length (a power of two of at
+ * least 256 positions, about two chunks per compute unit over B * T_max);
+ * otherwise a multiple of 64 in [64, 65536].  Each (chunk, sequence) is one
+ * workgroup serving all H heads; a sequence of length L uses ceil(L / chunk)
+ * chunks, merged afterwards.
  * workspace: at least attn_decode_mla_workspace_bytes(...) bytes, 256-byte
- * aligned, zero-filled before its first use with these sizes.
+ * aligned, holding the absorbed queries and the per-chunk partial results; no
+ * initialisation is needed and every call overwrites what it uses.  One
+ * workspace per concurrent call.
  */
 size_t attn_decode_mla_workspace_bytes(int B, int H, int kv_lora_rank, int rope_dim, int T_max,
                                        int split_tokens);

@@ -130,16 +130,17 @@ struct MlaLayout {
 
 MlaLayout mla_layout(int B, int H, int r, int dR, int T_max, int split_tokens) {
   MlaLayout l;
-  // One (sequence, chunk) workgroup serves all heads, so there are B chunks
-  // rows of work; aim for ~4 workgroups per CU.
+  // One (chunk, sequence) workgroup serves all heads; aim for about two
+  // workgroups per CU over the whole batch, with chunks of at least 256 tokens
+  // so each wave's copy ring runs several steps.
   if (split_tokens) {
     l.split = split_tokens;
   } else {
-    long long want = (long long)B * T_max / 1024;
-    int s = pow2_floor(want < 1 ? 1 : want);
-    if (s < 128) s = 128;
-    if (s > 2048) s = 2048;
-    l.split = s;
+    const int cus = device_cus() > 0 ? device_cus() : 256;
+    const long long want = ((long long)B * T_max + 2LL * cus - 1) / (2LL * cus);
+    long long s = 256;
+    while (s < want && s < 65536) s <<= 1;
+    l.split = (int)s;
   }
   l.n_splits = (T_max + l.split - 1) / l.split;
   const size_t rows = (size_t)B * H * l.n_splits;
@@ -333,8 +334,9 @@ attn_status attn_decode_mla_absorbed(const void* q_nope, const void* q_rope, con
   if (!attn_decode_mla_supported(H, kv_lora_rank, rope_dim, in_dtype))
     return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: H=%d kv_lora_rank=%d rope_dim=%d %s is not built",
                 H, kv_lora_rank, rope_dim, in_dtype == ATTN_BF16 ? "bf16" : "fp32");
-  if (!aligned16(c_kv) || !aligned16(k_rope) || !aligned16(w_uv) || !aligned16(out))
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: c_kv, k_rope, w_uv and out must be 16-byte aligned");
+  if (!aligned16(c_kv) || !aligned16(k_rope) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(out))
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "attn_decode_mla_absorbed: c_kv, k_rope, w_uk, w_uv and out must be 16-byte aligned");
   const MlaLayout lay = mla_layout(B, H, kv_lora_rank, rope_dim, T_max, split_tokens);
   if (!workspace || workspace_bytes < lay.total)
     return fail(ATTN_ERR_WORKSPACE, "attn_decode_mla_absorbed: workspace of %zu bytes needed, %zu given%s",

@@ -9,17 +9,24 @@
 //   q_lat  = [W_UK[h]^T q_nope , q_rope],  s_t = scale q_lat . [c_t , k_rope_t],
 //   o_lat  = sum_t softmax(s)_t c_t,       out = W_UV[h] o_lat.
 //
-// Kernels (not from the pages; designed for CDNA4):
-//  1. mla_absorb: q_lat per (sequence, head) in fp32, stored as a bf16 hi/lo
-//     pair so the MFMA score keeps ~16 mantissa bits of q_lat.
-//  2. mla_decode_partial: one workgroup per (chunk, sequence) serves all heads
-//     (padded to 16), so every [c_kv , k_rope] row is read from HBM once per
-//     sequence.  S^T = [c k_rope] q_lat^T on v_mfma_f32_16x16x32_bf16 (plus one
-//     16x16x16 step when rope_dim is an odd multiple of 16); the latent tile is
-//     reused as V (values share it with the un-rotated key): it is staged
-//     row-major in LDS and read back transposed with ds_read_b64_tr_b16.  Online base-2 softmax as in the GQA decode.
-//  3. mla_merge_wuv: log2-sum-exp merge of the chunks into o_lat, then
-//     out = W_UV[h] o_lat in fp32.
+// Three kernels (not from the pages; designed for CDNA4), each a single memory
+// round trip where it can be:
+//  1. mla_absorb, one workgroup per (head, sequence): q_lat in fp32, kept as a
+//     bf16 hi/lo pair (the MFMA score then sees ~16 mantissa bits of q_lat).
+//  2. mla_decode_fused, grid (chunk, sequence), 4 waves, every workgroup serving
+//     all heads (padded to 16) of one chunk of one sequence, so each cache row is
+//     read from HBM once.  Wave w owns the 16-token slices c0 + 64k + 16w of the
+//     chunk and runs its own 3-stage ring of buffer_load_dwordx4 ... lds copies
+//     of the c_kv and k_rope slices.  S^T = [c k_rope] q_lat^T on 16x16x32 MFMA
+//     (a trailing 16-wide rope chunk is zero-padded to 32) with the latent read
+//     from LDS; P^T is the accumulator as it stands; O^T += V^T P^T on 16x16x16
+//     MFMA with V^T read transposed (ds_read_b64_tr_b16) from the same latent
+//     slice, since values share the latent with the un-rotated key.  A wave only
+//     reads rows it copied itself, so the loop has no workgroup barrier.  The
+//     four waves merge through LDS and the chunk's normalised o_lat and
+//     log2-sum-exp go to the workspace.
+//  3. mla_merge_wuv, one workgroup per (head, sequence): log2-sum-exp merge of
+//     the chunks, then out = W_UV[h] o_lat with the W_UV rows already in flight.
 #include <hip/hip_runtime.h>
 
 #include "attn_internal.h"
@@ -36,24 +43,28 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kHeadsPad = 16;
+constexpr int kWaves = kDecodeWaves;     // 4
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSlice = 16;               // tokens per wave slice
+constexpr int kStep = kSlice * kWaves;   // tokens per workgroup step
+constexpr int kStages = 3;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Reductions across the four 16-lane rows of a wave without LDS traffic.
 // v_permlane16_swap_b32 a, b exchanges rows 1 and 3 of a with rows 0 and 2 of b;
 // v_permlane32_swap_b32 a, b the upper half of a with the lower half of b
 // (gfx950).  With a and b both holding x, lane l ends up with x_l and x_(l^16)
-// (resp. x_(l^32)) in a and b.  Written as inline asm (both operands read and
-// written) because the compiler builtin for these instructions loses its second
-// result; the s_nop pairs cover the VALU-write -> permlane-read hazard.
+// (resp. x_(l^32)).  Inline asm (both operands read and written) because the
+// compiler builtin for these instructions loses its second result; the s_nop
+// pairs cover the VALU-write -> permlane-read hazard.  No memory is touched.
 __device__ __forceinline__ float2 pair_xor16(float x) {
   float a = x, b = x;
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
   return make_float2(a, b);
 }
 __device__ __forceinline__ float2 pair_xor32(float x) {
   float a = x, b = x;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
   return make_float2(a, b);
 }
 __device__ __forceinline__ float max_xor16(float x) { const float2 p = pair_xor16(x); return fmaxf(p.x, p.y); }
@@ -62,13 +73,8 @@ __device__ __forceinline__ float sum_xor16(float x) { const float2 p = pair_xor1
 __device__ __forceinline__ float sum_xor32(float x) { const float2 p = pair_xor32(x); return p.x + p.y; }
 __device__ __forceinline__ float rescale(float m, float M) { return m == kNegInf ? 0.f : exp2_fast(m - M); }
 __device__ __forceinline__ int clamp_len(int L, int T_max) { return L < 0 ? 0 : (L > T_max ? T_max : L); }
+__device__ __forceinline__ float bf16_to_f32(u16 x) { return __builtin_bit_cast(float, (unsigned)x << 16); }
 
-__device__ __forceinline__ bf16x8 load_bf16x8(const u16* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
-}
-__device__ __forceinline__ s16x4 load_s16x4(const u16* p) {
-  return __builtin_bit_cast(s16x4, *reinterpret_cast<const u16x4*>(p));
-}
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -76,315 +82,450 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(s16x4 a, s16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 // ds_read_b64_tr_b16: lane i of a 16-lane group points at row T0 + i/4,
-// columns 4(i%4).. of a row-major [token][dim] tile; lane j receives tokens
+// columns 4(i%4).. of a row-major [token][dim] block; lane j receives tokens
 // T0..T0+3 of column j.
-__device__ __forceinline__ u16x4 lds_read_tr16(const u16* p) {
+__device__ __forceinline__ s16x4 lds_read_tr16(const u16* p) {
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf;
   typedef __attribute__((address_space(3))) v4bf lds_v4bf;
-  return __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(p)));
+  return __builtin_bit_cast(s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(p)));
 }
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// Latent slice layout in LDS: 16 rows of R bf16, 16-byte chunk c of row r at
+// chunk position c ^ swz<R>(r).  gfx950's LDS serves 256 bytes per clock (16
+// lanes of a 16-byte read, 32 lanes of an 8-byte read).  The QK operand read
+// takes one chunk index from 16 consecutive rows, so swz is a bijection on them
+// modulo the 256-byte bank period; the transposed read takes a chunk pair from
+// 8 consecutive rows, so swz / 2 is a bijection on those (modulo the period).
+template <int R>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (R >= 128) return 2 * (r & 7) + ((r >> 3) & 1);
+  else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
 }
-__device__ __forceinline__ float bf16_to_f32(u16 x) { return __builtin_bit_cast(float, (unsigned)x << 16); }
+
+template <int R, int DR>
+struct Cfg {
+  static constexpr int RW = R + DR;
+  static constexpr int KC = R / 32;           // 32-wide latent chunks of the score
+  static constexpr int RC = DR / 32;          // 32-wide rope chunks
+  static constexpr bool R16 = (DR % 32) != 0; // one trailing 16-wide rope chunk
+  static constexpr int DW = R / 16;           // 16-wide latent blocks of O^T
+  static constexpr int kC = kSlice * R;       // latent slice (u16)
+  static constexpr int kCInst = kC * 2 / 1024;  // copy instructions per latent slice
+  static constexpr int kRInst = (kSlice * DR * 2 + 1023) / 1024;
+  static constexpr int kR = kRInst * 512;     // rope slice (u16), padded to whole copies
+  static constexpr int kInstPerSlice = kCInst + kRInst;
+};
+
+// Per-lane constants of the slice copies and reads.
+template <int R, int DR>
+struct Lanes {
+  int lane, row, grp;
+  int c_voff[Cfg<R, DR>::kCInst];  // byte offset in the global latent slice of this lane's copy
+  int k_off;                       // QK operand read: element offset, XOR 32c per chunk
+  int v_off;                       // transposed V read: element offset, XOR 16w per block
+  __device__ __forceinline__ Lanes(int lane_) : lane(lane_), row(lane_ & 15), grp(lane_ >> 4) {
+    constexpr int CPR = R / 8;  // chunks per row
+#pragma unroll
+    for (int q = 0; q < Cfg<R, DR>::kCInst; ++q) {
+      const int s = 64 * q + lane, r = s / CPR, p = s % CPR;
+      c_voff[q] = r * 2 * R + 16 * (p ^ swz<R>(r));
+    }
+    k_off = row * R + 8 * (grp ^ swz<R>(row));
+    const int i = lane & 15, r = 4 * grp + (i >> 2);
+    v_off = r * R + 8 * (((i & 3) >> 1) ^ swz<R>(r)) + 4 * (i & 1);
+  }
+};
+
+// Buffer resource over rows [t0, lim) of a [T_max, width] bf16 cache of sequence
+// b: rows at or past lim read as zeros and cost no memory traffic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int b, int T_max, int width, int t0,
+                                                           int lim) {
+  const int rows = lim - t0;
+  const char* p = static_cast<const char*>(base) + ((size_t)b * T_max + (rows > 0 ? t0 : 0)) * width * 2;
+  const unsigned long long n = rows > 0 ? (unsigned long long)rows * width * 2 : 0ull;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, (int)(n < 0xffffffffull ? n : 0xffffffffull),
+                                           0x00020000);
+}
+
+template <int R, int DR>
+__device__ __forceinline__ void issue_slice(u16* cdst, u16* rdst, const MlaDecodeArgs& a, int b, int t0, int lim,
+                                            const Lanes<R, DR>& ln) {
+  using C = Cfg<R, DR>;
+  const auto rc = rows_rsrc(a.c_kv, b, a.T_max, R, t0, lim);
+  const auto rr = rows_rsrc(a.k_rope, b, a.T_max, DR, t0, lim);
+#pragma unroll
+  for (int q = 0; q < C::kCInst; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (__attribute__((address_space(3))) void*)(cdst + 512 * q), 16,
+                                             ln.c_voff[q], 0, 0, 0);
+#pragma unroll
+  for (int q = 0; q < C::kRInst; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void*)(rdst + 512 * q), 16,
+                                             16 * (64 * q + ln.lane), 0, 0, 0);
+}
+
+// vmcnt(n): wait until at most n of this wave's vector memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
+template <int R, int DR>
+struct WaveState {
+  f32x4 o[R / 16];  // O^T[16w + 4grp + i][head row]
+  float m, lsum;    // running max (scaled, log2) and this lane's part of the row sum
+};
 
 // ---------------------------------------------------------------------------
-// q_lat[b][hl][h][0:r]     = hi / lo bf16 parts of W_UK[h]^T q_nope[b,h]
-// q_lat[b][0][h][r:r+dR]   = q_rope[b,h];  q_lat[b][1][h][r:r+dR] = 0
-// heads h in [H, 16) are zero.
-// Grid (16, B), block 256: one workgroup per (padded head, sequence); thread j
-// owns latent column j (coalesced reads of W_UK rows), q_nope comes from LDS.
-__global__ __launch_bounds__(256) void mla_absorb(MlaDecodeArgs a) {
-  __shared__ float qs[256];
+// q_lat[b][hl][h][0:R] = hi / lo bf16 parts of W_UK[h]^T q_nope[b,h] (fp32 sum);
+// q_lat[b][0][h][R:R+DR] = q_rope[b,h], q_lat[b][1][h][R:] = 0; padded heads
+// h in [H, 16) are zero.  Grid (16, B), 256 threads, one workgroup per (head,
+// sequence): thread t owns latent columns 8(t % (R/8)) .. +8 (16-byte loads of
+// W_UK rows, which stay in L2 across the sequences) and every P-th row (P =
+// 2048 / R); all of a thread's loads are issued before the first use, and the P
+// partial sums meet in LDS.
+template <int R, int DR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void mla_absorb(MlaDecodeArgs a) {
+  constexpr int RW = R + DR;
+  constexpr int OCT = R / 8;         // column octets
+  constexpr int P = 256 / OCT;       // row parts
+  constexpr int MAXI = (256 + P - 1) / P;  // rows per part for nope_head_dim <= 256
+  constexpr int U = MAXI < 16 ? MAXI : 16;
+  __shared__ float red[P][R];
   const int h = blockIdx.x, b = blockIdx.y;
-  const int RW = a.r + a.dR;
-  u16* ql_hi = static_cast<u16*>(a.q_lat) + ((size_t)b * 2 * kHeadsPad + h) * RW;
-  u16* ql_lo = ql_hi + (size_t)kHeadsPad * RW;
+  const int tid = threadIdx.x;
+  const int oct = tid % OCT, part = tid / OCT;
+  u16* ql = static_cast<u16*>(a.q_lat) + ((size_t)b * 2 * kHeadsPad + h) * RW;
   if (h >= a.H) {
-    for (int j = threadIdx.x; j < RW; j += 256) {
-      ql_hi[j] = 0;
-      ql_lo[j] = 0;
-    }
+    for (int e = tid; e < RW; e += 256) ql[e] = ql[kHeadsPad * RW + e] = 0;
     return;
   }
+  const u16* wk = static_cast<const u16*>(a.w_uk) + (size_t)h * a.dn * R + 8 * oct;
   const u16* qn = static_cast<const u16*>(a.q_nope) + ((size_t)b * a.H + h) * a.dn;
-  for (int i = threadIdx.x; i < a.dn; i += 256) qs[i] = bf16_to_f32(qn[i]);
-  __syncthreads();
-  const u16* wk = static_cast<const u16*>(a.w_uk) + (size_t)h * a.dn * a.r;
-  for (int j = threadIdx.x; j < a.r; j += 256) {
-    float acc = 0.f;
-    for (int i = 0; i < a.dn; ++i) acc = fmaf(bf16_to_f32(wk[(size_t)i * a.r + j]), qs[i], acc);
-    const __bf16 h16 = (__bf16)acc;
-    ql_hi[j] = __builtin_bit_cast(u16, h16);
-    ql_lo[j] = __builtin_bit_cast(u16, (__bf16)(acc - (float)h16));
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int i0 = part; i0 < a.dn; i0 += U * P) {
+    u16x8 wv[U];
+    u16 qv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = min(i0 + u * P, a.dn - 1);
+      wv[u] = *reinterpret_cast<const u16x8*>(wk + (size_t)i * R);
+      qv[u] = qn[i];
+    }
+    asm volatile("" ::: "memory");  // issue the whole batch before the first use
+    // rows past the end were loaded clamped; they count with q = 0 (no branch,
+    // so every load above stays in flight together)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float q = i0 + u * P < a.dn ? bf16_to_f32(qv[u]) : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(bf16_to_f32(wv[u][e]), q, acc[e]);
+    }
+
   }
-  const u16* qr = static_cast<const u16*>(a.q_rope) + ((size_t)b * a.H + h) * a.dR;
-  for (int e = threadIdx.x; e < a.dR; e += 256) {
-    ql_hi[a.r + e] = qr[e];
-    ql_lo[a.r + e] = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[part][8 * oct + e] = acc[e];
+  __syncthreads();
+  for (int j = tid; j < R; j += 256) {
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < P; ++q) v += red[q][j];
+    const __bf16 hi = (__bf16)v;
+    ql[j] = __builtin_bit_cast(u16, hi);
+    ql[kHeadsPad * RW + j] = __builtin_bit_cast(u16, (__bf16)(v - (float)hi));
+  }
+  const u16* qr = static_cast<const u16*>(a.q_rope) + ((size_t)b * a.H + h) * DR;
+  for (int e = tid; e < DR; e += 256) {
+    ql[R + e] = qr[e];
+    ql[kHeadsPad * RW + R + e] = 0;
   }
 }
 
-// ---------------------------------------------------------------------------
+// One 16-token slice from (cs, rs): scores, online softmax, O^T update.
 template <int R, int DR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 128 ? 4 : 1))) void mla_decode_partial(MlaDecodeArgs a) {
-  static_assert(R % 32 == 0 && DR % 16 == 0 && DR >= 16 && DR <= 64, "unsupported latent/rope widths");
-  constexpr int KC = R / 32;         // 32-wide latent chunks
-  constexpr int RC = DR / 32;        // 32-wide rope chunks
-  constexpr bool R16 = (DR % 32) != 0;  // one trailing 16-wide rope chunk
-  constexpr int RW = R + DR;
-  constexpr int DW = R / 16;         // 16-wide latent blocks of the PV output
-  constexpr int VP = R + 16;  // latent tile row pitch ([token][dim], padded)
-  constexpr int kVtElems = kDecodeWaves * kDecodeTileTokens * VP;
-  static_assert(2 * kDecodeWaves * kHeadsPad * 4 + kHeadsPad * R * 4 <= kVtElems * 2, "merge scratch must fit");
-  __shared__ __attribute__((aligned(16))) u16 smem[kVtElems];
+__device__ __forceinline__ void slice_step(WaveState<R, DR>& st, const u16* cs, const u16* rs, const bf16x8 (&qhi)[R / 32],
+                                           const bf16x8 (&qlo)[R / 32], const bf16x8* qr32, bf16x8 qr16, int t0, int c1,
+                                           float c, const Lanes<R, DR>& ln) {
+  using C = Cfg<R, DR>;
+  // S^T[token 4grp + i][head row]: A = slice rows (token = row), B = q_lat^T
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < C::KC; ++k) {
+    const bf16x8 cr = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(cs + (ln.k_off ^ (32 * k))));
+    acc = mfma_16x16x32(cr, qhi[k], acc);
+    acc = mfma_16x16x32(cr, qlo[k], acc);
+  }
+#pragma unroll
+  for (int k = 0; k < C::RC; ++k) {
+    const bf16x8 kr = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(rs + ln.row * DR + 32 * k + 8 * ln.grp));
+    acc = mfma_16x16x32(kr, qr32[k], acc);
+  }
+  if constexpr (C::R16) {
+    // trailing 16 rope dims as a 16x16x32 product whose upper 16 contraction
+    // lanes (grp >= 2) are zero in both operands: the score chain then uses one
+    // MFMA shape only (a dependent chain that switches shape needs more wait
+    // states than the compiler provides on gfx950)
+    const bf16x8 kr = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(rs + ln.row * DR + 32 * C::RC + 8 * ln.grp));
+    const bf16x8 z = {};
+    acc = mfma_16x16x32(ln.grp < 2 ? kr : z, qr16, acc);
+  }
+  float s[4], mt = kNegInf;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s[i] = t0 + 4 * ln.grp + i < c1 ? acc[i] * c : kNegInf;
+    mt = fmaxf(mt, s[i]);
+  }
+  mt = max_xor32(max_xor16(mt));
+  const float mn = fmaxf(st.m, mt);
+  const float alpha = rescale(st.m, mn);
+  const float ms = mn == kNegInf ? 0.f : mn;  // a fully masked slice so far: p = 2^-inf = 0
+  st.m = mn;
+  s16x4 pop;
+  float ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const __bf16 pb = (__bf16)exp2_fast(s[i] - ms);
+    pop[i] = __builtin_bit_cast(short, pb);
+    ps += (float)pb;  // the rounded probabilities the product uses
+  }
+  st.lsum = st.lsum * alpha + ps;
+#pragma unroll
+  for (int w = 0; w < C::DW; ++w) st.o[w] *= alpha;
+  // O^T[16w..16w+15][heads] += V^T[dims][16 tokens] P^T[tokens][heads]
+#pragma unroll
+  for (int w = 0; w < C::DW; ++w) st.o[w] = mfma_16x16x16(lds_read_tr16(cs + (ln.v_off ^ (16 * w))), pop, st.o[w]);
+}
+
+template <int R, int DR>
+__global__ __launch_bounds__(kThreads) void mla_decode_fused(MlaDecodeArgs a) {
+  using C = Cfg<R, DR>;
+  constexpr int RW = C::RW;
+  // three ring stages per wave, each a distinct LDS variable so the compiler can
+  // tell the copies in flight from the reads of the resident stage
+  __shared__ __attribute__((aligned(1024))) u16 cst0[kWaves][C::kC];
+  __shared__ __attribute__((aligned(1024))) u16 cst1[kWaves][C::kC];
+  __shared__ __attribute__((aligned(1024))) u16 cst2[kWaves][C::kC];
+  __shared__ __attribute__((aligned(1024))) u16 rst0[kWaves][C::kR];
+  __shared__ __attribute__((aligned(1024))) u16 rst1[kWaves][C::kR];
+  __shared__ __attribute__((aligned(1024))) u16 rst2[kWaves][C::kR];
+  static_assert((2 * kWaves * kHeadsPad + kHeadsPad * R) * 4 <= (int)sizeof(cst0),
+                "merge scratch must fit in stage 0");
 
   const int s = blockIdx.x, b = blockIdx.y;
   const int L = clamp_len(a.lens[b], a.T_max);
-  const int c0 = s * a.split;
-  if (c0 >= L) return;
-  const int c1 = min(c0 + a.split, L);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = lane & 15, grp = lane >> 4;
+  const int n_chunks = (L + a.split - 1) / a.split;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const Lanes<R, DR> ln(tid & 63);
 
-  const u16* ql = static_cast<const u16*>(a.q_lat) + (size_t)b * 2 * kHeadsPad * RW;
-  bf16x8 qhi[KC], qlo[KC], qr32[RC > 0 ? RC : 1];
-  s16x4 qr16 = {0, 0, 0, 0};
+  if (s >= n_chunks) return;  // past the sequence (an empty one is zeroed by the merge)
+  const int c0 = s * a.split, c1 = min(c0 + a.split, L);
+  const int n_steps = (c1 - c0 + kStep - 1) / kStep;
+  const int tw0 = c0 + kSlice * wave;  // first token of this wave's first slice
+
+  // The stages start zeroed: rows past the chunk end are read (with P = 0) by
+  // the transposed V product, and uninitialised LDS could hold NaN patterns.
+  {
+    const u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+    u16* const bufs[6] = {&cst0[0][0], &cst1[0][0], &cst2[0][0], &rst0[0][0], &rst1[0][0], &rst2[0][0]};
+    const int lens_[6] = {kWaves * C::kC, kWaves * C::kC, kWaves * C::kC, kWaves * C::kR, kWaves * C::kR,
+                          kWaves * C::kR};
 #pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    qhi[c] = load_bf16x8(ql + (size_t)row * RW + 32 * c + 8 * grp);
-    qlo[c] = load_bf16x8(ql + (size_t)(kHeadsPad + row) * RW + 32 * c + 8 * grp);
+    for (int k = 0; k < 6; ++k)
+      for (int e = 8 * tid; e < lens_[k]; e += 8 * kThreads) *reinterpret_cast<u16x8*>(bufs[k] + e) = z;
   }
-#pragma unroll
-  for (int c = 0; c < RC; ++c) qr32[c] = load_bf16x8(ql + (size_t)row * RW + R + 32 * c + 8 * grp);
-  if constexpr (R16) qr16 = load_s16x4(ql + (size_t)row * RW + R + 32 * RC + 4 * grp);
-
-  const u16* cp = static_cast<const u16*>(a.c_kv) + (size_t)b * a.T_max * R;
-  const u16* rp = static_cast<const u16*>(a.k_rope) + (size_t)b * a.T_max * DR;
-
-  float m = kNegInf, lsum = 0.f;
-  f32x4 o[DW];
-#pragma unroll
-  for (int w = 0; w < DW; ++w) o[w] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u16* vt = smem + wave * kDecodeTileTokens * VP;
-
-  constexpr int RCA = RC > 0 ? RC : 1;
-  // Latent rows as the A operand (row = token); indices clamped to L - 1 (rows
-  // past the chunk end re-read a valid row and are masked).
-  auto load_tile = [&](bf16x8 (&cr)[2][KC], bf16x8 (&kr32)[2][RCA], s16x4 (&kr16)[2], int t0) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tok = min(t0 + 16 * u + row, L - 1);
-      const u16* crow = cp + (size_t)tok * R + 8 * grp;
-      const u16* rrow = rp + (size_t)tok * DR;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) cr[u][c] = load_bf16x8(crow + 32 * c);
-#pragma unroll
-      for (int c = 0; c < RC; ++c) kr32[u][c] = load_bf16x8(rrow + 32 * c + 8 * grp);
-      if constexpr (R16) kr16[u] = load_s16x4(rrow + 32 * RC + 4 * grp);
-    }
-  };
-  auto process_tile = [&](const bf16x8 (&cr)[2][KC], const bf16x8 (&kr32)[2][RCA], const s16x4 (&kr16)[2],
-                          int t0) {
-    float sc[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        acc = mfma_16x16x32(cr[u][c], qhi[c], acc);
-        acc = mfma_16x16x32(cr[u][c], qlo[c], acc);
-      }
-#pragma unroll
-      for (int c = 0; c < RC; ++c) acc = mfma_16x16x32(kr32[u][c], qr32[c], acc);
-      if constexpr (R16) acc = mfma_16x16x16(kr16[u], qr16, acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + 16 * u + 4 * grp + i;
-        sc[u][i] = tok < c1 ? acc[i] * a.scale_log2e : kNegInf;
-      }
-    }
-    float mt = kNegInf;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sc[u][i]);
-    mt = max_xor16(mt);
-    mt = max_xor32(mt);
-    const float mn = fmaxf(m, mt);
-    const float alpha = exp2_fast(m - mn);
-    m = mn;
-    bf16x8 pop;
-    float ps = 0.f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2_fast(sc[u][i] - mn);
-        ps += p;
-        pop[4 * u + i] = (__bf16)p;
-      }
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int w = 0; w < DW; ++w) o[w] *= alpha;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int c = 0; c < KC; ++c)
-        *reinterpret_cast<u16x8*>(vt + (16 * u + row) * VP + 32 * c + 8 * grp) = __builtin_bit_cast(u16x8, cr[u][c]);
-    wave_lds_sync();
-    const u16* trbase = vt + (4 * grp + (row >> 2)) * VP + 4 * (row & 3);
-#pragma unroll
-    for (int w = 0; w < DW; ++w) {
-      const u16x4 lo = lds_read_tr16(trbase + 16 * w);
-      const u16x4 hi = lds_read_tr16(trbase + 16 * VP + 16 * w);
-      const u16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      o[w] = mfma_16x16x32(__builtin_bit_cast(bf16x8, av), pop, o[w]);
-    }
-    wave_lds_sync();
-  };
-
-  for (int t0 = c0 + wave * kDecodeTileTokens; t0 < c1; t0 += kDecodeWaves * kDecodeTileTokens) {
-    bf16x8 cA[2][KC], rA[2][RCA];
-    s16x4 sA[2];
-    load_tile(cA, rA, sA, t0);
-    process_tile(cA, rA, sA, t0);
-  }
-
-  lsum = sum_xor16(lsum);
-  lsum = sum_xor32(lsum);
   __syncthreads();
-  float* mw = reinterpret_cast<float*>(smem);  // [waves][16]
-  float* lw = mw + kDecodeWaves * kHeadsPad;   // [waves][16]
-  float* ob = lw + kDecodeWaves * kHeadsPad;   // [16][R]
-  if (grp == 0) {
-    mw[wave * kHeadsPad + row] = m;
-    lw[wave * kHeadsPad + row] = lsum;
+  // first two slices in flight while the q_lat operands are loaded; copies stop
+  // at the chunk end
+  issue_slice<R, DR>(cst0[wave], rst0[wave], a, b, tw0, c1, ln);
+  issue_slice<R, DR>(cst1[wave], rst1[wave], a, b, tw0 + kStep, c1, ln);
+  // q_lat^T as the B operand: lane holds q_lat[head row][32k + 8grp ..+8] (hi and lo)
+  const u16* qlat = static_cast<const u16*>(a.q_lat) + (size_t)b * 2 * kHeadsPad * RW;
+  bf16x8 qhi[C::KC], qlo[C::KC], qr32[C::RC > 0 ? C::RC : 1], qr16 = {};
+#pragma unroll
+  for (int k = 0; k < C::KC; ++k) {
+    qhi[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qlat + ln.row * RW + 32 * k + 8 * ln.grp));
+    qlo[k] = __builtin_bit_cast(bf16x8,
+                                *reinterpret_cast<const u16x8*>(qlat + (kHeadsPad + ln.row) * RW + 32 * k + 8 * ln.grp));
+  }
+#pragma unroll
+  for (int k = 0; k < C::RC; ++k)
+    qr32[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qlat + ln.row * RW + R + 32 * k + 8 * ln.grp));
+  if constexpr (C::R16) {  // the last 16 rope dims in contraction lanes 0..15, zero above
+    const bf16x8 v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qlat + ln.row * RW + R + 32 * C::RC + 8 * ln.grp));
+    if (ln.grp < 2) qr16 = v;
+  }
+
+  // ---- stream the wave's slices through the ring
+  WaveState<R, DR> st;
+#pragma unroll
+  for (int w = 0; w < C::DW; ++w) st.o[w] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = kNegInf;
+  st.lsum = 0.f;
+  const float c = a.scale_log2e;
+  // step k: copy slice k+2 into stage (k+2) % 3, wait for slice k, consume stage k % 3
+  auto step = [&](int k, const u16* cs, const u16* rs, u16* cn, u16* rn) {
+    issue_slice<R, DR>(cn, rn, a, b, tw0 + (k + 2) * kStep, c1, ln);
+    wait_vmcnt<2 * C::kInstPerSlice>();
+    slice_step<R, DR>(st, cs, rs, qhi, qlo, qr32, qr16, tw0 + k * kStep, c1, c, ln);
+  };
+  for (int k = 0; k < n_steps; k += kStages) {
+    step(k, cst0[wave], rst0[wave], cst2[wave], rst2[wave]);
+    if (k + 1 < n_steps) step(k + 1, cst1[wave], rst1[wave], cst0[wave], rst0[wave]);
+    if (k + 2 < n_steps) step(k + 2, cst2[wave], rst2[wave], cst1[wave], rst1[wave]);
+  }
+  wait_vmem();  // the copies past the end (zeros) land before the stages are reused
+  st.lsum = sum_xor32(sum_xor16(st.lsum));
+
+  // ---- merge the four waves (LDS, reusing stages 0 and 1)
+  __syncthreads();
+  float* mw = reinterpret_cast<float*>(&cst0[0][0]);  // [waves][16]
+  float* lw = mw + kWaves * kHeadsPad;                // [waves][16]
+  float* olat = lw + kWaves * kHeadsPad;              // [16][R]
+  if (ln.grp == 0) {
+    mw[wave * kHeadsPad + ln.row] = st.m;
+    lw[wave * kHeadsPad + ln.row] = st.lsum;
   }
   __syncthreads();
   {
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, mw[w * kHeadsPad + row]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w * kHeadsPad + ln.row]);
     float Lt = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) Lt += rescale(mw[w * kHeadsPad + row], M) * lw[w * kHeadsPad + row];
-    const float f = rescale(m, M) / Lt;
+    for (int w = 0; w < kWaves; ++w) Lt += rescale(mw[w * kHeadsPad + ln.row], M) * lw[w * kHeadsPad + ln.row];
+    const float f = rescale(st.m, M) / Lt;
 #pragma unroll
-    for (int w = 0; w < DW; ++w) o[w] *= f;
+    for (int w = 0; w < C::DW; ++w) st.o[w] *= f;
   }
-  for (int w = 0; w < kDecodeWaves; ++w) {
+  for (int w = 0; w < kWaves; ++w) {
     if (wave == w) {
 #pragma unroll
-      for (int dw = 0; dw < DW; ++dw)
+      for (int dw = 0; dw < C::DW; ++dw)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float* dst = ob + row * R + 16 * dw + 4 * grp + i;
-          *dst = (w == 0 ? 0.f : *dst) + o[dw][i];
+          float* dst = olat + ln.row * R + 16 * dw + 4 * ln.grp + i;
+          *dst = (w == 0 ? 0.f : *dst) + st.o[dw][i];
         }
     }
     __syncthreads();
   }
+
+  // publish this chunk's normalised o_lat and log2-sum-exp (ordered for the merge
+  // kernel by the kernel boundary)
   const size_t row0 = (size_t)b * a.H;
-  for (int e = threadIdx.x; e < a.H * R; e += 256) {
-    const int hd = e / R, d = e - hd * R;
-    a.o_part[((row0 + hd) * a.n_splits + s) * R + d] = ob[hd * R + d];
+  for (int e = tid; e < a.H * (R / 4); e += kThreads) {
+    const int h = e / (R / 4), d4 = e - h * (R / 4);
+    *reinterpret_cast<float4*>(a.o_part + ((row0 + h) * a.n_splits + s) * R + 4 * d4) =
+        *reinterpret_cast<const float4*>(olat + h * R + 4 * d4);
   }
-  for (int hd = threadIdx.x; hd < a.H; hd += 256) {
+  for (int h = tid; h < a.H; h += kThreads) {
     float M = kNegInf;
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, mw[w * kHeadsPad + hd]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w * kHeadsPad + h]);
     float Lt = 0.f;
-    for (int w = 0; w < kDecodeWaves; ++w) Lt += rescale(mw[w * kHeadsPad + hd], M) * lw[w * kHeadsPad + hd];
-    a.lse[(row0 + hd) * a.n_splits + s] = M + __log2f(Lt);
+    for (int w = 0; w < kWaves; ++w) Lt += rescale(mw[w * kHeadsPad + h], M) * lw[w * kHeadsPad + h];
+    a.lse[(row0 + h) * a.n_splits + s] = M + __log2f(Lt);
   }
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup per (head, sequence): merge the chunks into o_lat[r] (LDS),
-// then out[b,h,i] = sum_j W_UV[h][i][j] o_lat[j].  The W_UV product runs one
-// output row per wave step: lanes split the r-long dot product (16-byte loads of
-// the row) and a wave reduction finishes it.
-__global__ __launch_bounds__(256) void mla_merge_wuv(MlaDecodeArgs a) {
-  __shared__ float olat[256];
-  __shared__ float wts[64];
-  __shared__ float wsum_s;
+// out[b,h] = W_UV[h] o_lat[b,h], with o_lat the log2-sum-exp merge of the
+// sequence's chunk partials.  Grid (H, B), 256 threads.  The W_UV[h] rows are
+// loaded first (16-byte loads, R/8 lanes per row) so they are in flight while
+// the partials are merged; a sequence with an empty cache gets zeros.
+template <int R>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void mla_merge_wuv(MlaDecodeArgs a) {
+  constexpr int OCT = R / 8;      // lanes per W_UV row
+  constexpr int RPI = 256 / OCT;  // rows per pass of the workgroup
+  constexpr int MAXP = (256 + RPI - 1) / RPI;  // passes for v_head_dim <= 256
+  __shared__ float olat[R];
   const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
   const int L = clamp_len(a.lens[b], a.T_max);
   const int n = (L + a.split - 1) / a.split;
-  const int R = a.r;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const size_t row = (size_t)b * a.H + h;
-  const float* lse = a.lse + row * a.n_splits;
-  const float* op = a.o_part + row * a.n_splits * R;
-  if (wave == 0) {
-    // chunk weights 2^(lse_s - max); n <= n_splits, read 64 at a time
-    float M = kNegInf;
-    for (int s = lane; s < n; s += 64) M = fmaxf(M, lse[s]);
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float ws = 0.f;
-    for (int s0 = 0; s0 < n; s0 += 64) {
-      const int s = s0 + lane;
-      const float w = s < n ? exp2_fast(lse[s] - M) : 0.f;
-      ws += w;
-      if (s0 == 0) wts[lane] = w;
+  const size_t oi0 = ((size_t)b * a.H + h) * a.dv;
+  if (n == 0) {
+    for (int i = tid; i < a.dv; i += 256) {
+      if (a.out_bf16) static_cast<u16*>(a.out)[oi0 + i] = 0;
+      else static_cast<float*>(a.out)[oi0 + i] = 0.f;
     }
-    for (int off = 32; off >= 1; off >>= 1) ws += __shfl_xor(ws, off);
-    if (lane == 0) wsum_s = ws;
+    return;
   }
-  __syncthreads();
-  const float inv = n > 0 ? 1.f / wsum_s : 0.f;
-  for (int j = tid; j < R; j += 256) {
-    float acc = 0.f;
-    for (int s = 0; s < n; ++s) {
-      // weights of chunks >= 64 are recomputed (only for very long caches)
-      const float w = s < 64 ? wts[s] : 0.f;
-      acc = fmaf(w, op[(size_t)s * R + j], acc);
-    }
-    olat[j] = acc * inv;
-  }
-  if (n > 64) {
-    // rare: more than 64 chunks; add the rest with recomputed weights
-    __syncthreads();
-    float M = kNegInf;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, lse[s]);
-    for (int j = tid; j < R; j += 256) {
-      float acc = 0.f;
-      for (int s = 64; s < n; ++s) acc = fmaf(exp2_fast(lse[s] - M), op[(size_t)s * R + j], acc);
-      olat[j] += acc * inv;
-    }
-  }
-  __syncthreads();
-  const u16* wv = static_cast<const u16*>(a.w_uv) + (size_t)h * a.dv * R;
-  for (int i = wave; i < a.dv; i += 4) {
-    const u16* wrow = wv + (size_t)i * R;
-    float acc = 0.f;
-    for (int j = 8 * lane; j < R; j += 512) {
-      const u16x8 w8 = *reinterpret_cast<const u16x8*>(wrow + j);
+  const int oct = tid % OCT, sub = tid / OCT;
+  const u16* wv = static_cast<const u16*>(a.w_uv) + (size_t)h * a.dv * R + 8 * oct;
+  const int passes = (a.dv + RPI - 1) / RPI;
+  // unconditional (row-clamped) loads: a branch per load would wait for each one
+  u16x8 w8[MAXP];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc = fmaf(bf16_to_f32(w8[k]), olat[j + k], acc);
+  for (int p = 0; p < MAXP; ++p) w8[p] = *reinterpret_cast<const u16x8*>(wv + (size_t)min(p * RPI + sub, a.dv - 1) * R);
+  // merge: thread j < R owns column j; eight chunks in flight, running max
+  const size_t row = (size_t)b * a.H + h;
+  for (int j = tid; j < R; j += 256) {
+    const float* lse = a.lse + row * a.n_splits;
+    const float* op = a.o_part + row * a.n_splits * R + j;
+    float M = kNegInf, S = 0.f, acc = 0.f;
+    for (int k0 = 0; k0 < n; k0 += 8) {
+      float lv[8], ov[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = min(k0 + u, n - 1);
+        lv[u] = lse[k];
+        ov[u] = op[(size_t)k * R];
+      }
+      // chunks past the end (loaded clamped) get weight 2^-inf = 0; entry u = 0
+      // is always a real chunk, so M is finite before any of them
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (k0 + u >= n) lv[u] = kNegInf;
+        const float Mn = fmaxf(M, lv[u]);
+        const float f = rescale(M, Mn), w = exp2_fast(lv[u] - Mn);
+        S = S * f + w;
+        acc = acc * f + w * ov[u];
+        M = Mn;
+      }
     }
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) {
-      const size_t oi = row * a.dv + i;
-      if (a.out_bf16) static_cast<__bf16*>(a.out)[oi] = (__bf16)acc;
-      else static_cast<float*>(a.out)[oi] = acc;
+    olat[j] = acc / S;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    if (p >= passes) break;
+    const int i = p * RPI + sub;
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(bf16_to_f32(w8[p][e]), olat[8 * oct + e], acc);
+#pragma unroll
+    for (int off = OCT / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (oct == 0 && i < a.dv) {
+      if (a.out_bf16) static_cast<__bf16*>(a.out)[oi0 + i] = (__bf16)acc;
+      else static_cast<float*>(a.out)[oi0 + i] = acc;
     }
   }
 }
 
+template <int R, int DR>
+hipError_t launch_rd(const MlaDecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((mla_absorb<R, DR>), dim3(kHeadsPad, a.B), dim3(256), 0, st, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((mla_decode_fused<R, DR>), dim3(a.n_splits, a.B), dim3(kThreads), 0, st, a);
+  const hipError_t e2 = hipGetLastError();
+  if (e2 != hipSuccess) return e2;
+  hipLaunchKernelGGL((mla_merge_wuv<R>), dim3(a.H, a.B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int R>
-hipError_t launch_partial(const MlaDecodeArgs& a, dim3 grid, hipStream_t st) {
+hipError_t launch_r(const MlaDecodeArgs& a, hipStream_t st) {
   switch (a.dR) {
-    case 16: hipLaunchKernelGGL((mla_decode_partial<R, 16>), grid, dim3(256), 0, st, a); break;
-    case 32: hipLaunchKernelGGL((mla_decode_partial<R, 32>), grid, dim3(256), 0, st, a); break;
-    case 48: hipLaunchKernelGGL((mla_decode_partial<R, 48>), grid, dim3(256), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((mla_decode_partial<R, 64>), grid, dim3(256), 0, st, a); break;
+    case 16: return launch_rd<R, 16>(a, st);
+    case 32: return launch_rd<R, 32>(a, st);
+    case 48: return launch_rd<R, 48>(a, st);
+    case 64: return launch_rd<R, 64>(a, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -396,17 +537,8 @@ bool mla_decode_supported(int H, int r, int dR) {
 
 hipError_t launch_mla_decode(const MlaDecodeArgs& a, hipStream_t st) {
   if (!mla_decode_supported(a.H, a.r, a.dR)) return hipErrorInvalidValue;
-  // w_uv rows are read 16 bytes at a time
-  if (a.r % 8 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mla_absorb, dim3(kHeadsPad, a.B), dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 grid(a.n_splits, a.B);
-  e = a.r == 64 ? launch_partial<64>(a, grid, st) : a.r == 128 ? launch_partial<128>(a, grid, st)
-                                                               : launch_partial<256>(a, grid, st);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_merge_wuv, dim3(a.H, a.B), dim3(256), 0, st, a);
-  return hipGetLastError();
+  if (a.split % kStep != 0) return hipErrorInvalidValue;
+  return a.r == 64 ? launch_r<64>(a, st) : a.r == 128 ? launch_r<128>(a, st) : launch_r<256>(a, st);
 }
 
 }  // namespace attn

@@ -50,6 +50,12 @@ def test_workspace_sizes():
     assert attn.attn_decode_gqa_workspace_bytes(0, 32, 8, 128, 8192, 0) == 0
     assert attn.attn_decode_gqa_workspace_bytes(1, 32, 8, 128, 8192, 100) == 0  # split not a multiple of 64
     assert attn.attn_decode_mla_workspace_bytes(64, 8, 128, 48, 4096, 0) > 0
+    # MLA with fixed chunks of 512: q_lat [B, 2, 16, r + dR] bf16, partials
+    # [B*H*n_splits, r] fp32, lse [B*H*n_splits] fp32
+    B, H, r, dR, T = 64, 8, 128, 48, 4096
+    rows = B * H * (T // 512)
+    assert attn.attn_decode_mla_workspace_bytes(B, H, r, dR, T, 512) == (
+        al(B * 2 * 16 * (r + dR) * 2) + al(rows * r * 4) + al(rows * 4))
     assert attn.attn_decode_mla_supported(8, 128, 48)
     assert not attn.attn_decode_mla_supported(8, 100, 48)
     assert not attn.attn_decode_mla_supported(8, 128, 48, torch.float32)
