@@ -48,6 +48,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kSlice = 16;               // tokens per wave slice
 constexpr int kStep = kSlice * kWaves;   // tokens per workgroup step
 constexpr int kStages = 3;
+constexpr float kRescaleSlack = 8.f;     // log2 units the reference max may trail the true max
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -175,7 +176,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int R, int DR>
 struct WaveState {
   f32x4 o[R / 16];  // O^T[16w + 4grp + i][head row]
-  float m, lsum;    // running max (scaled, log2) and this lane's part of the row sum
+  float m, lsum;    // reference max (scaled, log2) and this lane's part of the row sum
 };
 
 // ---------------------------------------------------------------------------
@@ -184,15 +185,34 @@ struct WaveState {
 // h in [H, 16) are zero.  Grid (16, B), 256 threads, one workgroup per (head,
 // sequence): thread t owns latent columns 8(t % (R/8)) .. +8 (16-byte loads of
 // W_UK rows, which stay in L2 across the sequences) and every P-th row (P =
-// 2048 / R); all of a thread's loads are issued before the first use, and the P
-// partial sums meet in LDS.
+// 2048 / R); a thread's loads are issued together before the first use, and
+// the P partial sums meet in LDS.
+// Rows [i0, i0 + U*P) of this thread's part: U loads of 16 bytes (row-clamped,
+// so there is no branch between them) issued before any use.
+template <int R, int U, int P>
+__device__ __forceinline__ void absorb_rows(float (&acc)[8], const u16* wk, const u16* qn, int i0, int dn) {
+  u16x8 wv[U];
+  u16 qv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = min(i0 + u * P, dn - 1);
+    wv[u] = *reinterpret_cast<const u16x8*>(wk + (size_t)i * R);
+    qv[u] = qn[i];
+  }
+  asm volatile("" ::: "memory");  // issue the whole batch before the first use
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float q = i0 + u * P < dn ? bf16_to_f32(qv[u]) : 0.f;  // clamped rows count 0
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(bf16_to_f32(wv[u][e]), q, acc[e]);
+  }
+}
+
 template <int R, int DR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void mla_absorb(MlaDecodeArgs a) {
   constexpr int RW = R + DR;
-  constexpr int OCT = R / 8;         // column octets
-  constexpr int P = 256 / OCT;       // row parts
-  constexpr int MAXI = (256 + P - 1) / P;  // rows per part for nope_head_dim <= 256
-  constexpr int U = MAXI < 16 ? MAXI : 16;
+  constexpr int OCT = R / 8;    // column octets
+  constexpr int P = 256 / OCT;  // row parts
   __shared__ float red[P][R];
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
@@ -205,26 +225,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
   const u16* wk = static_cast<const u16*>(a.w_uk) + (size_t)h * a.dn * R + 8 * oct;
   const u16* qn = static_cast<const u16*>(a.q_nope) + ((size_t)b * a.H + h) * a.dn;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int i0 = part; i0 < a.dn; i0 += U * P) {
-    u16x8 wv[U];
-    u16 qv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = min(i0 + u * P, a.dn - 1);
-      wv[u] = *reinterpret_cast<const u16x8*>(wk + (size_t)i * R);
-      qv[u] = qn[i];
-    }
-    asm volatile("" ::: "memory");  // issue the whole batch before the first use
-    // rows past the end were loaded clamped; they count with q = 0 (no branch,
-    // so every load above stays in flight together)
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float q = i0 + u * P < a.dn ? bf16_to_f32(qv[u]) : 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(bf16_to_f32(wv[u][e]), q, acc[e]);
-    }
-
-  }
+  const int rows_per_part = (a.dn + P - 1) / P;  // uniform: pick the batch that covers it
+  if (rows_per_part <= 2) absorb_rows<R, 2, P>(acc, wk, qn, part, a.dn);
+  else if (rows_per_part <= 4) absorb_rows<R, 4, P>(acc, wk, qn, part, a.dn);
+  else if (rows_per_part <= 8) absorb_rows<R, 8, P>(acc, wk, qn, part, a.dn);
+  else
+    for (int i0 = part; i0 < a.dn; i0 += 16 * P) absorb_rows<R, 16, P>(acc, wk, qn, i0, a.dn);
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[part][8 * oct + e] = acc[e];
   __syncthreads();
@@ -278,10 +284,18 @@ __device__ __forceinline__ void slice_step(WaveState<R, DR>& st, const u16* cs, 
     mt = fmaxf(mt, s[i]);
   }
   mt = max_xor32(max_xor16(mt));
-  const float mn = fmaxf(st.m, mt);
-  const float alpha = rescale(st.m, mn);
-  const float ms = mn == kNegInf ? 0.f : mn;  // a fully masked slice so far: p = 2^-inf = 0
-  st.m = mn;
+  // The reference max only moves (and O, l are rescaled) when the slice's max
+  // exceeds it by more than 2^8: probabilities stay below 256, well inside bf16
+  // and fp32, and most slices skip the rescale.
+  if (__builtin_amdgcn_ballot_w64(mt > st.m + kRescaleSlack) != 0) {
+    const float mn = fmaxf(st.m, mt);
+    const float alpha = rescale(st.m, mn);
+    st.m = mn;
+    st.lsum *= alpha;
+#pragma unroll
+    for (int w = 0; w < C::DW; ++w) st.o[w] *= alpha;
+  }
+  const float ms = st.m == kNegInf ? 0.f : st.m;  // nothing visible yet: p = 2^-inf = 0
   s16x4 pop;
   float ps = 0.f;
 #pragma unroll
@@ -290,9 +304,7 @@ __device__ __forceinline__ void slice_step(WaveState<R, DR>& st, const u16* cs, 
     pop[i] = __builtin_bit_cast(short, pb);
     ps += (float)pb;  // the rounded probabilities the product uses
   }
-  st.lsum = st.lsum * alpha + ps;
-#pragma unroll
-  for (int w = 0; w < C::DW; ++w) st.o[w] *= alpha;
+  st.lsum += ps;
   // O^T[16w..16w+15][heads] += V^T[dims][16 tokens] P^T[tokens][heads]
 #pragma unroll
   for (int w = 0; w < C::DW; ++w) st.o[w] = mfma_16x16x16(lds_read_tr16(cs + (ln.v_off ^ (16 * w))), pop, st.o[w]);
@@ -304,13 +316,14 @@ __global__ __launch_bounds__(kThreads) void mla_decode_fused(MlaDecodeArgs a) {
   constexpr int RW = C::RW;
   // three ring stages per wave, each a distinct LDS variable so the compiler can
   // tell the copies in flight from the reads of the resident stage
-  __shared__ __attribute__((aligned(1024))) u16 cst0[kWaves][C::kC];
-  __shared__ __attribute__((aligned(1024))) u16 cst1[kWaves][C::kC];
-  __shared__ __attribute__((aligned(1024))) u16 cst2[kWaves][C::kC];
-  __shared__ __attribute__((aligned(1024))) u16 rst0[kWaves][C::kR];
-  __shared__ __attribute__((aligned(1024))) u16 rst1[kWaves][C::kR];
-  __shared__ __attribute__((aligned(1024))) u16 rst2[kWaves][C::kR];
-  static_assert((2 * kWaves * kHeadsPad + kHeadsPad * R) * 4 <= (int)sizeof(cst0),
+  // per wave and stage: the latent slice and the rope slice
+  __shared__ __attribute__((aligned(1024))) u16 stg0[kWaves][C::kC];
+  __shared__ __attribute__((aligned(1024))) u16 stg1[kWaves][C::kC];
+  __shared__ __attribute__((aligned(1024))) u16 stg2[kWaves][C::kC];
+  __shared__ __attribute__((aligned(1024))) u16 rop0[kWaves][C::kR];
+  __shared__ __attribute__((aligned(1024))) u16 rop1[kWaves][C::kR];
+  __shared__ __attribute__((aligned(1024))) u16 rop2[kWaves][C::kR];
+  static_assert((2 * kWaves * kHeadsPad + kHeadsPad * R) * 4 <= (int)sizeof(stg0),
                 "merge scratch must fit in stage 0");
 
   const int s = blockIdx.x, b = blockIdx.y;
@@ -329,18 +342,14 @@ __global__ __launch_bounds__(kThreads) void mla_decode_fused(MlaDecodeArgs a) {
   // the transposed V product, and uninitialised LDS could hold NaN patterns.
   {
     const u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-    u16* const bufs[6] = {&cst0[0][0], &cst1[0][0], &cst2[0][0], &rst0[0][0], &rst1[0][0], &rst2[0][0]};
-    const int lens_[6] = {kWaves * C::kC, kWaves * C::kC, kWaves * C::kC, kWaves * C::kR, kWaves * C::kR,
-                          kWaves * C::kR};
+    u16* const bufs[6] = {&stg0[0][0], &stg1[0][0], &stg2[0][0], &rop0[0][0], &rop1[0][0], &rop2[0][0]};
 #pragma unroll
     for (int k = 0; k < 6; ++k)
-      for (int e = 8 * tid; e < lens_[k]; e += 8 * kThreads) *reinterpret_cast<u16x8*>(bufs[k] + e) = z;
+      for (int e = 8 * tid; e < kWaves * (k < 3 ? C::kC : C::kR); e += 8 * kThreads)
+        *reinterpret_cast<u16x8*>(bufs[k] + e) = z;
   }
   __syncthreads();
-  // first two slices in flight while the q_lat operands are loaded; copies stop
-  // at the chunk end
-  issue_slice<R, DR>(cst0[wave], rst0[wave], a, b, tw0, c1, ln);
-  issue_slice<R, DR>(cst1[wave], rst1[wave], a, b, tw0 + kStep, c1, ln);
+  // q_lat operands first, then the first two slices (copies stop at the chunk end)
   // q_lat^T as the B operand: lane holds q_lat[head row][32k + 8grp ..+8] (hi and lo)
   const u16* qlat = static_cast<const u16*>(a.q_lat) + (size_t)b * 2 * kHeadsPad * RW;
   bf16x8 qhi[C::KC], qlo[C::KC], qr32[C::RC > 0 ? C::RC : 1], qr16 = {};
@@ -358,6 +367,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode_fused(MlaDecodeArgs a) {
     if (ln.grp < 2) qr16 = v;
   }
 
+  wait_vmem();  // the operands are in registers before the first copy
+
   // ---- stream the wave's slices through the ring
   WaveState<R, DR> st;
 #pragma unroll
@@ -365,23 +376,29 @@ __global__ __launch_bounds__(kThreads) void mla_decode_fused(MlaDecodeArgs a) {
   st.m = kNegInf;
   st.lsum = 0.f;
   const float c = a.scale_log2e;
-  // step k: copy slice k+2 into stage (k+2) % 3, wait for slice k, consume stage k % 3
+  // Step k: copy slice k+2 into stage (k+2) % 3, wait for slice k, consume stage
+  // k % 3.  The loop starts at k = -2 (copies only), so every copy comes from
+  // the same three places in the loop body: the compiler then tracks which
+  // stage each copy in flight belongs to across the back edge and adds no
+  // waits beyond this one.  Copies of slices past the chunk read nothing.
   auto step = [&](int k, const u16* cs, const u16* rs, u16* cn, u16* rn) {
     issue_slice<R, DR>(cn, rn, a, b, tw0 + (k + 2) * kStep, c1, ln);
-    wait_vmcnt<2 * C::kInstPerSlice>();
-    slice_step<R, DR>(st, cs, rs, qhi, qlo, qr32, qr16, tw0 + k * kStep, c1, c, ln);
+    if (k >= 0 && k < n_steps) {
+      wait_vmcnt<2 * C::kInstPerSlice>();
+      slice_step<R, DR>(st, cs, rs, qhi, qlo, qr32, qr16, tw0 + k * kStep, c1, c, ln);
+    }
   };
-  for (int k = 0; k < n_steps; k += kStages) {
-    step(k, cst0[wave], rst0[wave], cst2[wave], rst2[wave]);
-    if (k + 1 < n_steps) step(k + 1, cst1[wave], rst1[wave], cst0[wave], rst0[wave]);
-    if (k + 2 < n_steps) step(k + 2, cst2[wave], rst2[wave], cst1[wave], rst1[wave]);
+  for (int k = -2; k < n_steps; k += kStages) {  // k = -2, 1, 4, ... : stage (k+2) % 3 = 0
+    step(k, stg1[wave], rop1[wave], stg0[wave], rop0[wave]);
+    step(k + 1, stg2[wave], rop2[wave], stg1[wave], rop1[wave]);
+    step(k + 2, stg0[wave], rop0[wave], stg2[wave], rop2[wave]);
   }
   wait_vmem();  // the copies past the end (zeros) land before the stages are reused
   st.lsum = sum_xor32(sum_xor16(st.lsum));
 
-  // ---- merge the four waves (LDS, reusing stages 0 and 1)
+  // ---- merge the four waves (LDS, reusing stage 0)
   __syncthreads();
-  float* mw = reinterpret_cast<float*>(&cst0[0][0]);  // [waves][16]
+  float* mw = reinterpret_cast<float*>(&stg0[0][0]);  // [waves][16]
   float* lw = mw + kWaves * kHeadsPad;                // [waves][16]
   float* olat = lw + kWaves * kHeadsPad;              // [16][R]
   if (ln.grp == 0) {
@@ -432,15 +449,16 @@ __global__ __launch_bounds__(kThreads) void mla_decode_fused(MlaDecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // out[b,h] = W_UV[h] o_lat[b,h], with o_lat the log2-sum-exp merge of the
-// sequence's chunk partials.  Grid (H, B), 256 threads.  The W_UV[h] rows are
-// loaded first (16-byte loads, R/8 lanes per row) so they are in flight while
-// the partials are merged; a sequence with an empty cache gets zeros.
+// sequence's chunk partials.  Grid (H, B), 256 threads.  Thread i < v_head_dim
+// owns output row i: its W_UV row (R/8 loads of 16 bytes) is requested first,
+// so it is in flight while threads j < R merge latent column j; the dot product
+// then reads o_lat from LDS (the same address in every lane).  A sequence with
+// an empty cache gets zeros.
 template <int R>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void mla_merge_wuv(MlaDecodeArgs a) {
-  constexpr int OCT = R / 8;      // lanes per W_UV row
-  constexpr int RPI = 256 / OCT;  // rows per pass of the workgroup
-  constexpr int MAXP = (256 + RPI - 1) / RPI;  // passes for v_head_dim <= 256
-  __shared__ float olat[R];
+  constexpr int OCT = R / 8;
+  constexpr int U = OCT < 16 ? OCT : 16;  // row loads in flight per batch
+  __shared__ __attribute__((aligned(16))) float olat[R];
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
   const int L = clamp_len(a.lens[b], a.T_max);
@@ -453,13 +471,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
     }
     return;
   }
-  const int oct = tid % OCT, sub = tid / OCT;
-  const u16* wv = static_cast<const u16*>(a.w_uv) + (size_t)h * a.dv * R + 8 * oct;
-  const int passes = (a.dv + RPI - 1) / RPI;
-  // unconditional (row-clamped) loads: a branch per load would wait for each one
-  u16x8 w8[MAXP];
+  const u16* wrow = static_cast<const u16*>(a.w_uv) + ((size_t)h * a.dv + min(tid, a.dv - 1)) * R;
+  u16x8 w8[U];
 #pragma unroll
-  for (int p = 0; p < MAXP; ++p) w8[p] = *reinterpret_cast<const u16x8*>(wv + (size_t)min(p * RPI + sub, a.dv - 1) * R);
+  for (int c = 0; c < U; ++c) w8[c] = *reinterpret_cast<const u16x8*>(wrow + 8 * c);
   // merge: thread j < R owns column j; eight chunks in flight, running max
   const size_t row = (size_t)b * a.H + h;
   for (int j = tid; j < R; j += 256) {
@@ -489,19 +504,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
     olat[j] = acc / S;
   }
   __syncthreads();
+  float acc = 0.f;
 #pragma unroll
-  for (int p = 0; p < MAXP; ++p) {
-    if (p >= passes) break;
-    const int i = p * RPI + sub;
-    float acc = 0.f;
+  for (int c = 0; c < U; ++c) {
+    const float4 o0 = *reinterpret_cast<const float4*>(olat + 8 * c);
+    const float4 o1 = *reinterpret_cast<const float4*>(olat + 8 * c + 4);
+    acc = fmaf(bf16_to_f32(w8[c][0]), o0.x, acc);
+    acc = fmaf(bf16_to_f32(w8[c][1]), o0.y, acc);
+    acc = fmaf(bf16_to_f32(w8[c][2]), o0.z, acc);
+    acc = fmaf(bf16_to_f32(w8[c][3]), o0.w, acc);
+    acc = fmaf(bf16_to_f32(w8[c][4]), o1.x, acc);
+    acc = fmaf(bf16_to_f32(w8[c][5]), o1.y, acc);
+    acc = fmaf(bf16_to_f32(w8[c][6]), o1.z, acc);
+    acc = fmaf(bf16_to_f32(w8[c][7]), o1.w, acc);
+  }
+  for (int c0 = U; c0 < OCT; c0 += U) {  // R = 256: the rest of the row
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(bf16_to_f32(w8[p][e]), olat[8 * oct + e], acc);
+    for (int c = 0; c < U; ++c) w8[c] = *reinterpret_cast<const u16x8*>(wrow + 8 * (c0 + c));
 #pragma unroll
-    for (int off = OCT / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (oct == 0 && i < a.dv) {
-      if (a.out_bf16) static_cast<__bf16*>(a.out)[oi0 + i] = (__bf16)acc;
-      else static_cast<float*>(a.out)[oi0 + i] = acc;
-    }
+    for (int c = 0; c < U; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf(bf16_to_f32(w8[c][e]), olat[8 * (c0 + c) + e], acc);
+  }
+  if (tid < a.dv) {
+    if (a.out_bf16) static_cast<__bf16*>(a.out)[oi0 + tid] = (__bf16)acc;
+    else static_cast<float*>(a.out)[oi0 + tid] = acc;
   }
 }
 
