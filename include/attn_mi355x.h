@@ -86,23 +86,24 @@ const char* attn_last_error(void);
  * Hq/Hkv <= 64; in_dtype ATTN_F32 with head_dim in {64, 96, 128} and
  * Hq/Hkv <= 16.  out_dtype ATTN_F32 or ATTN_BF16.
  *
- * Work is cut into pieces of cached positions of one (sequence, KV head); a
- * workgroup reads a piece's K/V rows once for all Hq/Hkv query heads of the
- * group, and pieces of one sequence are merged by their log-sum-exp in the same
- * kernel.  split_tokens = 0 lets the library plan on the device from cache_lens
- * (equal work per workgroup; batches up to 1024 sequences, else fixed chunks of
- * its choice); otherwise pieces are fixed chunks of split_tokens positions, a
- * multiple of 64 in [64, 65536].  The result does not depend on the split
- * beyond fp32 rounding.
+ * Work is cut into units: chunks of split_tokens cached positions of one
+ * (sequence, KV head).  A workgroup reads a unit's K/V rows once for all Hq/Hkv
+ * query heads of the group.  Sequences of one chunk are written directly; the
+ * chunks of longer ones are combined by their log-sum-exp in a second, small
+ * kernel on the same stream.  Batches of up to 1024 sequences run the units
+ * through a device-wide queue taken by the resident workgroups (planned on the
+ * device from cache_lens, so the host never reads the lengths); larger batches
+ * launch one workgroup per unit.  split_tokens = 0 lets the library choose the
+ * chunk from the sizes; otherwise it is a multiple of 64 in [64, 65536].  The
+ * result does not depend on the chunk beyond fp32 rounding.
  *
  * workspace: device memory of at least attn_decode_gqa_workspace_bytes(...)
- * bytes for the same arguments, 256-byte aligned.  Its first B*Hkv int32 are
- * completion counters: they must be zero before the first call that uses the
+ * bytes for the same arguments, 256-byte aligned.  Its first 4 bytes are the
+ * work-queue counter: they must be zero before the first call that uses the
  * workspace (e.g. allocate it zero-filled), and every call leaves them zero, so
- * later calls with the same B, Hq, Hkv, head_dim, T_max and split_tokens may
- * reuse it as is.  Zero it again before using it for other sizes (their
- * counters lie where these sizes keep partial results).  The rest needs no
- * initialisation.  One workspace per concurrent call.
+ * any later call whose size needs fit may reuse it as is.  The rest needs no
+ * initialisation.  One workspace per concurrent call: calls that overlap in
+ * time on one workspace race.
  */
 size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int head_dim, int T_max,
                                        int split_tokens);

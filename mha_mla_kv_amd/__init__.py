@@ -119,16 +119,15 @@ def _stream(device) -> ctypes.c_void_p:
 _ws_cache: dict = {}
 
 
-def _workspace(nbytes: int, device, shape_key: tuple) -> torch.Tensor:
-    """A zero-filled workspace cached per (device, current stream, call shape).
+def _workspace(nbytes: int, device, kind: str) -> torch.Tensor:
+    """A zero-filled workspace cached per (device, current stream, entry point), grown as needed.
 
-    The decode kernels leave their completion counters zero after every call, so a cached
-    workspace stays valid for later calls of the same shape.  A workspace is never shared
-    between shapes: the counter region of one shape overlaps the partial results of another.
-    Calls on one stream are ordered, so they never use it concurrently."""
+    The GQA decode leaves its queue counter (the first 4 bytes) zero after every call and
+    the MLA decode needs no initialisation, so a cached workspace stays valid for later
+    calls of any shape.  Calls on one stream are ordered, so they never use it concurrently."""
     dev = torch.device(device)
     idx = dev.index if dev.index is not None else torch.cuda.current_device()
-    key = (idx, torch.cuda.current_stream(idx).cuda_stream) + tuple(shape_key)
+    key = (idx, torch.cuda.current_stream(idx).cuda_stream, kind)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=torch.device("cuda", idx))
@@ -147,7 +146,7 @@ def attn_decode_gqa(q, k_cache, v_cache, cache_lens, out=None, softmax_scale: fl
 
     q [B,Hq,D], k_cache/v_cache [B,T_max,Hkv,D] (same dtype, fp32 or bf16), cache_lens [B] int32,
     out [B,Hq,D] of out_dtype.  A caller-provided workspace (uint8) must have been zero-filled
-    before its first use with this shape (its completion counters); calls leave it so.
+    before its first use (its first 4 bytes are the work-queue counter); calls leave it so.
     Returns out."""
     _check(q, "q")
     B, Hq, D = q.shape
@@ -162,7 +161,7 @@ def attn_decode_gqa(q, k_cache, v_cache, cache_lens, out=None, softmax_scale: fl
     _check(out, "out", shape=(B, Hq, D))
     need = attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T_max, split_tokens)
     if workspace is None:
-        workspace = _workspace(need, q.device, ("gqa", B, Hq, Hkv, D, T_max, int(split_tokens)))
+        workspace = _workspace(need, q.device, "gqa")
     _check(workspace, "workspace", dtype=torch.uint8)
     st = lib().attn_decode_gqa(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens), _ptr(out), B, Hq,
                                Hkv, D, T_max, float(softmax_scale), _dt(q), _dt(out), int(split_tokens),
@@ -234,7 +233,7 @@ def attn_decode_mla_absorbed(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, cache_len
     _check(out, "out", shape=(B, H, dv))
     need = attn_decode_mla_workspace_bytes(B, H, r, dR, T_max, split_tokens)
     if workspace is None:
-        workspace = _workspace(need, q_nope.device, ("mla", B, H, r, dR, T_max, int(split_tokens)))
+        workspace = _workspace(need, q_nope.device, "mla")
     _check(workspace, "workspace", dtype=torch.uint8)
     st = lib().attn_decode_mla_absorbed(_ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(c_kv),
                                         _ptr(k_rope), _ptr(cache_lens), _ptr(out), B, H, dn, dR, dv, r, T_max,

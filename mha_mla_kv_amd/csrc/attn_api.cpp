@@ -47,62 +47,44 @@ int pow2_floor(long long x) {
   return p;
 }
 
-// Tokens per decode chunk.  Aim for at least ~8 workgroups per compute unit
-// (256 CUs) when every sequence is full, but keep a chunk long enough that the
-// fp32 partial results (n_rep * D * 4 bytes written and read back per chunk)
-// stay small next to the chunk's cache bytes, and at least one 32-token tile
-// per wave.
-int choose_split(int B, int Hkv, int n_rep, int T_max) {
-  const long long target_wgs = 2048;
-  long long per_pair = (long long)T_max;
-  long long pairs = (long long)B * Hkv;
-  long long want = pairs * per_pair / target_wgs;
-  int split = pow2_floor(want < 1 ? 1 : want);
-  int lo = 128;
+// Positions per decode work unit when the caller leaves it to the library.
+// Enough units that every resident workgroup takes several (the queue then
+// evens out compute units that stream at different rates) when every sequence
+// is full, but long enough that the fp32 partial of a unit (n_rep * D * 4 bytes
+// written and read back) stays small next to its cache bytes (chunk * D * 4).
+int choose_chunk(int B, int Hkv, int n_rep, int T_max) {
+  const long long target_units = 4096;
+  int lo = 64;
+  if (n_rep >= 8) lo = 128;
   if (n_rep >= 16) lo = 256;
   if (n_rep >= 32) lo = 512;
-  if (split < lo) split = lo;
-  if (split > 2048) split = 2048;
-  return split;
+  int chunk = 1024;
+  while (chunk > lo && (long long)B * Hkv * ((T_max + chunk - 1) / chunk) < target_units) chunk /= 2;
+  return chunk;
 }
 
 bool valid_split(int split) { return split == 0 || (split >= 64 && split <= 65536 && split % 64 == 0); }
 
-// Decode schedule and workspace layout.  split_tokens > 0 selects fixed chunks;
-// 0 selects the balanced schedule (equal rows per workgroup, planned on the
-// device from cache_lens) when the batch fits its limits, else library-chosen
-// fixed chunks.  Workspace: [counters B*Hkv int32][lse slots*n_rep][o_part
-// slots*n_rep*D], each piece 256-byte aligned.
-constexpr int kBalancedMaxWgs = 2048;       // slot bound of the balanced schedule
-constexpr unsigned long long kBalancedMaxRows = 1ull << 31;
-
+// Decode schedule and workspace layout.  Work units are chunks of `chunk`
+// positions of one (sequence, KV head): split_tokens, or chosen by the library
+// when 0.  Workspace: [queue counter, 256 bytes][lse slots*n_rep][o_part
+// slots*n_rep*D] with slots = B*Hkv*n_chunks (none when every sequence is one
+// chunk), each piece 256-byte aligned.
 struct GqaLayout {
-  bool balanced;
-  int split, n_splits;
+  int chunk, n_chunks;
+  bool queue;  // units taken from the device-wide queue (else one workgroup per unit)
   long long slots;
-  size_t cnt_off, lse_off, o_off, total;
+  size_t lse_off, o_off, total;
 };
-
-bool use_balanced(int B, int Hkv, int T_max, int split_tokens) {
-  return split_tokens == 0 && B <= attn::kBalancedMaxB &&
-         (unsigned long long)B * (unsigned long long)Hkv * (unsigned long long)T_max < kBalancedMaxRows;
-}
 
 GqaLayout gqa_layout(int B, int Hq, int Hkv, int D, int T_max, int split_tokens) {
   GqaLayout l;
   const int n_rep = Hq / (Hkv > 0 ? Hkv : 1);
-  l.balanced = use_balanced(B, Hkv, T_max, split_tokens);
-  if (l.balanced) {
-    l.split = 0;
-    l.n_splits = 0;
-    l.slots = (long long)kBalancedMaxWgs + (long long)B * Hkv;
-  } else {
-    l.split = split_tokens ? split_tokens : choose_split(B, Hkv, n_rep, T_max);
-    l.n_splits = (T_max + l.split - 1) / l.split;
-    l.slots = (long long)B * Hkv * l.n_splits;
-  }
-  l.cnt_off = 0;
-  l.lse_off = align_up((size_t)B * Hkv * sizeof(int));
+  l.chunk = split_tokens ? split_tokens : choose_chunk(B, Hkv, n_rep, T_max);
+  l.n_chunks = (int)(((long long)T_max + l.chunk - 1) / l.chunk);
+  l.queue = B <= attn::kQueueMaxB && l.n_chunks >= 2;
+  l.slots = l.n_chunks >= 2 ? (long long)B * Hkv * l.n_chunks : 0;
+  l.lse_off = 256;
   l.o_off = l.lse_off + align_up((size_t)l.slots * n_rep * sizeof(float));
   l.total = l.o_off + align_up((size_t)l.slots * n_rep * D * sizeof(float));
   return l;
@@ -212,8 +194,8 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_gqa: q, caches and out must be 16-byte aligned");
   const GqaLayout lay = gqa_layout(B, Hq, Hkv, head_dim, T_max, split_tokens);
-  if (!lay.balanced && lay.n_splits > kMaxGridYZ)
-    return fail(ATTN_ERR_SHAPE, "attn_decode_gqa: ceil(T_max/split_tokens)=%d chunks exceed %d", lay.n_splits,
+  if (!lay.queue && lay.n_chunks > kMaxGridYZ)
+    return fail(ATTN_ERR_SHAPE, "attn_decode_gqa: ceil(T_max/split_tokens)=%d chunks exceed %d", lay.n_chunks,
                 kMaxGridYZ);
   if (lay.slots >= (1ll << 31) / (n_rep > 0 ? n_rep : 1))
     return fail(ATTN_ERR_SHAPE, "attn_decode_gqa: too many chunks (B*Hkv*ceil(T_max/split_tokens) too large)");
@@ -230,7 +212,7 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
   a.lens = cache_lens;
   a.out = out;
   char* ws = static_cast<char*>(workspace);
-  a.counters = reinterpret_cast<int*>(ws + lay.cnt_off);
+  a.queue = reinterpret_cast<unsigned*>(ws);
   a.lse = reinterpret_cast<float*>(ws + lay.lse_off);
   a.o_part = reinterpret_cast<float*>(ws + lay.o_off);
   a.B = B;
@@ -239,18 +221,18 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
   a.D = head_dim;
   a.T_max = T_max;
   a.n_rep = n_rep;
-  a.balanced = lay.balanced;
-  a.split = lay.split;
-  a.n_splits = lay.n_splits;
+  a.chunk = lay.chunk;
+  a.n_chunks = lay.n_chunks;
+  a.use_queue = lay.queue;
   a.grid_wgs = 0;
-  a.min_rows_per_wg = 0;
-  if (lay.balanced) {
-    // four decode workgroups fit on a compute unit (LDS and registers): one round
+  a.cus = 0;
+  if (lay.queue) {
+    // at most four decode workgroups fit on a compute unit; the launcher trims
+    // the grid to what is actually resident
     const int cus = device_cus();
     if (cus <= 0) return fail(ATTN_ERR_HIP, "attn_decode_gqa: cannot query the current device");
-    a.grid_wgs = cus * 4 < kBalancedMaxWgs ? cus * 4 : kBalancedMaxWgs;
-    // keep a piece long against its partial: >= 16*n_rep rows, >= 2 tiles per wave
-    a.min_rows_per_wg = 16 * n_rep > 256 ? 16 * n_rep : 256;
+    a.cus = cus;
+    a.grid_wgs = cus * 4;
   }
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   a.scale_log2e = scale * kLog2e;

@@ -12,9 +12,10 @@ constexpr int kDecodeTileTokens = 32;
 // Waves per decode workgroup.
 constexpr int kDecodeWaves = 4;
 
-// Largest batch the balanced decode schedule plans for (its per-workgroup
-// prefix sum of lengths lives in LDS); larger batches use fixed chunks.
-constexpr int kBalancedMaxB = 1024;
+// Largest batch the queue schedule of the decode kernels plans for (its
+// per-sequence prefix of chunk counts lives in LDS); larger batches launch one
+// workgroup per unit.
+constexpr int kQueueMaxB = 1024;
 
 struct GqaDecodeArgs {
   const void* q;          // [B, Hq, D]
@@ -22,15 +23,15 @@ struct GqaDecodeArgs {
   const void* v;          // [B, T_max, Hkv, D]
   const int32_t* lens;    // [B]
   void* out;              // [B, Hq, D]
-  int* counters;          // [B, Hkv] completion counters, zero between calls (workspace)
-  float* lse;             // [slots, n_rep] log2-sum-exp of each piece   (workspace)
-  float* o_part;          // [slots, n_rep, D] normalised piece outputs  (workspace)
+  unsigned* queue;        // work-queue counter, zero between calls (workspace)
+  float* lse;             // [B, Hkv, n_chunks, n_rep] log2-sum-exp of each unit    (workspace)
+  float* o_part;          // [B, Hkv, n_chunks, n_rep, D] normalised unit outputs  (workspace)
   int B, Hq, Hkv, D, T_max, n_rep;
-  int balanced;           // 1: balanced schedule, 0: fixed chunks
-  int split;              // fixed: positions per chunk (multiple of 64)
-  int n_splits;           // fixed: ceil(T_max / split)
-  int grid_wgs;           // balanced: workgroups launched
-  int min_rows_per_wg;    // balanced: fewest (position, KV head) rows per workgroup
+  int chunk;              // positions per work unit (multiple of 64)
+  int n_chunks;           // ceil(T_max / chunk)
+  int use_queue;          // 1: resident workgroups take units from the queue; 0: one workgroup per unit
+  int grid_wgs;           // queue: most workgroups to launch
+  int cus;                // queue: compute units of the device
   float scale_log2e;      // softmax scale * log2(e)
   int in_bf16;            // 1: bf16 inputs, 0: fp32 inputs
   int out_bf16;           // 1: bf16 output, 0: fp32 output

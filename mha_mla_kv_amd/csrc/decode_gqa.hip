@@ -8,31 +8,35 @@
 // contiguous query-head grouping its repeat_kv expansion defines.
 //
 // How (not from the pages; designed for CDNA4):
-//  * Work is cut into "pieces": a range of cached positions of one (sequence,
-//    KV head).  A workgroup streams a piece's K and V rows from HBM exactly once
-//    and applies them to all n_rep query heads of the group -- the repeat_kv
-//    copies are never made.  Its four waves take interleaved 32-token tiles.
-//  * Two schedules.  Fixed: chunks of `split` positions, grid (Hkv, chunks, B).
-//    Balanced (default): every workgroup derives the same plan from cache_lens
-//    on the device and takes an equal share of all cached (position, KV head)
-//    rows, so ragged lengths leave no tail of idle compute units.
+//  * Work is cut into units: a chunk of cached positions of one (sequence, KV
+//    head).  A workgroup streams a unit's K and V rows from HBM exactly once and
+//    applies them to all n_rep query heads of the group -- the repeat_kv copies
+//    are never made.  Its four waves take interleaved 32-token tiles.
+//  * Schedule: the resident workgroups take units from a device-wide queue
+//    (an atomic counter), planned on the device from cache_lens.  Under full
+//    load the compute units stream at different rates, so a static equal split
+//    ends with most of them idle; the queue keeps all of them busy until the
+//    last units.  Batches larger than the LDS plan launch one workgroup per unit.
+//  * Loads: K and V rows are read in row order with non-temporal buffer loads
+//    (whole 64-byte segments per load, bounded by the buffer size so rows past
+//    the unit end read as zeros without traffic), then staged per wave in LDS.
 //  * bf16 path: scores are S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with the
-//    tile's tokens as M and (padded) query heads as N, so the K tile is the A
-//    operand and is loaded straight from HBM with one 16-byte load per lane per
-//    32 dims.  P stays in the accumulator layout and becomes the B operand of
-//    O^T += V^T P^T after a token permutation that both operands share.  V is
-//    staged row-major in LDS (one private region per wave, 16-byte writes) and
+//    tile's tokens as M and (padded) query heads as N; the K operand is read
+//    from LDS.  P stays in the accumulator layout and becomes the B operand of
+//    O^T += V^T P^T after a token permutation that both operands share; V is
 //    read back transposed with ds_read_b64_tr_b16.
 //  * fp32 path (VALU): 16 lanes cover one token's row (head_dim/16 elements
 //    each); dot products are reduced inside the 16-lane DPP row.
-//  * Online softmax in base 2 (scale * log2 e folded in, v_exp_f32).  A piece
-//    that covers its whole sequence writes the output directly.  Otherwise it
-//    writes a normalised partial and its log2-sum-exp (cache-bypassing stores),
-//    then bumps the segment's completion counter; the workgroup that completes
-//    the segment merges all its pieces and resets the counter to 0.
-//  * Positions at or beyond L_b are never read: a tile's row index is clamped
-//    to the piece end - 1 and scores past the piece end are masked to -inf.
+//  * Online softmax in base 2 (scale * log2 e folded in, v_exp_f32).  A unit
+//    that covers its whole sequence writes the output directly; otherwise it
+//    writes a normalised partial and its log2-sum-exp, and a second kernel
+//    combines the partials of each (sequence, KV head).
+//  * Scores of positions at or beyond the unit end are masked to -inf; no
+//    cache row at or beyond L_b is read.
 #include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
 
 #include "attn_internal.h"
 
@@ -78,6 +82,10 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const u16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
 }
 
+// Cache policy of the K/V loads: non-temporal (streaming).  The cache is read
+// once per call; these loads neither displace reusable lines nor wait on them.
+constexpr int kStreamPolicy = 2;
+
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -117,65 +125,58 @@ __device__ __forceinline__ int clamp_len(int L, int T_max) { return L < 0 ? 0 : 
 // Values that are the same in every lane (read from LDS or computed from such
 // values), moved to scalar registers.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ unsigned long long uniform(unsigned long long x) {
-  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
-  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(x >> 32));
-  return ((unsigned long long)hi << 32) | lo;
-}
 
 // ---------------------------------------------------------------------------
-// Schedule
+// Work units and their schedule
+//
+// A unit is chunk j of one (sequence b, KV head g): positions
+// [j*chunk, min((j+1)*chunk, L_b)).  Sequence b has n_b = ceil(L_b / chunk)
+// chunks per KV head.  A unit of a one-chunk sequence writes the output rows of
+// its group directly; otherwise it writes a normalised partial output and its
+// log2-sum-exp to slot (b*Hkv + g)*n_chunks + j, and gqa_decode_merge combines
+// the partials of each (b, g) afterwards.
+//
+// Queue schedule: a grid of the workgroups that are resident at once; each takes
+// the next unit from a device-wide counter until none is left, so units go to
+// whichever workgroup is free (compute units do not stream at equal rates under
+// full load, and a static equal split leaves the fast ones idle at the end).
+// Units are numbered sequence-major, then chunk, then KV head: units taken at
+// about the same time read the same cache rows (all KV heads of a position are
+// adjacent in memory).  Fixed schedule (batches too large for the queue's plan
+// in LDS): grid (Hkv, n_chunks, B), one workgroup per unit, empty ones exit.
 
-struct Piece {
-  int b, g;         // sequence and KV head
-  int t0, t1;       // positions [t0, t1) of the sequence
-  int slot;         // partial-result slot of this piece
-  int first_slot;   // slots of the segment's pieces: first_slot .. first_slot + count - 1
-  int count;        // number of pieces of the segment (b, g)
+struct Unit {
+  int b, g;    // sequence and KV head
+  int t0, t1;  // positions [t0, t1)
+  int j, n;    // chunk index and chunks of the sequence
 };
 
-// Per-workgroup shared state of the schedule and of the piece epilogue.
-struct SchedShared {
-  int b0;                     // balanced: first sequence of this workgroup's range
-  int last;                   // this workgroup completed the current segment
-  float m[64], inv[64];       // merge: per-head max and 1/sum of chunk weights
+// Per-workgroup shared state of the schedule.
+struct UnitShared {
+  unsigned unit;     // queue: unit taken by this workgroup
+  int b;             // queue: its sequence
+  unsigned wsum[4];  // per-wave sums of the plan's prefix scan
 };
 
-// Balanced schedule.  Rows of (position, KV head) are numbered sequence-major,
-// then KV head, then position: segment (b, g) covers [Hkv*P_b + g*N_b, .. + N_b)
-// where P_b = sum_{b'<b} N_b'.  Workgroup w of G takes [w*N/G, (w+1)*N/G) of the
-// N = Hkv*P_B rows.  The piece of workgroup w in segment s gets slot w + s
-// (unique: moving to the next piece increments w or s), so the pieces of segment
-// s use the consecutive slots w_first + s .. w_last + s.
-struct Balanced {
-  unsigned N;  // total rows (< 2^31: checked on the host)
-  int G;       // workgroups that take work
-  __device__ unsigned start(int w) const { return (unsigned)(((unsigned long long)w * N) / (unsigned)G); }
-  // largest w with start(w) <= x  (x < N)
-  __device__ int owner(unsigned x) const {
-    return (int)((((unsigned long long)x + 1) * (unsigned)G - 1) / N);
-  }
-};
-
-// Block-wide exclusive prefix sum of clamped lengths into pre[0..B] (B <= 1024,
-// four sequences per thread).  pre and wsum live in LDS scratch; returns pre[B].
-__device__ unsigned long long length_prefix(const GqaDecodeArgs& a, unsigned long long* pre, unsigned long long* wsum) {
+// Block-wide exclusive prefix sum of n_b = ceil(L_b / chunk) into pre[0..B]
+// (B <= kQueueMaxB, four sequences per thread); returns pre[B].
+__device__ unsigned chunk_prefix(const GqaDecodeArgs& a, unsigned* pre, unsigned* wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  unsigned long long v[4], tsum = 0;
+  unsigned v[4], tsum = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int b = 4 * tid + i;
-    v[i] = b < a.B ? (unsigned long long)clamp_len(a.lens[b], a.T_max) : 0ull;
+    v[i] = b < a.B ? (unsigned)((clamp_len(a.lens[b], a.T_max) + a.chunk - 1) / a.chunk) : 0u;
     tsum += v[i];
   }
-  unsigned long long inc = tsum;  // inclusive scan over the wave
+  unsigned inc = tsum;  // inclusive scan over the wave
   for (int off = 1; off < 64; off <<= 1) {
-    const unsigned long long y = __shfl_up(inc, off);
+    const unsigned y = __shfl_up(inc, off);
     if (lane >= off) inc += y;
   }
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
-  unsigned long long run = inc - tsum;
+  unsigned run = inc - tsum;
   for (int w = 0; w < wave; ++w) run += wsum[w];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -188,102 +189,40 @@ __device__ unsigned long long length_prefix(const GqaDecodeArgs& a, unsigned lon
   return pre[a.B];
 }
 
-// ---------------------------------------------------------------------------
-// Cross-workgroup exchange of partial results.  An agent-scope __threadfence()
-// on gfx950 writes back and invalidates the whole L2 of the XCD, which is far too
-// slow to issue once per workgroup.  Instead the partials are written and read
-// with agent-scope atomic stores/loads, which bypass the non-coherent L2 copies
-// (sc1), and ordering is enforced by waiting for the stores' completion before
-// the completion counter is bumped.
-__device__ __forceinline__ void store_coherent(float* p, float x, float y) {
-  const unsigned long long v = ((unsigned long long)__builtin_bit_cast(unsigned, y) << 32) | __builtin_bit_cast(unsigned, x);
-  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Writes one output element pair (out_dtype) of row `row` (= b*Hq + h).
+__device__ __forceinline__ void store_out2(const GqaDecodeArgs& a, size_t row, int d, float x, float y) {
+  const size_t off = row * a.D + d;
+  if (a.out_bf16) {
+    const unsigned w = (unsigned)__builtin_bit_cast(u16, (__bf16)x) | ((unsigned)__builtin_bit_cast(u16, (__bf16)y) << 16);
+    *reinterpret_cast<unsigned*>(static_cast<u16*>(a.out) + off) = w;
+  } else {
+    *reinterpret_cast<float2*>(static_cast<float*>(a.out) + off) = make_float2(x, y);
+  }
 }
-__device__ __forceinline__ void store_coherent(float* p, float x) {
-  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __builtin_bit_cast(unsigned, x), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 load_coherent2(const float* p) {
-  const unsigned long long v =
-      __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__builtin_bit_cast(float, (unsigned)v), __builtin_bit_cast(float, (unsigned)(v >> 32)));
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __builtin_bit_cast(float, __hip_atomic_load(reinterpret_cast<const unsigned*>(p), __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT));
-}
-// Wait until this thread's memory operations have completed (vmcnt(0)).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
-// Piece epilogue: ob[n_rep][D] (normalised output of the piece) and lse[n_rep]
-// (log2-sum-exp) are in LDS.  Writes the output directly when the piece is the
-// whole segment; otherwise publishes the partial and, if this workgroup
-// completes the segment, merges the segment's partials into the output.
+// Unit epilogue: ob[n_rep][D] (normalised output of the unit) and lse[n_rep]
+// (its log2-sum-exp) are in LDS.  Ends with a barrier (ob is reused).
 template <int D>
-__device__ void finish_piece(const GqaDecodeArgs& a, const Piece& pc, const float* ob, const float* lse,
-                             SchedShared& sh) {
-  const int tid = threadIdx.x;
-  const int n_rep = a.n_rep;
-  const size_t out_row0 = (size_t)pc.b * a.Hq + (size_t)pc.g * n_rep;
-  auto store_out = [&](int hd, int d2, float2 v) {
-    const size_t off = (out_row0 + hd) * D + 2 * d2;
-    if (a.out_bf16) {
-      const unsigned w = (unsigned)__builtin_bit_cast(u16, (__bf16)v.x) |
-                         ((unsigned)__builtin_bit_cast(u16, (__bf16)v.y) << 16);
-      *reinterpret_cast<unsigned*>(static_cast<u16*>(a.out) + off) = w;
-    } else {
-      *reinterpret_cast<float2*>(static_cast<float*>(a.out) + off) = v;
-    }
-  };
+__device__ void store_unit(const GqaDecodeArgs& a, const Unit& u, const float* ob, const float* lse) {
+  const int tid = threadIdx.x, n_rep = a.n_rep;
   constexpr int D2 = D / 2;
-  if (pc.count == 1) {
+  if (u.n == 1) {
+    const size_t row0 = (size_t)u.b * a.Hq + (size_t)u.g * n_rep;
     for (int e = tid; e < n_rep * D2; e += 256) {
       const int hd = e / D2, d2 = e - hd * D2;
-      store_out(hd, d2, *reinterpret_cast<const float2*>(ob + hd * D + 2 * d2));
+      const float2 v = *reinterpret_cast<const float2*>(ob + hd * D + 2 * d2);
+      store_out2(a, row0 + hd, 2 * d2, v.x, v.y);
     }
-    __syncthreads();
-    return;
+  } else {
+    const size_t slot = ((size_t)u.b * a.Hkv + u.g) * a.n_chunks + u.j;
+    float2* o_ws = reinterpret_cast<float2*>(a.o_part + slot * n_rep * D);
+    for (int e = tid; e < n_rep * D2; e += 256) o_ws[e] = *reinterpret_cast<const float2*>(ob + 2 * e);
+    for (int hd = tid; hd < n_rep; hd += 256) a.lse[slot * n_rep + hd] = lse[hd];
   }
-  float* o_ws = a.o_part + (size_t)pc.slot * n_rep * D;
-  for (int e = tid; e < n_rep * D2; e += 256) store_coherent(o_ws + 2 * e, ob[2 * e], ob[2 * e + 1]);
-  for (int hd = tid; hd < n_rep; hd += 256) store_coherent(a.lse + (size_t)pc.slot * n_rep + hd, lse[hd]);
-  wait_vmem();      // this thread's partial stores have completed
-  __syncthreads();  // ... and every thread's
-  int* cnt = a.counters + (size_t)pc.b * a.Hkv + pc.g;
-  if (tid == 0) sh.last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == pc.count - 1;
-  __syncthreads();
-  if (!sh.last) return;
-  // this workgroup completed the segment: merge its pieces (coherent loads)
-  for (int hd = tid; hd < n_rep; hd += 256) {
-    float M = kNegInf;
-    for (int k = 0; k < pc.count; ++k) M = fmaxf(M, load_coherent(a.lse + (size_t)(pc.first_slot + k) * n_rep + hd));
-    float S = 0.f;
-    for (int k = 0; k < pc.count; ++k)
-      S += exp2_fast(load_coherent(a.lse + (size_t)(pc.first_slot + k) * n_rep + hd) - M);
-    sh.m[hd] = M;
-    sh.inv[hd] = 1.f / S;
-  }
-  __syncthreads();
-  for (int e = tid; e < n_rep * D2; e += 256) {
-    const int hd = e / D2, d2 = e - hd * D2;
-    const float M = sh.m[hd];
-    float2 acc = {0.f, 0.f};
-    for (int k = 0; k < pc.count; ++k) {
-      const size_t sl = (size_t)(pc.first_slot + k);
-      const float w = exp2_fast(load_coherent(a.lse + sl * n_rep + hd) - M);
-      const float2 v = load_coherent2(a.o_part + (sl * n_rep + hd) * D + 2 * d2);
-      acc.x = fmaf(w, v.x, acc.x);
-      acc.y = fmaf(w, v.y, acc.y);
-    }
-    const float sc = sh.inv[hd];
-    store_out(hd, d2, make_float2(acc.x * sc, acc.y * sc));
-  }
-  // leave the counter zero for the next call
-  if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
 }
 
-// Zero output rows of a (sequence, KV head) with an empty cache (it has no piece).
+// Zero output rows of a (sequence, KV head) with an empty cache (it has no unit).
 template <int D>
 __device__ void zero_rows(const GqaDecodeArgs& a, int b, int g) {
   const size_t row0 = (size_t)b * a.Hq + (size_t)g * a.n_rep;
@@ -293,86 +232,111 @@ __device__ void zero_rows(const GqaDecodeArgs& a, int b, int g) {
   }
 }
 
-// Drives the schedule: calls process(piece) for every piece of this workgroup,
-// in order, each followed by the epilogue.  process leaves ob/lse in LDS.
-// `scratch` (>= 8 * (B + 5) bytes of LDS) holds the balanced plan until the
-// first piece starts.
-template <int D, bool BALANCED, typename Process>
-__device__ void run_schedule(const GqaDecodeArgs& a, SchedShared& sh, void* scratch, float* ob, float* lse,
-                             Process&& process) {
-  if constexpr (!BALANCED) {
-    const int g = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+// Drives the schedule: for every unit of this workgroup, process(unit) leaves
+// the unit's normalised output in ob and its log2-sum-exp in lse (LDS), and
+// store_unit publishes it.  `pre` (queue only) holds kQueueMaxB + 1 unsigned in
+// LDS for the whole kernel.
+template <int D, bool QUEUE, typename Process>
+__device__ void run_units(const GqaDecodeArgs& a, UnitShared& sh, unsigned* pre, float* ob, float* lse,
+                          Process&& process) {
+  if constexpr (!QUEUE) {
+    const int g = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int L = clamp_len(a.lens[b], a.T_max);
     if (L == 0) {
-      if (s == 0) zero_rows<D>(a, b, g);
+      if (j == 0) zero_rows<D>(a, b, g);
       return;
     }
-    const int c0 = s * a.split;
-    if (c0 >= L) return;
-    Piece pc;
-    pc.b = b;
-    pc.g = g;
-    pc.t0 = c0;
-    pc.t1 = min(c0 + a.split, L);
-    pc.count = (L + a.split - 1) / a.split;
-    pc.first_slot = (b * a.Hkv + g) * a.n_splits;
-    pc.slot = pc.first_slot + s;
-    process(pc);
-    finish_piece<D>(a, pc, ob, lse, sh);
+    Unit u;
+    u.b = b;
+    u.g = g;
+    u.j = j;
+    u.t0 = j * a.chunk;
+    if (u.t0 >= L) return;
+    u.t1 = min(u.t0 + a.chunk, L);
+    u.n = (L + a.chunk - 1) / a.chunk;
+    process(u);
+    store_unit<D>(a, u, ob, lse);
   } else {
-    unsigned long long* pre = static_cast<unsigned long long*>(scratch);  // [B + 1]
-    unsigned long long* wsum = pre + (a.B + 1);                             // [4]
-    const unsigned long long P_B = uniform(length_prefix(a, pre, wsum));
-    const int w = blockIdx.x;
+    const int tid = threadIdx.x, Hkv = a.Hkv;
+    const unsigned per_head = uniform((int)chunk_prefix(a, pre, sh.wsum));
     // empty sequences: workgroups take them round-robin
-    for (int b = w; b < a.B; b += gridDim.x)
+    for (int b = blockIdx.x; b < a.B; b += gridDim.x)
       if (pre[b + 1] == pre[b])
-        for (int g = 0; g < a.Hkv; ++g) zero_rows<D>(a, b, g);
-    Balanced bl;
-    bl.N = (unsigned)(P_B * (unsigned)a.Hkv);
-    if (bl.N == 0) return;
-    bl.G = (int)min((unsigned)gridDim.x, (bl.N + a.min_rows_per_wg - 1) / a.min_rows_per_wg);
-    if (w >= bl.G) return;
-    const unsigned x0 = bl.start(w), x1 = bl.start(w + 1);
-    if (x0 >= x1) return;
-    // sequence holding row x0: Hkv*pre[b] <= x0 < Hkv*pre[b+1]
-    for (int b = threadIdx.x; b < a.B; b += 256)
-      if (pre[b] * a.Hkv <= x0 && x0 < pre[b + 1] * a.Hkv) sh.b0 = b;
-    __syncthreads();
-    int b = uniform(sh.b0);
-    const unsigned seq_start = (unsigned)uniform(pre[b]) * a.Hkv;
-    int L = uniform((int)(pre[b + 1] - pre[b]));
-    int g = (int)((x0 - seq_start) / (unsigned)L);
-    unsigned seg_start = seq_start + (unsigned)g * L;
-    __syncthreads();  // pre[] (in the tile scratch) is dead from here on
-    unsigned x = x0;
-    while (x < x1) {
-      const unsigned seg_end = seg_start + L;
-      const unsigned e = seg_end < x1 ? seg_end : x1;
-      Piece pc;
-      pc.b = b;
-      pc.g = g;
-      pc.t0 = (int)(x - seg_start);
-      pc.t1 = (int)(e - seg_start);
-      const int s = b * a.Hkv + g;
-      const int wf = bl.owner(seg_start), wl = bl.owner(seg_end - 1);
-      pc.count = wl - wf + 1;
-      pc.first_slot = wf + s;
-      pc.slot = w + s;
-      process(pc);
-      finish_piece<D>(a, pc, ob, lse, sh);
-      x = e;
-      if (x >= x1) break;
-      // next non-empty segment (one exists: x < x1 <= N)
-      seg_start = seg_end;
-      if (++g == a.Hkv) {
-        g = 0;
-        do {
-          ++b;
-          L = uniform(clamp_len(a.lens[b], a.T_max));
-        } while (L == 0);
+        for (int g = 0; g < Hkv; ++g) zero_rows<D>(a, b, g);
+    const unsigned n_units = per_head * (unsigned)Hkv;
+    for (;;) {
+      if (tid == 0) sh.unit = __hip_atomic_fetch_add(a.queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const unsigned x = (unsigned)uniform((int)sh.unit);
+      if (x >= n_units) break;
+      // sequence of unit x: Hkv*pre[b] <= x < Hkv*pre[b+1]
+      for (int b = tid; b < a.B; b += 256)
+        if (pre[b] * Hkv <= x && x < pre[b + 1] * Hkv) sh.b = b;
+      __syncthreads();
+      Unit u;
+      u.b = uniform(sh.b);
+      const unsigned p0 = (unsigned)uniform((int)pre[u.b]);
+      const unsigned r = x - p0 * Hkv;
+      u.j = (int)(r / (unsigned)Hkv);
+      u.g = (int)(r - (unsigned)u.j * Hkv);
+      u.n = uniform((int)(pre[u.b + 1] - p0));
+      u.t0 = u.j * a.chunk;
+      u.t1 = min(u.t0 + a.chunk, uniform(clamp_len(a.lens[u.b], a.T_max)));
+      process(u);
+      store_unit<D>(a, u, ob, lse);
+    }
+  }
+}
+
+// Combines the partials of every (sequence, KV head) with more than one chunk:
+// out = sum_j 2^(lse_j - M) o_j / sum_j 2^(lse_j - M), M = max_j lse_j.  Grid
+// (Hkv, B).  Also returns the queue counter to zero for the next call (the
+// decode kernel has finished: same stream).
+__global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
+  __shared__ float m_s[64], inv_s[64];
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  if (a.use_queue && g == 0 && b == 0 && tid == 0) *a.queue = 0u;
+  const int L = clamp_len(a.lens[b], a.T_max);
+  const int n = (L + a.chunk - 1) / a.chunk;
+  if (n <= 1) return;  // written by the decode kernel
+  const int n_rep = a.n_rep, D2 = a.D / 2;
+  const size_t s0 = ((size_t)b * a.Hkv + g) * a.n_chunks;
+  const float* lse = a.lse + s0 * n_rep;
+  for (int hd = tid; hd < n_rep; hd += 256) {
+    float M = kNegInf;
+    for (int j = 0; j < n; ++j) M = fmaxf(M, lse[(size_t)j * n_rep + hd]);
+    float S = 0.f;
+    for (int j = 0; j < n; ++j) S += exp2_fast(lse[(size_t)j * n_rep + hd] - M);
+    m_s[hd] = M;
+    inv_s[hd] = 1.f / S;
+  }
+  __syncthreads();
+  const size_t row0 = (size_t)b * a.Hq + (size_t)g * n_rep;
+  const float2* op = reinterpret_cast<const float2*>(a.o_part + s0 * n_rep * a.D);
+  const size_t jstride = (size_t)n_rep * D2;  // float2 per slot
+  for (int e = tid; e < n_rep * D2; e += 256) {
+    const int hd = e / D2, d2 = e - hd * D2;
+    const float M = m_s[hd];
+    float2 acc = {0.f, 0.f};
+    // eight partials per batch, loaded before use (indices clamped, extra weights 0)
+    for (int j0 = 0; j0 < n; j0 += 8) {
+      float w[8];
+      float2 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = min(j0 + k, n - 1);
+        w[k] = lse[(size_t)j * n_rep + hd];
+        v[k] = op[(size_t)j * jstride + e];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float wk = j0 + k < n ? exp2_fast(w[k] - M) : 0.f;
+        acc.x = fmaf(wk, v[k].x, acc.x);
+        acc.y = fmaf(wk, v[k].y, acc.y);
       }
     }
+    const float sc = inv_s[hd];
+    store_out2(a, row0 + hd, 2 * d2, acc.x * sc, acc.y * sc);
   }
 }
 
@@ -383,22 +347,27 @@ __device__ void run_schedule(const GqaDecodeArgs& a, SchedShared& sh, void* scra
 #ifndef ATTN_DECODE_WAVES_PER_EU_D128
 #define ATTN_DECODE_WAVES_PER_EU_D128 3
 #endif
-template <int D, int HB, bool BALANCED>
+template <int D, int HB, bool QUEUE>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(HB > 1 ? 1 : (D == 128 ? ATTN_DECODE_WAVES_PER_EU_D128 : 4))))
+__attribute__((amdgpu_waves_per_eu(HB > 1 ? 1 : (D >= 96 ? ATTN_DECODE_WAVES_PER_EU_D128 : 4))))
 void gqa_decode_bf16(GqaDecodeArgs a) {
   static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
   constexpr int KC = D / 32;           // 32-wide dim chunks (QK contraction)
   constexpr int DW = D / 16;           // 16-wide dim blocks (PV output rows)
   constexpr int VP = D + 16;           // V tile row pitch in elements ([token][dim], padded)
+  constexpr int KP = D + 8;            // K tile row pitch (16 rows of one column: distinct LDS banks)
+  constexpr int kUnits = D / 8;                              // 16-byte units per K/V row
+  constexpr int kLanesPerRow = kUnits <= 8 ? 8 : 16;          // lanes that load one row
+  constexpr int kRowsPerLoad = 64 / kLanesPerRow;
+  constexpr int kLoads = kDecodeTileTokens / kRowsPerLoad;   // 16-byte loads per lane per tile
   constexpr int kVtElems = kDecodeWaves * kDecodeTileTokens * VP;
   // epilogue scratch (floats): m and l per wave and head, [HB*16][D] outputs, lse
   static_assert(2 * kDecodeWaves * HB * 16 * 4 + HB * 16 * D * 4 + HB * 16 * 4 <= kVtElems * 2, "scratch");
-  static_assert((kBalancedMaxB + 5) * 8 <= kVtElems * 2, "balanced plan scratch");
   __shared__ __attribute__((aligned(16))) u16 smem[kVtElems];
-  __shared__ SchedShared sh;
+  __shared__ unsigned pre[QUEUE ? kQueueMaxB + 1 : 1];
+  __shared__ UnitShared sh;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = lane & 15, grp = lane >> 4;
   const int n_rep = a.n_rep;
   float* mw = reinterpret_cast<float*>(smem);   // [waves][HB*16]
@@ -407,8 +376,11 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   float* lse_s = ob + HB * 16 * D;              // [HB*16]
   u16* vt = smem + wave * kDecodeTileTokens * VP;
   const size_t tok_stride = (size_t)a.Hkv * D;
+  // this lane's row within a load and its 16-byte unit in the row
+  const int lrow = lane / kLanesPerRow, lunit = min(lane % kLanesPerRow, kUnits - 1);
+  const unsigned row_off = (unsigned)(lrow * tok_stride * 2 + 16 * lunit);
 
-  auto process = [&](const Piece& pc_) {
+  auto process = [&](const Unit& pc_) {
     const int pb = uniform(pc_.b), pg = uniform(pc_.g), pt0 = uniform(pc_.t0);
     const u16* qp = static_cast<const u16*>(a.q) + ((size_t)pb * a.Hq + (size_t)pg * n_rep) * D;
     const u16* kp = static_cast<const u16*>(a.k) + ((size_t)pb * a.T_max * a.Hkv + pg) * D;
@@ -433,54 +405,60 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
 #pragma unroll
       for (int w = 0; w < DW; ++w) o[hb][w] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // K as the A operand (row = token), V in the same layout.  Rows past the
-    // piece end re-read its last row (their scores are masked), which also makes
-    // the one-tile-ahead loads below safe to issue unconditionally.
-    auto load_k = [&](bf16x8 (&kr)[2][KC], int t0) {
+    // K and V tiles of 32 positions are read in row order with streaming
+    // (non-temporal) buffer loads: lane group lane / kLanesPerRow of load i
+    // fetches row kRowsPerLoad * i + lane / kLanesPerRow, each lane one 16-byte
+    // unit (head_dim 96: lanes past the 12th unit repeat it), so a load covers
+    // whole rows.  Each load has its own buffer resource starting at its first
+    // row and ending with row c1 - 1: rows at or past the unit end read as zeros
+    // and cost no memory traffic, so the one-tile-ahead loads below can be
+    // issued unconditionally.
+    const int row_bytes = uniform((int)(tok_stride * 2));
+    auto load_rows = [&](bf16x8 (&r)[kLoads], const u16* head0, int t0) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int tok = min(t0 + 16 * u + row, c1 - 1);
-        const u16* krow = kp + (size_t)tok * tok_stride + 8 * grp;
-#pragma unroll
-        for (int c = 0; c < KC; ++c) kr[u][c] = load_bf16x8(krow + 32 * c);
+      for (int i = 0; i < kLoads; ++i) {
+        const int t = t0 + kRowsPerLoad * i;
+        // rows of this load before c1, 0..kRowsPerLoad; bytes up to the end of the last
+        // (row_bytes >= 2 * D, so no rows gives a non-positive count)
+        const int rows = min(max(c1 - t, 0), kRowsPerLoad);
+        const int n = max(rows * row_bytes - row_bytes + 2 * D, 0);
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(head0 + (size_t)t * tok_stride), (short)0, n,
+                                                          0x00020000);
+        r[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)row_off, 0, kStreamPolicy));
       }
     };
-    auto load_v = [&](bf16x8 (&vr)[2][KC], int t0) {
+    // The same registers written to this wave's LDS tile, row pitch `pitch`.
+    auto store_rows = [&](const bf16x8 (&r)[kLoads], int pitch) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int tok = min(t0 + 16 * u + row, c1 - 1);
-        const u16* vrow = vp + (size_t)tok * tok_stride + 8 * grp;
-#pragma unroll
-        for (int c = 0; c < KC; ++c) vr[u][c] = load_bf16x8(vrow + 32 * c);
-      }
+      for (int i = 0; i < kLoads; ++i)
+        *reinterpret_cast<u16x8*>(vt + (kRowsPerLoad * i + lrow) * pitch + 8 * lunit) = __builtin_bit_cast(u16x8, r[i]);
     };
     constexpr int kStep = kDecodeWaves * kDecodeTileTokens;
     int t0 = pt0 + wave * kDecodeTileTokens;
-    bf16x8 kr[2][KC], vr[2][KC];
+    bf16x8 kr[kLoads], vr[kLoads];
     if (t0 < c1) {
-      load_k(kr, t0);
-      load_v(vr, t0);
+      load_rows(kr, kp, t0);
+      load_rows(vr, vp, t0);
     }
-    // Per tile: V(t) -> LDS, then V(t+1) is requested; scores on K(t), then
-    // K(t+1) is requested; PV from LDS.  About one tile stays in flight per wave
-    // with no extra registers.
+    // Per tile: K(t) -> LDS; scores from LDS; K(t+1) requested; V(t) -> LDS
+    // (same region); V(t+1) requested; softmax; PV from LDS.  About one tile
+    // stays in flight per wave.
     for (; t0 < c1; t0 += kStep) {
-      // V tile into this wave's LDS region, row-major [token][dim]
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int c = 0; c < KC; ++c)
-          *reinterpret_cast<u16x8*>(vt + (16 * u + row) * VP + 32 * c + 8 * grp) = __builtin_bit_cast(u16x8, vr[u][c]);
-      load_v(vr, t0 + kStep);
-      // Scores: lane holds S^T[token 16u + 4grp + i][head 16hb + row]
+      store_rows(kr, KP);
+      wave_lds_sync();
+      // Scores: lane holds S^T[token 16u + 4grp + i][head 16hb + row]; the A
+      // operand (token 16u + row, dims 32c + 8grp .. +8) comes from LDS.
       float sc[HB][2][4];
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 ka[KC];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int c = 0; c < KC; ++c) ka[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(vt + (16 * u + row) * KP + 32 * c + 8 * grp));
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int c = 0; c < KC; ++c) acc = mfma_16x16x32(kr[u][c], qop[hb][c], acc);
+          for (int c = 0; c < KC; ++c) acc = mfma_16x16x32(ka[c], qop[hb][c], acc);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int tok = t0 + 16 * u + 4 * grp + i;
@@ -488,7 +466,12 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
           }
         }
       }
-      load_k(kr, t0 + kStep);
+      // K(t+1) after the scores: its registers are then free (the tile is in LDS)
+      __builtin_amdgcn_sched_barrier(0);
+      load_rows(kr, kp, t0 + kStep);
+      wave_lds_sync();
+      store_rows(vr, VP);
+      load_rows(vr, vp, t0 + kStep);
       // Online softmax per head; P^T as the B operand of the PV product.
       bf16x8 pop[HB];
 #pragma unroll
@@ -577,27 +560,27 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
       __syncthreads();
     }
   };
-  run_schedule<D, BALANCED>(a, sh, smem, ob, lse_s, process);
+  run_units<D, QUEUE>(a, sh, pre, ob, lse_s, process);
 }
 
 // ---------------------------------------------------------------------------
 // fp32 inputs, VALU.  16 rows of 16 lanes; row r takes positions t0 + r + 16k.
-template <int D, int NR, bool BALANCED>
+template <int D, int NR, bool QUEUE>
 __global__ __launch_bounds__(256) void gqa_decode_f32(GqaDecodeArgs a) {
   static_assert(D % 16 == 0, "head_dim must be a multiple of 16");
   constexpr int E = D / 16;
   __shared__ float mw[kDecodeWaves][NR], lw[kDecodeWaves][NR];
   __shared__ __attribute__((aligned(16))) float ob[NR * D];
   __shared__ float lse_s[NR];
-  __shared__ unsigned long long plan[kBalancedMaxB + 5];
-  __shared__ SchedShared sh;
+  __shared__ unsigned pre[QUEUE ? kQueueMaxB + 1 : 1];
+  __shared__ UnitShared sh;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rid = threadIdx.x >> 4, col = threadIdx.x & 15;
   const int n_rep = a.n_rep;
   const size_t tok_stride = (size_t)a.Hkv * D;
 
-  auto process = [&](const Piece& pc) {
+  auto process = [&](const Unit& pc) {
     const float* qp = static_cast<const float*>(a.q) + ((size_t)pc.b * a.Hq + (size_t)pc.g * n_rep) * D + col * E;
     const float* kp = static_cast<const float*>(a.k) + ((size_t)pc.b * a.T_max * a.Hkv + pc.g) * D + col * E;
     const float* vp = static_cast<const float*>(a.v) + ((size_t)pc.b * a.T_max * a.Hkv + pc.g) * D + col * E;
@@ -694,38 +677,65 @@ __global__ __launch_bounds__(256) void gqa_decode_f32(GqaDecodeArgs a) {
       __syncthreads();
     }
   };
-  run_schedule<D, BALANCED>(a, sh, plan, ob, lse_s, process);
+  run_units<D, QUEUE>(a, sh, pre, ob, lse_s, process);
 }
 
-template <int D, bool BAL>
+// Workgroups of 256 threads of `kernel` that are resident on one compute unit of
+// the current device (0 if the query fails); asked once per kernel and device.
+int resident_per_cu(const void* kernel) {
+  struct Entry { const void* k; int dev, n; };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : cache)
+    if (e.k == kernel && e.dev == dev) return e.n;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess) n = 0;
+  cache.push_back({kernel, dev, n});
+  return n;
+}
+
+// Launches kernel(a).  A queue grid is trimmed to the workgroups that are
+// resident at once (more would only wait for the first ones to drain the queue).
+template <typename Kernel>
+hipError_t launch_one(Kernel kernel, const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
+  if (a.use_queue) {
+    const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kernel));
+    if (per_cu > 0 && a.cus > 0 && per_cu * a.cus < (int)grid.x) grid.x = per_cu * a.cus;
+  }
+  hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D, bool QUEUE>
 hipError_t launch_bf16(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
   const int hb = (a.n_rep + 15) / 16;
-  if (hb == 1) hipLaunchKernelGGL((gqa_decode_bf16<D, 1, BAL>), grid, dim3(256), 0, st, a);
-  else if (hb == 2) hipLaunchKernelGGL((gqa_decode_bf16<D, 2, BAL>), grid, dim3(256), 0, st, a);
-  else if (hb <= 4) hipLaunchKernelGGL((gqa_decode_bf16<D, 4, BAL>), grid, dim3(256), 0, st, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (hb == 1) return launch_one(gqa_decode_bf16<D, 1, QUEUE>, a, grid, st);
+  if (hb == 2) return launch_one(gqa_decode_bf16<D, 2, QUEUE>, a, grid, st);
+  if (hb <= 4) return launch_one(gqa_decode_bf16<D, 4, QUEUE>, a, grid, st);
+  return hipErrorInvalidValue;
 }
 
-template <int D, bool BAL>
+template <int D, bool QUEUE>
 hipError_t launch_f32(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
   const int n = a.n_rep;
-  if (n == 1) hipLaunchKernelGGL((gqa_decode_f32<D, 1, BAL>), grid, dim3(256), 0, st, a);
-  else if (n == 2) hipLaunchKernelGGL((gqa_decode_f32<D, 2, BAL>), grid, dim3(256), 0, st, a);
-  else if (n <= 4) hipLaunchKernelGGL((gqa_decode_f32<D, 4, BAL>), grid, dim3(256), 0, st, a);
-  else if (n <= 8) hipLaunchKernelGGL((gqa_decode_f32<D, 8, BAL>), grid, dim3(256), 0, st, a);
-  else if (n <= 16) hipLaunchKernelGGL((gqa_decode_f32<D, 16, BAL>), grid, dim3(256), 0, st, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (n == 1) return launch_one(gqa_decode_f32<D, 1, QUEUE>, a, grid, st);
+  if (n == 2) return launch_one(gqa_decode_f32<D, 2, QUEUE>, a, grid, st);
+  if (n <= 4) return launch_one(gqa_decode_f32<D, 4, QUEUE>, a, grid, st);
+  if (n <= 8) return launch_one(gqa_decode_f32<D, 8, QUEUE>, a, grid, st);
+  if (n <= 16) return launch_one(gqa_decode_f32<D, 16, QUEUE>, a, grid, st);
+  return hipErrorInvalidValue;
 }
 
-template <bool BAL>
+template <bool QUEUE>
 hipError_t launch_mode(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
   if (a.in_bf16)
-    return a.D == 64 ? launch_bf16<64, BAL>(a, grid, st) : a.D == 96 ? launch_bf16<96, BAL>(a, grid, st)
-                                                                      : launch_bf16<128, BAL>(a, grid, st);
-  return a.D == 64 ? launch_f32<64, BAL>(a, grid, st) : a.D == 96 ? launch_f32<96, BAL>(a, grid, st)
-                                                                   : launch_f32<128, BAL>(a, grid, st);
+    return a.D == 64 ? launch_bf16<64, QUEUE>(a, grid, st) : a.D == 96 ? launch_bf16<96, QUEUE>(a, grid, st)
+                                                                        : launch_bf16<128, QUEUE>(a, grid, st);
+  return a.D == 64 ? launch_f32<64, QUEUE>(a, grid, st) : a.D == 96 ? launch_f32<96, QUEUE>(a, grid, st)
+                                                                     : launch_f32<128, QUEUE>(a, grid, st);
 }
 
 }  // namespace
@@ -738,13 +748,19 @@ bool gqa_decode_supported(int D, int n_rep, int in_bf16) {
 
 hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t st) {
   if (!gqa_decode_supported(a.D, a.n_rep, a.in_bf16)) return hipErrorInvalidValue;
-  if (a.balanced) {
-    if (a.B > kBalancedMaxB || a.grid_wgs < 1 || a.min_rows_per_wg < 1) return hipErrorInvalidValue;
-    return launch_mode<true>(a, dim3(a.grid_wgs), st);
+  if (a.chunk < 1 || a.n_chunks < 1) return hipErrorInvalidValue;
+  hipError_t e;
+  if (a.use_queue) {
+    if (a.B > kQueueMaxB || a.n_chunks < 2 || a.grid_wgs < 1 || !a.queue) return hipErrorInvalidValue;
+    e = launch_mode<true>(a, dim3(a.grid_wgs), st);
+  } else {
+    // KV heads vary fastest so the workgroups of one chunk's heads (interleaved
+    // in memory, one row of Hkv*D per position) are dispatched together.
+    e = launch_mode<false>(a, dim3(a.Hkv, a.n_chunks, a.B), st);
   }
-  // KV heads vary fastest so the workgroups of one chunk's heads (interleaved in
-  // memory, one row of Hkv*D per token) are dispatched together.
-  return launch_mode<false>(a, dim3(a.Hkv, a.n_splits, a.B), st);
+  if (e != hipSuccess || a.n_chunks < 2) return e;
+  hipLaunchKernelGGL(gqa_decode_merge, dim3(a.Hkv, a.B), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace attn

@@ -38,15 +38,16 @@ def test_status_strings():
 
 def test_workspace_sizes():
     al = lambda x: (x + 255) // 256 * 256
-    # fixed chunks (split 512) at the Llama-3-8B decode shape: counters [B*Hkv], lse [slots*n_rep],
-    # partials [slots*n_rep*D] fp32, each piece 256-byte aligned
+    # chunks of 512 at the Llama-3-8B decode shape: queue counter (256 bytes), lse [slots*n_rep],
+    # partials [slots*n_rep*D] fp32 with slots = B*Hkv*ceil(T/512), each piece 256-byte aligned
     B, Hq, Hkv, D, T = 32, 32, 8, 128, 8192
     slots = B * Hkv * (T // 512)
     n = attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T, 512)
-    assert n == al(B * Hkv * 4) + al(slots * 4 * 4) + al(slots * 4 * D * 4)
-    # balanced schedule (split 0): 2048 + B*Hkv slots
-    slots = 2048 + B * Hkv
-    assert attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T, 0) == al(B * Hkv * 4) + al(slots * 4 * 4) + al(slots * 4 * D * 4)
+    assert n == 256 + al(slots * 4 * 4) + al(slots * 4 * D * 4)
+    # split 0: the library picks 512 here (B*Hkv*ceil(T/512) = 4096 units)
+    assert attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T, 0) == n
+    # a single chunk per sequence needs no partials
+    assert attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, 512, 512) == 256
     assert attn.attn_decode_gqa_workspace_bytes(0, 32, 8, 128, 8192, 0) == 0
     assert attn.attn_decode_gqa_workspace_bytes(1, 32, 8, 128, 8192, 100) == 0  # split not a multiple of 64
     assert attn.attn_decode_mla_workspace_bytes(64, 8, 128, 48, 4096, 0) > 0
@@ -80,7 +81,7 @@ def test_decode_gqa_validation():
     assert b"remainder 2" in lib.attn_last_error()
     assert _gqa(lib, Hq=32, Hkv=6) == GROUPS
     assert _gqa(lib, split=100) == SHAPE
-    assert _gqa(lib, T=64 * 70000, split=64) == SHAPE  # more than 65535 chunks
+    assert _gqa(lib, B=1025, T=64 * 70000, split=64) == SHAPE  # one workgroup per unit: > 65535 chunks
     assert _gqa(lib, ind=7) == UNSUP
     assert _gqa(lib, D=80) == UNSUP
     assert _gqa(lib, Hq=128, Hkv=1) == UNSUP     # n_rep 128 not built

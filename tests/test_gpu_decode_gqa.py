@@ -148,16 +148,34 @@ def test_full_size_sampled_rows(name):
         assert_close_rows(out[sl], ref, tol, f"{name} b={b} L={int(inp['cache_lens'][b])}")
 
 
-def test_workspace_reuse_across_calls_keeps_counters_zero():
-    """Calls that share one zero-filled workspace (same shape) stay correct, also when the
-    lengths change between calls, and leave the completion counters zero."""
+def test_workspace_reuse_across_calls_keeps_queue_counter_zero():
+    """Calls that share one zero-filled workspace stay correct, also when the lengths and the
+    sizes change between calls, and leave the work-queue counter (first 4 bytes) zero."""
     import mha_mla_kv_amd as attn
     B, Hq, Hkv, D, T = 6, 16, 4, 128, 3000
-    ws = torch.zeros(attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T, 0), dtype=torch.uint8, device="cuda")
-    for seed, lens in ((1, [3000, 1, 2999, 1500, 64, 0]), (2, [17, 3000, 3000, 2048, 1000, 999]), (3, [0, 0, 5, 3000, 2, 1])):
-        inp = synth.gqa_decode_inputs(B, Hq, Hkv, D, T, lens, seed=seed)
-        out = attn.attn_decode_gqa(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), inp["cache_lens"].cuda(), workspace=ws)
+    ws = torch.zeros(attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T, 64), dtype=torch.uint8, device="cuda")
+    runs = ((1, B, [3000, 1, 2999, 1500, 64, 0], 0), (2, B, [17, 3000, 3000, 2048, 1000, 999], 64),
+            (3, B, [0, 0, 5, 3000, 2, 1], 0), (4, 3, [2500, 700, 3000], 128))
+    for seed, b, lens, split in runs:
+        inp = synth.gqa_decode_inputs(b, Hq, Hkv, D, T, lens, seed=seed)
+        out = attn.attn_decode_gqa(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), inp["cache_lens"].cuda(),
+                                   split_tokens=split, workspace=ws)
         torch.cuda.synchronize()
         assert_close_rows(out, oracle.gqa_decode(inp["q"], inp["k"], inp["v"], inp["cache_lens"]), TOL_BF16,
                           f"reuse seed {seed}")
-        assert int(ws[:B * Hkv * 4].view(torch.int32).abs().sum()) == 0
+        assert int(ws[:4].view(torch.int32)[0]) == 0
+
+
+@pytest.mark.parametrize("B", [1024, 1025])
+def test_batch_limit_of_the_queue_schedule(B):
+    """1024 sequences is the largest batch the device-side queue plans for; 1025 launches one
+    workgroup per unit.  Both, with ragged and empty lengths over several chunks, match the oracle."""
+    Hq, Hkv, D, T = 8, 2, 64, 300
+    rng = np.random.default_rng(B)
+    lens = rng.integers(0, T + 1, size=B).tolist()
+    lens[0], lens[-1] = 0, T
+    inp = synth.gqa_decode_inputs(B, Hq, Hkv, D, T, lens, seed=B)
+    print(f"[case] B={B} Hq={Hq} Hkv={Hkv} D={D} T={T} split=64", flush=True)
+    out = _run(inp, split_tokens=64)
+    ref = oracle.gqa_decode(inp["q"], inp["k"], inp["v"], inp["cache_lens"])
+    assert_close_rows(out, ref, TOL_BF16, f"B={B}")
