@@ -47,20 +47,20 @@ int pow2_floor(long long x) {
   return p;
 }
 
-// Positions per decode work unit when the caller leaves it to the library.
-// Enough units that every resident workgroup takes several (the queue then
-// evens out compute units that stream at different rates) when every sequence
-// is full, but long enough that the fp32 partial of a unit (n_rep * D * 4 bytes
-// written and read back) stays small next to its cache bytes (chunk * D * 4).
+// Positions per decode block (the work unit of the fixed schedule; the queue
+// hands out units of four blocks, then single blocks) when the caller leaves it
+// to the library: about B*Hkv*T_max / 2048 rounded down to a multiple of 64,
+// so that every one of the ~256 queue workgroups takes several units even when
+// the lengths are ragged, at most 1024, and long enough that the fp32 partial of
+// a unit (n_rep * D * 4 bytes written and read back) stays small next to its
+// cache bytes (chunk * D * 4).
 int choose_chunk(int B, int Hkv, int n_rep, int T_max) {
-  const long long target_units = 4096;
   int lo = 64;
   if (n_rep >= 8) lo = 128;
   if (n_rep >= 16) lo = 256;
   if (n_rep >= 32) lo = 512;
-  int chunk = 1024;
-  while (chunk > lo && (long long)B * Hkv * ((T_max + chunk - 1) / chunk) < target_units) chunk /= 2;
-  return chunk;
+  const long long want = (long long)B * Hkv * T_max / 2048 / 64 * 64;
+  return (int)(want < lo ? lo : (want > 1024 ? 1024 : want));
 }
 
 bool valid_split(int split) { return split == 0 || (split >= 64 && split <= 65536 && split % 64 == 0); }

@@ -151,42 +151,101 @@ struct Unit {
   int j, n;    // chunk index and chunks of the sequence
 };
 
+// Queue: ticket of the workgroup's next unit, taken ahead of time by thread 0
+// while the current unit finishes (valid = 0: not taken yet).
+struct NextUnit {
+  unsigned v;
+  int valid;
+};
+
+// Units 0 .. gridDim.x - 1 go to the workgroups of the same index; the queue
+// hands out the rest: unit = gridDim.x + the counter before the increment.
+// (An increment, atomic_inc with no wrap bound, rather than an add: the add's
+// wave-level combining would wait for the result right where it is issued.)
+__device__ __forceinline__ unsigned take_ticket(const GqaDecodeArgs& a) {
+  return __builtin_amdgcn_atomic_inc32(a.queue, 0xffffffffu, __ATOMIC_RELAXED, "agent");
+}
+
 // Per-workgroup shared state of the schedule.
 struct UnitShared {
   unsigned unit;     // queue: unit taken by this workgroup
   int b;             // queue: its sequence
-  unsigned wsum[4];  // per-wave sums of the plan's prefix scan
+  unsigned wsum[8];  // per-wave sums of the plan's prefix scans
 };
 
-// Block-wide exclusive prefix sum of n_b = ceil(L_b / chunk) into pre[0..B]
-// (B <= kQueueMaxB, four sequences per thread); returns pre[B].
-__device__ unsigned chunk_prefix(const GqaDecodeArgs& a, unsigned* pre, unsigned* wsum) {
+// Blocks of `chunk` positions of one (sequence, KV head): nb = ceil(L / chunk).
+// In the queue schedule the first kBigBlocks * nbig blocks form big units of
+// kBigBlocks blocks, nbig = 3 nb / (4 kBigBlocks); the rest are single-block
+// units, handed out after every big unit of the batch.  The end of the queue
+// is thus made of small units, so the workgroups run out of work at about the
+// same time.  Partials are stored at the slot of their first block.
+constexpr int kBigBlocks = 4;
+
+struct Split {
+  int nb;    // blocks
+  int nbig;  // big units (0 in the fixed schedule)
+  __device__ int parts() const { return nb - (kBigBlocks - 1) * nbig; }
+  // block index (= slot) of partial p
+  __device__ int slot(int p) const { return p < nbig ? kBigBlocks * p : p + (kBigBlocks - 1) * nbig; }
+};
+
+__device__ __forceinline__ Split split_of(const GqaDecodeArgs& a, int L) {
+  Split sp;
+  sp.nb = (L + a.chunk - 1) / a.chunk;
+  sp.nbig = a.use_queue ? 3 * sp.nb / (4 * kBigBlocks) : 0;
+  return sp;
+}
+
+// Block-wide exclusive prefix sums over the batch (B <= kQueueMaxB, four
+// sequences per thread) of the big-unit counts into preB[0..B] and of the
+// single-block unit counts into preS[0..B]; the clamped lengths into len[0..B).
+__device__ void unit_prefix(const GqaDecodeArgs& a, unsigned* preB, unsigned* preS, int* len, unsigned* wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  unsigned v[4], tsum = 0;
+  unsigned vb[4], vs[4], tb = 0, ts = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int b = 4 * tid + i;
-    v[i] = b < a.B ? (unsigned)((clamp_len(a.lens[b], a.T_max) + a.chunk - 1) / a.chunk) : 0u;
-    tsum += v[i];
+    const int L = b < a.B ? clamp_len(a.lens[b], a.T_max) : 0;
+    if (b < a.B) len[b] = L;
+    const Split sp = split_of(a, L);
+    vb[i] = (unsigned)sp.nbig;
+    vs[i] = (unsigned)(sp.nb - kBigBlocks * sp.nbig);
+    tb += vb[i];
+    ts += vs[i];
   }
-  unsigned inc = tsum;  // inclusive scan over the wave
+  unsigned ib = tb, is = ts;  // inclusive scans over the wave
   for (int off = 1; off < 64; off <<= 1) {
-    const unsigned y = __shfl_up(inc, off);
-    if (lane >= off) inc += y;
+    const unsigned yb = __shfl_up(ib, off), ys = __shfl_up(is, off);
+    if (lane >= off) {
+      ib += yb;
+      is += ys;
+    }
   }
-  if (lane == 63) wsum[wave] = inc;
+  if (lane == 63) {
+    wsum[wave] = ib;
+    wsum[4 + wave] = is;
+  }
   __syncthreads();
-  unsigned run = inc - tsum;
-  for (int w = 0; w < wave; ++w) run += wsum[w];
+  unsigned rb = ib - tb, rs = is - ts;
+  for (int w = 0; w < wave; ++w) {
+    rb += wsum[w];
+    rs += wsum[4 + w];
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int b = 4 * tid + i;
-    if (b < a.B) pre[b] = run;
-    run += v[i];
+    if (b < a.B) {
+      preB[b] = rb;
+      preS[b] = rs;
+    }
+    rb += vb[i];
+    rs += vs[i];
   }
-  if (tid == 0) pre[a.B] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  if (tid == 0) {
+    preB[a.B] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    preS[a.B] = wsum[4] + wsum[5] + wsum[6] + wsum[7];
+  }
   __syncthreads();
-  return pre[a.B];
 }
 
 // Writes one output element pair (out_dtype) of row `row` (= b*Hq + h).
@@ -200,23 +259,37 @@ __device__ __forceinline__ void store_out2(const GqaDecodeArgs& a, size_t row, i
   }
 }
 
-// Unit epilogue: ob[n_rep][D] (normalised output of the unit) and lse[n_rep]
-// (its log2-sum-exp) are in LDS.  Ends with a barrier (ob is reused).
-template <int D>
-__device__ void store_unit(const GqaDecodeArgs& a, const Unit& u, const float* ob, const float* lse) {
+// Unit epilogue: the normalised output of the unit is the sum of NS slices
+// ob[s * slice + head * D + dim] in LDS, its log2-sum-exp lse[n_rep].  Ends
+// with a barrier (ob is reused).
+template <int D, int NS = 1>
+__device__ void store_unit(const GqaDecodeArgs& a, const Unit& u, const float* ob, const float* lse, int slice = 0) {
   const int tid = threadIdx.x, n_rep = a.n_rep;
   constexpr int D2 = D / 2;
+  auto value = [&](int hd, int d2) {
+    float2 v = *reinterpret_cast<const float2*>(ob + hd * D + 2 * d2);
+#pragma unroll
+    for (int sl = 1; sl < NS; ++sl) {
+      const float2 w = *reinterpret_cast<const float2*>(ob + sl * slice + hd * D + 2 * d2);
+      v.x += w.x;
+      v.y += w.y;
+    }
+    return v;
+  };
   if (u.n == 1) {
     const size_t row0 = (size_t)u.b * a.Hq + (size_t)u.g * n_rep;
     for (int e = tid; e < n_rep * D2; e += 256) {
       const int hd = e / D2, d2 = e - hd * D2;
-      const float2 v = *reinterpret_cast<const float2*>(ob + hd * D + 2 * d2);
+      const float2 v = value(hd, d2);
       store_out2(a, row0 + hd, 2 * d2, v.x, v.y);
     }
   } else {
     const size_t slot = ((size_t)u.b * a.Hkv + u.g) * a.n_chunks + u.j;
     float2* o_ws = reinterpret_cast<float2*>(a.o_part + slot * n_rep * D);
-    for (int e = tid; e < n_rep * D2; e += 256) o_ws[e] = *reinterpret_cast<const float2*>(ob + 2 * e);
+    for (int e = tid; e < n_rep * D2; e += 256) {
+      const int hd = e / D2, d2 = e - hd * D2;
+      o_ws[e] = value(hd, d2);
+    }
     for (int hd = tid; hd < n_rep; hd += 256) a.lse[slot * n_rep + hd] = lse[hd];
   }
   __syncthreads();
@@ -232,58 +305,118 @@ __device__ void zero_rows(const GqaDecodeArgs& a, int b, int g) {
   }
 }
 
-// Drives the schedule: for every unit of this workgroup, process(unit) leaves
-// the unit's normalised output in ob and its log2-sum-exp in lse (LDS), and
-// store_unit publishes it.  `pre` (queue only) holds kQueueMaxB + 1 unsigned in
-// LDS for the whole kernel.
+// Fixed schedule: the unit of this workgroup, grid (Hkv, n_chunks, B).  Returns
+// false (after zeroing the group's output rows for an empty sequence) when the
+// workgroup has no unit.
+template <int D>
+__device__ bool fixed_unit(const GqaDecodeArgs& a, Unit& u) {
+  const int g = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int L = clamp_len(a.lens[b], a.T_max);
+  if (L == 0) {
+    if (j == 0) zero_rows<D>(a, b, g);
+    return false;
+  }
+  u.b = b;
+  u.g = g;
+  u.j = j;
+  u.t0 = j * a.chunk;
+  if (u.t0 >= L) return false;
+  u.t1 = min(u.t0 + a.chunk, L);
+  u.n = split_of(a, L).parts();
+  return true;
+}
+
+// Queue schedule: unit counts of the batch (big units come first) and the
+// plan's LDS arrays.
+struct QueuePlan {
+  unsigned n_big, n_units;
+  const unsigned* preB;  // [B + 1] big units before sequence b (per KV head)
+  const unsigned* preS;  // [B + 1] single-block units before sequence b
+  const int* len;        // [B] clamped cache lengths
+};
+
+// LDS of the queue plan, in unsigned: preB, preS, len.
+constexpr int kQueuePlanWords = 3 * (kQueueMaxB + 1);
+
+// Plans the queue (prefix sums in LDS) and zeroes the output rows of empty
+// sequences (workgroups take them round-robin).
+template <int D>
+__device__ QueuePlan queue_plan(const GqaDecodeArgs& a, unsigned* lds, UnitShared& sh) {
+  unsigned* preB = lds;
+  unsigned* preS = lds + kQueueMaxB + 1;
+  int* len = reinterpret_cast<int*>(lds + 2 * (kQueueMaxB + 1));
+  unit_prefix(a, preB, preS, len, sh.wsum);
+  for (int b = blockIdx.x; b < a.B; b += gridDim.x)
+    if (len[b] == 0)
+      for (int g = 0; g < a.Hkv; ++g) zero_rows<D>(a, b, g);
+  QueuePlan pl;
+  pl.n_big = (unsigned)uniform((int)preB[a.B]) * (unsigned)a.Hkv;
+  pl.n_units = pl.n_big + (unsigned)uniform((int)preS[a.B]) * (unsigned)a.Hkv;
+  pl.preB = preB;
+  pl.preS = preS;
+  pl.len = len;
+  return pl;
+}
+
+// Units are numbered sequence-major, then block, then KV head: big units first,
+// then the single-block ones.  The thread that finds the sequence b of unit x
+// (Hkv*pre[b] <= x' < Hkv*pre[b+1]) writes it to sh.b; a barrier must follow.
+__device__ __forceinline__ void find_sequence(const GqaDecodeArgs& a, const QueuePlan& pl, unsigned x,
+                                              UnitShared& sh) {
+  const bool big = x < pl.n_big;
+  const unsigned* pr = big ? pl.preB : pl.preS;
+  const unsigned xr = big ? x : x - pl.n_big;
+  const unsigned Hkv = (unsigned)a.Hkv;
+  for (int b = threadIdx.x; b < a.B; b += 256)
+    if (pr[b] * Hkv <= xr && xr < pr[b + 1] * Hkv) sh.b = b;
+}
+
+// Unit x of sequence b (uniform values).
+__device__ __forceinline__ Unit queue_unit(const GqaDecodeArgs& a, const QueuePlan& pl, unsigned x, int b) {
+  const bool big = x < pl.n_big;
+  const unsigned* pr = big ? pl.preB : pl.preS;
+  const unsigned xr = big ? x : x - pl.n_big;
+  const unsigned Hkv = (unsigned)a.Hkv;
+  Unit u;
+  u.b = b;
+  const int L = uniform(pl.len[b]);
+  const Split sp = split_of(a, L);
+  const unsigned r = xr - (unsigned)uniform((int)pr[b]) * Hkv;
+  const int k = (int)(r / Hkv);
+  u.g = (int)(r - (unsigned)k * Hkv);
+  u.j = big ? kBigBlocks * k : kBigBlocks * sp.nbig + k;
+  u.n = sp.parts();
+  u.t0 = u.j * a.chunk;
+  u.t1 = min(u.t0 + (big ? kBigBlocks : 1) * a.chunk, L);
+  return u;
+}
+
+// Drives the schedule for a kernel without cross-unit prefetch: for every unit
+// of this workgroup, process(unit, next) leaves the unit's normalised output in
+// ob and its log2-sum-exp in lse (LDS), and store_unit publishes it.  `pre`
+// (queue only) holds kQueuePlanWords unsigned of LDS for the whole kernel.
 template <int D, bool QUEUE, typename Process>
 __device__ void run_units(const GqaDecodeArgs& a, UnitShared& sh, unsigned* pre, float* ob, float* lse,
                           Process&& process) {
   if constexpr (!QUEUE) {
-    const int g = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-    const int L = clamp_len(a.lens[b], a.T_max);
-    if (L == 0) {
-      if (j == 0) zero_rows<D>(a, b, g);
-      return;
-    }
     Unit u;
-    u.b = b;
-    u.g = g;
-    u.j = j;
-    u.t0 = j * a.chunk;
-    if (u.t0 >= L) return;
-    u.t1 = min(u.t0 + a.chunk, L);
-    u.n = (L + a.chunk - 1) / a.chunk;
-    process(u);
+    if (!fixed_unit<D>(a, u)) return;
+    NextUnit nx = {0u, 0};
+    process(u, nx);
     store_unit<D>(a, u, ob, lse);
   } else {
-    const int tid = threadIdx.x, Hkv = a.Hkv;
-    const unsigned per_head = uniform((int)chunk_prefix(a, pre, sh.wsum));
-    // empty sequences: workgroups take them round-robin
-    for (int b = blockIdx.x; b < a.B; b += gridDim.x)
-      if (pre[b + 1] == pre[b])
-        for (int g = 0; g < Hkv; ++g) zero_rows<D>(a, b, g);
-    const unsigned n_units = per_head * (unsigned)Hkv;
-    for (;;) {
-      if (tid == 0) sh.unit = __hip_atomic_fetch_add(a.queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const QueuePlan plan = queue_plan<D>(a, pre, sh);
+    unsigned x = blockIdx.x;
+    while (x < plan.n_units) {
+      find_sequence(a, plan, x, sh);
       __syncthreads();
-      const unsigned x = (unsigned)uniform((int)sh.unit);
-      if (x >= n_units) break;
-      // sequence of unit x: Hkv*pre[b] <= x < Hkv*pre[b+1]
-      for (int b = tid; b < a.B; b += 256)
-        if (pre[b] * Hkv <= x && x < pre[b + 1] * Hkv) sh.b = b;
+      const Unit u = queue_unit(a, plan, x, uniform(sh.b));
+      NextUnit nx = {0u, 0};
+      process(u, nx);
+      store_unit<D>(a, u, ob, lse);  // ends with a barrier: every thread has read sh.b and sh.unit
+      if (threadIdx.x == 0) sh.unit = gridDim.x + (nx.valid ? nx.v : take_ticket(a));
       __syncthreads();
-      Unit u;
-      u.b = uniform(sh.b);
-      const unsigned p0 = (unsigned)uniform((int)pre[u.b]);
-      const unsigned r = x - p0 * Hkv;
-      u.j = (int)(r / (unsigned)Hkv);
-      u.g = (int)(r - (unsigned)u.j * Hkv);
-      u.n = uniform((int)(pre[u.b + 1] - p0));
-      u.t0 = u.j * a.chunk;
-      u.t1 = min(u.t0 + a.chunk, uniform(clamp_len(a.lens[u.b], a.T_max)));
-      process(u);
-      store_unit<D>(a, u, ob, lse);
+      x = (unsigned)uniform((int)sh.unit);
     }
   }
 }
@@ -296,17 +429,17 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
   __shared__ float m_s[64], inv_s[64];
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   if (a.use_queue && g == 0 && b == 0 && tid == 0) *a.queue = 0u;
-  const int L = clamp_len(a.lens[b], a.T_max);
-  const int n = (L + a.chunk - 1) / a.chunk;
+  const Split sp = split_of(a, clamp_len(a.lens[b], a.T_max));
+  const int n = sp.parts();
   if (n <= 1) return;  // written by the decode kernel
   const int n_rep = a.n_rep, D2 = a.D / 2;
   const size_t s0 = ((size_t)b * a.Hkv + g) * a.n_chunks;
   const float* lse = a.lse + s0 * n_rep;
   for (int hd = tid; hd < n_rep; hd += 256) {
     float M = kNegInf;
-    for (int j = 0; j < n; ++j) M = fmaxf(M, lse[(size_t)j * n_rep + hd]);
+    for (int p = 0; p < n; ++p) M = fmaxf(M, lse[(size_t)sp.slot(p) * n_rep + hd]);
     float S = 0.f;
-    for (int j = 0; j < n; ++j) S += exp2_fast(lse[(size_t)j * n_rep + hd] - M);
+    for (int p = 0; p < n; ++p) S += exp2_fast(lse[(size_t)sp.slot(p) * n_rep + hd] - M);
     m_s[hd] = M;
     inv_s[hd] = 1.f / S;
   }
@@ -324,7 +457,7 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
       float2 v[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int j = min(j0 + k, n - 1);
+        const int j = sp.slot(min(j0 + k, n - 1));
         w[k] = lse[(size_t)j * n_rep + hd];
         v[k] = op[(size_t)j * jstride + e];
       }
@@ -342,14 +475,12 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // bf16 inputs, MFMA.  HB blocks of 16 query heads (n_rep <= 16 * HB).
-// Waves per SIMD the register allocation targets: four fit head_dim <= 96 with
-// the next tile in flight; head_dim 128 needs up to 168 registers (three waves).
-#ifndef ATTN_DECODE_WAVES_PER_EU_D128
-#define ATTN_DECODE_WAVES_PER_EU_D128 3
-#endif
+// Waves per SIMD the register allocation targets (the fixed schedule runs
+// several workgroups per compute unit): four fit head_dim 64, head_dim 96 and
+// 128 need up to 168 registers (three waves) with the next tile in flight.
 template <int D, int HB, bool QUEUE>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(HB > 1 ? 1 : (D >= 96 ? ATTN_DECODE_WAVES_PER_EU_D128 : 4))))
+__attribute__((amdgpu_waves_per_eu(HB > 1 ? 1 : (D >= 96 ? 3 : 4))))
 void gqa_decode_bf16(GqaDecodeArgs a) {
   static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
   constexpr int KC = D / 32;           // 32-wide dim chunks (QK contraction)
@@ -360,34 +491,72 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   constexpr int kLanesPerRow = kUnits <= 8 ? 8 : 16;          // lanes that load one row
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;
   constexpr int kLoads = kDecodeTileTokens / kRowsPerLoad;   // 16-byte loads per lane per tile
+  constexpr int kStep = kDecodeWaves * kDecodeTileTokens;    // positions per round of the four waves
   constexpr int kVtElems = kDecodeWaves * kDecodeTileTokens * VP;
-  // epilogue scratch (floats): m and l per wave and head, [HB*16][D] outputs, lse
-  static_assert(2 * kDecodeWaves * HB * 16 * 4 + HB * 16 * D * 4 + HB * 16 * 4 <= kVtElems * 2, "scratch");
+  // epilogue scratch (floats): m and l per wave and head, kSlices x [HB*16][D]
+  // outputs, lse.  Where the tile LDS holds one output slice per wave, the waves
+  // write their scaled outputs at once and the store sums the slices;
+  // otherwise they add into one slice in turn.
+  constexpr int kSliceFloats = HB * 16 * D;
+  constexpr bool kSliced = 2 * kDecodeWaves * HB * 16 * 4 + kDecodeWaves * kSliceFloats * 4 + HB * 16 * 4 <= kVtElems * 2;
+  constexpr int kSlices = kSliced ? kDecodeWaves : 1;
+  static_assert(2 * kDecodeWaves * HB * 16 * 4 + kSlices * kSliceFloats * 4 + HB * 16 * 4 <= kVtElems * 2, "scratch");
   __shared__ __attribute__((aligned(16))) u16 smem[kVtElems];
-  __shared__ unsigned pre[QUEUE ? kQueueMaxB + 1 : 1];
+  __shared__ unsigned pre[QUEUE ? kQueuePlanWords : 1];
   __shared__ UnitShared sh;
 
-  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6), lane = tid & 63;
   const int row = lane & 15, grp = lane >> 4;
   const int n_rep = a.n_rep;
   float* mw = reinterpret_cast<float*>(smem);   // [waves][HB*16]
   float* lw = mw + kDecodeWaves * HB * 16;      // [waves][HB*16]
-  float* ob = lw + kDecodeWaves * HB * 16;      // [HB*16][D]
-  float* lse_s = ob + HB * 16 * D;              // [HB*16]
+  float* ob = lw + kDecodeWaves * HB * 16;      // [kSlices][HB*16][D]
+  float* lse_s = ob + kSlices * kSliceFloats;   // [HB*16]
   u16* vt = smem + wave * kDecodeTileTokens * VP;
   const size_t tok_stride = (size_t)a.Hkv * D;
+  const int row_bytes = uniform((int)(tok_stride * 2));
   // this lane's row within a load and its 16-byte unit in the row
   const int lrow = lane / kLanesPerRow, lunit = min(lane % kLanesPerRow, kUnits - 1);
-  const unsigned row_off = (unsigned)(lrow * tok_stride * 2 + 16 * lunit);
+  const unsigned row_off = (unsigned)(lrow * row_bytes + 16 * lunit);
 
-  auto process = [&](const Unit& pc_) {
-    const int pb = uniform(pc_.b), pg = uniform(pc_.g), pt0 = uniform(pc_.t0);
-    const u16* qp = static_cast<const u16*>(a.q) + ((size_t)pb * a.Hq + (size_t)pg * n_rep) * D;
-    const u16* kp = static_cast<const u16*>(a.k) + ((size_t)pb * a.T_max * a.Hkv + pg) * D;
-    const u16* vp = static_cast<const u16*>(a.v) + ((size_t)pb * a.T_max * a.Hkv + pg) * D;
-    const int c1 = uniform(pc_.t1);
-    // Q^T as the B operand: lane holds Q[head = 16hb + row][dims 32c + 8grp .. +8]
-    bf16x8 qop[HB][KC];
+  auto k_head = [&](const Unit& u) { return static_cast<const u16*>(a.k) + ((size_t)u.b * a.T_max * a.Hkv + u.g) * D; };
+  auto v_head = [&](const Unit& u) { return static_cast<const u16*>(a.v) + ((size_t)u.b * a.T_max * a.Hkv + u.g) * D; };
+
+  // K and V tiles of 32 positions are read in row order with streaming
+  // (non-temporal) buffer loads: lane group lane / kLanesPerRow of load i
+  // fetches row kRowsPerLoad * i + lane / kLanesPerRow, each lane one 16-byte
+  // unit (head_dim 96: lanes past the 12th unit repeat it), so a load covers
+  // whole rows.  Each load has its own buffer resource starting at its first
+  // row and ending with row c1 - 1: rows at or past the unit end read as zeros
+  // and cost no memory traffic, so loads ahead can be issued unconditionally.
+  auto load_rows = [&](bf16x8 (&r)[kLoads], const u16* head0, int t0, int c1) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int t = t0 + kRowsPerLoad * i;
+      // rows of this load before c1, 0..kRowsPerLoad; bytes up to the end of the last
+      // (row_bytes >= 2 * D, so no rows gives a non-positive count)
+      const int rows = min(max(c1 - t, 0), kRowsPerLoad);
+      const int n = max(rows * row_bytes - row_bytes + 2 * D, 0);
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(head0 + (size_t)t * tok_stride), (short)0, n,
+                                                        0x00020000);
+      r[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)row_off, 0, kStreamPolicy));
+    }
+  };
+  // The same registers written to this wave's LDS tile, row pitch `pitch`.
+  auto store_rows = [&](const bf16x8 (&r)[kLoads], int pitch) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+      *reinterpret_cast<u16x8*>(vt + (kRowsPerLoad * i + lrow) * pitch + 8 * lunit) = __builtin_bit_cast(u16x8, r[i]);
+  };
+
+  // Registers that carry a unit's inputs: Q^T as the B operand (lane holds
+  // Q[head = 16hb + row][dims 32c + 8grp .. +8]) and this wave's next K/V tile.
+  bf16x8 qop[HB][KC];
+  bf16x8 kr[kLoads], vr[kLoads];
+  // Requests the query block of unit u and this wave's first tile of it.
+  auto begin_unit = [&](const Unit& u) {
+    const u16* qp = static_cast<const u16*>(a.q) + ((size_t)u.b * a.Hq + (size_t)u.g * n_rep) * D;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       const int head = hb * 16 + row;
@@ -396,8 +565,17 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
         qop[hb][c] = head < n_rep ? load_bf16x8(qp + (size_t)head * D + 32 * c + 8 * grp)
                                   : __builtin_bit_cast(bf16x8, u16x8{0, 0, 0, 0, 0, 0, 0, 0});
     }
-    float m[HB], lsum[HB];
-    f32x4 o[HB][DW];  // O^T: lane holds dims 16w + 4grp + i of head 16hb + row
+    load_rows(kr, k_head(u), u.t0 + wave * kDecodeTileTokens, u.t1);
+    load_rows(vr, v_head(u), u.t0 + wave * kDecodeTileTokens, u.t1);
+  };
+
+  // Streams unit u (begin_unit(u) issued): this wave's online-softmax state.
+  float m[HB], lsum[HB];
+  f32x4 o[HB][DW];  // O^T: lane holds dims 16w + 4grp + i of head 16hb + row
+  auto stream_unit = [&](const Unit& u, NextUnit& nx) {
+    const u16* kp = k_head(u);
+    const u16* vp = v_head(u);
+    const int c1 = u.t1;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       m[hb] = kNegInf;
@@ -405,55 +583,28 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
 #pragma unroll
       for (int w = 0; w < DW; ++w) o[hb][w] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // K and V tiles of 32 positions are read in row order with streaming
-    // (non-temporal) buffer loads: lane group lane / kLanesPerRow of load i
-    // fetches row kRowsPerLoad * i + lane / kLanesPerRow, each lane one 16-byte
-    // unit (head_dim 96: lanes past the 12th unit repeat it), so a load covers
-    // whole rows.  Each load has its own buffer resource starting at its first
-    // row and ending with row c1 - 1: rows at or past the unit end read as zeros
-    // and cost no memory traffic, so the one-tile-ahead loads below can be
-    // issued unconditionally.
-    const int row_bytes = uniform((int)(tok_stride * 2));
-    auto load_rows = [&](bf16x8 (&r)[kLoads], const u16* head0, int t0) {
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i) {
-        const int t = t0 + kRowsPerLoad * i;
-        // rows of this load before c1, 0..kRowsPerLoad; bytes up to the end of the last
-        // (row_bytes >= 2 * D, so no rows gives a non-positive count)
-        const int rows = min(max(c1 - t, 0), kRowsPerLoad);
-        const int n = max(rows * row_bytes - row_bytes + 2 * D, 0);
-        const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(head0 + (size_t)t * tok_stride), (short)0, n,
-                                                          0x00020000);
-        r[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)row_off, 0, kStreamPolicy));
+    // Per tile: K(t) -> LDS; scores from LDS; K(t + kStep) requested; V(t) ->
+    // LDS (same region); V(t + kStep) requested; softmax; PV from LDS.
+    for (int t0 = u.t0 + wave * kDecodeTileTokens; t0 < c1; t0 += kStep) {
+      if constexpr (QUEUE) {
+        // second-to-last tile of wave 0 (or its only one): take the workgroup's
+        // next unit, so the queue's round trip overlaps the end of this one
+        if (wave == 0 && t0 + 2 * kStep >= c1 && lane == 0 && !nx.valid) {
+          nx.v = take_ticket(a);
+          nx.valid = 1;
+        }
       }
-    };
-    // The same registers written to this wave's LDS tile, row pitch `pitch`.
-    auto store_rows = [&](const bf16x8 (&r)[kLoads], int pitch) {
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i)
-        *reinterpret_cast<u16x8*>(vt + (kRowsPerLoad * i + lrow) * pitch + 8 * lunit) = __builtin_bit_cast(u16x8, r[i]);
-    };
-    constexpr int kStep = kDecodeWaves * kDecodeTileTokens;
-    int t0 = pt0 + wave * kDecodeTileTokens;
-    bf16x8 kr[kLoads], vr[kLoads];
-    if (t0 < c1) {
-      load_rows(kr, kp, t0);
-      load_rows(vr, vp, t0);
-    }
-    // Per tile: K(t) -> LDS; scores from LDS; K(t+1) requested; V(t) -> LDS
-    // (same region); V(t+1) requested; softmax; PV from LDS.  About one tile
-    // stays in flight per wave.
-    for (; t0 < c1; t0 += kStep) {
       store_rows(kr, KP);
       wave_lds_sync();
       // Scores: lane holds S^T[token 16u + 4grp + i][head 16hb + row]; the A
       // operand (token 16u + row, dims 32c + 8grp .. +8) comes from LDS.
       float sc[HB][2][4];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int s = 0; s < 2; ++s) {
         bf16x8 ka[KC];
 #pragma unroll
-        for (int c = 0; c < KC; ++c) ka[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(vt + (16 * u + row) * KP + 32 * c + 8 * grp));
+        for (int c = 0; c < KC; ++c)
+          ka[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(vt + (16 * s + row) * KP + 32 * c + 8 * grp));
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -461,26 +612,27 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
           for (int c = 0; c < KC; ++c) acc = mfma_16x16x32(ka[c], qop[hb][c], acc);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int tok = t0 + 16 * u + 4 * grp + i;
-            sc[hb][u][i] = tok < c1 ? acc[i] * a.scale_log2e : kNegInf;
+            const int tok = t0 + 16 * s + 4 * grp + i;
+            sc[hb][s][i] = tok < c1 ? acc[i] * a.scale_log2e : kNegInf;
           }
         }
       }
-      // K(t+1) after the scores: its registers are then free (the tile is in LDS)
+      // the next K tile after the scores: its registers are then free (this
+      // tile is in LDS)
       __builtin_amdgcn_sched_barrier(0);
-      load_rows(kr, kp, t0 + kStep);
+      load_rows(kr, kp, t0 + kStep, c1);
       wave_lds_sync();
       store_rows(vr, VP);
-      load_rows(vr, vp, t0 + kStep);
+      load_rows(vr, vp, t0 + kStep, c1);
       // Online softmax per head; P^T as the B operand of the PV product.
       bf16x8 pop[HB];
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         float mt = kNegInf;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sc[hb][u][i]);
+          for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sc[hb][s][i]);
         mt = max_xor16(mt);
         mt = max_xor32(mt);
         const float mn = fmaxf(m[hb], mt);  // finite: the tile's first token is valid
@@ -488,12 +640,12 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
         m[hb] = mn;
         float ps = 0.f;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float p = exp2_fast(sc[hb][u][i] - mn);
+            const float p = exp2_fast(sc[hb][s][i] - mn);
             ps += p;
-            pop[hb][4 * u + i] = (__bf16)p;
+            pop[hb][4 * s + i] = (__bf16)p;
           }
         lsum[hb] = lsum[hb] * alpha + ps;
 #pragma unroll
@@ -516,21 +668,16 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
       }
       wave_lds_sync();
     }
-    // ---- merge the four waves into ob / lse_s ----
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       lsum[hb] = sum_xor16(lsum[hb]);
       lsum[hb] = sum_xor32(lsum[hb]);
     }
-    __syncthreads();  // every wave is done with its V region
-    if (grp == 0) {
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        mw[wave * HB * 16 + hb * 16 + row] = m[hb];
-        lw[wave * HB * 16 + hb * 16 + row] = lsum[hb];
-      }
-    }
-    __syncthreads();
+  };
+
+  // Merges the four waves' states of unit u into ob / lse_s and stores it.
+  // Entered after a barrier that follows the waves' mw / lw writes.
+  auto finish_unit = [&](const Unit& u) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       const int hd = hb * 16 + row;
@@ -545,22 +692,81 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
       for (int w = 0; w < DW; ++w) o[hb][w] *= f;
       if (wave == 0 && grp == 0) lse_s[hd] = M + __log2f(Lt);
     }
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      if (wave == w) {
+    if constexpr (kSliced) {
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
+      for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-          for (int dw = 0; dw < DW; ++dw) {
-            float4* dst = reinterpret_cast<float4*>(ob + (hb * 16 + row) * D + 16 * dw + 4 * grp);
-            const float4 cur = w == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : *dst;
-            *dst = make_float4(cur.x + o[hb][dw][0], cur.y + o[hb][dw][1], cur.z + o[hb][dw][2],
-                               cur.w + o[hb][dw][3]);
-          }
-      }
+        for (int dw = 0; dw < DW; ++dw)
+          *reinterpret_cast<float4*>(ob + wave * kSliceFloats + (hb * 16 + row) * D + 16 * dw + 4 * grp) =
+              make_float4(o[hb][dw][0], o[hb][dw][1], o[hb][dw][2], o[hb][dw][3]);
       __syncthreads();
+    } else {
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        if (wave == w) {
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int dw = 0; dw < DW; ++dw) {
+              float4* dst = reinterpret_cast<float4*>(ob + (hb * 16 + row) * D + 16 * dw + 4 * grp);
+              const float4 cur = w == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : *dst;
+              *dst = make_float4(cur.x + o[hb][dw][0], cur.y + o[hb][dw][1], cur.z + o[hb][dw][2],
+                                 cur.w + o[hb][dw][3]);
+            }
+        }
+        __syncthreads();
+      }
+    }
+    store_unit<D, kSlices>(a, u, ob, lse_s, kSliceFloats);  // ends with a barrier (ob is reused)
+  };
+  auto publish_state = [&]() {
+    if (grp == 0) {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        mw[wave * HB * 16 + hb * 16 + row] = m[hb];
+        lw[wave * HB * 16 + hb * 16 + row] = lsum[hb];
+      }
     }
   };
-  run_units<D, QUEUE>(a, sh, pre, ob, lse_s, process);
+
+  if constexpr (!QUEUE) {
+    Unit u;
+    if (!fixed_unit<D>(a, u)) return;
+    begin_unit(u);
+    NextUnit nx = {0u, 0};
+    stream_unit(u, nx);
+    __syncthreads();  // every wave is done with its LDS tile
+    publish_state();
+    __syncthreads();
+    finish_unit(u);
+  } else {
+    const QueuePlan plan = queue_plan<D>(a, pre, sh);
+    unsigned x = blockIdx.x;
+    if (x >= plan.n_units) return;
+    find_sequence(a, plan, x, sh);
+    __syncthreads();
+    Unit u = queue_unit(a, plan, x, uniform(sh.b));
+    begin_unit(u);
+    for (;;) {
+      NextUnit nx = {0u, 0};
+      stream_unit(u, nx);
+      if (tid == 0) sh.unit = gridDim.x + (nx.valid ? nx.v : take_ticket(a));
+      __syncthreads();  // every wave is done with its LDS tile; the next ticket is visible
+      x = (unsigned)uniform((int)sh.unit);
+      const bool more = x < plan.n_units;
+      if (more) find_sequence(a, plan, x, sh);
+      publish_state();
+      __syncthreads();
+      // request the next unit's inputs before this one is merged and stored
+      Unit un = u;
+      if (more) {
+        un = queue_unit(a, plan, x, uniform(sh.b));
+        begin_unit(un);
+      }
+      finish_unit(u);
+      if (!more) break;
+      u = un;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -572,7 +778,7 @@ __global__ __launch_bounds__(256) void gqa_decode_f32(GqaDecodeArgs a) {
   __shared__ float mw[kDecodeWaves][NR], lw[kDecodeWaves][NR];
   __shared__ __attribute__((aligned(16))) float ob[NR * D];
   __shared__ float lse_s[NR];
-  __shared__ unsigned pre[QUEUE ? kQueueMaxB + 1 : 1];
+  __shared__ unsigned pre[QUEUE ? kQueuePlanWords : 1];
   __shared__ UnitShared sh;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -580,7 +786,7 @@ __global__ __launch_bounds__(256) void gqa_decode_f32(GqaDecodeArgs a) {
   const int n_rep = a.n_rep;
   const size_t tok_stride = (size_t)a.Hkv * D;
 
-  auto process = [&](const Unit& pc) {
+  auto process = [&](const Unit& pc, NextUnit&) {
     const float* qp = static_cast<const float*>(a.q) + ((size_t)pc.b * a.Hq + (size_t)pc.g * n_rep) * D + col * E;
     const float* kp = static_cast<const float*>(a.k) + ((size_t)pc.b * a.T_max * a.Hkv + pc.g) * D + col * E;
     const float* vp = static_cast<const float*>(a.v) + ((size_t)pc.b * a.T_max * a.Hkv + pc.g) * D + col * E;
@@ -698,34 +904,44 @@ int resident_per_cu(const void* kernel) {
 }
 
 // Launches kernel(a).  A queue grid is trimmed to the workgroups that are
-// resident at once (more would only wait for the first ones to drain the queue).
+// resident at once (more would only wait for the first ones to drain the queue),
+// and to at most max_per_cu of them per compute unit.
 template <typename Kernel>
-hipError_t launch_one(Kernel kernel, const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
+hipError_t launch_one(Kernel kernel, const GqaDecodeArgs& a, dim3 grid, hipStream_t st, int max_per_cu) {
   if (a.use_queue) {
-    const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kernel));
+    int per_cu = resident_per_cu(reinterpret_cast<const void*>(kernel));
+    if (per_cu > max_per_cu) per_cu = max_per_cu;
     if (per_cu > 0 && a.cus > 0 && per_cu * a.cus < (int)grid.x) grid.x = per_cu * a.cus;
   }
   hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
+// Queue workgroups per compute unit of the MFMA kernel.  One: each keeps one
+// 32-position tile per wave in flight and the next unit's first tile requested
+// while it finishes a unit, which is enough to keep HBM busy, and with a single
+// workgroup per compute unit none of them is starved by the others (the
+// hardware favours older waves, so extra workgroups stream far slower and hold
+// their units longest).
+constexpr int kMfmaWgsPerCu = 1;
+
 template <int D, bool QUEUE>
 hipError_t launch_bf16(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
   const int hb = (a.n_rep + 15) / 16;
-  if (hb == 1) return launch_one(gqa_decode_bf16<D, 1, QUEUE>, a, grid, st);
-  if (hb == 2) return launch_one(gqa_decode_bf16<D, 2, QUEUE>, a, grid, st);
-  if (hb <= 4) return launch_one(gqa_decode_bf16<D, 4, QUEUE>, a, grid, st);
+  if (hb == 1) return launch_one(gqa_decode_bf16<D, 1, QUEUE>, a, grid, st, kMfmaWgsPerCu);
+  if (hb == 2) return launch_one(gqa_decode_bf16<D, 2, QUEUE>, a, grid, st, kMfmaWgsPerCu);
+  if (hb <= 4) return launch_one(gqa_decode_bf16<D, 4, QUEUE>, a, grid, st, kMfmaWgsPerCu);
   return hipErrorInvalidValue;
 }
 
 template <int D, bool QUEUE>
 hipError_t launch_f32(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
   const int n = a.n_rep;
-  if (n == 1) return launch_one(gqa_decode_f32<D, 1, QUEUE>, a, grid, st);
-  if (n == 2) return launch_one(gqa_decode_f32<D, 2, QUEUE>, a, grid, st);
-  if (n <= 4) return launch_one(gqa_decode_f32<D, 4, QUEUE>, a, grid, st);
-  if (n <= 8) return launch_one(gqa_decode_f32<D, 8, QUEUE>, a, grid, st);
-  if (n <= 16) return launch_one(gqa_decode_f32<D, 16, QUEUE>, a, grid, st);
+  if (n == 1) return launch_one(gqa_decode_f32<D, 1, QUEUE>, a, grid, st, 8);
+  if (n == 2) return launch_one(gqa_decode_f32<D, 2, QUEUE>, a, grid, st, 8);
+  if (n <= 4) return launch_one(gqa_decode_f32<D, 4, QUEUE>, a, grid, st, 8);
+  if (n <= 8) return launch_one(gqa_decode_f32<D, 8, QUEUE>, a, grid, st, 8);
+  if (n <= 16) return launch_one(gqa_decode_f32<D, 16, QUEUE>, a, grid, st, 8);
   return hipErrorInvalidValue;
 }
 

@@ -44,8 +44,9 @@ def test_workspace_sizes():
     slots = B * Hkv * (T // 512)
     n = attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T, 512)
     assert n == 256 + al(slots * 4 * 4) + al(slots * 4 * D * 4)
-    # split 0: the library picks 512 here (B*Hkv*ceil(T/512) = 4096 units)
-    assert attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T, 0) == n
+    # split 0: the library picks B*Hkv*T/2048 = 1024 positions per block here
+    slots = B * Hkv * (T // 1024)
+    assert attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T, 0) == 256 + al(slots * 4 * 4) + al(slots * 4 * D * 4)
     # a single chunk per sequence needs no partials
     assert attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, 512, 512) == 256
     assert attn.attn_decode_gqa_workspace_bytes(0, 32, 8, 128, 8192, 0) == 0
