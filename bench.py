@@ -13,7 +13,8 @@ One step = one pass over the three C-ABI entry points, each on its own synthetic
 
 The printed `value` is the GQA decode's KV-cache read rate (algorithmic bytes: every cached
 K and V row read once per KV head, 2*Hkv*head_dim*2 bytes per cached position) divided by
-its kernel time, measured with HIP events around each launch on the stream the library
+the time of one attn_decode_gqa call (its streaming kernel and the small kernel that merges
+the partial results), measured with HIP events around the call on the stream the library
 launches on.  The other two entry points are reported under "parts".  Inputs are resident in
 HBM before the timed region.  `cpu_baseline` times the fp64 CPU oracle (tests' checker, not
 tuned) on the same decode workload on this host.
@@ -144,7 +145,9 @@ def main():
     def run_prefill():
         attn.attn_prefill_gqa_causal(pre["q"], pre["k"], pre["v"], out=pre_out)
 
-    parts = [("gqa_decode", run_decode), ("mla_decode", run_mla), ("prefill", run_prefill)]
+    # prefill for new requests, then the decode steps of running ones (the order a serving
+    # step takes); each part is timed on its own
+    parts = [("prefill", run_prefill), ("mla_decode", run_mla), ("gqa_decode", run_decode)]
     if args.copy_calibration:
         parts.append(("copy_1GiB", lambda: copy_dst.copy_(copy_src)))
 
@@ -191,13 +194,14 @@ def main():
         "config": {
             "workload": (f"llama3_8b_gqa_decode: B={B} Hq={Hq} Hkv={Hkv} head_dim={D} T_max={T_max} "
                          f"cache_lens~U[{dspec['lens'][0]},{dspec['lens'][1]}] (sum {sum_len}) seed={dspec['seed']}, "
-                         "bf16 in, fp32 out, schedule=balanced"),
-            "step": "attn_decode_gqa + attn_decode_mla_absorbed + attn_prefill_gqa_causal, one launch each",
+                         "bf16 in, fp32 out, default schedule (device-wide unit queue, library-chosen blocks)"),
+            "step": "attn_prefill_gqa_causal, attn_decode_mla_absorbed, attn_decode_gqa: one call each, in this order",
             "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "prefill": PB * S},
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gqa_decode_bf16<128, 1, true> (attn_decode_gqa, one launch)",
+            "kernel": ("gqa_decode_bf16<128, 1, true> + gqa_decode_merge: one attn_decode_gqa call "
+                       "(two launches), timed together"),
             "achieved": round(dec_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
