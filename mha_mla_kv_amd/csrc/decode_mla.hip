@@ -349,25 +349,29 @@ __global__ __launch_bounds__(kThreads) void mla_decode_fused(MlaDecodeArgs a) {
         *reinterpret_cast<u16x8*>(bufs[k] + e) = z;
   }
   __syncthreads();
-  // q_lat operands first, then the first two slices (copies stop at the chunk end)
-  // q_lat^T as the B operand: lane holds q_lat[head row][32k + 8grp ..+8] (hi and lo)
+  // q_lat^T as the B operand: lane holds q_lat[head row][32k + 8grp ..+8] (hi and lo);
+  // requested after the first two slices (their copies are then already in flight)
   const u16* qlat = static_cast<const u16*>(a.q_lat) + (size_t)b * 2 * kHeadsPad * RW;
   bf16x8 qhi[C::KC], qlo[C::KC], qr32[C::RC > 0 ? C::RC : 1], qr16 = {};
+  auto load_q = [&]() {
 #pragma unroll
-  for (int k = 0; k < C::KC; ++k) {
-    qhi[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qlat + ln.row * RW + 32 * k + 8 * ln.grp));
-    qlo[k] = __builtin_bit_cast(bf16x8,
-                                *reinterpret_cast<const u16x8*>(qlat + (kHeadsPad + ln.row) * RW + 32 * k + 8 * ln.grp));
-  }
+    for (int k = 0; k < C::KC; ++k) {
+      qhi[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qlat + ln.row * RW + 32 * k + 8 * ln.grp));
+      qlo[k] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u16x8*>(qlat + (kHeadsPad + ln.row) * RW + 32 * k + 8 * ln.grp));
+    }
 #pragma unroll
-  for (int k = 0; k < C::RC; ++k)
-    qr32[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qlat + ln.row * RW + R + 32 * k + 8 * ln.grp));
-  if constexpr (C::R16) {  // the last 16 rope dims in contraction lanes 0..15, zero above
-    const bf16x8 v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qlat + ln.row * RW + R + 32 * C::RC + 8 * ln.grp));
-    if (ln.grp < 2) qr16 = v;
-  }
-
-  wait_vmem();  // the operands are in registers before the first copy
+    for (int k = 0; k < C::RC; ++k)
+      qr32[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qlat + ln.row * RW + R + 32 * k + 8 * ln.grp));
+    if constexpr (C::R16) {  // the last 16 rope dims in contraction lanes 0..15, zero above
+      const bf16x8 v =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qlat + ln.row * RW + R + 32 * C::RC + 8 * ln.grp));
+      if (ln.grp < 2) qr16 = v;
+    }
+    // wait here (this also covers the first two slices' copies, issued earlier):
+    // the operands are then known to be in registers everywhere in the loop
+    wait_vmem();
+  };
 
   // ---- stream the wave's slices through the ring
   WaveState<R, DR> st;
@@ -388,9 +392,13 @@ __global__ __launch_bounds__(kThreads) void mla_decode_fused(MlaDecodeArgs a) {
       slice_step<R, DR>(st, cs, rs, qhi, qlo, qr32, qr16, tw0 + k * kStep, c1, c, ln);
     }
   };
+  // the iteration that loads q_lat, as a value the compiler does not fold (a
+  // first iteration peeled off the loop would end with a wait for every copy)
+  const int k_q = __builtin_amdgcn_readfirstlane(n_steps > 0 ? -2 : -1);
   for (int k = -2; k < n_steps; k += kStages) {  // k = -2, 1, 4, ... : stage (k+2) % 3 = 0
     step(k, stg1[wave], rop1[wave], stg0[wave], rop0[wave]);
     step(k + 1, stg2[wave], rop2[wave], stg1[wave], rop1[wave]);
+    if (k == k_q) load_q();
     step(k + 2, stg0[wave], rop0[wave], stg2[wave], rop2[wave]);
   }
   wait_vmem();  // the copies past the end (zeros) land before the stages are reused
