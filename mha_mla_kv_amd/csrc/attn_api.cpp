@@ -48,17 +48,19 @@ int pow2_floor(long long x) {
 }
 
 // Positions per decode block (the work unit of the fixed schedule; the queue
-// hands out units of four blocks, then single blocks) when the caller leaves it
-// to the library: about B*Hkv*T_max / 2048 rounded down to a multiple of 64,
-// so that every one of the ~256 queue workgroups takes several units even when
-// the lengths are ragged, at most 1024, and long enough that the fp32 partial of
-// a unit (n_rep * D * 4 bytes written and read back) stays small next to its
-// cache bytes (chunk * D * 4).
+// hands out single blocks, or for large batches units of four blocks first)
+// when the caller leaves it to the library: about B*Hkv*T_max / 2048 rounded
+// down to a multiple of 64, so that every one of the ~256 queue workgroups
+// takes several units even when the lengths are ragged, at most 1024, and long
+// enough that the fp32 partial of a unit (n_rep * D * 4 bytes written and read
+// back) stays small next to its cache bytes (chunk * D * 4); with 16 or more
+// query heads per KV head the per-unit costs dominate a short chunk (measured),
+// hence the higher floors.
 int choose_chunk(int B, int Hkv, int n_rep, int T_max) {
   int lo = 64;
   if (n_rep >= 8) lo = 128;
-  if (n_rep >= 16) lo = 256;
-  if (n_rep >= 32) lo = 512;
+  if (n_rep >= 16) lo = 512;
+  if (n_rep >= 32) lo = 1024;
   const long long want = (long long)B * Hkv * T_max / 2048 / 64 * 64;
   return (int)(want < lo ? lo : (want > 1024 ? 1024 : want));
 }
@@ -224,6 +226,7 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
   a.chunk = lay.chunk;
   a.n_chunks = lay.n_chunks;
   a.use_queue = lay.queue;
+  a.big_units = 0;
   a.grid_wgs = 0;
   a.cus = 0;
   if (lay.queue) {
@@ -233,6 +236,9 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
     if (cus <= 0) return fail(ATTN_ERR_HIP, "attn_decode_gqa: cannot query the current device");
     a.cus = cus;
     a.grid_wgs = cus * 4;
+    // big units only where every workgroup still gets many units when the
+    // cache is full (B*Hkv*n_chunks blocks at most)
+    a.big_units = (long long)B * Hkv * lay.n_chunks >= 16LL * cus;
   }
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   a.scale_log2e = scale * kLog2e;

@@ -30,6 +30,7 @@ struct GqaDecodeArgs {
   int chunk;              // positions per work unit (multiple of 64)
   int n_chunks;           // ceil(T_max / chunk)
   int use_queue;          // 1: resident workgroups take units from the queue; 0: one workgroup per unit
+  int big_units;          // queue: 1 to hand out most of each sequence in units of four blocks
   int grid_wgs;           // queue: most workgroups to launch
   int cus;                // queue: compute units of the device
   float scale_log2e;      // softmax scale * log2(e)

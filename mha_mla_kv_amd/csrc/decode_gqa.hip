@@ -174,9 +174,10 @@ struct UnitShared {
 };
 
 // Blocks of `chunk` positions of one (sequence, KV head): nb = ceil(L / chunk).
-// In the queue schedule the first kBigBlocks * nbig blocks form big units of
-// kBigBlocks blocks, nbig = 3 nb / (4 kBigBlocks); the rest are single-block
-// units, handed out after every big unit of the batch.  The end of the queue
+// In the queue schedule (when the batch has blocks enough for it) the first
+// kBigBlocks * nbig blocks form big units of kBigBlocks blocks, nbig =
+// 3 nb / (4 kBigBlocks); the rest are single-block units, handed out after
+// every big unit of the batch.  The end of the queue
 // is thus made of small units, so the workgroups run out of work at about the
 // same time.  Partials are stored at the slot of their first block.
 constexpr int kBigBlocks = 4;
@@ -192,7 +193,7 @@ struct Split {
 __device__ __forceinline__ Split split_of(const GqaDecodeArgs& a, int L) {
   Split sp;
   sp.nb = (L + a.chunk - 1) / a.chunk;
-  sp.nbig = a.use_queue ? 3 * sp.nb / (4 * kBigBlocks) : 0;
+  sp.nbig = a.use_queue && a.big_units ? 3 * sp.nb / (4 * kBigBlocks) : 0;
   return sp;
 }
 
@@ -426,7 +427,6 @@ __device__ void run_units(const GqaDecodeArgs& a, UnitShared& sh, unsigned* pre,
 // (Hkv, B).  Also returns the queue counter to zero for the next call (the
 // decode kernel has finished: same stream).
 __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
-  __shared__ float m_s[64], inv_s[64];
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   if (a.use_queue && g == 0 && b == 0 && tid == 0) *a.queue = 0u;
   const Split sp = split_of(a, clamp_len(a.lens[b], a.T_max));
@@ -435,23 +435,15 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
   const int n_rep = a.n_rep, D2 = a.D / 2;
   const size_t s0 = ((size_t)b * a.Hkv + g) * a.n_chunks;
   const float* lse = a.lse + s0 * n_rep;
-  for (int hd = tid; hd < n_rep; hd += 256) {
-    float M = kNegInf;
-    for (int p = 0; p < n; ++p) M = fmaxf(M, lse[(size_t)sp.slot(p) * n_rep + hd]);
-    float S = 0.f;
-    for (int p = 0; p < n; ++p) S += exp2_fast(lse[(size_t)sp.slot(p) * n_rep + hd] - M);
-    m_s[hd] = M;
-    inv_s[hd] = 1.f / S;
-  }
-  __syncthreads();
   const size_t row0 = (size_t)b * a.Hq + (size_t)g * n_rep;
   const float2* op = reinterpret_cast<const float2*>(a.o_part + s0 * n_rep * a.D);
   const size_t jstride = (size_t)n_rep * D2;  // float2 per slot
   for (int e = tid; e < n_rep * D2; e += 256) {
     const int hd = e / D2, d2 = e - hd * D2;
-    const float M = m_s[hd];
+    // one pass with a running max; eight partials per batch, loaded before use
+    // (indices clamped, the extra ones weigh 2^-inf = 0)
+    float M = kNegInf, S = 0.f;
     float2 acc = {0.f, 0.f};
-    // eight partials per batch, loaded before use (indices clamped, extra weights 0)
     for (int j0 = 0; j0 < n; j0 += 8) {
       float w[8];
       float2 v[8];
@@ -463,12 +455,16 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float wk = j0 + k < n ? exp2_fast(w[k] - M) : 0.f;
-        acc.x = fmaf(wk, v[k].x, acc.x);
-        acc.y = fmaf(wk, v[k].y, acc.y);
+        if (j0 + k >= n) w[k] = kNegInf;
+        const float Mn = fmaxf(M, w[k]);  // finite from the first partial on
+        const float f = rescale(M, Mn), wk = exp2_fast(w[k] - Mn);
+        S = S * f + wk;
+        acc.x = acc.x * f + wk * v[k].x;
+        acc.y = acc.y * f + wk * v[k].y;
+        M = Mn;
       }
     }
-    const float sc = inv_s[hd];
+    const float sc = 1.f / S;
     store_out2(a, row0 + hd, 2 * d2, acc.x * sc, acc.y * sc);
   }
 }
