@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "attn_internal.h"
@@ -476,7 +477,7 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
 // 128 need up to 168 registers (three waves) with the next tile in flight.
 template <int D, int HB, bool QUEUE>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(HB > 1 ? 1 : (D >= 96 ? 3 : 4))))
+__attribute__((amdgpu_waves_per_eu(HB > 1 ? 1 : (D >= 96 ? (QUEUE ? 2 : 3) : 4))))
 void gqa_decode_bf16(GqaDecodeArgs a) {
   static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
   constexpr int KC = D / 32;           // 32-wide dim chunks (QK contraction)
@@ -581,7 +582,11 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
     }
     // Per tile: K(t) -> LDS; scores from LDS; K(t + kStep) requested; V(t) ->
     // LDS (same region); V(t + kStep) requested; softmax; PV from LDS.
-    for (int t0 = u.t0 + wave * kDecodeTileTokens; t0 < c1; t0 += kStep) {
+    // The wave's last tile requests nothing further: a load past the unit end
+    // would read nothing, but it still makes a round trip, and the next unit's
+    // loads into the same registers would wait for it.
+    auto tile = [&](const int t0, auto next) {
+      constexpr bool NEXT = decltype(next)::value;
       if constexpr (QUEUE) {
         // second-to-last tile of wave 0 (or its only one): take the workgroup's
         // next unit, so the queue's round trip overlaps the end of this one
@@ -616,10 +621,10 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
       // the next K tile after the scores: its registers are then free (this
       // tile is in LDS)
       __builtin_amdgcn_sched_barrier(0);
-      load_rows(kr, kp, t0 + kStep, c1);
+      if constexpr (NEXT) load_rows(kr, kp, t0 + kStep, c1);
       wave_lds_sync();
       store_rows(vr, VP);
-      load_rows(vr, vp, t0 + kStep, c1);
+      if constexpr (NEXT) load_rows(vr, vp, t0 + kStep, c1);
       // Online softmax per head; P^T as the B operand of the PV product.
       bf16x8 pop[HB];
 #pragma unroll
@@ -663,7 +668,10 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
         if (w == DW / 2 - 1) __builtin_amdgcn_sched_barrier(0);
       }
       wave_lds_sync();
-    }
+    };
+    int t0 = u.t0 + wave * kDecodeTileTokens;
+    for (; t0 + kStep < c1; t0 += kStep) tile(t0, std::true_type{});
+    if (t0 < c1) tile(t0, std::false_type{});
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       lsum[hb] = sum_xor16(lsum[hb]);
