@@ -168,7 +168,7 @@ attn_status attn_prefill_gqa_causal(const void* q, const void* k, const void* v,
  * v_head_dim in [1, 256].  c_kv, k_rope, w_uk, w_uv and out must be 16-byte
  * aligned (else ATTN_ERR_UNSUPPORTED).
  * split_tokens: 0 lets the library choose the chunk length (a power of two of at
- * least 256 positions, about two chunks per compute unit over B * T_max);
+ * least 256 positions, about one chunk per compute unit over B * T_max);
  * otherwise a multiple of 64 in [64, 65536].  Each (chunk, sequence) is one
  * workgroup serving all H heads; a sequence of length L uses ceil(L / chunk)
  * chunks, merged afterwards.

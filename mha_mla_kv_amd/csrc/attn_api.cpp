@@ -114,14 +114,16 @@ struct MlaLayout {
 
 MlaLayout mla_layout(int B, int H, int r, int dR, int T_max, int split_tokens) {
   MlaLayout l;
-  // One (chunk, sequence) workgroup serves all heads; aim for about two
-  // workgroups per CU over the whole batch, with chunks of at least 256 tokens
-  // so each wave's copy ring runs several steps.
+  // One (chunk, sequence) workgroup serves all heads; aim for about one
+  // workgroup per CU over the whole batch (measured faster than two: every
+  // chunk pays the ring's first-copy latency and the merge reads one partial
+  // per chunk), with chunks of at least 256 tokens so each wave's copy ring
+  // runs several steps.
   if (split_tokens) {
     l.split = split_tokens;
   } else {
     const int cus = device_cus() > 0 ? device_cus() : 256;
-    const long long want = ((long long)B * T_max + 2LL * cus - 1) / (2LL * cus);
+    const long long want = ((long long)B * T_max + cus - 1) / cus;
     long long s = 256;
     while (s < want && s < 65536) s <<= 1;
     l.split = (int)s;

@@ -1,0 +1,73 @@
+"""The three entry points captured in a HIP graph (torch.cuda.graph) and replayed.
+
+Each call is launched with a caller-provided workspace, so it allocates nothing; the GQA
+decode's work-queue counter is returned to zero by the call itself, so every replay starts
+from the same state.  Replays are interleaved with unrelated eager work and synchronisations,
+and every replay must reproduce the eager result bit for bit (the result of a call does not
+depend on which workgroup takes which unit)."""
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _graph_matches_eager(call, out, replays=4):
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on a side stream, as capture requires
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    scratch = torch.ones(1 << 20, device="cuda")
+    for i in range(replays):
+        out.fill_(float("nan"))
+        scratch.mul_(1.5).add_(i)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from the eager call"
+    return eager
+
+
+def test_gqa_decode_graph_replay():
+    import mha_mla_kv_amd as attn
+    B, Hq, Hkv, D, T = 4, 32, 8, 128, 3000
+    inp = {k: v.cuda() for k, v in synth.gqa_decode_inputs(B, Hq, Hkv, D, T, [3000, 17, 2048, 0], seed=7).items()}
+    print(f"[case] gqa decode graph B={B} Hq={Hq} Hkv={Hkv} D={D} T={T}", flush=True)
+    ws = torch.zeros(attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T, 0), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hq, D, device="cuda")
+    eager = _graph_matches_eager(
+        lambda: attn.attn_decode_gqa(inp["q"], inp["k"], inp["v"], inp["cache_lens"], out=out, workspace=ws), out)
+    assert torch.isfinite(eager).all()
+    assert int(ws[:4].view(torch.int32)[0]) == 0  # the queue counter is back to zero
+
+
+def test_mla_decode_graph_replay():
+    import mha_mla_kv_amd as attn
+    B, H, dn, dR, dv, r, T = 3, 8, 96, 48, 96, 128, 1500
+    inp = {k: v.cuda() for k, v in synth.mla_decode_inputs(B, H, dn, dR, dv, r, T, [1500, 1, 700], seed=8).items()}
+    print(f"[case] mla decode graph B={B} H={H} r={r} dR={dR} T={T}", flush=True)
+    ws = torch.zeros(attn.attn_decode_mla_workspace_bytes(B, H, r, dR, T, 0), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, H, dv, device="cuda")
+    keys = ("q_nope", "q_rope", "w_uk", "w_uv", "c_kv", "k_rope", "cache_lens")
+    eager = _graph_matches_eager(
+        lambda: attn.attn_decode_mla_absorbed(*(inp[k] for k in keys), out=out, workspace=ws), out)
+    assert torch.isfinite(eager).all()
+
+
+def test_prefill_graph_replay():
+    import mha_mla_kv_amd as attn
+    B, S, Hq, Hkv, D = 1, 700, 16, 4, 128
+    inp = {k: v.cuda() for k, v in synth.gqa_prefill_inputs(B, S, Hq, Hkv, D, seed=9).items()}
+    print(f"[case] prefill graph B={B} S={S} Hq={Hq} Hkv={Hkv} D={D}", flush=True)
+    out = torch.empty_like(inp["q"])
+    eager = _graph_matches_eager(lambda: attn.attn_prefill_gqa_causal(inp["q"], inp["k"], inp["v"], out=out), out)
+    assert torch.isfinite(eager.float()).all()
