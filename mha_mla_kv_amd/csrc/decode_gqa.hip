@@ -423,23 +423,31 @@ __device__ void run_units(const GqaDecodeArgs& a, UnitShared& sh, unsigned* pre,
   }
 }
 
+// Element pairs of one (sequence, KV head) output block that a merge
+// workgroup combines.
+constexpr int kMergePairs = 256;
+
 // Combines the partials of every (sequence, KV head) with more than one chunk:
 // out = sum_j 2^(lse_j - M) o_j / sum_j 2^(lse_j - M), M = max_j lse_j.  Grid
-// (Hkv, B).  Also returns the queue counter to zero for the next call (the
-// decode kernel has finished: same stream).
+// (Hkv * ceil(n_rep * D / 2 / kMergePairs), B): each thread merges one pair
+// of output elements.  Also returns the queue counter to zero for the next
+// call (the decode kernel has finished: same stream).
 __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
-  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  if (a.use_queue && g == 0 && b == 0 && tid == 0) *a.queue = 0u;
+  const int tid = threadIdx.x, b = blockIdx.y;
+  if (a.use_queue && blockIdx.x == 0 && b == 0 && tid == 0) *a.queue = 0u;
+  const int n_rep = a.n_rep, D2 = a.D / 2;
+  const int n_eb = (n_rep * D2 + kMergePairs - 1) / kMergePairs;
+  const int g = blockIdx.x / n_eb, e = (blockIdx.x - g * n_eb) * kMergePairs + tid;
+  if (e >= n_rep * D2) return;
   const Split sp = split_of(a, clamp_len(a.lens[b], a.T_max));
   const int n = sp.parts();
   if (n <= 1) return;  // written by the decode kernel
-  const int n_rep = a.n_rep, D2 = a.D / 2;
   const size_t s0 = ((size_t)b * a.Hkv + g) * a.n_chunks;
   const float* lse = a.lse + s0 * n_rep;
   const size_t row0 = (size_t)b * a.Hq + (size_t)g * n_rep;
   const float2* op = reinterpret_cast<const float2*>(a.o_part + s0 * n_rep * a.D);
   const size_t jstride = (size_t)n_rep * D2;  // float2 per slot
-  for (int e = tid; e < n_rep * D2; e += 256) {
+  {
     const int hd = e / D2, d2 = e - hd * D2;
     // one pass with a running max; eight partials per batch, loaded before use
     // (indices clamped, the extra ones weigh 2^-inf = 0)
@@ -490,15 +498,17 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   constexpr int kLoads = kDecodeTileTokens / kRowsPerLoad;   // 16-byte loads per lane per tile
   constexpr int kStep = kDecodeWaves * kDecodeTileTokens;    // positions per round of the four waves
   constexpr int kVtElems = kDecodeWaves * kDecodeTileTokens * VP;
-  // epilogue scratch (floats): m and l per wave and head, kSlices x [HB*16][D]
-  // outputs, lse.  Where the tile LDS holds one output slice per wave, the waves
-  // write their scaled outputs at once and the store sums the slices;
-  // otherwise they add into one slice in turn.
+  // epilogue scratch (floats), overlaying the tiles: m and l per wave and head,
+  // one [HB*16][D] output slice per wave (the waves write their scaled outputs
+  // at once and the store sums the slices), lse.  With more than one head
+  // block the slices outgrow the tiles and the LDS array grows to hold them
+  // (up to 130 KB at HB 4: one workgroup per compute unit in any case).
   constexpr int kSliceFloats = HB * 16 * D;
-  constexpr bool kSliced = 2 * kDecodeWaves * HB * 16 * 4 + kDecodeWaves * kSliceFloats * 4 + HB * 16 * 4 <= kVtElems * 2;
-  constexpr int kSlices = kSliced ? kDecodeWaves : 1;
-  static_assert(2 * kDecodeWaves * HB * 16 * 4 + kSlices * kSliceFloats * 4 + HB * 16 * 4 <= kVtElems * 2, "scratch");
-  __shared__ __attribute__((aligned(16))) u16 smem[kVtElems];
+  constexpr int kScratchElems = (2 * kDecodeWaves * HB * 16 + kDecodeWaves * kSliceFloats + HB * 16) * 2;
+  constexpr int kSmemElems = kScratchElems > kVtElems ? kScratchElems : kVtElems;
+  static_assert(HB == 1 || kSmemElems * 2 + kQueuePlanWords * 4 <= 160 * 1024, "LDS");
+  static_assert(HB > 1 || kSmemElems == kVtElems, "one head block: the scratch fits the tiles");
+  __shared__ __attribute__((aligned(16))) u16 smem[kSmemElems];
   __shared__ unsigned pre[QUEUE ? kQueuePlanWords : 1];
   __shared__ UnitShared sh;
 
@@ -508,8 +518,8 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   const int n_rep = a.n_rep;
   float* mw = reinterpret_cast<float*>(smem);   // [waves][HB*16]
   float* lw = mw + kDecodeWaves * HB * 16;      // [waves][HB*16]
-  float* ob = lw + kDecodeWaves * HB * 16;      // [kSlices][HB*16][D]
-  float* lse_s = ob + kSlices * kSliceFloats;   // [HB*16]
+  float* ob = lw + kDecodeWaves * HB * 16;      // [waves][HB*16][D]
+  float* lse_s = ob + kDecodeWaves * kSliceFloats;  // [HB*16]
   u16* vt = smem + wave * kDecodeTileTokens * VP;
   const size_t tok_stride = (size_t)a.Hkv * D;
   const int row_bytes = uniform((int)(tok_stride * 2));
@@ -696,31 +706,14 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
       for (int w = 0; w < DW; ++w) o[hb][w] *= f;
       if (wave == 0 && grp == 0) lse_s[hd] = M + __log2f(Lt);
     }
-    if constexpr (kSliced) {
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb)
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-        for (int dw = 0; dw < DW; ++dw)
-          *reinterpret_cast<float4*>(ob + wave * kSliceFloats + (hb * 16 + row) * D + 16 * dw + 4 * grp) =
-              make_float4(o[hb][dw][0], o[hb][dw][1], o[hb][dw][2], o[hb][dw][3]);
-      __syncthreads();
-    } else {
-      for (int w = 0; w < kDecodeWaves; ++w) {
-        if (wave == w) {
-#pragma unroll
-          for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-            for (int dw = 0; dw < DW; ++dw) {
-              float4* dst = reinterpret_cast<float4*>(ob + (hb * 16 + row) * D + 16 * dw + 4 * grp);
-              const float4 cur = w == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : *dst;
-              *dst = make_float4(cur.x + o[hb][dw][0], cur.y + o[hb][dw][1], cur.z + o[hb][dw][2],
-                                 cur.w + o[hb][dw][3]);
-            }
-        }
-        __syncthreads();
-      }
-    }
-    store_unit<D, kSlices>(a, u, ob, lse_s, kSliceFloats);  // ends with a barrier (ob is reused)
+      for (int dw = 0; dw < DW; ++dw)
+        *reinterpret_cast<float4*>(ob + wave * kSliceFloats + (hb * 16 + row) * D + 16 * dw + 4 * grp) =
+            make_float4(o[hb][dw][0], o[hb][dw][1], o[hb][dw][2], o[hb][dw][3]);
+    __syncthreads();
+    store_unit<D, kDecodeWaves>(a, u, ob, lse_s, kSliceFloats);  // ends with a barrier (ob is reused)
   };
   auto publish_state = [&]() {
     if (grp == 0) {
@@ -979,7 +972,8 @@ hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t st) {
     e = launch_mode<false>(a, dim3(a.Hkv, a.n_chunks, a.B), st);
   }
   if (e != hipSuccess || a.n_chunks < 2) return e;
-  hipLaunchKernelGGL(gqa_decode_merge, dim3(a.Hkv, a.B), dim3(256), 0, st, a);
+  const int n_eb = (a.n_rep * (a.D / 2) + kMergePairs - 1) / kMergePairs;
+  hipLaunchKernelGGL(gqa_decode_merge, dim3(a.Hkv * n_eb, a.B), dim3(kMergePairs), 0, st, a);
   return hipGetLastError();
 }
 
