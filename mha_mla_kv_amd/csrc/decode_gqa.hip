@@ -79,10 +79,6 @@ __device__ __forceinline__ float sum_xor32(float x) { const float2 p = pair_xor3
 // exp2(m - M) that is 0 (not NaN) when m is -inf.
 __device__ __forceinline__ float rescale(float m, float M) { return m == kNegInf ? 0.f : exp2_fast(m - M); }
 
-__device__ __forceinline__ bf16x8 load_bf16x8(const u16* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
-}
-
 // Cache policy of the K/V loads: non-temporal (streaming).  The cache is read
 // once per call; these loads neither displace reusable lines nor wait on them.
 constexpr int kStreamPolicy = 2;
@@ -262,17 +258,17 @@ __device__ __forceinline__ void store_out2(const GqaDecodeArgs& a, size_t row, i
 }
 
 // Unit epilogue: the normalised output of the unit is the sum of NS slices
-// ob[s * slice + head * D + dim] in LDS, its log2-sum-exp lse[n_rep].  Ends
-// with a barrier (ob is reused).
-template <int D, int NS = 1>
+// ob[s * slice + head * OP + dim] in LDS (row pitch OP floats), its
+// log2-sum-exp lse[n_rep].  Ends with a barrier (ob is reused).
+template <int D, int NS = 1, int OP = D>
 __device__ void store_unit(const GqaDecodeArgs& a, const Unit& u, const float* ob, const float* lse, int slice = 0) {
   const int tid = threadIdx.x, n_rep = a.n_rep;
   constexpr int D2 = D / 2;
   auto value = [&](int hd, int d2) {
-    float2 v = *reinterpret_cast<const float2*>(ob + hd * D + 2 * d2);
+    float2 v = *reinterpret_cast<const float2*>(ob + hd * OP + 2 * d2);
 #pragma unroll
     for (int sl = 1; sl < NS; ++sl) {
-      const float2 w = *reinterpret_cast<const float2*>(ob + sl * slice + hd * D + 2 * d2);
+      const float2 w = *reinterpret_cast<const float2*>(ob + sl * slice + hd * OP + 2 * d2);
       v.x += w.x;
       v.y += w.y;
     }
@@ -499,11 +495,14 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   constexpr int kStep = kDecodeWaves * kDecodeTileTokens;    // positions per round of the four waves
   constexpr int kVtElems = kDecodeWaves * kDecodeTileTokens * VP;
   // epilogue scratch (floats), overlaying the tiles: m and l per wave and head,
-  // one [HB*16][D] output slice per wave (the waves write their scaled outputs
-  // at once and the store sums the slices), lse.  With more than one head
-  // block the slices outgrow the tiles and the LDS array grows to hold them
-  // (up to 130 KB at HB 4: one workgroup per compute unit in any case).
-  constexpr int kSliceFloats = HB * 16 * D;
+  // one [HB*16][OP] output slice per wave (the waves write their scaled outputs
+  // at once and the store sums the slices), lse.  The row pitch OP = D + 4
+  // puts the 16 head rows of one 16-byte-per-lane write on distinct LDS banks
+  // (with pitch D they all hit the same four).  With more than one head block
+  // the slices outgrow the tiles and the LDS array grows to hold them (up to
+  // 134 KB at HB 4: one workgroup per compute unit in any case).
+  constexpr int OP = D + 4;
+  constexpr int kSliceFloats = HB * 16 * OP;
   constexpr int kScratchElems = (2 * kDecodeWaves * HB * 16 + kDecodeWaves * kSliceFloats + HB * 16) * 2;
   constexpr int kSmemElems = kScratchElems > kVtElems ? kScratchElems : kVtElems;
   static_assert(HB == 1 || kSmemElems * 2 + kQueuePlanWords * 4 <= 160 * 1024, "LDS");
@@ -518,7 +517,7 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   const int n_rep = a.n_rep;
   float* mw = reinterpret_cast<float*>(smem);   // [waves][HB*16]
   float* lw = mw + kDecodeWaves * HB * 16;      // [waves][HB*16]
-  float* ob = lw + kDecodeWaves * HB * 16;      // [waves][HB*16][D]
+  float* ob = lw + kDecodeWaves * HB * 16;      // [waves][HB*16][OP]
   float* lse_s = ob + kDecodeWaves * kSliceFloats;  // [HB*16]
   u16* vt = smem + wave * kDecodeTileTokens * VP;
   const size_t tok_stride = (size_t)a.Hkv * D;
@@ -534,21 +533,22 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   // (non-temporal) buffer loads: lane group lane / kLanesPerRow of load i
   // fetches row kRowsPerLoad * i + lane / kLanesPerRow, each lane one 16-byte
   // unit (head_dim 96: lanes past the 12th unit repeat it), so a load covers
-  // whole rows.  Each load has its own buffer resource starting at its first
-  // row and ending with row c1 - 1: rows at or past the unit end read as zeros
-  // and cost no memory traffic, so loads ahead can be issued unconditionally.
+  // whole rows.  The tile's buffer resource starts at its first row and ends
+  // with this head's part of row c1 - 1: rows at or past the unit end read as
+  // zeros and cost no memory traffic, so loads ahead can be issued
+  // unconditionally.  One resource per tile keeps the scalar work per load to
+  // an offset.
   auto load_rows = [&](bf16x8 (&r)[kLoads], const u16* head0, int t0, int c1) {
+    // rows of the tile before c1, 0..32; bytes up to the end of the last
+    // (row_bytes >= 2 * D, so no rows gives a non-positive count)
+    const int rows = min(max(c1 - t0, 0), kDecodeTileTokens);
+    const int n = max(rows * row_bytes - row_bytes + 2 * D, 0);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(head0 + (size_t)t0 * tok_stride), (short)0, n,
+                                                      0x00020000);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int t = t0 + kRowsPerLoad * i;
-      // rows of this load before c1, 0..kRowsPerLoad; bytes up to the end of the last
-      // (row_bytes >= 2 * D, so no rows gives a non-positive count)
-      const int rows = min(max(c1 - t, 0), kRowsPerLoad);
-      const int n = max(rows * row_bytes - row_bytes + 2 * D, 0);
-      const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(head0 + (size_t)t * tok_stride), (short)0, n,
-                                                        0x00020000);
-      r[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)row_off, 0, kStreamPolicy));
-    }
+    for (int i = 0; i < kLoads; ++i)
+      r[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, (int)(row_off + (unsigned)(kRowsPerLoad * i * row_bytes)), 0, kStreamPolicy));
   };
   // The same registers written to this wave's LDS tile, row pitch `pitch`.
   auto store_rows = [&](const bf16x8 (&r)[kLoads], int pitch) {
@@ -562,15 +562,18 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   bf16x8 qop[HB][KC];
   bf16x8 kr[kLoads], vr[kLoads];
   // Requests the query block of unit u and this wave's first tile of it.
+  // The query block is read through a buffer resource that ends with head
+  // n_rep - 1: the padding heads read as zeros, with no branch.
   auto begin_unit = [&](const Unit& u) {
     const u16* qp = static_cast<const u16*>(a.q) + ((size_t)u.b * a.Hq + (size_t)u.g * n_rep) * D;
+    const auto qs = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(qp), (short)0, n_rep * D * 2, 0x00020000);
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       const int head = hb * 16 + row;
 #pragma unroll
       for (int c = 0; c < KC; ++c)
-        qop[hb][c] = head < n_rep ? load_bf16x8(qp + (size_t)head * D + 32 * c + 8 * grp)
-                                  : __builtin_bit_cast(bf16x8, u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+        qop[hb][c] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qs, (head * D + 32 * c + 8 * grp) * 2, 0, 0));
     }
     load_rows(kr, k_head(u), u.t0 + wave * kDecodeTileTokens, u.t1);
     load_rows(vr, v_head(u), u.t0 + wave * kDecodeTileTokens, u.t1);
@@ -710,10 +713,10 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int dw = 0; dw < DW; ++dw)
-        *reinterpret_cast<float4*>(ob + wave * kSliceFloats + (hb * 16 + row) * D + 16 * dw + 4 * grp) =
+        *reinterpret_cast<float4*>(ob + wave * kSliceFloats + (hb * 16 + row) * OP + 16 * dw + 4 * grp) =
             make_float4(o[hb][dw][0], o[hb][dw][1], o[hb][dw][2], o[hb][dw][3]);
     __syncthreads();
-    store_unit<D, kDecodeWaves>(a, u, ob, lse_s, kSliceFloats);  // ends with a barrier (ob is reused)
+    store_unit<D, kDecodeWaves, OP>(a, u, ob, lse_s, kSliceFloats);  // ends with a barrier (ob is reused)
   };
   auto publish_state = [&]() {
     if (grp == 0) {
