@@ -323,8 +323,10 @@ __global__ __launch_bounds__(kThreads) void mla_decode_fused(MlaDecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) u16 rop0[kWaves][C::kR];
   __shared__ __attribute__((aligned(1024))) u16 rop1[kWaves][C::kR];
   __shared__ __attribute__((aligned(1024))) u16 rop2[kWaves][C::kR];
-  static_assert((2 * kWaves * kHeadsPad + kHeadsPad * R) * 4 <= (int)sizeof(stg0),
-                "merge scratch must fit in stage 0");
+  // epilogue scratch: one [16 heads][R] fp32 output slice per wave, two in each
+  // of stages 0 and 1; m and l per wave and head in stage 2
+  static_assert(2 * kHeadsPad * R * 4 == (int)sizeof(stg0), "two output slices per stage");
+  static_assert(2 * kWaves * kHeadsPad * 4 <= (int)sizeof(stg2), "m, l scratch");
 
   const int s = blockIdx.x, b = blockIdx.y;
   const int L = clamp_len(a.lens[b], a.T_max);
@@ -333,13 +335,9 @@ __global__ __launch_bounds__(kThreads) void mla_decode_fused(MlaDecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Lanes<R, DR> ln(tid & 63);
 
-  if (s >= n_chunks) return;  // past the sequence (an empty one is zeroed by the merge)
-  const int c0 = s * a.split, c1 = min(c0 + a.split, L);
-  const int n_steps = (c1 - c0 + kStep - 1) / kStep;
-  const int tw0 = c0 + kSlice * wave;  // first token of this wave's first slice
-
   // The stages start zeroed: rows past the chunk end are read (with P = 0) by
   // the transposed V product, and uninitialised LDS could hold NaN patterns.
+  // (Done while the length is in flight.)
   {
     const u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
     u16* const bufs[6] = {&stg0[0][0], &stg1[0][0], &stg2[0][0], &rop0[0][0], &rop1[0][0], &rop2[0][0]};
@@ -348,6 +346,10 @@ __global__ __launch_bounds__(kThreads) void mla_decode_fused(MlaDecodeArgs a) {
       for (int e = 8 * tid; e < kWaves * (k < 3 ? C::kC : C::kR); e += 8 * kThreads)
         *reinterpret_cast<u16x8*>(bufs[k] + e) = z;
   }
+  if (s >= n_chunks) return;  // past the sequence (an empty one is zeroed by the merge)
+  const int c0 = s * a.split, c1 = min(c0 + a.split, L);
+  const int n_steps = (c1 - c0 + kStep - 1) / kStep;
+  const int tw0 = c0 + kSlice * wave;  // first token of this wave's first slice
   __syncthreads();
   // q_lat^T as the B operand: lane holds q_lat[head row][32k + 8grp ..+8] (hi and lo);
   // requested after the first two slices (their copies are then already in flight)
@@ -404,11 +406,16 @@ __global__ __launch_bounds__(kThreads) void mla_decode_fused(MlaDecodeArgs a) {
   wait_vmem();  // the copies past the end (zeros) land before the stages are reused
   st.lsum = sum_xor32(sum_xor16(st.lsum));
 
-  // ---- merge the four waves (LDS, reusing stage 0)
+  // ---- merge the four waves (LDS, reusing the stages)
+  // Each wave writes its scaled O^T into its own [16][R] slice; 16-byte unit u
+  // of head row h sits at unit position u ^ (h & 15), so the 16 rows of one
+  // write land on distinct banks.
   __syncthreads();
-  float* mw = reinterpret_cast<float*>(&stg0[0][0]);  // [waves][16]
+  float* mw = reinterpret_cast<float*>(&stg2[0][0]);  // [waves][16]
   float* lw = mw + kWaves * kHeadsPad;                // [waves][16]
-  float* olat = lw + kWaves * kHeadsPad;              // [16][R]
+  auto slice = [&](int w) {
+    return reinterpret_cast<float*>(w < 2 ? &stg0[0][0] : &stg1[0][0]) + (w & 1) * kHeadsPad * R;
+  };
   if (ln.grp == 0) {
     mw[wave * kHeadsPad + ln.row] = st.m;
     lw[wave * kHeadsPad + ln.row] = st.lsum;
@@ -425,26 +432,24 @@ __global__ __launch_bounds__(kThreads) void mla_decode_fused(MlaDecodeArgs a) {
 #pragma unroll
     for (int w = 0; w < C::DW; ++w) st.o[w] *= f;
   }
-  for (int w = 0; w < kWaves; ++w) {
-    if (wave == w) {
+  {
+    float* ob = slice(wave) + ln.row * R;
 #pragma unroll
-      for (int dw = 0; dw < C::DW; ++dw)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float* dst = olat + ln.row * R + 16 * dw + 4 * ln.grp + i;
-          *dst = (w == 0 ? 0.f : *dst) + st.o[dw][i];
-        }
-    }
-    __syncthreads();
+    for (int dw = 0; dw < C::DW; ++dw)
+      *reinterpret_cast<f32x4*>(ob + 4 * ((4 * dw + ln.grp) ^ ln.row)) = st.o[dw];
   }
+  __syncthreads();
 
-  // publish this chunk's normalised o_lat and log2-sum-exp (ordered for the merge
-  // kernel by the kernel boundary)
+  // publish this chunk's normalised o_lat (the sum of the four slices) and
+  // log2-sum-exp (ordered for the merge kernel by the kernel boundary)
   const size_t row0 = (size_t)b * a.H;
   for (int e = tid; e < a.H * (R / 4); e += kThreads) {
     const int h = e / (R / 4), d4 = e - h * (R / 4);
-    *reinterpret_cast<float4*>(a.o_part + ((row0 + h) * a.n_splits + s) * R + 4 * d4) =
-        *reinterpret_cast<const float4*>(olat + h * R + 4 * d4);
+    const int off = h * R + 4 * (d4 ^ (h & 15));
+    f32x4 v = *reinterpret_cast<const f32x4*>(slice(0) + off);
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) v += *reinterpret_cast<const f32x4*>(slice(w) + off);
+    *reinterpret_cast<f32x4*>(a.o_part + ((row0 + h) * a.n_splits + s) * R + 4 * d4) = v;
   }
   for (int h = tid; h < a.H; h += kThreads) {
     float M = kNegInf;
