@@ -203,17 +203,17 @@ __device__ __forceinline__ LdsOffsets lds_offsets(const Lane& w) {
 template <int D>
 __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const u16* kc, const bf16x8 (&qop)[D / 16], int off) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    f32x16 acc;
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int i = 0; i < 16; ++i) s[j][i] = 0.f;
+  // the two 32-key blocks' chains alternate, so no MFMA waits for the one before it
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
+  for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
       const u16* kr = kc + 32 * j * D + (off ^ (16 * c));
-      acc = mfma_32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(kr)), qop[c], acc);
+      s[j] = mfma_32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(kr)), qop[c], s[j]);
     }
-    s[j] = acc;
-  }
 }
 
 // O^T[dims 32d..][rows] += V^T P^T over one tile from the V tile vc.  Step v of the
