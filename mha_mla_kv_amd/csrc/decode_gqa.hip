@@ -613,23 +613,35 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
       // Scores: lane holds S^T[token 16u + 4grp + i][head 16hb + row]; the A
       // operand (token 16u + row, dims 32c + 8grp .. +8) comes from LDS.
       float sc[HB][2][4];
+      {
+        bf16x8 ka[2][KC];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        bf16x8 ka[KC];
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int c = 0; c < KC; ++c)
+            ka[s][c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(vt + (16 * s + row) * KP + 32 * c + 8 * grp));
+        // the accumulation chains of the two token blocks (and head blocks)
+        // alternate, so no MFMA waits for the one issued just before it
+        f32x4 acc[HB][2];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) acc[hb][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < KC; ++c)
-          ka[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(vt + (16 * s + row) * KP + 32 * c + 8 * grp));
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-          for (int c = 0; c < KC; ++c) acc = mfma_16x16x32(ka[c], qop[hb][c], acc);
+            for (int s = 0; s < 2; ++s) acc[hb][s] = mfma_16x16x32(ka[s][c], qop[hb][c], acc[hb][s]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tok = t0 + 16 * s + 4 * grp + i;
-            sc[hb][s][i] = tok < c1 ? acc[i] * a.scale_log2e : kNegInf;
-          }
-        }
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int tok = t0 + 16 * s + 4 * grp + i;
+              sc[hb][s][i] = tok < c1 ? acc[hb][s][i] * a.scale_log2e : kNegInf;
+            }
       }
       // the next K tile after the scores: its registers are then free (this
       // tile is in LDS)

@@ -255,13 +255,15 @@ __device__ __forceinline__ void slice_step(WaveState<R, DR>& st, const u16* cs, 
                                            const bf16x8 (&qlo)[R / 32], const bf16x8* qr32, bf16x8 qr16, int t0, int c1,
                                            float c, const Lanes<R, DR>& ln) {
   using C = Cfg<R, DR>;
-  // S^T[token 4grp + i][head row]: A = slice rows (token = row), B = q_lat^T
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // S^T[token 4grp + i][head row]: A = slice rows (token = row), B = q_lat^T.
+  // Two accumulation chains (the hi and lo parts of q_lat) alternate, so no
+  // MFMA waits for the one issued just before it; they meet at the end.
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < C::KC; ++k) {
     const bf16x8 cr = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(cs + (ln.k_off ^ (32 * k))));
     acc = mfma_16x16x32(cr, qhi[k], acc);
-    acc = mfma_16x16x32(cr, qlo[k], acc);
+    acc2 = mfma_16x16x32(cr, qlo[k], acc2);
   }
 #pragma unroll
   for (int k = 0; k < C::RC; ++k) {
@@ -275,8 +277,9 @@ __device__ __forceinline__ void slice_step(WaveState<R, DR>& st, const u16* cs, 
     // states than the compiler provides on gfx950)
     const bf16x8 kr = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(rs + ln.row * DR + 32 * C::RC + 8 * ln.grp));
     const bf16x8 z = {};
-    acc = mfma_16x16x32(ln.grp < 2 ? kr : z, qr16, acc);
+    acc2 = mfma_16x16x32(ln.grp < 2 ? kr : z, qr16, acc2);
   }
+  acc += acc2;
   float s[4], mt = kNegInf;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
