@@ -214,6 +214,13 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const u16* kc, const bf1
       const u16* kr = kc + 32 * j * D + (off ^ (16 * c));
       s[j] = mfma_32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(kr)), qop[c], s[j]);
     }
+  // issue order: operand reads four MFMAs ahead of their use
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int u = 0; u < 2 * (D / 16); ++u) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
 }
 
 // O^T[dims 32d..][rows] += V^T P^T over one tile from the V tile vc.  Step v of the
