@@ -61,7 +61,7 @@ int choose_chunk(int B, int Hkv, int n_rep, int T_max) {
   if (n_rep >= 8) lo = 128;
   if (n_rep >= 16) lo = 512;
   if (n_rep >= 32) lo = 1024;
-  const long long want = (long long)B * Hkv * T_max / 2048 / 64 * 64;
+  const long long want = (long long)B * Hkv * T_max / 4096 / 64 * 64;
   return (int)(want < lo ? lo : (want > 1024 ? 1024 : want));
 }
 

@@ -44,8 +44,8 @@ def test_workspace_sizes():
     slots = B * Hkv * (T // 512)
     n = attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T, 512)
     assert n == 256 + al(slots * 4 * 4) + al(slots * 4 * D * 4)
-    # split 0: the library picks B*Hkv*T/2048 = 1024 positions per block here
-    slots = B * Hkv * (T // 1024)
+    # split 0: the library picks B*Hkv*T/4096 = 512 positions per block here
+    slots = B * Hkv * (T // 512)
     assert attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T, 0) == 256 + al(slots * 4 * 4) + al(slots * 4 * D * 4)
     # a single chunk per sequence needs no partials
     assert attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, 512, 512) == 256
