@@ -179,3 +179,19 @@ def test_batch_limit_of_the_queue_schedule(B):
     out = _run(inp, split_tokens=64)
     ref = oracle.gqa_decode(inp["q"], inp["k"], inp["v"], inp["cache_lens"])
     assert_close_rows(out, ref, TOL_BF16, f"B={B}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,B,T", [(32, 8, 16, 2048), (32, 1, 64, 4096)], ids=["gqa4", "mqa"])
+def test_four_block_units_every_row(Hq, Hkv, B, T):
+    """Problems with at least 16 blocks per compute unit run the queue with units of four
+    blocks first; every output row (ragged lengths, some shorter than one block, one empty,
+    one full) matches the oracle.  The MQA case also covers two 16-head blocks per unit."""
+    D = 128
+    rng = np.random.default_rng(B + Hkv)
+    lens = rng.integers(1, T + 1, size=B).tolist()
+    lens[0], lens[1], lens[-1] = 0, 40, T
+    inp = synth.gqa_decode_inputs(B, Hq, Hkv, D, T, lens, seed=11 + Hkv)
+    print(f"[case] four-block units B={B} Hq={Hq} Hkv={Hkv} D={D} T={T} split=64", flush=True)
+    out = _run(inp, split_tokens=64)
+    ref = oracle.gqa_decode(inp["q"], inp["k"], inp["v"], inp["cache_lens"])
+    assert_close_rows(out, ref, TOL_BF16, f"four-block units Hkv={Hkv}")
