@@ -49,9 +49,10 @@ int pow2_floor(long long x) {
 
 // Positions per decode block (the work unit of the fixed schedule; the queue
 // hands out single blocks, or for large batches units of four blocks first)
-// when the caller leaves it to the library: about B*Hkv*T_max / 2048 rounded
+// when the caller leaves it to the library: about B*Hkv*T_max / 4096 rounded
 // down to a multiple of 64, so that every one of the ~256 queue workgroups
-// takes several units even when the lengths are ragged, at most 1024, and long
+// takes several units even when the lengths are ragged and the last units are
+// short (512 at B 32, Hkv 8, T_max 8192: measured best), at most 1024, and long
 // enough that the fp32 partial of a unit (n_rep * D * 4 bytes written and read
 // back) stays small next to its cache bytes (chunk * D * 4); with 16 or more
 // query heads per KV head the per-unit costs dominate a short chunk (measured),
