@@ -52,6 +52,8 @@ def _declare(lib):
     lib.oracle_gqa_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, D]
     lib.oracle_gqa_prefill_causal.restype = None
     lib.oracle_gqa_prefill_causal.argtypes = [P, P, P, P, I, I, I, I, I, D, P, I]
+    lib.oracle_gqa_prefill_cached.restype = None
+    lib.oracle_gqa_prefill_cached.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D]
     for name in ("oracle_mla_decode_decompressed", "oracle_mla_decode_absorbed"):
         fn = getattr(lib, name)
         fn.restype = None
@@ -122,6 +124,24 @@ def gqa_prefill_causal(q, k, v, softmax_scale: float = 0.0, rows=None, lib=None)
     (lib or load()).oracle_gqa_prefill_causal(_p(q), _p(k), _p(v), _p(out), B, S, Hq, Hkv, D,
                                               float(softmax_scale), _p(r),
                                               0 if r is None else int(r.size))
+    return out
+
+
+def gqa_prefill_cached(q, k_cache, v_cache, start_pos, q_lens=None, softmax_scale: float = 0.0,
+                       lib=None) -> np.ndarray:
+    """Causal prefill after a cached prefix: q [B,S,Hq,D] (new tokens), k/v caches
+    [B,T_max,Hkv,D] holding the new rows at start_pos[b] .., start_pos [B], q_lens [B] or None
+    -> out [B,S,Hq,D] float64 (rows past q_lens[b] zero)."""
+    q, k, v, sp = _f32(q), _f32(k_cache), _f32(v_cache), _i32(start_pos)
+    B, S, Hq, D = q.shape
+    _, T_max, Hkv, _ = k.shape
+    _check_groups(Hq, Hkv)
+    assert k.shape == (B, T_max, Hkv, D) and v.shape == k.shape and sp.shape == (B,)
+    ql = None if q_lens is None else _i32(q_lens)
+    assert ql is None or ql.shape == (B,)
+    out = np.zeros((B, S, Hq, D), dtype=np.float64)
+    (lib or load()).oracle_gqa_prefill_cached(_p(q), _p(k), _p(v), _p(sp), _p(ql), _p(out), B, S, Hq, Hkv, D,
+                                              T_max, float(softmax_scale))
     return out
 
 

@@ -35,7 +35,9 @@
  *    decode attends to t in [0, L_b) with no mask.  Values are clamped to
  *    [0, T_max].  L_b = 0 gives an output row of zeros.
  *  - Causal prefill lets query i see keys j <= i (no cached prefix, so the
- *    top-left and bottom-right alignments coincide).
+ *    top-left and bottom-right alignments coincide).  With a cached prefix of
+ *    P positions, new token i sits at position P + i and sees keys j <= P + i
+ *    (bottom-right alignment).
  *  - softmax_scale <= 0 selects the default scale.
  */
 #include <math.h>
@@ -144,6 +146,57 @@ void oracle_gqa_prefill_causal(const float* q, const float* k, const float* v,
         const float* vbase = v + ((long)b * S * Hkv + g) * D;
         softmax_weighted_sum(s, n, vbase, (long)Hkv * D, D,
                              out + (((long)b * S + i) * Hq + h) * D);
+        free(s);
+      }
+    }
+  }
+}
+
+/*
+ * Causal GQA prefill after a cached prefix (chunked prefill), per sequence.
+ *   q, out [B, S, Hq, D] (the new tokens)   k, v [B, T_max, Hkv, D] (the cache,
+ *   the new tokens' rows already written at positions P_b .. P_b + n_b - 1)
+ *   start_pos [B] = P_b, q_lens [B] = n_b new tokens (NULL: S each)
+ *   out[b,i,h] = softmax_{j <= P_b + i}( scale * q[b,i,h] . k[b,j,g] ) . v[b,j,g]
+ *   for i < n_b; rows i >= n_b are zero.
+ * This is Attention.forward of the MQA & GQA survey page with start_pos > 0:
+ * the new K/V are written at start_pos first, the keys are the cache up to
+ * start_pos + seqlen, and the additive mask spans cache_len + seqlen; its
+ * plainest reading (bottom-right alignment) lets new token i, at position
+ * start_pos + i, see every cached position up to its own.
+ * P_b is clamped to [0, T_max] and n_b to [0, min(S, T_max - P_b)].
+ */
+void oracle_gqa_prefill_cached(const float* q, const float* k, const float* v,
+                               const int32_t* start_pos, const int32_t* q_lens,
+                               double* out, int B, int S, int Hq, int Hkv,
+                               int D, int T_max, double scale) {
+  const int n_rep = Hq / Hkv;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+#pragma omp parallel for collapse(3) schedule(dynamic)
+  for (int b = 0; b < B; ++b) {
+    for (int i = 0; i < S; ++i) {
+      for (int h = 0; h < Hq; ++h) {
+        const int P = clamp_len(start_pos[b], T_max);
+        int nq = q_lens ? (int)q_lens[b] : S;
+        if (nq > S) nq = S;
+        if (nq > T_max - P) nq = T_max - P;
+        double* o = out + (((long)b * S + i) * Hq + h) * D;
+        if (i >= nq) {
+          for (int d = 0; d < D; ++d) o[d] = 0.0;
+          continue;
+        }
+        const int g = h / n_rep;
+        const int n = P + i + 1; /* keys 0 .. P + i */
+        double* s = (double*)malloc(sizeof(double) * (size_t)n);
+        const float* qv = q + (((long)b * S + i) * Hq + h) * D;
+        for (int j = 0; j < n; ++j) {
+          const float* kr = k + (((long)b * T_max + j) * Hkv + g) * D;
+          double dot = 0.0;
+          for (int d = 0; d < D; ++d) dot += (double)qv[d] * (double)kr[d];
+          s[j] = scale * dot;
+        }
+        const float* vbase = v + ((long)b * T_max * Hkv + g) * D;
+        softmax_weighted_sum(s, n, vbase, (long)Hkv * D, D, o);
         free(s);
       }
     }

@@ -15,6 +15,9 @@ oracle disagrees with:
   * invariants: a joint permutation of cached tokens, a constant added to every
     score, per-head MHA, MQA = every head reading KV head 0, GQA = MHA on K/V
     expanded by the repeat_kv expand+reshape, MLA absorbed = decompressed;
+  * cached-prefix prefill: torch SDPA with an explicit position mask, an empty
+    prefix reducing to causal prefill, and each new row equal to a decode at its
+    own position;
   * the empty cache giving zeros (a reading; the pages are silent).
 The tests run them on the real oracle; tests/test_oracle_mutants.py runs them on
 broken copies and requires that each planted mistake trips at least one pin.
@@ -267,6 +270,79 @@ def pin_prefill_rows(lib):
         _close(full[:, i], dec, 1e-14, f"row {i} vs decode")
 
 
+# ----------------------------------------------------------------------------- cached-prefix prefill pins
+
+CACHED_SHAPES = [
+    # B, S, Hq, Hkv, D, T_max, start_pos, q_lens
+    (2, 5, 8, 2, 16, 12, [4, 7], [5, 3]),
+    (3, 4, 4, 4, 8, 9, [0, 5, 2], [4, 4, 1]),     # MHA, one sequence with an empty prefix
+    (2, 6, 6, 1, 8, 10, [3, 4], [6, 6]),          # MQA
+    (1, 9, 8, 2, 128, 30, [21], [9]),
+]
+
+
+def sdpa_cached_ref(q, k, v, start_pos, q_lens, scale=None):
+    """torch float64 SDPA per sequence with an explicit boolean mask: new token i, at position
+    P + i, may attend cache positions j <= P + i, out of the first P + n positions."""
+    B, S, Hq, D = q.shape
+    n_rep = Hq // k.shape[2]
+    out = np.zeros((B, S, Hq, D))
+    for b in range(B):
+        P, n = int(start_pos[b]), int(q_lens[b])
+        if n == 0:
+            continue
+        L = P + n
+        qt = torch.from_numpy(q[b, :n].astype(np.float64)).permute(1, 0, 2)[None]            # [1,Hq,n,D]
+        kt = torch.from_numpy(k[b, :L].astype(np.float64)).repeat_interleave(n_rep, dim=1).permute(1, 0, 2)[None]
+        vt = torch.from_numpy(v[b, :L].astype(np.float64)).repeat_interleave(n_rep, dim=1).permute(1, 0, 2)[None]
+        mask = torch.arange(L)[None, :] <= (P + torch.arange(n))[:, None]                     # [n, L]
+        o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+        out[b, :n] = o[0].permute(1, 0, 2).numpy()
+    return out
+
+
+def pin_cached_vs_sdpa(lib):
+    for i, (B, S, Hq, Hkv, D, T, sp, ql) in enumerate(CACHED_SHAPES):
+        rng = _rng(400 + i)
+        q, k, v = _rand(rng, B, S, Hq, D), _rand(rng, B, T, Hkv, D), _rand(rng, B, T, Hkv, D)
+        sp, ql = np.array(sp, np.int32), np.array(ql, np.int32)
+        got = oracle.gqa_prefill_cached(q, k, v, sp, ql, lib=lib)
+        _close(got, sdpa_cached_ref(q, k, v, sp, ql), what=f"cached prefill {B,S,Hq,Hkv,D}")
+        for b in range(B):  # rows past the new-token count are zero
+            assert not np.any(got[b, ql[b]:]), "rows past q_lens"
+        _close(oracle.gqa_prefill_cached(q, k, v, sp, ql, softmax_scale=0.3, lib=lib),
+               sdpa_cached_ref(q, k, v, sp, ql, scale=0.3), what="cached prefill scale")
+
+
+def pin_cached_reductions(lib):
+    """An empty prefix is causal prefill over the new tokens; each new row is a decode of that
+    query against the cache up to its own position; a cache whose keys are all equal makes every
+    row the mean of the visible V rows."""
+    rng = _rng(29)
+    B, S, Hq, Hkv, D, T = 2, 6, 8, 2, 16, 15
+    q, k, v = _rand(rng, B, S, Hq, D), _rand(rng, B, T, Hkv, D), _rand(rng, B, T, Hkv, D)
+    zero = oracle.gqa_prefill_cached(q, k, v, np.zeros(B, np.int32), None, lib=lib)
+    causal = oracle.gqa_prefill_causal(q, np.ascontiguousarray(k[:, :S]), np.ascontiguousarray(v[:, :S]), lib=lib)
+    _close(zero, causal, 1e-14, "empty prefix vs causal prefill")
+    sp = np.array([9, 3], np.int32)
+    got = oracle.gqa_prefill_cached(q, k, v, sp, None, lib=lib)
+    for i in range(S):
+        dec = oracle.gqa_decode(np.ascontiguousarray(q[:, i]), k, v, sp + i + 1, lib=lib)
+        _close(got[:, i], dec, 1e-14, f"cached row {i} vs decode")
+    kc = np.broadcast_to(k[:, :1], k.shape).copy()
+    got = oracle.gqa_prefill_cached(q, kc, v, sp, None, lib=lib)
+    n_rep = Hq // Hkv
+    for b in range(B):
+        for i in range(S):
+            L = sp[b] + i + 1
+            want = v[b, :L].astype(np.float64).mean(axis=0)          # [Hkv, D]
+            for h in range(Hq):
+                _close(got[b, i, h], want[h // n_rep], 1e-13, "equal keys -> mean of V")
+    # the prefix fills the cache: the new-token count is clamped to the room left
+    got = oracle.gqa_prefill_cached(q, k, v, np.array([T - 2, T], np.int32), None, lib=lib)
+    assert not np.any(got[0, 2:]) and not np.any(got[1]), "clamp at T_max"
+
+
 # ----------------------------------------------------------------------------- MLA pins
 
 MLA_SHAPES = [
@@ -335,5 +411,5 @@ def pin_mla_selection(lib):
 
 
 ALL_PINS = [pin_decode_vs_sdpa, pin_decode_closed_forms, pin_decode_invariants, pin_decode_head_structure,
-            pin_prefill_vs_sdpa, pin_prefill_rows, pin_mla_vs_sdpa, pin_mla_absorbed_equals_decompressed,
+            pin_prefill_vs_sdpa, pin_prefill_rows, pin_cached_vs_sdpa, pin_cached_reductions, pin_mla_vs_sdpa, pin_mla_absorbed_equals_decompressed,
             pin_mla_selection]

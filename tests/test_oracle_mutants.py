@@ -32,6 +32,10 @@ MUTATIONS = {
                                "if (scale <= 0.0) scale = 1.0 / sqrt((double)(r + dR));\n  const int N = bh_list ? n_bh : B * H;\n#pragma omp parallel for schedule(dynamic)\n  for (int idx = 0; idx < N; ++idx) {\n    const int bh = bh_list ? bh_list[idx] : idx;\n    const int b = bh / H, h = bh % H;\n    if (b < 0 || b >= B) continue;\n    const int L = clamp_len(cache_lens[b], T_max);\n    double* q_abs"),
     # decode reads one token past the cache length
     "decode_reads_past_len": ("const int L = clamp_len(cache_lens[b], T_max);\n      double* s", "const int L = clamp_len(cache_lens[b] + 1, T_max);\n      double* s"),
+    # cached prefill aligned top-left (new token i sees keys 0..i, ignoring the prefix)
+    "cached_top_left": ("const int n = P + i + 1; /* keys 0 .. P + i */", "const int n = i + 1;"),
+    # cached prefill attends the whole new chunk (no causal cut among the new tokens)
+    "cached_no_causal_cut": ("const int n = P + i + 1; /* keys 0 .. P + i */", "const int n = P + nq;"),
     # value row taken from the wrong KV head (always head 0)
     "value_head_zero": ("const float* vbase = v + ((long)b * T_max * Hkv + g) * D;", "const float* vbase = v + ((long)b * T_max * Hkv + 0) * D;"),
 }
