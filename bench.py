@@ -10,6 +10,8 @@ One step = one pass over the three C-ABI entry points, each on its own synthetic
                               kv_lora_rank 128, cache 4096, bf16
   * attn_prefill_gqa_causal   Llama-3-8B-shaped causal prefill: B 4, S 4096, Hq 32, Hkv 8,
                               head_dim 128, bf16 in / out
+  * attn_prefill_gqa_cached   the same heads, a 512-token chunk after a 3584-token cached
+                              prefix in each of 4 sequences (chunked prefill), bf16 in / out
 
 The printed `value` is the GQA decode's KV-cache read rate (algorithmic bytes: every cached
 K and V row read once per KV head, 2*Hkv*head_dim*2 bytes per cached position) divided by
@@ -126,6 +128,18 @@ def main():
     PB, S, PHq, PD = pre["q"].shape
     pre_flops = 4 * PB * PHq * PD * S * (S + 1) // 2           # unmasked (i, j <= i) pairs only
     pre_out = torch.empty_like(pre["q"])
+    cspec = synth.WORKLOADS["llama3_8b_gqa_chunked_prefill"]
+    chk_cpu = synth.make("llama3_8b_gqa_chunked_prefill")
+    chk = {k: v.to(dev) for k, v in chk_cpu.items()}
+    CB, CS, CHq, CD = chk["q"].shape
+    CT = chk["k"].shape[1]
+    chk_flops = 0
+    for P, n in zip(chk_cpu["start_pos"].tolist(), chk_cpu["q_lens"].tolist()):
+        P = max(0, min(P, CT))
+        n = max(0, min(n, CS, CT - P))
+        chk_flops += 4 * CHq * CD * (n * P + n * (n + 1) // 2)   # new token i sees P + i + 1 keys
+    chk_tokens = int(chk_cpu["q_lens"].sum())
+    chk_out = torch.empty_like(chk["q"])
     copy_src = copy_dst = None
     if args.copy_calibration:
         copy_src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
@@ -145,9 +159,13 @@ def main():
     def run_prefill():
         attn.attn_prefill_gqa_causal(pre["q"], pre["k"], pre["v"], out=pre_out)
 
+    def run_chunked():
+        attn.attn_prefill_gqa_cached(chk["q"], chk["k"], chk["v"], chk["start_pos"], chk["q_lens"], out=chk_out)
+
     # prefill for new requests, then the decode steps of running ones (the order a serving
     # step takes); each part is timed on its own
-    parts = [("prefill", run_prefill), ("mla_decode", run_mla), ("gqa_decode", run_decode)]
+    parts = [("prefill", run_prefill), ("chunked_prefill", run_chunked), ("mla_decode", run_mla),
+             ("gqa_decode", run_decode)]
     if args.copy_calibration:
         parts.append(("copy_1GiB", lambda: copy_dst.copy_(copy_src)))
 
@@ -174,6 +192,7 @@ def main():
     dec_gbs = dec_bytes / (ms["gqa_decode"] * 1e-3) / 1e9
     mla_gbs = mla_bytes / (ms["mla_decode"] * 1e-3) / 1e9
     pre_tfs = pre_flops / (ms["prefill"] * 1e-3) / 1e12
+    chk_tfs = chk_flops / (ms["chunked_prefill"] * 1e-3) / 1e12
 
     dec_hash = source_hash("decode_gqa.hip", "attn_internal.h")
     traffic = measured_traffic("gqa_decode_bf16<128, 1, true>", dec_hash)
@@ -195,8 +214,9 @@ def main():
             "workload": (f"llama3_8b_gqa_decode: B={B} Hq={Hq} Hkv={Hkv} head_dim={D} T_max={T_max} "
                          f"cache_lens~U[{dspec['lens'][0]},{dspec['lens'][1]}] (sum {sum_len}) seed={dspec['seed']}, "
                          "bf16 in, fp32 out, default schedule (device-wide unit queue, library-chosen blocks)"),
-            "step": "attn_prefill_gqa_causal, attn_decode_mla_absorbed, attn_decode_gqa: one call each, in this order",
-            "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "prefill": PB * S},
+            "step": ("attn_prefill_gqa_causal, attn_prefill_gqa_cached, attn_decode_mla_absorbed, attn_decode_gqa: "
+                     "one call each, in this order"),
+            "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "prefill": PB * S, "chunked_prefill": chk_tokens},
         },
         "roofline": {
             "bound": "hbm",
@@ -227,6 +247,13 @@ def main():
                         "tokens_per_s": round(PB * S / (ms["prefill"] * 1e-3), 1),
                         "workload": f"llama3_8b_gqa_prefill: B={PB} S={S} Hq={PHq} Hkv={pre['k'].shape[2]} "
                                     f"head_dim={PD} seed={pspec['seed']} bf16 causal"},
+            "chunked_prefill": {"ms": round(ms["chunked_prefill"], 5), "TFLOP/s": round(chk_tfs, 1),
+                                "mfma_frac": round(chk_tfs / BF16_DENSE_PEAK_TFLOPS, 4),
+                                "algorithmic_flops_per_launch": chk_flops,
+                                "tokens_per_s": round(chk_tokens / (ms["chunked_prefill"] * 1e-3), 1),
+                                "workload": f"llama3_8b_gqa_chunked_prefill: B={CB} chunk={CS} "
+                                            f"start_pos={cspec['start_pos']} T_max={CT} Hq={CHq} "
+                                            f"Hkv={chk['k'].shape[2]} head_dim={CD} seed={cspec['seed']} bf16"},
         },
         "input_generation_s": round(t_gen, 2),
     }

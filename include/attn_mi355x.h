@@ -1,7 +1,8 @@
 /*
  * attn_mi355x.h -- C ABI of a small attention library for AMD Instinct MI355X
  * (gfx950 / CDNA4): grouped-query attention over a KV cache (decode and causal
- * prefill) and multi-head latent attention (MLA) decode over a latent cache.
+ * prefill, also after a cached prefix) and multi-head latent attention (MLA)
+ * decode over a latent cache.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -134,6 +135,42 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
  */
 attn_status attn_prefill_gqa_causal(const void* q, const void* k, const void* v, void* out, int B,
                                     int S, int Hq, int Hkv, int head_dim, float softmax_scale,
+                                    attn_dtype in_dtype, attn_dtype out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Causal GQA prefill after a cached prefix (chunked prefill).
+ *
+ *   P = start_pos[b], n = q_lens[b] (q_lens NULL: n = S), for i < n:
+ *   out[b,i,h,:] = sum_{j <= P+i} softmax_j(scale * q[b,i,h,:] . k[b,j,g,:]) v[b,j,g,:]
+ *   out[b,i,h,:] = 0 for n <= i < S.
+ *
+ * This is Attention.forward on the "模型架构｜MQA & GQA 调研" page with
+ * start_pos > 0: the new tokens' K/V rows have been written into the cache at
+ * positions start_pos .. start_pos + seqlen - 1 before the call, the keys are
+ * the first start_pos + seqlen cache rows, and the causal mask is aligned to
+ * the bottom right, so new token i (at position P + i) sees every cached
+ * position up to and including its own.  start_pos = 0 for every sequence is
+ * attn_prefill_gqa_causal over the first S cache rows.  Same arithmetic as
+ * attn_prefill_gqa_causal (bf16 MFMA, fp32 accumulation, probabilities rounded
+ * to bf16 before PV).
+ *
+ *   q         [B, S, Hq, head_dim]      bf16 (the new tokens, padded to S)
+ *   k_cache   [B, T_max, Hkv, head_dim] bf16, v_cache likewise; read only at
+ *             rows 0 .. P + n - 1 of each sequence
+ *   start_pos [B] int32, device memory, required; clamped to [0, T_max]
+ *   q_lens    [B] int32, device memory, or NULL (all S); clamped to
+ *             [0, min(S, T_max - P)]
+ *   out       [B, S, Hq, head_dim]      out_dtype (ATTN_BF16 or ATTN_F32)
+ *
+ * All pointers are device memory owned by the caller.  Errors as for
+ * attn_prefill_gqa_causal, plus ATTN_ERR_NULL for a NULL start_pos and
+ * ATTN_ERR_SHAPE for T_max < 1.  The per-sequence values are not read on the
+ * host (they are device memory); the kernel clamps them as stated.  No
+ * workspace.
+ */
+attn_status attn_prefill_gqa_cached(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* start_pos, const int32_t* q_lens, void* out, int B, int S,
+                                    int Hq, int Hkv, int head_dim, int T_max, float softmax_scale,
                                     attn_dtype in_dtype, attn_dtype out_dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */

@@ -1,5 +1,5 @@
-"""Python binding of libattn_mi355x.so: GQA/MQA/MHA decode, causal GQA prefill and MLA
-absorbed decode on AMD MI355X (gfx950).
+"""Python binding of libattn_mi355x.so: GQA/MQA/MHA decode, causal GQA prefill (also after a
+cached prefix) and MLA absorbed decode on AMD MI355X (gfx950).
 
 The functions carry the C entry points' names and do argument marshalling only: they check
 that the torch tensors are CUDA (HIP) tensors of the right dtype, shape and layout, allocate
@@ -54,6 +54,8 @@ def _declare(lib):
     lib.attn_decode_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, Z, P]
     lib.attn_prefill_gqa_causal.restype = I
     lib.attn_prefill_gqa_causal.argtypes = [P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.attn_prefill_gqa_cached.restype = I
+    lib.attn_prefill_gqa_cached.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
     lib.attn_decode_mla_workspace_bytes.restype = Z
     lib.attn_decode_mla_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.attn_decode_mla_supported.restype = I
@@ -190,6 +192,33 @@ def attn_prefill_gqa_causal(q, k, v, out=None, softmax_scale: float = 0.0, out_d
     return out
 
 
+def attn_prefill_gqa_cached(q, k_cache, v_cache, start_pos, q_lens=None, out=None, softmax_scale: float = 0.0,
+                            out_dtype=torch.bfloat16):
+    """Causal prefill after a cached prefix: new token i of sequence b sits at position
+    start_pos[b] + i and attends cache rows j <= start_pos[b] + i; rows i >= q_lens[b] are zeros.
+
+    q [B,S,Hq,D] bf16 (new tokens), k_cache/v_cache [B,T_max,Hkv,D] bf16 already holding the new
+    rows at start_pos[b]..; start_pos, q_lens [B] int32 (q_lens None: S).  Returns out."""
+    _check(q, "q")
+    B, S, Hq, D = q.shape
+    _check(k_cache, "k_cache", dtype=q.dtype)
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError(f"k_cache must be [B={B}, T_max, Hkv, {D}] (got {tuple(k_cache.shape)})")
+    T_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _check(v_cache, "v_cache", shape=k_cache.shape, dtype=q.dtype)
+    _check(start_pos, "start_pos", shape=(B,), dtype=torch.int32)
+    if q_lens is not None:
+        _check(q_lens, "q_lens", shape=(B,), dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, S, Hq, D), dtype=out_dtype, device=q.device)
+    _check(out, "out", shape=(B, S, Hq, D))
+    st = lib().attn_prefill_gqa_cached(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(start_pos),
+                                       _ptr(q_lens), _ptr(out), B, S, Hq, Hkv, D,
+                                       T_max, float(softmax_scale), _dt(q), _dt(out), _stream(q.device))
+    _raise_if(st, "attn_prefill_gqa_cached")
+    return out
+
+
 def attn_decode_mla_workspace_bytes(B: int, H: int, kv_lora_rank: int, rope_dim: int, T_max: int,
                                     split_tokens: int = 0) -> int:
     return int(lib().attn_decode_mla_workspace_bytes(B, H, kv_lora_rank, rope_dim, T_max, split_tokens))
@@ -243,6 +272,6 @@ def attn_decode_mla_absorbed(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, cache_len
     return out
 
 
-__all__ = ["attn_decode_gqa", "attn_decode_gqa_workspace_bytes", "attn_prefill_gqa_causal",
+__all__ = ["attn_decode_gqa", "attn_decode_gqa_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached",
            "attn_decode_mla_absorbed", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",
            "AttnError", "lib", "header_functions", "LIB_PATH", "ATTN_F32", "ATTN_BF16"]

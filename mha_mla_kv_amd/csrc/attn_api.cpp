@@ -250,31 +250,38 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
   return hip_status(attn::launch_gqa_decode(a, static_cast<hipStream_t>(stream)), "attn_decode_gqa");
 }
 
-attn_status attn_prefill_gqa_causal(const void* q, const void* k, const void* v, void* out, int B,
-                                    int S, int Hq, int Hkv, int head_dim, float softmax_scale,
-                                    attn_dtype in_dtype, attn_dtype out_dtype, void* stream) {
+namespace {
+
+// Shared checks and launch of the two prefill entry points.  start_pos == null
+// means no cached prefix (k and v then hold exactly S rows per sequence).
+attn_status prefill_common(const char* fn, const void* q, const void* k, const void* v,
+                           const int32_t* start_pos, const int32_t* q_lens, void* out, int B, int S, int Hq,
+                           int Hkv, int head_dim, int T_kv, float softmax_scale, attn_dtype in_dtype,
+                           attn_dtype out_dtype, void* stream) {
   if (!q || !k || !v || !out)
-    return fail(ATTN_ERR_NULL, "attn_prefill_gqa_causal: q, k, v and out must be non-NULL");
-  if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || head_dim <= 0)
-    return fail(ATTN_ERR_SHAPE, "attn_prefill_gqa_causal: sizes must be positive (B=%d S=%d Hq=%d Hkv=%d head_dim=%d)",
-                B, S, Hq, Hkv, head_dim);
+    return fail(ATTN_ERR_NULL, "%s: q, k, v and out must be non-NULL", fn);
+  if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || head_dim <= 0 || T_kv <= 0)
+    return fail(ATTN_ERR_SHAPE, "%s: sizes must be positive (B=%d S=%d Hq=%d Hkv=%d head_dim=%d T=%d)", fn, B, S,
+                Hq, Hkv, head_dim, T_kv);
   if (B > kMaxGridYZ || Hq > kMaxGridYZ)
-    return fail(ATTN_ERR_SHAPE, "attn_prefill_gqa_causal: B and Hq must be <= %d", kMaxGridYZ);
+    return fail(ATTN_ERR_SHAPE, "%s: B and Hq must be <= %d", fn, kMaxGridYZ);
   if (Hq % Hkv != 0)
-    return fail(ATTN_ERR_GROUPS, "attn_prefill_gqa_causal: Hkv=%d does not divide Hq=%d (remainder %d); not rounded",
-                Hkv, Hq, Hq % Hkv);
+    return fail(ATTN_ERR_GROUPS, "%s: Hkv=%d does not divide Hq=%d (remainder %d); not rounded", fn, Hkv, Hq,
+                Hq % Hkv);
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_gqa_causal: unknown dtype");
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
   if (in_dtype != ATTN_BF16)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_gqa_causal: only bf16 inputs are built (MFMA path)");
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: only bf16 inputs are built (MFMA path)", fn);
   if (!attn::prefill_supported(head_dim))
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_gqa_causal: head_dim=%d is not built", head_dim);
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: head_dim=%d is not built", fn, head_dim);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_gqa_causal: q, k, v and out must be 16-byte aligned");
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: q, k, v and out must be 16-byte aligned", fn);
   attn::PrefillArgs a;
   a.q = q;
   a.k = k;
   a.v = v;
+  a.start_pos = start_pos;
+  a.q_lens = q_lens;
   a.out = out;
   a.B = B;
   a.S = S;
@@ -282,10 +289,30 @@ attn_status attn_prefill_gqa_causal(const void* q, const void* k, const void* v,
   a.Hkv = Hkv;
   a.D = head_dim;
   a.n_rep = Hq / Hkv;
+  a.T_kv = T_kv;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   a.scale_log2e = scale * kLog2e;
   a.out_bf16 = out_dtype == ATTN_BF16;
-  return hip_status(attn::launch_prefill(a, static_cast<hipStream_t>(stream)), "attn_prefill_gqa_causal");
+  return hip_status(attn::launch_prefill(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace
+
+attn_status attn_prefill_gqa_causal(const void* q, const void* k, const void* v, void* out, int B,
+                                    int S, int Hq, int Hkv, int head_dim, float softmax_scale,
+                                    attn_dtype in_dtype, attn_dtype out_dtype, void* stream) {
+  return prefill_common("attn_prefill_gqa_causal", q, k, v, nullptr, nullptr, out, B, S, Hq, Hkv, head_dim, S,
+                        softmax_scale, in_dtype, out_dtype, stream);
+}
+
+attn_status attn_prefill_gqa_cached(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* start_pos, const int32_t* q_lens, void* out, int B, int S,
+                                    int Hq, int Hkv, int head_dim, int T_max, float softmax_scale,
+                                    attn_dtype in_dtype, attn_dtype out_dtype, void* stream) {
+  if (!start_pos)
+    return fail(ATTN_ERR_NULL, "attn_prefill_gqa_cached: start_pos must be non-NULL");
+  return prefill_common("attn_prefill_gqa_cached", q, k_cache, v_cache, start_pos, q_lens, out, B, S, Hq, Hkv,
+                        head_dim, T_max, softmax_scale, in_dtype, out_dtype, stream);
 }
 
 size_t attn_decode_mla_workspace_bytes(int B, int H, int kv_lora_rank, int rope_dim, int T_max,

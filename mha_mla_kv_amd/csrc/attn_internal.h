@@ -39,11 +39,14 @@ struct GqaDecodeArgs {
 };
 
 struct PrefillArgs {
-  const void* q;  // [B, S, Hq, D] bf16
-  const void* k;  // [B, S, Hkv, D] bf16
-  const void* v;  // [B, S, Hkv, D] bf16
-  void* out;      // [B, S, Hq, D]
+  const void* q;                // [B, S, Hq, D] bf16 (the new tokens)
+  const void* k;                // [B, T_kv, Hkv, D] bf16
+  const void* v;                // [B, T_kv, Hkv, D] bf16
+  const int32_t* start_pos;     // [B] cached prefix length, or null: 0
+  const int32_t* q_lens;        // [B] new tokens per sequence, or null: S
+  void* out;                    // [B, S, Hq, D]
   int B, S, Hq, Hkv, D, n_rep;
+  int T_kv;                     // key rows per sequence in k and v (S without a prefix)
   float scale_log2e;
   int out_bf16;
 };

@@ -1,11 +1,15 @@
-// Causal GQA prefill on bf16 MFMA for gfx950.
+// Causal GQA prefill on bf16 MFMA for gfx950, with or without a cached prefix.
 //
-// What is computed: out[b,i,h] = sum_{j<=i} softmax_j(scale q[b,i,h].k[b,j,g]) v[b,j,g]
-// with g = floor(h / n_rep) -- Attention.forward of the "模型架构｜MQA & GQA 调研"
-// page (code section) with start_pos = 0 and its additive causal mask, i.e. the
-// scaled_dot_product_attention(is_causal=True) call in the MultiHeadLatentAttention
-// listing of the qqstock DeepSeek MLA article.  P is rounded to bf16 before the
-// PV product, as the page's softmax(...).type_as(xq) does.
+// What is computed: out[b,i,h] = sum_{j<=P+i} softmax_j(scale q[b,i,h].k[b,j,g]) v[b,j,g]
+// with g = floor(h / n_rep) and P = start_pos[b] the number of cached positions
+// before the new tokens -- Attention.forward of the "模型架构｜MQA & GQA 调研"
+// page (code section): the new K/V rows sit in the cache at start_pos.., the keys
+// are the first start_pos + seqlen cache rows, and the additive causal mask is
+// aligned to the bottom right, so new token i (position P + i) sees every cached
+// position up to its own.  P = 0 is the scaled_dot_product_attention(is_causal=True)
+// call in the MultiHeadLatentAttention listing of the qqstock DeepSeek MLA
+// article.  Rows i >= q_lens[b] are written as zeros.  P is rounded to bf16
+// before the PV product, as the page's softmax(...).type_as(xq) does.
 //
 // How (not from the pages; designed for CDNA4):
 //  * One workgroup = 4 waves = a tile of 128 query rows of one (head, sequence);
@@ -31,6 +35,8 @@
 //    it by more than 2^8: probabilities then stay below 256, far inside bf16 and
 //    fp32 range, and most tiles skip the O rescale.
 //  * A wave skips tiles entirely above its diagonal; only diagonal tiles mask.
+//    With a prefix the diagonal is shifted right by P; a q-tile with no new
+//    token left writes zeros and reads nothing.
 #include <hip/hip_runtime.h>
 
 #include "attn_internal.h"
@@ -117,11 +123,12 @@ struct TileCopy {
     }
   }
 
-  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const u16* p, int kt, int n_kt, int S, int row_bytes) {
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const u16* p, int kt, int n_kt, int kv_len,
+                                                                int row_bytes) {
     const bool ok = kt >= 0 && kt < n_kt;
     const int key0 = ok ? kt * kBN : 0;
     const char* base = reinterpret_cast<const char*>(p) + (size_t)key0 * row_bytes;
-    const unsigned long long end = (unsigned long long)(S - 1 - key0) * row_bytes + 2 * D;
+    const unsigned long long end = (unsigned long long)(kv_len - 1 - key0) * row_bytes + 2 * D;
     const unsigned num = ok ? (unsigned)(end < 0xffffffffull ? end : 0xffffffffull) : 0u;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)num, 0x00020000);
   }
@@ -168,9 +175,10 @@ __device__ __forceinline__ Tile map_tile(const PrefillArgs& a, int id) {
   return t;
 }
 
-// Per-lane constants of a wave.
+// Per-lane constants of a wave.  row0 / my_row index the new tokens; pos0 /
+// my_pos are their positions in the sequence (P added), which the causal cut uses.
 struct Lane {
-  int lane, ln, h2, row0, my_row;
+  int lane, ln, h2, row0, my_row, pos0, my_pos;
   float c;  // softmax scale * log2(e)
 };
 
@@ -257,18 +265,18 @@ struct RowState {
 template <int D>
 __device__ __forceinline__ void tile_step(RowState<D>& st, const u16* kc, const u16* vc, u16* kn, u16* vn,
                                           const bf16x8 (&qop)[D / 16], int kt, int n_kt, int last_kt,
-                                          const u16* kp, const u16* vp, int row_bytes, int S,
+                                          const u16* kp, const u16* vp, int row_bytes, int kv_len,
                                           const TileCopy<D>& cp, const LdsOffsets& off, const Lane& w) {
   if (kt + 1 < n_kt) {  // (kn, vn) were released by the last barrier
-    cp.issue(kn, TileCopy<D>::rsrc(kp, kt + 1, n_kt, S, row_bytes));
-    cp.issue(vn, TileCopy<D>::rsrc(vp, kt + 1, n_kt, S, row_bytes));
+    cp.issue(kn, TileCopy<D>::rsrc(kp, kt + 1, n_kt, kv_len, row_bytes));
+    cp.issue(vn, TileCopy<D>::rsrc(vp, kt + 1, n_kt, kv_len, row_bytes));
   }
   if (kt <= last_kt) {
     const int kv0 = kt * kBN;
     f32x16 sc[2];
     qk_tile<D>(sc, kc, qop, off.k);
-    if (kv0 + kBN - 1 > w.row0) {  // the tile reaches above the diagonal of some row
-      const int t = w.my_row - kv0 - 4 * w.h2;
+    if (kv0 + kBN - 1 > w.pos0) {  // the tile reaches above the diagonal of some row
+      const int t = w.my_pos - kv0 - 4 * w.h2;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -313,6 +321,36 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, const u16* kc, const 
   __syncthreads();  // ... and everyone's; nobody reads tile kt any more
 }
 
+// Stores one output row from the O^T accumulators (lane holds O^T[dims
+// 32d + 8(i/4) + 4h2 + (i%4)][row ln]) times inv, or zeros when !valid.
+template <int D>
+__device__ __forceinline__ void store_rows(void* out, size_t orow, int out_bf16, const f32x16 (&o)[D / 32], bool valid,
+                                           float inv, int h2) {
+  constexpr int DB = D / 32;
+  if (out_bf16) {
+    u16* op = static_cast<u16*>(out) + orow * D;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        u16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = __builtin_bit_cast(u16, (__bf16)(valid ? o[d][4 * q4 + e] * inv : 0.f));
+        *reinterpret_cast<u16x4*>(op + 32 * d + 8 * q4 + 4 * h2) = o4;
+      }
+  } else {
+    float* op = static_cast<float*>(out) + orow * D;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (valid) f = make_float4(o[d][4 * q4] * inv, o[d][4 * q4 + 1] * inv, o[d][4 * q4 + 2] * inv, o[d][4 * q4 + 3] * inv);
+        *reinterpret_cast<float4*>(op + 32 * d + 8 * q4 + 4 * h2) = f;
+      }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_causal(PrefillArgs a) {
   static_assert(D % 32 == 0 && D <= 128, "head_dim");
@@ -331,29 +369,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int q0 = tl.qt * kBM;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // cached prefix P (clamped to the cache) and new tokens n_q (clamped to S and
+  // to the room left in the cache)
+  const int P = a.start_pos ? min(max(a.start_pos[b], 0), a.T_kv) : 0;
+  const int n_q = min(a.q_lens ? min(max(a.q_lens[b], 0), a.S) : a.S, a.T_kv - P);
   Lane w;
   w.lane = tid & 63;
   w.ln = w.lane & 31;
   w.h2 = w.lane >> 5;
   w.row0 = q0 + wave * 32;
   w.my_row = w.row0 + w.ln;
+  w.pos0 = P + w.row0;
+  w.my_pos = P + w.my_row;
   w.c = a.scale_log2e;
 
   const size_t q_row = (size_t)a.Hq * D;
   const int row_bytes = a.Hkv * D * 2;
+  const size_t orow = ((size_t)b * a.S + w.my_row) * a.Hq + h;
+  if (q0 >= n_q) {  // no new token in this q-tile: zero rows, nothing to read
+    const f32x16 none[D / 32] = {};
+    if (w.my_row < a.S) store_rows<D>(a.out, orow, a.out_bf16, none, false, 0.f, w.h2);
+    return;
+  }
   const u16* qp = static_cast<const u16*>(a.q) + ((size_t)b * a.S * a.Hq + h) * D;
-  const u16* kp = static_cast<const u16*>(a.k) + ((size_t)b * a.S * a.Hkv + g) * D;
-  const u16* vp = static_cast<const u16*>(a.v) + ((size_t)b * a.S * a.Hkv + g) * D;
+  const u16* kp = static_cast<const u16*>(a.k) + ((size_t)b * a.T_kv * a.Hkv + g) * D;
+  const u16* vp = static_cast<const u16*>(a.v) + ((size_t)b * a.T_kv * a.Hkv + g) * D;
 
-  // keys needed by the workgroup: [0, min(S, q0 + BM)); tiles 0..last_kt are
-  // visible to some row of this wave
-  const int kv_end = min(a.S, q0 + kBM);
+  // keys of the sequence: [0, kv_len); keys needed by the workgroup:
+  // [0, min(kv_len, P + q0 + BM)); tiles 0..last_kt are visible to some row of
+  // this wave
+  const int kv_len = P + n_q;
+  const int kv_end = min(kv_len, P + q0 + kBM);
   const int n_kt = (kv_end + kBN - 1) / kBN;
-  const int last_kt = min(n_kt - 1, (w.row0 + 31) / kBN);
+  const int last_kt = min(n_kt - 1, (w.pos0 + 31) / kBN);
 
   const TileCopy<D> cp(wave, w.lane, row_bytes);
-  cp.issue(k0, TileCopy<D>::rsrc(kp, 0, n_kt, a.S, row_bytes));
-  cp.issue(v0, TileCopy<D>::rsrc(vp, 0, n_kt, a.S, row_bytes));
+  cp.issue(k0, TileCopy<D>::rsrc(kp, 0, n_kt, kv_len, row_bytes));
+  cp.issue(v0, TileCopy<D>::rsrc(vp, 0, n_kt, kv_len, row_bytes));
   const LdsOffsets off = lds_offsets<D>(w);
 
   // Q^T as the B operand: lane holds Q[row ln][16c + 8h2 ..+8]
@@ -375,38 +427,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   wait_vmem();
   __syncthreads();
   for (int kt = 0; kt < n_kt; kt += 2) {
-    tile_step<D>(st, k0, v0, k1, v1, qop, kt, n_kt, last_kt, kp, vp, row_bytes, a.S, cp, off, w);
+    tile_step<D>(st, k0, v0, k1, v1, qop, kt, n_kt, last_kt, kp, vp, row_bytes, kv_len, cp, off, w);
     if (kt + 1 < n_kt)
-      tile_step<D>(st, k1, v1, k0, v0, qop, kt + 1, n_kt, last_kt, kp, vp, row_bytes, a.S, cp, off, w);
+      tile_step<D>(st, k1, v1, k0, v0, qop, kt + 1, n_kt, last_kt, kp, vp, row_bytes, kv_len, cp, off, w);
   }
 
-  // normalise and store: lane holds O^T[dims 32d + 8(i/4) + 4h2 + (i%4)][row ln]
+  // normalise and store; rows past the new tokens are zeros
   const float lsum = sum_xor32(st.lsum);
-  if (w.my_row < a.S) {
-    const float inv = 1.f / lsum;
-    const size_t orow = ((size_t)b * a.S + w.my_row) * a.Hq + h;
-    if (a.out_bf16) {
-      u16* op = static_cast<u16*>(a.out) + orow * D;
-#pragma unroll
-      for (int d = 0; d < DB; ++d)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          u16x4 o4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o4[e] = __builtin_bit_cast(u16, (__bf16)(st.o[d][4 * q4 + e] * inv));
-          *reinterpret_cast<u16x4*>(op + 32 * d + 8 * q4 + 4 * w.h2) = o4;
-        }
-    } else {
-      float* op = static_cast<float*>(a.out) + orow * D;
-#pragma unroll
-      for (int d = 0; d < DB; ++d)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<float4*>(op + 32 * d + 8 * q4 + 4 * w.h2) =
-              make_float4(st.o[d][4 * q4] * inv, st.o[d][4 * q4 + 1] * inv, st.o[d][4 * q4 + 2] * inv,
-                          st.o[d][4 * q4 + 3] * inv);
-    }
-  }
+  if (w.my_row < a.S) store_rows<D>(a.out, orow, a.out_bf16, st.o, w.my_row < n_q, 1.f / lsum, w.h2);
 }
 
 }  // namespace

@@ -82,6 +82,28 @@ def gqa_prefill_inputs(B: int, S: int, Hq: int, Hkv: int, D: int, dtype: str = "
     return {"q": q, "k": k, "v": v}
 
 
+def gqa_prefill_cached_inputs(B: int, S: int, Hq: int, Hkv: int, D: int, T_max: int, start_pos,
+                              q_lens=None, dtype: str = "bf16", seed: int = 0, poison: bool = True) -> dict:
+    """Chunked prefill after a cached prefix: q [B,S,Hq,D] (the new tokens, padded to S), k/v
+    caches [B,T_max,Hkv,D] already holding the new tokens' rows at start_pos[b]..,
+    start_pos [B] and q_lens [B] int32 (``_lengths`` forms; q_lens None: S each).  Draw order q,
+    k, v, start_pos, q_lens.  With poison, q rows past q_lens[b] and cache rows past
+    start_pos[b] + q_lens[b] are NaN."""
+    rng = _rng(seed)
+    q = _as(_normal(rng, (B, S, Hq, D)), dtype)
+    k = _as(_normal(rng, (B, T_max, Hkv, D)), dtype)
+    v = _as(_normal(rng, (B, T_max, Hkv, D)), dtype)
+    sp = _lengths(rng, B, T_max, start_pos)
+    ql = _lengths(rng, B, S, S if q_lens is None else q_lens)
+    if poison:
+        _poison_tail(q, ql)
+        end = np.minimum(np.maximum(sp.astype(np.int64), 0) + np.maximum(ql, 0), T_max).astype(np.int32)
+        _poison_tail(k, end)
+        _poison_tail(v, end)
+    return {"q": q, "k": k, "v": v, "start_pos": torch.from_numpy(sp.copy()),
+            "q_lens": torch.from_numpy(ql.copy())}
+
+
 def mla_decode_inputs(B: int, H: int, nope_head_dim: int, rope_dim: int, v_head_dim: int,
                       kv_lora_rank: int, T_max: int, lens, dtype: str = "bf16", seed: int = 0,
                       poison: bool = True) -> dict:
@@ -121,6 +143,8 @@ WORKLOADS = {
                          dtype="bf16", seed=3),
     "llama3_8b_gqa_prefill": dict(kind="gqa_prefill", B=4, S=4096, Hq=32, Hkv=8, D=128,
                                   dtype="bf16", seed=4),
+    "llama3_8b_gqa_chunked_prefill": dict(kind="gqa_prefill_cached", B=4, S=512, Hq=32, Hkv=8, D=128,
+                                          T_max=4096, start_pos=3584, q_lens=512, dtype="bf16", seed=6),
     "minimind768_mla_decode": dict(kind="mla_decode", B=64, H=8, nope_head_dim=96, rope_dim=48,
                                    v_head_dim=96, kv_lora_rank=128, T_max=4096, lens=4096,
                                    dtype="bf16", seed=5),
@@ -136,6 +160,8 @@ def make(name_or_spec, **overrides) -> dict:
         return gqa_decode_inputs(**spec)
     if kind == "gqa_prefill":
         return gqa_prefill_inputs(**spec)
+    if kind == "gqa_prefill_cached":
+        return gqa_prefill_cached_inputs(**spec)
     if kind == "mla_decode":
         return mla_decode_inputs(**spec)
     raise ValueError(kind)

@@ -22,7 +22,8 @@ no_gpu_only = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer
 def test_library_loads_and_exports_every_declared_symbol():
     lib = attn.lib()
     names = attn.header_functions()
-    for required in ("attn_decode_gqa", "attn_prefill_gqa_causal", "attn_decode_mla_absorbed"):
+    for required in ("attn_decode_gqa", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached",
+                     "attn_decode_mla_absorbed"):
         assert required in names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/attn_mi355x.h but not exported"
@@ -106,6 +107,24 @@ def test_prefill_validation():
     assert f(ind=F32) == UNSUP
     assert f(D=80) == UNSUP
     assert f(out=FAKE_MIS) == UNSUP
+
+
+@no_gpu_only
+def test_cached_prefill_validation():
+    lib = attn.lib()
+
+    def f(**kw):
+        return lib.attn_prefill_gqa_cached(kw.get("q", FAKE), FAKE, FAKE, kw.get("sp", FAKE), kw.get("ql", FAKE),
+                                           FAKE, kw.get("B", 2), kw.get("S", 16), kw.get("Hq", 8), kw.get("Hkv", 2),
+                                           kw.get("D", 128), kw.get("T", 64), 0.0, kw.get("ind", BF16), BF16, None)
+    assert f(sp=None) == NULL
+    assert f(q=None) == NULL
+    assert f(T=0) == SHAPE
+    assert f(S=0) == SHAPE
+    assert f(Hq=8, Hkv=3) == GROUPS
+    assert f(ind=F32) == UNSUP
+    assert f(D=96) == UNSUP
+    assert f(q=FAKE_MIS) == UNSUP
 
 
 @no_gpu_only
