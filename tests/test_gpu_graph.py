@@ -1,4 +1,4 @@
-"""The three entry points captured in a HIP graph (torch.cuda.graph) and replayed.
+"""The compute entry points captured in a HIP graph (torch.cuda.graph) and replayed.
 
 Each call is launched with a caller-provided workspace, so it allocates nothing; the GQA
 decode's work-queue counter is returned to zero by the call itself, so every replay starts
@@ -71,3 +71,16 @@ def test_prefill_graph_replay():
     out = torch.empty_like(inp["q"])
     eager = _graph_matches_eager(lambda: attn.attn_prefill_gqa_causal(inp["q"], inp["k"], inp["v"], out=out), out)
     assert torch.isfinite(eager.float()).all()
+
+
+def test_cached_prefill_graph_replay():
+    import mha_mla_kv_amd as attn
+    B, S, Hq, Hkv, D, T = 2, 300, 16, 4, 128, 1200
+    inp = {k: v.cuda() for k, v in synth.gqa_prefill_cached_inputs(B, S, Hq, Hkv, D, T, [700, 64], [300, 111],
+                                                                   seed=10).items()}
+    print(f"[case] cached prefill graph B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} T={T}", flush=True)
+    out = torch.empty_like(inp["q"])
+    eager = _graph_matches_eager(lambda: attn.attn_prefill_gqa_cached(inp["q"], inp["k"], inp["v"], inp["start_pos"],
+                                                                      inp["q_lens"], out=out), out)
+    assert torch.isfinite(eager.float()).all()
+    assert not eager[1, 111:].any()  # rows past the chunk are zeros
