@@ -52,6 +52,8 @@ def _declare(lib):
     lib.oracle_gqa_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, D]
     lib.oracle_gqa_prefill_causal.restype = None
     lib.oracle_gqa_prefill_causal.argtypes = [P, P, P, P, I, I, I, I, I, D, P, I]
+    lib.oracle_mla_prefill_causal.restype = None
+    lib.oracle_mla_prefill_causal.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, D]
     lib.oracle_gqa_prefill_cached.restype = None
     lib.oracle_gqa_prefill_cached.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D]
     for name in ("oracle_mla_decode_decompressed", "oracle_mla_decode_absorbed"):
@@ -176,6 +178,30 @@ def mla_decode_absorbed(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, cache_lens,
     """MLA decode with W_UK folded into the query and W_UV applied after the weighted sum."""
     return _mla("oracle_mla_decode_absorbed", q_nope, q_rope, w_uk, w_uv, c_kv, k_rope,
                 cache_lens, softmax_scale, bh, lib)
+
+
+def mla_prefill_causal(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, start_pos=None, q_lens=None,
+                       softmax_scale: float = 0.0, lib=None) -> np.ndarray:
+    """MLA causal prefill (keys/values rebuilt from the latent): q_nope [B,S,H,dn], q_rope
+    [B,S,H,dR], w_uk [H,dn,r], w_uv [H,dv,r], c_kv [B,T_max,r], k_rope [B,T_max,dR] holding the
+    new rows at start_pos[b].. (None: 0), q_lens [B] or None (S) -> out [B,S,H,dv] float64."""
+    q_nope, q_rope, w_uk, w_uv = _f32(q_nope), _f32(q_rope), _f32(w_uk), _f32(w_uv)
+    c_kv, k_rope = _f32(c_kv), _f32(k_rope)
+    B, S, H, dn = q_nope.shape
+    dR = q_rope.shape[3]
+    _, dv, r = w_uv.shape
+    T_max = c_kv.shape[1]
+    assert q_rope.shape == (B, S, H, dR) and w_uk.shape == (H, dn, r) and w_uv.shape == (H, dv, r)
+    assert c_kv.shape == (B, T_max, r) and k_rope.shape == (B, T_max, dR)
+    sp = None if start_pos is None else _i32(start_pos)
+    ql = None if q_lens is None else _i32(q_lens)
+    assert sp is None or sp.shape == (B,)
+    assert ql is None or ql.shape == (B,)
+    out = np.zeros((B, S, H, dv), dtype=np.float64)
+    (lib or load()).oracle_mla_prefill_causal(_p(q_nope), _p(q_rope), _p(w_uk), _p(w_uv), _p(c_kv), _p(k_rope),
+                                              _p(sp), _p(ql), _p(out), B, S, H, dn, dR, dv, r, T_max,
+                                              float(softmax_scale))
+    return out
 
 
 def threads(lib=None) -> int:

@@ -273,6 +273,91 @@ void oracle_mla_decode_decompressed(const float* q_nope, const float* q_rope,
 }
 
 /*
+ * MLA causal prefill, decompressed form: the scaled_dot_product_attention
+ * (is_causal=True) call of the MultiHeadLatentAttention listing on the qqstock
+ * DeepSeek MLA article, with the keys and values rebuilt from the latent cache.
+ *   q_nope [B, S, H, dn]   q_rope [B, S, H, dR]   (the new tokens; q_rope rotated)
+ *   w_uk [H, dn, r]   w_uv [H, dv, r]   (per-head rows of the up-projections)
+ *   c_kv [B, T_max, r]   k_rope [B, T_max, dR]   (the new tokens' rows already
+ *   written at start_pos[b] ..)   start_pos [B] or NULL (0)   q_lens [B] or NULL (S)
+ *   out [B, S, H, dv]
+ *   k_nope[h,t] = w_uk[h] c_kv[b,t];  v[h,t] = w_uv[h] c_kv[b,t]
+ *   s_j = scale * (q_nope[b,i,h] . k_nope[h,j] + q_rope[b,i,h] . k_rope[b,j])
+ *   out[b,i,h] = sum_{j <= P + i} softmax(s)_j v[h,j]   for i < n_b; zeros after.
+ * P = start_pos[b] clamped to [0, T_max]; n_b = q_lens[b] clamped to
+ * [0, min(S, T_max - P)].  The rebuilt keys and values of a (sequence, head)
+ * are computed once, as the listing materialises key_nope and value.
+ */
+void oracle_mla_prefill_causal(const float* q_nope, const float* q_rope,
+                               const float* w_uk, const float* w_uv,
+                               const float* c_kv, const float* k_rope,
+                               const int32_t* start_pos, const int32_t* q_lens,
+                               double* out, int B, int S, int H, int dn, int dR,
+                               int dv, int r, int T_max, double scale) {
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)(dn + dR));
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int b = 0; b < B; ++b) {
+    for (int h = 0; h < H; ++h) {
+      const int P = start_pos ? clamp_len(start_pos[b], T_max) : 0;
+      int nq = q_lens ? (int)q_lens[b] : S;
+      if (nq > S) nq = S;
+      if (nq > T_max - P) nq = T_max - P;
+      if (nq < 0) nq = 0;
+      for (int i = nq; i < S; ++i) {
+        double* o = out + (((long)b * S + i) * H + h) * dv;
+        for (int e = 0; e < dv; ++e) o[e] = 0.0;
+      }
+      if (nq == 0) continue;
+      const int L = P + nq; /* cache rows any new token of this sequence sees */
+      const float* Wk = w_uk + (long)h * dn * r;
+      const float* Wv = w_uv + (long)h * dv * r;
+      double* kn = (double*)malloc(sizeof(double) * (size_t)L * dn);
+      double* vv = (double*)malloc(sizeof(double) * (size_t)L * dv);
+      double* sc = (double*)malloc(sizeof(double) * (size_t)L);
+      for (int t = 0; t < L; ++t) {
+        const float* c = c_kv + ((long)b * T_max + t) * r;
+        for (int i = 0; i < dn; ++i) {
+          double a = 0.0;
+          for (int j = 0; j < r; ++j) a += (double)Wk[(long)i * r + j] * (double)c[j];
+          kn[(long)t * dn + i] = a;
+        }
+        for (int e = 0; e < dv; ++e) {
+          double a = 0.0;
+          for (int j = 0; j < r; ++j) a += (double)Wv[(long)e * r + j] * (double)c[j];
+          vv[(long)t * dv + e] = a;
+        }
+      }
+      for (int i = 0; i < nq; ++i) {
+        const float* qn = q_nope + (((long)b * S + i) * H + h) * dn;
+        const float* qr = q_rope + (((long)b * S + i) * H + h) * dR;
+        const int n = P + i + 1; /* keys 0 .. P + i */
+        for (int t = 0; t < n; ++t) {
+          const float* kr = k_rope + ((long)b * T_max + t) * dR;
+          double dot = 0.0;
+          for (int d = 0; d < dn; ++d) dot += (double)qn[d] * kn[(long)t * dn + d];
+          for (int e = 0; e < dR; ++e) dot += (double)qr[e] * (double)kr[e];
+          sc[t] = scale * dot;
+        }
+        double m = sc[0];
+        for (int t = 1; t < n; ++t)
+          if (sc[t] > m) m = sc[t];
+        double denom = 0.0;
+        for (int t = 0; t < n; ++t) denom += exp(sc[t] - m);
+        double* o = out + (((long)b * S + i) * H + h) * dv;
+        for (int e = 0; e < dv; ++e) o[e] = 0.0;
+        for (int t = 0; t < n; ++t) {
+          const double p = exp(sc[t] - m) / denom;
+          for (int e = 0; e < dv; ++e) o[e] += p * vv[(long)t * dv + e];
+        }
+      }
+      free(sc);
+      free(vv);
+      free(kn);
+    }
+  }
+}
+
+/*
  * MLA decode, absorbed form: the k-nope up-projection is folded into the query
  * and the value up-projection is applied once after the weighted sum.
  *   q_abs[j] = sum_i w_uk[h][i][j] q_nope[b,h][i]           (j < r)

@@ -18,6 +18,9 @@ oracle disagrees with:
   * cached-prefix prefill: torch SDPA with an explicit position mask, an empty
     prefix reducing to causal prefill, and each new row equal to a decode at its
     own position;
+  * MLA prefill: the listing's own scaled_dot_product_attention(is_causal=True) over
+    keys and values rebuilt with F.linear, and each new row equal to an MLA decode
+    at its position;
   * the empty cache giving zeros (a reading; the pages are silent).
 The tests run them on the real oracle; tests/test_oracle_mutants.py runs them on
 broken copies and requires that each planted mistake trips at least one pin.
@@ -410,6 +413,82 @@ def pin_mla_selection(lib):
             assert np.array_equal(out[0, h], want), "MLA selection"
 
 
+def sdpa_mla_prefill_ref(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, start_pos, q_lens, scale=None):
+    """The listing's prefill: keys [F.linear(c, W_UK) , k_rope broadcast to every head], values
+    F.linear(c, W_UV), torch SDPA per sequence; is_causal=True when there is no prefix, else an
+    explicit mask letting new token i (position P + i) see cache rows j <= P + i."""
+    B, S, H, dn = q_nope.shape
+    dR = q_rope.shape[3]
+    dv, r = w_uv.shape[1], w_uv.shape[2]
+    Wk = torch.from_numpy(w_uk.astype(np.float64)).reshape(H * dn, r)
+    Wv = torch.from_numpy(w_uv.astype(np.float64)).reshape(H * dv, r)
+    out = np.zeros((B, S, H, dv))
+    for b in range(B):
+        P, n = int(start_pos[b]), int(q_lens[b])
+        if n == 0:
+            continue
+        L = P + n
+        c = torch.from_numpy(c_kv[b, :L].astype(np.float64))
+        k_nope = F.linear(c, Wk).view(L, H, dn).permute(1, 0, 2)
+        value = F.linear(c, Wv).view(L, H, dv).permute(1, 0, 2)
+        kr = torch.from_numpy(k_rope[b, :L].astype(np.float64))[None].expand(H, L, dR)
+        k_rec = torch.cat([k_nope, kr], dim=-1)[None]
+        q_rec = torch.cat([torch.from_numpy(q_nope[b, :n].astype(np.float64)),
+                           torch.from_numpy(q_rope[b, :n].astype(np.float64))], dim=-1).permute(1, 0, 2)[None]
+        if P == 0:
+            o = F.scaled_dot_product_attention(q_rec, k_rec, value[None], is_causal=True, scale=scale)
+        else:
+            mask = torch.arange(L)[None, :] <= (P + torch.arange(n))[:, None]
+            o = F.scaled_dot_product_attention(q_rec, k_rec, value[None], attn_mask=mask, scale=scale)
+        out[b, :n] = o[0].permute(1, 0, 2).numpy()
+    return out
+
+
+MLA_PREFILL_SHAPES = [
+    # B, S, H, dn, dR, dv, r, T_max, start_pos, q_lens
+    (2, 6, 4, 8, 4, 6, 16, 6, [0, 0], [6, 6]),
+    (2, 5, 3, 8, 4, 6, 16, 14, [7, 2], [5, 3]),
+    (1, 7, 8, 96, 48, 96, 128, 12, [5], [7]),
+]
+
+
+def pin_mla_prefill_vs_sdpa(lib):
+    for i, (B, S, H, dn, dR, dv, r, T, sp, ql) in enumerate(MLA_PREFILL_SHAPES):
+        rng = _rng(500 + i)
+        qn, qr = _rand(rng, B, S, H, dn), _rand(rng, B, S, H, dR)
+        w_uk = _rand(rng, H, dn, r) / np.float32(math.sqrt(r))
+        w_uv = _rand(rng, H, dv, r) / np.float32(math.sqrt(r))
+        c, kr = _rand(rng, B, T, r), _rand(rng, B, T, dR)
+        sp, ql = np.array(sp, np.int32), np.array(ql, np.int32)
+        got = oracle.mla_prefill_causal(qn, qr, w_uk, w_uv, c, kr, sp, ql, lib=lib)
+        _close(got, sdpa_mla_prefill_ref(qn, qr, w_uk, w_uv, c, kr, sp, ql), what=f"MLA prefill {i}")
+        for b in range(B):
+            assert not np.any(got[b, ql[b]:]), "MLA prefill rows past q_lens"
+        _close(oracle.mla_prefill_causal(qn, qr, w_uk, w_uv, c, kr, sp, ql, softmax_scale=0.09, lib=lib),
+               sdpa_mla_prefill_ref(qn, qr, w_uk, w_uv, c, kr, sp, ql, scale=0.09), what="MLA prefill scale")
+
+
+def pin_mla_prefill_rows_are_decodes(lib):
+    """New token i of an MLA prefill equals an MLA decode of its query over the cache up to its
+    own position (the decode is pinned on its own), in both the decompressed and absorbed forms."""
+    rng = _rng(31)
+    B, S, H, dn, dR, dv, r, T = 2, 5, 4, 16, 8, 12, 32, 20
+    qn, qr = _rand(rng, B, S, H, dn), _rand(rng, B, S, H, dR)
+    w_uk = _rand(rng, H, dn, r) / np.float32(math.sqrt(r))
+    w_uv = _rand(rng, H, dv, r) / np.float32(math.sqrt(r))
+    c, kr = _rand(rng, B, T, r), _rand(rng, B, T, dR)
+    sp = np.array([11, 0], np.int32)
+    got = oracle.mla_prefill_causal(qn, qr, w_uk, w_uv, c, kr, sp, None, lib=lib)
+    for i in range(S):
+        args = (np.ascontiguousarray(qn[:, i]), np.ascontiguousarray(qr[:, i]), w_uk, w_uv, c, kr, sp + i + 1)
+        _close(got[:, i], oracle.mla_decode_decompressed(*args, lib=lib), 1e-13, f"MLA prefill row {i}")
+        _close(got[:, i], oracle.mla_decode_absorbed(*args, lib=lib), 1e-12, f"MLA prefill row {i} absorbed")
+    # no prefix and no q_lens is the same as start_pos 0 and q_lens S
+    _close(oracle.mla_prefill_causal(qn, qr, w_uk, w_uv, c, kr, None, None, lib=lib),
+           oracle.mla_prefill_causal(qn, qr, w_uk, w_uv, c, kr, np.zeros(B, np.int32), np.full(B, S, np.int32),
+                                     lib=lib), 0.0, "MLA prefill defaults")
+
+
 ALL_PINS = [pin_decode_vs_sdpa, pin_decode_closed_forms, pin_decode_invariants, pin_decode_head_structure,
             pin_prefill_vs_sdpa, pin_prefill_rows, pin_cached_vs_sdpa, pin_cached_reductions, pin_mla_vs_sdpa, pin_mla_absorbed_equals_decompressed,
-            pin_mla_selection]
+            pin_mla_selection, pin_mla_prefill_vs_sdpa, pin_mla_prefill_rows_are_decodes]

@@ -36,6 +36,12 @@ MUTATIONS = {
     "cached_top_left": ("const int n = P + i + 1; /* keys 0 .. P + i */", "const int n = i + 1;"),
     # cached prefill attends the whole new chunk (no causal cut among the new tokens)
     "cached_no_causal_cut": ("const int n = P + i + 1; /* keys 0 .. P + i */", "const int n = P + nq;"),
+    # MLA prefill: rope term dropped from the score
+    "mla_prefill_drop_rope": ("          for (int e = 0; e < dR; ++e) dot += (double)qr[e] * (double)kr[e];\n          sc[t] = scale * dot;",
+                              "          sc[t] = scale * dot;"),
+    # MLA prefill: the causal cut ignores the prefix
+    "mla_prefill_top_left": ("const int n = P + i + 1; /* keys 0 .. P + i */\n        for (int t = 0; t < n; ++t) {\n          const float* kr",
+                             "const int n = i + 1;\n        for (int t = 0; t < n; ++t) {\n          const float* kr"),
     # value row taken from the wrong KV head (always head 0)
     "value_head_zero": ("const float* vbase = v + ((long)b * T_max * Hkv + g) * D;", "const float* vbase = v + ((long)b * T_max * Hkv + 0) * D;"),
 }
