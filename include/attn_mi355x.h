@@ -2,7 +2,7 @@
  * attn_mi355x.h -- C ABI of a small attention library for AMD Instinct MI355X
  * (gfx950 / CDNA4): grouped-query attention over a KV cache (decode and causal
  * prefill, also after a cached prefix) and multi-head latent attention (MLA)
- * decode over a latent cache.
+ * decode and causal prefill over a latent cache.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -227,6 +227,49 @@ attn_status attn_decode_mla_absorbed(const void* q_nope, const void* q_rope, con
                                      int kv_lora_rank, int T_max, float softmax_scale,
                                      attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* MLA causal prefill over the latent cache (absorbed form).
+ *
+ *   P = start_pos[b] (NULL: 0), n = q_lens[b] (NULL: S), for i < n:
+ *   s_j = scale * (q_nope[b,i,h] . W_UK[h] c_kv[b,j] + q_rope[b,i,h] . k_rope[b,j])
+ *   out[b,i,h,:] = W_UV[h] sum_{j <= P+i} softmax_j(s) c_kv[b,j]
+ *   out[b,i,h,:] = 0 for n <= i < S.
+ *
+ * This is the scaled_dot_product_attention(is_causal=True) call of the
+ * MultiHeadLatentAttention listing on the qqstock DeepSeek MLA article: keys
+ * [W_UK c, k_rope] (k_rope shared by every head, section 3) and values W_UV c
+ * rebuilt from the latent; folding W_UK into the query and applying W_UV after
+ * the weighted sum (sections 2 and 4) gives the same result.  With a cached
+ * prefix the causal cut is aligned to the bottom right, as for
+ * attn_prefill_gqa_cached.  The default scale is 1/sqrt(nope_head_dim +
+ * rope_dim), scaled_dot_product_attention's default over the listing's
+ * recombined query.  Scores, softmax and accumulation in fp32 on bf16 MFMA; the
+ * absorbed query, the probabilities and the latent output are rounded to bf16
+ * before their MFMA products.
+ *
+ *   q_nope  [B, S, H, nope_head_dim]   q_rope [B, S, H, rope_dim]   bf16 (the
+ *           new tokens, padded to S; q_rope already rotated)
+ *   w_uk    [H, nope_head_dim, kv_lora_rank]   w_uv [H, v_head_dim, kv_lora_rank]
+ *           bf16: the per-head rows of the key-nope and value up-projection
+ *           weights
+ *   c_kv    [B, T_max, kv_lora_rank]   k_rope [B, T_max, rope_dim]   bf16, the
+ *           new tokens' rows already written at start_pos[b] ..; read only at
+ *           rows 0 .. P + n - 1
+ *   start_pos, q_lens  [B] int32 device memory, or NULL; clamped as for
+ *           attn_prefill_gqa_cached
+ *   out     [B, S, H, v_head_dim]   out_dtype (ATTN_BF16 or ATTN_F32)
+ *
+ * Built widths: nope 96, rope 48, v 96, kv_lora_rank 128 (MiniMind-768's MLA);
+ * others return ATTN_ERR_UNSUPPORTED.  in_dtype must be ATTN_BF16.  All
+ * pointers are device memory owned by the caller, 16-byte aligned.  No
+ * workspace.
+ */
+attn_status attn_prefill_mla_causal(const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv,
+                                    const void* c_kv, const void* k_rope, const int32_t* start_pos,
+                                    const int32_t* q_lens, void* out, int B, int S, int H, int nope_head_dim,
+                                    int rope_dim, int v_head_dim, int kv_lora_rank, int T_max, float softmax_scale,
+                                    attn_dtype in_dtype, attn_dtype out_dtype, void* stream);
 
 #ifdef __cplusplus
 }

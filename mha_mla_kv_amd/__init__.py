@@ -1,5 +1,5 @@
 """Python binding of libattn_mi355x.so: GQA/MQA/MHA decode, causal GQA prefill (also after a
-cached prefix) and MLA absorbed decode on AMD MI355X (gfx950).
+cached prefix), MLA absorbed decode and MLA causal prefill on AMD MI355X (gfx950).
 
 The functions carry the C entry points' names and do argument marshalling only: they check
 that the torch tensors are CUDA (HIP) tensors of the right dtype, shape and layout, allocate
@@ -54,6 +54,8 @@ def _declare(lib):
     lib.attn_decode_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, Z, P]
     lib.attn_prefill_gqa_causal.restype = I
     lib.attn_prefill_gqa_causal.argtypes = [P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.attn_prefill_mla_causal.restype = I
+    lib.attn_prefill_mla_causal.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, P]
     lib.attn_prefill_gqa_cached.restype = I
     lib.attn_prefill_gqa_cached.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
     lib.attn_decode_mla_workspace_bytes.restype = Z
@@ -219,6 +221,47 @@ def attn_prefill_gqa_cached(q, k_cache, v_cache, start_pos, q_lens=None, out=Non
     return out
 
 
+def attn_prefill_mla_causal(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, start_pos=None, q_lens=None, out=None,
+                            softmax_scale: float = 0.0, out_dtype=torch.bfloat16):
+    """MLA causal prefill over the latent cache: new token i of sequence b (position start_pos[b] + i)
+    attends cache rows j <= start_pos[b] + i with keys [W_UK c, k_rope] and values W_UV c.
+
+    q_nope [B,S,H,dn], q_rope [B,S,H,dR], w_uk [H,dn,r], w_uv [H,dv,r], c_kv [B,T_max,r],
+    k_rope [B,T_max,dR] bf16 (the new rows already in the cache); start_pos, q_lens [B] int32 or
+    None.  Returns out [B,S,H,dv]."""
+    _check(q_nope, "q_nope")
+    B, S, H, dn = q_nope.shape
+    _check(q_rope, "q_rope", dtype=q_nope.dtype)
+    if q_rope.dim() != 4 or tuple(q_rope.shape[:3]) != (B, S, H):
+        raise ValueError(f"q_rope must be [B={B}, S={S}, H={H}, rope_dim] (got {tuple(q_rope.shape)})")
+    dR = q_rope.shape[3]
+    _check(w_uk, "w_uk", dtype=q_nope.dtype)
+    if w_uk.dim() != 3 or w_uk.shape[0] != H or w_uk.shape[1] != dn:
+        raise ValueError(f"w_uk must be [H={H}, {dn}, kv_lora_rank] (got {tuple(w_uk.shape)})")
+    r = w_uk.shape[2]
+    _check(w_uv, "w_uv", dtype=q_nope.dtype)
+    if w_uv.dim() != 3 or w_uv.shape[0] != H or w_uv.shape[2] != r:
+        raise ValueError(f"w_uv must be [H={H}, v_head_dim, {r}] (got {tuple(w_uv.shape)})")
+    dv = w_uv.shape[1]
+    _check(c_kv, "c_kv", dtype=q_nope.dtype)
+    if c_kv.dim() != 3 or c_kv.shape[0] != B or c_kv.shape[2] != r:
+        raise ValueError(f"c_kv must be [B={B}, T_max, {r}] (got {tuple(c_kv.shape)})")
+    T_max = c_kv.shape[1]
+    _check(k_rope, "k_rope", shape=(B, T_max, dR), dtype=q_nope.dtype)
+    if start_pos is not None:
+        _check(start_pos, "start_pos", shape=(B,), dtype=torch.int32)
+    if q_lens is not None:
+        _check(q_lens, "q_lens", shape=(B,), dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, S, H, dv), dtype=out_dtype, device=q_nope.device)
+    _check(out, "out", shape=(B, S, H, dv))
+    st = lib().attn_prefill_mla_causal(_ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(c_kv), _ptr(k_rope),
+                                       _ptr(start_pos), _ptr(q_lens), _ptr(out), B, S, H, dn, dR, dv, r, T_max,
+                                       float(softmax_scale), _dt(q_nope), _dt(out), _stream(q_nope.device))
+    _raise_if(st, "attn_prefill_mla_causal")
+    return out
+
+
 def attn_decode_mla_workspace_bytes(B: int, H: int, kv_lora_rank: int, rope_dim: int, T_max: int,
                                     split_tokens: int = 0) -> int:
     return int(lib().attn_decode_mla_workspace_bytes(B, H, kv_lora_rank, rope_dim, T_max, split_tokens))
@@ -273,5 +316,6 @@ def attn_decode_mla_absorbed(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, cache_len
 
 
 __all__ = ["attn_decode_gqa", "attn_decode_gqa_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached",
+           "attn_prefill_mla_causal",
            "attn_decode_mla_absorbed", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",
            "AttnError", "lib", "header_functions", "LIB_PATH", "ATTN_F32", "ATTN_BF16"]

@@ -315,6 +315,52 @@ attn_status attn_prefill_gqa_cached(const void* q, const void* k_cache, const vo
                         head_dim, T_max, softmax_scale, in_dtype, out_dtype, stream);
 }
 
+attn_status attn_prefill_mla_causal(const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv,
+                                    const void* c_kv, const void* k_rope, const int32_t* start_pos,
+                                    const int32_t* q_lens, void* out, int B, int S, int H, int nope_head_dim,
+                                    int rope_dim, int v_head_dim, int kv_lora_rank, int T_max, float softmax_scale,
+                                    attn_dtype in_dtype, attn_dtype out_dtype, void* stream) {
+  static const char* fn = "attn_prefill_mla_causal";
+  if (!q_nope || !q_rope || !w_uk || !w_uv || !c_kv || !k_rope || !out)
+    return fail(ATTN_ERR_NULL, "%s: q_nope, q_rope, w_uk, w_uv, c_kv, k_rope and out must be non-NULL", fn);
+  if (B <= 0 || S <= 0 || H <= 0 || nope_head_dim <= 0 || rope_dim <= 0 || v_head_dim <= 0 || kv_lora_rank <= 0 ||
+      T_max <= 0)
+    return fail(ATTN_ERR_SHAPE, "%s: sizes must be positive (B=%d S=%d H=%d T_max=%d)", fn, B, S, H, T_max);
+  if (B > kMaxGridYZ || H > kMaxGridYZ) return fail(ATTN_ERR_SHAPE, "%s: B and H must be <= %d", fn, kMaxGridYZ);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(ATTN_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  if (in_dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: only bf16 inputs are built (MFMA path)", fn);
+  if (!attn::mla_prefill_supported(nope_head_dim, rope_dim, v_head_dim, kv_lora_rank))
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "%s: widths nope=%d rope=%d v=%d kv_lora_rank=%d are not built (built: 96, 48, 96, 128)", fn,
+                nope_head_dim, rope_dim, v_head_dim, kv_lora_rank);
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(c_kv) ||
+      !aligned16(k_rope) || !aligned16(out))
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: every tensor must be 16-byte aligned", fn);
+  attn::MlaPrefillArgs a;
+  a.q_nope = q_nope;
+  a.q_rope = q_rope;
+  a.w_uk = w_uk;
+  a.w_uv = w_uv;
+  a.c_kv = c_kv;
+  a.k_rope = k_rope;
+  a.start_pos = start_pos;
+  a.q_lens = q_lens;
+  a.out = out;
+  a.B = B;
+  a.S = S;
+  a.H = H;
+  a.dn = nope_head_dim;
+  a.dR = rope_dim;
+  a.dv = v_head_dim;
+  a.r = kv_lora_rank;
+  a.T_kv = T_max;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)(nope_head_dim + rope_dim));
+  a.scale_log2e = scale * kLog2e;
+  a.out_bf16 = out_dtype == ATTN_BF16;
+  return hip_status(attn::launch_mla_prefill(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 size_t attn_decode_mla_workspace_bytes(int B, int H, int kv_lora_rank, int rope_dim, int T_max,
                                        int split_tokens) {
   if (B <= 0 || H <= 0 || kv_lora_rank <= 0 || rope_dim < 0 || T_max <= 0 || !valid_split(split_tokens))

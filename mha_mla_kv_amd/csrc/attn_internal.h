@@ -51,6 +51,21 @@ struct PrefillArgs {
   int out_bf16;
 };
 
+struct MlaPrefillArgs {
+  const void* q_nope;           // [B, S, H, dn] bf16 (the new tokens)
+  const void* q_rope;           // [B, S, H, dR] bf16
+  const void* w_uk;             // [H, dn, r] bf16
+  const void* w_uv;             // [H, dv, r] bf16
+  const void* c_kv;             // [B, T_kv, r] bf16
+  const void* k_rope;           // [B, T_kv, dR] bf16
+  const int32_t* start_pos;     // [B] cached prefix length, or null: 0
+  const int32_t* q_lens;        // [B] new tokens per sequence, or null: S
+  void* out;                    // [B, S, H, dv]
+  int B, S, H, dn, dR, dv, r, T_kv;
+  float scale_log2e;
+  int out_bf16;
+};
+
 struct MlaDecodeArgs {
   const void* q_nope;   // [B, H, dn]
   const void* q_rope;   // [B, H, dR]
@@ -77,6 +92,9 @@ hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t stream);
 
 bool prefill_supported(int D);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+bool mla_prefill_supported(int dn, int dR, int dv, int r);
+hipError_t launch_mla_prefill(const MlaPrefillArgs& a, hipStream_t stream);
 
 bool mla_decode_supported(int H, int r, int dR);
 hipError_t launch_mla_decode(const MlaDecodeArgs& a, hipStream_t stream);

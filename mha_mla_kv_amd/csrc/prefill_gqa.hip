@@ -123,12 +123,14 @@ struct TileCopy {
     }
   }
 
+  // payload: bytes of one key's row that belong to this head (2 * D unless the
+  // source rows are narrower than the LDS rows)
   __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const u16* p, int kt, int n_kt, int kv_len,
-                                                                int row_bytes) {
+                                                                int row_bytes, int payload = 2 * D) {
     const bool ok = kt >= 0 && kt < n_kt;
     const int key0 = ok ? kt * kBN : 0;
     const char* base = reinterpret_cast<const char*>(p) + (size_t)key0 * row_bytes;
-    const unsigned long long end = (unsigned long long)(kv_len - 1 - key0) * row_bytes + 2 * D;
+    const unsigned long long end = (unsigned long long)(kv_len - 1 - key0) * row_bytes + payload;
     const unsigned num = ok ? (unsigned)(end < 0xffffffffull ? end : 0xffffffffull) : 0u;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)num, 0x00020000);
   }
@@ -152,25 +154,25 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70)
 struct Tile {
   int qt, h, b;
 };
-__device__ __forceinline__ Tile map_tile(const PrefillArgs& a, int id) {
-  const int n_qt = (a.S + kBM - 1) / kBM;
-  const int groups = a.B * a.Hkv;
+__device__ __forceinline__ Tile map_tile(int S, int B, int Hq, int Hkv, int n_rep, int id) {
+  const int n_qt = (S + kBM - 1) / kBM;
+  const int groups = B * Hkv;
   Tile t;
   if (groups % 8 == 0) {
     const int xcd = id & 7, slot = id >> 3;
     const int gpx = groups / 8;
-    const int per_rank = gpx * a.n_rep;
+    const int per_rank = gpx * n_rep;
     const int rank = slot / per_rank, rem = slot - rank * per_rank;
-    const int grp = xcd * gpx + rem / a.n_rep;
+    const int grp = xcd * gpx + rem / n_rep;
     t.qt = n_qt - 1 - rank;
-    t.b = grp / a.Hkv;
-    t.h = (grp - t.b * a.Hkv) * a.n_rep + rem % a.n_rep;
+    t.b = grp / Hkv;
+    t.h = (grp - t.b * Hkv) * n_rep + rem % n_rep;
   } else {
-    const int per_rank = a.B * a.Hq;
+    const int per_rank = B * Hq;
     const int rank = id / per_rank, rem = id - rank * per_rank;
     t.qt = n_qt - 1 - rank;
-    t.b = rem / a.Hq;
-    t.h = rem - t.b * a.Hq;
+    t.b = rem / Hq;
+    t.h = rem - t.b * Hq;
   }
   return t;
 }
@@ -257,6 +259,53 @@ struct RowState {
   float m, lsum;
 };
 
+// Online softmax of one tile's scores sc (S^T layout of qk_tile): masks keys
+// past the diagonal, moves the reference max when needed (rescaling O and the
+// row sum), and returns the probabilities as the four bf16 P^T operands of PV.
+template <int D>
+__device__ __forceinline__ void softmax_tile(RowState<D>& st, f32x16 (&sc)[2], bf16x8 (&pop)[4], int kv0,
+                                             const Lane& w) {
+  if (kv0 + kBN - 1 > w.pos0) {  // the tile reaches above the diagonal of some row
+    const int t = w.my_pos - kv0 - 4 * w.h2;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[j][i] = 32 * j + 8 * (i >> 2) + (i & 3) <= t ? sc[j][i] : kNegInf;
+  }
+  float mr = kNegInf;  // raw row max; the scale is positive
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mr = fmaxf(mr, sc[j][i]);
+  const float mt = max_xor32(mr) * w.c;
+  // key 0 is visible to every row, so tile 0 always sets a finite reference
+  if (__builtin_amdgcn_ballot_w64(mt > st.m + kRescaleSlack) != 0) {
+    const float mn = fmaxf(st.m, mt);
+    const float alpha = exp2_fast(st.m - mn);
+    st.m = mn;
+    st.lsum *= alpha;
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d) st.o[d] *= alpha;
+  }
+  // P^T operand of PV step v: S^T block v/2, values 8(v%2)..+8
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) pop[v][jj] = (__bf16)exp2_fast(fmaf(sc[v >> 1][8 * (v & 1) + jj], w.c, -st.m));
+  // row sum of the bf16-rounded probabilities (the ones the PV product uses),
+  // two per v_dot2_f32_bf16 against (1, 1), in four independent chains
+  const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+  float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x2 pair = {pop[v][2 * q], pop[v][2 * q + 1]};
+      ps4[q] = __builtin_amdgcn_fdot2_f32_bf16(pair, one, ps4[q], false);
+    }
+  st.lsum += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+}
+
 // One 64-key tile: issue the copies of tile kt+1 into (kn, vn), consume tile kt
 // from (kc, vc) if some row of the wave sees it, then wait for the copies and
 // meet at the barrier.  The four buffers are distinct LDS variables addressed
@@ -272,49 +321,10 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, const u16* kc, const 
     cp.issue(vn, TileCopy<D>::rsrc(vp, kt + 1, n_kt, kv_len, row_bytes));
   }
   if (kt <= last_kt) {
-    const int kv0 = kt * kBN;
     f32x16 sc[2];
     qk_tile<D>(sc, kc, qop, off.k);
-    if (kv0 + kBN - 1 > w.pos0) {  // the tile reaches above the diagonal of some row
-      const int t = w.my_pos - kv0 - 4 * w.h2;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[j][i] = 32 * j + 8 * (i >> 2) + (i & 3) <= t ? sc[j][i] : kNegInf;
-    }
-    float mr = kNegInf;  // raw row max; the scale is positive
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mr = fmaxf(mr, sc[j][i]);
-    const float mt = max_xor32(mr) * w.c;
-    // key 0 is visible to every row, so tile 0 always sets a finite reference
-    if (__builtin_amdgcn_ballot_w64(mt > st.m + kRescaleSlack) != 0) {
-      const float mn = fmaxf(st.m, mt);
-      const float alpha = exp2_fast(st.m - mn);
-      st.m = mn;
-      st.lsum *= alpha;
-#pragma unroll
-      for (int d = 0; d < D / 32; ++d) st.o[d] *= alpha;
-    }
-    // P^T operand of PV step v: S^T block v/2, values 8(v%2)..+8
     bf16x8 pop[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) pop[v][jj] = (__bf16)exp2_fast(fmaf(sc[v >> 1][8 * (v & 1) + jj], w.c, -st.m));
-    // row sum of the bf16-rounded probabilities (the ones the PV product uses),
-    // two per v_dot2_f32_bf16 against (1, 1), in four independent chains
-    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
-    float ps4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bf16x2 pair = {pop[v][2 * q], pop[v][2 * q + 1]};
-        ps4[q] = __builtin_amdgcn_fdot2_f32_bf16(pair, one, ps4[q], false);
-      }
-    st.lsum += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+    softmax_tile<D>(st, sc, pop, kt * kBN, w);
     pv_tile<D>(st.o, vc, pop, off.v_lo, off.v_hi);
   }
   wait_vmem();      // this thread's copies of tile kt+1 have landed
@@ -363,7 +373,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   __shared__ __attribute__((aligned(1024))) u16 v0[kTile];
   __shared__ __attribute__((aligned(1024))) u16 v1[kTile];
 
-  const Tile tl = map_tile(a, blockIdx.x);
+  const Tile tl = map_tile(a.S, a.B, a.Hq, a.Hkv, a.n_rep, blockIdx.x);
   const int h = tl.h, b = tl.b;
   const int g = h / a.n_rep;
   const int q0 = tl.qt * kBM;
@@ -437,6 +447,266 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   if (w.my_row < a.S) store_rows<D>(a.out, orow, a.out_bf16, st.o, w.my_row < n_q, 1.f / lsum, w.h2);
 }
 
+
+// ---------------------------------------------------------------------------
+// MLA causal prefill, absorbed form.
+//
+// What is computed: out[b,i,h] = W_UV[h] sum_{j<=P+i} softmax_j(scale (q_c . c_j +
+// q_rope[b,i,h] . k_rope_j)) c_j with q_c = W_UK[h]^T q_nope[b,i,h] -- the
+// scaled_dot_product_attention(is_causal=True) call of the MultiHeadLatentAttention
+// listing on the qqstock DeepSeek MLA article, whose keys [W_UK c, k_rope] and
+// values W_UV c are rebuilt from the latent: folding W_UK into the query and
+// applying W_UV after the weighted sum (sections 2 and 4 of the article) gives
+// the same numbers, and k_rope is shared by all heads (section 3).  With a cached
+// prefix of P positions new token i sits at position P + i (bottom-right causal
+// cut), as in the GQA prefill above.
+//
+// How (not from the pages): the GQA prefill's tiles and online softmax with one
+// KV stream shared by all H heads.  The latent tile c [64 keys x 128] is the K
+// operand of the first 128 score dimensions and also the V operand of PV, so one
+// copy serves both; a second tile holds k_rope [64 x dR] (LDS rows of 64
+// elements, XOR-swizzled as the head_dim-64 tiles) for the last dR dimensions.
+// Prologue: each wave's 32 absorbed query rows q_c^T = W_UK[h]^T q_nope^T on
+// MFMA, with W_UK[h] staged transposed in LDS; the accumulator layout is moved
+// into the B-operand layout by exchanging half of each lane's values with lane ^ 32.
+// Epilogue: out^T = W_UV[h] O^T on MFMA from the normalised O^T, moved the same
+// way.  q_c and o_lat enter those MFMAs as bf16, like P.
+
+// A 32x32 MFMA accumulator block X^T[k][row] (lane holds k = 8q + 4h2 + e for
+// i = 4q + e, row = lane % 32), times f, as the B operands of two 16-wide
+// k-steps: op[s] holds X[row][16s + 8h2 + 0..7] in bf16.  For k-step s the lane
+// half h2 = 0 needs its own k = 16s + 0..3 and the other half's 16s + 4..7, the
+// half h2 = 1 the first half's 16s + 8..11 and its own 16s + 12..15: each lane
+// sends one of its two groups to lane ^ 32 (ds_bpermute, which the compiler
+// orders after the MFMA that wrote the accumulator).
+__device__ __forceinline__ void acc_to_operands(const f32x16& acc, float f, bf16x8* op, int h2) {
+#pragma unroll
+  for (int sblk = 0; sblk < 2; ++sblk) {
+    float lo[4], hi[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e] = acc[8 * sblk + e] * f;
+      hi[e] = acc[8 * sblk + 4 + e] * f;
+      const float got = __shfl_xor(h2 ? lo[e] : hi[e], 32);
+      if (h2) lo[e] = got;
+      else hi[e] = got;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      op[sblk][e] = (__bf16)lo[e];
+      op[sblk][4 + e] = (__bf16)hi[e];
+    }
+  }
+}
+
+// S^T of one tile: 128 latent dimensions from the c tile, DR rope dimensions
+// from the rope tile (rows of 64 elements).
+template <int DR>
+__device__ __forceinline__ void qk_tile_mla(f32x16 (&s)[2], const u16* cc, const u16* rc, const bf16x8 (&qop)[8],
+                                            const bf16x8 (&qrop)[DR / 16], int off, int off_r) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[j][i] = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const u16* kr = cc + 32 * j * 128 + (off ^ (16 * c));
+      s[j] = mfma_32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(kr)), qop[c], s[j]);
+    }
+#pragma unroll
+  for (int c = 0; c < DR / 16; ++c)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const u16* kr = rc + 32 * j * 64 + (off_r ^ (16 * c));
+      s[j] = mfma_32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(kr)), qrop[c], s[j]);
+    }
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int u = 0; u < 2 * (8 + DR / 16); ++u) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+template <int DR>
+__device__ __forceinline__ void tile_step_mla(RowState<128>& st, const u16* cc, const u16* rc, u16* cn, u16* rn,
+                                              const bf16x8 (&qop)[8], const bf16x8 (&qrop)[DR / 16], int kt,
+                                              int n_kt, int last_kt, const u16* cp, const u16* rp, int kv_len,
+                                              const TileCopy<128>& cpc, const TileCopy<64>& cpr,
+                                              const LdsOffsets& off, int off_r, const Lane& w) {
+  if (kt + 1 < n_kt) {  // (cn, rn) were released by the last barrier
+    cpc.issue(cn, TileCopy<128>::rsrc(cp, kt + 1, n_kt, kv_len, 256));
+    cpr.issue(rn, TileCopy<64>::rsrc(rp, kt + 1, n_kt, kv_len, 2 * DR, 2 * DR));
+  }
+  if (kt <= last_kt) {
+    f32x16 sc[2];
+    qk_tile_mla<DR>(sc, cc, rc, qop, qrop, off.k, off_r);
+    bf16x8 pop[4];
+    softmax_tile<128>(st, sc, pop, kt * kBN, w);
+    pv_tile<128>(st.o, cc, pop, off.v_lo, off.v_hi);  // V = the latent tile
+  }
+  wait_vmem();
+  __syncthreads();
+}
+
+// Stores out^T blocks (lane holds out^T[32eb + 8q + 4h2 + e][row ln]) of one row,
+// or zeros when !valid.
+template <int DV>
+__device__ __forceinline__ void store_mla_row(void* out, size_t orow, int out_bf16, const f32x16 (&o)[DV / 32],
+                                              bool valid, int h2) {
+  if (out_bf16) {
+    u16* op = static_cast<u16*>(out) + orow * DV;
+#pragma unroll
+    for (int eb = 0; eb < DV / 32; ++eb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        u16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = __builtin_bit_cast(u16, (__bf16)(valid ? o[eb][4 * q4 + e] : 0.f));
+        *reinterpret_cast<u16x4*>(op + 32 * eb + 8 * q4 + 4 * h2) = o4;
+      }
+  } else {
+    float* op = static_cast<float*>(out) + orow * DV;
+#pragma unroll
+    for (int eb = 0; eb < DV / 32; ++eb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (valid) f = make_float4(o[eb][4 * q4], o[eb][4 * q4 + 1], o[eb][4 * q4 + 2], o[eb][4 * q4 + 3]);
+        *reinterpret_cast<float4*>(op + 32 * eb + 8 * q4 + 4 * h2) = f;
+      }
+  }
+}
+
+template <int DN, int DR, int DV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mla(MlaPrefillArgs a) {
+  static_assert(DN % 16 == 0 && DN <= 128 && DR % 16 == 0 && DR <= 64 && DV % 32 == 0 && DV <= 128, "widths");
+  constexpr int R = 128;         // kv_lora_rank
+  constexpr int WP = DN + 8;     // row pitch of W_UK^T in LDS: 16-byte reads of 16 rows hit distinct banks
+  __shared__ __attribute__((aligned(1024))) u16 c0[kBN * R];
+  __shared__ __attribute__((aligned(1024))) u16 c1[kBN * R];
+  __shared__ __attribute__((aligned(1024))) u16 r0[kBN * 64];
+  __shared__ __attribute__((aligned(1024))) u16 r1[kBN * 64];
+  __shared__ __attribute__((aligned(16))) u16 wukT[R * WP];
+
+  const Tile tl = map_tile(a.S, a.B, a.H, 1, a.H, blockIdx.x);
+  const int h = tl.h, b = tl.b;
+  const int q0 = tl.qt * kBM;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int P = a.start_pos ? min(max(a.start_pos[b], 0), a.T_kv) : 0;
+  const int n_q = min(a.q_lens ? min(max(a.q_lens[b], 0), a.S) : a.S, a.T_kv - P);
+  Lane w;
+  w.lane = tid & 63;
+  w.ln = w.lane & 31;
+  w.h2 = w.lane >> 5;
+  w.row0 = q0 + wave * 32;
+  w.my_row = w.row0 + w.ln;
+  w.pos0 = P + w.row0;
+  w.my_pos = P + w.my_row;
+  w.c = a.scale_log2e;
+  const size_t orow = ((size_t)b * a.S + w.my_row) * a.H + h;
+  if (q0 >= n_q) {  // no new token in this q-tile: zero rows, nothing to read
+    const f32x16 none[DV / 32] = {};
+    if (w.my_row < a.S) store_mla_row<DV>(a.out, orow, a.out_bf16, none, false, w.h2);
+    return;
+  }
+  const u16* cp = static_cast<const u16*>(a.c_kv) + (size_t)b * a.T_kv * R;
+  const u16* rp = static_cast<const u16*>(a.k_rope) + (size_t)b * a.T_kv * DR;
+  const int kv_len = P + n_q;
+  const int kv_end = min(kv_len, P + q0 + kBM);
+  const int n_kt = (kv_end + kBN - 1) / kBN;
+  const int last_kt = min(n_kt - 1, (w.pos0 + 31) / kBN);
+
+  const TileCopy<128> cpc(wave, w.lane, 2 * R);
+  const TileCopy<64> cpr(wave, w.lane, 2 * DR);
+  cpc.issue(c0, TileCopy<128>::rsrc(cp, 0, n_kt, kv_len, 2 * R));
+  cpr.issue(r0, TileCopy<64>::rsrc(rp, 0, n_kt, kv_len, 2 * DR, 2 * DR));
+
+  // W_UK[h] [DN][R] -> LDS transposed [R][WP]: thread-consecutive rows i, so the
+  // 2-byte writes of a wave are consecutive
+  const u16* wk = static_cast<const u16*>(a.w_uk) + (size_t)h * DN * R;
+#pragma unroll
+  for (int k = 0; k < DN / 16; ++k) {
+    const int id = tid + 256 * k;
+    const int i = id % DN, jc = id / DN;
+    const u16x8 v = *reinterpret_cast<const u16x8*>(wk + (size_t)i * R + 8 * jc);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wukT[(8 * jc + e) * WP + i] = v[e];
+  }
+  // q_nope^T and q_rope^T B operands: lane holds row ln's dims 16c + 8h2 .. +8
+  const int qrow = min(w.my_row, a.S - 1);
+  const u16* qn = static_cast<const u16*>(a.q_nope) + (((size_t)b * a.S + qrow) * a.H + h) * DN + 8 * w.h2;
+  const u16* qr = static_cast<const u16*>(a.q_rope) + (((size_t)b * a.S + qrow) * a.H + h) * DR + 8 * w.h2;
+  bf16x8 qnop[DN / 16];
+#pragma unroll
+  for (int c = 0; c < DN / 16; ++c) qnop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qn + 16 * c));
+  bf16x8 qrop[DR / 16];
+#pragma unroll
+  for (int c = 0; c < DR / 16; ++c) qrop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qr + 16 * c));
+  __syncthreads();  // W_UK^T staged
+
+  // q_c^T[j][row] = sum_i W_UK^T[j][i] q_nope^T[i][row], 32 j at a time
+  bf16x8 qop[8];
+#pragma unroll
+  for (int jb = 0; jb < R / 32; ++jb) {
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    const u16* ar = wukT + (32 * jb + w.ln) * WP + 8 * w.h2;
+#pragma unroll
+    for (int c = 0; c < DN / 16; ++c)
+      acc = mfma_32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(ar + 16 * c)), qnop[c], acc);
+    acc_to_operands(acc, 1.f, &qop[2 * jb], w.h2);
+  }
+
+  const LdsOffsets off = lds_offsets<128>(w);
+  const int off_r = lds_offsets<64>(w).k;
+  RowState<128> st;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.o[d][i] = 0.f;
+  st.m = kNegInf;
+  st.lsum = 0.f;
+
+  wait_vmem();
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    tile_step_mla<DR>(st, c0, r0, c1, r1, qop, qrop, kt, n_kt, last_kt, cp, rp, kv_len, cpc, cpr, off, off_r, w);
+    if (kt + 1 < n_kt)
+      tile_step_mla<DR>(st, c1, r1, c0, r0, qop, qrop, kt + 1, n_kt, last_kt, cp, rp, kv_len, cpc, cpr, off, off_r,
+                        w);
+  }
+
+  // o_lat = O / l as the B operand, then out^T = W_UV[h] o_lat^T, 32 output dims at a time
+  const float inv = 1.f / sum_xor32(st.lsum);
+  bf16x8 oop[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) acc_to_operands(st.o[d], inv, &oop[2 * d], w.h2);
+  const u16* wv = static_cast<const u16*>(a.w_uv) + ((size_t)h * DV + w.ln) * R + 8 * w.h2;
+  f32x16 ov[DV / 32];
+#pragma unroll
+  for (int eb = 0; eb < DV / 32; ++eb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ov[eb][i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      ov[eb] = mfma_32x32x16(
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(wv + (size_t)32 * eb * R + 16 * c)), oop[c],
+          ov[eb]);
+  }
+  if (w.my_row < a.S) store_mla_row<DV>(a.out, orow, a.out_bf16, ov, w.my_row < n_q, w.h2);
+}
+
+// Explicit instantiations: without them the host stubs of only some of the
+// kernel templates launched below were emitted.
+template __global__ void prefill_causal<128>(PrefillArgs);
+template __global__ void prefill_causal<64>(PrefillArgs);
+template __global__ void prefill_mla<96, 48, 96>(MlaPrefillArgs);
+
 }  // namespace
 
 bool prefill_supported(int D) { return D == 64 || D == 128; }
@@ -448,6 +718,17 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)wgs);
   if (a.D == 128) hipLaunchKernelGGL(prefill_causal<128>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(prefill_causal<64>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+bool mla_prefill_supported(int dn, int dR, int dv, int r) { return r == 128 && dn == 96 && dR == 48 && dv == 96; }
+
+hipError_t launch_mla_prefill(const MlaPrefillArgs& a, hipStream_t st) {
+  if (!mla_prefill_supported(a.dn, a.dR, a.dv, a.r)) return hipErrorInvalidValue;
+  const long long wgs = (long long)((a.S + kBM - 1) / kBM) * a.H * a.B;
+  if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wgs);
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_mla<96, 48, 96>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -129,6 +129,34 @@ def mla_decode_inputs(B: int, H: int, nope_head_dim: int, rope_dim: int, v_head_
             "k_rope": k_rope, "cache_lens": torch.from_numpy(L.copy())}
 
 
+def mla_prefill_inputs(B: int, S: int, H: int, nope_head_dim: int, rope_dim: int, v_head_dim: int,
+                       kv_lora_rank: int, T_max: int, start_pos=0, q_lens=None, dtype: str = "bf16",
+                       seed: int = 0, poison: bool = True) -> dict:
+    """MLA prefill: q_nope [B,S,H,dn], q_rope [B,S,H,dR] (the new tokens, padded to S), w_uk
+    [H,dn,r], w_uv [H,dv,r] (N(0, 1/r)), c_kv [B,T_max,r], k_rope [B,T_max,dR] (holding the new
+    rows at start_pos[b]..), start_pos and q_lens [B] int32 (``_lengths`` forms; q_lens None: S).
+    Draw order as named.  With poison, q rows past q_lens[b] and cache rows past
+    start_pos[b] + q_lens[b] are NaN."""
+    rng = _rng(seed)
+    dn, dR, dv, r = nope_head_dim, rope_dim, v_head_dim, kv_lora_rank
+    q_nope = _as(_normal(rng, (B, S, H, dn)), dtype)
+    q_rope = _as(_normal(rng, (B, S, H, dR)), dtype)
+    w_uk = _as(_normal(rng, (H, dn, r), std=float(1.0 / np.sqrt(r))), dtype)
+    w_uv = _as(_normal(rng, (H, dv, r), std=float(1.0 / np.sqrt(r))), dtype)
+    c_kv = _as(_normal(rng, (B, T_max, r)), dtype)
+    k_rope = _as(_normal(rng, (B, T_max, dR)), dtype)
+    sp = _lengths(rng, B, T_max, start_pos)
+    ql = _lengths(rng, B, S, S if q_lens is None else q_lens)
+    if poison:
+        _poison_tail(q_nope, ql)
+        _poison_tail(q_rope, ql)
+        end = np.minimum(np.maximum(sp.astype(np.int64), 0) + np.maximum(ql, 0), T_max).astype(np.int32)
+        _poison_tail(c_kv, end)
+        _poison_tail(k_rope, end)
+    return {"q_nope": q_nope, "q_rope": q_rope, "w_uk": w_uk, "w_uv": w_uv, "c_kv": c_kv, "k_rope": k_rope,
+            "start_pos": torch.from_numpy(sp.copy()), "q_lens": torch.from_numpy(ql.copy())}
+
+
 # The workloads the pages' shapes give (name -> generator kwargs).  Seeds are fixed per workload.
 WORKLOADS = {
     "minimind768_gqa_decode": dict(kind="gqa_decode", B=1, Hq=8, Hkv=4, D=96, T_max=512, lens=512,
@@ -145,6 +173,8 @@ WORKLOADS = {
                                   dtype="bf16", seed=4),
     "llama3_8b_gqa_chunked_prefill": dict(kind="gqa_prefill_cached", B=4, S=512, Hq=32, Hkv=8, D=128,
                                           T_max=4096, start_pos=3584, q_lens=512, dtype="bf16", seed=6),
+    "minimind768_mla_prefill": dict(kind="mla_prefill", B=4, S=4096, H=8, nope_head_dim=96, rope_dim=48,
+                                    v_head_dim=96, kv_lora_rank=128, T_max=4096, start_pos=0, dtype="bf16", seed=7),
     "minimind768_mla_decode": dict(kind="mla_decode", B=64, H=8, nope_head_dim=96, rope_dim=48,
                                    v_head_dim=96, kv_lora_rank=128, T_max=4096, lens=4096,
                                    dtype="bf16", seed=5),
@@ -162,6 +192,8 @@ def make(name_or_spec, **overrides) -> dict:
         return gqa_prefill_inputs(**spec)
     if kind == "gqa_prefill_cached":
         return gqa_prefill_cached_inputs(**spec)
+    if kind == "mla_prefill":
+        return mla_prefill_inputs(**spec)
     if kind == "mla_decode":
         return mla_decode_inputs(**spec)
     raise ValueError(kind)

@@ -23,7 +23,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = attn.lib()
     names = attn.header_functions()
     for required in ("attn_decode_gqa", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached",
-                     "attn_decode_mla_absorbed"):
+                     "attn_decode_mla_absorbed", "attn_prefill_mla_causal"):
         assert required in names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/attn_mi355x.h but not exported"
@@ -125,6 +125,26 @@ def test_cached_prefill_validation():
     assert f(ind=F32) == UNSUP
     assert f(D=96) == UNSUP
     assert f(q=FAKE_MIS) == UNSUP
+
+
+@no_gpu_only
+def test_mla_prefill_validation():
+    lib = attn.lib()
+
+    def f(**kw):
+        return lib.attn_prefill_mla_causal(kw.get("qn", FAKE), FAKE, FAKE, FAKE, kw.get("c", FAKE), FAKE, None, None,
+                                           FAKE, kw.get("B", 2), kw.get("S", 16), kw.get("H", 8), kw.get("dn", 96),
+                                           kw.get("dR", 48), kw.get("dv", 96), kw.get("r", 128), kw.get("T", 64), 0.0,
+                                           kw.get("ind", BF16), BF16, None)
+    assert f(qn=None) == NULL
+    assert f(T=0) == SHAPE
+    assert f(S=0) == SHAPE
+    assert f(r=256) == UNSUP
+    assert f(dR=64) == UNSUP
+    assert f(dn=128) == UNSUP
+    assert f(ind=F32) == UNSUP
+    assert f(c=FAKE_MIS) == UNSUP
+    assert b"not built" in lib.attn_last_error() or b"aligned" in lib.attn_last_error()
 
 
 @no_gpu_only
