@@ -12,6 +12,8 @@ One step = one pass over the three C-ABI entry points, each on its own synthetic
                               head_dim 128, bf16 in / out
   * attn_prefill_gqa_cached   the same heads, a 512-token chunk after a 3584-token cached
                               prefix in each of 4 sequences (chunked prefill), bf16 in / out
+  * attn_prefill_mla_causal   MiniMind-768 MLA causal prefill: B 4, S 4096, 8 heads, nope 96,
+                              rope 48, v 96, kv_lora_rank 128, bf16 in / out
 
 The printed `value` is the GQA decode's KV-cache read rate (algorithmic bytes: every cached
 K and V row read once per KV head, 2*Hkv*head_dim*2 bytes per cached position) divided by
@@ -140,6 +142,17 @@ def main():
         chk_flops += 4 * CHq * CD * (n * P + n * (n + 1) // 2)   # new token i sees P + i + 1 keys
     chk_tokens = int(chk_cpu["q_lens"].sum())
     chk_out = torch.empty_like(chk["q"])
+
+    mpspec = synth.WORKLOADS["minimind768_mla_prefill"]
+    mlp = {k: v.to(dev) for k, v in synth.make("minimind768_mla_prefill").items()}
+    MPB, MPS, MPH, MPdn = mlp["q_nope"].shape
+    MPdR = mlp["q_rope"].shape[3]
+    MPdv, MPr = mlp["w_uv"].shape[1], mlp["w_uv"].shape[2]
+    # MFMA work of the absorbed form: 2(r + dR) + 2r per unmasked (query, key) pair and head, plus
+    # the query absorption (2 dn r) and the value up-projection (2 dv r) per new token and head
+    mlp_flops = (MPB * MPH * MPS * (MPS + 1) // 2 * (2 * (MPr + MPdR) + 2 * MPr)
+                 + MPB * MPS * MPH * 2 * MPr * (MPdn + MPdv))
+    mlp_out = torch.empty(MPB, MPS, MPH, MPdv, dtype=torch.bfloat16, device=dev)
     copy_src = copy_dst = None
     if args.copy_calibration:
         copy_src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
@@ -159,13 +172,17 @@ def main():
     def run_prefill():
         attn.attn_prefill_gqa_causal(pre["q"], pre["k"], pre["v"], out=pre_out)
 
+    def run_mla_prefill():
+        attn.attn_prefill_mla_causal(mlp["q_nope"], mlp["q_rope"], mlp["w_uk"], mlp["w_uv"], mlp["c_kv"], mlp["k_rope"],
+                                     out=mlp_out)
+
     def run_chunked():
         attn.attn_prefill_gqa_cached(chk["q"], chk["k"], chk["v"], chk["start_pos"], chk["q_lens"], out=chk_out)
 
     # prefill for new requests, then the decode steps of running ones (the order a serving
     # step takes); each part is timed on its own
-    parts = [("prefill", run_prefill), ("chunked_prefill", run_chunked), ("mla_decode", run_mla),
-             ("gqa_decode", run_decode)]
+    parts = [("prefill", run_prefill), ("chunked_prefill", run_chunked), ("mla_prefill", run_mla_prefill),
+             ("mla_decode", run_mla), ("gqa_decode", run_decode)]
     if args.copy_calibration:
         parts.append(("copy_1GiB", lambda: copy_dst.copy_(copy_src)))
 
@@ -193,6 +210,7 @@ def main():
     mla_gbs = mla_bytes / (ms["mla_decode"] * 1e-3) / 1e9
     pre_tfs = pre_flops / (ms["prefill"] * 1e-3) / 1e12
     chk_tfs = chk_flops / (ms["chunked_prefill"] * 1e-3) / 1e12
+    mlp_tfs = mlp_flops / (ms["mla_prefill"] * 1e-3) / 1e12
 
     dec_hash = source_hash("decode_gqa.hip", "attn_internal.h")
     traffic = measured_traffic("gqa_decode_bf16<128, 1, true>", dec_hash)
@@ -214,9 +232,10 @@ def main():
             "workload": (f"llama3_8b_gqa_decode: B={B} Hq={Hq} Hkv={Hkv} head_dim={D} T_max={T_max} "
                          f"cache_lens~U[{dspec['lens'][0]},{dspec['lens'][1]}] (sum {sum_len}) seed={dspec['seed']}, "
                          "bf16 in, fp32 out, default schedule (device-wide unit queue, library-chosen blocks)"),
-            "step": ("attn_prefill_gqa_causal, attn_prefill_gqa_cached, attn_decode_mla_absorbed, attn_decode_gqa: "
-                     "one call each, in this order"),
-            "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "prefill": PB * S, "chunked_prefill": chk_tokens},
+            "step": ("attn_prefill_gqa_causal, attn_prefill_gqa_cached, attn_prefill_mla_causal, "
+                     "attn_decode_mla_absorbed, attn_decode_gqa: one call each, in this order"),
+            "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "prefill": PB * S, "chunked_prefill": chk_tokens,
+                                "mla_prefill": MPB * MPS},
         },
         "roofline": {
             "bound": "hbm",
@@ -254,6 +273,12 @@ def main():
                                 "workload": f"llama3_8b_gqa_chunked_prefill: B={CB} chunk={CS} "
                                             f"start_pos={cspec['start_pos']} T_max={CT} Hq={CHq} "
                                             f"Hkv={chk['k'].shape[2]} head_dim={CD} seed={cspec['seed']} bf16"},
+            "mla_prefill": {"ms": round(ms["mla_prefill"], 5), "TFLOP/s": round(mlp_tfs, 1),
+                            "mfma_frac": round(mlp_tfs / BF16_DENSE_PEAK_TFLOPS, 4),
+                            "algorithmic_flops_per_launch": mlp_flops,
+                            "tokens_per_s": round(MPB * MPS / (ms["mla_prefill"] * 1e-3), 1),
+                            "workload": f"minimind768_mla_prefill: B={MPB} S={MPS} H={MPH} nope={MPdn} rope={MPdR} "
+                                        f"v={MPdv} r={MPr} seed={mpspec['seed']} bf16 causal"},
         },
         "input_generation_s": round(t_gen, 2),
     }

@@ -84,3 +84,17 @@ def test_cached_prefill_graph_replay():
                                                                       inp["q_lens"], out=out), out)
     assert torch.isfinite(eager.float()).all()
     assert not eager[1, 111:].any()  # rows past the chunk are zeros
+
+
+def test_mla_prefill_graph_replay():
+    import mha_mla_kv_amd as attn
+    B, S, H, T = 2, 200, 8, 600
+    inp = {k: v.cuda() for k, v in synth.mla_prefill_inputs(B, S, H, 96, 48, 96, 128, T, [300, 0], [200, 77],
+                                                            seed=11).items()}
+    print(f"[case] mla prefill graph B={B} S={S} H={H} T={T}", flush=True)
+    out = torch.empty(B, S, H, 96, dtype=torch.bfloat16, device="cuda")
+    keys = ("q_nope", "q_rope", "w_uk", "w_uv", "c_kv", "k_rope")
+    eager = _graph_matches_eager(lambda: attn.attn_prefill_mla_causal(*(inp[k] for k in keys), inp["start_pos"],
+                                                                      inp["q_lens"], out=out), out)
+    assert torch.isfinite(eager.float()).all()
+    assert not eager[1, 77:].any()
