@@ -204,6 +204,23 @@ def mla_prefill_causal(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, start_pos=None,
     return out
 
 
+def cache_append(cache, new, start_pos=None, n_new=None) -> np.ndarray:
+    """The cache write of Attention.forward on the MQA & GQA survey page (code section):
+    cache[b, P : P + n] = new[b, :n] with P = start_pos[b] clamped to [0, T_max] and n = n_new[b]
+    clamped to [0, min(S, T_max - P)].  Returns a new array; the arguments are not modified.
+    Works on any dtype (bf16 tensors are compared as raw 16-bit patterns by the tests)."""
+    out = np.array(cache, copy=True)
+    new = np.asarray(new)
+    B, S = new.shape[0], new.shape[1]
+    T_max = out.shape[1]
+    for b in range(B):
+        P = 0 if start_pos is None else min(max(int(start_pos[b]), 0), T_max)
+        n = S if n_new is None else int(n_new[b])
+        n = max(0, min(n, S, T_max - P))
+        out[b, P:P + n] = new[b, :n]
+    return out
+
+
 def threads(lib=None) -> int:
     """OpenMP threads the oracle runs with."""
     return int((lib or load()).oracle_threads())

@@ -489,6 +489,29 @@ def pin_mla_prefill_rows_are_decodes(lib):
                                      lib=lib), 0.0, "MLA prefill defaults")
 
 
+def pin_cache_append(lib):
+    """Appending a chunk after a prefix and running the cached-prefix prefill over the cache gives
+    the causal prefill of the concatenated sequence at the chunk's rows; the prefix and the rows
+    after the chunk stay as they were; a chunk that overruns the cache is cut at T_max."""
+    rng = _rng(37)
+    B, P, n, Hq, Hkv, D, T = 2, 9, 5, 4, 2, 8, 20
+    prefix_k, prefix_v = _rand(rng, B, P, Hkv, D), _rand(rng, B, P, Hkv, D)
+    new_k, new_v, q = _rand(rng, B, n, Hkv, D), _rand(rng, B, n, Hkv, D), _rand(rng, B, n, Hq, D)
+    cache_k, cache_v = _rand(rng, B, T, Hkv, D), _rand(rng, B, T, Hkv, D)
+    cache_k[:, :P], cache_v[:, :P] = prefix_k, prefix_v
+    sp = np.full(B, P, np.int32)
+    k2, v2 = oracle.cache_append(cache_k, new_k, sp), oracle.cache_append(cache_v, new_v, sp)
+    assert np.array_equal(k2[:, :P], prefix_k) and np.array_equal(k2[:, P + n:], cache_k[:, P + n:]), "untouched"
+    got = oracle.gqa_prefill_cached(q, k2, v2, sp, None, lib=lib)
+    full_q = np.concatenate([_rand(rng, B, P, Hq, D), q], axis=1)
+    ref = oracle.gqa_prefill_causal(full_q, np.concatenate([prefix_k, new_k], 1), np.concatenate([prefix_v, new_v], 1),
+                                    lib=lib)
+    _close(got, ref[:, P:], 1e-14, "append + cached prefill vs causal prefill of the concatenation")
+    k3 = oracle.cache_append(cache_k, new_k, np.array([T - 2, -3], np.int32), np.array([5, 2], np.int32))
+    assert np.array_equal(k3[0, T - 2:], new_k[0, :2]) and np.array_equal(k3[0, :T - 2], cache_k[0, :T - 2])
+    assert np.array_equal(k3[1, :2], new_k[1, :2]) and np.array_equal(k3[1, 2:], cache_k[1, 2:])
+
+
 ALL_PINS = [pin_decode_vs_sdpa, pin_decode_closed_forms, pin_decode_invariants, pin_decode_head_structure,
             pin_prefill_vs_sdpa, pin_prefill_rows, pin_cached_vs_sdpa, pin_cached_reductions, pin_mla_vs_sdpa, pin_mla_absorbed_equals_decompressed,
-            pin_mla_selection, pin_mla_prefill_vs_sdpa, pin_mla_prefill_rows_are_decodes]
+            pin_mla_selection, pin_mla_prefill_vs_sdpa, pin_mla_prefill_rows_are_decodes, pin_cache_append]
