@@ -271,6 +271,37 @@ attn_status attn_prefill_mla_causal(const void* q_nope, const void* q_rope, cons
                                     int rope_dim, int v_head_dim, int kv_lora_rank, int T_max, float softmax_scale,
                                     attn_dtype in_dtype, attn_dtype out_dtype, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Cache append: write the new tokens' rows into one or two caches.
+ *
+ *   P = start_pos[b] (NULL: 0), n = n_new[b] (NULL: S), for i < n:
+ *   cache_a[b, P + i, :] = new_a[b, i, :]   and, when row_bytes_b > 0,
+ *   cache_b[b, P + i, :] = new_b[b, i, :]
+ *
+ * These are the cache_k / cache_v writes at start_pos .. start_pos + seqlen of
+ * Attention.forward on the "模型架构｜MQA & GQA 调研" page (code section), which
+ * come before the cache is read: (a, b) = (K cache, V cache) with rows of
+ * Hkv * head_dim elements, or, for MLA, (c_kv, k_rope), the latent and the
+ * shared rotated key that the qqstock DeepSeek MLA article caches (sections 1
+ * and 3).  Rotary embedding is not applied: rows are copied as given.  After
+ * the call, attn_decode_gqa with cache_lens = P + n, attn_prefill_gqa_cached,
+ * attn_decode_mla_absorbed and attn_prefill_mla_causal read the new rows.
+ *
+ *   new_a   [B, S, row_bytes_a bytes]       cache_a [B, T_max, row_bytes_a bytes]
+ *   new_b   [B, S, row_bytes_b bytes]       cache_b [B, T_max, row_bytes_b bytes]
+ *           (row_bytes_b = 0: no second pair; new_b, cache_b may be NULL)
+ *   start_pos, n_new  [B] int32 device memory or NULL; P clamped to [0, T_max],
+ *           n to [0, min(S, T_max - P)]; rows outside [P, P + n) are untouched
+ *
+ * Bytes are moved as they are (any element type).  Row sizes must be
+ * multiples of 16 bytes and every buffer 16-byte aligned (else
+ * ATTN_ERR_UNSUPPORTED).  All pointers are device memory owned by the caller;
+ * new and cache rows must not overlap.  No workspace.
+ */
+attn_status attn_cache_append(const void* new_a, void* cache_a, int row_bytes_a, const void* new_b, void* cache_b,
+                              int row_bytes_b, const int32_t* start_pos, const int32_t* n_new, int B, int S,
+                              int T_max, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -54,6 +54,8 @@ def _declare(lib):
     lib.attn_decode_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, Z, P]
     lib.attn_prefill_gqa_causal.restype = I
     lib.attn_prefill_gqa_causal.argtypes = [P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.attn_cache_append.restype = I
+    lib.attn_cache_append.argtypes = [P, P, I, P, P, I, P, P, I, I, I, P]
     lib.attn_prefill_mla_causal.restype = I
     lib.attn_prefill_mla_causal.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, P]
     lib.attn_prefill_gqa_cached.restype = I
@@ -262,6 +264,34 @@ def attn_prefill_mla_causal(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, start_pos=
     return out
 
 
+def attn_cache_append(new_a, cache_a, new_b=None, cache_b=None, start_pos=None, n_new=None):
+    """cache_a[b, start_pos[b] + i] = new_a[b, i] for i < n_new[b] (and the same for the b pair):
+    K and V caches [B, T_max, Hkv, D] with new rows [B, S, Hkv, D], or the MLA caches c_kv
+    [B, T_max, r] and k_rope [B, T_max, dR].  start_pos, n_new [B] int32 or None (0, S)."""
+    _check(new_a, "new_a")
+    B, S = new_a.shape[0], new_a.shape[1]
+    _check(cache_a, "cache_a", dtype=new_a.dtype)
+    if cache_a.dim() != new_a.dim() or cache_a.shape[0] != B or tuple(cache_a.shape[2:]) != tuple(new_a.shape[2:]):
+        raise ValueError(f"cache_a must be [B={B}, T_max, {tuple(new_a.shape[2:])}] (got {tuple(cache_a.shape)})")
+    T_max = cache_a.shape[1]
+    rb_a = new_a[0, 0].numel() * new_a.element_size()
+    rb_b = 0
+    if new_b is not None:
+        _check(new_b, "new_b")
+        _check(cache_b, "cache_b", dtype=new_b.dtype)
+        if new_b.shape[0] != B or new_b.shape[1] != S or cache_b.shape[0] != B or cache_b.shape[1] != T_max or \
+                tuple(cache_b.shape[2:]) != tuple(new_b.shape[2:]):
+            raise ValueError("new_b / cache_b must be [B, S, ...] / [B, T_max, ...] like the a pair")
+        rb_b = new_b[0, 0].numel() * new_b.element_size()
+    if start_pos is not None:
+        _check(start_pos, "start_pos", shape=(B,), dtype=torch.int32)
+    if n_new is not None:
+        _check(n_new, "n_new", shape=(B,), dtype=torch.int32)
+    st = lib().attn_cache_append(_ptr(new_a), _ptr(cache_a), rb_a, _ptr(new_b), _ptr(cache_b), rb_b, _ptr(start_pos),
+                                 _ptr(n_new), B, S, T_max, _stream(new_a.device))
+    _raise_if(st, "attn_cache_append")
+
+
 def attn_decode_mla_workspace_bytes(B: int, H: int, kv_lora_rank: int, rope_dim: int, T_max: int,
                                     split_tokens: int = 0) -> int:
     return int(lib().attn_decode_mla_workspace_bytes(B, H, kv_lora_rank, rope_dim, T_max, split_tokens))
@@ -316,6 +346,6 @@ def attn_decode_mla_absorbed(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, cache_len
 
 
 __all__ = ["attn_decode_gqa", "attn_decode_gqa_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached",
-           "attn_prefill_mla_causal",
+           "attn_prefill_mla_causal", "attn_cache_append",
            "attn_decode_mla_absorbed", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",
            "AttnError", "lib", "header_functions", "LIB_PATH", "ATTN_F32", "ATTN_BF16"]

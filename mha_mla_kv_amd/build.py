@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn_mi355x.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_api.cpp", "decode_gqa.hip", "decode_mla.hip", "prefill_gqa.hip"]
+SOURCES = ["attn_api.cpp", "decode_gqa.hip", "decode_mla.hip", "prefill_gqa.hip", "cache_append.hip"]
 
 # -packed-fp32-ops off: keep fp32 arithmetic on plain (non-packed) VALU instructions.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -361,6 +361,39 @@ attn_status attn_prefill_mla_causal(const void* q_nope, const void* q_rope, cons
   return hip_status(attn::launch_mla_prefill(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+attn_status attn_cache_append(const void* new_a, void* cache_a, int row_bytes_a, const void* new_b, void* cache_b,
+                              int row_bytes_b, const int32_t* start_pos, const int32_t* n_new, int B, int S,
+                              int T_max, void* stream) {
+  static const char* fn = "attn_cache_append";
+  if (!new_a || !cache_a) return fail(ATTN_ERR_NULL, "%s: new_a and cache_a must be non-NULL", fn);
+  if (B <= 0 || S <= 0 || T_max <= 0 || row_bytes_a <= 0 || row_bytes_b < 0)
+    return fail(ATTN_ERR_SHAPE, "%s: sizes must be positive (B=%d S=%d T_max=%d row_bytes_a=%d row_bytes_b=%d)", fn, B,
+                S, T_max, row_bytes_a, row_bytes_b);
+  if (B > kMaxGridYZ) return fail(ATTN_ERR_SHAPE, "%s: B must be <= %d", fn, kMaxGridYZ);
+  if (row_bytes_a % 16 != 0 || row_bytes_b % 16 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: row sizes must be multiples of 16 bytes (%d, %d)", fn, row_bytes_a,
+                row_bytes_b);
+  if (row_bytes_b > 0 && (!new_b || !cache_b))
+    return fail(ATTN_ERR_NULL, "%s: new_b and cache_b must be non-NULL when row_bytes_b > 0", fn);
+  if ((long long)(row_bytes_a + (long long)row_bytes_b) / 16 * S > 0x7fffffffLL)
+    return fail(ATTN_ERR_SHAPE, "%s: S * row bytes too large", fn);
+  if (!aligned16(new_a) || !aligned16(cache_a) || (row_bytes_b > 0 && (!aligned16(new_b) || !aligned16(cache_b))))
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: buffers must be 16-byte aligned", fn);
+  attn::CacheAppendArgs a;
+  a.new_a = new_a;
+  a.cache_a = cache_a;
+  a.new_b = row_bytes_b > 0 ? new_b : nullptr;
+  a.cache_b = row_bytes_b > 0 ? cache_b : nullptr;
+  a.start_pos = start_pos;
+  a.n_new = n_new;
+  a.row_bytes_a = row_bytes_a;
+  a.row_bytes_b = row_bytes_b;
+  a.B = B;
+  a.S = S;
+  a.T_max = T_max;
+  return hip_status(attn::launch_cache_append(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 size_t attn_decode_mla_workspace_bytes(int B, int H, int kv_lora_rank, int rope_dim, int T_max,
                                        int split_tokens) {
   if (B <= 0 || H <= 0 || kv_lora_rank <= 0 || rope_dim < 0 || T_max <= 0 || !valid_split(split_tokens))

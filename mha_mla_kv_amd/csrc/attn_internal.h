@@ -66,6 +66,17 @@ struct MlaPrefillArgs {
   int out_bf16;
 };
 
+struct CacheAppendArgs {
+  const void* new_a;            // [B, S, row_bytes_a]
+  void* cache_a;                // [B, T_max, row_bytes_a]
+  const void* new_b;            // [B, S, row_bytes_b] (row_bytes_b 0: no second pair)
+  void* cache_b;                // [B, T_max, row_bytes_b]
+  const int32_t* start_pos;     // [B], or null: 0
+  const int32_t* n_new;         // [B], or null: S
+  int row_bytes_a, row_bytes_b; // multiples of 16
+  int B, S, T_max;
+};
+
 struct MlaDecodeArgs {
   const void* q_nope;   // [B, H, dn]
   const void* q_rope;   // [B, H, dR]
@@ -95,6 +106,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 bool mla_prefill_supported(int dn, int dR, int dv, int r);
 hipError_t launch_mla_prefill(const MlaPrefillArgs& a, hipStream_t stream);
+
+hipError_t launch_cache_append(const CacheAppendArgs& a, hipStream_t stream);
 
 bool mla_decode_supported(int H, int r, int dR);
 hipError_t launch_mla_decode(const MlaDecodeArgs& a, hipStream_t stream);

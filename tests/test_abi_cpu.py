@@ -23,7 +23,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = attn.lib()
     names = attn.header_functions()
     for required in ("attn_decode_gqa", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached",
-                     "attn_decode_mla_absorbed", "attn_prefill_mla_causal"):
+                     "attn_decode_mla_absorbed", "attn_prefill_mla_causal", "attn_cache_append"):
         assert required in names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/attn_mi355x.h but not exported"
@@ -145,6 +145,24 @@ def test_mla_prefill_validation():
     assert f(ind=F32) == UNSUP
     assert f(c=FAKE_MIS) == UNSUP
     assert b"not built" in lib.attn_last_error() or b"aligned" in lib.attn_last_error()
+
+
+@no_gpu_only
+def test_cache_append_validation():
+    lib = attn.lib()
+
+    def f(**kw):
+        return lib.attn_cache_append(kw.get("na", FAKE), kw.get("ca", FAKE), kw.get("ra", 256), kw.get("nb", FAKE),
+                                     kw.get("cb", FAKE), kw.get("rb", 256), None, None, kw.get("B", 2), kw.get("S", 4),
+                                     kw.get("T", 64), None)
+    assert f(na=None) == NULL
+    assert f(nb=None) == NULL
+    assert f(B=0) == SHAPE
+    assert f(T=0) == SHAPE
+    assert f(ra=0) == SHAPE
+    assert f(ra=100) == UNSUP
+    assert f(rb=8) == UNSUP
+    assert f(ca=FAKE_MIS) == UNSUP
 
 
 @no_gpu_only
