@@ -116,6 +116,42 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
                             size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* GQA decode step with the new token's K/V: append and attend in one call.
+ *
+ *   L = cache_lens[b] (positions cached before this token, clamped to [0, T_max])
+ *   out[b,h,:] = softmax over { k_cache[b,t,g] (t < L), k_new[b,g] } of
+ *                scale * q[b,h,:] . key, applied to the matching V rows
+ *   k_cache[b,L,g,:] = k_new[b,g,:], v_cache[b,L,g,:] = v_new[b,g,:]  when L < T_max
+ *
+ * This is one decode iteration of Attention.forward on the "模型架构｜MQA & GQA
+ * 调研" page (code section) with start_pos = L: the new token's K/V rows are
+ * written at start_pos and the query attends to the first start_pos + 1 rows.
+ * The result equals attn_cache_append followed by attn_decode_gqa with
+ * cache_lens + 1 (up to rounding: the new token's probability is not rounded
+ * to bf16), without the separate launch.  The cache rows below L are read, row
+ * L is written after they have been read; cache_lens itself is not changed (the
+ * caller advances it).  When L = T_max the new token is attended to but not
+ * stored.  Rotary embedding is the caller's (applied to q and k_new before).
+ *
+ *   q [B, Hq, head_dim], k_new, v_new [B, Hkv, head_dim] (in_dtype)
+ *   k_cache, v_cache, cache_lens, out, T_max, split_tokens: as attn_decode_gqa
+ *   workspace: at least attn_decode_gqa_append_workspace_bytes(...) bytes,
+ *   256-byte aligned, the first 4 bytes zero before first use (as for
+ *   attn_decode_gqa; every call leaves them zero)
+ *
+ * Supported shapes, errors and ownership as attn_decode_gqa, plus
+ * ATTN_ERR_NULL for a NULL k_new or v_new.
+ */
+size_t attn_decode_gqa_append_workspace_bytes(int B, int Hq, int Hkv, int head_dim, int T_max,
+                                              int split_tokens);
+
+attn_status attn_decode_gqa_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                   void* v_cache, const int32_t* cache_lens, void* out, int B, int Hq, int Hkv,
+                                   int head_dim, int T_max, float softmax_scale, attn_dtype in_dtype,
+                                   attn_dtype out_dtype, int split_tokens, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Causal GQA prefill (no cached prefix): query i attends to keys j <= i.
  *
  *   out[b,i,h,:] = sum_{j <= i} softmax_j(scale * q[b,i,h,:] . k[b,j,g,:]) v[b,j,g,:]

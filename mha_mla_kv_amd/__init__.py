@@ -54,6 +54,10 @@ def _declare(lib):
     lib.attn_decode_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, Z, P]
     lib.attn_prefill_gqa_causal.restype = I
     lib.attn_prefill_gqa_causal.argtypes = [P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.attn_decode_gqa_append_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_decode_gqa_append_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.attn_decode_gqa_append.restype = I
+    lib.attn_decode_gqa_append.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, ctypes.c_size_t, P]
     lib.attn_cache_append.restype = I
     lib.attn_cache_append.argtypes = [P, P, I, P, P, I, P, P, I, I, I, P]
     lib.attn_prefill_mla_causal.restype = I
@@ -173,6 +177,41 @@ def attn_decode_gqa(q, k_cache, v_cache, cache_lens, out=None, softmax_scale: fl
                                Hkv, D, T_max, float(softmax_scale), _dt(q), _dt(out), int(split_tokens),
                                _ptr(workspace), workspace.numel(), _stream(q.device))
     _raise_if(st, "attn_decode_gqa")
+    return out
+
+
+def attn_decode_gqa_append_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, T_max: int,
+                                           split_tokens: int = 0) -> int:
+    return int(lib().attn_decode_gqa_append_workspace_bytes(B, Hq, Hkv, D, T_max, split_tokens))
+
+
+def attn_decode_gqa_append(q, k_new, v_new, k_cache, v_cache, cache_lens, out=None, softmax_scale: float = 0.0,
+                           out_dtype=torch.float32, split_tokens: int = 0, workspace=None):
+    """One decode step with the new token: writes k_new/v_new [B,Hkv,D] into the caches at row
+    cache_lens[b] and attends q [B,Hq,D] to the cache_lens[b] cached rows plus the new one.
+    cache_lens is not changed.  Returns out [B,Hq,D]."""
+    _check(q, "q")
+    B, Hq, D = q.shape
+    _check(k_cache, "k_cache", dtype=q.dtype)
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError(f"k_cache must be [B={B}, T_max, Hkv, {D}] (got {tuple(k_cache.shape)})")
+    T_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _check(v_cache, "v_cache", shape=k_cache.shape, dtype=q.dtype)
+    _check(k_new, "k_new", shape=(B, Hkv, D), dtype=q.dtype)
+    _check(v_new, "v_new", shape=(B, Hkv, D), dtype=q.dtype)
+    _check(cache_lens, "cache_lens", shape=(B,), dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    _check(out, "out", shape=(B, Hq, D))
+    need = attn_decode_gqa_append_workspace_bytes(B, Hq, Hkv, D, T_max, split_tokens)
+    if workspace is None:
+        workspace = _workspace(need, q.device, "gqa_append")
+    _check(workspace, "workspace", dtype=torch.uint8)
+    st = lib().attn_decode_gqa_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(cache_lens), _ptr(out), B, Hq, Hkv, D, T_max, float(softmax_scale), _dt(q),
+                                      _dt(out), int(split_tokens), _ptr(workspace), workspace.numel(),
+                                      _stream(q.device))
+    _raise_if(st, "attn_decode_gqa_append")
     return out
 
 
@@ -345,7 +384,8 @@ def attn_decode_mla_absorbed(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, cache_len
     return out
 
 
-__all__ = ["attn_decode_gqa", "attn_decode_gqa_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached",
+__all__ = ["attn_decode_gqa", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_append",
+           "attn_decode_gqa_append_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached",
            "attn_prefill_mla_causal", "attn_cache_append",
            "attn_decode_mla_absorbed", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",
            "AttnError", "lib", "header_functions", "LIB_PATH", "ATTN_F32", "ATTN_BF16"]

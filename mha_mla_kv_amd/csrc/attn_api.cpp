@@ -80,13 +80,13 @@ struct GqaLayout {
   size_t lse_off, o_off, total;
 };
 
-GqaLayout gqa_layout(int B, int Hq, int Hkv, int D, int T_max, int split_tokens) {
+GqaLayout gqa_layout(int B, int Hq, int Hkv, int D, int T_max, int split_tokens, bool all_partials = false) {
   GqaLayout l;
   const int n_rep = Hq / (Hkv > 0 ? Hkv : 1);
   l.chunk = split_tokens ? split_tokens : choose_chunk(B, Hkv, n_rep, T_max);
   l.n_chunks = (int)(((long long)T_max + l.chunk - 1) / l.chunk);
   l.queue = B <= attn::kQueueMaxB && l.n_chunks >= 2;
-  l.slots = l.n_chunks >= 2 ? (long long)B * Hkv * l.n_chunks : 0;
+  l.slots = (l.n_chunks >= 2 || all_partials) ? (long long)B * Hkv * l.n_chunks : 0;
   l.lse_off = 256;
   l.o_off = l.lse_off + align_up((size_t)l.slots * n_rep * sizeof(float));
   l.total = l.o_off + align_up((size_t)l.slots * n_rep * D * sizeof(float));
@@ -171,44 +171,48 @@ size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int head_dim, int
   return gqa_layout(B, Hq, Hkv, head_dim, T_max, split_tokens).total;
 }
 
-attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* cache_lens, void* out, int B, int Hq, int Hkv,
-                            int head_dim, int T_max, float softmax_scale, attn_dtype in_dtype,
-                            attn_dtype out_dtype, int split_tokens, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+namespace {
+
+// Shared checks and launch of the two decode entry points.  k_new != null: a
+// decode step that also takes the new token's K/V (see attn_decode_gqa_append).
+attn_status gqa_decode_common(const char* fn, const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                              const void* v_cache, const int32_t* cache_lens, void* out, int B, int Hq, int Hkv,
+                              int head_dim, int T_max, float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype,
+                              int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  const bool append = k_new != nullptr;
   if (!q || !k_cache || !v_cache || !cache_lens || !out)
-    return fail(ATTN_ERR_NULL, "attn_decode_gqa: q, k_cache, v_cache, cache_lens and out must be non-NULL");
+    return fail(ATTN_ERR_NULL, "%s: q, k_cache, v_cache, cache_lens and out must be non-NULL", fn);
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || head_dim <= 0 || T_max <= 0)
-    return fail(ATTN_ERR_SHAPE, "attn_decode_gqa: sizes must be positive (B=%d Hq=%d Hkv=%d head_dim=%d T_max=%d)",
+    return fail(ATTN_ERR_SHAPE, "%s: sizes must be positive (B=%d Hq=%d Hkv=%d head_dim=%d T_max=%d)", fn,
                 B, Hq, Hkv, head_dim, T_max);
   if (B > kMaxGridYZ || Hkv > kMaxGridYZ)
-    return fail(ATTN_ERR_SHAPE, "attn_decode_gqa: B and Hkv must be <= %d", kMaxGridYZ);
+    return fail(ATTN_ERR_SHAPE, "%s: B and Hkv must be <= %d", fn, kMaxGridYZ);
   if (Hq % Hkv != 0)
-    return fail(ATTN_ERR_GROUPS, "attn_decode_gqa: Hkv=%d does not divide Hq=%d (remainder %d); not rounded",
+    return fail(ATTN_ERR_GROUPS, "%s: Hkv=%d does not divide Hq=%d (remainder %d); not rounded", fn,
                 Hkv, Hq, Hq % Hkv);
   if (!valid_split(split_tokens))
-    return fail(ATTN_ERR_SHAPE, "attn_decode_gqa: split_tokens=%d must be 0 or a multiple of 64 in [64, 65536]",
+    return fail(ATTN_ERR_SHAPE, "%s: split_tokens=%d must be 0 or a multiple of 64 in [64, 65536]", fn,
                 split_tokens);
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_gqa: unknown dtype");
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
   const int n_rep = Hq / Hkv;
   const int in_bf16 = in_dtype == ATTN_BF16;
   if (!attn::gqa_decode_supported(head_dim, n_rep, in_bf16))
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_gqa: head_dim=%d with Hq/Hkv=%d and %s inputs is not built",
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: head_dim=%d with Hq/Hkv=%d and %s inputs is not built", fn,
                 head_dim, n_rep, in_bf16 ? "bf16" : "fp32");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_gqa: q, caches and out must be 16-byte aligned");
-  const GqaLayout lay = gqa_layout(B, Hq, Hkv, head_dim, T_max, split_tokens);
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: q, caches and out must be 16-byte aligned", fn);
+  const GqaLayout lay = gqa_layout(B, Hq, Hkv, head_dim, T_max, split_tokens, append);
   if (!lay.queue && lay.n_chunks > kMaxGridYZ)
-    return fail(ATTN_ERR_SHAPE, "attn_decode_gqa: ceil(T_max/split_tokens)=%d chunks exceed %d", lay.n_chunks,
+    return fail(ATTN_ERR_SHAPE, "%s: ceil(T_max/split_tokens)=%d chunks exceed %d", fn, lay.n_chunks,
                 kMaxGridYZ);
   if (lay.slots >= (1ll << 31) / (n_rep > 0 ? n_rep : 1))
-    return fail(ATTN_ERR_SHAPE, "attn_decode_gqa: too many chunks (B*Hkv*ceil(T_max/split_tokens) too large)");
+    return fail(ATTN_ERR_SHAPE, "%s: too many chunks (B*Hkv*ceil(T_max/split_tokens) too large)", fn);
   if (!workspace || workspace_bytes < lay.total)
-    return fail(ATTN_ERR_WORKSPACE, "attn_decode_gqa: workspace of %zu bytes needed, %zu given%s", lay.total,
+    return fail(ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given%s", fn, lay.total,
                 workspace_bytes, workspace ? "" : " (NULL)");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(ATTN_ERR_WORKSPACE, "attn_decode_gqa: workspace must be 256-byte aligned");
+    return fail(ATTN_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
 
   attn::GqaDecodeArgs a;
   a.q = q;
@@ -236,7 +240,7 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
     // at most four decode workgroups fit on a compute unit; the launcher trims
     // the grid to what is actually resident
     const int cus = device_cus();
-    if (cus <= 0) return fail(ATTN_ERR_HIP, "attn_decode_gqa: cannot query the current device");
+    if (cus <= 0) return fail(ATTN_ERR_HIP, "%s: cannot query the current device", fn);
     a.cus = cus;
     a.grid_wgs = cus * 4;
     // big units only where every workgroup still gets many units when the
@@ -247,7 +251,44 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
   a.scale_log2e = scale * kLog2e;
   a.in_bf16 = in_bf16;
   a.out_bf16 = out_dtype == ATTN_BF16;
-  return hip_status(attn::launch_gqa_decode(a, static_cast<hipStream_t>(stream)), "attn_decode_gqa");
+  a.append = append;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = const_cast<void*>(k_cache);
+  a.v_cache = const_cast<void*>(v_cache);
+  return hip_status(attn::launch_gqa_decode(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace
+
+attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* cache_lens, void* out, int B, int Hq, int Hkv,
+                            int head_dim, int T_max, float softmax_scale, attn_dtype in_dtype,
+                            attn_dtype out_dtype, int split_tokens, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return gqa_decode_common("attn_decode_gqa", q, nullptr, nullptr, k_cache, v_cache, cache_lens, out, B, Hq, Hkv,
+                           head_dim, T_max, softmax_scale, in_dtype, out_dtype, split_tokens, workspace,
+                           workspace_bytes, stream);
+}
+
+size_t attn_decode_gqa_append_workspace_bytes(int B, int Hq, int Hkv, int head_dim, int T_max, int split_tokens) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || head_dim <= 0 || T_max <= 0 || !valid_split(split_tokens))
+    return 0;
+  return gqa_layout(B, Hq, Hkv, head_dim, T_max, split_tokens, true).total;
+}
+
+attn_status attn_decode_gqa_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                   void* v_cache, const int32_t* cache_lens, void* out, int B, int Hq, int Hkv,
+                                   int head_dim, int T_max, float softmax_scale, attn_dtype in_dtype,
+                                   attn_dtype out_dtype, int split_tokens, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (!k_new || !v_new)
+    return fail(ATTN_ERR_NULL, "attn_decode_gqa_append: k_new and v_new must be non-NULL");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_gqa_append: k_new and v_new must be 16-byte aligned");
+  return gqa_decode_common("attn_decode_gqa_append", q, k_new, v_new, k_cache, v_cache, cache_lens, out, B, Hq,
+                           Hkv, head_dim, T_max, softmax_scale, in_dtype, out_dtype, split_tokens, workspace,
+                           workspace_bytes, stream);
 }
 
 namespace {

@@ -36,6 +36,14 @@ struct GqaDecodeArgs {
   float scale_log2e;      // softmax scale * log2(e)
   int in_bf16;            // 1: bf16 inputs, 0: fp32 inputs
   int out_bf16;           // 1: bf16 output, 0: fp32 output
+  // decode step with the new token's K/V (append != 0): every unit writes a
+  // partial, and the merge adds the new token and writes it to the cache at
+  // position lens[b] (when lens[b] < T_max)
+  int append;
+  const void* k_new;      // [B, Hkv, D]
+  const void* v_new;      // [B, Hkv, D]
+  void* k_cache;          // the k array, written at the new position
+  void* v_cache;          // the v array
 };
 
 struct PrefillArgs {

@@ -78,6 +78,7 @@ __device__ __forceinline__ float sum_xor32(float x) { const float2 p = pair_xor3
 
 // exp2(m - M) that is 0 (not NaN) when m is -inf.
 __device__ __forceinline__ float rescale(float m, float M) { return m == kNegInf ? 0.f : exp2_fast(m - M); }
+__device__ __forceinline__ float bf16_to_f32(u16 x) { return __builtin_bit_cast(float, (unsigned)x << 16); }
 
 // Cache policy of the K/V loads: non-temporal (streaming).  The cache is read
 // once per call; these loads neither displace reusable lines nor wait on them.
@@ -274,7 +275,7 @@ __device__ void store_unit(const GqaDecodeArgs& a, const Unit& u, const float* o
     }
     return v;
   };
-  if (u.n == 1) {
+  if (u.n == 1 && !a.append) {
     const size_t row0 = (size_t)u.b * a.Hq + (size_t)u.g * n_rep;
     for (int e = tid; e < n_rep * D2; e += 256) {
       const int hd = e / D2, d2 = e - hd * D2;
@@ -428,6 +429,11 @@ constexpr int kMergePairs = 256;
 // (Hkv * ceil(n_rep * D / 2 / kMergePairs), B): each thread merges one pair
 // of output elements.  Also returns the queue counter to zero for the next
 // call (the decode kernel has finished: same stream).
+// In a decode step with the new token (a.append), every (sequence, KV head) is
+// merged: the new token is one more partial, with log2 score
+// scale_log2e * q . k_new and output v_new, and the thread of query head 0 of
+// the group writes its element pair of k_new and v_new to the cache row
+// lens[b] (the decode kernel read only rows below it).
 __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
   const int tid = threadIdx.x, b = blockIdx.y;
   if (a.use_queue && blockIdx.x == 0 && b == 0 && tid == 0) *a.queue = 0u;
@@ -435,9 +441,10 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
   const int n_eb = (n_rep * D2 + kMergePairs - 1) / kMergePairs;
   const int g = blockIdx.x / n_eb, e = (blockIdx.x - g * n_eb) * kMergePairs + tid;
   if (e >= n_rep * D2) return;
-  const Split sp = split_of(a, clamp_len(a.lens[b], a.T_max));
+  const int L = clamp_len(a.lens[b], a.T_max);
+  const Split sp = split_of(a, L);
   const int n = sp.parts();
-  if (n <= 1) return;  // written by the decode kernel
+  if (n <= 1 && !a.append) return;  // written by the decode kernel
   const size_t s0 = ((size_t)b * a.Hkv + g) * a.n_chunks;
   const float* lse = a.lse + s0 * n_rep;
   const size_t row0 = (size_t)b * a.Hq + (size_t)g * n_rep;
@@ -468,6 +475,56 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
         acc.y = acc.y * f + wk * v[k].y;
         M = Mn;
       }
+    }
+    if (a.append) {
+      const size_t kv = ((size_t)b * a.Hkv + g) * a.D;
+      const size_t qr = (row0 + hd) * a.D;
+      float dot = 0.f, vx, vy;
+      if (a.in_bf16) {
+        const u16* qp = static_cast<const u16*>(a.q) + qr;
+        const u16* kp = static_cast<const u16*>(a.k_new) + kv;
+        for (int d = 0; d < a.D; d += 8) {
+          const u16x8 qa = *reinterpret_cast<const u16x8*>(qp + d);
+          const u16x8 ka = *reinterpret_cast<const u16x8*>(kp + d);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dot = fmaf(bf16_to_f32(qa[i]), bf16_to_f32(ka[i]), dot);
+        }
+        const unsigned vw = *reinterpret_cast<const unsigned*>(static_cast<const u16*>(a.v_new) + kv + 2 * d2);
+        vx = bf16_to_f32((u16)(vw & 0xffffu));
+        vy = bf16_to_f32((u16)(vw >> 16));
+        if (hd == 0 && L < a.T_max) {
+          const size_t dst = ((size_t)b * a.T_max + L) * a.Hkv * a.D + (size_t)g * a.D + 2 * d2;
+          *reinterpret_cast<unsigned*>(static_cast<u16*>(a.k_cache) + dst) =
+              *reinterpret_cast<const unsigned*>(kp + 2 * d2);
+          *reinterpret_cast<unsigned*>(static_cast<u16*>(a.v_cache) + dst) = vw;
+        }
+      } else {
+        const float* qp = static_cast<const float*>(a.q) + qr;
+        const float* kp = static_cast<const float*>(a.k_new) + kv;
+        for (int d = 0; d < a.D; d += 4) {
+          const float4 qa = *reinterpret_cast<const float4*>(qp + d);
+          const float4 ka = *reinterpret_cast<const float4*>(kp + d);
+          dot = fmaf(qa.x, ka.x, dot);
+          dot = fmaf(qa.y, ka.y, dot);
+          dot = fmaf(qa.z, ka.z, dot);
+          dot = fmaf(qa.w, ka.w, dot);
+        }
+        const float2 vv = *reinterpret_cast<const float2*>(static_cast<const float*>(a.v_new) + kv + 2 * d2);
+        vx = vv.x;
+        vy = vv.y;
+        if (hd == 0 && L < a.T_max) {
+          const size_t dst = ((size_t)b * a.T_max + L) * a.Hkv * a.D + (size_t)g * a.D + 2 * d2;
+          *reinterpret_cast<float2*>(static_cast<float*>(a.k_cache) + dst) =
+              *reinterpret_cast<const float2*>(kp + 2 * d2);
+          *reinterpret_cast<float2*>(static_cast<float*>(a.v_cache) + dst) = vv;
+        }
+      }
+      const float s = dot * a.scale_log2e;
+      const float Mn = fmaxf(M, s);
+      const float f = rescale(M, Mn), wk = exp2_fast(s - Mn);
+      S = S * f + wk;
+      acc.x = acc.x * f + wk * vx;
+      acc.y = acc.y * f + wk * vy;
     }
     const float sc = 1.f / S;
     store_out2(a, row0 + hd, 2 * d2, acc.x * sc, acc.y * sc);

@@ -23,7 +23,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = attn.lib()
     names = attn.header_functions()
     for required in ("attn_decode_gqa", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached",
-                     "attn_decode_mla_absorbed", "attn_prefill_mla_causal", "attn_cache_append"):
+                     "attn_decode_mla_absorbed", "attn_prefill_mla_causal", "attn_cache_append",
+                     "attn_decode_gqa_append"):
         assert required in names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/attn_mi355x.h but not exported"
@@ -93,6 +94,24 @@ def test_decode_gqa_validation():
     assert _gqa(lib, wsb=16) == WS
     assert b"workspace" in lib.attn_last_error()
     assert _gqa(lib, ws=FAKE_MIS) == WS
+
+
+@no_gpu_only
+def test_decode_append_validation():
+    lib = attn.lib()
+
+    def f(**kw):
+        return lib.attn_decode_gqa_append(FAKE, kw.get("kn", FAKE), kw.get("vn", FAKE), FAKE, FAKE, FAKE, FAKE,
+                                          kw.get("B", 2), 8, 2, 128, kw.get("T", 64), 0.0, BF16, F32, 0,
+                                          kw.get("ws", FAKE), kw.get("wsb", 1 << 30), None)
+    assert f(kn=None) == NULL
+    assert f(vn=FAKE_MIS) == UNSUP
+    assert f(B=0) == SHAPE
+    assert f(ws=None) == WS
+    assert f(wsb=300) == WS   # partials are needed even for a single chunk
+    # a single chunk per sequence still needs partial slots in the fused step
+    plain = attn.attn_decode_gqa_workspace_bytes(2, 8, 2, 128, 64, 0)
+    assert plain == 256 and attn.attn_decode_gqa_append_workspace_bytes(2, 8, 2, 128, 64, 0) > plain
 
 
 @no_gpu_only
