@@ -17,6 +17,8 @@ One step = one pass over the three C-ABI entry points, each on its own synthetic
   * attn_cache_append         the decode step's K/V write: each of the 32 Llama-3 sequences'
                               newest K and V rows written at position cache_lens - 1 (the rows
                               it already holds, so the decode inputs do not change)
+  * attn_decode_gqa_append    the same write and the decode in one call (cache_lens - 1 cached
+                              rows plus the new one: the same attention as attn_decode_gqa)
 
 The printed `value` is the GQA decode's KV-cache read rate (algorithmic bytes: every cached
 K and V row read once per KV head, 2*Hkv*head_dim*2 bytes per cached position) divided by
@@ -119,6 +121,10 @@ def main():
     app_k = dec["k"][torch.arange(B, device=dev), last.long()].unsqueeze(1).contiguous()  # [B, 1, Hkv, D]
     app_v = dec["v"][torch.arange(B, device=dev), last.long()].unsqueeze(1).contiguous()
     app_bytes = 2 * 2 * B * Hkv * D * 2                       # K and V rows, read once and written once
+    app_new_k, app_new_v = app_k[:, 0].contiguous(), app_v[:, 0].contiguous()  # [B, Hkv, D]
+    step_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    step_ws = torch.zeros(attn.attn_decode_gqa_append_workspace_bytes(B, Hq, Hkv, D, T_max, 0), dtype=torch.uint8,
+                          device=dev)
 
     mspec = synth.WORKLOADS["minimind768_mla_decode"]
     mla_cpu = synth.make("minimind768_mla_decode")
@@ -183,6 +189,10 @@ def main():
     def run_append():
         attn.attn_cache_append(app_k, dec["k"], app_v, dec["v"], app_pos)
 
+    def run_step():
+        attn.attn_decode_gqa_append(dec["q"], app_new_k, app_new_v, dec["k"], dec["v"], app_pos, out=step_out,
+                                    workspace=step_ws)
+
     def run_mla_prefill():
         attn.attn_prefill_mla_causal(mlp["q_nope"], mlp["q_rope"], mlp["w_uk"], mlp["w_uv"], mlp["c_kv"], mlp["k_rope"],
                                      out=mlp_out)
@@ -193,7 +203,8 @@ def main():
     # prefill for new requests, then the decode steps of running ones (the order a serving
     # step takes); each part is timed on its own
     parts = [("prefill", run_prefill), ("chunked_prefill", run_chunked), ("mla_prefill", run_mla_prefill),
-             ("mla_decode", run_mla), ("kv_append", run_append), ("gqa_decode", run_decode)]
+             ("mla_decode", run_mla), ("kv_append", run_append), ("gqa_decode", run_decode),
+             ("gqa_decode_step", run_step)]
     if args.copy_calibration:
         parts.append(("copy_1GiB", lambda: copy_dst.copy_(copy_src)))
 
@@ -244,7 +255,8 @@ def main():
                          f"cache_lens~U[{dspec['lens'][0]},{dspec['lens'][1]}] (sum {sum_len}) seed={dspec['seed']}, "
                          "bf16 in, fp32 out, default schedule (device-wide unit queue, library-chosen blocks)"),
             "step": ("attn_prefill_gqa_causal, attn_prefill_gqa_cached, attn_prefill_mla_causal, "
-                     "attn_decode_mla_absorbed, attn_cache_append, attn_decode_gqa: one call each, in this order"),
+                     "attn_decode_mla_absorbed, attn_cache_append, attn_decode_gqa, attn_decode_gqa_append: one "
+                     "call each, in this order"),
             "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "prefill": PB * S, "chunked_prefill": chk_tokens,
                                 "mla_prefill": MPB * MPS},
         },
@@ -284,6 +296,10 @@ def main():
                                 "workload": f"llama3_8b_gqa_chunked_prefill: B={CB} chunk={CS} "
                                             f"start_pos={cspec['start_pos']} T_max={CT} Hq={CHq} "
                                             f"Hkv={chk['k'].shape[2]} head_dim={CD} seed={cspec['seed']} bf16"},
+            "gqa_decode_step": {"ms": round(ms["gqa_decode_step"], 5),
+                                "GB/s": round(dec_bytes / (ms["gqa_decode_step"] * 1e-3) / 1e9, 1),
+                                "workload": "llama3_8b_gqa_decode with the newest rows as the new token "
+                                            "(attn_decode_gqa_append: write + decode in one call)"},
             "kv_append": {"ms": round(ms["kv_append"], 5), "bytes_per_launch": app_bytes,
                           "GB/s": round(app_bytes / (ms["kv_append"] * 1e-3) / 1e9, 1),
                           "workload": f"llama3_8b_gqa_decode step write: B={B} rows of Hkv={Hkv} x {D} for K and V"},
