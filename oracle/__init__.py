@@ -221,6 +221,21 @@ def cache_append(cache, new, start_pos=None, n_new=None) -> np.ndarray:
     return out
 
 
+def e4m3_to_float(codes, scale: float = 1.0) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes (uint8 array) times scale, as float64: sign bit 7,
+    exponent bits 6..3 with bias 7, mantissa bits 2..0; exponent 0 is subnormal
+    (m/8 * 2^-6); exponent 15 with mantissa 7 is NaN (there is no infinity).  Written from the
+    format's definition; the low-precision cache reading of the MHA, MQA and GQA e-book
+    (fp8: one byte per cached number) takes this format with one scale per cache."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val * float(scale)
+
+
 def threads(lib=None) -> int:
     """OpenMP threads the oracle runs with."""
     return int((lib or load()).oracle_threads())

@@ -72,6 +72,30 @@ def gqa_decode_inputs(B: int, Hq: int, Hkv: int, D: int, T_max: int, lens, dtype
     return {"q": q, "k": k, "v": v, "cache_lens": torch.from_numpy(L.copy())}
 
 
+def gqa_decode_fp8_inputs(B: int, Hq: int, Hkv: int, D: int, T_max: int, lens, seed: int = 0,
+                          poison: bool = True) -> dict:
+    """q [B,Hq,D] bf16 and K/V caches [B,T_max,Hkv,D] stored as FP8 E4M3 (torch.float8_e4m3fn)
+    with one scale per cache: each cache is drawn N(0, 1) in float32 and divided by
+    scale = max|x| / 448 before the cast (round to nearest even), so the largest code is 448.
+    Draw order q, k, v, lens.  With poison, codes past each length are NaN (0x7F)."""
+    rng = _rng(seed)
+    q = _as(_normal(rng, (B, Hq, D)), "bf16")
+    k = _normal(rng, (B, T_max, Hkv, D))
+    v = _normal(rng, (B, T_max, Hkv, D))
+    L = _lengths(rng, B, T_max, lens)
+    out = {"q": q, "cache_lens": torch.from_numpy(L.copy())}
+    for name, x in (("k", k), ("v", v)):
+        scale = float(np.abs(x).max()) / 448.0
+        codes = torch.from_numpy(x / np.float32(scale)).to(torch.float8_e4m3fn)
+        if poison:
+            raw = codes.view(torch.uint8)
+            for b, n in enumerate(L.tolist()):
+                raw[b, max(0, min(int(n), T_max)):] = 0x7F
+        out[name] = codes
+        out[name + "_scale"] = scale
+    return out
+
+
 def gqa_prefill_inputs(B: int, S: int, Hq: int, Hkv: int, D: int, dtype: str = "bf16",
                        seed: int = 0) -> dict:
     """q [B,S,Hq,D], k/v [B,S,Hkv,D].  Draw order q, k, v."""

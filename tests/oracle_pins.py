@@ -512,6 +512,20 @@ def pin_cache_append(lib):
     assert np.array_equal(k3[1, :2], new_k[1, :2]) and np.array_equal(k3[1, 2:], cache_k[1, 2:])
 
 
+def pin_e4m3_decoding(lib):
+    """Every FP8 E4M3 code against torch's float8_e4m3fn conversion (a library routine), plus
+    the format's landmarks: 1.0, the largest finite 448, the smallest subnormal 2^-9, NaN."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.e4m3_to_float(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isnan(got), ~fin), "NaN codes"
+    assert np.array_equal(got[fin], ref[fin]), "E4M3 values"
+    assert oracle.e4m3_to_float([0x38])[0] == 1.0 and oracle.e4m3_to_float([0x7E])[0] == 448.0
+    assert oracle.e4m3_to_float([0x01])[0] == 2.0 ** -9 and oracle.e4m3_to_float([0xB8], 0.5)[0] == -0.5
+
+
 ALL_PINS = [pin_decode_vs_sdpa, pin_decode_closed_forms, pin_decode_invariants, pin_decode_head_structure,
             pin_prefill_vs_sdpa, pin_prefill_rows, pin_cached_vs_sdpa, pin_cached_reductions, pin_mla_vs_sdpa, pin_mla_absorbed_equals_decompressed,
-            pin_mla_selection, pin_mla_prefill_vs_sdpa, pin_mla_prefill_rows_are_decodes, pin_cache_append]
+            pin_mla_selection, pin_mla_prefill_vs_sdpa, pin_mla_prefill_rows_are_decodes, pin_cache_append,
+            pin_e4m3_decoding]
