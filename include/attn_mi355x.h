@@ -116,6 +116,32 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
                             size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* GQA decode over caches stored as 8-bit floats (OCP FP8 E4M3).
+ *
+ *   K[b,t,g,:] = k_scale * e4m3(k_cache[b,t,g,:]),  V likewise with v_scale,
+ *   out[b,h,:] = sum_{t<L_b} softmax_t(scale * q[b,h,:] . K[b,t,g,:]) V[b,t,g,:]
+ *
+ * The same attention as attn_decode_gqa over caches of half the bytes: the fp8
+ * number type of the "MHA, MQA và GQA" e-book's simulator configuration (8 bits
+ * per cached number).  The pages give no quantisation scheme; the one taken here is one
+ * byte per element in the OCP FP8 E4M3 format (sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits, largest finite 448; the byte 0x7F/0xFF is NaN) and one
+ * fp32 scale per cache.  Encoding the cache is the caller's.  The codes are
+ * widened to bf16 exactly; q is bf16; scores, softmax and accumulation are as
+ * in attn_decode_gqa.
+ *
+ *   q [B, Hq, 128] bf16;  k_cache, v_cache [B, T_max, Hkv, 128] one byte each;
+ *   k_scale, v_scale > 0 and finite (else ATTN_ERR_SHAPE);  cache_lens, out,
+ *   split_tokens, workspace (attn_decode_gqa_workspace_bytes) as attn_decode_gqa
+ *
+ * head_dim must be 128 (else ATTN_ERR_UNSUPPORTED); Hq/Hkv up to 64.
+ */
+attn_status attn_decode_gqa_fp8kv(const void* q, const void* k_cache, const void* v_cache, float k_scale,
+                                  float v_scale, const int32_t* cache_lens, void* out, int B, int Hq, int Hkv,
+                                  int head_dim, int T_max, float softmax_scale, attn_dtype out_dtype, int split_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* GQA decode step with the new token's K/V: append and attend in one call.
  *
  *   L = cache_lens[b] (positions cached before this token, clamped to [0, T_max])

@@ -54,6 +54,8 @@ def _declare(lib):
     lib.attn_decode_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, Z, P]
     lib.attn_prefill_gqa_causal.restype = I
     lib.attn_prefill_gqa_causal.argtypes = [P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.attn_decode_gqa_fp8kv.restype = I
+    lib.attn_decode_gqa_fp8kv.argtypes = [P, P, P, F, F, P, P, I, I, I, I, I, F, I, I, P, ctypes.c_size_t, P]
     lib.attn_decode_gqa_append_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode_gqa_append_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.attn_decode_gqa_append.restype = I
@@ -177,6 +179,33 @@ def attn_decode_gqa(q, k_cache, v_cache, cache_lens, out=None, softmax_scale: fl
                                Hkv, D, T_max, float(softmax_scale), _dt(q), _dt(out), int(split_tokens),
                                _ptr(workspace), workspace.numel(), _stream(q.device))
     _raise_if(st, "attn_decode_gqa")
+    return out
+
+
+def attn_decode_gqa_fp8kv(q, k_cache, v_cache, k_scale: float, v_scale: float, cache_lens, out=None,
+                          softmax_scale: float = 0.0, out_dtype=torch.float32, split_tokens: int = 0, workspace=None):
+    """GQA decode over FP8 E4M3 caches (torch.float8_e4m3fn, [B,T_max,Hkv,128]) holding K/k_scale
+    and V/v_scale; q [B,Hq,128] bf16.  Returns out [B,Hq,128]."""
+    _check(q, "q", dtype=torch.bfloat16)
+    B, Hq, D = q.shape
+    _check(k_cache, "k_cache", dtype=torch.float8_e4m3fn)
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError(f"k_cache must be [B={B}, T_max, Hkv, {D}] (got {tuple(k_cache.shape)})")
+    T_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _check(v_cache, "v_cache", shape=k_cache.shape, dtype=torch.float8_e4m3fn)
+    _check(cache_lens, "cache_lens", shape=(B,), dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    _check(out, "out", shape=(B, Hq, D))
+    need = attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T_max, split_tokens)
+    if workspace is None:
+        workspace = _workspace(need, q.device, "gqa")
+    _check(workspace, "workspace", dtype=torch.uint8)
+    st = lib().attn_decode_gqa_fp8kv(_ptr(q), _ptr(k_cache), _ptr(v_cache), float(k_scale), float(v_scale),
+                                     _ptr(cache_lens), _ptr(out), B, Hq, Hkv, D, T_max, float(softmax_scale),
+                                     _dt(out), int(split_tokens), _ptr(workspace), workspace.numel(),
+                                     _stream(q.device))
+    _raise_if(st, "attn_decode_gqa_fp8kv")
     return out
 
 
@@ -384,7 +413,7 @@ def attn_decode_mla_absorbed(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, cache_len
     return out
 
 
-__all__ = ["attn_decode_gqa", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_append",
+__all__ = ["attn_decode_gqa", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
            "attn_decode_gqa_append_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached",
            "attn_prefill_mla_causal", "attn_cache_append",
            "attn_decode_mla_absorbed", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",

@@ -175,11 +175,14 @@ namespace {
 
 // Shared checks and launch of the two decode entry points.  k_new != null: a
 // decode step that also takes the new token's K/V (see attn_decode_gqa_append).
+// kv_scales != null: caches of FP8 E4M3 codes with scales {k_scale, v_scale}.
 attn_status gqa_decode_common(const char* fn, const void* q, const void* k_new, const void* v_new, const void* k_cache,
                               const void* v_cache, const int32_t* cache_lens, void* out, int B, int Hq, int Hkv,
                               int head_dim, int T_max, float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype,
-                              int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+                              int split_tokens, void* workspace, size_t workspace_bytes, void* stream,
+                              const float* kv_scales = nullptr) {
   const bool append = k_new != nullptr;
+  const bool kv_fp8 = kv_scales != nullptr;
   if (!q || !k_cache || !v_cache || !cache_lens || !out)
     return fail(ATTN_ERR_NULL, "%s: q, k_cache, v_cache, cache_lens and out must be non-NULL", fn);
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || head_dim <= 0 || T_max <= 0)
@@ -200,6 +203,8 @@ attn_status gqa_decode_common(const char* fn, const void* q, const void* k_new, 
   if (!attn::gqa_decode_supported(head_dim, n_rep, in_bf16))
     return fail(ATTN_ERR_UNSUPPORTED, "%s: head_dim=%d with Hq/Hkv=%d and %s inputs is not built", fn,
                 head_dim, n_rep, in_bf16 ? "bf16" : "fp32");
+  if (kv_fp8 && head_dim != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: fp8 caches are built for head_dim 128 only (got %d)", fn, head_dim);
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(ATTN_ERR_UNSUPPORTED, "%s: q, caches and out must be 16-byte aligned", fn);
   const GqaLayout lay = gqa_layout(B, Hq, Hkv, head_dim, T_max, split_tokens, append);
@@ -248,9 +253,11 @@ attn_status gqa_decode_common(const char* fn, const void* q, const void* k_new, 
     a.big_units = (long long)B * Hkv * lay.n_chunks >= 16LL * cus;
   }
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
-  a.scale_log2e = scale * kLog2e;
+  a.scale_log2e = scale * kLog2e * (kv_fp8 ? kv_scales[0] : 1.f);
   a.in_bf16 = in_bf16;
   a.out_bf16 = out_dtype == ATTN_BF16;
+  a.kv_fp8 = kv_fp8;
+  a.v_scale = kv_fp8 ? kv_scales[1] : 1.f;
   a.append = append;
   a.k_new = k_new;
   a.v_new = v_new;
@@ -269,6 +276,18 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
   return gqa_decode_common("attn_decode_gqa", q, nullptr, nullptr, k_cache, v_cache, cache_lens, out, B, Hq, Hkv,
                            head_dim, T_max, softmax_scale, in_dtype, out_dtype, split_tokens, workspace,
                            workspace_bytes, stream);
+}
+
+attn_status attn_decode_gqa_fp8kv(const void* q, const void* k_cache, const void* v_cache, float k_scale,
+                                  float v_scale, const int32_t* cache_lens, void* out, int B, int Hq, int Hkv,
+                                  int head_dim, int T_max, float softmax_scale, attn_dtype out_dtype, int split_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(ATTN_ERR_SHAPE, "attn_decode_gqa_fp8kv: k_scale and v_scale must be positive and finite");
+  const float scales[2] = {k_scale, v_scale};
+  return gqa_decode_common("attn_decode_gqa_fp8kv", q, nullptr, nullptr, k_cache, v_cache, cache_lens, out, B, Hq, Hkv,
+                           head_dim, T_max, softmax_scale, ATTN_BF16, out_dtype, split_tokens, workspace,
+                           workspace_bytes, stream, scales);
 }
 
 size_t attn_decode_gqa_append_workspace_bytes(int B, int Hq, int Hkv, int head_dim, int T_max, int split_tokens) {

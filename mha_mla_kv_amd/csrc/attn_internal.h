@@ -44,6 +44,10 @@ struct GqaDecodeArgs {
   const void* v_new;      // [B, Hkv, D]
   void* k_cache;          // the k array, written at the new position
   void* v_cache;          // the v array
+  // caches of OCP FP8 E4M3 values (kv_fp8 != 0): value = v_scale * code for V;
+  // the K scale is folded into scale_log2e
+  int kv_fp8;
+  float v_scale;
 };
 
 struct PrefillArgs {

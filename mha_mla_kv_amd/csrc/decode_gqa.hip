@@ -49,6 +49,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -536,16 +538,21 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
 // Waves per SIMD the register allocation targets (the fixed schedule runs
 // several workgroups per compute unit): four fit head_dim 64, head_dim 96 and
 // 128 need up to 168 registers (three waves) with the next tile in flight.
-template <int D, int HB, bool QUEUE>
+// KV8: the caches hold OCP FP8 E4M3 values (one byte each), converted to bf16
+// (exactly) on their way into LDS; the K scale is folded into the softmax
+// scale by the host, the V scale is applied to each unit's output.
+template <int D, int HB, bool QUEUE, bool KV8 = false>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(HB > 1 ? 1 : (D >= 96 ? (QUEUE ? 2 : 3) : 4))))
 void gqa_decode_bf16(GqaDecodeArgs a) {
   static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
+  static_assert(!KV8 || D == 128, "fp8 caches: head_dim 128");
+  constexpr int EB = KV8 ? 1 : 2;      // bytes per cached element
   constexpr int KC = D / 32;           // 32-wide dim chunks (QK contraction)
   constexpr int DW = D / 16;           // 16-wide dim blocks (PV output rows)
   constexpr int VP = D + 16;           // V tile row pitch in elements ([token][dim], padded)
   constexpr int KP = D + 8;            // K tile row pitch (16 rows of one column: distinct LDS banks)
-  constexpr int kUnits = D / 8;                              // 16-byte units per K/V row
+  constexpr int kUnits = D * EB / 16;                        // 16-byte units per K/V row
   constexpr int kLanesPerRow = kUnits <= 8 ? 8 : 16;          // lanes that load one row
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;
   constexpr int kLoads = kDecodeTileTokens / kRowsPerLoad;   // 16-byte loads per lane per tile
@@ -578,13 +585,17 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   float* lse_s = ob + kDecodeWaves * kSliceFloats;  // [HB*16]
   u16* vt = smem + wave * kDecodeTileTokens * VP;
   const size_t tok_stride = (size_t)a.Hkv * D;
-  const int row_bytes = uniform((int)(tok_stride * 2));
+  const int row_bytes = uniform((int)(tok_stride * EB));
   // this lane's row within a load and its 16-byte unit in the row
   const int lrow = lane / kLanesPerRow, lunit = min(lane % kLanesPerRow, kUnits - 1);
   const unsigned row_off = (unsigned)(lrow * row_bytes + 16 * lunit);
 
-  auto k_head = [&](const Unit& u) { return static_cast<const u16*>(a.k) + ((size_t)u.b * a.T_max * a.Hkv + u.g) * D; };
-  auto v_head = [&](const Unit& u) { return static_cast<const u16*>(a.v) + ((size_t)u.b * a.T_max * a.Hkv + u.g) * D; };
+  auto k_head = [&](const Unit& u) {
+    return static_cast<const char*>(a.k) + ((size_t)u.b * a.T_max * a.Hkv + u.g) * D * EB;
+  };
+  auto v_head = [&](const Unit& u) {
+    return static_cast<const char*>(a.v) + ((size_t)u.b * a.T_max * a.Hkv + u.g) * D * EB;
+  };
 
   // K and V tiles of 32 positions are read in row order with streaming
   // (non-temporal) buffer loads: lane group lane / kLanesPerRow of load i
@@ -595,12 +606,12 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   // zeros and cost no memory traffic, so loads ahead can be issued
   // unconditionally.  One resource per tile keeps the scalar work per load to
   // an offset.
-  auto load_rows = [&](bf16x8 (&r)[kLoads], const u16* head0, int t0, int c1) {
+  auto load_rows = [&](bf16x8 (&r)[kLoads], const char* head0, int t0, int c1) {
     // rows of the tile before c1, 0..32; bytes up to the end of the last
-    // (row_bytes >= 2 * D, so no rows gives a non-positive count)
+    // (row_bytes >= EB * D, so no rows gives a non-positive count)
     const int rows = min(max(c1 - t0, 0), kDecodeTileTokens);
-    const int n = max(rows * row_bytes - row_bytes + 2 * D, 0);
-    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(head0 + (size_t)t0 * tok_stride), (short)0, n,
+    const int n = max(rows * row_bytes - row_bytes + EB * D, 0);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(head0 + (size_t)t0 * row_bytes), (short)0, n,
                                                       0x00020000);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
@@ -608,10 +619,29 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
                                             rs, (int)(row_off + (unsigned)(kRowsPerLoad * i * row_bytes)), 0, kStreamPolicy));
   };
   // The same registers written to this wave's LDS tile, row pitch `pitch`.
+  // fp8 rows: each 16-byte unit holds 16 values, widened to two 16-byte bf16 writes.
   auto store_rows = [&](const bf16x8 (&r)[kLoads], int pitch) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-      *reinterpret_cast<u16x8*>(vt + (kRowsPerLoad * i + lrow) * pitch + 8 * lunit) = __builtin_bit_cast(u16x8, r[i]);
+    for (int i = 0; i < kLoads; ++i) {
+      u16* dst = vt + (kRowsPerLoad * i + lrow) * pitch + (16 / EB) * lunit;
+      if constexpr (KV8) {
+        // each conversion widens the codes of one 16-bit half of a word into a
+        // pair of bf16 (one 32-bit word); the pairs are moved as whole words
+        // (extracting the two bf16 of a pair separately was miscompiled into a
+        // copy of the first one)
+        const u32x4 wd = __builtin_bit_cast(u32x4, r[i]);
+        u32x4 h[2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          h[q >> 1][2 * (q & 1)] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[q], 1.f, false));
+          h[q >> 1][2 * (q & 1) + 1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[q], 1.f, true));
+        }
+        *reinterpret_cast<u32x4*>(dst) = h[0];
+        *reinterpret_cast<u32x4*>(dst + 8) = h[1];
+      } else {
+        *reinterpret_cast<u16x8*>(dst) = __builtin_bit_cast(u16x8, r[i]);
+      }
+    }
   };
 
   // Registers that carry a unit's inputs: Q^T as the B operand (lane holds
@@ -640,8 +670,8 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   float m[HB], lsum[HB];
   f32x4 o[HB][DW];  // O^T: lane holds dims 16w + 4grp + i of head 16hb + row
   auto stream_unit = [&](const Unit& u, NextUnit& nx) {
-    const u16* kp = k_head(u);
-    const u16* vp = v_head(u);
+    const char* kp = k_head(u);
+    const char* vp = v_head(u);
     const int c1 = u.t1;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
@@ -773,7 +803,7 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
       float Lt = 0.f;
 #pragma unroll
       for (int w = 0; w < kDecodeWaves; ++w) Lt += rescale(mw[w * HB * 16 + hd], M) * lw[w * HB * 16 + hd];
-      const float f = rescale(m[hb], M) / Lt;
+      const float f = rescale(m[hb], M) / Lt * (KV8 ? a.v_scale : 1.f);
 #pragma unroll
       for (int w = 0; w < DW; ++w) o[hb][w] *= f;
       if (wave == 0 && grp == 0) lse_s[hd] = M + __log2f(Lt);
@@ -994,12 +1024,12 @@ hipError_t launch_one(Kernel kernel, const GqaDecodeArgs& a, dim3 grid, hipStrea
 // their units longest).
 constexpr int kMfmaWgsPerCu = 1;
 
-template <int D, bool QUEUE>
+template <int D, bool QUEUE, bool KV8 = false>
 hipError_t launch_bf16(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
   const int hb = (a.n_rep + 15) / 16;
-  if (hb == 1) return launch_one(gqa_decode_bf16<D, 1, QUEUE>, a, grid, st, kMfmaWgsPerCu);
-  if (hb == 2) return launch_one(gqa_decode_bf16<D, 2, QUEUE>, a, grid, st, kMfmaWgsPerCu);
-  if (hb <= 4) return launch_one(gqa_decode_bf16<D, 4, QUEUE>, a, grid, st, kMfmaWgsPerCu);
+  if (hb == 1) return launch_one(gqa_decode_bf16<D, 1, QUEUE, KV8>, a, grid, st, kMfmaWgsPerCu);
+  if (hb == 2) return launch_one(gqa_decode_bf16<D, 2, QUEUE, KV8>, a, grid, st, kMfmaWgsPerCu);
+  if (hb <= 4) return launch_one(gqa_decode_bf16<D, 4, QUEUE, KV8>, a, grid, st, kMfmaWgsPerCu);
   return hipErrorInvalidValue;
 }
 
@@ -1016,6 +1046,7 @@ hipError_t launch_f32(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
 
 template <bool QUEUE>
 hipError_t launch_mode(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
+  if (a.kv_fp8) return a.D == 128 ? launch_bf16<128, QUEUE, true>(a, grid, st) : hipErrorInvalidValue;
   if (a.in_bf16)
     return a.D == 64 ? launch_bf16<64, QUEUE>(a, grid, st) : a.D == 96 ? launch_bf16<96, QUEUE>(a, grid, st)
                                                                         : launch_bf16<128, QUEUE>(a, grid, st);
@@ -1043,7 +1074,7 @@ hipError_t launch_gqa_decode(const GqaDecodeArgs& a, hipStream_t st) {
     // in memory, one row of Hkv*D per position) are dispatched together.
     e = launch_mode<false>(a, dim3(a.Hkv, a.n_chunks, a.B), st);
   }
-  if (e != hipSuccess || a.n_chunks < 2) return e;
+  if (e != hipSuccess || (a.n_chunks < 2 && !a.append)) return e;
   const int n_eb = (a.n_rep * (a.D / 2) + kMergePairs - 1) / kMergePairs;
   hipLaunchKernelGGL(gqa_decode_merge, dim3(a.Hkv * n_eb, a.B), dim3(kMergePairs), 0, st, a);
   return hipGetLastError();

@@ -24,7 +24,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     names = attn.header_functions()
     for required in ("attn_decode_gqa", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached",
                      "attn_decode_mla_absorbed", "attn_prefill_mla_causal", "attn_cache_append",
-                     "attn_decode_gqa_append"):
+                     "attn_decode_gqa_append", "attn_decode_gqa_fp8kv"):
         assert required in names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/attn_mi355x.h but not exported"
@@ -112,6 +112,19 @@ def test_decode_append_validation():
     # a single chunk per sequence still needs partial slots in the fused step
     plain = attn.attn_decode_gqa_workspace_bytes(2, 8, 2, 128, 64, 0)
     assert plain == 256 and attn.attn_decode_gqa_append_workspace_bytes(2, 8, 2, 128, 64, 0) > plain
+
+
+@no_gpu_only
+def test_fp8_decode_validation():
+    lib = attn.lib()
+
+    def f(**kw):
+        return lib.attn_decode_gqa_fp8kv(FAKE, FAKE, FAKE, kw.get("ks", 0.01), kw.get("vs", 0.01), FAKE, FAKE, 2, 8, 2,
+                                         kw.get("D", 128), 64, 0.0, F32, 0, FAKE, 1 << 30, None)
+    assert f(ks=0.0) == SHAPE
+    assert f(vs=float("inf")) == SHAPE
+    assert f(vs=float("nan")) == SHAPE
+    assert f(D=64) == UNSUP
 
 
 @no_gpu_only

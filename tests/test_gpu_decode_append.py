@@ -49,6 +49,7 @@ CASES = [
     ("mha", 2, 8, 8, 128, 900, [899, 100], "bf16", 64),
     ("d64", 3, 16, 4, 64, 700, [0, 333, 700], "bf16", 0),
     ("d96_fp32", 2, 8, 4, 96, 512, [511, 40], "f32", 0),
+    ("single_chunk_split", 3, 8, 2, 128, 200, [200, 0, 57], "bf16", 256),  # one chunk: merge still runs
 ]
 
 
