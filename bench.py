@@ -19,6 +19,8 @@ One step = one pass over the three C-ABI entry points, each on its own synthetic
                               it already holds, so the decode inputs do not change)
   * attn_decode_gqa_append    the same write and the decode in one call (cache_lens - 1 cached
                               rows plus the new one: the same attention as attn_decode_gqa)
+  * attn_decode_gqa_fp8kv     the Llama-3 decode shape and lengths over FP8 E4M3 caches (one
+                              byte per element, one scale per cache)
 
 The printed `value` is the GQA decode's KV-cache read rate (algorithmic bytes: every cached
 K and V row read once per KV head, 2*Hkv*head_dim*2 bytes per cached position) divided by
@@ -123,6 +125,12 @@ def main():
     app_bytes = 2 * 2 * B * Hkv * D * 2                       # K and V rows, read once and written once
     app_new_k, app_new_v = app_k[:, 0].contiguous(), app_v[:, 0].contiguous()  # [B, Hkv, D]
     step_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(8)
+    f8_scale = 4.5 / 448.0
+    f8_k = (torch.randn(B, T_max, Hkv, D, device=dev, generator=gen) / f8_scale).to(torch.float8_e4m3fn)
+    f8_v = (torch.randn(B, T_max, Hkv, D, device=dev, generator=gen) / f8_scale).to(torch.float8_e4m3fn)
+    f8_bytes = dec_bytes // 2                                 # one byte per cached element
+    f8_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     step_ws = torch.zeros(attn.attn_decode_gqa_append_workspace_bytes(B, Hq, Hkv, D, T_max, 0), dtype=torch.uint8,
                           device=dev)
 
@@ -193,6 +201,10 @@ def main():
         attn.attn_decode_gqa_append(dec["q"], app_new_k, app_new_v, dec["k"], dec["v"], app_pos, out=step_out,
                                     workspace=step_ws)
 
+    def run_fp8():
+        attn.attn_decode_gqa_fp8kv(dec["q"], f8_k, f8_v, f8_scale, f8_scale, dec["cache_lens"], out=f8_out,
+                                   workspace=dec_ws)
+
     def run_mla_prefill():
         attn.attn_prefill_mla_causal(mlp["q_nope"], mlp["q_rope"], mlp["w_uk"], mlp["w_uv"], mlp["c_kv"], mlp["k_rope"],
                                      out=mlp_out)
@@ -204,7 +216,7 @@ def main():
     # step takes); each part is timed on its own
     parts = [("prefill", run_prefill), ("chunked_prefill", run_chunked), ("mla_prefill", run_mla_prefill),
              ("mla_decode", run_mla), ("kv_append", run_append), ("gqa_decode", run_decode),
-             ("gqa_decode_step", run_step)]
+             ("gqa_decode_step", run_step), ("gqa_decode_fp8", run_fp8)]
     if args.copy_calibration:
         parts.append(("copy_1GiB", lambda: copy_dst.copy_(copy_src)))
 
@@ -255,8 +267,8 @@ def main():
                          f"cache_lens~U[{dspec['lens'][0]},{dspec['lens'][1]}] (sum {sum_len}) seed={dspec['seed']}, "
                          "bf16 in, fp32 out, default schedule (device-wide unit queue, library-chosen blocks)"),
             "step": ("attn_prefill_gqa_causal, attn_prefill_gqa_cached, attn_prefill_mla_causal, "
-                     "attn_decode_mla_absorbed, attn_cache_append, attn_decode_gqa, attn_decode_gqa_append: one "
-                     "call each, in this order"),
+                     "attn_decode_mla_absorbed, attn_cache_append, attn_decode_gqa, attn_decode_gqa_append, "
+                     "attn_decode_gqa_fp8kv: one call each, in this order"),
             "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "prefill": PB * S, "chunked_prefill": chk_tokens,
                                 "mla_prefill": MPB * MPS},
         },
@@ -296,6 +308,13 @@ def main():
                                 "workload": f"llama3_8b_gqa_chunked_prefill: B={CB} chunk={CS} "
                                             f"start_pos={cspec['start_pos']} T_max={CT} Hq={CHq} "
                                             f"Hkv={chk['k'].shape[2]} head_dim={CD} seed={cspec['seed']} bf16"},
+            "gqa_decode_fp8": {"ms": round(ms["gqa_decode_fp8"], 5),
+                               "GB/s": round(f8_bytes / (ms["gqa_decode_fp8"] * 1e-3) / 1e9, 1),
+                               "hbm_frac": round(f8_bytes / (ms["gqa_decode_fp8"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                               "algorithmic_bytes_per_launch": f8_bytes,
+                               "tokens_per_s": round(B / (ms["gqa_decode_fp8"] * 1e-3), 1),
+                               "workload": "llama3_8b_gqa_decode shape and lengths, K/V as FP8 E4M3 codes of "
+                                           "N(0,1)/scale (device-generated, seed 8), scale 4.5/448"},
             "gqa_decode_step": {"ms": round(ms["gqa_decode_step"], 5),
                                 "GB/s": round(dec_bytes / (ms["gqa_decode_step"] * 1e-3) / 1e9, 1),
                                 "workload": "llama3_8b_gqa_decode with the newest rows as the new token "
