@@ -247,7 +247,7 @@ def main():
     mlp_tfs = mlp_flops / (ms["mla_prefill"] * 1e-3) / 1e12
 
     dec_hash = source_hash("decode_gqa.hip", "attn_internal.h")
-    traffic = measured_traffic("gqa_decode_bf16<128, 1, true>", dec_hash)
+    traffic = measured_traffic("gqa_decode_bf16<128, 1, true, false>", dec_hash)
 
     result = {
         "metric": METRIC,
@@ -274,7 +274,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("gqa_decode_bf16<128, 1, true> + gqa_decode_merge: one attn_decode_gqa call "
+            "kernel": ("gqa_decode_bf16<128, 1, true, false> + gqa_decode_merge: one attn_decode_gqa call "
                        "(two launches), timed together"),
             "achieved": round(dec_gbs, 1),
             "peak": HBM_PEAK_GBS,
