@@ -1,8 +1,9 @@
 /*
  * attn_mi355x.h -- C ABI of a small attention library for AMD Instinct MI355X
- * (gfx950 / CDNA4): grouped-query attention over a KV cache (decode and causal
- * prefill, also after a cached prefix) and multi-head latent attention (MLA)
- * decode and causal prefill over a latent cache.
+ * (gfx950 / CDNA4): grouped-query attention over a KV cache (decode, also over
+ * FP8 caches and fused with the new token's cache write; causal prefill, also
+ * after a cached prefix), multi-head latent attention (MLA) decode and causal
+ * prefill over a latent cache, and the cache write itself.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
