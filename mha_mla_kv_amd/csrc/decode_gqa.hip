@@ -481,15 +481,27 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
     if (a.append) {
       const size_t kv = ((size_t)b * a.Hkv + g) * a.D;
       const size_t qr = (row0 + hd) * a.D;
+      // head_dim 64 and 128: the D/2 threads of a head are consecutive lanes of
+      // one wave (blocks of 256 threads start at a head), so each multiplies its
+      // own pair and the wave sums them; other widths loop over the whole row
+      const bool lanes_sum = D2 == 32 || D2 == 64;
       float dot = 0.f, vx, vy;
       if (a.in_bf16) {
         const u16* qp = static_cast<const u16*>(a.q) + qr;
         const u16* kp = static_cast<const u16*>(a.k_new) + kv;
-        for (int d = 0; d < a.D; d += 8) {
-          const u16x8 qa = *reinterpret_cast<const u16x8*>(qp + d);
-          const u16x8 ka = *reinterpret_cast<const u16x8*>(kp + d);
+        if (lanes_sum) {
+          const unsigned qw = *reinterpret_cast<const unsigned*>(qp + 2 * d2);
+          const unsigned kw = *reinterpret_cast<const unsigned*>(kp + 2 * d2);
+          dot = fmaf(bf16_to_f32((u16)(qw & 0xffffu)), bf16_to_f32((u16)(kw & 0xffffu)),
+                     bf16_to_f32((u16)(qw >> 16)) * bf16_to_f32((u16)(kw >> 16)));
+          for (int off = D2 / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
+        } else {
+          for (int d = 0; d < a.D; d += 8) {
+            const u16x8 qa = *reinterpret_cast<const u16x8*>(qp + d);
+            const u16x8 ka = *reinterpret_cast<const u16x8*>(kp + d);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) dot = fmaf(bf16_to_f32(qa[i]), bf16_to_f32(ka[i]), dot);
+            for (int i = 0; i < 8; ++i) dot = fmaf(bf16_to_f32(qa[i]), bf16_to_f32(ka[i]), dot);
+          }
         }
         const unsigned vw = *reinterpret_cast<const unsigned*>(static_cast<const u16*>(a.v_new) + kv + 2 * d2);
         vx = bf16_to_f32((u16)(vw & 0xffffu));
@@ -503,13 +515,20 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
       } else {
         const float* qp = static_cast<const float*>(a.q) + qr;
         const float* kp = static_cast<const float*>(a.k_new) + kv;
-        for (int d = 0; d < a.D; d += 4) {
-          const float4 qa = *reinterpret_cast<const float4*>(qp + d);
-          const float4 ka = *reinterpret_cast<const float4*>(kp + d);
-          dot = fmaf(qa.x, ka.x, dot);
-          dot = fmaf(qa.y, ka.y, dot);
-          dot = fmaf(qa.z, ka.z, dot);
-          dot = fmaf(qa.w, ka.w, dot);
+        if (lanes_sum) {
+          const float2 qa = *reinterpret_cast<const float2*>(qp + 2 * d2);
+          const float2 ka = *reinterpret_cast<const float2*>(kp + 2 * d2);
+          dot = fmaf(qa.x, ka.x, qa.y * ka.y);
+          for (int off = D2 / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
+        } else {
+          for (int d = 0; d < a.D; d += 4) {
+            const float4 qa = *reinterpret_cast<const float4*>(qp + d);
+            const float4 ka = *reinterpret_cast<const float4*>(kp + d);
+            dot = fmaf(qa.x, ka.x, dot);
+            dot = fmaf(qa.y, ka.y, dot);
+            dot = fmaf(qa.z, ka.z, dot);
+            dot = fmaf(qa.w, ka.w, dot);
+          }
         }
         const float2 vv = *reinterpret_cast<const float2*>(static_cast<const float*>(a.v_new) + kv + 2 * d2);
         vx = vv.x;
