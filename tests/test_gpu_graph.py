@@ -98,3 +98,27 @@ def test_mla_prefill_graph_replay():
                                                                       inp["q_lens"], out=out), out)
     assert torch.isfinite(eager.float()).all()
     assert not eager[1, 77:].any()
+
+
+def test_decode_step_and_fp8_decode_graph_replay():
+    """The decode step with the new token (its cache write repeats the same bytes on every replay)
+    and the decode over FP8 caches, captured and replayed."""
+    import mha_mla_kv_amd as attn
+    B, Hq, Hkv, D, T = 4, 32, 8, 128, 2000
+    inp = {k: v.cuda() for k, v in synth.gqa_decode_inputs(B, Hq, Hkv, D, T, [1999, 0, 700, 64], seed=12).items()}
+    g = torch.Generator().manual_seed(12)
+    k_new, v_new = (torch.randn(B, Hkv, D, generator=g).to(torch.bfloat16).cuda() for _ in range(2))
+    print(f"[case] decode step graph B={B} Hq={Hq} Hkv={Hkv} T={T}", flush=True)
+    ws = torch.zeros(attn.attn_decode_gqa_append_workspace_bytes(B, Hq, Hkv, D, T, 0), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hq, D, device="cuda")
+    eager = _graph_matches_eager(lambda: attn.attn_decode_gqa_append(inp["q"], k_new, v_new, inp["k"], inp["v"],
+                                                                     inp["cache_lens"], out=out, workspace=ws), out)
+    assert torch.isfinite(eager).all()
+    f8 = synth.gqa_decode_fp8_inputs(B, Hq, Hkv, D, T, [1999, 0, 700, 64], seed=13)
+    fk, fv, fl, fq = f8["k"].cuda(), f8["v"].cuda(), f8["cache_lens"].cuda(), f8["q"].cuda()
+    print("[case] fp8 decode graph", flush=True)
+    ws8 = torch.zeros(attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T, 0), dtype=torch.uint8, device="cuda")
+    out8 = torch.empty(B, Hq, D, device="cuda")
+    eager8 = _graph_matches_eager(lambda: attn.attn_decode_gqa_fp8kv(fq, fk, fv, f8["k_scale"], f8["v_scale"], fl,
+                                                                     out=out8, workspace=ws8), out8)
+    assert torch.isfinite(eager8).all()
