@@ -40,6 +40,7 @@ CASES = [
     ("h1", 2, 100, 1, 300, [37, 150], [100, 100]),
     ("empty_chunk", 2, 90, 8, 300, [10, 40], [0, 90]),
     ("prefix_fills_cache", 2, 64, 8, 256, [256, 250], [64, 64]),
+    ("b8_xcd_mapping", 8, 140, 8, 400, [0, 13, 64, 100, 0, 255, 7, 1], [140, 140, 99, 140, 1, 140, 64, 128]),
 ]
 
 
