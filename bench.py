@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-One step = one pass over the three C-ABI entry points, each on its own synthetic workload
+One step = one pass over the C-ABI compute entry points, each on its own synthetic workload
 (shapes from the pages' configurations, i.i.d. N(0,1) inputs from fixed seeds):
 
   * attn_decode_gqa           Llama-3-8B-shaped GQA decode: B 32, Hq 32, Hkv 8, head_dim 128,
