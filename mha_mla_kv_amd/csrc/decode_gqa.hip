@@ -1042,15 +1042,11 @@ hipError_t launch_one(Kernel kernel, const GqaDecodeArgs& a, dim3 grid, hipStrea
 // hardware favours older waves, so extra workgroups stream far slower and hold
 // their units longest).
 constexpr int kMfmaWgsPerCu = 1;
-// With fp8 caches a tile carries half the bytes, so one workgroup per compute
-// unit keeps too little in flight: two are faster (Llama-3 decode shape: 55 vs
-// 58 us).
-constexpr int kFp8WgsPerCu = 2;
 
 template <int D, bool QUEUE, bool KV8 = false>
 hipError_t launch_bf16(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
   const int hb = (a.n_rep + 15) / 16;
-  if (hb == 1) return launch_one(gqa_decode_bf16<D, 1, QUEUE, KV8>, a, grid, st, KV8 ? kFp8WgsPerCu : kMfmaWgsPerCu);
+  if (hb == 1) return launch_one(gqa_decode_bf16<D, 1, QUEUE, KV8>, a, grid, st, kMfmaWgsPerCu);
   if (hb == 2) return launch_one(gqa_decode_bf16<D, 2, QUEUE, KV8>, a, grid, st, kMfmaWgsPerCu);
   if (hb <= 4) return launch_one(gqa_decode_bf16<D, 4, QUEUE, KV8>, a, grid, st, kMfmaWgsPerCu);
   return hipErrorInvalidValue;
