@@ -4,31 +4,40 @@
 One step = one pass over the C-ABI compute entry points, each on its own synthetic workload
 (shapes from the pages' configurations, i.i.d. N(0,1) inputs from fixed seeds):
 
-  * attn_decode_gqa           Llama-3-8B-shaped GQA decode: B 32, Hq 32, Hkv 8, head_dim 128,
-                              cache lengths uniform in [1024, 8192] (T_max 8192), bf16 in, fp32 out
-  * attn_decode_mla_absorbed  MiniMind-768 MLA decode: B 64, 8 heads, nope 96, rope 48, v 96,
-                              kv_lora_rank 128, cache 4096, bf16
   * attn_prefill_gqa_causal   Llama-3-8B-shaped causal prefill: B 4, S 4096, Hq 32, Hkv 8,
                               head_dim 128, bf16 in / out
   * attn_prefill_gqa_cached   the same heads, a 512-token chunk after a 3584-token cached
                               prefix in each of 4 sequences (chunked prefill), bf16 in / out
   * attn_prefill_mla_causal   MiniMind-768 MLA causal prefill: B 4, S 4096, 8 heads, nope 96,
                               rope 48, v 96, kv_lora_rank 128, bf16 in / out
+  * attn_decode_mla_absorbed  MiniMind-768 MLA decode: B 64, 8 heads, nope 96, rope 48, v 96,
+                              kv_lora_rank 128, cache 4096, bf16 (six cache copies used in turn)
   * attn_cache_append         the decode step's K/V write: each of the 32 Llama-3 sequences'
                               newest K and V rows written at position cache_lens - 1 (the rows
                               it already holds, so the decode inputs do not change)
+  * attn_decode_gqa           Llama-3-8B-shaped GQA decode: B 32, Hq 32, Hkv 8, head_dim 128,
+                              cache lengths uniform in [1024, 8192] (T_max 8192), bf16 in, fp32 out
   * attn_decode_gqa_append    the same write and the decode in one call (cache_lens - 1 cached
                               rows plus the new one: the same attention as attn_decode_gqa)
   * attn_decode_gqa_fp8kv     the Llama-3 decode shape and lengths over FP8 E4M3 caches (one
                               byte per element, one scale per cache)
+  * attn_decode_gqa           KV-group sweep: Hq 32, head_dim 128, B 16, cache 8192, bf16, with
+                              Hkv 32 (MHA), 8 (GQA-8) and 1 (MQA); 1, 2 and 8 cache copies used in
+                              turn, so each setting's copies total at least 1 GiB
+  * attn_decode_gqa           MiniMind-768 GQA decode: Hq 8, Hkv 4, head_dim 96, B 1, cache 512,
+                              fp32 in / out (1.5 MiB of K/V: latency-bound by size)
 
-The printed `value` is the GQA decode's KV-cache read rate (algorithmic bytes: every cached
-K and V row read once per KV head, 2*Hkv*head_dim*2 bytes per cached position) divided by
-the time of one attn_decode_gqa call (its streaming kernel and the small kernel that merges
+Cache copies used in turn keep every decode part reading from HBM rather than from the
+256 MB Infinity Cache when a part is timed on its own; inside a step the other parts'
+traffic (several GB) separates two calls of one part in any case.
+
+The printed `value` is the Llama-3 GQA decode's KV-cache read rate (algorithmic bytes: every
+cached K and V row read once per KV head, 2*Hkv*head_dim*2 bytes per cached position) divided
+by the time of one attn_decode_gqa call (its streaming kernel and the small kernel that merges
 the partial results), measured with HIP events around the call on the stream the library
-launches on.  The other two entry points are reported under "parts".  Inputs are resident in
-HBM before the timed region.  `cpu_baseline` times the fp64 CPU oracle (tests' checker, not
-tuned) on the same decode workload on this host.
+launches on.  Every other part is reported under "parts" with its own algorithmic unit.
+Inputs are resident in HBM before the timed region.  `cpu_baseline` times the fp64 CPU oracle
+(the tests' checker, not tuned) on a bounded sample of each configuration on this host.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -47,6 +56,9 @@ sys.path.insert(0, ROOT)
 METRIC = "GQA/MLA decode KV-cache GB/s (% HBM peak) + causal prefill TFLOP/s, 1 MI355X"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published (no sparsity)
+# dense bf16 MFMA flop per compute unit and clock on CDNA4: 4 matrix cores of 1024 flop/clock
+# each (twice CDNA3's rate); times the device's compute units and peak engine clock
+BF16_FLOP_PER_CU_CLK = 4096
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gqa_decode_llama3_traffic.txt")
 
 
@@ -56,9 +68,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU oracle time")
+    ap.add_argument("--cpu-seconds", type=float, default=3.0, help="target CPU oracle time per configuration")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy per step (for counter calibration)")
+    ap.add_argument("--parts", default="", help="comma-separated subset of parts to run (default: all)")
     return ap.parse_args()
 
 
@@ -84,6 +97,22 @@ def measured_traffic(kernel: str, src_hash: str):
     return e.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def gqa_decode_bytes(Hkv, D, elem_bytes, sum_len):
+    """Algorithmic K/V bytes of a decode: every cached K and V row read once per KV head."""
+    return 2 * Hkv * D * elem_bytes * sum_len
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -104,16 +133,26 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     attn.lib()  # fail loudly now if the library is missing
+    props = torch.cuda.get_device_properties(dev)
+    want = set(p for p in args.parts.split(",") if p)
 
     t_gen = time.time()
-    # ---- workloads (generated on the host from fixed seeds, then moved to HBM) ----
+    gen = torch.Generator(device=dev).manual_seed(8)
+
+    def dev_normal(shape, dtype=torch.bfloat16, scale=1.0):
+        x = torch.randn(*shape, device=dev, generator=gen)
+        if scale != 1.0:
+            x *= scale
+        return x.to(dtype)
+
+    # ---- Llama-3-8B GQA decode (the headline), its append / fused step, FP8 caches ----
     dspec = synth.WORKLOADS["llama3_8b_gqa_decode"]
     dec_cpu = synth.make("llama3_8b_gqa_decode")
     dec = {k: v.to(dev) for k, v in dec_cpu.items()}
     B, Hq, D = dec["q"].shape
     T_max, Hkv = dec["k"].shape[1], dec["k"].shape[2]
     sum_len = int(dec_cpu["cache_lens"].clamp(0, T_max).sum())
-    dec_bytes = 2 * Hkv * D * 2 * sum_len                      # K and V rows, bf16, once per KV head
+    dec_bytes = gqa_decode_bytes(Hkv, D, 2, sum_len)
     dec_flops = 4 * Hq * D * sum_len                           # QK^T and PV
     dec_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     dec_ws = torch.zeros(attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T_max, 0), dtype=torch.uint8,
@@ -125,7 +164,6 @@ def main():
     app_bytes = 2 * 2 * B * Hkv * D * 2                       # K and V rows, read once and written once
     app_new_k, app_new_v = app_k[:, 0].contiguous(), app_v[:, 0].contiguous()  # [B, Hkv, D]
     step_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
-    gen = torch.Generator(device=dev).manual_seed(8)
     f8_scale = 4.5 / 448.0
     f8_k = (torch.randn(B, T_max, Hkv, D, device=dev, generator=gen) / f8_scale).to(torch.float8_e4m3fn)
     f8_v = (torch.randn(B, T_max, Hkv, D, device=dev, generator=gen) / f8_scale).to(torch.float8_e4m3fn)
@@ -134,6 +172,39 @@ def main():
     step_ws = torch.zeros(attn.attn_decode_gqa_append_workspace_bytes(B, Hq, Hkv, D, T_max, 0), dtype=torch.uint8,
                           device=dev)
 
+    # ---- KV-group sweep (MHA / GQA-8 / MQA): caches drawn on the device, copies used in turn ----
+    sweep = {}
+    for name, copies in (("kv_sweep_mha", 1), ("kv_sweep_gqa8", 2), ("kv_sweep_mqa", 8)):
+        if want and name not in want:
+            continue
+        sp = synth.WORKLOADS[name]
+        SB, SHq, SHkv, SD, ST = sp["B"], sp["Hq"], sp["Hkv"], sp["D"], sp["T_max"]
+        lens = torch.full((SB,), sp["lens"], dtype=torch.int32, device=dev)
+        kv = [(dev_normal((SB, ST, SHkv, SD)), dev_normal((SB, ST, SHkv, SD))) for _ in range(copies)]
+        sweep[name] = {
+            "q": dev_normal((SB, SHq, SD)), "kv": kv, "lens": lens,
+            "out": torch.empty(SB, SHq, SD, dtype=torch.float32, device=dev),
+            "ws": torch.zeros(attn.attn_decode_gqa_workspace_bytes(SB, SHq, SHkv, SD, ST, 0), dtype=torch.uint8,
+                              device=dev),
+            "bytes": gqa_decode_bytes(SHkv, SD, 2, SB * sp["lens"]), "flops": 4 * SHq * SD * SB * sp["lens"],
+            "tokens": SB, "copies": copies,
+            "workload": f"{name}: B={SB} Hq={SHq} Hkv={SHkv} head_dim={SD} cache={sp['lens']} bf16 in, fp32 out; "
+                        f"N(0,1) caches drawn on the device (seed 8), {copies} cache cop{'y' if copies == 1 else 'ies'} "
+                        "used in turn",
+        }
+
+    # ---- MiniMind-768 GQA decode, fp32 ----
+    mm_cpu = synth.make("minimind768_gqa_decode")
+    mm = {k: v.to(dev) for k, v in mm_cpu.items()}
+    MMB, MMHq, MMD = mm["q"].shape
+    MMT, MMHkv = mm["k"].shape[1], mm["k"].shape[2]
+    mm_len = int(mm_cpu["cache_lens"].clamp(0, MMT).sum())
+    mm_bytes = gqa_decode_bytes(MMHkv, MMD, 4, mm_len)
+    mm_out = torch.empty(MMB, MMHq, MMD, dtype=torch.float32, device=dev)
+    mm_ws = torch.zeros(attn.attn_decode_gqa_workspace_bytes(MMB, MMHq, MMHkv, MMD, MMT, 0), dtype=torch.uint8,
+                        device=dev)
+
+    # ---- MiniMind-768 MLA decode: the seeded workload plus five device-drawn cache copies ----
     mspec = synth.WORKLOADS["minimind768_mla_decode"]
     mla_cpu = synth.make("minimind768_mla_decode")
     mla = {k: v.to(dev) for k, v in mla_cpu.items()}
@@ -141,12 +212,15 @@ def main():
     dR = mla["q_rope"].shape[2]
     dv, r = mla["w_uv"].shape[1], mla["w_uv"].shape[2]
     MT = mla["c_kv"].shape[1]
+    mla_copies = [(mla["c_kv"], mla["k_rope"])] + [(dev_normal((MB, MT, r)), dev_normal((MB, MT, dR)))
+                                                   for _ in range(5)]
     mla_len = int(mla_cpu["cache_lens"].clamp(0, MT).sum())
     mla_bytes = (r + dR) * 2 * mla_len                          # one [c_kv, k_rope] row per position
     mla_flops = H * (2 * (r + dR) + 2 * r) * mla_len
     mla_out = torch.empty(MB, H, dv, dtype=torch.float32, device=dev)
     mla_ws = torch.zeros(attn.attn_decode_mla_workspace_bytes(MB, H, r, dR, MT, 0), dtype=torch.uint8, device=dev)
 
+    # ---- prefills ----
     pspec = synth.WORKLOADS["llama3_8b_gqa_prefill"]
     pre = {k: v.to(dev) for k, v in synth.make("llama3_8b_gqa_prefill").items()}
     PB, S, PHq, PD = pre["q"].shape
@@ -170,10 +244,12 @@ def main():
     MPB, MPS, MPH, MPdn = mlp["q_nope"].shape
     MPdR = mlp["q_rope"].shape[3]
     MPdv, MPr = mlp["w_uv"].shape[1], mlp["w_uv"].shape[2]
+    mlp_pairs = MPB * MPH * MPS * (MPS + 1) // 2
     # MFMA work of the absorbed form: 2(r + dR) + 2r per unmasked (query, key) pair and head, plus
     # the query absorption (2 dn r) and the value up-projection (2 dv r) per new token and head
-    mlp_flops = (MPB * MPH * MPS * (MPS + 1) // 2 * (2 * (MPr + MPdR) + 2 * MPr)
-                 + MPB * MPS * MPH * 2 * MPr * (MPdn + MPdv))
+    mlp_flops = mlp_pairs * (2 * (MPr + MPdR) + 2 * MPr) + MPB * MPS * MPH * 2 * MPr * (MPdn + MPdv)
+    # the listing's decompressed SDPA: 2 (dn + dR) + 2 dv per pair and head (K and V rebuilt first)
+    mlp_flops_sdpa = mlp_pairs * (2 * (MPdn + MPdR) + 2 * MPdv)
     mlp_out = torch.empty(MPB, MPS, MPH, MPdv, dtype=torch.bfloat16, device=dev)
     copy_src = copy_dst = None
     if args.copy_calibration:
@@ -184,45 +260,61 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
 
-    def run_decode():
+    def run_decode(i):
         attn.attn_decode_gqa(dec["q"], dec["k"], dec["v"], dec["cache_lens"], out=dec_out, workspace=dec_ws)
 
-    def run_mla():
-        attn.attn_decode_mla_absorbed(mla["q_nope"], mla["q_rope"], mla["w_uk"], mla["w_uv"], mla["c_kv"],
-                                      mla["k_rope"], mla["cache_lens"], out=mla_out, workspace=mla_ws)
+    def run_mla(i):
+        c, kr = mla_copies[i % len(mla_copies)]
+        attn.attn_decode_mla_absorbed(mla["q_nope"], mla["q_rope"], mla["w_uk"], mla["w_uv"], c, kr,
+                                      mla["cache_lens"], out=mla_out, workspace=mla_ws)
 
-    def run_prefill():
+    def run_prefill(i):
         attn.attn_prefill_gqa_causal(pre["q"], pre["k"], pre["v"], out=pre_out)
 
-    def run_append():
+    def run_append(i):
         attn.attn_cache_append(app_k, dec["k"], app_v, dec["v"], app_pos)
 
-    def run_step():
+    def run_step(i):
         attn.attn_decode_gqa_append(dec["q"], app_new_k, app_new_v, dec["k"], dec["v"], app_pos, out=step_out,
                                     workspace=step_ws)
 
-    def run_fp8():
+    def run_fp8(i):
         attn.attn_decode_gqa_fp8kv(dec["q"], f8_k, f8_v, f8_scale, f8_scale, dec["cache_lens"], out=f8_out,
                                    workspace=dec_ws)
 
-    def run_mla_prefill():
+    def run_mla_prefill(i):
         attn.attn_prefill_mla_causal(mlp["q_nope"], mlp["q_rope"], mlp["w_uk"], mlp["w_uv"], mlp["c_kv"], mlp["k_rope"],
                                      out=mlp_out)
 
-    def run_chunked():
+    def run_chunked(i):
         attn.attn_prefill_gqa_cached(chk["q"], chk["k"], chk["v"], chk["start_pos"], chk["q_lens"], out=chk_out)
 
+    def run_sweep(name):
+        w = sweep[name]
+
+        def fn(i):
+            k, v = w["kv"][i % w["copies"]]
+            attn.attn_decode_gqa(w["q"], k, v, w["lens"], out=w["out"], workspace=w["ws"])
+        return fn
+
+    def run_minimind(i):
+        attn.attn_decode_gqa(mm["q"], mm["k"], mm["v"], mm["cache_lens"], out=mm_out, workspace=mm_ws)
+
     # prefill for new requests, then the decode steps of running ones (the order a serving
-    # step takes); each part is timed on its own
+    # step takes), then the sweep settings; each part is timed on its own
     parts = [("prefill", run_prefill), ("chunked_prefill", run_chunked), ("mla_prefill", run_mla_prefill),
              ("mla_decode", run_mla), ("kv_append", run_append), ("gqa_decode", run_decode),
              ("gqa_decode_step", run_step), ("gqa_decode_fp8", run_fp8)]
+    parts += [(name, run_sweep(name)) for name in sweep]
+    parts.append(("minimind768_gqa_decode", run_minimind))
+    if want:
+        parts = [p for p in parts if p[0] in want or p[0] == "gqa_decode"]
     if args.copy_calibration:
-        parts.append(("copy_1GiB", lambda: copy_dst.copy_(copy_src)))
+        parts.append(("copy_1GiB", lambda i: copy_dst.copy_(copy_src)))
 
-    for _ in range(args.warmup):
+    for i in range(args.warmup):
         for _, fn in parts:
-            fn()
+            fn(i)
     torch.cuda.synchronize()
 
     K = args.steps
@@ -234,20 +326,22 @@ def main():
         for name, fn in parts:
             e0, e1 = ev[name][i]
             e0.record(stream)
-            fn()
+            fn(i)
             e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = {name: float(np.mean([a.elapsed_time(b) for a, b in ev[name]])) for name, _ in parts}
+    times = {name: [a.elapsed_time(b) for a, b in ev[name]] for name, _ in parts}
+    ms = {name: float(np.mean(t)) for name, t in times.items()}
+    med = {name: float(np.median(t)) for name, t in times.items()}
 
-    dec_gbs = dec_bytes / (ms["gqa_decode"] * 1e-3) / 1e9
-    mla_gbs = mla_bytes / (ms["mla_decode"] * 1e-3) / 1e9
-    pre_tfs = pre_flops / (ms["prefill"] * 1e-3) / 1e12
-    chk_tfs = chk_flops / (ms["chunked_prefill"] * 1e-3) / 1e12
-    mlp_tfs = mlp_flops / (ms["mla_prefill"] * 1e-3) / 1e12
+    def rate(nbytes, name):
+        return nbytes / (ms[name] * 1e-3) / 1e9
 
+    dec_gbs = rate(dec_bytes, "gqa_decode")
     dec_hash = source_hash("decode_gqa.hip", "attn_internal.h")
     traffic = measured_traffic("gqa_decode_bf16<128, 1, true, false>", dec_hash)
+    clk_ghz = props.clock_rate / 1e6 if getattr(props, "clock_rate", 0) else None
+    derived_peak = (props.multi_processor_count * BF16_FLOP_PER_CU_CLK * clk_ghz * 1e9 / 1e12) if clk_ghz else None
 
     result = {
         "metric": METRIC,
@@ -266,9 +360,7 @@ def main():
             "workload": (f"llama3_8b_gqa_decode: B={B} Hq={Hq} Hkv={Hkv} head_dim={D} T_max={T_max} "
                          f"cache_lens~U[{dspec['lens'][0]},{dspec['lens'][1]}] (sum {sum_len}) seed={dspec['seed']}, "
                          "bf16 in, fp32 out, default schedule (device-wide unit queue, library-chosen blocks)"),
-            "step": ("attn_prefill_gqa_causal, attn_prefill_gqa_cached, attn_prefill_mla_causal, "
-                     "attn_decode_mla_absorbed, attn_cache_append, attn_decode_gqa, attn_decode_gqa_append, "
-                     "attn_decode_gqa_fp8kv: one call each, in this order"),
+            "step": ", ".join(name for name, _ in parts) + ": one call each, in this order",
             "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "prefill": PB * S, "chunked_prefill": chk_tokens,
                                 "mla_prefill": MPB * MPS},
         },
@@ -284,82 +376,147 @@ def main():
             "algorithmic_bytes_per_launch": dec_bytes,
             "avg_launch_ms": round(ms["gqa_decode"], 5),
         },
-        "parts": {
-            "gqa_decode": {"ms": round(ms["gqa_decode"], 5), "GB/s": round(dec_gbs, 1),
-                           "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4), "TFLOP/s": round(dec_flops / (ms["gqa_decode"] * 1e-3) / 1e12, 2),
-                           "tokens_per_s": round(B / (ms["gqa_decode"] * 1e-3), 1)},
-            "mla_decode": {"ms": round(ms["mla_decode"], 5), "GB/s": round(mla_gbs, 1),
-                           "hbm_frac": round(mla_gbs / HBM_PEAK_GBS, 4),
-                           "algorithmic_bytes_per_launch": mla_bytes,
-                           "TFLOP/s": round(mla_flops / (ms["mla_decode"] * 1e-3) / 1e12, 2),
-                           "tokens_per_s": round(MB / (ms["mla_decode"] * 1e-3), 1),
-                           "workload": f"minimind768_mla_decode: B={MB} H={H} nope={dn} rope={dR} v={dv} r={r} "
-                                       f"cache={MT} seed={mspec['seed']}"},
-            "prefill": {"ms": round(ms["prefill"], 5), "TFLOP/s": round(pre_tfs, 1),
-                        "mfma_frac": round(pre_tfs / BF16_DENSE_PEAK_TFLOPS, 4),
-                        "algorithmic_flops_per_launch": pre_flops,
-                        "tokens_per_s": round(PB * S / (ms["prefill"] * 1e-3), 1),
-                        "workload": f"llama3_8b_gqa_prefill: B={PB} S={S} Hq={PHq} Hkv={pre['k'].shape[2]} "
-                                    f"head_dim={PD} seed={pspec['seed']} bf16 causal"},
-            "chunked_prefill": {"ms": round(ms["chunked_prefill"], 5), "TFLOP/s": round(chk_tfs, 1),
-                                "mfma_frac": round(chk_tfs / BF16_DENSE_PEAK_TFLOPS, 4),
-                                "algorithmic_flops_per_launch": chk_flops,
-                                "tokens_per_s": round(chk_tokens / (ms["chunked_prefill"] * 1e-3), 1),
-                                "workload": f"llama3_8b_gqa_chunked_prefill: B={CB} chunk={CS} "
-                                            f"start_pos={cspec['start_pos']} T_max={CT} Hq={CHq} "
-                                            f"Hkv={chk['k'].shape[2]} head_dim={CD} seed={cspec['seed']} bf16"},
-            "gqa_decode_fp8": {"ms": round(ms["gqa_decode_fp8"], 5),
-                               "GB/s": round(f8_bytes / (ms["gqa_decode_fp8"] * 1e-3) / 1e9, 1),
-                               "hbm_frac": round(f8_bytes / (ms["gqa_decode_fp8"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                               "algorithmic_bytes_per_launch": f8_bytes,
-                               "tokens_per_s": round(B / (ms["gqa_decode_fp8"] * 1e-3), 1),
-                               "workload": "llama3_8b_gqa_decode shape and lengths, K/V as FP8 E4M3 codes of "
-                                           "N(0,1)/scale (device-generated, seed 8), scale 4.5/448"},
-            "gqa_decode_step": {"ms": round(ms["gqa_decode_step"], 5),
-                                "GB/s": round(dec_bytes / (ms["gqa_decode_step"] * 1e-3) / 1e9, 1),
-                                "workload": "llama3_8b_gqa_decode with the newest rows as the new token "
-                                            "(attn_decode_gqa_append: write + decode in one call)"},
-            "kv_append": {"ms": round(ms["kv_append"], 5), "bytes_per_launch": app_bytes,
-                          "GB/s": round(app_bytes / (ms["kv_append"] * 1e-3) / 1e9, 1),
-                          "workload": f"llama3_8b_gqa_decode step write: B={B} rows of Hkv={Hkv} x {D} for K and V"},
-            "mla_prefill": {"ms": round(ms["mla_prefill"], 5), "TFLOP/s": round(mlp_tfs, 1),
-                            "mfma_frac": round(mlp_tfs / BF16_DENSE_PEAK_TFLOPS, 4),
-                            "algorithmic_flops_per_launch": mlp_flops,
-                            "tokens_per_s": round(MPB * MPS / (ms["mla_prefill"] * 1e-3), 1),
-                            "workload": f"minimind768_mla_prefill: B={MPB} S={MPS} H={MPH} nope={MPdn} rope={MPdR} "
-                                        f"v={MPdv} r={MPr} seed={mpspec['seed']} bf16 causal"},
-        },
+        "peaks": {"hbm_GB/s": HBM_PEAK_GBS, "bf16_dense_TFLOP/s_published": BF16_DENSE_PEAK_TFLOPS,
+                  "bf16_dense_TFLOP/s_from_device": round(derived_peak, 1) if derived_peak else None,
+                  "device": {"name": props.name, "compute_units": props.multi_processor_count,
+                             "max_clock_GHz": clk_ghz}},
+        "parts": {},
         "input_generation_s": round(t_gen, 2),
     }
+    P = result["parts"]
+
+    def decode_part(name, nbytes, tokens, flops=None, workload=None, extra=None):
+        gbs = rate(nbytes, name)
+        e = {"ms": round(ms[name], 5), "ms_median": round(med[name], 5), "GB/s": round(gbs, 1),
+             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": nbytes,
+             "tokens_per_s": round(tokens / (ms[name] * 1e-3), 1)}
+        if flops is not None:
+            e["TFLOP/s"] = round(flops / (ms[name] * 1e-3) / 1e12, 2)
+        if workload:
+            e["workload"] = workload
+        if extra:
+            e.update(extra)
+        P[name] = e
+
+    def prefill_part(name, flops, tokens, workload, extra=None):
+        tfs = flops / (ms[name] * 1e-3) / 1e12
+        e = {"ms": round(ms[name], 5), "ms_median": round(med[name], 5), "TFLOP/s": round(tfs, 1),
+             "mfma_frac": round(tfs / BF16_DENSE_PEAK_TFLOPS, 4), "algorithmic_flops_per_launch": flops,
+             "tokens_per_s": round(tokens / (ms[name] * 1e-3), 1), "workload": workload}
+        if extra:
+            e.update(extra)
+        P[name] = e
+
+    decode_part("gqa_decode", dec_bytes, B, dec_flops)
+    if "mla_decode" in ms:
+        decode_part("mla_decode", mla_bytes, MB, mla_flops,
+                    f"minimind768_mla_decode: B={MB} H={H} nope={dn} rope={dR} v={dv} r={r} cache={MT} "
+                    f"seed={mspec['seed']} (+5 device-drawn cache copies, used in turn)")
+    if "prefill" in ms:
+        prefill_part("prefill", pre_flops, PB * S,
+                     f"llama3_8b_gqa_prefill: B={PB} S={S} Hq={PHq} Hkv={pre['k'].shape[2]} head_dim={PD} "
+                     f"seed={pspec['seed']} bf16 causal")
+    if "chunked_prefill" in ms:
+        prefill_part("chunked_prefill", chk_flops, chk_tokens,
+                     f"llama3_8b_gqa_chunked_prefill: B={CB} chunk={CS} start_pos={cspec['start_pos']} T_max={CT} "
+                     f"Hq={CHq} Hkv={chk['k'].shape[2]} head_dim={CD} seed={cspec['seed']} bf16")
+    if "mla_prefill" in ms:
+        prefill_part("mla_prefill", mlp_flops, MPB * MPS,
+                     f"minimind768_mla_prefill: B={MPB} S={MPS} H={MPH} nope={MPdn} rope={MPdR} v={MPdv} "
+                     f"r={MPr} seed={mpspec['seed']} bf16 causal",
+                     {"flop_count": "absorbed form: 2(r+dR)+2r per unmasked pair and head + 2r(dn+dv) per token "
+                                    "and head",
+                      "TFLOP/s_sdpa_count": round(mlp_flops_sdpa / (ms["mla_prefill"] * 1e-3) / 1e12, 1),
+                      "mfma_frac_sdpa_count": round(mlp_flops_sdpa / (ms["mla_prefill"] * 1e-3) / 1e12
+                                                    / BF16_DENSE_PEAK_TFLOPS, 4),
+                      "algorithmic_flops_sdpa_count": mlp_flops_sdpa})
+    if "gqa_decode_fp8" in ms:
+        decode_part("gqa_decode_fp8", f8_bytes, B, None,
+                    "llama3_8b_gqa_decode shape and lengths, K/V as FP8 E4M3 codes of N(0,1)/scale "
+                    "(device-drawn, seed 8), scale 4.5/448")
+    if "gqa_decode_step" in ms:
+        decode_part("gqa_decode_step", dec_bytes, B, None,
+                    "llama3_8b_gqa_decode with the newest rows as the new token "
+                    "(attn_decode_gqa_append: write + decode in one call)")
+    if "kv_append" in ms:
+        P["kv_append"] = {"ms": round(ms["kv_append"], 5), "bytes_per_launch": app_bytes,
+                          "GB/s": round(rate(app_bytes, "kv_append"), 1),
+                          "workload": f"llama3_8b_gqa_decode step write: B={B} rows of Hkv={Hkv} x {D} for K and V"}
+    for name, w in sweep.items():
+        decode_part(name, w["bytes"], w["tokens"], w["flops"], w["workload"])
+    if "minimind768_gqa_decode" in ms:
+        decode_part("minimind768_gqa_decode", mm_bytes, MMB, 4 * MMHq * MMD * mm_len,
+                    f"minimind768_gqa_decode: B={MMB} Hq={MMHq} Hkv={MMHkv} head_dim={MMD} cache={MMT} fp32 in/out "
+                    f"seed={synth.WORKLOADS['minimind768_gqa_decode']['seed']} (1.5 MiB of K/V: cache-resident and "
+                    "launch-bound by size; the HBM bar does not apply)")
     if args.copy_calibration:
-        result["parts"]["copy_1GiB"] = {"ms": round(ms["copy_1GiB"], 5),
-                                        "GB/s_read+write": round(2 * (1 << 30) / (ms["copy_1GiB"] * 1e-3) / 1e9, 1)}
+        P["copy_1GiB"] = {"ms": round(ms["copy_1GiB"], 5),
+                          "GB/s_read+write": round(2 * (1 << 30) / (ms["copy_1GiB"] * 1e-3) / 1e9, 1)}
 
     if not args.no_cpu_baseline:
-        import oracle
-        # the oracle as it stands, on the same decode workload (all 32 sequences), repeated until
-        # about --cpu-seconds of host time
-        reps, t_cpu = 0, 0.0
-        t_begin = time.perf_counter()
-        while True:
-            t1 = time.perf_counter()
-            oracle.gqa_decode(dec_cpu["q"], dec_cpu["k"], dec_cpu["v"], dec_cpu["cache_lens"])
-            t_cpu += time.perf_counter() - t1
-            reps += 1
-            if time.perf_counter() - t_begin >= args.cpu_seconds or reps >= 50:
-                break
-        result["cpu_baseline"] = {
-            "value": round(dec_bytes * reps / t_cpu / 1e9, 3),
-            "unit": "GB/s",
-            "cores": oracle.threads(),
-            "kind": "oracle",
-            "sample": (f"fp64 C oracle (oracle/oracle.c, OpenMP over (sequence, head) rows) on the full "
-                       f"llama3_8b_gqa_decode workload, {reps} run(s) in {t_cpu:.2f} s (float32 copies of the "
-                       f"bf16 inputs; conversion included)"),
-        }
+        result["cpu_baseline"] = cpu_baseline(args, dec_cpu, dec_bytes, mm_cpu, mm_bytes, synth, np)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, dec_cpu, dec_bytes, mm_cpu, mm_bytes, synth, np):
+    """The fp64 C oracle, as it stands, on a bounded sample of each configuration (about
+    --cpu-seconds each), on this host's cores.  `value` is the Llama-3 decode sample's rate in
+    the headline unit; `per_config` holds every configuration's sample, time and rate."""
+    import oracle
+
+    def timed(fn):
+        reps, t = 0, 0.0
+        t_begin = time.perf_counter()
+        while True:
+            t1 = time.perf_counter()
+            fn()
+            t += time.perf_counter() - t1
+            reps += 1
+            if time.perf_counter() - t_begin >= args.cpu_seconds or reps >= 50:
+                return reps, t
+
+    per = {}
+    reps, t = timed(lambda: oracle.gqa_decode(dec_cpu["q"], dec_cpu["k"], dec_cpu["v"], dec_cpu["cache_lens"]))
+    per["llama3_8b_gqa_decode"] = {"sample": f"all {dec_cpu['q'].shape[0]} sequences", "runs": reps,
+                                   "s_per_run": round(t / reps, 4), "GB/s": round(dec_bytes * reps / t / 1e9, 3)}
+    headline = per["llama3_8b_gqa_decode"]["GB/s"]
+    reps, t = timed(lambda: oracle.gqa_decode(mm_cpu["q"], mm_cpu["k"], mm_cpu["v"], mm_cpu["cache_lens"]))
+    per["minimind768_gqa_decode"] = {"sample": "the whole workload", "runs": reps, "s_per_run": round(t / reps, 5),
+                                     "GB/s": round(mm_bytes * reps / t / 1e9, 3)}
+    for name in ("kv_sweep_mha", "kv_sweep_gqa8", "kv_sweep_mqa"):
+        w = synth.make(name, B=2)
+        nb = gqa_decode_bytes(w["k"].shape[2], w["k"].shape[3], 2, int(w["cache_lens"].sum()))
+        reps, t = timed(lambda: oracle.gqa_decode(w["q"], w["k"], w["v"], w["cache_lens"]))
+        per[name] = {"sample": "2 of the 16 sequences", "runs": reps, "s_per_run": round(t / reps, 4),
+                     "GB/s": round(nb * reps / t / 1e9, 3)}
+    pw = synth.make("llama3_8b_gqa_prefill", B=1, Hq=4, Hkv=1)
+    S = pw["q"].shape[1]
+    rows = list(range(S - 1, -1, -64))  # 64 query rows spread over the sequence
+    fl = sum(4 * 4 * 128 * (i + 1) for i in rows)
+    reps, t = timed(lambda: oracle.gqa_prefill_causal(pw["q"], pw["k"], pw["v"], rows=rows))
+    per["llama3_8b_gqa_prefill"] = {"sample": "1 sequence, 1 KV group (4 query heads), 64 of the 4096 query rows",
+                                    "runs": reps, "s_per_run": round(t / reps, 4),
+                                    "TFLOP/s": round(fl * reps / t / 1e12, 5)}
+    mw = synth.make("minimind768_mla_decode", B=4)
+    mb = (mw["c_kv"].shape[2] + mw["k_rope"].shape[2]) * 2 * int(mw["cache_lens"].sum())
+    keys = ("q_nope", "q_rope", "w_uk", "w_uv", "c_kv", "k_rope", "cache_lens")
+    reps, t = timed(lambda: oracle.mla_decode_decompressed(*(mw[k] for k in keys)))
+    per["minimind768_mla_decode"] = {"sample": "4 of the 64 sequences, decompressed form (keys and values rebuilt)",
+                                     "runs": reps, "s_per_run": round(t / reps, 4),
+                                     "GB/s": round(mb * reps / t / 1e9, 4)}
+    return {
+        "value": headline,
+        "unit": "GB/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "cpu_model": cpu_model(),
+        "sample": ("fp64 C oracle (oracle/oracle.c, OpenMP over output rows) on the full llama3_8b_gqa_decode "
+                   "workload (float32 copies of the bf16 inputs; conversion included); per_config lists a "
+                   "bounded sample of every configuration"),
+        "per_config": per,
+    }
 
 
 if __name__ == "__main__":

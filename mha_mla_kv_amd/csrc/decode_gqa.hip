@@ -775,9 +775,10 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
         for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float p = exp2_fast(sc[hb][s][i] - mn);
-            ps += p;
-            pop[hb][4 * s + i] = (__bf16)p;
+            // the row sum adds the bf16-rounded probability the PV product uses
+            const __bf16 pb = (__bf16)exp2_fast(sc[hb][s][i] - mn);
+            ps += (float)pb;
+            pop[hb][4 * s + i] = pb;
           }
         lsum[hb] = lsum[hb] * alpha + ps;
 #pragma unroll

@@ -361,7 +361,9 @@ __device__ __forceinline__ void store_rows(void* out, size_t orow, int out_bf16,
   }
 }
 
-template <int D>
+// CACHED tags the instance launched for a cached prefix (start_pos given); the
+// code is the same, the separate symbol keeps the two apart in kernel profiles.
+template <int D, bool CACHED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_causal(PrefillArgs a) {
   static_assert(D % 32 == 0 && D <= 128, "head_dim");
   static_assert(kBM == 32 * kWaves, "one 32-row slice per wave");
@@ -703,8 +705,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
 // Explicit instantiations: without them the host stubs of only some of the
 // kernel templates launched below were emitted.
-template __global__ void prefill_causal<128>(PrefillArgs);
-template __global__ void prefill_causal<64>(PrefillArgs);
+template __global__ void prefill_causal<128, false>(PrefillArgs);
+template __global__ void prefill_causal<64, false>(PrefillArgs);
+template __global__ void prefill_causal<128, true>(PrefillArgs);
+template __global__ void prefill_causal<64, true>(PrefillArgs);
 template __global__ void prefill_mla<96, 48, 96>(MlaPrefillArgs);
 
 }  // namespace
@@ -716,8 +720,14 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const long long wgs = (long long)((a.S + kBM - 1) / kBM) * a.Hq * a.B;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)wgs);
-  if (a.D == 128) hipLaunchKernelGGL(prefill_causal<128>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(prefill_causal<64>, grid, dim3(256), 0, st, a);
+  const bool cached = a.start_pos != nullptr;
+  if (a.D == 128) {
+    if (cached) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<128, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<128, false>), grid, dim3(256), 0, st, a);
+  } else {
+    if (cached) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<64, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<64, false>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -14,7 +14,8 @@ oracle disagrees with:
     gap; a saturating one-hot key selects one V row bit-exactly;
   * invariants: a joint permutation of cached tokens, a constant added to every
     score, per-head MHA, MQA = every head reading KV head 0, GQA = MHA on K/V
-    expanded by the repeat_kv expand+reshape, MLA absorbed = decompressed;
+    expanded by the contiguous head-to-group map h -> h // n_rep, MLA absorbed =
+    decompressed;
   * cached-prefix prefill: torch SDPA with an explicit position mask, an empty
     prefix reducing to causal prefill, and each new row equal to a decode at its
     own position;
@@ -227,20 +228,17 @@ def pin_decode_head_structure(lib):
     mqa = oracle.gqa_decode(q, k1, v1, lens, lib=lib)
     _close(mqa, oracle.gqa_decode(q, np.repeat(k1, Hq, axis=2), np.repeat(v1, Hq, axis=2), lens, lib=lib),
            0.0, "MQA")
-    # GQA equals MHA on K/V expanded by repeat_kv: x[:, :, :, None, :] broadcast over n_rep, reshaped
+    # GQA equals MHA on K/V expanded to one head per query head, built from the grouping
+    # definition itself: query head h reads KV head h // n_rep (the contiguous grouping)
     for Hkv in (2, 4):
         n_rep = Hq // Hkv
         kg, vg = _rand(rng, B, T, Hkv, D), _rand(rng, B, T, Hkv, D)
-
-        def repeat_kv(x):
-            bs, slen, nkv, hd = x.shape
-            return np.broadcast_to(x[:, :, :, None, :], (bs, slen, nkv, n_rep, hd)).reshape(bs, slen, nkv * n_rep, hd)
-
-        ke, ve = repeat_kv(kg), repeat_kv(vg)
-        assert np.array_equal(ke, np.repeat(kg, n_rep, axis=2))  # the docstring's repeat_interleave
+        src = np.arange(Hq) // n_rep
+        ke, ve = kg[:, :, src], vg[:, :, src]
+        assert np.array_equal(ke, np.repeat(kg, n_rep, axis=2))  # the same expansion as repeat_interleave
         _close(oracle.gqa_decode(q, kg, vg, lens, lib=lib),
                oracle.gqa_decode(q, np.ascontiguousarray(ke), np.ascontiguousarray(ve), lens, lib=lib),
-               0.0, f"repeat_kv n_rep={n_rep}")
+               0.0, f"expanded K/V n_rep={n_rep}")
 
 
 # ----------------------------------------------------------------------------- prefill pins
