@@ -117,6 +117,34 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
                             size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* GQA decode that allocates nothing: attn_decode_gqa without a workspace.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The same computation,
+ * kernels and arguments as attn_decode_gqa, minus workspace / workspace_bytes:
+ * the partial results and the work-queue counter live in a scratch array of
+ * ATTN_NOALLOC_SCRATCH_BYTES bytes that the library's code object holds in
+ * device memory, one copy per device, kept until the process ends.  Its device
+ * address is looked up on the first call on each device (a runtime query, no
+ * allocation); each call first zeroes its queue counter with a one-thread
+ * kernel on `stream`, then runs the decode.  The call allocates and frees
+ * nothing.
+ *
+ * Sizes whose attn_decode_gqa_workspace_bytes(...) exceeds
+ * ATTN_NOALLOC_SCRATCH_BYTES return ATTN_ERR_WORKSPACE and enqueue nothing
+ * (the Llama-3-8B decode shape, B 32 x Hkv 8 x T_max 8192, needs about 8.5 MB).
+ * Every call on one device shares that device's scratch and leaves the last
+ * call's contents in it: calls that overlap in time on one device (different
+ * streams, or threads) race and must be serialised by the caller.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+attn_status attn_decode_gqa_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* cache_lens, void* out, int B, int Hq, int Hkv, int head_dim,
+                                    int T_max, float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype,
+                                    int split_tokens, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* GQA decode over caches stored as 8-bit floats (OCP FP8 E4M3).
  *
  *   K[b,t,g,:] = k_scale * e4m3(k_cache[b,t,g,:]),  V likewise with v_scale,

@@ -54,6 +54,8 @@ def _declare(lib):
     lib.attn_decode_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, Z, P]
     lib.attn_prefill_gqa_causal.restype = I
     lib.attn_prefill_gqa_causal.argtypes = [P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.attn_decode_gqa_noalloc.restype = I
+    lib.attn_decode_gqa_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P]
     lib.attn_decode_gqa_fp8kv.restype = I
     lib.attn_decode_gqa_fp8kv.argtypes = [P, P, P, F, F, P, P, I, I, I, I, I, F, I, I, P, ctypes.c_size_t, P]
     lib.attn_decode_gqa_append_workspace_bytes.restype = ctypes.c_size_t
@@ -179,6 +181,31 @@ def attn_decode_gqa(q, k_cache, v_cache, cache_lens, out=None, softmax_scale: fl
                                Hkv, D, T_max, float(softmax_scale), _dt(q), _dt(out), int(split_tokens),
                                _ptr(workspace), workspace.numel(), _stream(q.device))
     _raise_if(st, "attn_decode_gqa")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # ATTN_NOALLOC_SCRATCH_BYTES
+
+
+def attn_decode_gqa_noalloc(q, k_cache, v_cache, cache_lens, out, softmax_scale: float = 0.0,
+                            split_tokens: int = 0):
+    """attn_decode_gqa without a workspace: the library's per-device scratch holds the partial
+    results (sizes needing more than NOALLOC_SCRATCH_BYTES are rejected).  The caller passes
+    out [B,Hq,D] (fp32 or bf16); nothing is allocated.  Calls that overlap on one device race.
+    Returns out."""
+    _check(q, "q")
+    B, Hq, D = q.shape
+    _check(k_cache, "k_cache", dtype=q.dtype)
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError(f"k_cache must be [B={B}, T_max, Hkv, {D}] (got {tuple(k_cache.shape)})")
+    T_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _check(v_cache, "v_cache", shape=k_cache.shape, dtype=q.dtype)
+    _check(cache_lens, "cache_lens", shape=(B,), dtype=torch.int32)
+    _check(out, "out", shape=(B, Hq, D))
+    st = lib().attn_decode_gqa_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens), _ptr(out), B, Hq,
+                                       Hkv, D, T_max, float(softmax_scale), _dt(q), _dt(out), int(split_tokens),
+                                       _stream(q.device))
+    _raise_if(st, "attn_decode_gqa_noalloc")
     return out
 
 
@@ -413,7 +440,7 @@ def attn_decode_mla_absorbed(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, cache_len
     return out
 
 
-__all__ = ["attn_decode_gqa", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
+__all__ = ["attn_decode_gqa", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_noalloc", "NOALLOC_SCRATCH_BYTES", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
            "attn_decode_gqa_append_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached",
            "attn_prefill_mla_causal", "attn_cache_append",
            "attn_decode_mla_absorbed", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",

@@ -13,6 +13,8 @@
 
 #include "attn_internal.h"
 
+static_assert(attn::kNoallocScratchBytes == ATTN_NOALLOC_SCRATCH_BYTES, "scratch size of the header");
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -180,7 +182,7 @@ attn_status gqa_decode_common(const char* fn, const void* q, const void* k_new, 
                               const void* v_cache, const int32_t* cache_lens, void* out, int B, int Hq, int Hkv,
                               int head_dim, int T_max, float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype,
                               int split_tokens, void* workspace, size_t workspace_bytes, void* stream,
-                              const float* kv_scales = nullptr) {
+                              const float* kv_scales = nullptr, bool noalloc = false) {
   const bool append = k_new != nullptr;
   const bool kv_fp8 = kv_scales != nullptr;
   if (!q || !k_cache || !v_cache || !cache_lens || !out)
@@ -213,12 +215,26 @@ attn_status gqa_decode_common(const char* fn, const void* q, const void* k_new, 
                 kMaxGridYZ);
   if (lay.slots >= (1ll << 31) / (n_rep > 0 ? n_rep : 1))
     return fail(ATTN_ERR_SHAPE, "%s: too many chunks (B*Hkv*ceil(T_max/split_tokens) too large)", fn);
-  if (!workspace || workspace_bytes < lay.total)
-    return fail(ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given%s", fn, lay.total,
-                workspace_bytes, workspace ? "" : " (NULL)");
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(ATTN_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  if (noalloc) {
+    if (lay.total > attn::kNoallocScratchBytes)
+      return fail(ATTN_ERR_WORKSPACE, "%s: these sizes need %zu bytes of scratch; the built-in scratch holds %zu",
+                  fn, lay.total, attn::kNoallocScratchBytes);
+  } else {
+    if (!workspace || workspace_bytes < lay.total)
+      return fail(ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given%s", fn, lay.total,
+                  workspace_bytes, workspace ? "" : " (NULL)");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(ATTN_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  }
 
+  if (noalloc) {
+    // every call on a device shares its scratch; the queue counter is zeroed first
+    const attn_status st = hip_status(attn::noalloc_scratch(&workspace), fn);
+    if (st != ATTN_OK) return st;
+    const attn_status sc =
+        hip_status(attn::launch_clear_queue(static_cast<unsigned*>(workspace), static_cast<hipStream_t>(stream)), fn);
+    if (sc != ATTN_OK) return sc;
+  }
   attn::GqaDecodeArgs a;
   a.q = q;
   a.k = k_cache;
@@ -276,6 +292,15 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
   return gqa_decode_common("attn_decode_gqa", q, nullptr, nullptr, k_cache, v_cache, cache_lens, out, B, Hq, Hkv,
                            head_dim, T_max, softmax_scale, in_dtype, out_dtype, split_tokens, workspace,
                            workspace_bytes, stream);
+}
+
+attn_status attn_decode_gqa_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* cache_lens, void* out, int B, int Hq, int Hkv, int head_dim,
+                                    int T_max, float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype,
+                                    int split_tokens, void* stream) {
+  return gqa_decode_common("attn_decode_gqa_noalloc", q, nullptr, nullptr, k_cache, v_cache, cache_lens, out, B, Hq,
+                           Hkv, head_dim, T_max, softmax_scale, in_dtype, out_dtype, split_tokens, nullptr, 0, stream,
+                           nullptr, true);
 }
 
 attn_status attn_decode_gqa_fp8kv(const void* q, const void* k_cache, const void* v_cache, float k_scale,

@@ -124,4 +124,11 @@ hipError_t launch_cache_append(const CacheAppendArgs& a, hipStream_t stream);
 bool mla_decode_supported(int H, int r, int dR);
 hipError_t launch_mla_decode(const MlaDecodeArgs& a, hipStream_t stream);
 
+// The device-resident scratch of the allocation-free decode (decode_gqa.hip):
+// its address on the current device (looked up once per device, then cached),
+// and a launch that zeroes its work-queue counter (the first 4 bytes).
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(void** ptr);
+hipError_t launch_clear_queue(unsigned* queue, hipStream_t stream);
+
 }  // namespace attn

@@ -1074,7 +1074,43 @@ hipError_t launch_mode(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
                                                                      : launch_f32<128, QUEUE>(a, grid, st);
 }
 
+// Zeroes the work-queue counter of a scratch buffer (a kernel rather than a
+// memset, so that the call can be captured in a graph).
+__global__ void clear_queue(unsigned* queue) { *queue = 0u; }
+
+// Scratch of the allocation-free decode: the workspace of attn_decode_gqa
+// (queue counter, log2-sum-exps, partial outputs) in device memory that the
+// code object holds, one copy per device, for callers that cannot allocate.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
 }  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  // in host code `scratch` names a host-side stand-in; the device address of
+  // each device's copy comes from the runtime, once per device
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_clear_queue(unsigned* queue, hipStream_t st) {
+  hipLaunchKernelGGL(clear_queue, dim3(1), dim3(1), 0, st, queue);
+  return hipGetLastError();
+}
 
 bool gqa_decode_supported(int D, int n_rep, int in_bf16) {
   if (D != 64 && D != 96 && D != 128) return false;

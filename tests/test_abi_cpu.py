@@ -225,3 +225,30 @@ def test_python_binding_rejects_cpu_tensors():
     k = torch.zeros(1, 16, 2, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         attn.attn_decode_gqa(q, k, k, torch.zeros(1, dtype=torch.int32))
+
+
+@no_gpu_only
+def test_noalloc_decode_validation():
+    lib = attn.lib()
+
+    def f(q=FAKE, B=2, Hq=8, Hkv=2, D=128, T=64, split=0):
+        return lib.attn_decode_gqa_noalloc(q, FAKE, FAKE, FAKE, FAKE, B, Hq, Hkv, D, T, 0.0, BF16, F32, split, None)
+    assert f(q=None) == NULL
+    assert f(B=0) == SHAPE
+    assert f(Hq=32, Hkv=3) == GROUPS
+    assert f(D=80) == UNSUP
+    assert f(split=100) == SHAPE
+    # sizes whose workspace exceeds the built-in scratch are rejected before anything runs
+    B, Hq, Hkv, D, T = 64, 64, 64, 128, 65536
+    assert attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T, 0) > attn.NOALLOC_SCRATCH_BYTES
+    assert f(B=B, Hq=Hq, Hkv=Hkv, D=D, T=T) == WS
+    assert b"scratch" in lib.attn_last_error()
+    # the Llama-3-8B decode shape fits
+    assert attn.attn_decode_gqa_workspace_bytes(32, 32, 8, 128, 8192, 0) <= attn.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_scratch_size_matches_header():
+    import re
+    text = open(attn.HEADER_PATH).read()
+    m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == attn.NOALLOC_SCRATCH_BYTES
