@@ -292,18 +292,24 @@ attn_status attn_prefill_gqa_cached(const void* q, const void* k_cache, const vo
  *   all of q_nope, q_rope, w_uk, w_uv, c_kv, k_rope in in_dtype (ATTN_BF16).
  *
  * Supported (attn_decode_mla_supported): in_dtype ATTN_BF16, kv_lora_rank in
- * {64, 128, 256}, rope_dim in {16, 32, 48, 64}, H <= 16; nope_head_dim and
- * v_head_dim in [1, 256].  c_kv, k_rope, w_uk, w_uv and out must be 16-byte
- * aligned (else ATTN_ERR_UNSUPPORTED).
+ * {64, 128, 256}, rope_dim in {16, 32, 48, 64}, H <= 16; nope_head_dim a
+ * multiple of 8 in [8, 256]; v_head_dim a multiple of 16 in [16, 256].  c_kv, k_rope, w_uk, w_uv
+ * and out must be 16-byte aligned (else ATTN_ERR_UNSUPPORTED).  One kernel
+ * launch: the absorbed query, the cache pass, the merge of a sequence's chunks
+ * and the W_UV product all run in it.
  * split_tokens: 0 lets the library choose the chunk length (a power of two of at
- * least 256 positions, about one chunk per compute unit over B * T_max);
- * otherwise a multiple of 64 in [64, 65536].  Each (chunk, sequence) is one
- * workgroup serving all H heads; a sequence of length L uses ceil(L / chunk)
- * chunks, merged afterwards.
+ * least 256 positions, about one chunk per compute unit of a 256-unit MI355X
+ * over B * T_max; the choice, and so the workspace size, does not depend on the
+ * current device); otherwise a multiple of 64 in [64, 65536].  Each (chunk,
+ * sequence) is one workgroup serving all H heads; a sequence of length L uses
+ * ceil(L / chunk) chunks, merged inside the same launch by the chunk that
+ * finishes last.
  * workspace: at least attn_decode_mla_workspace_bytes(...) bytes, 256-byte
- * aligned, holding the absorbed queries and the per-chunk partial results; no
- * initialisation is needed and every call overwrites what it uses.  One
- * workspace per concurrent call.
+ * aligned: per-sequence counters of finished chunks (the first 4 * B bytes),
+ * then the per-chunk partial results.  The counters must be zero before the
+ * first call that uses the workspace (e.g. allocate it zero-filled) and every
+ * call leaves them zero; the rest needs no initialisation.  One workspace per
+ * concurrent call: calls that overlap in time on one workspace race.
  */
 size_t attn_decode_mla_workspace_bytes(int B, int H, int kv_lora_rank, int rope_dim, int T_max,
                                        int split_tokens);

@@ -110,33 +110,37 @@ int device_cus() {
   return cus;
 }
 
+// Compute units the default MLA chunk length is planned for (MI355X).  A fixed
+// number rather than the current device's, so that the workspace size of a
+// call does not depend on which device is current; on a device with another
+// count the plan stays valid, only less balanced.
+constexpr int kPlanCUs = 256;
+
+// MLA decode workspace: [per-sequence done counters, B x 4 bytes][lse B x
+// n_splits x H][o_part B x n_splits x H x r] fp32, each piece 256-byte aligned.
 struct MlaLayout {
   int split, n_splits;
-  size_t q_lat_off, o_part_off, lse_off, total;
+  size_t lse_off, o_part_off, total;
 };
 
-MlaLayout mla_layout(int B, int H, int r, int dR, int T_max, int split_tokens) {
+MlaLayout mla_layout(int B, int H, int r, int T_max, int split_tokens) {
   MlaLayout l;
   // One (chunk, sequence) workgroup serves all heads; aim for about one
-  // workgroup per CU over the whole batch (measured faster than two: every
-  // chunk pays the ring's first-copy latency and the merge reads one partial
-  // per chunk), with chunks of at least 256 tokens so each wave's copy ring
-  // runs several steps.
+  // workgroup per compute unit over the whole batch, with chunks of at least
+  // 256 positions so that each wave's copy ring runs several steps.
   if (split_tokens) {
     l.split = split_tokens;
   } else {
-    const int cus = device_cus() > 0 ? device_cus() : 256;
-    const long long want = ((long long)B * T_max + cus - 1) / cus;
+    const long long want = ((long long)B * T_max + kPlanCUs - 1) / kPlanCUs;
     long long s = 256;
     while (s < want && s < 65536) s <<= 1;
     l.split = (int)s;
   }
   l.n_splits = (T_max + l.split - 1) / l.split;
   const size_t rows = (size_t)B * H * l.n_splits;
-  l.q_lat_off = 0;
-  l.o_part_off = align_up((size_t)B * 2 * 16 * (r + dR) * 2);
-  l.lse_off = l.o_part_off + align_up(rows * r * sizeof(float));
-  l.total = l.lse_off + align_up(rows * sizeof(float));
+  l.lse_off = align_up((size_t)B * sizeof(unsigned));
+  l.o_part_off = l.lse_off + align_up(rows * sizeof(float));
+  l.total = l.o_part_off + align_up(rows * r * sizeof(float));
   return l;
 }
 
@@ -483,7 +487,7 @@ size_t attn_decode_mla_workspace_bytes(int B, int H, int kv_lora_rank, int rope_
                                        int split_tokens) {
   if (B <= 0 || H <= 0 || kv_lora_rank <= 0 || rope_dim < 0 || T_max <= 0 || !valid_split(split_tokens))
     return 0;
-  return mla_layout(B, H, kv_lora_rank, rope_dim, T_max, split_tokens).total;
+  return mla_layout(B, H, kv_lora_rank, T_max, split_tokens).total;
 }
 
 int attn_decode_mla_supported(int H, int kv_lora_rank, int rope_dim, attn_dtype in_dtype) {
@@ -506,8 +510,10 @@ attn_status attn_decode_mla_absorbed(const void* q_nope, const void* q_rope, con
                 B, H, nope_head_dim, rope_dim, v_head_dim, kv_lora_rank, T_max);
   if (B > kMaxGridYZ)
     return fail(ATTN_ERR_SHAPE, "attn_decode_mla_absorbed: B must be <= %d", kMaxGridYZ);
-  if (nope_head_dim > 256 || v_head_dim > 256)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: nope_head_dim and v_head_dim must be <= 256");
+  if (nope_head_dim > 256 || nope_head_dim % 8 != 0 || v_head_dim > 256 || v_head_dim % 16 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "attn_decode_mla_absorbed: nope_head_dim must be a multiple of 8 and v_head_dim a multiple of 16, "
+                "both up to 256 (got %d, %d)", nope_head_dim, v_head_dim);
   if (!valid_split(split_tokens))
     return fail(ATTN_ERR_SHAPE, "attn_decode_mla_absorbed: split_tokens=%d must be 0 or a multiple of 64 in [64, 65536]",
                 split_tokens);
@@ -519,7 +525,7 @@ attn_status attn_decode_mla_absorbed(const void* q_nope, const void* q_rope, con
   if (!aligned16(c_kv) || !aligned16(k_rope) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(out))
     return fail(ATTN_ERR_UNSUPPORTED,
                 "attn_decode_mla_absorbed: c_kv, k_rope, w_uk, w_uv and out must be 16-byte aligned");
-  const MlaLayout lay = mla_layout(B, H, kv_lora_rank, rope_dim, T_max, split_tokens);
+  const MlaLayout lay = mla_layout(B, H, kv_lora_rank, T_max, split_tokens);
   if (!workspace || workspace_bytes < lay.total)
     return fail(ATTN_ERR_WORKSPACE, "attn_decode_mla_absorbed: workspace of %zu bytes needed, %zu given%s",
                 lay.total, workspace_bytes, workspace ? "" : " (NULL)");
@@ -535,7 +541,7 @@ attn_status attn_decode_mla_absorbed(const void* q_nope, const void* q_rope, con
   a.lens = cache_lens;
   a.out = out;
   char* ws = static_cast<char*>(workspace);
-  a.q_lat = ws + lay.q_lat_off;
+  a.done = reinterpret_cast<unsigned*>(ws);
   a.o_part = reinterpret_cast<float*>(ws + lay.o_part_off);
   a.lse = reinterpret_cast<float*>(ws + lay.lse_off);
   a.B = B;

@@ -98,9 +98,9 @@ struct MlaDecodeArgs {
   const void* k_rope;   // [B, T_max, dR]
   const int32_t* lens;  // [B]
   void* out;            // [B, H, dv]
-  void* q_lat;          // [B, 2, 16, r + dR] bf16 (hi, lo), workspace
-  float* o_part;        // [B, H, n_splits, r]  workspace
-  float* lse;           // [B, H, n_splits]     workspace
+  unsigned* done;       // [B] chunks of the sequence finished so far, zero between calls (workspace)
+  float* o_part;        // [B, n_splits, H, r]  normalised chunk outputs in the latent space (workspace)
+  float* lse;           // [B, n_splits, H]     their log2-sum-exps (workspace)
   int B, H, dn, dR, dv, r, T_max;
   int split, n_splits;
   float scale_log2e;

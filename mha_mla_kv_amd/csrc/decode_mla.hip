@@ -1,4 +1,4 @@
-// MLA decode in absorbed form for gfx950.
+// MLA decode in absorbed form for gfx950, one kernel launch per call.
 //
 // What is computed (qqstock DeepSeek MLA article, sections 1-4 and 6, and its
 // MultiHeadLatentAttention listing): keys are [W_UK[h] c , k_rope] and values
@@ -9,24 +9,34 @@
 //   q_lat  = [W_UK[h]^T q_nope , q_rope],  s_t = scale q_lat . [c_t , k_rope_t],
 //   o_lat  = sum_t softmax(s)_t c_t,       out = W_UV[h] o_lat.
 //
-// Three kernels (not from the pages; designed for CDNA4), each a single memory
-// round trip where it can be:
-//  1. mla_absorb, one workgroup per (head, sequence): q_lat in fp32, kept as a
-//     bf16 hi/lo pair (the MFMA score then sees ~16 mantissa bits of q_lat).
-//  2. mla_decode_fused, grid (chunk, sequence), 4 waves, every workgroup serving
-//     all heads (padded to 16) of one chunk of one sequence, so each cache row is
-//     read from HBM once.  Wave w owns the 16-token slices c0 + 64k + 16w of the
-//     chunk and runs its own 3-stage ring of buffer_load_dwordx4 ... lds copies
-//     of the c_kv and k_rope slices.  S^T = [c k_rope] q_lat^T on 16x16x32 MFMA
-//     (a trailing 16-wide rope chunk is zero-padded to 32) with the latent read
-//     from LDS; P^T is the accumulator as it stands; O^T += V^T P^T on 16x16x16
-//     MFMA with V^T read transposed (ds_read_b64_tr_b16) from the same latent
-//     slice, since values share the latent with the un-rotated key.  A wave only
-//     reads rows it copied itself, so the loop has no workgroup barrier.  The
-//     four waves merge through LDS and the chunk's normalised o_lat and
-//     log2-sum-exp go to the workspace.
-//  3. mla_merge_wuv, one workgroup per (head, sequence): log2-sum-exp merge of
-//     the chunks, then out = W_UV[h] o_lat with the W_UV rows already in flight.
+// How (not from the pages; designed for CDNA4).  One workgroup per (chunk of
+// cached positions, sequence) serves all heads (padded to 16), so each cache
+// row is read from HBM once.  Eight waves with two roles:
+//  * waves 0-3 stream the chunk: wave w owns the 16-token slices c0 + 64k + 16w
+//    and runs its own ring of kStages buffer_load_dwordx4 ... lds copies
+//    (non-temporal) of the c_kv and k_rope slices, so a compute unit keeps about
+//    four slices per wave in flight.  S^T = [c k_rope] q_lat^T on 16x16x32 MFMA
+//    (a trailing 16-wide rope chunk zero-padded to 32) with the latent read from
+//    LDS; P^T is the accumulator as it stands; O^T += V^T P^T on 16x16x16 MFMA
+//    with V^T read transposed (ds_read_b64_tr_b16) from the same latent slice,
+//    since values share the latent with the un-rotated key.  A wave only reads
+//    rows it copied itself, so the loop has no workgroup barrier.
+//  * waves 4-7 ("helpers") absorb the query while the first copies are in
+//    flight, two heads each: their first W_UK and q_nope loads go out before
+//    the cache length is known and before the streaming waves' copies (rows
+//    read as they are stored, fp32 sums of bf16 pairs, the result kept as a
+//    bf16 hi/lo pair so that the MFMA score sees ~16 mantissa bits); then they
+//    request the W_UV rows of their first head and wait; after the stream each
+//    applies out^T = W_UV o_lat^T on MFMA for its heads (o_lat as a bf16 hi/lo
+//    pair), one head per product with the other heads' columns of the o_lat
+//    operand zero.
+// A sequence of several chunks is merged inside the same launch: every chunk
+// stores its normalised o_lat and log2-sum-exp with device-coherent stores,
+// waits for them to complete and counts itself done on the sequence's counter;
+// the workgroup that finishes last (the counter's old value is n - 1) reads the
+// partials back with device-coherent loads, merges them by their
+// log2-sum-exps, applies W_UV and returns the counter to zero.  Nothing waits
+// on another workgroup, so no schedule can deadlock.
 #include <hip/hip_runtime.h>
 
 #include "attn_internal.h"
@@ -35,6 +45,7 @@ namespace attn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
@@ -43,12 +54,14 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kHeadsPad = 16;
-constexpr int kWaves = kDecodeWaves;     // 4
-constexpr int kThreads = 64 * kWaves;
+constexpr int kWaves = kDecodeWaves;     // 4 streaming waves
+constexpr int kHelpers = 4;              // helper waves
+constexpr int kThreads = 64 * (kWaves + kHelpers);
 constexpr int kSlice = 16;               // tokens per wave slice
 constexpr int kStep = kSlice * kWaves;   // tokens per workgroup step
-constexpr int kStages = 3;
 constexpr float kRescaleSlack = 8.f;     // log2 units the reference max may trail the true max
+// Cache policy of the ring copies: non-temporal (the cache is read once per call).
+constexpr int kStreamPolicy = 2;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -75,6 +88,7 @@ __device__ __forceinline__ float sum_xor32(float x) { const float2 p = pair_xor3
 __device__ __forceinline__ float rescale(float m, float M) { return m == kNegInf ? 0.f : exp2_fast(m - M); }
 __device__ __forceinline__ int clamp_len(int L, int T_max) { return L < 0 ? 0 : (L > T_max ? T_max : L); }
 __device__ __forceinline__ float bf16_to_f32(u16 x) { return __builtin_bit_cast(float, (unsigned)x << 16); }
+__device__ __forceinline__ u16 f32_to_bf16(float x) { return __builtin_bit_cast(u16, (__bf16)x); }
 
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -92,6 +106,19 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const u16* p) {
 }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// Device-coherent 32-bit accesses of the cross-workgroup merge: relaxed atomics
+// at agent scope, which gfx950 performs at the device's coherence point (they
+// bypass the per-XCD L2 for reads and write through it), so a workgroup on
+// another XCD sees them once they have completed.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __builtin_bit_cast(unsigned, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __builtin_bit_cast(float, __hip_atomic_load(reinterpret_cast<const unsigned*>(p), __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+}
 
 // Latent slice layout in LDS: 16 rows of R bf16, 16-byte chunk c of row r at
 // chunk position c ^ swz<R>(r).  gfx950's LDS serves 256 bytes per clock (16
@@ -117,6 +144,14 @@ struct Cfg {
   static constexpr int kRInst = (kSlice * DR * 2 + 1023) / 1024;
   static constexpr int kR = kRInst * 512;     // rope slice (u16), padded to whole copies
   static constexpr int kInstPerSlice = kCInst + kRInst;
+  // ring depth: as many stages as fit next to the absorbed query and the merge
+  // buffers in about 158 KB of LDS, at most 5
+  static constexpr int kStageBytes = kWaves * (kC + kR) * 2;
+  static constexpr int kQlatBytes = 2 * kHeadsPad * RW * 2;
+  static constexpr int kOlatBytes = 2 * kHeadsPad * R * 2;
+  static constexpr int kFit = (158 * 1024 - kQlatBytes - kOlatBytes) / kStageBytes;
+  static constexpr int kStages = kFit > 5 ? 5 : kFit;
+  static_assert(kStages >= 3, "ring depth");
 };
 
 // Per-lane constants of the slice copies and reads.
@@ -150,6 +185,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
                                            0x00020000);
 }
 
+// Copies the 16-row slice at t0 (rows past lim read as zeros) into (cdst, rdst).
 template <int R, int DR>
 __device__ __forceinline__ void issue_slice(u16* cdst, u16* rdst, const MlaDecodeArgs& a, int b, int t0, int lim,
                                             const Lanes<R, DR>& ln) {
@@ -159,11 +195,11 @@ __device__ __forceinline__ void issue_slice(u16* cdst, u16* rdst, const MlaDecod
 #pragma unroll
   for (int q = 0; q < C::kCInst; ++q)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (__attribute__((address_space(3))) void*)(cdst + 512 * q), 16,
-                                             ln.c_voff[q], 0, 0, 0);
+                                             ln.c_voff[q], 0, 0, kStreamPolicy);
 #pragma unroll
   for (int q = 0; q < C::kRInst; ++q)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void*)(rdst + 512 * q), 16,
-                                             16 * (64 * q + ln.lane), 0, 0, 0);
+                                             16 * (64 * q + ln.lane), 0, 0, kStreamPolicy);
 }
 
 // vmcnt(n): wait until at most n of this wave's vector memory operations are outstanding.
@@ -178,76 +214,6 @@ struct WaveState {
   f32x4 o[R / 16];  // O^T[16w + 4grp + i][head row]
   float m, lsum;    // reference max (scaled, log2) and this lane's part of the row sum
 };
-
-// ---------------------------------------------------------------------------
-// q_lat[b][hl][h][0:R] = hi / lo bf16 parts of W_UK[h]^T q_nope[b,h] (fp32 sum);
-// q_lat[b][0][h][R:R+DR] = q_rope[b,h], q_lat[b][1][h][R:] = 0; padded heads
-// h in [H, 16) are zero.  Grid (16, B), 256 threads, one workgroup per (head,
-// sequence): thread t owns latent columns 8(t % (R/8)) .. +8 (16-byte loads of
-// W_UK rows, which stay in L2 across the sequences) and every P-th row (P =
-// 2048 / R); a thread's loads are issued together before the first use, and
-// the P partial sums meet in LDS.
-// Rows [i0, i0 + U*P) of this thread's part: U loads of 16 bytes (row-clamped,
-// so there is no branch between them) issued before any use.
-template <int R, int U, int P>
-__device__ __forceinline__ void absorb_rows(float (&acc)[8], const u16* wk, const u16* qn, int i0, int dn) {
-  u16x8 wv[U];
-  u16 qv[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int i = min(i0 + u * P, dn - 1);
-    wv[u] = *reinterpret_cast<const u16x8*>(wk + (size_t)i * R);
-    qv[u] = qn[i];
-  }
-  asm volatile("" ::: "memory");  // issue the whole batch before the first use
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const float q = i0 + u * P < dn ? bf16_to_f32(qv[u]) : 0.f;  // clamped rows count 0
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = fmaf(bf16_to_f32(wv[u][e]), q, acc[e]);
-  }
-}
-
-template <int R, int DR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void mla_absorb(MlaDecodeArgs a) {
-  constexpr int RW = R + DR;
-  constexpr int OCT = R / 8;    // column octets
-  constexpr int P = 256 / OCT;  // row parts
-  __shared__ float red[P][R];
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int oct = tid % OCT, part = tid / OCT;
-  u16* ql = static_cast<u16*>(a.q_lat) + ((size_t)b * 2 * kHeadsPad + h) * RW;
-  if (h >= a.H) {
-    for (int e = tid; e < RW; e += 256) ql[e] = ql[kHeadsPad * RW + e] = 0;
-    return;
-  }
-  const u16* wk = static_cast<const u16*>(a.w_uk) + (size_t)h * a.dn * R + 8 * oct;
-  const u16* qn = static_cast<const u16*>(a.q_nope) + ((size_t)b * a.H + h) * a.dn;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const int rows_per_part = (a.dn + P - 1) / P;  // uniform: pick the batch that covers it
-  if (rows_per_part <= 2) absorb_rows<R, 2, P>(acc, wk, qn, part, a.dn);
-  else if (rows_per_part <= 4) absorb_rows<R, 4, P>(acc, wk, qn, part, a.dn);
-  else if (rows_per_part <= 8) absorb_rows<R, 8, P>(acc, wk, qn, part, a.dn);
-  else
-    for (int i0 = part; i0 < a.dn; i0 += 16 * P) absorb_rows<R, 16, P>(acc, wk, qn, i0, a.dn);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) red[part][8 * oct + e] = acc[e];
-  __syncthreads();
-  for (int j = tid; j < R; j += 256) {
-    float v = 0.f;
-#pragma unroll
-    for (int q = 0; q < P; ++q) v += red[q][j];
-    const __bf16 hi = (__bf16)v;
-    ql[j] = __builtin_bit_cast(u16, hi);
-    ql[kHeadsPad * RW + j] = __builtin_bit_cast(u16, (__bf16)(v - (float)hi));
-  }
-  const u16* qr = static_cast<const u16*>(a.q_rope) + ((size_t)b * a.H + h) * DR;
-  for (int e = tid; e < DR; e += 256) {
-    ql[R + e] = qr[e];
-    ql[kHeadsPad * RW + R + e] = 0;
-  }
-}
 
 // One 16-token slice from (cs, rs): scores, online softmax, O^T update.
 template <int R, int DR>
@@ -313,52 +279,323 @@ __device__ __forceinline__ void slice_step(WaveState<R, DR>& st, const u16* cs, 
   for (int w = 0; w < C::DW; ++w) st.o[w] = mfma_16x16x16(lds_read_tr16(cs + (ln.v_off ^ (16 * w))), pop, st.o[w]);
 }
 
+// ---------------------------------------------------------------------------
+// Helper work.
+//
+// Absorb: q_lat[hl][h][0:R] = hi / lo bf16 parts of W_UK[h]^T q_nope[b,h]
+// (fp32 sums), q_lat[0][h][R:R+DR] = q_rope[b,h], q_lat[1][h][R:] = 0; padding
+// heads h in [H, 16) are zero.  The four helper waves do it, helper j the heads
+// j + 4i two at a time (j and j + 4, then j + 8 and j + 12); lane (o, p) owns
+// latent octet o (columns 8o .. 8o+7, R/8 octets) and the kAbsorbRows
+// consecutive W_UK rows from p * kAbsorbRows of a round (P = 64 / (R/8) phases
+// per round).  All loads of a round -- the W_UK rows and the matching q_nope
+// elements of both heads -- are requested before the first is used, through
+// buffer resources that end with the head's rows, so rows past nope_head_dim
+// read as zeros.  Two rows at a time meet the q_nope pair in one
+// v_dot2_f32_bf16 per column; the P phases meet by lane exchanges.
+constexpr int kAbsorbRows = 12;
+
+template <int R>
+struct AbsorbLoads {
+  u16x8 w[2][kAbsorbRows];            // W_UK rows of the two heads (8 latent columns each)
+  u16x8 q[2][(kAbsorbRows + 7) / 8];  // q_nope elements of those rows (and a few past them)
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bytes_rsrc(const void* p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
+
+// Requests the loads of round k0 (rows k0 + p * kAbsorbRows ..) of heads h0, h1.
+template <int R>
+__device__ __forceinline__ void absorb_issue(AbsorbLoads<R>& ld, const MlaDecodeArgs& a, int b, int h0, int h1, int k0,
+                                             int lane) {
+  constexpr int OCT = R / 8;
+  const int o = lane % OCT, p = lane / OCT;
+  const int r0 = k0 + p * kAbsorbRows;
+  // one per-lane offset per operand kind; the row step is the (uniform) scalar offset
+  const int wv = (r0 * R + 8 * o) * 2, qv = r0 * 2;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int h = hh ? h1 : h0;
+    const auto wr = bytes_rsrc(static_cast<const u16*>(a.w_uk) + (size_t)h * a.dn * R, a.dn * R * 2);
+    const auto qr = bytes_rsrc(static_cast<const u16*>(a.q_nope) + ((size_t)b * a.H + h) * a.dn, a.dn * 2);
+#pragma unroll
+    for (int t = 0; t < kAbsorbRows; ++t)
+      ld.w[hh][t] = __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(wr, wv, t * R * 2, 0));
+#pragma unroll
+    for (int t = 0; t < (kAbsorbRows + 7) / 8; ++t)
+      ld.q[hh][t] = __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, qv, 16 * t, 0));
+  }
+}
+
+template <int R>
+__device__ __forceinline__ void absorb_dot(float (&acc)[2][8], const AbsorbLoads<R>& ld) {
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int t = 0; t < kAbsorbRows; t += 2) {
+      const bf16x2 q2 = __builtin_bit_cast(bf16x2, (unsigned)ld.q[hh][t / 8][t % 8] |
+                                                       ((unsigned)ld.q[hh][t / 8][t % 8 + 1] << 16));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bf16x2 w2 = __builtin_bit_cast(bf16x2, (unsigned)ld.w[hh][t][e] | ((unsigned)ld.w[hh][t + 1][e] << 16));
+        acc[hh][e] = __builtin_amdgcn_fdot2_f32_bf16(w2, q2, acc[hh][e], false);
+      }
+    }
+}
+
+// Writes the padding heads and the rope part of q_lat for helper j's heads
+// (j + 4i); rope[i] holds element `lane` of head j + 4i's q_rope (loaded with
+// the absorb's other operands, so that nothing here waits on memory).
 template <int R, int DR>
-__global__ __launch_bounds__(kThreads) void mla_decode_fused(MlaDecodeArgs a) {
+__device__ void absorb_fixed_parts(const MlaDecodeArgs& a, int j, int lane, const u16 (&rope)[4], u16* qlat) {
+  constexpr int RW = R + DR;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = j + i * kHelpers;
+    u16* hi = qlat + h * RW;
+    u16* lo = qlat + (kHeadsPad + h) * RW;
+    if (h >= a.H) {
+      for (int e = lane; e < RW; e += 64) hi[e] = lo[e] = 0;
+    } else if (lane < DR) {
+      hi[R + lane] = rope[i];
+      lo[R + lane] = 0;
+    }
+  }
+}
+
+// Sums the phases of the two heads' accumulators and writes their q_lat rows.
+template <int R, int DR>
+__device__ __forceinline__ void absorb_store(float (&acc)[2][8], int h0, int h1, bool two, int lane, u16* qlat) {
+  constexpr int RW = R + DR;
+  constexpr int OCT = R / 8;
+  const int o = lane % OCT, p = lane / OCT;
+#pragma unroll
+  for (int off = OCT; off < 64; off <<= 1)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] += __shfl_xor(acc[hh][e], off);
+  if (p == 0) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (hh == 1 && !two) break;
+      const int h = hh ? h1 : h0;
+      u16x8 vh, vl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 x = (__bf16)acc[hh][e];
+        vh[e] = __builtin_bit_cast(u16, x);
+        vl[e] = f32_to_bf16(acc[hh][e] - (float)x);
+      }
+      *reinterpret_cast<u16x8*>(qlat + h * RW + 8 * o) = vh;
+      *reinterpret_cast<u16x8*>(qlat + (kHeadsPad + h) * RW + 8 * o) = vl;
+    }
+  }
+}
+
+// W_UV: out[b,h,i] = sum_j W_UV[h][i][j] o_lat[h][j] on 16x16x32 MFMA,
+// out^T[16ib + 4grp + r][col] = sum_k A[i][k] B[k][col] with A = the W_UV[h] rows
+// (as stored: 8 consecutive j per lane) and B = o_lat^T (its bf16 hi and lo
+// parts, two products) with every column but h zeroed, so that column h of the
+// product is head h's output.  Helper j takes heads j, j + 4, ...; the A
+// operands of a batch of 16-row blocks of one head are requested together (the
+// first batch while the stream runs).
+template <int R>
+struct UvBatch {
+  static constexpr int kBlocks = R >= 256 ? 3 : 6;  // 96 registers of operands
+  bf16x8 a[kBlocks][R / 32];
+};
+
+template <int R>
+__device__ __forceinline__ void load_uv(UvBatch<R>& u, const MlaDecodeArgs& a, int h, int ib0, int lane) {
+  const int row = lane & 15, grp = lane >> 4;
+  const u16* base = static_cast<const u16*>(a.w_uv) + (size_t)h * a.dv * R;
+#pragma unroll
+  for (int ib = 0; ib < UvBatch<R>::kBlocks; ++ib) {
+    const int i = min(16 * (ib0 + ib) + row, a.dv - 1);  // rows past dv: clamped, never stored
+#pragma unroll
+    for (int k = 0; k < R / 32; ++k)
+      u.a[ib][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(base + (size_t)i * R + 32 * k + 8 * grp));
+  }
+}
+
+// Applies a loaded batch (head h, blocks ib0..) to o_lat (olat: [2][16][R] bf16
+// hi and lo parts in LDS) and writes the head's output rows.
+template <int R>
+__device__ __forceinline__ void apply_uv(const UvBatch<R>& u, const MlaDecodeArgs& a, const u16* olat, int b, int h,
+                                         int ib0, int lane) {
+  const int col = lane & 15, grp = lane >> 4;
+  const bool mine = col == h;
+  constexpr int NB = UvBatch<R>::kBlocks;
+  const bf16x8 z = {};
+  f32x4 acc[NB];
+#pragma unroll
+  for (int ib = 0; ib < NB; ++ib) acc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < R / 32; ++k) {
+    const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(olat + col * R + 32 * k + 8 * grp));
+    const bf16x8 bl =
+        __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(olat + (kHeadsPad + col) * R + 32 * k + 8 * grp));
+    const bf16x8 oh = mine ? bh : z, ol = mine ? bl : z;
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib) {
+      acc[ib] = mfma_16x16x32(u.a[ib][k], oh, acc[ib]);
+      acc[ib] = mfma_16x16x32(u.a[ib][k], ol, acc[ib]);
+    }
+  }
+  if (mine) {
+    const size_t o0 = ((size_t)b * a.H + h) * a.dv;
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib) {
+      const int i = 16 * (ib0 + ib) + 4 * grp;
+      if (i < a.dv) {  // dv is a multiple of 16: a block is valid as a whole
+        if (a.out_bf16) {
+          u16x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = f32_to_bf16(acc[ib][r]);
+          *reinterpret_cast<u16x4*>(static_cast<u16*>(a.out) + o0 + i) = v;
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o0 + i) = acc[ib];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int R, int DR>
+__global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
   using C = Cfg<R, DR>;
   constexpr int RW = C::RW;
-  // three ring stages per wave, each a distinct LDS variable so the compiler can
-  // tell the copies in flight from the reads of the resident stage
-  // per wave and stage: the latent slice and the rope slice
+  constexpr int S = C::kStages;
+  // ring stages, each a distinct LDS variable so that the compiler can tell the
+  // copies in flight from the reads of the resident stage
   __shared__ __attribute__((aligned(1024))) u16 stg0[kWaves][C::kC];
   __shared__ __attribute__((aligned(1024))) u16 stg1[kWaves][C::kC];
   __shared__ __attribute__((aligned(1024))) u16 stg2[kWaves][C::kC];
+  __shared__ alignas(S > 3 ? 1024 : 16) u16 stg3[S > 3 ? kWaves : 1][S > 3 ? C::kC : 8];
+  __shared__ alignas(S > 4 ? 1024 : 16) u16 stg4[S > 4 ? kWaves : 1][S > 4 ? C::kC : 8];
   __shared__ __attribute__((aligned(1024))) u16 rop0[kWaves][C::kR];
   __shared__ __attribute__((aligned(1024))) u16 rop1[kWaves][C::kR];
   __shared__ __attribute__((aligned(1024))) u16 rop2[kWaves][C::kR];
-  // epilogue scratch: one [16 heads][R] fp32 output slice per wave, two in each
-  // of stages 0 and 1; m and l per wave and head in stage 2
+  __shared__ alignas(S > 3 ? 1024 : 16) u16 rop3[S > 3 ? kWaves : 1][S > 3 ? C::kR : 8];
+  __shared__ alignas(S > 4 ? 1024 : 16) u16 rop4[S > 4 ? kWaves : 1][S > 4 ? C::kR : 8];
+  __shared__ __attribute__((aligned(16))) u16 qlat[2 * kHeadsPad * RW];  // [hi, lo][16][RW]
+  __shared__ __attribute__((aligned(16))) u16 olat[2 * kHeadsPad * R];   // [hi, lo][16][R]
+  __shared__ float lse_s[kHeadsPad];
+  __shared__ int last_s;
+  // after the stream: one [16 heads][R] fp32 output slice per streaming wave,
+  // two in each of stages 0 and 1; m and l per wave and head in stage 2
   static_assert(2 * kHeadsPad * R * 4 == (int)sizeof(stg0), "two output slices per stage");
   static_assert(2 * kWaves * kHeadsPad * 4 <= (int)sizeof(stg2), "m, l scratch");
 
   const int s = blockIdx.x, b = blockIdx.y;
-  const int L = clamp_len(a.lens[b], a.T_max);
-  const int n_chunks = (L + a.split - 1) / a.split;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const Lanes<R, DR> ln(tid & 63);
-
-  // The stages start zeroed: rows past the chunk end are read (with P = 0) by
-  // the transposed V product, and uninitialised LDS could hold NaN patterns.
-  // (Done while the length is in flight.)
-  {
-    const u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-    u16* const bufs[6] = {&stg0[0][0], &stg1[0][0], &stg2[0][0], &rop0[0][0], &rop1[0][0], &rop2[0][0]};
-#pragma unroll
-    for (int k = 0; k < 6; ++k)
-      for (int e = 8 * tid; e < kWaves * (k < 3 ? C::kC : C::kR); e += 8 * kThreads)
-        *reinterpret_cast<u16x8*>(bufs[k] + e) = z;
+  const int lane = tid & 63;
+  const bool streamer = wave < kWaves;
+  const int j = wave - kWaves;  // helper index
+  // a helper's first round of absorb loads does not depend on the cache length:
+  // it goes out while the length is read
+  AbsorbLoads<R> ld;
+  if (!streamer && j < a.H) absorb_issue<R>(ld, a, b, j, j + kHelpers < a.H ? j + kHelpers : j, 0, lane);
+  const int L = clamp_len(a.lens[b], a.T_max);
+  const int n_chunks = (L + a.split - 1) / a.split;
+  if (s >= n_chunks) {  // past the sequence; an empty sequence gets zeros from chunk 0
+    wait_vmem();
+    if (n_chunks == 0 && s == 0)
+      for (int e = tid; e < a.H * a.dv; e += kThreads) {
+        if (a.out_bf16) static_cast<u16*>(a.out)[(size_t)b * a.H * a.dv + e] = 0;
+        else static_cast<float*>(a.out)[(size_t)b * a.H * a.dv + e] = 0.f;
+      }
+    return;
   }
-  if (s >= n_chunks) return;  // past the sequence (an empty one is zeroed by the merge)
   const int c0 = s * a.split, c1 = min(c0 + a.split, L);
-  const int n_steps = (c1 - c0 + kStep - 1) / kStep;
-  const int tw0 = c0 + kSlice * wave;  // first token of this wave's first slice
-  __syncthreads();
-  // q_lat^T as the B operand: lane holds q_lat[head row][32k + 8grp ..+8] (hi and lo);
-  // requested after the first two slices (their copies are then already in flight)
-  const u16* qlat = static_cast<const u16*>(a.q_lat) + (size_t)b * 2 * kHeadsPad * RW;
-  bf16x8 qhi[C::KC], qlo[C::KC], qr32[C::RC > 0 ? C::RC : 1], qr16 = {};
-  auto load_q = [&]() {
+  float* mw = reinterpret_cast<float*>(&stg2[0][0]);  // [waves][16]
+  float* lw = mw + kWaves * kHeadsPad;                // [waves][16]
+  auto slice = [&](int w) {
+    return reinterpret_cast<float*>(w < 2 ? &stg0[0][0] : &stg1[0][0]) + (w & 1) * kHeadsPad * R;
+  };
+
+  WaveState<R, DR> st;
+  // W_UV operands of the wave's first head: requested by a helper while the
+  // stream runs, by a streaming wave once its ring has drained
+  UvBatch<R> uv;
+  // a streaming wave's ring stages and lane constants (made where they are used,
+  // so that they take no registers in the helpers' code)
+  auto stage_c = [&](int i) -> u16* {
+    u16* const c[5] = {stg0[wave], stg1[wave], stg2[wave], stg3[S > 3 ? wave : 0], stg4[S > 4 ? wave : 0]};
+    return c[i];
+  };
+  auto stage_r = [&](int i) -> u16* {
+    u16* const r[5] = {rop0[wave], rop1[wave], rop2[wave], rop3[S > 3 ? wave : 0], rop4[S > 4 ? wave : 0]};
+    return r[i];
+  };
+  const int tw0 = c0 + kSlice * wave;  // streaming wave: first token of its first slice
+
+  // ---- the helpers absorb the query while the streaming waves start their
+  // cache copies.  The copies go out once the helpers' first two rounds of
+  // weight reads have (a bare barrier, no wait for the loads): issued after a
+  // burst of cache copies, the weight reads waited behind the whole device's
+  // burst in the memory queues.
+  if (streamer) {
+    const Lanes<R, DR> ln(lane);
+    __builtin_amdgcn_s_barrier();  // (0)
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i) issue_slice<R, DR>(stage_c(i), stage_r(i), a, b, tw0 + i * kStep, c1, ln);
+  } else {
+    constexpr int P = 64 / (R / 8);
+    constexpr int kRound = P * kAbsorbRows;  // W_UK rows per round
+    u16 rope[4] = {0, 0, 0, 0};
+    const u16* qr = static_cast<const u16*>(a.q_rope) + (size_t)b * a.H * DR + lane;
+    if (lane < DR) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (j + i * kHelpers < a.H) rope[i] = qr[(j + i * kHelpers) * DR];
+    }
+    // the first pair (j, j + 4): its first round is in flight; barrier (0) after
+    // the second round's loads are issued (or after the first round)
+    {
+      const int h0 = j, h1 = j + kHelpers;
+      const bool have = h0 < a.H, two = h1 < a.H;
+      float acc[2][8] = {};
+      int k0 = 0;
+      if (have) {
+        absorb_dot<R>(acc, ld);
+        k0 = kRound;
+        if (k0 < a.dn) absorb_issue<R>(ld, a, b, h0, two ? h1 : h0, k0, lane);
+      }
+      __builtin_amdgcn_s_barrier();  // (0)
+      absorb_fixed_parts<R, DR>(a, j, lane, rope, qlat);
+      if (have) {
+        for (; k0 < a.dn; k0 += kRound) {
+          absorb_dot<R>(acc, ld);
+          if (k0 + kRound < a.dn) absorb_issue<R>(ld, a, b, h0, two ? h1 : h0, k0 + kRound, lane);
+        }
+        absorb_store<R, DR>(acc, h0, h1, two, lane, qlat);
+      }
+    }
+    // further pairs (more than 8 heads)
+    for (int h0 = j + 2 * kHelpers; h0 < a.H; h0 += 2 * kHelpers) {
+      const int h1 = h0 + kHelpers;
+      const bool two = h1 < a.H;
+      float acc[2][8] = {};
+      absorb_issue<R>(ld, a, b, h0, two ? h1 : h0, 0, lane);
+      for (int k0 = 0; k0 < a.dn; k0 += kRound) {
+        absorb_dot<R>(acc, ld);
+        if (k0 + kRound < a.dn) absorb_issue<R>(ld, a, b, h0, two ? h1 : h0, k0 + kRound, lane);
+      }
+      absorb_store<R, DR>(acc, h0, h1, two, lane, qlat);
+    }
+  }
+  __syncthreads();  // (1) q_lat is complete
+  if (streamer) {
+    // ---- stream the wave's slices through the ring
+    const Lanes<R, DR> ln(lane);
+    const int n_steps = (c1 - c0 + kStep - 1) / kStep;
+    // q_lat^T as the B operand: lane holds q_lat[head row][32k + 8grp ..+8] (hi and lo)
+    bf16x8 qhi[C::KC], qlo[C::KC], qr32[C::RC > 0 ? C::RC : 1], qr16 = {};
 #pragma unroll
     for (int k = 0; k < C::KC; ++k) {
       qhi[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qlat + ln.row * RW + 32 * k + 8 * ln.grp));
@@ -373,190 +610,145 @@ __global__ __launch_bounds__(kThreads) void mla_decode_fused(MlaDecodeArgs a) {
           __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qlat + ln.row * RW + R + 32 * C::RC + 8 * ln.grp));
       if (ln.grp < 2) qr16 = v;
     }
-    // wait here (this also covers the first two slices' copies, issued earlier):
-    // the operands are then known to be in registers everywhere in the loop
-    wait_vmem();
-  };
-
-  // ---- stream the wave's slices through the ring
-  WaveState<R, DR> st;
 #pragma unroll
-  for (int w = 0; w < C::DW; ++w) st.o[w] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = kNegInf;
-  st.lsum = 0.f;
-  const float c = a.scale_log2e;
-  // Step k: copy slice k+2 into stage (k+2) % 3, wait for slice k, consume stage
-  // k % 3.  The loop starts at k = -2 (copies only), so every copy comes from
-  // the same three places in the loop body: the compiler then tracks which
-  // stage each copy in flight belongs to across the back edge and adds no
-  // waits beyond this one.  Copies of slices past the chunk read nothing.
-  auto step = [&](int k, const u16* cs, const u16* rs, u16* cn, u16* rn) {
-    issue_slice<R, DR>(cn, rn, a, b, tw0 + (k + 2) * kStep, c1, ln);
-    if (k >= 0 && k < n_steps) {
-      wait_vmcnt<2 * C::kInstPerSlice>();
-      slice_step<R, DR>(st, cs, rs, qhi, qlo, qr32, qr16, tw0 + k * kStep, c1, c, ln);
+    for (int w = 0; w < C::DW; ++w) st.o[w] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m = kNegInf;
+    st.lsum = 0.f;
+    const float c = a.scale_log2e;
+    // Step k: copy slice k + S - 1 into stage (k + S - 1) % S, wait for slice
+    // k, consume stage k % S.  The body is unrolled over the S stages, so every
+    // copy comes from the same S places in the loop: the compiler then tracks
+    // which stage each copy in flight belongs to across the back edge and adds
+    // no waits beyond this one.  Copies of slices past the chunk read nothing.
+    for (int k = 0; k < n_steps; k += S) {
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        const int kk = k + i;
+        issue_slice<R, DR>(stage_c((i + S - 1) % S), stage_r((i + S - 1) % S), a, b, tw0 + (kk + S - 1) * kStep, c1,
+                           ln);
+        if (kk < n_steps) {
+          wait_vmcnt<(S - 1) * C::kInstPerSlice>();
+          slice_step<R, DR>(st, stage_c(i), stage_r(i), qhi, qlo, qr32, qr16, tw0 + kk * kStep, c1, c, ln);
+        }
+      }
     }
-  };
-  // the iteration that loads q_lat, as a value the compiler does not fold (a
-  // first iteration peeled off the loop would end with a wait for every copy)
-  const int k_q = __builtin_amdgcn_readfirstlane(n_steps > 0 ? -2 : -1);
-  for (int k = -2; k < n_steps; k += kStages) {  // k = -2, 1, 4, ... : stage (k+2) % 3 = 0
-    step(k, stg1[wave], rop1[wave], stg0[wave], rop0[wave]);
-    step(k + 1, stg2[wave], rop2[wave], stg1[wave], rop1[wave]);
-    if (k == k_q) load_q();
-    step(k + 2, stg0[wave], rop0[wave], stg2[wave], rop2[wave]);
+    wait_vmem();  // the copies past the end (zeros) land before the stages are reused
+    st.lsum = sum_xor32(sum_xor16(st.lsum));
   }
-  wait_vmem();  // the copies past the end (zeros) land before the stages are reused
-  st.lsum = sum_xor32(sum_xor16(st.lsum));
+  if (!streamer && j < a.H) load_uv<R>(uv, a, j, 0, lane);
 
-  // ---- merge the four waves (LDS, reusing the stages)
+  // ---- merge the four streaming waves (LDS, reusing the stages)
   // Each wave writes its scaled O^T into its own [16][R] slice; 16-byte unit u
   // of head row h sits at unit position u ^ (h & 15), so the 16 rows of one
   // write land on distinct banks.
-  __syncthreads();
-  float* mw = reinterpret_cast<float*>(&stg2[0][0]);  // [waves][16]
-  float* lw = mw + kWaves * kHeadsPad;                // [waves][16]
-  auto slice = [&](int w) {
-    return reinterpret_cast<float*>(w < 2 ? &stg0[0][0] : &stg1[0][0]) + (w & 1) * kHeadsPad * R;
-  };
-  if (ln.grp == 0) {
-    mw[wave * kHeadsPad + ln.row] = st.m;
-    lw[wave * kHeadsPad + ln.row] = st.lsum;
+  __syncthreads();  // (2) every streaming wave is done with its ring
+  const int row = lane & 15, grp = lane >> 4;
+  if (streamer && grp == 0) {
+    mw[wave * kHeadsPad + row] = st.m;
+    lw[wave * kHeadsPad + row] = st.lsum;
   }
-  __syncthreads();
-  {
+  __syncthreads();  // (3)
+  if (streamer) {
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w * kHeadsPad + ln.row]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w * kHeadsPad + row]);
     float Lt = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) Lt += rescale(mw[w * kHeadsPad + ln.row], M) * lw[w * kHeadsPad + ln.row];
+    for (int w = 0; w < kWaves; ++w) Lt += rescale(mw[w * kHeadsPad + row], M) * lw[w * kHeadsPad + row];
     const float f = rescale(st.m, M) / Lt;
-#pragma unroll
-    for (int w = 0; w < C::DW; ++w) st.o[w] *= f;
-  }
-  {
-    float* ob = slice(wave) + ln.row * R;
+    float* ob = slice(wave) + row * R;
 #pragma unroll
     for (int dw = 0; dw < C::DW; ++dw)
-      *reinterpret_cast<f32x4*>(ob + 4 * ((4 * dw + ln.grp) ^ ln.row)) = st.o[dw];
+      *reinterpret_cast<f32x4*>(ob + 4 * ((4 * dw + grp) ^ row)) = st.o[dw] * f;
+    if (wave == 0 && grp == 0) lse_s[row] = M + __log2f(Lt);
   }
-  __syncthreads();
+  __syncthreads();  // (4)
 
-  // publish this chunk's normalised o_lat (the sum of the four slices) and
-  // log2-sum-exp (ordered for the merge kernel by the kernel boundary)
-  const size_t row0 = (size_t)b * a.H;
+  // this chunk's normalised o_lat (the sum of the four slices): as the hi / lo
+  // operand of W_UV when it is the sequence's only chunk, else to the workspace
+  const bool single = n_chunks == 1;
+  const size_t prow = ((size_t)b * a.n_splits + s) * a.H;  // partial rows of this chunk
   for (int e = tid; e < a.H * (R / 4); e += kThreads) {
     const int h = e / (R / 4), d4 = e - h * (R / 4);
     const int off = h * R + 4 * (d4 ^ (h & 15));
     f32x4 v = *reinterpret_cast<const f32x4*>(slice(0) + off);
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) v += *reinterpret_cast<const f32x4*>(slice(w) + off);
-    *reinterpret_cast<f32x4*>(a.o_part + ((row0 + h) * a.n_splits + s) * R + 4 * d4) = v;
+    if (single) {
+      u16x4 vh, vl;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const __bf16 x = (__bf16)v[r];
+        vh[r] = __builtin_bit_cast(u16, x);
+        vl[r] = f32_to_bf16(v[r] - (float)x);
+      }
+      *reinterpret_cast<u16x4*>(olat + h * R + 4 * d4) = vh;
+      *reinterpret_cast<u16x4*>(olat + (kHeadsPad + h) * R + 4 * d4) = vl;
+    } else {
+      float* dst = a.o_part + (prow + h) * R + 4 * d4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) store_coherent(dst + r, v[r]);
+    }
   }
-  for (int h = tid; h < a.H; h += kThreads) {
-    float M = kNegInf;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w * kHeadsPad + h]);
-    float Lt = 0.f;
-    for (int w = 0; w < kWaves; ++w) Lt += rescale(mw[w * kHeadsPad + h], M) * lw[w * kHeadsPad + h];
-    a.lse[(row0 + h) * a.n_splits + s] = M + __log2f(Lt);
+  if (!single) {
+    for (int h = tid; h < a.H; h += kThreads) store_coherent(a.lse + prow + h, lse_s[h]);
+    wait_vmem();      // this thread's partial stores have completed
+    __syncthreads();  // (5) ... and every thread's
+    if (tid == 0) {
+      const unsigned before = __hip_atomic_fetch_add(a.done + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_s = before == (unsigned)(n_chunks - 1);
+    }
+    __syncthreads();  // (6)
+    if (!last_s) return;
+    // the last chunk to finish: merge every chunk's partial by its log2-sum-exp
+    if (tid == 0) __hip_atomic_store(a.done + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const size_t row0 = (size_t)b * a.n_splits * a.H;
+    for (int e = tid; e < a.H * R; e += kThreads) {
+      const int h = e / R, d = e - h * R;
+      float M = kNegInf, Ssum = 0.f, acc = 0.f;
+      for (int k0 = 0; k0 < n_chunks; k0 += 8) {
+        float lv[8], ov[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int k = min(k0 + u, n_chunks - 1);
+          lv[u] = load_coherent(a.lse + row0 + (size_t)k * a.H + h);
+          ov[u] = load_coherent(a.o_part + (row0 + (size_t)k * a.H + h) * R + d);
+        }
+        // chunks past the end (loaded clamped) weigh 2^-inf = 0; entry 0 of the
+        // first batch is a real chunk, so M is finite before any of them
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (k0 + u >= n_chunks) lv[u] = kNegInf;
+          const float Mn = fmaxf(M, lv[u]);
+          const float f = rescale(M, Mn), w = exp2_fast(lv[u] - Mn);
+          Ssum = Ssum * f + w;
+          acc = acc * f + w * ov[u];
+          M = Mn;
+        }
+      }
+      const float v = acc / Ssum;
+      const __bf16 x = (__bf16)v;
+      olat[h * R + d] = __builtin_bit_cast(u16, x);
+      olat[(kHeadsPad + h) * R + d] = f32_to_bf16(v - (float)x);
+    }
   }
-}
+  __syncthreads();  // (7) o_lat is in LDS
 
-// ---------------------------------------------------------------------------
-// out[b,h] = W_UV[h] o_lat[b,h], with o_lat the log2-sum-exp merge of the
-// sequence's chunk partials.  Grid (H, B), 256 threads.  Thread i < v_head_dim
-// owns output row i: its W_UV row (R/8 loads of 16 bytes) is requested first,
-// so it is in flight while threads j < R merge latent column j; the dot product
-// then reads o_lat from LDS (the same address in every lane).  A sequence with
-// an empty cache gets zeros.
-template <int R>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void mla_merge_wuv(MlaDecodeArgs a) {
-  constexpr int OCT = R / 8;
-  constexpr int U = OCT < 16 ? OCT : 16;  // row loads in flight per batch
-  __shared__ __attribute__((aligned(16))) float olat[R];
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int L = clamp_len(a.lens[b], a.T_max);
-  const int n = (L + a.split - 1) / a.split;
-  const size_t oi0 = ((size_t)b * a.H + h) * a.dv;
-  if (n == 0) {
-    for (int i = tid; i < a.dv; i += 256) {
-      if (a.out_bf16) static_cast<u16*>(a.out)[oi0 + i] = 0;
-      else static_cast<float*>(a.out)[oi0 + i] = 0.f;
-    }
-    return;
-  }
-  const u16* wrow = static_cast<const u16*>(a.w_uv) + ((size_t)h * a.dv + min(tid, a.dv - 1)) * R;
-  u16x8 w8[U];
-#pragma unroll
-  for (int c = 0; c < U; ++c) w8[c] = *reinterpret_cast<const u16x8*>(wrow + 8 * c);
-  // merge: thread j < R owns column j; eight chunks in flight, running max
-  const size_t row = (size_t)b * a.H + h;
-  for (int j = tid; j < R; j += 256) {
-    const float* lse = a.lse + row * a.n_splits;
-    const float* op = a.o_part + row * a.n_splits * R + j;
-    float M = kNegInf, S = 0.f, acc = 0.f;
-    for (int k0 = 0; k0 < n; k0 += 8) {
-      float lv[8], ov[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = min(k0 + u, n - 1);
-        lv[u] = lse[k];
-        ov[u] = op[(size_t)k * R];
-      }
-      // chunks past the end (loaded clamped) get weight 2^-inf = 0; entry u = 0
-      // is always a real chunk, so M is finite before any of them
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (k0 + u >= n) lv[u] = kNegInf;
-        const float Mn = fmaxf(M, lv[u]);
-        const float f = rescale(M, Mn), w = exp2_fast(lv[u] - Mn);
-        S = S * f + w;
-        acc = acc * f + w * ov[u];
-        M = Mn;
+  // ---- out = W_UV o_lat, helper j taking heads j, j + 4, ...
+  if (!streamer) {
+    const int nb = a.dv / 16;
+    for (int h = j; h < a.H; h += kHelpers) {
+      for (int ib0 = 0; ib0 < nb; ib0 += UvBatch<R>::kBlocks) {
+        if (h != j || ib0 != 0) load_uv<R>(uv, a, h, ib0, lane);
+        apply_uv<R>(uv, a, olat, b, h, ib0, lane);
       }
     }
-    olat[j] = acc / S;
-  }
-  __syncthreads();
-  float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < U; ++c) {
-    const float4 o0 = *reinterpret_cast<const float4*>(olat + 8 * c);
-    const float4 o1 = *reinterpret_cast<const float4*>(olat + 8 * c + 4);
-    acc = fmaf(bf16_to_f32(w8[c][0]), o0.x, acc);
-    acc = fmaf(bf16_to_f32(w8[c][1]), o0.y, acc);
-    acc = fmaf(bf16_to_f32(w8[c][2]), o0.z, acc);
-    acc = fmaf(bf16_to_f32(w8[c][3]), o0.w, acc);
-    acc = fmaf(bf16_to_f32(w8[c][4]), o1.x, acc);
-    acc = fmaf(bf16_to_f32(w8[c][5]), o1.y, acc);
-    acc = fmaf(bf16_to_f32(w8[c][6]), o1.z, acc);
-    acc = fmaf(bf16_to_f32(w8[c][7]), o1.w, acc);
-  }
-  for (int c0 = U; c0 < OCT; c0 += U) {  // R = 256: the rest of the row
-#pragma unroll
-    for (int c = 0; c < U; ++c) w8[c] = *reinterpret_cast<const u16x8*>(wrow + 8 * (c0 + c));
-#pragma unroll
-    for (int c = 0; c < U; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = fmaf(bf16_to_f32(w8[c][e]), olat[8 * (c0 + c) + e], acc);
-  }
-  if (tid < a.dv) {
-    if (a.out_bf16) static_cast<__bf16*>(a.out)[oi0 + tid] = (__bf16)acc;
-    else static_cast<float*>(a.out)[oi0 + tid] = acc;
   }
 }
 
 template <int R, int DR>
 hipError_t launch_rd(const MlaDecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((mla_absorb<R, DR>), dim3(kHeadsPad, a.B), dim3(256), 0, st, a);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((mla_decode_fused<R, DR>), dim3(a.n_splits, a.B), dim3(kThreads), 0, st, a);
-  const hipError_t e2 = hipGetLastError();
-  if (e2 != hipSuccess) return e2;
-  hipLaunchKernelGGL((mla_merge_wuv<R>), dim3(a.H, a.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((mla_decode<R, DR>), dim3(a.n_splits, a.B), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -580,7 +772,7 @@ bool mla_decode_supported(int H, int r, int dR) {
 
 hipError_t launch_mla_decode(const MlaDecodeArgs& a, hipStream_t st) {
   if (!mla_decode_supported(a.H, a.r, a.dR)) return hipErrorInvalidValue;
-  if (a.split % kStep != 0) return hipErrorInvalidValue;
+  if (a.split % kStep != 0 || a.dv % 16 != 0 || a.dv > 256 || a.dn > 256 || !a.done) return hipErrorInvalidValue;
   return a.r == 64 ? launch_r<64>(a, st) : a.r == 128 ? launch_r<128>(a, st) : launch_r<256>(a, st);
 }
 

@@ -54,12 +54,15 @@ def test_workspace_sizes():
     assert attn.attn_decode_gqa_workspace_bytes(0, 32, 8, 128, 8192, 0) == 0
     assert attn.attn_decode_gqa_workspace_bytes(1, 32, 8, 128, 8192, 100) == 0  # split not a multiple of 64
     assert attn.attn_decode_mla_workspace_bytes(64, 8, 128, 48, 4096, 0) > 0
-    # MLA with fixed chunks of 512: q_lat [B, 2, 16, r + dR] bf16, partials
-    # [B*H*n_splits, r] fp32, lse [B*H*n_splits] fp32
+    # MLA with fixed chunks of 512: per-sequence done counters [B] uint32, lse
+    # [B*n_splits*H] fp32, partials [B*n_splits*H, r] fp32
     B, H, r, dR, T = 64, 8, 128, 48, 4096
     rows = B * H * (T // 512)
-    assert attn.attn_decode_mla_workspace_bytes(B, H, r, dR, T, 512) == (
-        al(B * 2 * 16 * (r + dR) * 2) + al(rows * r * 4) + al(rows * 4))
+    assert attn.attn_decode_mla_workspace_bytes(B, H, r, dR, T, 512) == al(B * 4) + al(rows * 4) + al(rows * r * 4)
+    # split 0: chunks of at least 256 positions, about one per compute unit of a
+    # 256-unit device over B * T (1024 here), whatever device is current
+    rows = B * H * (T // 1024)
+    assert attn.attn_decode_mla_workspace_bytes(B, H, r, dR, T, 0) == al(B * 4) + al(rows * 4) + al(rows * r * 4)
     assert attn.attn_decode_mla_supported(8, 128, 48)
     assert not attn.attn_decode_mla_supported(8, 100, 48)
     assert not attn.attn_decode_mla_supported(8, 128, 48, torch.float32)
@@ -215,6 +218,8 @@ def test_mla_validation():
     assert f(dR=40) == UNSUP
     assert f(ind=F32) == UNSUP
     assert f(dn=300) == UNSUP
+    assert f(dn=100) == UNSUP   # nope_head_dim: a multiple of 8
+    assert f(dv=90) == UNSUP    # v_head_dim: a multiple of 16
     assert f(c=FAKE_MIS) == UNSUP
     assert f(ws=None) == WS
     assert f(wsb=10) == WS
