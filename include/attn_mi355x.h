@@ -221,7 +221,7 @@ attn_status attn_decode_gqa_append(const void* q, const void* k_new, const void*
  *   q   [B, S, Hq, head_dim]   bf16          k, v [B, S, Hkv, head_dim]   bf16
  *   out [B, S, Hq, head_dim]   out_dtype (ATTN_BF16 or ATTN_F32)
  *
- * Supported: in_dtype ATTN_BF16, head_dim 128 (64 also built), any S >= 1,
+ * Supported: in_dtype ATTN_BF16, head_dim 64, 96 or 128, any S >= 1,
  * Hq/Hkv any divisor split.  No workspace.
  */
 attn_status attn_prefill_gqa_causal(const void* q, const void* k, const void* v, void* out, int B,
@@ -293,8 +293,9 @@ attn_status attn_prefill_gqa_cached(const void* q, const void* k_cache, const vo
  *
  * Supported (attn_decode_mla_supported): in_dtype ATTN_BF16, kv_lora_rank in
  * {64, 128, 256}, rope_dim in {16, 32, 48, 64}, H <= 16; nope_head_dim a
- * multiple of 8 in [8, 256]; v_head_dim a multiple of 16 in [16, 256].  c_kv, k_rope, w_uk, w_uv
- * and out must be 16-byte aligned (else ATTN_ERR_UNSUPPORTED).  One kernel
+ * multiple of 8 in [8, 256]; v_head_dim a multiple of 16 in [16, 256].  c_kv,
+ * k_rope, w_uk, w_uv and out must be 16-byte aligned (else
+ * ATTN_ERR_UNSUPPORTED).  One kernel
  * launch: the absorbed query, the cache pass, the merge of a sequence's chunks
  * and the W_UV product all run in it.
  * split_tokens: 0 lets the library choose the chunk length (a power of two of at

@@ -209,8 +209,9 @@ __device__ __forceinline__ LdsOffsets lds_offsets(const Lane& w) {
 }
 
 // S^T of one tile from the K tile kc: lane holds S^T[key 32j + 8(i/4) + 4h2 + i%4][row ln]
-// (keys relative to the tile).  A = 32-key K block, B = the wave's Q^T.
-template <int D>
+// (keys relative to the tile).  A = 32-key K block, B = the wave's Q^T.  D is
+// the head size, DL the LDS row pitch of the tile (>= D).
+template <int D, int DL = D>
 __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const u16* kc, const bf16x8 (&qop)[D / 16], int off) {
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -221,7 +222,7 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const u16* kc, const bf1
   for (int c = 0; c < D / 16; ++c)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const u16* kr = kc + 32 * j * D + (off ^ (16 * c));
+      const u16* kr = kc + 32 * j * DL + (off ^ (16 * c));
       s[j] = mfma_32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(kr)), qop[c], s[j]);
     }
   // issue order: operand reads four MFMAs ahead of their use
@@ -237,15 +238,15 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const u16* kc, const bf1
 // contraction covers keys 16v + 4h2 + (0..3) and 16v + 8 + 4h2 + (0..3); 16-lane
 // group (g16, h2) of a transposed read points at key 16v + 4h2 + (i16 >> 2) (+8),
 // dims 32d + 16g16 + 4(i16 & 3).
-template <int D>
+template <int D, int DL = D>
 __device__ __forceinline__ void pv_tile(f32x16 (&o)[D / 32], const u16* vc, const bf16x8 (&p)[4], int off_lo,
                                         int off_hi) {
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
 #pragma unroll
     for (int d = 0; d < D / 32; ++d) {
-      const u16x4 lo = lds_read_tr16(vc + 16 * v * D + (off_lo ^ (32 * d)));
-      const u16x4 hi = lds_read_tr16(vc + 16 * v * D + (off_hi ^ (32 * d)));
+      const u16x4 lo = lds_read_tr16(vc + 16 * v * DL + (off_lo ^ (32 * d)));
+      const u16x4 hi = lds_read_tr16(vc + 16 * v * DL + (off_hi ^ (32 * d)));
       const u16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       o[d] = mfma_32x32x16(__builtin_bit_cast(bf16x8, av), p[v], o[d]);
     }
@@ -311,21 +312,21 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, f32x16 (&sc)[2], b
 // meet at the barrier.  The four buffers are distinct LDS variables addressed
 // directly, so the compiler can tell the copies in flight from the reads of the
 // current tile and does not wait for them before reading.
-template <int D>
+template <int D, int DL>
 __device__ __forceinline__ void tile_step(RowState<D>& st, const u16* kc, const u16* vc, u16* kn, u16* vn,
                                           const bf16x8 (&qop)[D / 16], int kt, int n_kt, int last_kt,
                                           const u16* kp, const u16* vp, int row_bytes, int kv_len,
-                                          const TileCopy<D>& cp, const LdsOffsets& off, const Lane& w) {
+                                          const TileCopy<DL>& cp, const LdsOffsets& off, const Lane& w) {
   if (kt + 1 < n_kt) {  // (kn, vn) were released by the last barrier
-    cp.issue(kn, TileCopy<D>::rsrc(kp, kt + 1, n_kt, kv_len, row_bytes));
-    cp.issue(vn, TileCopy<D>::rsrc(vp, kt + 1, n_kt, kv_len, row_bytes));
+    cp.issue(kn, TileCopy<DL>::rsrc(kp, kt + 1, n_kt, kv_len, row_bytes, 2 * D));
+    cp.issue(vn, TileCopy<DL>::rsrc(vp, kt + 1, n_kt, kv_len, row_bytes, 2 * D));
   }
   if (kt <= last_kt) {
     f32x16 sc[2];
-    qk_tile<D>(sc, kc, qop, off.k);
+    qk_tile<D, DL>(sc, kc, qop, off.k);
     bf16x8 pop[4];
     softmax_tile<D>(st, sc, pop, kt * kBN, w);
-    pv_tile<D>(st.o, vc, pop, off.v_lo, off.v_hi);
+    pv_tile<D, DL>(st.o, vc, pop, off.v_lo, off.v_hi);
   }
   wait_vmem();      // this thread's copies of tile kt+1 have landed
   __syncthreads();  // ... and everyone's; nobody reads tile kt any more
@@ -369,7 +370,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   static_assert(kBM == 32 * kWaves, "one 32-row slice per wave");
   constexpr int KC = D / 16;
   constexpr int DB = D / 32;
-  constexpr int kTile = kBN * D;
+  // LDS row pitch: head_dim 96 rows (192 bytes, which no 16-byte XOR swizzle
+  // covers) sit in the head_dim-128 layout; the copies' lanes that fall past the
+  // row's 12 chunks read the next bytes or zeros, and QK and PV never read those
+  // columns
+  constexpr int DL = D == 96 ? 128 : D;
+  constexpr int kTile = kBN * DL;
   __shared__ __attribute__((aligned(1024))) u16 k0[kTile];
   __shared__ __attribute__((aligned(1024))) u16 k1[kTile];
   __shared__ __attribute__((aligned(1024))) u16 v0[kTile];
@@ -415,10 +421,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int n_kt = (kv_end + kBN - 1) / kBN;
   const int last_kt = min(n_kt - 1, (w.pos0 + 31) / kBN);
 
-  const TileCopy<D> cp(wave, w.lane, row_bytes);
-  cp.issue(k0, TileCopy<D>::rsrc(kp, 0, n_kt, kv_len, row_bytes));
-  cp.issue(v0, TileCopy<D>::rsrc(vp, 0, n_kt, kv_len, row_bytes));
-  const LdsOffsets off = lds_offsets<D>(w);
+  const TileCopy<DL> cp(wave, w.lane, row_bytes);
+  cp.issue(k0, TileCopy<DL>::rsrc(kp, 0, n_kt, kv_len, row_bytes, 2 * D));
+  cp.issue(v0, TileCopy<DL>::rsrc(vp, 0, n_kt, kv_len, row_bytes, 2 * D));
+  const LdsOffsets off = lds_offsets<DL>(w);
 
   // Q^T as the B operand: lane holds Q[row ln][16c + 8h2 ..+8]
   bf16x8 qop[KC];
@@ -439,9 +445,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   wait_vmem();
   __syncthreads();
   for (int kt = 0; kt < n_kt; kt += 2) {
-    tile_step<D>(st, k0, v0, k1, v1, qop, kt, n_kt, last_kt, kp, vp, row_bytes, kv_len, cp, off, w);
+    tile_step<D, DL>(st, k0, v0, k1, v1, qop, kt, n_kt, last_kt, kp, vp, row_bytes, kv_len, cp, off, w);
     if (kt + 1 < n_kt)
-      tile_step<D>(st, k1, v1, k0, v0, qop, kt + 1, n_kt, last_kt, kp, vp, row_bytes, kv_len, cp, off, w);
+      tile_step<D, DL>(st, k1, v1, k0, v0, qop, kt + 1, n_kt, last_kt, kp, vp, row_bytes, kv_len, cp, off, w);
   }
 
   // normalise and store; rows past the new tokens are zeros
@@ -706,14 +712,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 // Explicit instantiations: without them the host stubs of only some of the
 // kernel templates launched below were emitted.
 template __global__ void prefill_causal<128, false>(PrefillArgs);
+template __global__ void prefill_causal<96, false>(PrefillArgs);
 template __global__ void prefill_causal<64, false>(PrefillArgs);
 template __global__ void prefill_causal<128, true>(PrefillArgs);
+template __global__ void prefill_causal<96, true>(PrefillArgs);
 template __global__ void prefill_causal<64, true>(PrefillArgs);
 template __global__ void prefill_mla<96, 48, 96>(MlaPrefillArgs);
 
 }  // namespace
 
-bool prefill_supported(int D) { return D == 64 || D == 128; }
+bool prefill_supported(int D) { return D == 64 || D == 96 || D == 128; }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (!prefill_supported(a.D)) return hipErrorInvalidValue;
@@ -724,6 +732,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.D == 128) {
     if (cached) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<128, true>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<128, false>), grid, dim3(256), 0, st, a);
+  } else if (a.D == 96) {
+    if (cached) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<96, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<96, false>), grid, dim3(256), 0, st, a);
   } else {
     if (cached) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<64, true>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<64, false>), grid, dim3(256), 0, st, a);

@@ -158,7 +158,7 @@ def test_cached_prefill_validation():
     assert f(S=0) == SHAPE
     assert f(Hq=8, Hkv=3) == GROUPS
     assert f(ind=F32) == UNSUP
-    assert f(D=96) == UNSUP
+    assert f(D=80) == UNSUP
     assert f(q=FAKE_MIS) == UNSUP
 
 

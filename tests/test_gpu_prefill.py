@@ -26,6 +26,8 @@ CASES = [
     ("s1", 2, 1, 8, 2, 128),
     ("s63", 1, 63, 4, 2, 128),
     ("d64_s200", 2, 200, 8, 2, 64),
+    ("minimind768_d96_s300", 2, 300, 8, 4, 96),  # the MiniMind-768 GQA heads (2*4*96 cached per token)
+    ("d96_mqa_s200", 1, 200, 8, 1, 96),
 ]
 
 

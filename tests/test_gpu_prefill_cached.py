@@ -38,6 +38,8 @@ CASES = [
     ("prefix_fills_cache", 2, 64, 8, 2, 128, 256, [256, 251], [64, 64]),
     ("negative_start_clamps", 1, 70, 8, 2, 128, 128, [-5], [70]),
     ("d64", 2, 200, 8, 2, 64, 600, [64, 399], [200, 199]),
+    ("minimind768_d96", 2, 300, 8, 4, 96, 1000, [0, 517], [300, 77]),
+    ("d96_mqa", 2, 150, 8, 1, 96, 500, [201, 33], [150, 90]),
 ]
 
 
