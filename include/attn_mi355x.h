@@ -327,6 +327,37 @@ attn_status attn_decode_mla_absorbed(const void* q_nope, const void* q_rope, con
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* MLA decode step with the new token's latent row: append and attend in one call.
+ *
+ *   L = cache_lens[b] (positions cached before this token, clamped to [0, T_max])
+ *   out[b,h,:] = attn_decode_mla_absorbed over { rows t < L of (c_kv, k_rope),
+ *                and the new row (c_new[b], k_rope_new[b]) }
+ *   c_kv[b,L,:] = c_new[b,:], k_rope[b,L,:] = k_rope_new[b,:]  when L < T_max
+ *
+ * One decode iteration of MLA with only the compressed latent and the rotated
+ * shared key part cached (qqstock DeepSeek MLA article, sections 1 and 3): the
+ * new token's rows are appended at position L and the query attends to the L + 1
+ * rows.  The result equals attn_cache_append of the two rows followed by
+ * attn_decode_mla_absorbed with cache_lens + 1 (up to rounding: the new token
+ * is merged as one more partial), in one launch.  Rows below L are read, row L
+ * is written by the workgroup that finishes the sequence after every chunk has
+ * been read; cache_lens itself is not changed (the caller advances it).  When
+ * L = T_max the new token is attended to but not stored.  Rotary embedding is
+ * the caller's (q_rope and k_rope_new already rotated).
+ *
+ *   c_new [B, kv_lora_rank], k_rope_new [B, rope_dim]   in_dtype (16-byte aligned)
+ *   everything else, supported shapes, errors and the workspace
+ *   (attn_decode_mla_workspace_bytes): as attn_decode_mla_absorbed, plus
+ *   ATTN_ERR_NULL for a NULL c_new or k_rope_new
+ */
+attn_status attn_decode_mla_append(const void* q_nope, const void* q_rope, const void* c_new, const void* k_rope_new,
+                                   const void* w_uk, const void* w_uv, void* c_kv, void* k_rope,
+                                   const int32_t* cache_lens, void* out, int B, int H, int nope_head_dim,
+                                   int rope_dim, int v_head_dim, int kv_lora_rank, int T_max, float softmax_scale,
+                                   attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* MLA causal prefill over the latent cache (absorbed form).
  *
  *   P = start_pos[b] (NULL: 0), n = q_lens[b] (NULL: S), for i < n:

@@ -72,6 +72,8 @@ def _declare(lib):
     lib.attn_decode_mla_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.attn_decode_mla_supported.restype = I
     lib.attn_decode_mla_supported.argtypes = [I, I, I, I]
+    lib.attn_decode_mla_append.restype = I
+    lib.attn_decode_mla_append.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, I, P, Z, P]
     lib.attn_decode_mla_absorbed.restype = I
     lib.attn_decode_mla_absorbed.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, I,
                                              P, Z, P]
@@ -440,8 +442,48 @@ def attn_decode_mla_absorbed(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, cache_len
     return out
 
 
+def attn_decode_mla_append(q_nope, q_rope, c_new, k_rope_new, w_uk, w_uv, c_kv, k_rope, cache_lens, out=None,
+                           softmax_scale: float = 0.0, out_dtype=torch.float32, split_tokens: int = 0, workspace=None):
+    """One MLA decode step with the new token: writes c_new [B,r] and k_rope_new [B,dR] into the
+    caches at row cache_lens[b] and attends to the cache_lens[b] cached rows plus the new one.
+    Other arguments as attn_decode_mla_absorbed; cache_lens is not changed.  Returns out [B,H,dv]."""
+    _check(q_nope, "q_nope")
+    B, H, dn = q_nope.shape
+    dt = q_nope.dtype
+    _check(c_kv, "c_kv", dtype=dt)
+    if c_kv.dim() != 3 or c_kv.shape[0] != B:
+        raise ValueError(f"c_kv must be [B={B}, T_max, kv_lora_rank] (got {tuple(c_kv.shape)})")
+    T_max, r = c_kv.shape[1], c_kv.shape[2]
+    _check(k_rope, "k_rope", dtype=dt)
+    if k_rope.dim() != 3 or k_rope.shape[:2] != (B, T_max):
+        raise ValueError(f"k_rope must be [B={B}, T_max={T_max}, rope_dim] (got {tuple(k_rope.shape)})")
+    dR = k_rope.shape[2]
+    _check(q_rope, "q_rope", shape=(B, H, dR), dtype=dt)
+    _check(c_new, "c_new", shape=(B, r), dtype=dt)
+    _check(k_rope_new, "k_rope_new", shape=(B, dR), dtype=dt)
+    _check(w_uk, "w_uk", shape=(H, dn, r), dtype=dt)
+    _check(w_uv, "w_uv", dtype=dt)
+    if w_uv.dim() != 3 or w_uv.shape[0] != H or w_uv.shape[2] != r:
+        raise ValueError(f"w_uv must be [H={H}, v_head_dim, kv_lora_rank={r}] (got {tuple(w_uv.shape)})")
+    dv = w_uv.shape[1]
+    _check(cache_lens, "cache_lens", shape=(B,), dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=out_dtype, device=q_nope.device)
+    _check(out, "out", shape=(B, H, dv))
+    need = attn_decode_mla_workspace_bytes(B, H, r, dR, T_max, split_tokens)
+    if workspace is None:
+        workspace = _workspace(need, q_nope.device, "mla")
+    _check(workspace, "workspace", dtype=torch.uint8)
+    st = lib().attn_decode_mla_append(_ptr(q_nope), _ptr(q_rope), _ptr(c_new), _ptr(k_rope_new), _ptr(w_uk),
+                                      _ptr(w_uv), _ptr(c_kv), _ptr(k_rope), _ptr(cache_lens), _ptr(out), B, H, dn, dR,
+                                      dv, r, T_max, float(softmax_scale), _dt(q_nope), _dt(out), int(split_tokens),
+                                      _ptr(workspace), workspace.numel(), _stream(q_nope.device))
+    _raise_if(st, "attn_decode_mla_append")
+    return out
+
+
 __all__ = ["attn_decode_gqa", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_noalloc", "NOALLOC_SCRATCH_BYTES", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
            "attn_decode_gqa_append_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached",
            "attn_prefill_mla_causal", "attn_cache_append",
-           "attn_decode_mla_absorbed", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",
+           "attn_decode_mla_absorbed", "attn_decode_mla_append", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",
            "AttnError", "lib", "header_functions", "LIB_PATH", "ATTN_F32", "ATTN_BF16"]

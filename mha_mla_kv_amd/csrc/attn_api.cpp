@@ -494,43 +494,45 @@ int attn_decode_mla_supported(int H, int kv_lora_rank, int rope_dim, attn_dtype 
   return in_dtype == ATTN_BF16 && attn::mla_decode_supported(H, kv_lora_rank, rope_dim) ? 1 : 0;
 }
 
-attn_status attn_decode_mla_absorbed(const void* q_nope, const void* q_rope, const void* w_uk,
-                                     const void* w_uv, const void* c_kv, const void* k_rope,
-                                     const int32_t* cache_lens, void* out, int B, int H,
-                                     int nope_head_dim, int rope_dim, int v_head_dim,
-                                     int kv_lora_rank, int T_max, float softmax_scale,
-                                     attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Shared checks and launch of the two MLA decode entry points.  c_new != null:
+// a decode step that also takes the new token's latent row (attn_decode_mla_append).
+attn_status mla_decode_common(const char* fn, const void* q_nope, const void* q_rope, const void* c_new,
+                              const void* kr_new, const void* w_uk, const void* w_uv, const void* c_kv,
+                              const void* k_rope, const int32_t* cache_lens, void* out, int B, int H,
+                              int nope_head_dim, int rope_dim, int v_head_dim, int kv_lora_rank, int T_max,
+                              float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  const bool append = c_new != nullptr;
   if (!q_nope || !q_rope || !w_uk || !w_uv || !c_kv || !k_rope || !cache_lens || !out)
-    return fail(ATTN_ERR_NULL, "attn_decode_mla_absorbed: all tensor pointers must be non-NULL");
+    return fail(ATTN_ERR_NULL, "%s: all tensor pointers must be non-NULL", fn);
   if (B <= 0 || H <= 0 || nope_head_dim <= 0 || rope_dim <= 0 || v_head_dim <= 0 || kv_lora_rank <= 0 ||
       T_max <= 0)
-    return fail(ATTN_ERR_SHAPE,
-                "attn_decode_mla_absorbed: sizes must be positive (B=%d H=%d nope=%d rope=%d v=%d rank=%d T_max=%d)",
+    return fail(ATTN_ERR_SHAPE, "%s: sizes must be positive (B=%d H=%d nope=%d rope=%d v=%d rank=%d T_max=%d)", fn,
                 B, H, nope_head_dim, rope_dim, v_head_dim, kv_lora_rank, T_max);
-  if (B > kMaxGridYZ)
-    return fail(ATTN_ERR_SHAPE, "attn_decode_mla_absorbed: B must be <= %d", kMaxGridYZ);
+  if (B > kMaxGridYZ) return fail(ATTN_ERR_SHAPE, "%s: B must be <= %d", fn, kMaxGridYZ);
   if (nope_head_dim > 256 || nope_head_dim % 8 != 0 || v_head_dim > 256 || v_head_dim % 16 != 0)
     return fail(ATTN_ERR_UNSUPPORTED,
-                "attn_decode_mla_absorbed: nope_head_dim must be a multiple of 8 and v_head_dim a multiple of 16, "
-                "both up to 256 (got %d, %d)", nope_head_dim, v_head_dim);
+                "%s: nope_head_dim must be a multiple of 8 and v_head_dim a multiple of 16, both up to 256 "
+                "(got %d, %d)", fn, nope_head_dim, v_head_dim);
   if (!valid_split(split_tokens))
-    return fail(ATTN_ERR_SHAPE, "attn_decode_mla_absorbed: split_tokens=%d must be 0 or a multiple of 64 in [64, 65536]",
+    return fail(ATTN_ERR_SHAPE, "%s: split_tokens=%d must be 0 or a multiple of 64 in [64, 65536]", fn,
                 split_tokens);
-  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: unknown dtype");
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(ATTN_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
   if (!attn_decode_mla_supported(H, kv_lora_rank, rope_dim, in_dtype))
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: H=%d kv_lora_rank=%d rope_dim=%d %s is not built",
-                H, kv_lora_rank, rope_dim, in_dtype == ATTN_BF16 ? "bf16" : "fp32");
-  if (!aligned16(c_kv) || !aligned16(k_rope) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(out))
-    return fail(ATTN_ERR_UNSUPPORTED,
-                "attn_decode_mla_absorbed: c_kv, k_rope, w_uk, w_uv and out must be 16-byte aligned");
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: H=%d kv_lora_rank=%d rope_dim=%d %s is not built", fn, H, kv_lora_rank,
+                rope_dim, in_dtype == ATTN_BF16 ? "bf16" : "fp32");
+  if (!aligned16(c_kv) || !aligned16(k_rope) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(out) ||
+      (append && (!aligned16(c_new) || !aligned16(kr_new))))
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: c_kv, k_rope, w_uk, w_uv, out (and the new rows) must be 16-byte aligned",
+                fn);
   const MlaLayout lay = mla_layout(B, H, kv_lora_rank, T_max, split_tokens);
   if (!workspace || workspace_bytes < lay.total)
-    return fail(ATTN_ERR_WORKSPACE, "attn_decode_mla_absorbed: workspace of %zu bytes needed, %zu given%s",
-                lay.total, workspace_bytes, workspace ? "" : " (NULL)");
+    return fail(ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given%s", fn, lay.total, workspace_bytes,
+                workspace ? "" : " (NULL)");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(ATTN_ERR_WORKSPACE, "attn_decode_mla_absorbed: workspace must be 256-byte aligned");
+    return fail(ATTN_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
   attn::MlaDecodeArgs a;
   a.q_nope = q_nope;
   a.q_rope = q_rope;
@@ -553,11 +555,42 @@ attn_status attn_decode_mla_absorbed(const void* q_nope, const void* q_rope, con
   a.T_max = T_max;
   a.split = lay.split;
   a.n_splits = lay.n_splits;
-  const float scale =
-      softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)(nope_head_dim + rope_dim));
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)(nope_head_dim + rope_dim));
   a.scale_log2e = scale * kLog2e;
   a.out_bf16 = out_dtype == ATTN_BF16;
-  return hip_status(attn::launch_mla_decode(a, static_cast<hipStream_t>(stream)), "attn_decode_mla_absorbed");
+  a.append = append;
+  a.c_new = c_new;
+  a.kr_new = kr_new;
+  a.c_cache = const_cast<void*>(c_kv);
+  a.kr_cache = const_cast<void*>(k_rope);
+  return hip_status(attn::launch_mla_decode(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace
+
+attn_status attn_decode_mla_absorbed(const void* q_nope, const void* q_rope, const void* w_uk,
+                                     const void* w_uv, const void* c_kv, const void* k_rope,
+                                     const int32_t* cache_lens, void* out, int B, int H,
+                                     int nope_head_dim, int rope_dim, int v_head_dim,
+                                     int kv_lora_rank, int T_max, float softmax_scale,
+                                     attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return mla_decode_common("attn_decode_mla_absorbed", q_nope, q_rope, nullptr, nullptr, w_uk, w_uv, c_kv, k_rope,
+                           cache_lens, out, B, H, nope_head_dim, rope_dim, v_head_dim, kv_lora_rank, T_max,
+                           softmax_scale, in_dtype, out_dtype, split_tokens, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_mla_append(const void* q_nope, const void* q_rope, const void* c_new, const void* k_rope_new,
+                                   const void* w_uk, const void* w_uv, void* c_kv, void* k_rope,
+                                   const int32_t* cache_lens, void* out, int B, int H, int nope_head_dim,
+                                   int rope_dim, int v_head_dim, int kv_lora_rank, int T_max, float softmax_scale,
+                                   attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!c_new || !k_rope_new)
+    return fail(ATTN_ERR_NULL, "attn_decode_mla_append: c_new and k_rope_new must be non-NULL");
+  return mla_decode_common("attn_decode_mla_append", q_nope, q_rope, c_new, k_rope_new, w_uk, w_uv, c_kv, k_rope,
+                           cache_lens, out, B, H, nope_head_dim, rope_dim, v_head_dim, kv_lora_rank, T_max,
+                           softmax_scale, in_dtype, out_dtype, split_tokens, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -105,6 +105,15 @@ struct MlaDecodeArgs {
   int split, n_splits;
   float scale_log2e;
   int out_bf16;
+  // decode step with the new token (append != 0): its latent row and rotated
+  // key part are merged as one more partial by the workgroup that finishes the
+  // sequence, which then writes them into the caches at row lens[b] (when
+  // lens[b] < T_max); the cache pass reads only rows below lens[b]
+  int append;
+  const void* c_new;    // [B, r]
+  const void* kr_new;   // [B, dR]
+  void* c_cache;        // the c_kv array, written at the new position
+  void* kr_cache;       // the k_rope array
 };
 
 // Each launcher validates nothing (the host layer has done it) and returns the

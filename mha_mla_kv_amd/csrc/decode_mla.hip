@@ -37,6 +37,10 @@
 // partials back with device-coherent loads, merges them by their
 // log2-sum-exps, applies W_UV and returns the counter to zero.  Nothing waits
 // on another workgroup, so no schedule can deadlock.
+// A decode step with the new token (attn_decode_mla_append) adds the new
+// token as one more partial in that merge (its log2 score from q_lat and the
+// new rows, its value the new latent row) and writes the new rows into the
+// caches at row L, which the cache pass never reads.
 #include <hip/hip_runtime.h>
 
 #include "attn_internal.h"
@@ -484,6 +488,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
   __shared__ __attribute__((aligned(16))) u16 qlat[2 * kHeadsPad * RW];  // [hi, lo][16][RW]
   __shared__ __attribute__((aligned(16))) u16 olat[2 * kHeadsPad * R];   // [hi, lo][16][R]
   __shared__ float lse_s[kHeadsPad];
+  __shared__ float snew_s[kHeadsPad];  // decode step: the new token's log2 score per head
   __shared__ int last_s;
   // after the stream: one [16 heads][R] fp32 output slice per streaming wave,
   // two in each of stages 0 and 1; m and l per wave and head in stage 2
@@ -501,7 +506,9 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
   AbsorbLoads<R> ld;
   if (!streamer && j < a.H) absorb_issue<R>(ld, a, b, j, j + kHelpers < a.H ? j + kHelpers : j, 0, lane);
   const int L = clamp_len(a.lens[b], a.T_max);
-  const int n_chunks = (L + a.split - 1) / a.split;
+  // a decode step with the new token has at least one (possibly empty) chunk,
+  // whose workgroup adds the new token
+  const int n_chunks = max((L + a.split - 1) / a.split, a.append ? 1 : 0);
   if (s >= n_chunks) {  // past the sequence; an empty sequence gets zeros from chunk 0
     wait_vmem();
     if (n_chunks == 0 && s == 0)
@@ -635,7 +642,24 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
     wait_vmem();  // the copies past the end (zeros) land before the stages are reused
     st.lsum = sum_xor32(sum_xor16(st.lsum));
   }
-  if (!streamer && j < a.H) load_uv<R>(uv, a, j, 0, lane);
+  if (!streamer) {
+    if (j < a.H) load_uv<R>(uv, a, j, 0, lane);
+    // decode step: the new token's score, scale * q_lat . [c_new, k_rope_new], per head
+    if (a.append) {
+      const u16* cn = static_cast<const u16*>(a.c_new) + (size_t)b * R;
+      const u16* kn = static_cast<const u16*>(a.kr_new) + (size_t)b * DR;
+      for (int h = j; h < a.H; h += kHelpers) {
+        float acc = 0.f;
+        for (int e = lane; e < RW; e += 64) {
+          const float x = bf16_to_f32(e < R ? cn[e] : kn[e - R]);
+          acc = fmaf(bf16_to_f32(qlat[h * RW + e]) + bf16_to_f32(qlat[(kHeadsPad + h) * RW + e]), x, acc);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+        if (lane == 0) snew_s[h] = acc * a.scale_log2e;
+      }
+    }
+  }
 
   // ---- merge the four streaming waves (LDS, reusing the stages)
   // Each wave writes its scaled O^T into its own [16][R] slice; 16-byte unit u
@@ -655,7 +679,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
     float Lt = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) Lt += rescale(mw[w * kHeadsPad + row], M) * lw[w * kHeadsPad + row];
-    const float f = rescale(st.m, M) / Lt;
+    const float f = Lt > 0.f ? rescale(st.m, M) / Lt : 0.f;  // an empty chunk (decode step, L = 0)
     float* ob = slice(wave) + row * R;
 #pragma unroll
     for (int dw = 0; dw < C::DW; ++dw)
@@ -675,6 +699,14 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) v += *reinterpret_cast<const f32x4*>(slice(w) + off);
     if (single) {
+      if (a.append) {  // the new token as one more partial
+        const float lo = lse_s[h], sn = snew_s[h];
+        const float M = fmaxf(lo, sn);
+        const float wo = rescale(lo, M), wn = exp2_fast(sn - M), inv = 1.f / (wo + wn);
+        const u16* cn = static_cast<const u16*>(a.c_new) + (size_t)b * R + 4 * d4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (wo * v[r] + wn * bf16_to_f32(cn[r])) * inv;
+      }
       u16x4 vh, vl;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -726,6 +758,13 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
           M = Mn;
         }
       }
+      if (a.append) {  // the new token as one more partial
+        const float sn = snew_s[h];
+        const float Mn = fmaxf(M, sn);
+        const float f = rescale(M, Mn), w = exp2_fast(sn - Mn);
+        Ssum = Ssum * f + w;
+        acc = acc * f + w * bf16_to_f32(static_cast<const u16*>(a.c_new)[(size_t)b * R + d]);
+      }
       const float v = acc / Ssum;
       const __bf16 x = (__bf16)v;
       olat[h * R + d] = __builtin_bit_cast(u16, x);
@@ -733,6 +772,18 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
     }
   }
   __syncthreads();  // (7) o_lat is in LDS
+
+  // decode step: the new token's rows go into the caches (every chunk of the
+  // sequence has finished reading them, and none reads row L)
+  if (a.append && L < a.T_max) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    if (tid < R / 8)
+      reinterpret_cast<u32x4*>(static_cast<u16*>(a.c_cache) + ((size_t)b * a.T_max + L) * R)[tid] =
+          reinterpret_cast<const u32x4*>(static_cast<const u16*>(a.c_new) + (size_t)b * R)[tid];
+    else if (tid >= 64 && tid < 64 + DR / 8)
+      reinterpret_cast<u32x4*>(static_cast<u16*>(a.kr_cache) + ((size_t)b * a.T_max + L) * DR)[tid - 64] =
+          reinterpret_cast<const u32x4*>(static_cast<const u16*>(a.kr_new) + (size_t)b * DR)[tid - 64];
+  }
 
   // ---- out = W_UV o_lat, helper j taking heads j, j + 4, ...
   if (!streamer) {

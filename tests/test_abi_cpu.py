@@ -257,3 +257,19 @@ def test_noalloc_scratch_size_matches_header():
     text = open(attn.HEADER_PATH).read()
     m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == attn.NOALLOC_SCRATCH_BYTES
+
+
+@no_gpu_only
+def test_mla_append_validation():
+    lib = attn.lib()
+
+    def f(cn=FAKE, kn=FAKE, **kw):
+        return lib.attn_decode_mla_append(FAKE, FAKE, cn, kn, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("B", 2), 8, 96,
+                                          48, kw.get("dv", 96), 128, 64, 0.0, BF16, F32, 0, kw.get("ws", FAKE),
+                                          kw.get("wsb", 1 << 30), None)
+    assert f(cn=None) == NULL
+    assert f(kn=None) == NULL
+    assert f(kn=FAKE_MIS) == UNSUP
+    assert f(B=0) == SHAPE
+    assert f(dv=90) == UNSUP
+    assert f(ws=None) == WS
