@@ -265,6 +265,47 @@ attn_status attn_prefill_gqa_cached(const void* q, const void* k_cache, const vo
                                     attn_dtype in_dtype, attn_dtype out_dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Causal GQA prefill after a cached prefix that also appends the new rows.
+ *
+ *   P = start_pos[b], n = q_lens[b] (NULL: S), both clamped as for
+ *   attn_prefill_gqa_cached; for i < n:
+ *   out[b,i,h,:] = sum_{j <= P+i} softmax_j(scale * q[b,i,h,:] . key_j) val_j
+ *     with key_j = k_cache[b,j,g,:] for j < P and k_new[b,j-P,g,:] for j >= P
+ *     (val likewise from v_cache / v_new)
+ *   k_cache[b,P+i,:,:] = k_new[b,i,:,:], v_cache[b,P+i,:,:] = v_new[b,i,:,:]
+ *   out[b,i,h,:] = 0 for n <= i < S.
+ *
+ * The whole of Attention.forward with start_pos > 0 on the "模型架构｜MQA & GQA
+ * 调研" page in one launch: the new tokens' K/V rows are written into the cache
+ * at start_pos .. and the new tokens attend to the cached prefix and, causally,
+ * to each other.  The kernel reads the new keys and values from k_new / v_new
+ * and only rows below P from the caches, so the writes (made by the workgroups
+ * of the first query head of each KV group) race with no read.  The result
+ * equals attn_cache_append of (k_new, v_new) followed by
+ * attn_prefill_gqa_cached (up to fp32 rounding: the first 64-key tile of the
+ * new rows starts at P rather than at a multiple of 64).  Rows outside
+ * [P, P + n) of the caches are untouched; start_pos and q_lens are not changed
+ * (the caller advances them).
+ *
+ *   q             [B, S, Hq, head_dim]      bf16 (the new tokens, padded to S)
+ *   k_new, v_new  [B, S, Hkv, head_dim]     bf16 (their keys and values)
+ *   k_cache, v_cache [B, T_max, Hkv, head_dim] bf16, read at rows < P,
+ *                 written at rows P .. P + n - 1
+ *   start_pos     [B] int32, required; q_lens [B] int32 or NULL
+ *   out           [B, S, Hq, head_dim]      out_dtype
+ *
+ * All pointers are device memory owned by the caller, 16-byte aligned; the new
+ * rows must not overlap the caches.  Supported shapes and errors as for
+ * attn_prefill_gqa_cached, plus ATTN_ERR_NULL for a NULL k_new or v_new.  No
+ * workspace.
+ */
+attn_status attn_prefill_gqa_cached_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                           void* v_cache, const int32_t* start_pos, const int32_t* q_lens, void* out,
+                                           int B, int S, int Hq, int Hkv, int head_dim, int T_max,
+                                           float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype,
+                                           void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* MLA decode, absorbed form, over a latent cache plus one shared RoPE key.
  *
  * Source: qqstock DeepSeek MLA article -- sections 1 (only the low-rank latent

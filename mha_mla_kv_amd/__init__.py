@@ -68,6 +68,8 @@ def _declare(lib):
     lib.attn_prefill_mla_causal.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, P]
     lib.attn_prefill_gqa_cached.restype = I
     lib.attn_prefill_gqa_cached.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
+    lib.attn_prefill_gqa_cached_append.restype = I
+    lib.attn_prefill_gqa_cached_append.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
     lib.attn_decode_mla_workspace_bytes.restype = Z
     lib.attn_decode_mla_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.attn_decode_mla_supported.restype = I
@@ -320,6 +322,36 @@ def attn_prefill_gqa_cached(q, k_cache, v_cache, start_pos, q_lens=None, out=Non
     return out
 
 
+def attn_prefill_gqa_cached_append(q, k_new, v_new, k_cache, v_cache, start_pos, q_lens=None, out=None,
+                                   softmax_scale: float = 0.0, out_dtype=torch.bfloat16):
+    """Causal prefill after a cached prefix that also appends the new rows, in one launch: new token
+    i of sequence b attends cache rows j < start_pos[b] and new rows j <= i, and k_new / v_new rows
+    i < q_lens[b] are written into the caches at start_pos[b] + i.
+
+    q [B,S,Hq,D] bf16, k_new/v_new [B,S,Hkv,D] bf16, k_cache/v_cache [B,T_max,Hkv,D] bf16 (updated in
+    place), start_pos, q_lens [B] int32 (q_lens None: S).  Returns out."""
+    _check(q, "q")
+    B, S, Hq, D = q.shape
+    _check(k_cache, "k_cache", dtype=q.dtype)
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError(f"k_cache must be [B={B}, T_max, Hkv, {D}] (got {tuple(k_cache.shape)})")
+    T_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _check(v_cache, "v_cache", shape=k_cache.shape, dtype=q.dtype)
+    _check(k_new, "k_new", shape=(B, S, Hkv, D), dtype=q.dtype)
+    _check(v_new, "v_new", shape=(B, S, Hkv, D), dtype=q.dtype)
+    _check(start_pos, "start_pos", shape=(B,), dtype=torch.int32)
+    if q_lens is not None:
+        _check(q_lens, "q_lens", shape=(B,), dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, S, Hq, D), dtype=out_dtype, device=q.device)
+    _check(out, "out", shape=(B, S, Hq, D))
+    st = lib().attn_prefill_gqa_cached_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                              _ptr(start_pos), _ptr(q_lens), _ptr(out), B, S, Hq, Hkv, D, T_max,
+                                              float(softmax_scale), _dt(q), _dt(out), _stream(q.device))
+    _raise_if(st, "attn_prefill_gqa_cached_append")
+    return out
+
+
 def attn_prefill_mla_causal(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, start_pos=None, q_lens=None, out=None,
                             softmax_scale: float = 0.0, out_dtype=torch.bfloat16):
     """MLA causal prefill over the latent cache: new token i of sequence b (position start_pos[b] + i)
@@ -483,7 +515,7 @@ def attn_decode_mla_append(q_nope, q_rope, c_new, k_rope_new, w_uk, w_uv, c_kv, 
 
 
 __all__ = ["attn_decode_gqa", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_noalloc", "NOALLOC_SCRATCH_BYTES", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
-           "attn_decode_gqa_append_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached",
+           "attn_decode_gqa_append_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached", "attn_prefill_gqa_cached_append",
            "attn_prefill_mla_causal", "attn_cache_append",
            "attn_decode_mla_absorbed", "attn_decode_mla_append", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",
            "AttnError", "lib", "header_functions", "LIB_PATH", "ATTN_F32", "ATTN_BF16"]

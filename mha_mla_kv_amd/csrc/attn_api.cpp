@@ -341,14 +341,19 @@ attn_status attn_decode_gqa_append(const void* q, const void* k_new, const void*
 
 namespace {
 
-// Shared checks and launch of the two prefill entry points.  start_pos == null
-// means no cached prefix (k and v then hold exactly S rows per sequence).
+// Shared checks and launch of the prefill entry points.  start_pos == null
+// means no cached prefix (k and v then hold exactly S rows per sequence);
+// k_new != null that the new rows come in k_new / v_new and are written into
+// k and v by the same launch.
 attn_status prefill_common(const char* fn, const void* q, const void* k, const void* v,
                            const int32_t* start_pos, const int32_t* q_lens, void* out, int B, int S, int Hq,
                            int Hkv, int head_dim, int T_kv, float softmax_scale, attn_dtype in_dtype,
-                           attn_dtype out_dtype, void* stream) {
+                           attn_dtype out_dtype, void* stream, const void* k_new = nullptr,
+                           const void* v_new = nullptr) {
   if (!q || !k || !v || !out)
     return fail(ATTN_ERR_NULL, "%s: q, k, v and out must be non-NULL", fn);
+  if ((k_new != nullptr) != (v_new != nullptr))
+    return fail(ATTN_ERR_NULL, "%s: k_new and v_new must be non-NULL", fn);
   if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || head_dim <= 0 || T_kv <= 0)
     return fail(ATTN_ERR_SHAPE, "%s: sizes must be positive (B=%d S=%d Hq=%d Hkv=%d head_dim=%d T=%d)", fn, B, S,
                 Hq, Hkv, head_dim, T_kv);
@@ -363,9 +368,12 @@ attn_status prefill_common(const char* fn, const void* q, const void* k, const v
     return fail(ATTN_ERR_UNSUPPORTED, "%s: only bf16 inputs are built (MFMA path)", fn);
   if (!attn::prefill_supported(head_dim))
     return fail(ATTN_ERR_UNSUPPORTED, "%s: head_dim=%d is not built", fn, head_dim);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return fail(ATTN_ERR_UNSUPPORTED, "%s: q, k, v and out must be 16-byte aligned", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(k_new) ||
+      !aligned16(v_new))
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: q, k, v, out and the new rows must be 16-byte aligned", fn);
   attn::PrefillArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -402,6 +410,18 @@ attn_status attn_prefill_gqa_cached(const void* q, const void* k_cache, const vo
     return fail(ATTN_ERR_NULL, "attn_prefill_gqa_cached: start_pos must be non-NULL");
   return prefill_common("attn_prefill_gqa_cached", q, k_cache, v_cache, start_pos, q_lens, out, B, S, Hq, Hkv,
                         head_dim, T_max, softmax_scale, in_dtype, out_dtype, stream);
+}
+
+attn_status attn_prefill_gqa_cached_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                           void* v_cache, const int32_t* start_pos, const int32_t* q_lens, void* out,
+                                           int B, int S, int Hq, int Hkv, int head_dim, int T_max,
+                                           float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype,
+                                           void* stream) {
+  static const char* fn = "attn_prefill_gqa_cached_append";
+  if (!start_pos) return fail(ATTN_ERR_NULL, "%s: start_pos must be non-NULL", fn);
+  if (!k_new || !v_new) return fail(ATTN_ERR_NULL, "%s: k_new and v_new must be non-NULL", fn);
+  return prefill_common(fn, q, k_cache, v_cache, start_pos, q_lens, out, B, S, Hq, Hkv, head_dim, T_max,
+                        softmax_scale, in_dtype, out_dtype, stream, k_new, v_new);
 }
 
 attn_status attn_prefill_mla_causal(const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv,

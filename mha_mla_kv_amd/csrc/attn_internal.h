@@ -61,6 +61,10 @@ struct PrefillArgs {
   int T_kv;                     // key rows per sequence in k and v (S without a prefix)
   float scale_log2e;
   int out_bf16;
+  // new rows in their own arrays (k_new != null, start_pos required): keys at
+  // positions P.. are read from them, and they are written into k and v at P..
+  const void* k_new = nullptr;  // [B, S, Hkv, D] bf16
+  const void* v_new = nullptr;  // [B, S, Hkv, D] bf16
 };
 
 struct MlaPrefillArgs {

@@ -260,14 +260,17 @@ struct RowState {
   float m, lsum;
 };
 
-// Online softmax of one tile's scores sc (S^T layout of qk_tile): masks keys
-// past the diagonal, moves the reference max when needed (rescaling O and the
-// row sum), and returns the probabilities as the four bf16 P^T operands of PV.
+// Online softmax of one tile's scores sc (S^T layout of qk_tile): masks the keys
+// at positions past each row's cut (its own position, or the last cached
+// position for a tile of cached keys), moves the reference max when needed
+// (rescaling O and the row sum), and returns the probabilities as the four bf16
+// P^T operands of PV.  kv0: position of the tile's first key; cut0: the lowest
+// cut of the wave's rows (wave-uniform), cut: this lane's row's cut.
 template <int D>
-__device__ __forceinline__ void softmax_tile(RowState<D>& st, f32x16 (&sc)[2], bf16x8 (&pop)[4], int kv0,
-                                             const Lane& w) {
-  if (kv0 + kBN - 1 > w.pos0) {  // the tile reaches above the diagonal of some row
-    const int t = w.my_pos - kv0 - 4 * w.h2;
+__device__ __forceinline__ void softmax_tile(RowState<D>& st, f32x16 (&sc)[2], bf16x8 (&pop)[4], int kv0, int cut0,
+                                             int cut, const Lane& w) {
+  if (kv0 + kBN - 1 > cut0) {  // the tile reaches past the cut of some row
+    const int t = cut - kv0 - 4 * w.h2;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -307,25 +310,50 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, f32x16 (&sc)[2], b
   st.lsum += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
 }
 
+// Where the keys of a sequence come from.  Tiles 0 .. n1-1 hold positions
+// 0 .. P-1 from the cache (k, v); tiles n1 .. n_kt-1 hold positions P .. from
+// the new rows (kn, vn), one 64-key tile after another.  Without separate new
+// rows n1 = n_kt and every tile comes from the cache.
+template <int D, int DL>
+struct KeySource {
+  const u16 *k, *v, *kn, *vn;
+  int row_bytes;
+  int P, n1, n_kt;
+  int len1, len2;  // keys in the first and in the second source
+
+  __device__ __forceinline__ int kv0(int kt) const { return kt < n1 ? kt * kBN : P + (kt - n1) * kBN; }
+  __device__ __forceinline__ void issue(const TileCopy<DL>& cp, u16* kl, u16* vl, int kt) const {
+    if (kt < n1) {
+      cp.issue(kl, TileCopy<DL>::rsrc(k, kt, n1, len1, row_bytes, 2 * D));
+      cp.issue(vl, TileCopy<DL>::rsrc(v, kt, n1, len1, row_bytes, 2 * D));
+    } else {
+      cp.issue(kl, TileCopy<DL>::rsrc(kn, kt - n1, n_kt - n1, len2, row_bytes, 2 * D));
+      cp.issue(vl, TileCopy<DL>::rsrc(vn, kt - n1, n_kt - n1, len2, row_bytes, 2 * D));
+    }
+  }
+};
+
 // One 64-key tile: issue the copies of tile kt+1 into (kn, vn), consume tile kt
 // from (kc, vc) if some row of the wave sees it, then wait for the copies and
 // meet at the barrier.  The four buffers are distinct LDS variables addressed
 // directly, so the compiler can tell the copies in flight from the reads of the
-// current tile and does not wait for them before reading.
+// current tile and does not wait for them before reading.  Tiles of the cache
+// (kt < n1) when the new rows come separately are cut at the last cached
+// position P - 1 (their tail reads as zeros); the others at each row's own
+// position.
 template <int D, int DL>
 __device__ __forceinline__ void tile_step(RowState<D>& st, const u16* kc, const u16* vc, u16* kn, u16* vn,
-                                          const bf16x8 (&qop)[D / 16], int kt, int n_kt, int last_kt,
-                                          const u16* kp, const u16* vp, int row_bytes, int kv_len,
-                                          const TileCopy<DL>& cp, const LdsOffsets& off, const Lane& w) {
-  if (kt + 1 < n_kt) {  // (kn, vn) were released by the last barrier
-    cp.issue(kn, TileCopy<DL>::rsrc(kp, kt + 1, n_kt, kv_len, row_bytes, 2 * D));
-    cp.issue(vn, TileCopy<DL>::rsrc(vp, kt + 1, n_kt, kv_len, row_bytes, 2 * D));
-  }
+                                          const bf16x8 (&qop)[D / 16], int kt, int last_kt,
+                                          const KeySource<D, DL>& src, const TileCopy<DL>& cp,
+                                          const LdsOffsets& off, const Lane& w) {
+  if (kt + 1 < src.n_kt) src.issue(cp, kn, vn, kt + 1);  // (kn, vn) were released by the last barrier
   if (kt <= last_kt) {
     f32x16 sc[2];
     qk_tile<D, DL>(sc, kc, qop, off.k);
     bf16x8 pop[4];
-    softmax_tile<D>(st, sc, pop, kt * kBN, w);
+    const bool cached_tile = kt < src.n1 && src.n1 < src.n_kt;
+    softmax_tile<D>(st, sc, pop, src.kv0(kt), cached_tile ? src.P - 1 : w.pos0, cached_tile ? src.P - 1 : w.my_pos,
+                    w);
     pv_tile<D, DL>(st.o, vc, pop, off.v_lo, off.v_hi);
   }
   wait_vmem();      // this thread's copies of tile kt+1 have landed
@@ -362,9 +390,12 @@ __device__ __forceinline__ void store_rows(void* out, size_t orow, int out_bf16,
   }
 }
 
-// CACHED tags the instance launched for a cached prefix (start_pos given); the
-// code is the same, the separate symbol keeps the two apart in kernel profiles.
-template <int D, bool CACHED>
+// MODE 0: no prefix (start_pos null); 1: a cached prefix, the new rows already
+// in the cache; 2: a cached prefix, the new rows in their own arrays (k_new,
+// v_new), read from there and written into the cache at P.. by the workgroups
+// of the first head of each KV group.  Modes 0 and 1 run the same code; the
+// separate symbols keep them apart in kernel profiles.
+template <int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_causal(PrefillArgs a) {
   static_assert(D % 32 == 0 && D <= 128, "head_dim");
   static_assert(kBM == 32 * kWaves, "one 32-row slice per wave");
@@ -418,12 +449,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // this wave
   const int kv_len = P + n_q;
   const int kv_end = min(kv_len, P + q0 + kBM);
-  const int n_kt = (kv_end + kBN - 1) / kBN;
-  const int last_kt = min(n_kt - 1, (w.pos0 + 31) / kBN);
+  KeySource<D, DL> src;
+  src.k = kp;
+  src.v = vp;
+  src.row_bytes = row_bytes;
+  src.P = P;
+  int last_kt;
+  if constexpr (MODE == 2) {  // the new rows have the same layout as the cache's, S rows per sequence
+    src.kn = static_cast<const u16*>(a.k_new) + ((size_t)b * a.S * a.Hkv + g) * D;
+    src.vn = static_cast<const u16*>(a.v_new) + ((size_t)b * a.S * a.Hkv + g) * D;
+    src.n1 = (P + kBN - 1) / kBN;
+    src.n_kt = src.n1 + (kv_end - P + kBN - 1) / kBN;
+    src.len1 = P;
+    src.len2 = n_q;
+    last_kt = min(src.n_kt - 1, src.n1 + (w.row0 + 31) / kBN);
+  } else {
+    src.kn = kp;
+    src.vn = vp;
+    src.n_kt = src.n1 = (kv_end + kBN - 1) / kBN;
+    src.len1 = src.len2 = kv_len;
+    last_kt = min(src.n_kt - 1, (w.pos0 + 31) / kBN);
+  }
+  const int n_kt = src.n_kt;
 
   const TileCopy<DL> cp(wave, w.lane, row_bytes);
-  cp.issue(k0, TileCopy<DL>::rsrc(kp, 0, n_kt, kv_len, row_bytes, 2 * D));
-  cp.issue(v0, TileCopy<DL>::rsrc(vp, 0, n_kt, kv_len, row_bytes, 2 * D));
+  src.issue(cp, k0, v0, 0);
   const LdsOffsets off = lds_offsets<DL>(w);
 
   // Q^T as the B operand: lane holds Q[row ln][16c + 8h2 ..+8]
@@ -445,14 +495,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   wait_vmem();
   __syncthreads();
   for (int kt = 0; kt < n_kt; kt += 2) {
-    tile_step<D, DL>(st, k0, v0, k1, v1, qop, kt, n_kt, last_kt, kp, vp, row_bytes, kv_len, cp, off, w);
-    if (kt + 1 < n_kt)
-      tile_step<D, DL>(st, k1, v1, k0, v0, qop, kt + 1, n_kt, last_kt, kp, vp, row_bytes, kv_len, cp, off, w);
+    tile_step<D, DL>(st, k0, v0, k1, v1, qop, kt, last_kt, src, cp, off, w);
+    if (kt + 1 < n_kt) tile_step<D, DL>(st, k1, v1, k0, v0, qop, kt + 1, last_kt, src, cp, off, w);
   }
 
   // normalise and store; rows past the new tokens are zeros
   const float lsum = sum_xor32(st.lsum);
   if (w.my_row < a.S) store_rows<D>(a.out, orow, a.out_bf16, st.o, w.my_row < n_q, 1.f / lsum, w.h2);
+
+  if constexpr (MODE == 2) {
+    // the cache write of this q-tile's new rows (first head of the KV group
+    // only): rows q0 .. min(q0 + BM, n_q) - 1 to cache rows P + q0 ..  No
+    // workgroup of this launch reads cache rows at or past P.
+    if (h % a.n_rep == 0) {
+      constexpr int kChunks = D / 8;  // 16-byte chunks of a row of one KV head
+      const int rows = min(kBM, n_q - q0);
+      const size_t ld = (size_t)a.Hkv * D;  // elements between rows, both sides
+      u16* kc = const_cast<u16*>(kp) + (size_t)(P + q0) * ld;
+      u16* vc = const_cast<u16*>(vp) + (size_t)(P + q0) * ld;
+      const u16* kn = src.kn + (size_t)q0 * ld;
+      const u16* vn = src.vn + (size_t)q0 * ld;
+      for (int i = tid; i < rows * kChunks; i += 256) {
+        const size_t e = (size_t)(i / kChunks) * ld + 8 * (i % kChunks);
+        const u16x8 kx = *reinterpret_cast<const u16x8*>(kn + e);
+        const u16x8 vx = *reinterpret_cast<const u16x8*>(vn + e);
+        *reinterpret_cast<u16x8*>(kc + e) = kx;
+        *reinterpret_cast<u16x8*>(vc + e) = vx;
+      }
+    }
+  }
 }
 
 
@@ -552,7 +623,7 @@ __device__ __forceinline__ void tile_step_mla(RowState<128>& st, const u16* cc, 
     f32x16 sc[2];
     qk_tile_mla<DR>(sc, cc, rc, qop, qrop, off.k, off_r);
     bf16x8 pop[4];
-    softmax_tile<128>(st, sc, pop, kt * kBN, w);
+    softmax_tile<128>(st, sc, pop, kt * kBN, w.pos0, w.my_pos, w);
     pv_tile<128>(st.o, cc, pop, off.v_lo, off.v_hi);  // V = the latent tile
   }
   wait_vmem();
@@ -711,12 +782,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
 // Explicit instantiations: without them the host stubs of only some of the
 // kernel templates launched below were emitted.
-template __global__ void prefill_causal<128, false>(PrefillArgs);
-template __global__ void prefill_causal<96, false>(PrefillArgs);
-template __global__ void prefill_causal<64, false>(PrefillArgs);
-template __global__ void prefill_causal<128, true>(PrefillArgs);
-template __global__ void prefill_causal<96, true>(PrefillArgs);
-template __global__ void prefill_causal<64, true>(PrefillArgs);
+template __global__ void prefill_causal<128, 0>(PrefillArgs);
+template __global__ void prefill_causal<96, 0>(PrefillArgs);
+template __global__ void prefill_causal<64, 0>(PrefillArgs);
+template __global__ void prefill_causal<128, 1>(PrefillArgs);
+template __global__ void prefill_causal<96, 1>(PrefillArgs);
+template __global__ void prefill_causal<64, 1>(PrefillArgs);
+template __global__ void prefill_causal<128, 2>(PrefillArgs);
+template __global__ void prefill_causal<96, 2>(PrefillArgs);
+template __global__ void prefill_causal<64, 2>(PrefillArgs);
 template __global__ void prefill_mla<96, 48, 96>(MlaPrefillArgs);
 
 }  // namespace
@@ -728,17 +802,18 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const long long wgs = (long long)((a.S + kBM - 1) / kBM) * a.Hq * a.B;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)wgs);
-  const bool cached = a.start_pos != nullptr;
-  if (a.D == 128) {
-    if (cached) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<128, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<128, false>), grid, dim3(256), 0, st, a);
-  } else if (a.D == 96) {
-    if (cached) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<96, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<96, false>), grid, dim3(256), 0, st, a);
-  } else {
-    if (cached) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<64, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<64, false>), grid, dim3(256), 0, st, a);
-  }
+  const int mode = a.k_new ? 2 : a.start_pos ? 1 : 0;
+  if (mode == 2 && !a.start_pos) return hipErrorInvalidValue;
+#define ATTN_PREFILL_LAUNCH(DD)                                                                                  \
+  do {                                                                                                             \
+    if (mode == 2) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<DD, 2>), grid, dim3(256), 0, st, a);         \
+    else if (mode == 1) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<DD, 1>), grid, dim3(256), 0, st, a);    \
+    else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<DD, 0>), grid, dim3(256), 0, st, a);                   \
+  } while (0)
+  if (a.D == 128) ATTN_PREFILL_LAUNCH(128);
+  else if (a.D == 96) ATTN_PREFILL_LAUNCH(96);
+  else ATTN_PREFILL_LAUNCH(64);
+#undef ATTN_PREFILL_LAUNCH
   return hipGetLastError();
 }
 

@@ -163,6 +163,23 @@ def test_cached_prefill_validation():
 
 
 @no_gpu_only
+def test_cached_append_prefill_validation():
+    lib = attn.lib()
+
+    def f(**kw):
+        return lib.attn_prefill_gqa_cached_append(FAKE, kw.get("kn", FAKE), kw.get("vn", FAKE), FAKE, FAKE,
+                                                  kw.get("sp", FAKE), None, FAKE, kw.get("B", 2), 16, 8, 2,
+                                                  kw.get("D", 128), kw.get("T", 64), 0.0, BF16, BF16, None)
+    assert f(sp=None) == NULL
+    assert f(kn=None) == NULL
+    assert f(vn=None) == NULL
+    assert f(T=0) == SHAPE
+    assert f(B=0) == SHAPE
+    assert f(D=80) == UNSUP
+    assert f(vn=FAKE_MIS) == UNSUP
+
+
+@no_gpu_only
 def test_mla_prefill_validation():
     lib = attn.lib()
 
