@@ -219,6 +219,16 @@ def main():
     mla_flops = H * (2 * (r + dR) + 2 * r) * mla_len
     mla_out = torch.empty(MB, H, dv, dtype=torch.float32, device=dev)
     mla_ws = torch.zeros(attn.attn_decode_mla_workspace_bytes(MB, H, r, dR, MT, 0), dtype=torch.uint8, device=dev)
+    # decode step with the new token: the row at cache_lens - 1 of each cache copy is appended again
+    # at that position, so every step rewrites a row with its own value and the caches stay the same
+    mla_last = (mla_cpu["cache_lens"].clamp(1, MT) - 1).to(dev)
+    mla_step_pos = mla_last.to(torch.int32)
+    mla_step_new = [(c[torch.arange(MB, device=dev), mla_last.long()].contiguous(),             # [B, r]
+                     kr[torch.arange(MB, device=dev), mla_last.long()].contiguous())            # [B, dR]
+                    for c, kr in mla_copies]
+    mla_step_out = torch.empty(MB, H, dv, dtype=torch.float32, device=dev)
+    mla_step_ws = torch.zeros(attn.attn_decode_mla_workspace_bytes(MB, H, r, dR, MT, 0), dtype=torch.uint8,
+                              device=dev)
 
     # ---- prefills ----
     pspec = synth.WORKLOADS["llama3_8b_gqa_prefill"]
@@ -238,6 +248,13 @@ def main():
         chk_flops += 4 * CHq * CD * (n * P + n * (n + 1) // 2)   # new token i sees P + i + 1 keys
     chk_tokens = int(chk_cpu["q_lens"].sum())
     chk_out = torch.empty_like(chk["q"])
+    # the same chunk through the one-launch append + prefill: the new rows are the cache rows at
+    # start_pos.., written back unchanged every step
+    chk_sp = chk_cpu["start_pos"].clamp(0, CT)
+    chk_rows = torch.stack([torch.arange(CS) + int(p) for p in chk_sp]).clamp(max=CT - 1)      # [B, S]
+    chk_k_new = torch.stack([chk_cpu["k"][b, chk_rows[b]] for b in range(CB)]).to(dev)
+    chk_v_new = torch.stack([chk_cpu["v"][b, chk_rows[b]] for b in range(CB)]).to(dev)
+    chk_app_out = torch.empty_like(chk["q"])
 
     mpspec = synth.WORKLOADS["minimind768_mla_prefill"]
     mlp = {k: v.to(dev) for k, v in synth.make("minimind768_mla_prefill").items()}
@@ -289,6 +306,16 @@ def main():
     def run_chunked(i):
         attn.attn_prefill_gqa_cached(chk["q"], chk["k"], chk["v"], chk["start_pos"], chk["q_lens"], out=chk_out)
 
+    def run_chunked_append(i):
+        attn.attn_prefill_gqa_cached_append(chk["q"], chk_k_new, chk_v_new, chk["k"], chk["v"], chk["start_pos"],
+                                            chk["q_lens"], out=chk_app_out)
+
+    def run_mla_step(i):  # a different cache copy from the one mla_decode read just before
+        j = (i + 3) % len(mla_copies)
+        (c, kr), (cn, krn) = mla_copies[j], mla_step_new[j]
+        attn.attn_decode_mla_append(mla["q_nope"], mla["q_rope"], cn, krn, mla["w_uk"], mla["w_uv"], c, kr,
+                                    mla_step_pos, out=mla_step_out, workspace=mla_step_ws)
+
     def run_sweep(name):
         w = sweep[name]
 
@@ -302,9 +329,10 @@ def main():
 
     # prefill for new requests, then the decode steps of running ones (the order a serving
     # step takes), then the sweep settings; each part is timed on its own
-    parts = [("prefill", run_prefill), ("chunked_prefill", run_chunked), ("mla_prefill", run_mla_prefill),
-             ("mla_decode", run_mla), ("kv_append", run_append), ("gqa_decode", run_decode),
-             ("gqa_decode_step", run_step), ("gqa_decode_fp8", run_fp8)]
+    parts = [("prefill", run_prefill), ("chunked_prefill", run_chunked), ("chunked_prefill_append", run_chunked_append),
+             ("mla_prefill", run_mla_prefill), ("mla_decode", run_mla), ("mla_decode_step", run_mla_step),
+             ("kv_append", run_append), ("gqa_decode", run_decode), ("gqa_decode_step", run_step),
+             ("gqa_decode_fp8", run_fp8)]
     parts += [(name, run_sweep(name)) for name in sweep]
     parts.append(("minimind768_gqa_decode", run_minimind))
     if want:
@@ -361,7 +389,8 @@ def main():
                          f"cache_lens~U[{dspec['lens'][0]},{dspec['lens'][1]}] (sum {sum_len}) seed={dspec['seed']}, "
                          "bf16 in, fp32 out, default schedule (device-wide unit queue, library-chosen blocks)"),
             "step": ", ".join(name for name, _ in parts) + ": one call each, in this order",
-            "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "prefill": PB * S, "chunked_prefill": chk_tokens,
+            "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "mla_decode_step": MB, "prefill": PB * S,
+                                "chunked_prefill": chk_tokens, "chunked_prefill_append": chk_tokens,
                                 "mla_prefill": MPB * MPS},
         },
         "roofline": {
@@ -420,6 +449,14 @@ def main():
         prefill_part("chunked_prefill", chk_flops, chk_tokens,
                      f"llama3_8b_gqa_chunked_prefill: B={CB} chunk={CS} start_pos={cspec['start_pos']} T_max={CT} "
                      f"Hq={CHq} Hkv={chk['k'].shape[2]} head_dim={CD} seed={cspec['seed']} bf16")
+    if "chunked_prefill_append" in ms:
+        prefill_part("chunked_prefill_append", chk_flops, chk_tokens,
+                     "llama3_8b_gqa_chunked_prefill through attn_prefill_gqa_cached_append: the chunk's K/V rows "
+                     "come in their own arrays and are written into the caches by the same launch")
+    if "mla_decode_step" in ms:
+        decode_part("mla_decode_step", mla_bytes, MB, mla_flops,
+                    "minimind768_mla_decode with the newest rows as the new token (attn_decode_mla_append: "
+                    "decode over cache_lens - 1 rows plus the new row, which is written at cache_lens - 1)")
     if "mla_prefill" in ms:
         prefill_part("mla_prefill", mlp_flops, MPB * MPS,
                      f"minimind768_mla_prefill: B={MPB} S={MPS} H={MPH} nope={MPdn} rope={MPdR} v={MPdv} "

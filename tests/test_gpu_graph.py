@@ -122,3 +122,34 @@ def test_decode_step_and_fp8_decode_graph_replay():
     eager8 = _graph_matches_eager(lambda: attn.attn_decode_gqa_fp8kv(fq, fk, fv, f8["k_scale"], f8["v_scale"], fl,
                                                                      out=out8, workspace=ws8), out8)
     assert torch.isfinite(eager8).all()
+
+
+def test_mla_step_and_cached_append_prefill_graph_replay():
+    """The MLA decode step with the new token and the cached prefill that appends its rows, captured
+    and replayed (their cache writes repeat the same bytes on every replay)."""
+    import mha_mla_kv_amd as attn
+    B, H, dn, dR, dv, r, T = 3, 8, 96, 48, 96, 128, 1500
+    inp = {k: v.cuda() for k, v in synth.mla_decode_inputs(B, H, dn, dR, dv, r, T, [1499, 0, 700], seed=14).items()}
+    g = torch.Generator().manual_seed(14)
+    c_new = torch.randn(B, r, generator=g).to(torch.bfloat16).cuda()
+    kr_new = torch.randn(B, dR, generator=g).to(torch.bfloat16).cuda()
+    print(f"[case] mla decode step graph B={B} H={H} T={T}", flush=True)
+    ws = torch.zeros(attn.attn_decode_mla_workspace_bytes(B, H, r, dR, T, 0), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, H, dv, device="cuda")
+    eager = _graph_matches_eager(lambda: attn.attn_decode_mla_append(
+        inp["q_nope"], inp["q_rope"], c_new, kr_new, inp["w_uk"], inp["w_uv"], inp["c_kv"], inp["k_rope"],
+        inp["cache_lens"], out=out, workspace=ws), out)
+    assert torch.isfinite(eager).all()
+    assert not ws[:4 * B].any()  # the per-sequence chunk counters are back to zero
+
+    Bp, S, Hq, Hkv, D, Tp = 2, 300, 16, 4, 128, 1200
+    pin = {k: v.cuda() for k, v in synth.gqa_prefill_cached_inputs(Bp, S, Hq, Hkv, D, Tp, [700, 64], [300, 111],
+                                                                   seed=15).items()}
+    k_new = torch.stack([pin["k"][b, p:p + S] for b, p in enumerate([700, 64])]).contiguous()
+    v_new = torch.stack([pin["v"][b, p:p + S] for b, p in enumerate([700, 64])]).contiguous()
+    print(f"[case] cached append prefill graph B={Bp} S={S} Hq={Hq} Hkv={Hkv} T={Tp}", flush=True)
+    pout = torch.empty_like(pin["q"])
+    peager = _graph_matches_eager(lambda: attn.attn_prefill_gqa_cached_append(
+        pin["q"], k_new, v_new, pin["k"], pin["v"], pin["start_pos"], pin["q_lens"], out=pout), pout)
+    assert torch.isfinite(peager.float()).all()
+    assert not peager[1, 111:].any()
