@@ -56,6 +56,8 @@ def _declare(lib):
     lib.oracle_mla_prefill_causal.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, D]
     lib.oracle_gqa_prefill_cached.restype = None
     lib.oracle_gqa_prefill_cached.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D]
+    lib.oracle_rope.restype = None
+    lib.oracle_rope.argtypes = [P, P, I, I, I, D, P]
     for name in ("oracle_mla_decode_decompressed", "oracle_mla_decode_absorbed"):
         fn = getattr(lib, name)
         fn.restype = None
@@ -218,6 +220,55 @@ def cache_append(cache, new, start_pos=None, n_new=None) -> np.ndarray:
         n = S if n_new is None else int(n_new[b])
         n = max(0, min(n, S, T_max - P))
         out[b, P:P + n] = new[b, :n]
+    return out
+
+
+def rope(x, positions, base: float = 10000.0, lib=None) -> np.ndarray:
+    """Rotary position embedding (oracle_rope in oracle.c): x [..., H, d] with d even, positions
+    [...] (one absolute position per token, the leading dimensions of x) -> float64 [..., H, d].
+    Pair (x[2j], x[2j+1]) is turned by the angle m * base^(-2j/d)."""
+    x = _f32(x)
+    H, d = x.shape[-2], x.shape[-1]
+    assert d % 2 == 0, "rope width must be even"
+    pos = _i32(np.broadcast_to(np.asarray(positions), x.shape[:-2]))
+    N = int(np.prod(x.shape[:-2], dtype=np.int64))
+    out = np.zeros(x.shape, dtype=np.float64)
+    (lib or load()).oracle_rope(_p(x), _p(pos), N, H, d, float(base), _p(out))
+    return out
+
+
+def rope_append(k_new, k_cache=None, q=None, start_pos=None, n_new=None, x_new=None, x_cache=None,
+                base: float = 10000.0, lib=None) -> dict:
+    """The decode / prefill step before attention in Attention.forward on the MQA & GQA survey page
+    (code section): rotate the new tokens' queries and keys (``rope``) at their absolute positions,
+    then write the rotated keys (and the second stream x, as given) into the caches at start_pos.
+
+    k_new [B,S,Hk,d], q [B,S,Hq,d] or None, k_cache [B,T_max,Hk,d] or None (then the rotated k_new
+    is returned instead), x_new [B,S,...] / x_cache [B,T_max,...] or None.  Token i of sequence b
+    sits at position P + i with P = max(start_pos[b], 0) (None: 0); rows i < n = n_new[b] clamped
+    to [0, S] (None: S) are rotated, the others are returned unchanged.  The cache writes are
+    ``cache_append`` at P with n rows (rows that do not fit in T_max are not stored).
+    Returns float64 arrays: "q" (rotated q), "k" (rotated k_new) and, when given, "k_cache" and
+    "x_cache" (x_cache keeps the input dtype)."""
+    B, S = k_new.shape[0], k_new.shape[1]
+    P = np.zeros(B, np.int64) if start_pos is None else np.maximum(np.asarray(start_pos, np.int64), 0)
+    n = np.full(B, S, np.int64) if n_new is None else np.clip(np.asarray(n_new, np.int64), 0, S)
+    pos = P[:, None] + np.arange(S)[None, :]
+    live = np.arange(S)[None, :] < n[:, None]                          # [B, S] rows that are rotated
+
+    def rotate(t):
+        t64 = _f32(t).astype(np.float64)
+        r = rope(t, pos, base, lib)
+        return np.where(live[:, :, None, None], r, t64)
+
+    out = {"k": rotate(k_new)}
+    if q is not None:
+        out["q"] = rotate(q)
+    if k_cache is not None:
+        kc = _f32(k_cache) if hasattr(k_cache, "detach") else k_cache  # float64 caches are kept as they are
+        out["k_cache"] = cache_append(np.asarray(kc, dtype=np.float64), out["k"], P, n)
+    if x_cache is not None:
+        out["x_cache"] = cache_append(x_cache, x_new, P, n)
     return out
 
 

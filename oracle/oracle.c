@@ -412,3 +412,37 @@ void oracle_mla_decode_absorbed(const float* q_nope, const float* q_rope,
     free(q_abs);
   }
 }
+
+/* Rotary position embedding of head vectors.
+ *
+ * The pages call it without printing it: Attention.forward on the "模型架构｜MQA &
+ * GQA 调研" page (code section) applies apply_rotary_emb(xq, xk, freqs_cis) to
+ * the new tokens' queries and keys before the cache write, and the
+ * MultiHeadLatentAttention listing of the qqstock DeepSeek MLA article applies
+ * apply_rope(query_rope, key_rope, cis=freqs_cis) to the rotated parts only
+ * (section 3: decoupled RoPE).  Reading: the rotation of LLaMA-2, whose
+ * Attention class the GQA page prints.  A head vector x of width d (even) is
+ * taken as d/2 consecutive pairs (x[2j], x[2j+1]), each the complex number
+ * x[2j] + i x[2j+1], which is multiplied by exp(i m theta_j) with
+ * theta_j = base^(-2j/d) and m the token's absolute position:
+ *   out[2j]   = x[2j] cos(m theta_j) - x[2j+1] sin(m theta_j)
+ *   out[2j+1] = x[2j] sin(m theta_j) + x[2j+1] cos(m theta_j)
+ * x [N, H, d] float32 (N tokens of H heads), pos [N] int32, out [N, H, d].
+ */
+void oracle_rope(const float* x, const int32_t* pos, int N, int H, int d, double base, double* out) {
+#pragma omp parallel for schedule(static)
+  for (long n = 0; n < N; ++n) {
+    const double m = (double)pos[n];
+    for (int h = 0; h < H; ++h) {
+      const float* xr = x + (n * H + h) * (long)d;
+      double* o = out + (n * H + h) * (long)d;
+      for (int j = 0; j < d / 2; ++j) {
+        const double theta = pow(base, -2.0 * (double)j / (double)d);
+        const double a = m * theta;
+        const double re = (double)xr[2 * j], im = (double)xr[2 * j + 1];
+        o[2 * j] = re * cos(a) - im * sin(a);
+        o[2 * j + 1] = re * sin(a) + im * cos(a);
+      }
+    }
+  }
+}

@@ -523,7 +523,82 @@ def pin_e4m3_decoding(lib):
     assert oracle.e4m3_to_float([0x01])[0] == 2.0 ** -9 and oracle.e4m3_to_float([0xB8], 0.5)[0] == -0.5
 
 
+def pin_rope_quarter_turns(lib):
+    """Closed forms that fix which elements pair up, the turning direction and the frequency
+    exponent 2j/d.  With d = 4 and base = (2/pi)^2 the second pair turns by base^(-1/2) = pi/2 per
+    position: (x2, x3) = (0.25, -0.5) becomes (0.5, 0.25), (-0.25, 0.5), (-0.5, -0.25) and back at
+    positions 1..4, while the first pair turns by 1 radian per position, taking (1, 0) to
+    (cos m, sin m).  With d = 6 and base = (2/pi)^(3/2) the third pair turns by base^(-2/3) = pi/2."""
+    base4 = (2.0 / math.pi) ** 2
+    x = np.array([[[1.0, 0.0, 0.25, -0.5]]], np.float32)  # one token, one head, d = 4
+    quarter = {1: (0.5, 0.25), 2: (-0.25, 0.5), 3: (-0.5, -0.25), 4: (0.25, -0.5)}
+    for m, (a, b) in quarter.items():
+        got = oracle.rope(x, [m], base4, lib=lib)[0, 0]
+        _close(got, [math.cos(m), math.sin(m), a, b], 1e-14, f"d=4 position {m}")
+    base6 = (2.0 / math.pi) ** 1.5
+    y = np.array([[[0.0, 0.0, 0.0, 0.0, 1.0, 2.0]]], np.float32)
+    _close(oracle.rope(y, [1], base6, lib=lib)[0, 0, 4:], [-2.0, 1.0], 1e-14, "d=6 third pair, position 1")
+    # a lone second element of the first pair stays in the first pair: (0, 1) -> (-sin m, cos m)
+    z = np.array([[[0.0, 1.0, 0.0, 0.0]]], np.float32)
+    _close(oracle.rope(z, [2], base4, lib=lib)[0, 0], [-math.sin(2.0), math.cos(2.0), 0.0, 0.0], 1e-14,
+           "first pair holds elements 0 and 1")
+
+
+def pin_rope_invariants(lib):
+    """Position 0 is the identity; every pair keeps its length; the score between a rotated query
+    at position m and a rotated key at position n depends on n - m only (checked for shifts up to
+    10^5 and the LLaMA base 10000)."""
+    rng = _rng(41)
+    x = _rand(rng, 3, 4, 16)
+    assert np.array_equal(oracle.rope(x, [0, 0, 0], lib=lib), x.astype(np.float64)), "position 0"
+    r = oracle.rope(x, [5, 77, 4096], lib=lib)
+    n0 = np.hypot(x[..., 0::2].astype(np.float64), x[..., 1::2].astype(np.float64))
+    _close(np.hypot(r[..., 0::2], r[..., 1::2]), n0, 1e-13, "pair lengths")
+    q, k = _rand(rng, 1, 1, 64), _rand(rng, 1, 1, 64)
+    for m, n in ((0, 0), (3, 17), (200, 9), (4095, 4096)):
+        ref = float(np.sum(oracle.rope(q, [m], lib=lib) * oracle.rope(k, [n], lib=lib)))
+        for sft in (1, 31, 1000, 100000):
+            got = float(np.sum(oracle.rope(q, [m + sft], lib=lib) * oracle.rope(k, [n + sft], lib=lib)))
+            assert abs(got - ref) <= 1e-9 * max(1.0, abs(ref)), f"score at ({m}, {n}) shifted by {sft}"
+
+
+def pin_rope_append(lib):
+    """The rotate-and-append step: appending a sequence in two chunks (the second at start_pos =
+    the first's length) writes the same caches as appending it in one; each new row is the
+    rotation at its absolute position; rows past n_new are neither rotated nor written, rows past
+    T_max are rotated but not stored; and a decode over the rotated caches does not change when
+    every position is shifted by the same amount (the relative-position property in use)."""
+    rng = _rng(43)
+    B, T, Hq, Hk, d = 2, 24, 4, 2, 8
+    q, k = _rand(rng, B, T, Hq, d), _rand(rng, B, T, Hk, d)
+    v = _rand(rng, B, T, Hk, d)
+    cache_k, cache_v = np.zeros((B, T, Hk, d), np.float32), np.zeros((B, T, Hk, d), np.float32)
+    one = oracle.rope_append(k, cache_k, q, None, None, v, cache_v, lib=lib)
+    P = 10
+    first = oracle.rope_append(k[:, :P], cache_k, q[:, :P], None, None, v[:, :P], cache_v, lib=lib)
+    second = oracle.rope_append(k[:, P:], first["k_cache"], q[:, P:], np.full(B, P), None,
+                                v[:, P:], first["x_cache"], lib=lib)
+    assert np.array_equal(second["k_cache"], one["k_cache"]) and np.array_equal(second["x_cache"], one["x_cache"])
+    assert np.array_equal(np.concatenate([first["q"], second["q"]], 1), one["q"]), "queries in two chunks"
+    pos = np.broadcast_to(np.arange(T), (B, T))
+    _close(one["k"], oracle.rope(k, pos, lib=lib), 0.0, "rows rotated at their positions")
+    # n_new and T_max cuts: sequence 0 starts at T - 3 with 5 new rows (3 stored), sequence 1 has 2 of 5
+    part = oracle.rope_append(k[:, :5], cache_k, q[:, :5], np.array([T - 3, 4]), np.array([5, 2]), lib=lib)
+    _close(part["q"][0], oracle.rope(q[0, :5], np.arange(T - 3, T + 2), lib=lib), 0.0, "rotated past T_max")
+    assert np.array_equal(part["q"][1, 2:], q[1, 2:5].astype(np.float64)), "rows past n_new untouched"
+    assert np.array_equal(part["k_cache"][0, T - 3:], part["k"][0, :3]) and not part["k_cache"][0, :T - 3].any()
+    assert np.array_equal(part["k_cache"][1, 4:6], part["k"][1, :2]) and not part["k_cache"][1, 6:].any()
+    # decode of the last query over all T rotated keys (rows in order): a common shift of 500
+    # positions changes nothing
+    lens = np.full(B, T, np.int32)
+    outs = []
+    for start in (0, 500):
+        r = oracle.rope_append(k, None, q, np.full(B, start), None, lib=lib)
+        outs.append(oracle.gqa_decode(r["q"][:, -1].astype(np.float32), r["k"].astype(np.float32), v, lens, lib=lib))
+    _close(outs[1], outs[0], 2e-6, "decode under a common position shift (float32 rounding of the rotated rows)")
+
+
 ALL_PINS = [pin_decode_vs_sdpa, pin_decode_closed_forms, pin_decode_invariants, pin_decode_head_structure,
             pin_prefill_vs_sdpa, pin_prefill_rows, pin_cached_vs_sdpa, pin_cached_reductions, pin_mla_vs_sdpa, pin_mla_absorbed_equals_decompressed,
             pin_mla_selection, pin_mla_prefill_vs_sdpa, pin_mla_prefill_rows_are_decodes, pin_cache_append,
-            pin_e4m3_decoding]
+            pin_e4m3_decoding, pin_rope_quarter_turns, pin_rope_invariants, pin_rope_append]

@@ -42,6 +42,16 @@ MUTATIONS = {
     # MLA prefill: the causal cut ignores the prefix
     "mla_prefill_top_left": ("const int n = P + i + 1; /* keys 0 .. P + i */\n        for (int t = 0; t < n; ++t) {\n          const float* kr",
                              "const int n = i + 1;\n        for (int t = 0; t < n; ++t) {\n          const float* kr"),
+    # RoPE: pairs taken as (x[j], x[j + d/2]) instead of consecutive elements
+    "rope_half_split_pairs": ("const double re = (double)xr[2 * j], im = (double)xr[2 * j + 1];\n        o[2 * j] = re * cos(a) - im * sin(a);\n        o[2 * j + 1] = re * sin(a) + im * cos(a);",
+                              "const double re = (double)xr[j], im = (double)xr[j + d / 2];\n        o[j] = re * cos(a) - im * sin(a);\n        o[j + d / 2] = re * sin(a) + im * cos(a);"),
+    # RoPE: turned the other way
+    "rope_direction": ("o[2 * j] = re * cos(a) - im * sin(a);\n        o[2 * j + 1] = re * sin(a) + im * cos(a);",
+                       "o[2 * j] = re * cos(a) + im * sin(a);\n        o[2 * j + 1] = -re * sin(a) + im * cos(a);"),
+    # RoPE: frequency exponent j/d instead of 2j/d
+    "rope_exponent": ("pow(base, -2.0 * (double)j / (double)d)", "pow(base, -1.0 * (double)j / (double)d)"),
+    # RoPE: a reflection instead of a rotation (sign slip in the second component)
+    "rope_reflection": ("o[2 * j + 1] = re * sin(a) + im * cos(a);", "o[2 * j + 1] = re * sin(a) - im * cos(a);"),
     # value row taken from the wrong KV head (always head 0)
     "value_head_zero": ("const float* vbase = v + ((long)b * T_max * Hkv + g) * D;", "const float* vbase = v + ((long)b * T_max * Hkv + 0) * D;"),
 }
