@@ -255,6 +255,13 @@ def main():
     chk_k_new = torch.stack([chk_cpu["k"][b, chk_rows[b]] for b in range(CB)]).to(dev)
     chk_v_new = torch.stack([chk_cpu["v"][b, chk_rows[b]] for b in range(CB)]).to(dev)
     chk_app_out = torch.empty_like(chk["q"])
+    # rotary embedding + cache write of the same chunk: q rotated in place (a copy, so the prefill
+    # parts keep their inputs), K rotated into the cache at start_pos.., V copied
+    rope_q = chk["q"].clone()
+    chk_sp_dev = chk["start_pos"]
+    rope_chunk_bytes = 2 * (CB * CS * CHq * CD * 2) + 2 * 2 * (CB * CS * chk["k"].shape[2] * CD * 2)
+    rope_dec_q = dec["q"].clone().unsqueeze(1)                       # [B, 1, Hq, D]
+    rope_dec_bytes = 2 * (B * Hq * D * 2) + 2 * 2 * (B * Hkv * D * 2)
 
     mpspec = synth.WORKLOADS["minimind768_mla_prefill"]
     mlp = {k: v.to(dev) for k, v in synth.make("minimind768_mla_prefill").items()}
@@ -310,6 +317,12 @@ def main():
         attn.attn_prefill_gqa_cached_append(chk["q"], chk_k_new, chk_v_new, chk["k"], chk["v"], chk["start_pos"],
                                             chk["q_lens"], out=chk_app_out)
 
+    def run_rope_chunk(i):
+        attn.attn_rope_append(chk_k_new, chk["k"], rope_q, chk_sp_dev, chk["q_lens"], chk_v_new, chk["v"])
+
+    def run_rope_decode(i):
+        attn.attn_rope_append(app_k, dec["k"], rope_dec_q, app_pos, None, app_v, dec["v"])
+
     def run_mla_step(i):  # a different cache copy from the one mla_decode read just before
         j = (i + 3) % len(mla_copies)
         (c, kr), (cn, krn) = mla_copies[j], mla_step_new[j]
@@ -331,7 +344,8 @@ def main():
     # step takes), then the sweep settings; each part is timed on its own
     parts = [("prefill", run_prefill), ("chunked_prefill", run_chunked), ("chunked_prefill_append", run_chunked_append),
              ("mla_prefill", run_mla_prefill), ("mla_decode", run_mla), ("mla_decode_step", run_mla_step),
-             ("kv_append", run_append), ("gqa_decode", run_decode), ("gqa_decode_step", run_step),
+             ("kv_append", run_append), ("rope_append_decode", run_rope_decode), ("rope_append_chunk", run_rope_chunk),
+             ("gqa_decode", run_decode), ("gqa_decode_step", run_step),
              ("gqa_decode_fp8", run_fp8)]
     parts += [(name, run_sweep(name)) for name in sweep]
     parts.append(("minimind768_gqa_decode", run_minimind))
@@ -479,6 +493,19 @@ def main():
         P["kv_append"] = {"ms": round(ms["kv_append"], 5), "bytes_per_launch": app_bytes,
                           "GB/s": round(rate(app_bytes, "kv_append"), 1),
                           "workload": f"llama3_8b_gqa_decode step write: B={B} rows of Hkv={Hkv} x {D} for K and V"}
+    if "rope_append_chunk" in ms:
+        P["rope_append_chunk"] = {
+            "ms": round(ms["rope_append_chunk"], 5), "bytes_per_launch": rope_chunk_bytes,
+            "GB/s": round(rate(rope_chunk_bytes, "rope_append_chunk"), 1),
+            "hbm_frac": round(rate(rope_chunk_bytes, "rope_append_chunk") / HBM_PEAK_GBS, 4),
+            "workload": f"llama3_8b_gqa_chunked_prefill chunk through attn_rope_append: q [{CB},{CS},{CHq},{CD}] "
+                        f"rotated in place, K rotated into the cache and V copied at start_pos (bf16, base 10000)"}
+    if "rope_append_decode" in ms:
+        P["rope_append_decode"] = {
+            "ms": round(ms["rope_append_decode"], 5), "bytes_per_launch": rope_dec_bytes,
+            "GB/s": round(rate(rope_dec_bytes, "rope_append_decode"), 1),
+            "workload": f"llama3_8b_gqa_decode step through attn_rope_append: q [{B},1,{Hq},{D}] rotated in place, "
+                        f"one K row rotated into the cache and one V row copied per sequence"}
     for name, w in sweep.items():
         decode_part(name, w["bytes"], w["tokens"], w["flops"], w["workload"])
     if "minimind768_gqa_decode" in ms:

@@ -472,6 +472,57 @@ attn_status attn_cache_append(const void* new_a, void* cache_a, int row_bytes_a,
                               int row_bytes_b, const int32_t* start_pos, const int32_t* n_new, int B, int S,
                               int T_max, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Rotary position embedding of the new tokens, fused with the cache write.
+ *
+ *   P = max(start_pos[b], 0) (NULL: 0), n = n_new[b] clamped to [0, S] (NULL: S);
+ *   token i < n of sequence b sits at position m = P + i, and every head vector
+ *   x (width d = rope_dim) of its query and key rows is rotated pair by pair:
+ *     x'[2j]   = x[2j] cos(m t_j) - x[2j+1] sin(m t_j)
+ *     x'[2j+1] = x[2j] sin(m t_j) + x[2j+1] cos(m t_j),   t_j = rope_base^(-2j/d)
+ *   q[b,i]           <- rotated q[b,i]                (in place; q may be NULL)
+ *   k_cache[b,m]     <- rotated k_new[b,i]            when m < T_max
+ *                       (k_cache NULL: k_new[b,i] is rotated in place instead)
+ *   x_cache[b,m]     <- x_new[b,i], bytes as given    when m < T_max and x_row_bytes > 0
+ *   rows i >= n are not touched.
+ *
+ * The step of Attention.forward on the "模型架构｜MQA & GQA 调研" page (code
+ * section) before the cache is read: apply_rotary_emb(xq, xk, freqs_cis), then
+ * the cache_k / cache_v writes at start_pos.  The pages call the rotation but do
+ * not print it; this is LLaMA-2's rotation (consecutive pairs as complex
+ * numbers times exp(i m t_j)), whose Attention class that page prints, with
+ * LLaMA's rope_base 10000 as the usual choice.  For MLA (qqstock DeepSeek MLA
+ * article, sections 1 and 3, and the apply_rope call of its listing) q is
+ * q_rope with Hq = H, k is the shared k_rope with Hk = 1, and x is the latent
+ * c_kv row.  For GQA q is [.., Hq, head_dim], k the new K rows with Hk = Hkv and
+ * x the new V rows.  Follow with attn_decode_gqa / attn_prefill_gqa_cached /
+ * attn_decode_mla_absorbed / attn_prefill_mla_causal over the extended cache,
+ * or rotate in place (k_cache NULL) and pass the rows to attn_decode_gqa_append,
+ * attn_prefill_gqa_cached_append or attn_decode_mla_append.
+ *
+ * The angle m t_j and its reduction modulo 2 pi are computed in fp64, the sine
+ * and cosine of the reduced angle and the rotation in fp32, and the result is
+ * rounded once to dtype.
+ *
+ *   q       [B, S, Hq, rope_dim]  dtype, or NULL
+ *   k_new   [B, S, Hk, rope_dim]  dtype, required
+ *   k_cache [B, T_max, Hk, rope_dim] dtype, or NULL
+ *   x_new   [B, S, x_row_bytes bytes], x_cache [B, T_max, x_row_bytes bytes]
+ *           (x_row_bytes = 0: none; x needs k_cache)
+ *   start_pos, n_new [B] int32 device memory, or NULL
+ *   dtype   ATTN_BF16 or ATTN_F32 (of q, k_new and k_cache)
+ *
+ * rope_dim must be a multiple of 8 in [8, 1024] and x_row_bytes a multiple of
+ * 16 (else ATTN_ERR_UNSUPPORTED); every buffer 16-byte aligned (else
+ * ATTN_ERR_UNSUPPORTED); rope_base positive and finite (else ATTN_ERR_SHAPE);
+ * T_max >= 1 when a cache is written.  All pointers are device memory owned by
+ * the caller; new rows and caches must not overlap.  One launch, no workspace.
+ */
+attn_status attn_rope_append(void* q, void* k_new, void* k_cache, const void* x_new, void* x_cache,
+                             const int32_t* start_pos, const int32_t* n_new, int B, int S, int Hq, int Hk,
+                             int rope_dim, int x_row_bytes, int T_max, float rope_base, attn_dtype dtype,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

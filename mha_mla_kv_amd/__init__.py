@@ -62,6 +62,8 @@ def _declare(lib):
     lib.attn_decode_gqa_append_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.attn_decode_gqa_append.restype = I
     lib.attn_decode_gqa_append.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, ctypes.c_size_t, P]
+    lib.attn_rope_append.restype = I
+    lib.attn_rope_append.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
     lib.attn_cache_append.restype = I
     lib.attn_cache_append.argtypes = [P, P, I, P, P, I, P, P, I, I, I, P]
     lib.attn_prefill_mla_causal.restype = I
@@ -393,6 +395,51 @@ def attn_prefill_mla_causal(q_nope, q_rope, w_uk, w_uv, c_kv, k_rope, start_pos=
     return out
 
 
+def attn_rope_append(k_new, k_cache=None, q=None, start_pos=None, n_new=None, x_new=None, x_cache=None,
+                     rope_base: float = 10000.0):
+    """Rotary position embedding of the new tokens fused with the cache write, in one launch: token
+    i of sequence b sits at position max(start_pos[b], 0) + i; q (in place) and k_new are rotated
+    pair by pair (angle m * rope_base^(-2j/d)); the rotated keys go to k_cache and the x_new rows,
+    as given, to x_cache at those positions (rows past T_max are not stored).  k_cache None: k_new
+    is rotated in place.  Rows i >= n_new[b] are left alone.
+
+    k_new [B,S,Hk,d] (or [B,S,d]: Hk = 1), q [B,S,Hq,d] or None, k_cache [B,T_max,Hk,d] (or
+    [B,T_max,d]) or None, all bf16 or all fp32; x_new [B,S,...] and x_cache [B,T_max,...] of any
+    dtype with equal row sizes, or None; start_pos, n_new [B] int32 or None.  Returns None."""
+    _check(k_new, "k_new")
+    if k_new.dim() not in (3, 4):
+        raise ValueError(f"k_new must be [B, S, Hk, d] or [B, S, d] (got {tuple(k_new.shape)})")
+    B, S, d = k_new.shape[0], k_new.shape[1], k_new.shape[-1]
+    Hk = k_new.shape[2] if k_new.dim() == 4 else 1
+    Hq, T_max, xb = 0, 0, 0
+    if q is not None:
+        _check(q, "q", dtype=k_new.dtype)
+        if q.dim() != 4 or tuple(q.shape[:2]) != (B, S) or q.shape[3] != d:
+            raise ValueError(f"q must be [B={B}, S={S}, Hq, {d}] (got {tuple(q.shape)})")
+        Hq = q.shape[2]
+    if k_cache is not None:
+        _check(k_cache, "k_cache", dtype=k_new.dtype)
+        if k_cache.dim() != k_new.dim() or k_cache.shape[0] != B or tuple(k_cache.shape[2:]) != tuple(k_new.shape[2:]):
+            raise ValueError(f"k_cache must be [B, T_max] + {tuple(k_new.shape[2:])} (got {tuple(k_cache.shape)})")
+        T_max = k_cache.shape[1]
+    if (x_new is None) != (x_cache is None):
+        raise ValueError("x_new and x_cache go together")
+    if x_new is not None:
+        _check(x_new, "x_new", dtype=x_new.dtype)
+        _check(x_cache, "x_cache", dtype=x_new.dtype)
+        if k_cache is None or tuple(x_new.shape[:2]) != (B, S) or x_cache.shape[0] != B or \
+                x_cache.shape[1] != T_max or tuple(x_cache.shape[2:]) != tuple(x_new.shape[2:]):
+            raise ValueError("x_new must be [B, S, ...] and x_cache [B, T_max, ...] (with k_cache)")
+        xb = x_new[0, 0].numel() * x_new.element_size()
+    for t, name in ((start_pos, "start_pos"), (n_new, "n_new")):
+        if t is not None:
+            _check(t, name, shape=(B,), dtype=torch.int32)
+    st = lib().attn_rope_append(_ptr(q), _ptr(k_new), _ptr(k_cache), _ptr(x_new), _ptr(x_cache), _ptr(start_pos),
+                                _ptr(n_new), B, S, Hq, Hk, d, xb, T_max, float(rope_base), _dt(k_new),
+                                _stream(k_new.device))
+    _raise_if(st, "attn_rope_append")
+
+
 def attn_cache_append(new_a, cache_a, new_b=None, cache_b=None, start_pos=None, n_new=None):
     """cache_a[b, start_pos[b] + i] = new_a[b, i] for i < n_new[b] (and the same for the b pair):
     K and V caches [B, T_max, Hkv, D] with new rows [B, S, Hkv, D], or the MLA caches c_kv
@@ -516,6 +563,6 @@ def attn_decode_mla_append(q_nope, q_rope, c_new, k_rope_new, w_uk, w_uv, c_kv, 
 
 __all__ = ["attn_decode_gqa", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_noalloc", "NOALLOC_SCRATCH_BYTES", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
            "attn_decode_gqa_append_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached", "attn_prefill_gqa_cached_append",
-           "attn_prefill_mla_causal", "attn_cache_append",
+           "attn_prefill_mla_causal", "attn_cache_append", "attn_rope_append",
            "attn_decode_mla_absorbed", "attn_decode_mla_append", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",
            "AttnError", "lib", "header_functions", "LIB_PATH", "ATTN_F32", "ATTN_BF16"]

@@ -470,6 +470,51 @@ attn_status attn_prefill_mla_causal(const void* q_nope, const void* q_rope, cons
   return hip_status(attn::launch_mla_prefill(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+attn_status attn_rope_append(void* q, void* k_new, void* k_cache, const void* x_new, void* x_cache,
+                             const int32_t* start_pos, const int32_t* n_new, int B, int S, int Hq, int Hk,
+                             int rope_dim, int x_row_bytes, int T_max, float rope_base, attn_dtype dtype,
+                             void* stream) {
+  static const char* fn = "attn_rope_append";
+  if (!k_new) return fail(ATTN_ERR_NULL, "%s: k_new must be non-NULL", fn);
+  if (B <= 0 || S <= 0 || Hk <= 0 || rope_dim <= 0 || x_row_bytes < 0 || (q && Hq <= 0))
+    return fail(ATTN_ERR_SHAPE, "%s: sizes must be positive (B=%d S=%d Hq=%d Hk=%d rope_dim=%d x_row_bytes=%d)", fn,
+                B, S, Hq, Hk, rope_dim, x_row_bytes);
+  if ((k_cache || x_row_bytes > 0) && T_max <= 0)
+    return fail(ATTN_ERR_SHAPE, "%s: T_max must be positive when a cache is written (T_max=%d)", fn, T_max);
+  if (x_row_bytes > 0 && (!x_new || !x_cache))
+    return fail(ATTN_ERR_NULL, "%s: x_new and x_cache must be non-NULL when x_row_bytes > 0", fn);
+  if (x_row_bytes > 0 && !k_cache)
+    return fail(ATTN_ERR_NULL, "%s: x is written only together with k_cache", fn);
+  if (!valid_dtype(dtype)) return fail(ATTN_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  if (rope_dim % 8 != 0 || rope_dim > attn::rope_max_dim())
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: rope_dim=%d must be a multiple of 8 in [8, %d]", fn, rope_dim,
+                attn::rope_max_dim());
+  if (x_row_bytes % 16 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: x_row_bytes=%d must be a multiple of 16", fn, x_row_bytes);
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(k_cache) || !aligned16(x_new) || !aligned16(x_cache))
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: buffers must be 16-byte aligned", fn);
+  if (!(rope_base > 0.f) || !std::isfinite(rope_base))
+    return fail(ATTN_ERR_SHAPE, "%s: rope_base must be positive and finite (got %g)", fn, (double)rope_base);
+  attn::RopeAppendArgs a;
+  a.q = q;
+  a.k_new = k_new;
+  a.k_cache = k_cache;
+  a.x_new = x_row_bytes > 0 ? x_new : nullptr;
+  a.x_cache = x_row_bytes > 0 ? x_cache : nullptr;
+  a.start_pos = start_pos;
+  a.n_new = n_new;
+  a.B = B;
+  a.S = S;
+  a.Hq = q ? Hq : 0;
+  a.Hk = Hk;
+  a.d = rope_dim;
+  a.x_row_bytes = x_row_bytes;
+  a.T_max = T_max;
+  a.log2_base = std::log2((double)rope_base);
+  a.bf16 = dtype == ATTN_BF16;
+  return hip_status(attn::launch_rope_append(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 attn_status attn_cache_append(const void* new_a, void* cache_a, int row_bytes_a, const void* new_b, void* cache_b,
                               int row_bytes_b, const int32_t* start_pos, const int32_t* n_new, int B, int S,
                               int T_max, void* stream) {

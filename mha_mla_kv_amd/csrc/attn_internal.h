@@ -120,6 +120,19 @@ struct MlaDecodeArgs {
   void* kr_cache;       // the k_rope array
 };
 
+struct RopeAppendArgs {
+  void* q;                      // [B, S, Hq, d] rotated in place, or null
+  const void* k_new;            // [B, S, Hk, d]
+  void* k_cache;                // [B, T_max, Hk, d] written at the positions, or null: k_new rotated in place
+  const void* x_new;            // [B, S, x_row_bytes] copied as is (x_row_bytes 0: none)
+  void* x_cache;                // [B, T_max, x_row_bytes]
+  const int32_t* start_pos;     // [B], or null: 0
+  const int32_t* n_new;         // [B], or null: S
+  int B, S, Hq, Hk, d, x_row_bytes, T_max;
+  double log2_base;             // log2 of the rope base
+  int bf16;                     // 1: bf16 q and k, 0: fp32
+};
+
 // Each launcher validates nothing (the host layer has done it) and returns the
 // HIP status of its launches.  Returns hipErrorInvalidValue for an
 // unsupported template combination (the host layer checks *_supported first).
@@ -133,6 +146,9 @@ bool mla_prefill_supported(int dn, int dR, int dv, int r);
 hipError_t launch_mla_prefill(const MlaPrefillArgs& a, hipStream_t stream);
 
 hipError_t launch_cache_append(const CacheAppendArgs& a, hipStream_t stream);
+
+int rope_max_dim();
+hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t stream);
 
 bool mla_decode_supported(int H, int r, int dR);
 hipError_t launch_mla_decode(const MlaDecodeArgs& a, hipStream_t stream);

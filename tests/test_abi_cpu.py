@@ -290,3 +290,25 @@ def test_mla_append_validation():
     assert f(B=0) == SHAPE
     assert f(dv=90) == UNSUP
     assert f(ws=None) == WS
+
+
+@no_gpu_only
+def test_rope_append_validation():
+    lib = attn.lib()
+
+    def f(k=FAKE, kc=FAKE, x=FAKE, xc=FAKE, **kw):
+        return lib.attn_rope_append(kw.get("q", FAKE), k, kc, x, xc, None, None, kw.get("B", 2), 4, 8, 2,
+                                    kw.get("d", 128), kw.get("xb", 512), kw.get("T", 64), kw.get("base", 10000.0),
+                                    BF16, None)
+    assert f(k=None) == NULL
+    assert f(x=None) == NULL
+    assert f(kc=None) == NULL          # x goes only with a key cache
+    assert f(kc=None, xb=0, T=0) == HIP       # valid: reaches the launch, which fails without a GPU
+    assert f(B=0) == SHAPE
+    assert f(T=0) == SHAPE
+    assert f(base=0.0) == SHAPE
+    assert f(base=float("inf")) == SHAPE
+    assert f(d=12) == UNSUP
+    assert f(d=2048) == UNSUP
+    assert f(xb=24) == UNSUP
+    assert f(q=FAKE_MIS) == UNSUP
