@@ -169,6 +169,15 @@ def main():
     f8_v = (torch.randn(B, T_max, Hkv, D, device=dev, generator=gen) / f8_scale).to(torch.float8_e4m3fn)
     f8_bytes = dec_bytes // 2                                 # one byte per cached element
     f8_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    # paged view of the same caches: 64-position pages, every sequence's pages scattered over the
+    # whole pool by a seeded permutation (the pool is the contiguous cache, seen as pages)
+    pg_size = 64
+    pg_max = T_max // pg_size
+    pg_k = dec["k"].view(B * pg_max, pg_size, Hkv, D)
+    pg_v = dec["v"].view(B * pg_max, pg_size, Hkv, D)
+    pg_table = torch.randperm(B * pg_max, generator=torch.Generator().manual_seed(11)).to(torch.int32)
+    pg_table = pg_table.view(B, pg_max).to(dev)
+    pg_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     step_ws = torch.zeros(attn.attn_decode_gqa_append_workspace_bytes(B, Hq, Hkv, D, T_max, 0), dtype=torch.uint8,
                           device=dev)
 
@@ -302,6 +311,9 @@ def main():
         attn.attn_decode_gqa_append(dec["q"], app_new_k, app_new_v, dec["k"], dec["v"], app_pos, out=step_out,
                                     workspace=step_ws)
 
+    def run_paged(i):
+        attn.attn_decode_gqa_paged(dec["q"], pg_k, pg_v, pg_table, dec["cache_lens"], out=pg_out, workspace=dec_ws)
+
     def run_fp8(i):
         attn.attn_decode_gqa_fp8kv(dec["q"], f8_k, f8_v, f8_scale, f8_scale, dec["cache_lens"], out=f8_out,
                                    workspace=dec_ws)
@@ -345,7 +357,7 @@ def main():
     parts = [("prefill", run_prefill), ("chunked_prefill", run_chunked), ("chunked_prefill_append", run_chunked_append),
              ("mla_prefill", run_mla_prefill), ("mla_decode", run_mla), ("mla_decode_step", run_mla_step),
              ("kv_append", run_append), ("rope_append_decode", run_rope_decode), ("rope_append_chunk", run_rope_chunk),
-             ("gqa_decode", run_decode), ("gqa_decode_step", run_step),
+             ("gqa_decode", run_decode), ("gqa_decode_paged", run_paged), ("gqa_decode_step", run_step),
              ("gqa_decode_fp8", run_fp8)]
     parts += [(name, run_sweep(name)) for name in sweep]
     parts.append(("minimind768_gqa_decode", run_minimind))
@@ -485,6 +497,10 @@ def main():
         decode_part("gqa_decode_fp8", f8_bytes, B, None,
                     "llama3_8b_gqa_decode shape and lengths, K/V as FP8 E4M3 codes of N(0,1)/scale "
                     "(device-drawn, seed 8), scale 4.5/448")
+    if "gqa_decode_paged" in ms:
+        decode_part("gqa_decode_paged", dec_bytes, B, None,
+                    f"llama3_8b_gqa_decode shape and lengths over paged caches: {pg_size}-position pages, each "
+                    "sequence's pages scattered over the pool by a seeded permutation (attn_decode_gqa_paged)")
     if "gqa_decode_step" in ms:
         decode_part("gqa_decode_step", dec_bytes, B, None,
                     "llama3_8b_gqa_decode with the newest rows as the new token "

@@ -207,6 +207,42 @@ attn_status attn_decode_gqa_append(const void* q, const void* k_new, const void*
                                    void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* GQA decode over paged K/V caches (a page pool and a block table).
+ *
+ *   T_max = page_size * max_pages_per_seq, L = cache_lens[b] clamped to [0, T_max];
+ *   K[b,t,g,:] = k_pages[block_table[b * max_pages_per_seq + t / page_size], t % page_size, g, :]
+ *   (V likewise from v_pages), and out is attn_decode_gqa over those rows.
+ *
+ * The pages mention paging only as the serving system's cost of handing out
+ * cache memory to many requests (the "MHA, MQA và GQA" interactive e-book, whose
+ * byte counts leave it out on purpose), and define no scheme.  Reading: the common
+ * block-table layout -- fixed-size pages in one pool, per sequence a row of
+ * page numbers in position order; a page holds page_size consecutive
+ * positions, each row the same [Hkv, head_dim] layout as a contiguous cache.
+ * Same arithmetic and results as attn_decode_gqa on the gathered caches.
+ *
+ *   q           [B, Hq, head_dim]                       bf16
+ *   k_pages, v_pages [n_pages, page_size, Hkv, head_dim] bf16
+ *   block_table [B, max_pages_per_seq] int32, device memory: entries for the
+ *               pages below ceil(L / page_size) are read, each clamped to
+ *               [0, n_pages); unused entries may hold anything
+ *   cache_lens  [B] int32        out [B, Hq, head_dim] out_dtype
+ *
+ * Supported: in_dtype ATTN_BF16, head_dim 64/96/128, page_size a multiple of 32
+ * (else ATTN_ERR_UNSUPPORTED), split_tokens 0 or a multiple of 64 up to 1024.
+ * workspace: attn_decode_gqa_workspace_bytes(B, Hq, Hkv, head_dim,
+ * page_size * max_pages_per_seq, split_tokens) bytes, 256-byte aligned; its
+ * first 4 bytes zero before the first call (every call leaves them zero).
+ * Errors as attn_decode_gqa, plus ATTN_ERR_NULL for a NULL block_table and
+ * ATTN_ERR_SHAPE for non-positive page counts.
+ */
+attn_status attn_decode_gqa_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                                  const int32_t* cache_lens, void* out, int B, int Hq, int Hkv, int head_dim,
+                                  int page_size, int n_pages, int max_pages_per_seq, float softmax_scale,
+                                  attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Causal GQA prefill (no cached prefix): query i attends to keys j <= i.
  *
  *   out[b,i,h,:] = sum_{j <= i} softmax_j(scale * q[b,i,h,:] . k[b,j,g,:]) v[b,j,g,:]

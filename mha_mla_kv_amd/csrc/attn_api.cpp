@@ -186,7 +186,8 @@ attn_status gqa_decode_common(const char* fn, const void* q, const void* k_new, 
                               const void* v_cache, const int32_t* cache_lens, void* out, int B, int Hq, int Hkv,
                               int head_dim, int T_max, float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype,
                               int split_tokens, void* workspace, size_t workspace_bytes, void* stream,
-                              const float* kv_scales = nullptr, bool noalloc = false) {
+                              const float* kv_scales = nullptr, bool noalloc = false,
+                              const int32_t* block_table = nullptr, int page_size = 0, int n_pages = 0) {
   const bool append = k_new != nullptr;
   const bool kv_fp8 = kv_scales != nullptr;
   if (!q || !k_cache || !v_cache || !cache_lens || !out)
@@ -283,6 +284,10 @@ attn_status gqa_decode_common(const char* fn, const void* q, const void* k_new, 
   a.v_new = v_new;
   a.k_cache = const_cast<void*>(k_cache);
   a.v_cache = const_cast<void*>(v_cache);
+  a.block_table = block_table;
+  a.page_size = page_size;
+  a.table_stride = block_table ? T_max / page_size : 0;
+  a.n_pages = n_pages;
   return hip_status(attn::launch_gqa_decode(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -296,6 +301,29 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
   return gqa_decode_common("attn_decode_gqa", q, nullptr, nullptr, k_cache, v_cache, cache_lens, out, B, Hq, Hkv,
                            head_dim, T_max, softmax_scale, in_dtype, out_dtype, split_tokens, workspace,
                            workspace_bytes, stream);
+}
+
+attn_status attn_decode_gqa_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                                  const int32_t* cache_lens, void* out, int B, int Hq, int Hkv, int head_dim,
+                                  int page_size, int n_pages, int max_pages_per_seq, float softmax_scale,
+                                  attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  static const char* fn = "attn_decode_gqa_paged";
+  if (!block_table) return fail(ATTN_ERR_NULL, "%s: block_table must be non-NULL", fn);
+  if (page_size <= 0 || n_pages <= 0 || max_pages_per_seq <= 0)
+    return fail(ATTN_ERR_SHAPE, "%s: page_size, n_pages and max_pages_per_seq must be positive (%d, %d, %d)", fn,
+                page_size, n_pages, max_pages_per_seq);
+  if ((long long)page_size * max_pages_per_seq > 0x7fffffffLL)
+    return fail(ATTN_ERR_SHAPE, "%s: page_size * max_pages_per_seq too large", fn);
+  if (page_size % 32 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: page_size=%d must be a multiple of 32", fn, page_size);
+  if (in_dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: paged caches are built for bf16 inputs only", fn);
+  if (split_tokens > 1024)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: split_tokens=%d: at most 1024 with paged caches", fn, split_tokens);
+  return gqa_decode_common(fn, q, nullptr, nullptr, k_pages, v_pages, cache_lens, out, B, Hq, Hkv, head_dim,
+                           page_size * max_pages_per_seq, softmax_scale, in_dtype, out_dtype, split_tokens, workspace,
+                           workspace_bytes, stream, nullptr, false, block_table, page_size, n_pages);
 }
 
 attn_status attn_decode_gqa_noalloc(const void* q, const void* k_cache, const void* v_cache,

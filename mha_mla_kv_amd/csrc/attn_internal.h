@@ -48,6 +48,15 @@ struct GqaDecodeArgs {
   // the K scale is folded into scale_log2e
   int kv_fp8;
   float v_scale;
+  // paged caches (block_table != null): k and v are pools of n_pages pages of
+  // page_size positions ([n_pages, page_size, Hkv, D]); position t of sequence
+  // b sits in page block_table[b * table_stride + t / page_size] (clamped to
+  // [0, n_pages)), at row t % page_size.  page_size is a multiple of 32 and a
+  // unit spans at most 128 pages.
+  const int32_t* block_table = nullptr;
+  int page_size = 0;
+  int table_stride = 0;
+  int n_pages = 0;
 };
 
 struct PrefillArgs {

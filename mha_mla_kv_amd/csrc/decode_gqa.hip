@@ -560,7 +560,11 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
 // KV8: the caches hold OCP FP8 E4M3 values (one byte each), converted to bf16
 // (exactly) on their way into LDS; the K scale is folded into the softmax
 // scale by the host, the V scale is applied to each unit's output.
-template <int D, int HB, bool QUEUE, bool KV8 = false>
+// PAGED: the caches are page pools and a block table maps positions to pages;
+// a unit's page numbers are read once (two per lane) when the unit begins, and
+// every 32-position tile, which lies within one page, reads its page number
+// from those registers.
+template <int D, int HB, bool QUEUE, bool KV8 = false, bool PAGED = false>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(HB > 1 ? 1 : (D >= 96 ? (QUEUE ? 2 : 3) : 4))))
 void gqa_decode_bf16(GqaDecodeArgs a) {
@@ -609,11 +613,28 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   const int lrow = lane / kLanesPerRow, lunit = min(lane % kLanesPerRow, kUnits - 1);
   const unsigned row_off = (unsigned)(lrow * row_bytes + 16 * lunit);
 
+  // base of this (sequence, KV head)'s rows (paged: of the head's rows in the pool)
   auto k_head = [&](const Unit& u) {
+    if constexpr (PAGED) return static_cast<const char*>(a.k) + (size_t)u.g * D * EB;
     return static_cast<const char*>(a.k) + ((size_t)u.b * a.T_max * a.Hkv + u.g) * D * EB;
   };
   auto v_head = [&](const Unit& u) {
+    if constexpr (PAGED) return static_cast<const char*>(a.v) + (size_t)u.g * D * EB;
     return static_cast<const char*>(a.v) + ((size_t)u.b * a.T_max * a.Hkv + u.g) * D * EB;
+  };
+  // paged: the current unit's first page slot and its page numbers (slot
+  // unit_p0 + i in lane i % 64 of pg[i / 64])
+  int unit_p0 = 0;
+  int pg[2] = {0, 0};
+  // address of position t0's row (t0 a multiple of 32)
+  auto tile_base = [&](const char* head0, int t0) -> const char* {
+    if constexpr (PAGED) {
+      const int rel = min(max(t0 / a.page_size - unit_p0, 0), 127);
+      const int e = rel < 64 ? __builtin_amdgcn_readlane(pg[0], rel) : __builtin_amdgcn_readlane(pg[1], rel - 64);
+      const int page = min(max(e, 0), a.n_pages - 1);
+      return head0 + ((size_t)page * a.page_size + (size_t)(t0 - (t0 / a.page_size) * a.page_size)) * row_bytes;
+    }
+    return head0 + (size_t)t0 * row_bytes;
   };
 
   // K and V tiles of 32 positions are read in row order with streaming
@@ -630,8 +651,7 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
     // (row_bytes >= EB * D, so no rows gives a non-positive count)
     const int rows = min(max(c1 - t0, 0), kDecodeTileTokens);
     const int n = max(rows * row_bytes - row_bytes + EB * D, 0);
-    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(head0 + (size_t)t0 * row_bytes), (short)0, n,
-                                                      0x00020000);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(tile_base(head0, t0)), (short)0, n, 0x00020000);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
       r[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
@@ -671,6 +691,14 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   // The query block is read through a buffer resource that ends with head
   // n_rep - 1: the padding heads read as zeros, with no branch.
   auto begin_unit = [&](const Unit& u) {
+    if constexpr (PAGED) {
+      // the unit's page numbers, before the query block (the first tile waits for them)
+      unit_p0 = u.t0 / a.page_size;
+      const int np = (u.t1 - 1) / a.page_size - unit_p0 + 1;
+      const int32_t* tb = a.block_table + (size_t)u.b * a.table_stride + unit_p0;
+      pg[0] = lane < np ? tb[lane] : 0;
+      pg[1] = lane + 64 < np ? tb[lane + 64] : 0;
+    }
     const u16* qp = static_cast<const u16*>(a.q) + ((size_t)u.b * a.Hq + (size_t)u.g * n_rep) * D;
     const auto qs = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(qp), (short)0, n_rep * D * 2, 0x00020000);
 #pragma unroll
@@ -1048,12 +1076,13 @@ hipError_t launch_one(Kernel kernel, const GqaDecodeArgs& a, dim3 grid, hipStrea
 constexpr int kMfmaWgsPerCu = 1;
 constexpr int kMfmaWgsPerCuFp8 = 2;
 
-template <int D, bool QUEUE, bool KV8 = false>
+template <int D, bool QUEUE, bool KV8 = false, bool PAGED = false>
 hipError_t launch_bf16(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
   const int hb = (a.n_rep + 15) / 16;
-  if (hb == 1) return launch_one(gqa_decode_bf16<D, 1, QUEUE, KV8>, a, grid, st, KV8 ? kMfmaWgsPerCuFp8 : kMfmaWgsPerCu);
-  if (hb == 2) return launch_one(gqa_decode_bf16<D, 2, QUEUE, KV8>, a, grid, st, kMfmaWgsPerCu);
-  if (hb <= 4) return launch_one(gqa_decode_bf16<D, 4, QUEUE, KV8>, a, grid, st, kMfmaWgsPerCu);
+  if (hb == 1)
+    return launch_one(gqa_decode_bf16<D, 1, QUEUE, KV8, PAGED>, a, grid, st, KV8 ? kMfmaWgsPerCuFp8 : kMfmaWgsPerCu);
+  if (hb == 2) return launch_one(gqa_decode_bf16<D, 2, QUEUE, KV8, PAGED>, a, grid, st, kMfmaWgsPerCu);
+  if (hb <= 4) return launch_one(gqa_decode_bf16<D, 4, QUEUE, KV8, PAGED>, a, grid, st, kMfmaWgsPerCu);
   return hipErrorInvalidValue;
 }
 
@@ -1071,6 +1100,12 @@ hipError_t launch_f32(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
 template <bool QUEUE>
 hipError_t launch_mode(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
   if (a.kv_fp8) return a.D == 128 ? launch_bf16<128, QUEUE, true>(a, grid, st) : hipErrorInvalidValue;
+  if (a.block_table) {
+    if (!a.in_bf16) return hipErrorInvalidValue;
+    return a.D == 64 ? launch_bf16<64, QUEUE, false, true>(a, grid, st)
+           : a.D == 96 ? launch_bf16<96, QUEUE, false, true>(a, grid, st)
+                       : launch_bf16<128, QUEUE, false, true>(a, grid, st);
+  }
   if (a.in_bf16)
     return a.D == 64 ? launch_bf16<64, QUEUE>(a, grid, st) : a.D == 96 ? launch_bf16<96, QUEUE>(a, grid, st)
                                                                         : launch_bf16<128, QUEUE>(a, grid, st);

@@ -223,6 +223,28 @@ def cache_append(cache, new, start_pos=None, n_new=None) -> np.ndarray:
     return out
 
 
+def gather_pages(pages, block_table, cache_lens, page_size: int | None = None) -> np.ndarray:
+    """A paged cache written out as a contiguous one: pages [n_pages, page_size, ...] and
+    block_table [B, max_pages] give cache [B, max_pages * page_size, ...] with
+    cache[b, t] = pages[block_table[b, t // page_size], t % page_size] for t < cache_lens[b]
+    (clamped to [0, max_pages * page_size]) and zeros elsewhere.  The block-table layout is the
+    reading of paging taken here (the pages only mention paging as a serving cost); page numbers
+    are clamped to [0, n_pages).  Works on any dtype."""
+    pages = np.asarray(pages)
+    table = np.asarray(block_table, dtype=np.int64)
+    ps = pages.shape[1] if page_size is None else int(page_size)
+    B, max_pages = table.shape
+    T = max_pages * ps
+    out = np.zeros((B, T) + pages.shape[2:], dtype=pages.dtype)
+    for b in range(B):
+        L = min(max(int(cache_lens[b]), 0), T)
+        for p in range((L + ps - 1) // ps):  # logical page p holds positions p * ps ..
+            page = min(max(int(table[b, p]), 0), pages.shape[0] - 1)
+            rows = min(ps, L - p * ps)
+            out[b, p * ps:p * ps + rows] = pages[page, :rows]
+    return out
+
+
 def rope(x, positions, base: float = 10000.0, lib=None) -> np.ndarray:
     """Rotary position embedding (oracle_rope in oracle.c): x [..., H, d] with d even, positions
     [...] (one absolute position per token, the leading dimensions of x) -> float64 [..., H, d].

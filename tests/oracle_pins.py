@@ -598,7 +598,36 @@ def pin_rope_append(lib):
     _close(outs[1], outs[0], 2e-6, "decode under a common position shift (float32 rounding of the rotated rows)")
 
 
+def pin_gather_pages(lib):
+    """The block-table layout: a pool holding a contiguous cache page by page in order, with the
+    identity table, gives that cache back (and zeros past each length); shuffling the pool's pages
+    and renumbering the table to match changes nothing; pages no table entry below the length
+    points at, and table entries past it, are never read; a decode over the gathered caches equals
+    the decode over the original ones."""
+    rng = _rng(47)
+    B, ps, mp, Hkv, D = 3, 4, 5, 2, 8
+    cache = _rand(rng, B, mp * ps, Hkv, D)
+    lens = np.array([20, 7, 0], np.int32)
+    pool = cache.reshape(B * mp, ps, Hkv, D)
+    ident = np.arange(B * mp, dtype=np.int32).reshape(B, mp)
+    got = oracle.gather_pages(pool, ident, lens)
+    for b in range(B):
+        assert np.array_equal(got[b, :lens[b]], cache[b, :lens[b]]) and not got[b, lens[b]:].any(), "identity"
+    perm = rng.permutation(B * mp)
+    shuffled = np.empty_like(pool)
+    shuffled[perm] = pool  # old page i is now page perm[i]
+    table = perm[ident].astype(np.int32)
+    table[1, 2:] = -99  # entries past sequence 1's length (7 positions: pages 0, 1)
+    assert np.array_equal(oracle.gather_pages(shuffled, table, lens), got), "shuffled pool"
+    spare = np.concatenate([shuffled, np.full((2, ps, Hkv, D), np.nan, np.float32)])
+    assert np.array_equal(oracle.gather_pages(spare, table, lens), got), "unreferenced pages"
+    q = _rand(rng, B, 4, D)
+    _close(oracle.gqa_decode(q, got, oracle.gather_pages(shuffled, table, lens), lens, lib=lib),
+           oracle.gqa_decode(q, cache, cache, lens, lib=lib), 0.0, "decode over gathered caches")
+
+
 ALL_PINS = [pin_decode_vs_sdpa, pin_decode_closed_forms, pin_decode_invariants, pin_decode_head_structure,
             pin_prefill_vs_sdpa, pin_prefill_rows, pin_cached_vs_sdpa, pin_cached_reductions, pin_mla_vs_sdpa, pin_mla_absorbed_equals_decompressed,
             pin_mla_selection, pin_mla_prefill_vs_sdpa, pin_mla_prefill_rows_are_decodes, pin_cache_append,
-            pin_e4m3_decoding, pin_rope_quarter_turns, pin_rope_invariants, pin_rope_append]
+            pin_e4m3_decoding, pin_rope_quarter_turns, pin_rope_invariants, pin_rope_append,
+            pin_gather_pages]
