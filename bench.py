@@ -393,7 +393,10 @@ def main():
 
     dec_gbs = rate(dec_bytes, "gqa_decode")
     dec_hash = source_hash("decode_gqa.hip", "attn_internal.h")
-    traffic = measured_traffic("gqa_decode_bf16<128, 1, true, false>", dec_hash)
+    # HBM bytes of the call's two launches (decode + merge), from the committed counter runs
+    t_main = measured_traffic("gqa_decode_bf16<128, 1, true, false, false>", dec_hash)
+    t_merge = measured_traffic("gqa_decode_merge", dec_hash)
+    traffic = round(t_main + t_merge) if t_main is not None and t_merge is not None else None
     clk_ghz = props.clock_rate / 1e6 if getattr(props, "clock_rate", 0) else None
     derived_peak = (props.multi_processor_count * BF16_FLOP_PER_CU_CLK * clk_ghz * 1e9 / 1e12) if clk_ghz else None
 
@@ -421,7 +424,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("gqa_decode_bf16<128, 1, true, false> + gqa_decode_merge: one attn_decode_gqa call "
+            "kernel": ("gqa_decode_bf16<128, 1, true, false, false> + gqa_decode_merge: one attn_decode_gqa call "
                        "(two launches), timed together"),
             "achieved": round(dec_gbs, 1),
             "peak": HBM_PEAK_GBS,
