@@ -556,7 +556,10 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
 // bf16 inputs, MFMA.  HB blocks of 16 query heads (n_rep <= 16 * HB).
 // Waves per SIMD the register allocation targets (the fixed schedule runs
 // several workgroups per compute unit): four fit head_dim 64, head_dim 96 and
-// 128 need up to 168 registers (three waves) with the next tile in flight.
+// 128 need up to 168 registers (three waves) with the next tile in flight.  Two
+// head blocks fit 256 registers without spilling (two waves); allowed more, the
+// compiler kept the accumulators in AGPRs and the MQA sweep setting (n_rep 32)
+// ran 6% slower (22.3 vs 21.0 us).  Four head blocks need more (one wave).
 // KV8: the caches hold OCP FP8 E4M3 values (one byte each), converted to bf16
 // (exactly) on their way into LDS; the K scale is folded into the softmax
 // scale by the host, the V scale is applied to each unit's output.
@@ -566,7 +569,7 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
 // from those registers.
 template <int D, int HB, bool QUEUE, bool KV8 = false, bool PAGED = false>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(HB > 1 ? 1 : (D >= 96 ? (QUEUE ? 2 : 3) : 4))))
+__attribute__((amdgpu_waves_per_eu(HB > 2 ? 1 : (HB > 1 ? 2 : (D >= 96 ? (QUEUE ? 2 : 3) : 4)))))
 void gqa_decode_bf16(GqaDecodeArgs a) {
   static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
   static_assert(!KV8 || D == 128, "fp8 caches: head_dim 128");
