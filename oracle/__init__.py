@@ -294,6 +294,21 @@ def rope_append(k_new, k_cache=None, q=None, start_pos=None, n_new=None, x_new=N
     return out
 
 
+def int4_to_float(packed, scales=None) -> np.ndarray:
+    """Values of packed signed 4-bit codes: packed [..., n] uint8 holds 2n codes, code 2i in the
+    low nibble (bits 3..0) of byte i and code 2i + 1 in the high nibble, each a two's-complement
+    integer in [-8, 7]; scales (broadcast over the last axis of the result, e.g. one per cached
+    row) multiply them.  Returns float64 [..., 2n].  The int4 cache reading: the "MHA, MQA và GQA"
+    e-book counts an int4 number as half a byte and gives no layout; this is the plainest one."""
+    b = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    lo, hi = b & 0xF, (b >> 4) & 0xF
+    codes = np.stack([lo, hi], axis=-1).reshape(b.shape[:-1] + (2 * b.shape[-1],))
+    vals = np.where(codes >= 8, codes - 16, codes).astype(np.float64)
+    if scales is not None:
+        vals = vals * np.asarray(scales, dtype=np.float64)[..., None]
+    return vals
+
+
 def e4m3_to_float(codes, scale: float = 1.0) -> np.ndarray:
     """Values of OCP FP8 E4M3 codes (uint8 array) times scale, as float64: sign bit 7,
     exponent bits 6..3 with bias 7, mantissa bits 2..0; exponent 0 is subnormal

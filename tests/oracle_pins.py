@@ -626,8 +626,24 @@ def pin_gather_pages(lib):
            oracle.gqa_decode(q, cache, cache, lens, lib=lib), 0.0, "decode over gathered caches")
 
 
+def pin_int4_decoding(lib):
+    """Every one of the 256 bytes against the two's-complement reading of each nibble computed by
+    integer arithmetic (low nibble first), plus landmarks: 0x07 -> (7, 0), 0x80 -> (0, -8),
+    0xF1 -> (1, -1), 0xFF -> (-1, -1); a row scale multiplies every code of its row."""
+    allb = np.arange(256, dtype=np.uint8)[:, None]
+    got = oracle.int4_to_float(allb)
+    for v in range(256):
+        lo, hi = v % 16, v // 16
+        want = (lo - 16 if lo > 7 else lo, hi - 16 if hi > 7 else hi)
+        assert tuple(got[v]) == want, (v, got[v], want)
+    assert tuple(oracle.int4_to_float(np.array([0x07, 0x80, 0xF1, 0xFF], np.uint8))) == (7, 0, 0, -8, 1, -1, -1, -1)
+    rows = np.array([[0x21, 0x43], [0x21, 0x43]], np.uint8)
+    scaled = oracle.int4_to_float(rows, np.array([0.5, -2.0]))
+    assert np.array_equal(scaled, [[0.5, 1.0, 1.5, 2.0], [-2.0, -4.0, -6.0, -8.0]]), scaled
+
+
 ALL_PINS = [pin_decode_vs_sdpa, pin_decode_closed_forms, pin_decode_invariants, pin_decode_head_structure,
             pin_prefill_vs_sdpa, pin_prefill_rows, pin_cached_vs_sdpa, pin_cached_reductions, pin_mla_vs_sdpa, pin_mla_absorbed_equals_decompressed,
             pin_mla_selection, pin_mla_prefill_vs_sdpa, pin_mla_prefill_rows_are_decodes, pin_cache_append,
             pin_e4m3_decoding, pin_rope_quarter_turns, pin_rope_invariants, pin_rope_append,
-            pin_gather_pages]
+            pin_gather_pages, pin_int4_decoding]
