@@ -169,6 +169,14 @@ def main():
     f8_v = (torch.randn(B, T_max, Hkv, D, device=dev, generator=gen) / f8_scale).to(torch.float8_e4m3fn)
     f8_bytes = dec_bytes // 2                                 # one byte per cached element
     f8_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    # int4 caches: random code bytes and per-row scales in [0.25, 0.75), drawn on the device, three
+    # copies used in turn (152 MB each, so a call does not find its rows in the Infinity Cache)
+    i4 = [(torch.randint(0, 256, (B, T_max, Hkv, D // 2), device=dev, generator=gen, dtype=torch.uint8),
+           torch.randint(0, 256, (B, T_max, Hkv, D // 2), device=dev, generator=gen, dtype=torch.uint8),
+           torch.rand(B, T_max, Hkv, device=dev, generator=gen) * 0.5 + 0.25,
+           torch.rand(B, T_max, Hkv, device=dev, generator=gen) * 0.5 + 0.25) for _ in range(3)]
+    i4_bytes = 2 * Hkv * (D // 2 + 4) * sum_len              # codes and row scales of K and V
+    i4_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     # paged view of the same caches: 64-position pages, every sequence's pages scattered over the
     # whole pool by a seeded permutation (the pool is the contiguous cache, seen as pages)
     pg_size = 64
@@ -311,6 +319,10 @@ def main():
         attn.attn_decode_gqa_append(dec["q"], app_new_k, app_new_v, dec["k"], dec["v"], app_pos, out=step_out,
                                     workspace=step_ws)
 
+    def run_int4(i):
+        kc, vc, ks, vs = i4[i % len(i4)]
+        attn.attn_decode_gqa_int4kv(dec["q"], kc, vc, ks, vs, dec["cache_lens"], out=i4_out, workspace=dec_ws)
+
     def run_paged(i):
         attn.attn_decode_gqa_paged(dec["q"], pg_k, pg_v, pg_table, dec["cache_lens"], out=pg_out, workspace=dec_ws)
 
@@ -358,7 +370,7 @@ def main():
              ("mla_prefill", run_mla_prefill), ("mla_decode", run_mla), ("mla_decode_step", run_mla_step),
              ("kv_append", run_append), ("rope_append_decode", run_rope_decode), ("rope_append_chunk", run_rope_chunk),
              ("gqa_decode", run_decode), ("gqa_decode_paged", run_paged), ("gqa_decode_step", run_step),
-             ("gqa_decode_fp8", run_fp8)]
+             ("gqa_decode_fp8", run_fp8), ("gqa_decode_int4", run_int4)]
     parts += [(name, run_sweep(name)) for name in sweep]
     parts.append(("minimind768_gqa_decode", run_minimind))
     if want:
@@ -504,6 +516,10 @@ def main():
         decode_part("gqa_decode_paged", dec_bytes, B, None,
                     f"llama3_8b_gqa_decode shape and lengths over paged caches: {pg_size}-position pages, each "
                     "sequence's pages scattered over the pool by a seeded permutation (attn_decode_gqa_paged)")
+    if "gqa_decode_int4" in ms:
+        decode_part("gqa_decode_int4", i4_bytes, B, None,
+                    "llama3_8b_gqa_decode shape and lengths, K/V as packed signed 4-bit codes with one fp32 scale "
+                    "per row (random bytes, scales U[0.25, 0.75), device-drawn, 3 copies used in turn)")
     if "gqa_decode_step" in ms:
         decode_part("gqa_decode_step", dec_bytes, B, None,
                     "llama3_8b_gqa_decode with the newest rows as the new token "

@@ -171,6 +171,36 @@ attn_status attn_decode_gqa_fp8kv(const void* q, const void* k_cache, const void
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* GQA decode over caches stored as signed 4-bit integers with one scale per row.
+ *
+ *   K[b,t,g,2i]   = k_scales[b,t,g] * int4(low nibble of k_codes[b,t,g,i]),
+ *   K[b,t,g,2i+1] = k_scales[b,t,g] * int4(high nibble of k_codes[b,t,g,i]),
+ *   V likewise, and out is attn_decode_gqa over K and V.
+ *
+ * The int4 number type of the "MHA, MQA và GQA" e-book's simulator
+ * configuration, where a number takes half a byte; the e-book gives no layout
+ * or scale.  The reading taken: two's-complement codes in [-8, 7], two per
+ * byte with the even element in the low nibble, and one fp32 scale per cached
+ * row (one KV head of one position), so a row of 128 elements is 64 bytes of
+ * codes plus 4 bytes of scale.  Encoding the cache is the caller's.  Each code
+ * c enters the bf16 MFMA as the exact value 136 + c and the offset is removed
+ * in fp32 after the products; q is bf16; scores, softmax and accumulation are
+ * as in attn_decode_gqa.
+ *
+ *   q [B, Hq, 128] bf16;  k_codes, v_codes [B, T_max, Hkv, 64] bytes (16-byte
+ *   aligned);  k_scales, v_scales [B, T_max, Hkv] fp32 (4-byte aligned; NULL
+ *   is ATTN_ERR_NULL);  cache_lens, out, split_tokens, workspace
+ *   (attn_decode_gqa_workspace_bytes) as attn_decode_gqa
+ *
+ * head_dim must be 128 (else ATTN_ERR_UNSUPPORTED); Hq/Hkv up to 64.  Rows at
+ * or past cache_lens[b] are not read (codes or scales).
+ */
+attn_status attn_decode_gqa_int4kv(const void* q, const void* k_codes, const void* v_codes, const float* k_scales,
+                                   const float* v_scales, const int32_t* cache_lens, void* out, int B, int Hq, int Hkv,
+                                   int head_dim, int T_max, float softmax_scale, attn_dtype out_dtype,
+                                   int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* GQA decode step with the new token's K/V: append and attend in one call.
  *
  *   L = cache_lens[b] (positions cached before this token, clamped to [0, T_max])

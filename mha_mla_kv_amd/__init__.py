@@ -58,6 +58,8 @@ def _declare(lib):
     lib.attn_decode_gqa_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, I, P, Z, P]
     lib.attn_decode_gqa_noalloc.restype = I
     lib.attn_decode_gqa_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P]
+    lib.attn_decode_gqa_int4kv.restype = I
+    lib.attn_decode_gqa_int4kv.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, Z, P]
     lib.attn_decode_gqa_fp8kv.restype = I
     lib.attn_decode_gqa_fp8kv.argtypes = [P, P, P, F, F, P, P, I, I, I, I, I, F, I, I, P, ctypes.c_size_t, P]
     lib.attn_decode_gqa_append_workspace_bytes.restype = ctypes.c_size_t
@@ -189,6 +191,39 @@ def attn_decode_gqa(q, k_cache, v_cache, cache_lens, out=None, softmax_scale: fl
                                Hkv, D, T_max, float(softmax_scale), _dt(q), _dt(out), int(split_tokens),
                                _ptr(workspace), workspace.numel(), _stream(q.device))
     _raise_if(st, "attn_decode_gqa")
+    return out
+
+
+def attn_decode_gqa_int4kv(q, k_codes, v_codes, k_scales, v_scales, cache_lens, out=None,
+                           softmax_scale: float = 0.0, out_dtype=torch.float32, split_tokens: int = 0,
+                           workspace=None):
+    """attn_decode_gqa over caches of packed signed 4-bit codes with one fp32 scale per row: element
+    2i of a row is the low nibble of byte i, 2i + 1 the high nibble, each times the row's scale.
+
+    q [B,Hq,128] bf16, k_codes/v_codes [B,T_max,Hkv,64] uint8, k_scales/v_scales [B,T_max,Hkv]
+    float32, cache_lens [B] int32.  Returns out [B,Hq,128] of out_dtype."""
+    _check(q, "q", dtype=torch.bfloat16)
+    B, Hq, D = q.shape
+    _check(k_codes, "k_codes", dtype=torch.uint8)
+    if k_codes.dim() != 4 or k_codes.shape[0] != B or k_codes.shape[3] * 2 != D:
+        raise ValueError(f"k_codes must be [B={B}, T_max, Hkv, {D // 2}] (got {tuple(k_codes.shape)})")
+    T_max, Hkv = k_codes.shape[1], k_codes.shape[2]
+    _check(v_codes, "v_codes", shape=k_codes.shape, dtype=torch.uint8)
+    _check(k_scales, "k_scales", shape=(B, T_max, Hkv), dtype=torch.float32)
+    _check(v_scales, "v_scales", shape=(B, T_max, Hkv), dtype=torch.float32)
+    _check(cache_lens, "cache_lens", shape=(B,), dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    _check(out, "out", shape=(B, Hq, D))
+    need = attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, T_max, split_tokens)
+    if workspace is None:
+        workspace = _workspace(need, q.device, "gqa")
+    _check(workspace, "workspace", dtype=torch.uint8)
+    st = lib().attn_decode_gqa_int4kv(_ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_scales), _ptr(v_scales),
+                                      _ptr(cache_lens), _ptr(out), B, Hq, Hkv, D, T_max, float(softmax_scale),
+                                      _dt(out), int(split_tokens), _ptr(workspace), workspace.numel(),
+                                      _stream(q.device))
+    _raise_if(st, "attn_decode_gqa_int4kv")
     return out
 
 
@@ -598,7 +633,7 @@ def attn_decode_mla_append(q_nope, q_rope, c_new, k_rope_new, w_uk, w_uv, c_kv, 
     return out
 
 
-__all__ = ["attn_decode_gqa", "attn_decode_gqa_paged", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_noalloc", "NOALLOC_SCRATCH_BYTES", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
+__all__ = ["attn_decode_gqa", "attn_decode_gqa_paged", "attn_decode_gqa_int4kv", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_noalloc", "NOALLOC_SCRATCH_BYTES", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
            "attn_decode_gqa_append_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached", "attn_prefill_gqa_cached_append",
            "attn_prefill_mla_causal", "attn_cache_append", "attn_rope_append",
            "attn_decode_mla_absorbed", "attn_decode_mla_append", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",

@@ -187,7 +187,8 @@ attn_status gqa_decode_common(const char* fn, const void* q, const void* k_new, 
                               int head_dim, int T_max, float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype,
                               int split_tokens, void* workspace, size_t workspace_bytes, void* stream,
                               const float* kv_scales = nullptr, bool noalloc = false,
-                              const int32_t* block_table = nullptr, int page_size = 0, int n_pages = 0) {
+                              const int32_t* block_table = nullptr, int page_size = 0, int n_pages = 0,
+                              const float* k_row_scales = nullptr, const float* v_row_scales = nullptr) {
   const bool append = k_new != nullptr;
   const bool kv_fp8 = kv_scales != nullptr;
   if (!q || !k_cache || !v_cache || !cache_lens || !out)
@@ -284,6 +285,9 @@ attn_status gqa_decode_common(const char* fn, const void* q, const void* k_new, 
   a.v_new = v_new;
   a.k_cache = const_cast<void*>(k_cache);
   a.v_cache = const_cast<void*>(v_cache);
+  a.kv_int4 = k_row_scales != nullptr;
+  a.k_scales = k_row_scales;
+  a.v_scales = v_row_scales;
   a.block_table = block_table;
   a.page_size = page_size;
   a.table_stride = block_table ? T_max / page_size : 0;
@@ -324,6 +328,21 @@ attn_status attn_decode_gqa_paged(const void* q, const void* k_pages, const void
   return gqa_decode_common(fn, q, nullptr, nullptr, k_pages, v_pages, cache_lens, out, B, Hq, Hkv, head_dim,
                            page_size * max_pages_per_seq, softmax_scale, in_dtype, out_dtype, split_tokens, workspace,
                            workspace_bytes, stream, nullptr, false, block_table, page_size, n_pages);
+}
+
+attn_status attn_decode_gqa_int4kv(const void* q, const void* k_codes, const void* v_codes, const float* k_scales,
+                                   const float* v_scales, const int32_t* cache_lens, void* out, int B, int Hq, int Hkv,
+                                   int head_dim, int T_max, float softmax_scale, attn_dtype out_dtype,
+                                   int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "attn_decode_gqa_int4kv";
+  if (!k_scales || !v_scales) return fail(ATTN_ERR_NULL, "%s: k_scales and v_scales must be non-NULL", fn);
+  if (head_dim != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: int4 caches are built for head_dim 128 only (got %d)", fn, head_dim);
+  if ((reinterpret_cast<uintptr_t>(k_scales) & 3u) || (reinterpret_cast<uintptr_t>(v_scales) & 3u))
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: the scales must be 4-byte aligned", fn);
+  return gqa_decode_common(fn, q, nullptr, nullptr, k_codes, v_codes, cache_lens, out, B, Hq, Hkv, head_dim, T_max,
+                           softmax_scale, ATTN_BF16, out_dtype, split_tokens, workspace, workspace_bytes, stream,
+                           nullptr, false, nullptr, 0, 0, k_scales, v_scales);
 }
 
 attn_status attn_decode_gqa_noalloc(const void* q, const void* k_cache, const void* v_cache,

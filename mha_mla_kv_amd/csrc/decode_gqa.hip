@@ -567,19 +567,30 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
 // a unit's page numbers are read once (two per lane) when the unit begins, and
 // every 32-position tile, which lies within one page, reads its page number
 // from those registers.
-template <int D, int HB, bool QUEUE, bool KV8 = false, bool PAGED = false>
+// KV4: the caches hold signed 4-bit codes (two per byte, low nibble first) with
+// one fp32 scale per cached row.  Each code c goes into the LDS tile as the
+// bf16 value 136 + c, whose bits are 0x4300 | (c + 8): a bit operation, no
+// arithmetic.  The offset is removed after the products, exactly in fp32: the
+// scores subtract 136 * sum(q) (q as the MFMA sees it), the outputs 136 *
+// sum(p') with p' = bf16(p * v_scale) the PV operand; the row's K scale
+// multiplies its score, its V scale its probability.  The wave's 32 K and 32 V
+// scales of a tile are read with the tile (one per lane) and staged in LDS.
+template <int D, int HB, bool QUEUE, bool KV8 = false, bool PAGED = false, bool KV4 = false>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(HB > 2 ? 1 : (HB > 1 ? 2 : (D >= 96 ? (QUEUE ? 2 : 3) : 4)))))
 void gqa_decode_bf16(GqaDecodeArgs a) {
   static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
   static_assert(!KV8 || D == 128, "fp8 caches: head_dim 128");
-  constexpr int EB = KV8 ? 1 : 2;      // bytes per cached element
+  static_assert(!KV4 || (D == 128 && !KV8 && !PAGED), "int4 caches: head_dim 128, contiguous");
+  constexpr int EB = KV8 ? 1 : 2;      // bytes per cached element (bf16, fp8)
+  constexpr int RB = KV4 ? D / 2 : D * EB;  // bytes of one KV head's row
+  constexpr int kEPU = 16 * D / RB;    // elements per 16-byte unit
   constexpr int KC = D / 32;           // 32-wide dim chunks (QK contraction)
   constexpr int DW = D / 16;           // 16-wide dim blocks (PV output rows)
   constexpr int VP = D + 16;           // V tile row pitch in elements ([token][dim], padded)
   constexpr int KP = D + 8;            // K tile row pitch (16 rows of one column: distinct LDS banks)
-  constexpr int kUnits = D * EB / 16;                        // 16-byte units per K/V row
-  constexpr int kLanesPerRow = kUnits <= 8 ? 8 : 16;          // lanes that load one row
+  constexpr int kUnits = RB / 16;                             // 16-byte units per K/V row
+  constexpr int kLanesPerRow = kUnits <= 4 ? 4 : kUnits <= 8 ? 8 : 16;  // lanes that load one row
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;
   constexpr int kLoads = kDecodeTileTokens / kRowsPerLoad;   // 16-byte loads per lane per tile
   constexpr int kStep = kDecodeWaves * kDecodeTileTokens;    // positions per round of the four waves
@@ -598,6 +609,7 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   static_assert(HB == 1 || kSmemElems * 2 + kQueuePlanWords * 4 <= 160 * 1024, "LDS");
   static_assert(HB > 1 || kSmemElems == kVtElems, "one head block: the scratch fits the tiles");
   __shared__ __attribute__((aligned(16))) u16 smem[kSmemElems];
+  __shared__ __attribute__((aligned(16))) float scl[KV4 ? kDecodeWaves * 64 : 4];  // int4: K, V scales per wave
   __shared__ unsigned pre[QUEUE ? kQueuePlanWords : 1];
   __shared__ UnitShared sh;
 
@@ -611,19 +623,19 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   float* lse_s = ob + kDecodeWaves * kSliceFloats;  // [HB*16]
   u16* vt = smem + wave * kDecodeTileTokens * VP;
   const size_t tok_stride = (size_t)a.Hkv * D;
-  const int row_bytes = uniform((int)(tok_stride * EB));
+  const int row_bytes = uniform(a.Hkv * RB);
   // this lane's row within a load and its 16-byte unit in the row
   const int lrow = lane / kLanesPerRow, lunit = min(lane % kLanesPerRow, kUnits - 1);
   const unsigned row_off = (unsigned)(lrow * row_bytes + 16 * lunit);
 
   // base of this (sequence, KV head)'s rows (paged: of the head's rows in the pool)
   auto k_head = [&](const Unit& u) {
-    if constexpr (PAGED) return static_cast<const char*>(a.k) + (size_t)u.g * D * EB;
-    return static_cast<const char*>(a.k) + ((size_t)u.b * a.T_max * a.Hkv + u.g) * D * EB;
+    if constexpr (PAGED) return static_cast<const char*>(a.k) + (size_t)u.g * RB;
+    return static_cast<const char*>(a.k) + ((size_t)u.b * a.T_max * a.Hkv + u.g) * RB;
   };
   auto v_head = [&](const Unit& u) {
-    if constexpr (PAGED) return static_cast<const char*>(a.v) + (size_t)u.g * D * EB;
-    return static_cast<const char*>(a.v) + ((size_t)u.b * a.T_max * a.Hkv + u.g) * D * EB;
+    if constexpr (PAGED) return static_cast<const char*>(a.v) + (size_t)u.g * RB;
+    return static_cast<const char*>(a.v) + ((size_t)u.b * a.T_max * a.Hkv + u.g) * RB;
   };
   // paged: the current unit's first page slot and its page numbers (slot
   // unit_p0 + i in lane i % 64 of pg[i / 64])
@@ -651,22 +663,51 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   // an offset.
   auto load_rows = [&](bf16x8 (&r)[kLoads], const char* head0, int t0, int c1) {
     // rows of the tile before c1, 0..32; bytes up to the end of the last
-    // (row_bytes >= EB * D, so no rows gives a non-positive count)
+    // (row_bytes >= RB, so no rows gives a non-positive count)
     const int rows = min(max(c1 - t0, 0), kDecodeTileTokens);
-    const int n = max(rows * row_bytes - row_bytes + EB * D, 0);
+    const int n = max(rows * row_bytes - row_bytes + RB, 0);
     const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(tile_base(head0, t0)), (short)0, n, 0x00020000);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
       r[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                             rs, (int)(row_off + (unsigned)(kRowsPerLoad * i * row_bytes)), 0, kStreamPolicy));
   };
+  // int4: the tile's scales, lane l < 32 the K scale of row t0 + l, lane l >= 32
+  // the V scale of row t0 + l - 32 (rows at or past c1 read as zeros)
+  auto load_scales = [&](float& sr, const Unit& u, int t0, int c1) {
+    if constexpr (KV4) {
+      const int rows = min(max(c1 - t0, 0), kDecodeTileTokens);
+      const size_t r0 = ((size_t)u.b * a.T_max + t0) * a.Hkv + u.g;
+      const float* base = (lane < 32 ? a.k_scales : a.v_scales) + r0;
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0,
+                                                        max((rows - 1) * a.Hkv * 4 + 4, 0), 0x00020000);
+      sr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (lane & 31) * a.Hkv * 4, 0, 0));
+    }
+  };
   // The same registers written to this wave's LDS tile, row pitch `pitch`.
   // fp8 rows: each 16-byte unit holds 16 values, widened to two 16-byte bf16 writes.
+  // int4 rows: each 16-byte unit holds 32 codes, widened to four 16-byte writes.
   auto store_rows = [&](const bf16x8 (&r)[kLoads], int pitch) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      u16* dst = vt + (kRowsPerLoad * i + lrow) * pitch + (16 / EB) * lunit;
-      if constexpr (KV8) {
+      u16* dst = vt + (kRowsPerLoad * i + lrow) * pitch + kEPU * lunit;
+      if constexpr (KV4) {
+        // word w holds codes 8w .. 8w+7 of the unit, low nibble first; offset
+        // binary (c + 8) by flipping the sign bits; pair k of the word as one
+        // 32-bit word of two bf16 (136 + c)
+        const u32x4 wd = __builtin_bit_cast(u32x4, r[i]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const unsigned u8s = wd[w] ^ 0x88888888u;
+          u32x4 h;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const unsigned t = (u8s >> (8 * k)) & 0xFFu;  // the pair's byte alone
+            h[k] = (((t << 12) | t) & 0x000F000Fu) | 0x43004300u;
+          }
+          *reinterpret_cast<u32x4*>(dst + 8 * w) = h;
+        }
+      } else if constexpr (KV8) {
         // each conversion widens the codes of one 16-bit half of a word into a
         // pair of bf16 (one 32-bit word); the pairs are moved as whole words
         // (extracting the two bf16 of a pair separately was miscompiled into a
@@ -690,6 +731,7 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   // Q[head = 16hb + row][dims 32c + 8grp .. +8]) and this wave's next K/V tile.
   bf16x8 qop[HB][KC];
   bf16x8 kr[kLoads], vr[kLoads];
+  float sr = 0.f;  // int4: the next tile's scale (see load_scales)
   // Requests the query block of unit u and this wave's first tile of it.
   // The query block is read through a buffer resource that ends with head
   // n_rep - 1: the padding heads read as zeros, with no branch.
@@ -714,10 +756,12 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
     }
     load_rows(kr, k_head(u), u.t0 + wave * kDecodeTileTokens, u.t1);
     load_rows(vr, v_head(u), u.t0 + wave * kDecodeTileTokens, u.t1);
+    load_scales(sr, u, u.t0 + wave * kDecodeTileTokens, u.t1);
   };
 
   // Streams unit u (begin_unit(u) issued): this wave's online-softmax state.
   float m[HB], lsum[HB];
+  float psum[HB], qsum[HB];  // int4: sum of the PV probabilities, sum of q (this lane's head row)
   f32x4 o[HB][DW];  // O^T: lane holds dims 16w + 4grp + i of head 16hb + row
   auto stream_unit = [&](const Unit& u, NextUnit& nx) {
     const char* kp = k_head(u);
@@ -727,8 +771,17 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
     for (int hb = 0; hb < HB; ++hb) {
       m[hb] = kNegInf;
       lsum[hb] = 0.f;
+      psum[hb] = 0.f;
 #pragma unroll
       for (int w = 0; w < DW; ++w) o[hb][w] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (KV4) {
+        float qs = 0.f;
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qs += (float)qop[hb][c][e];
+        qsum[hb] = sum_xor32(sum_xor16(qs));
+      }
     }
     // Per tile: K(t) -> LDS; scores from LDS; K(t + kStep) requested; V(t) ->
     // LDS (same region); V(t + kStep) requested; softmax; PV from LDS.
@@ -746,6 +799,7 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
         }
       }
       store_rows(kr, KP);
+      if constexpr (KV4) scl[wave * 64 + lane] = sr;
       wave_lds_sync();
       // Scores: lane holds S^T[token 16u + 4grp + i][head 16hb + row]; the A
       // operand (token 16u + row, dims 32c + 8grp .. +8) comes from LDS.
@@ -770,6 +824,11 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
           for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
             for (int s = 0; s < 2; ++s) acc[hb][s] = mfma_16x16x32(ka[s][c], qop[hb][c], acc[hb][s]);
+        f32x4 ks[2] = {};
+        if constexpr (KV4) {
+#pragma unroll
+          for (int s = 0; s < 2; ++s) ks[s] = *reinterpret_cast<const f32x4*>(&scl[wave * 64 + 16 * s + 4 * grp]);
+        }
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
@@ -777,13 +836,23 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int tok = t0 + 16 * s + 4 * grp + i;
-              sc[hb][s][i] = tok < c1 ? acc[hb][s][i] * a.scale_log2e : kNegInf;
+              float x = acc[hb][s][i] * a.scale_log2e;
+              if constexpr (KV4) x = (acc[hb][s][i] - 136.f * qsum[hb]) * ks[s][i] * a.scale_log2e;
+              sc[hb][s][i] = tok < c1 ? x : kNegInf;
             }
       }
       // the next K tile after the scores: its registers are then free (this
       // tile is in LDS)
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (NEXT) load_rows(kr, kp, t0 + kStep, c1);
+      f32x4 vs[2] = {};
+      if constexpr (KV4) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) vs[s] = *reinterpret_cast<const f32x4*>(&scl[wave * 64 + 32 + 16 * s + 4 * grp]);
+      }
+      if constexpr (NEXT) {
+        load_rows(kr, kp, t0 + kStep, c1);
+        load_scales(sr, u, t0 + kStep, c1);
+      }
       wave_lds_sync();
       store_rows(vr, VP);
       if constexpr (NEXT) load_rows(vr, vp, t0 + kStep, c1);
@@ -801,17 +870,25 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
         const float mn = fmaxf(m[hb], mt);  // finite: the tile's first token is valid
         const float alpha = exp2_fast(m[hb] - mn);
         m[hb] = mn;
-        float ps = 0.f;
+        float ps = 0.f, pv = 0.f;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             // the row sum adds the bf16-rounded probability the PV product uses
-            const __bf16 pb = (__bf16)exp2_fast(sc[hb][s][i] - mn);
+            const float p = exp2_fast(sc[hb][s][i] - mn);
+            const __bf16 pb = (__bf16)p;
             ps += (float)pb;
-            pop[hb][4 * s + i] = pb;
+            if constexpr (KV4) {
+              const __bf16 pvb = (__bf16)(p * vs[s][i]);  // the V scale of the row
+              pv += (float)pvb;
+              pop[hb][4 * s + i] = pvb;
+            } else {
+              pop[hb][4 * s + i] = pb;
+            }
           }
         lsum[hb] = lsum[hb] * alpha + ps;
+        if constexpr (KV4) psum[hb] = psum[hb] * alpha + pv;
 #pragma unroll
         for (int w = 0; w < DW; ++w) o[hb][w] *= alpha;
       }
@@ -839,6 +916,12 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
     for (int hb = 0; hb < HB; ++hb) {
       lsum[hb] = sum_xor16(lsum[hb]);
       lsum[hb] = sum_xor32(lsum[hb]);
+      if constexpr (KV4) {
+        // remove the codes' offset: O^T holds sum p' (136 + c)
+        const float off = 136.f * sum_xor32(sum_xor16(psum[hb]));
+#pragma unroll
+        for (int w = 0; w < DW; ++w) o[hb][w] -= off;
+      }
     }
   };
 
@@ -1079,13 +1162,13 @@ hipError_t launch_one(Kernel kernel, const GqaDecodeArgs& a, dim3 grid, hipStrea
 constexpr int kMfmaWgsPerCu = 1;
 constexpr int kMfmaWgsPerCuFp8 = 2;
 
-template <int D, bool QUEUE, bool KV8 = false, bool PAGED = false>
+template <int D, bool QUEUE, bool KV8 = false, bool PAGED = false, bool KV4 = false>
 hipError_t launch_bf16(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
   const int hb = (a.n_rep + 15) / 16;
-  if (hb == 1)
-    return launch_one(gqa_decode_bf16<D, 1, QUEUE, KV8, PAGED>, a, grid, st, KV8 ? kMfmaWgsPerCuFp8 : kMfmaWgsPerCu);
-  if (hb == 2) return launch_one(gqa_decode_bf16<D, 2, QUEUE, KV8, PAGED>, a, grid, st, kMfmaWgsPerCu);
-  if (hb <= 4) return launch_one(gqa_decode_bf16<D, 4, QUEUE, KV8, PAGED>, a, grid, st, kMfmaWgsPerCu);
+  constexpr int kNarrow = KV8 || KV4 ? kMfmaWgsPerCuFp8 : kMfmaWgsPerCu;  // workgroups per CU, one head block
+  if (hb == 1) return launch_one(gqa_decode_bf16<D, 1, QUEUE, KV8, PAGED, KV4>, a, grid, st, kNarrow);
+  if (hb == 2) return launch_one(gqa_decode_bf16<D, 2, QUEUE, KV8, PAGED, KV4>, a, grid, st, kMfmaWgsPerCu);
+  if (hb <= 4) return launch_one(gqa_decode_bf16<D, 4, QUEUE, KV8, PAGED, KV4>, a, grid, st, kMfmaWgsPerCu);
   return hipErrorInvalidValue;
 }
 
@@ -1103,6 +1186,7 @@ hipError_t launch_f32(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
 template <bool QUEUE>
 hipError_t launch_mode(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
   if (a.kv_fp8) return a.D == 128 ? launch_bf16<128, QUEUE, true>(a, grid, st) : hipErrorInvalidValue;
+  if (a.kv_int4) return a.D == 128 ? launch_bf16<128, QUEUE, false, false, true>(a, grid, st) : hipErrorInvalidValue;
   if (a.block_table) {
     if (!a.in_bf16) return hipErrorInvalidValue;
     return a.D == 64 ? launch_bf16<64, QUEUE, false, true>(a, grid, st)

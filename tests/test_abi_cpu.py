@@ -330,3 +330,17 @@ def test_paged_decode_validation():
     assert f(ind=F32) == UNSUP
     assert f(split=2048) == UNSUP
     assert f(D=80) == UNSUP
+
+
+@no_gpu_only
+def test_int4_decode_validation():
+    lib = attn.lib()
+
+    def f(ks=FAKE, vs=FAKE, **kw):
+        return lib.attn_decode_gqa_int4kv(FAKE, kw.get("kc", FAKE), FAKE, ks, vs, FAKE, FAKE, 2, 32, 8,
+                                          kw.get("D", 128), 64, 0.0, F32, 0, FAKE, 1 << 30, None)
+    assert f(ks=None) == NULL
+    assert f(vs=None) == NULL
+    assert f(D=96) == UNSUP
+    assert f(ks=ctypes.c_void_p(0x100002)) == UNSUP
+    assert f(kc=FAKE_MIS) == UNSUP
