@@ -58,7 +58,10 @@ int pow2_floor(long long x) {
 // enough that the fp32 partial of a unit (n_rep * D * 4 bytes written and read
 // back) stays small next to its cache bytes (chunk * D * 4); with 16 or more
 // query heads per KV head the per-unit costs dominate a short chunk (measured),
-// hence the higher floors.
+// hence the higher floors.  At 32 query heads per KV head (B 16, one KV head,
+// 8192 positions) the 1024 floor leaves 128 units for 256 compute units, yet
+// 512 (256 units) measures no faster: 21.3-21.7 against 21.0-21.1 us; the
+// kernel's time there is its fixed start and end, not the streaming.
 int choose_chunk(int B, int Hkv, int n_rep, int T_max) {
   int lo = 64;
   if (n_rep >= 8) lo = 128;
