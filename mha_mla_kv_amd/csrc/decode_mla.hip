@@ -641,6 +641,9 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
     }
     wait_vmem();  // the copies past the end (zeros) land before the stages are reused
     st.lsum = sum_xor32(sum_xor16(st.lsum));
+    // the W_UV operands of this wave's head (wave + 4): requested now, in
+    // registers by the time o_lat is merged
+    if (wave + kHelpers < a.H) load_uv<R>(uv, a, wave + kHelpers, 0, lane);
   }
   if (!streamer) {
     if (j < a.H) load_uv<R>(uv, a, j, 0, lane);
@@ -785,12 +788,15 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
           reinterpret_cast<const u32x4*>(static_cast<const u16*>(a.kr_new) + (size_t)b * DR)[tid - 64];
   }
 
-  // ---- out = W_UV o_lat, helper j taking heads j, j + 4, ...
-  if (!streamer) {
+  // ---- out = W_UV o_lat, all eight waves: helper j takes heads j, j + 8, ...,
+  // streaming wave w heads w + 4, w + 12, ... (each wave's first batch already
+  // in registers)
+  {
+    const int h0 = streamer ? wave + kHelpers : j;
     const int nb = a.dv / 16;
-    for (int h = j; h < a.H; h += kHelpers) {
+    for (int h = h0; h < a.H; h += kWaves + kHelpers) {
       for (int ib0 = 0; ib0 < nb; ib0 += UvBatch<R>::kBlocks) {
-        if (h != j || ib0 != 0) load_uv<R>(uv, a, h, ib0, lane);
+        if (h != h0 || ib0 != 0) load_uv<R>(uv, a, h, ib0, lane);
         apply_uv<R>(uv, a, olat, b, h, ib0, lane);
       }
     }
