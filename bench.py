@@ -171,10 +171,11 @@ def main():
     f8_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     # int4 caches: random code bytes and per-row scales in [0.25, 0.75), drawn on the device, three
     # copies used in turn (152 MB each, so a call does not find its rows in the Infinity Cache)
-    i4 = [(torch.randint(0, 256, (B, T_max, Hkv, D // 2), device=dev, generator=gen, dtype=torch.uint8),
-           torch.randint(0, 256, (B, T_max, Hkv, D // 2), device=dev, generator=gen, dtype=torch.uint8),
-           torch.rand(B, T_max, Hkv, device=dev, generator=gen) * 0.5 + 0.25,
-           torch.rand(B, T_max, Hkv, device=dev, generator=gen) * 0.5 + 0.25) for _ in range(3)]
+    # (head-major: [B, Hkv, T_max, D/2] codes, [B, Hkv, T_max] scales)
+    i4 = [(torch.randint(0, 256, (B, Hkv, T_max, D // 2), device=dev, generator=gen, dtype=torch.uint8),
+           torch.randint(0, 256, (B, Hkv, T_max, D // 2), device=dev, generator=gen, dtype=torch.uint8),
+           torch.rand(B, Hkv, T_max, device=dev, generator=gen) * 0.5 + 0.25,
+           torch.rand(B, Hkv, T_max, device=dev, generator=gen) * 0.5 + 0.25) for _ in range(3)]
     i4_bytes = 2 * Hkv * (D // 2 + 4) * sum_len              # codes and row scales of K and V
     i4_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     # paged view of the same caches: 64-position pages, every sequence's pages scattered over the
@@ -408,7 +409,7 @@ def main():
     dec_gbs = rate(dec_bytes, "gqa_decode")
     dec_hash = source_hash("decode_gqa.hip", "attn_internal.h")
     # HBM bytes of the call's two launches (decode + merge), from the committed counter runs
-    t_main = measured_traffic("gqa_decode_bf16<128, 1, true, false, false>", dec_hash)
+    t_main = measured_traffic("gqa_decode_bf16<128, 1, true, false, false, false>", dec_hash)
     t_merge = measured_traffic("gqa_decode_merge", dec_hash)
     traffic = round(t_main + t_merge) if t_main is not None and t_merge is not None else None
     clk_ghz = props.clock_rate / 1e6 if getattr(props, "clock_rate", 0) else None
@@ -439,7 +440,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("gqa_decode_bf16<128, 1, true, false, false> + gqa_decode_merge: one attn_decode_gqa call "
+            "kernel": ("gqa_decode_bf16<128, 1, true, false, false, false> + gqa_decode_merge: one attn_decode_gqa call "
                        "(two launches), K calls back to back between one event pair"),
             "achieved": round(dec_gbs, 1),
             "peak": HBM_PEAK_GBS,

@@ -173,8 +173,8 @@ attn_status attn_decode_gqa_fp8kv(const void* q, const void* k_cache, const void
 /* ------------------------------------------------------------------------ */
 /* GQA decode over caches stored as signed 4-bit integers with one scale per row.
  *
- *   K[b,t,g,2i]   = k_scales[b,t,g] * int4(low nibble of k_codes[b,t,g,i]),
- *   K[b,t,g,2i+1] = k_scales[b,t,g] * int4(high nibble of k_codes[b,t,g,i]),
+ *   K[b,t,g,2i]   = k_scales[b,g,t] * int4(low nibble of k_codes[b,g,t,i]),
+ *   K[b,t,g,2i+1] = k_scales[b,g,t] * int4(high nibble of k_codes[b,g,t,i]),
  *   V likewise, and out is attn_decode_gqa over K and V.
  *
  * The int4 number type of the "MHA, MQA và GQA" e-book's simulator
@@ -182,13 +182,15 @@ attn_status attn_decode_gqa_fp8kv(const void* q, const void* k_cache, const void
  * or scale.  The reading taken: two's-complement codes in [-8, 7], two per
  * byte with the even element in the low nibble, and one fp32 scale per cached
  * row (one KV head of one position), so a row of 128 elements is 64 bytes of
- * codes plus 4 bytes of scale.  Encoding the cache is the caller's.  Each code
+ * codes plus 4 bytes of scale.  The codes and scales are stored head-major
+ * (each KV head's positions contiguous), so a head's 64-byte rows fill whole
+ * memory lines.  Encoding the cache is the caller's.  Each code
  * c enters the bf16 MFMA as the exact value 136 + c and the offset is removed
  * in fp32 after the products; q is bf16; scores, softmax and accumulation are
  * as in attn_decode_gqa.
  *
- *   q [B, Hq, 128] bf16;  k_codes, v_codes [B, T_max, Hkv, 64] bytes (16-byte
- *   aligned);  k_scales, v_scales [B, T_max, Hkv] fp32 (4-byte aligned; NULL
+ *   q [B, Hq, 128] bf16;  k_codes, v_codes [B, Hkv, T_max, 64] bytes (16-byte
+ *   aligned);  k_scales, v_scales [B, Hkv, T_max] fp32 (4-byte aligned; NULL
  *   is ATTN_ERR_NULL);  cache_lens, out, split_tokens, workspace
  *   (attn_decode_gqa_workspace_bytes) as attn_decode_gqa
  *

@@ -200,17 +200,17 @@ def attn_decode_gqa_int4kv(q, k_codes, v_codes, k_scales, v_scales, cache_lens, 
     """attn_decode_gqa over caches of packed signed 4-bit codes with one fp32 scale per row: element
     2i of a row is the low nibble of byte i, 2i + 1 the high nibble, each times the row's scale.
 
-    q [B,Hq,128] bf16, k_codes/v_codes [B,T_max,Hkv,64] uint8, k_scales/v_scales [B,T_max,Hkv]
-    float32, cache_lens [B] int32.  Returns out [B,Hq,128] of out_dtype."""
+    q [B,Hq,128] bf16, k_codes/v_codes [B,Hkv,T_max,64] uint8 and k_scales/v_scales [B,Hkv,T_max]
+    float32 (head-major), cache_lens [B] int32.  Returns out [B,Hq,128] of out_dtype."""
     _check(q, "q", dtype=torch.bfloat16)
     B, Hq, D = q.shape
     _check(k_codes, "k_codes", dtype=torch.uint8)
     if k_codes.dim() != 4 or k_codes.shape[0] != B or k_codes.shape[3] * 2 != D:
-        raise ValueError(f"k_codes must be [B={B}, T_max, Hkv, {D // 2}] (got {tuple(k_codes.shape)})")
-    T_max, Hkv = k_codes.shape[1], k_codes.shape[2]
+        raise ValueError(f"k_codes must be [B={B}, Hkv, T_max, {D // 2}] (got {tuple(k_codes.shape)})")
+    Hkv, T_max = k_codes.shape[1], k_codes.shape[2]
     _check(v_codes, "v_codes", shape=k_codes.shape, dtype=torch.uint8)
-    _check(k_scales, "k_scales", shape=(B, T_max, Hkv), dtype=torch.float32)
-    _check(v_scales, "v_scales", shape=(B, T_max, Hkv), dtype=torch.float32)
+    _check(k_scales, "k_scales", shape=(B, Hkv, T_max), dtype=torch.float32)
+    _check(v_scales, "v_scales", shape=(B, Hkv, T_max), dtype=torch.float32)
     _check(cache_lens, "cache_lens", shape=(B,), dtype=torch.int32)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)

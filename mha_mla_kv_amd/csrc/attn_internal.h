@@ -57,11 +57,11 @@ struct GqaDecodeArgs {
   int page_size = 0;
   int table_stride = 0;
   int n_pages = 0;
-  // caches of signed 4-bit codes (kv_int4 != 0): [B, T_max, Hkv, D/2] bytes,
-  // code 2i in the low nibble of byte i; value = scale of the row * code
+  // caches of signed 4-bit codes (kv_int4 != 0), head-major: [B, Hkv, T_max, D/2]
+  // bytes, code 2i in the low nibble of byte i; value = scale of the row * code
   int kv_int4 = 0;
-  const float* k_scales = nullptr;  // [B, T_max, Hkv]
-  const float* v_scales = nullptr;  // [B, T_max, Hkv]
+  const float* k_scales = nullptr;  // [B, Hkv, T_max]
+  const float* v_scales = nullptr;  // [B, Hkv, T_max]
 };
 
 struct PrefillArgs {

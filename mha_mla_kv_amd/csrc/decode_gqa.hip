@@ -623,7 +623,8 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   float* lse_s = ob + kDecodeWaves * kSliceFloats;  // [HB*16]
   u16* vt = smem + wave * kDecodeTileTokens * VP;
   const size_t tok_stride = (size_t)a.Hkv * D;
-  const int row_bytes = uniform(a.Hkv * RB);
+  // bytes between consecutive positions of one head: int4 caches are head-major
+  const int row_bytes = KV4 ? RB : uniform(a.Hkv * RB);
   // this lane's row within a load and its 16-byte unit in the row
   const int lrow = lane / kLanesPerRow, lunit = min(lane % kLanesPerRow, kUnits - 1);
   const unsigned row_off = (unsigned)(lrow * row_bytes + 16 * lunit);
@@ -631,10 +632,12 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   // base of this (sequence, KV head)'s rows (paged: of the head's rows in the pool)
   auto k_head = [&](const Unit& u) {
     if constexpr (PAGED) return static_cast<const char*>(a.k) + (size_t)u.g * RB;
+    if constexpr (KV4) return static_cast<const char*>(a.k) + ((size_t)u.b * a.Hkv + u.g) * a.T_max * RB;
     return static_cast<const char*>(a.k) + ((size_t)u.b * a.T_max * a.Hkv + u.g) * RB;
   };
   auto v_head = [&](const Unit& u) {
     if constexpr (PAGED) return static_cast<const char*>(a.v) + (size_t)u.g * RB;
+    if constexpr (KV4) return static_cast<const char*>(a.v) + ((size_t)u.b * a.Hkv + u.g) * a.T_max * RB;
     return static_cast<const char*>(a.v) + ((size_t)u.b * a.T_max * a.Hkv + u.g) * RB;
   };
   // paged: the current unit's first page slot and its page numbers (slot
@@ -677,11 +680,10 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   auto load_scales = [&](float& sr, const Unit& u, int t0, int c1) {
     if constexpr (KV4) {
       const int rows = min(max(c1 - t0, 0), kDecodeTileTokens);
-      const size_t r0 = ((size_t)u.b * a.T_max + t0) * a.Hkv + u.g;
+      const size_t r0 = ((size_t)u.b * a.Hkv + u.g) * a.T_max + t0;  // head-major: the 32 scales are contiguous
       const float* base = (lane < 32 ? a.k_scales : a.v_scales) + r0;
-      const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0,
-                                                        max((rows - 1) * a.Hkv * 4 + 4, 0), 0x00020000);
-      sr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (lane & 31) * a.Hkv * 4, 0, 0));
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, rows * 4, 0x00020000);
+      sr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (lane & 31) * 4, 0, 0));
     }
   };
   // The same registers written to this wave's LDS tile, row pitch `pitch`.

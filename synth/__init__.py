@@ -99,10 +99,11 @@ def gqa_decode_fp8_inputs(B: int, Hq: int, Hkv: int, D: int, T_max: int, lens, s
 def gqa_decode_int4_inputs(B: int, Hq: int, Hkv: int, D: int, T_max: int, lens, seed: int = 0,
                            poison: bool = True) -> dict:
     """q [B,Hq,D] bf16 and K/V caches stored as packed signed 4-bit codes with one fp32 scale per
-    cached row: k [B,T_max,Hkv,D/2] uint8 (code 2i in the low nibble of byte i, two's complement),
-    k_scale [B,T_max,Hkv] float32, the same for v.  Each row is drawn N(0, 1) in float32, its scale
-    is max|x| / 7 and its codes round(x / scale) clamped to [-8, 7] (round half to even).  Draw
-    order q, k, v, lens.  With poison, the scales of rows past each length are NaN."""
+    cached row, head-major: k [B,Hkv,T_max,D/2] uint8 (code 2i in the low nibble of byte i, two's
+    complement), k_scale [B,Hkv,T_max] float32, the same for v.  Each row is drawn N(0, 1) in
+    float32 (drawn as [B,T_max,Hkv,D], then stored head-major), its scale is max|x| / 7 and its
+    codes round(x / scale) clamped to [-8, 7] (round half to even).  Draw order q, k, v, lens.
+    With poison, the scales of rows past each length are NaN."""
     rng = _rng(seed)
     q = _as(_normal(rng, (B, Hq, D)), "bf16")
     k = _normal(rng, (B, T_max, Hkv, D))
@@ -110,6 +111,7 @@ def gqa_decode_int4_inputs(B: int, Hq: int, Hkv: int, D: int, T_max: int, lens, 
     L = _lengths(rng, B, T_max, lens)
     out = {"q": q, "cache_lens": torch.from_numpy(L.copy())}
     for name, x in (("k", k), ("v", v)):
+        x = x.transpose(0, 2, 1, 3)  # head-major
         scale = (np.abs(x).max(axis=-1) / np.float32(7.0)).astype(np.float32)
         scale = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
         codes = np.clip(np.rint(x / scale[..., None]), -8, 7).astype(np.int64)
@@ -117,7 +119,7 @@ def gqa_decode_int4_inputs(B: int, Hq: int, Hkv: int, D: int, T_max: int, lens, 
         packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
         if poison:
             for b, n in enumerate(L.tolist()):
-                scale[b, max(0, min(int(n), T_max)):] = np.nan
+                scale[b, :, max(0, min(int(n), T_max)):] = np.nan
         out[name] = torch.from_numpy(np.ascontiguousarray(packed))
         out[name + "_scale"] = torch.from_numpy(np.ascontiguousarray(scale))
     return out

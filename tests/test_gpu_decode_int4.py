@@ -13,7 +13,10 @@ pytestmark = pytest.mark.gpu
 
 
 def _values(inp, name, sl=slice(None)):
-    return oracle.int4_to_float(inp[name][sl].numpy(), inp[name + "_scale"][sl].numpy()).astype(np.float32)
+    """The cache's values in the [B,T_max,Hkv,128] layout the oracle decode takes (the int4 caches
+    are head-major)."""
+    x = oracle.int4_to_float(inp[name][sl].numpy(), inp[name + "_scale"][sl].numpy())
+    return np.ascontiguousarray(x.transpose(0, 2, 1, 3)).astype(np.float32)
 
 
 def _run(inp, **kw):
@@ -68,7 +71,7 @@ def test_int4_decode_extreme_codes():
     for name in ("k_scale", "v_scale"):
         sc = torch.full_like(inp[name], 0.125)
         for b in range(2):
-            sc[b, L[b]:] = float("nan")
+            sc[b, :, L[b]:] = float("nan")
         inp[name] = sc
     assert_close_rows(_run(inp), _ref(inp), TOL_BF16, "extreme codes")
 
