@@ -90,6 +90,32 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// int4 cache words: the 8 codes of a word (two per byte, low nibble first) as
+// eight bf16 of value 136 + c.  Byte t times 0x1001 puts its high nibble at
+// bits 16..19 beside the low one at bits 0..3; (x & 0x000F000F) ^ 0x43084308
+// keeps the two nibbles, flips their sign bits (c + 8) and sets the exponent
+// (0x4300), one v_bitop3 (truth table 0x6a: (s0 & s1) ^ s2).
+__device__ __forceinline__ u32x4 int4_word(unsigned w) {
+  u32x4 h;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    h[k] = __builtin_amdgcn_bitop3_b32(((w >> (8 * k)) & 0xFFu) * 0x1001u, 0x000F000Fu, 0x43084308u, 0x6a);
+  return h;
+}
+
+// fp8 cache words: the 8 E4M3 codes of two words as eight bf16 (exact).  Each
+// conversion widens the codes of one 16-bit half into a pair of bf16; the pairs
+// are moved as whole words (extracting the two bf16 of a pair separately was
+// miscompiled into a copy of the first one).
+__device__ __forceinline__ u32x4 fp8_words(unsigned w0, unsigned w1) {
+  u32x4 h;
+  h[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false));
+  h[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true));
+  h[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false));
+  h[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true));
+  return h;
+}
+
 // ds_read_b64_tr_b16 (gfx950): within each 16-lane group, lane i supplies the
 // address of 4 consecutive 16-bit elements M[i][0..3]; lane j receives
 // M[j/4 + 4k][j%4] for k = 0..3.  With lane i pointing at row (T0 + i/4),
@@ -588,11 +614,16 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   constexpr int KC = D / 32;           // 32-wide dim chunks (QK contraction)
   constexpr int DW = D / 16;           // 16-wide dim blocks (PV output rows)
   constexpr int VP = D + 16;           // V tile row pitch in elements ([token][dim], padded)
-  constexpr int KP = D + 8;            // K tile row pitch (16 rows of one column: distinct LDS banks)
   constexpr int kUnits = RB / 16;                             // 16-byte units per K/V row
   constexpr int kLanesPerRow = kUnits <= 4 ? 4 : kUnits <= 8 ? 8 : 16;  // lanes that load one row
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;
-  constexpr int kLoads = kDecodeTileTokens / kRowsPerLoad;   // 16-byte loads per lane per tile
+  constexpr int kLoads = kDecodeTileTokens / kRowsPerLoad;   // 16-byte V loads per lane per tile
+  // int4 K tiles go straight from memory into the MFMA operands; bf16 and
+  // fp8 K tiles go through LDS like V (a lane's operand is 64 bytes of a row
+  // in 16-byte pieces: read directly, each load instruction would take half
+  // of every line of 16 rows, and the bf16 decode ran 4% slower)
+  constexpr bool KD = KV4;
+  constexpr int KP = D + 8;            // K tile row pitch (16 rows of one column: distinct LDS banks)
   constexpr int kStep = kDecodeWaves * kDecodeTileTokens;    // positions per round of the four waves
   constexpr int kVtElems = kDecodeWaves * kDecodeTileTokens * VP;
   // epilogue scratch (floats), overlaying the tiles: m and l per wave and head,
@@ -622,7 +653,6 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   float* ob = lw + kDecodeWaves * HB * 16;      // [waves][HB*16][OP]
   float* lse_s = ob + kDecodeWaves * kSliceFloats;  // [HB*16]
   u16* vt = smem + wave * kDecodeTileTokens * VP;
-  const size_t tok_stride = (size_t)a.Hkv * D;
   // bytes between consecutive positions of one head: int4 caches are head-major
   const int row_bytes = KV4 ? RB : uniform(a.Hkv * RB);
   // this lane's row within a load and its 16-byte unit in the row
@@ -655,7 +685,7 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
     return head0 + (size_t)t0 * row_bytes;
   };
 
-  // K and V tiles of 32 positions are read in row order with streaming
+  // V tiles of 32 positions are read in row order with streaming
   // (non-temporal) buffer loads: lane group lane / kLanesPerRow of load i
   // fetches row kRowsPerLoad * i + lane / kLanesPerRow, each lane one 16-byte
   // unit (head_dim 96: lanes past the 12th unit repeat it), so a load covers
@@ -664,17 +694,38 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
   // zeros and cost no memory traffic, so loads ahead can be issued
   // unconditionally.  One resource per tile keeps the scalar work per load to
   // an offset.
-  auto load_rows = [&](bf16x8 (&r)[kLoads], const char* head0, int t0, int c1) {
+  // 16-byte chunk j of a tile row (dims 8j .. 8j+7) is stored at chunk
+  // swz(j) = j ^ ((j >> 3) & 1): with the widened fp8 and int4 rows, the
+  // eight lanes of one 128-byte LDS pass then write eight distinct bank groups
+  // (unswizzled, chunks j and j + 8 of a row share theirs).
+  auto swz = [](int j) { return j ^ ((j >> 3) & 1); };
+  auto tile_rsrc = [&](const char* head0, int t0, int c1) {
     // rows of the tile before c1, 0..32; bytes up to the end of the last
     // (row_bytes >= RB, so no rows gives a non-positive count)
     const int rows = min(max(c1 - t0, 0), kDecodeTileTokens);
     const int n = max(rows * row_bytes - row_bytes + RB, 0);
-    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(tile_base(head0, t0)), (short)0, n, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(tile_base(head0, t0)), (short)0, n, 0x00020000);
+  };
+  auto load_rows = [&](bf16x8 (&r)[kLoads], const char* head0, int t0, int c1) {
+    const auto rs = tile_rsrc(head0, t0, c1);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
       r[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                             rs, (int)(row_off + (unsigned)(kRowsPerLoad * i * row_bytes)), 0, kStreamPolicy));
   };
+  // int4 K tiles go straight into the scores' MFMA operands (no LDS): lane
+  // (row, grp) reads the 16 bytes of its 32 contiguous dims 32grp .. 32grp+31
+  // of the rows of tokens 16s + row (s = 0, 1), a whole 64-byte row per four
+  // lanes; operand slot c holds dims 32grp + 8c .. +8, and so does the query
+  // operand.  Rows at or past c1 read as zeros.
+  auto load_k = [&](bf16x8 (&r)[kLoads], const char* head0, int t0, int c1) {
+    const auto rs = tile_rsrc(head0, t0, c1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      r[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, (16 * s + row) * row_bytes + 16 * grp, 0, kStreamPolicy));
+  };
+  static_assert(!KD || kLoads == 2, "int4: two 16-byte loads per lane and tile, as the V tile");
   // int4: the tile's scales, lane l < 32 the K scale of row t0 + l, lane l >= 32
   // the V scale of row t0 + l - 32 (rows at or past c1 read as zeros)
   auto load_scales = [&](float& sr, const Unit& u, int t0, int c1) {
@@ -686,51 +737,33 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
       sr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (lane & 31) * 4, 0, 0));
     }
   };
-  // The same registers written to this wave's LDS tile, row pitch `pitch`.
+  // Tile registers written to this wave's LDS tile ([token][dim], row pitch
+  // `pitch`, chunks swizzled).
   // fp8 rows: each 16-byte unit holds 16 values, widened to two 16-byte bf16 writes.
   // int4 rows: each 16-byte unit holds 32 codes, widened to four 16-byte writes.
   auto store_rows = [&](const bf16x8 (&r)[kLoads], int pitch) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      u16* dst = vt + (kRowsPerLoad * i + lrow) * pitch + kEPU * lunit;
-      if constexpr (KV4) {
-        // word w holds codes 8w .. 8w+7 of the unit, low nibble first; offset
-        // binary (c + 8) by flipping the sign bits; pair k of the word as one
-        // 32-bit word of two bf16 (136 + c)
-        const u32x4 wd = __builtin_bit_cast(u32x4, r[i]);
+      u16* dst = vt + (kRowsPerLoad * i + lrow) * pitch;
+      constexpr int kChunks = kEPU / 8;  // 16-byte bf16 chunks per loaded unit
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const unsigned u8s = wd[w] ^ 0x88888888u;
-          u32x4 h;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const unsigned t = (u8s >> (8 * k)) & 0xFFu;  // the pair's byte alone
-            h[k] = (((t << 12) | t) & 0x000F000Fu) | 0x43004300u;
-          }
-          *reinterpret_cast<u32x4*>(dst + 8 * w) = h;
+      for (int w = 0; w < kChunks; ++w) {
+        const int j = kChunks * lunit + w;
+        u16* p = dst + 8 * swz(j);
+        if constexpr (KV4) {
+          *reinterpret_cast<u32x4*>(p) = int4_word(__builtin_bit_cast(u32x4, r[i])[w]);
+        } else if constexpr (KV8) {
+          const u32x4 wd = __builtin_bit_cast(u32x4, r[i]);
+          *reinterpret_cast<u32x4*>(p) = fp8_words(wd[2 * w], wd[2 * w + 1]);
+        } else {
+          *reinterpret_cast<u16x8*>(p) = __builtin_bit_cast(u16x8, r[i]);
         }
-      } else if constexpr (KV8) {
-        // each conversion widens the codes of one 16-bit half of a word into a
-        // pair of bf16 (one 32-bit word); the pairs are moved as whole words
-        // (extracting the two bf16 of a pair separately was miscompiled into a
-        // copy of the first one)
-        const u32x4 wd = __builtin_bit_cast(u32x4, r[i]);
-        u32x4 h[2];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          h[q >> 1][2 * (q & 1)] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[q], 1.f, false));
-          h[q >> 1][2 * (q & 1) + 1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[q], 1.f, true));
-        }
-        *reinterpret_cast<u32x4*>(dst) = h[0];
-        *reinterpret_cast<u32x4*>(dst + 8) = h[1];
-      } else {
-        *reinterpret_cast<u16x8*>(dst) = __builtin_bit_cast(u16x8, r[i]);
       }
     }
   };
 
   // Registers that carry a unit's inputs: Q^T as the B operand (lane holds
-  // Q[head = 16hb + row][dims 32c + 8grp .. +8]) and this wave's next K/V tile.
+  // Q[head = 16hb + row][the dims of slot c]) and this wave's next K/V tile.
   bf16x8 qop[HB][KC];
   bf16x8 kr[kLoads], vr[kLoads];
   float sr = 0.f;  // int4: the next tile's scale (see load_scales)
@@ -752,19 +785,26 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
     for (int hb = 0; hb < HB; ++hb) {
       const int head = hb * 16 + row;
 #pragma unroll
-      for (int c = 0; c < KC; ++c)
+      for (int c = 0; c < KC; ++c) {
+        const int dim = KD ? 32 * grp + 8 * c : 32 * c + 8 * grp;
         qop[hb][c] = __builtin_bit_cast(
-            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qs, (head * D + 32 * c + 8 * grp) * 2, 0, 0));
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qs, (head * D + dim) * 2, 0, 0));
+      }
     }
-    load_rows(kr, k_head(u), u.t0 + wave * kDecodeTileTokens, u.t1);
+    if constexpr (KD) load_k(kr, k_head(u), u.t0 + wave * kDecodeTileTokens, u.t1);
+    else load_rows(kr, k_head(u), u.t0 + wave * kDecodeTileTokens, u.t1);
     load_rows(vr, v_head(u), u.t0 + wave * kDecodeTileTokens, u.t1);
     load_scales(sr, u, u.t0 + wave * kDecodeTileTokens, u.t1);
   };
 
   // Streams unit u (begin_unit(u) issued): this wave's online-softmax state.
   float m[HB], lsum[HB];
-  float psum[HB], qsum[HB];  // int4: sum of the PV probabilities, sum of q (this lane's head row)
+  float psum[HB], q136[HB];  // int4: sum of the PV probabilities, 136 * sum of q (this lane's head row)
   f32x4 o[HB][DW];  // O^T: lane holds dims 16w + 4grp + i of head 16hb + row
+  // the transposed V reads: lane's 4-dim group of row 4grp + row / 4, for
+  // dim blocks w < 4 and (chunk parity flipped by the swizzle) w >= 4
+  const u16* trbase = vt + (4 * grp + (row >> 2)) * VP + 4 * (row & 3);
+  const u16* trbase_hi = vt + (4 * grp + (row >> 2)) * VP + 8 * (((row >> 1) & 1) ^ 1) + 4 * (row & 1);
   auto stream_unit = [&](const Unit& u, NextUnit& nx) {
     const char* kp = k_head(u);
     const char* vp = v_head(u);
@@ -782,16 +822,20 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
         for (int c = 0; c < KC; ++c)
 #pragma unroll
           for (int e = 0; e < 8; ++e) qs += (float)qop[hb][c][e];
-        qsum[hb] = sum_xor32(sum_xor16(qs));
+        q136[hb] = 136.f * sum_xor32(sum_xor16(qs));
       }
     }
-    // Per tile: K(t) -> LDS; scores from LDS; K(t + kStep) requested; V(t) ->
-    // LDS (same region); V(t + kStep) requested; softmax; PV from LDS.
-    // The wave's last tile requests nothing further: a load past the unit end
-    // would read nothing, but it still makes a round trip, and the next unit's
-    // loads into the same registers would wait for it.
+    // Per tile: K(t) -> LDS (int4: the K registers are the operands); scores;
+    // K(t + kStep) requested; V(t) -> LDS (same region); V(t + kStep)
+    // requested; softmax; PV from LDS.  Only a unit's last
+    // tile can hold positions at or past its end (the others end before
+    // t0 + kStep < c1), so only it masks the scores.  The wave's last tile
+    // requests nothing further: a load past the unit end would read nothing,
+    // but it still makes a round trip, and the next unit's loads into the same
+    // registers would wait for it.
     auto tile = [&](const int t0, auto next) {
       constexpr bool NEXT = decltype(next)::value;
+      constexpr bool MASK = !NEXT;
       if constexpr (QUEUE) {
         // second-to-last tile of wave 0 (or its only one): take the workgroup's
         // next unit, so the queue's round trip overlaps the end of this one
@@ -800,22 +844,31 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
           nx.valid = 1;
         }
       }
-      store_rows(kr, KP);
-      if constexpr (KV4) scl[wave * 64 + lane] = sr;
-      wave_lds_sync();
-      // Scores: lane holds S^T[token 16u + 4grp + i][head 16hb + row]; the A
-      // operand (token 16u + row, dims 32c + 8grp .. +8) comes from LDS.
-      float sc[HB][2][4];
+      // Raw scores: lane holds S^T[token 16s + 4grp + i][head 16hb + row]; the
+      // A operand (token 16s + row, the dims of slot c) from the K registers
+      // (int4) or from LDS (dims 32c + 8grp .. +8).
+      f32x4 acc[HB][2];
       {
         bf16x8 ka[2][KC];
+        if constexpr (KD) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+          for (int s = 0; s < 2; ++s) {
+            const u32x4 wd = __builtin_bit_cast(u32x4, kr[s]);
 #pragma unroll
-          for (int c = 0; c < KC; ++c)
-            ka[s][c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(vt + (16 * s + row) * KP + 32 * c + 8 * grp));
+            for (int c = 0; c < KC; ++c) ka[s][c] = __builtin_bit_cast(bf16x8, int4_word(wd[c]));
+          }
+        } else {
+          store_rows(kr, KP);
+          wave_lds_sync();
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+              ka[s][c] = __builtin_bit_cast(
+                  bf16x8, *reinterpret_cast<const u16x8*>(vt + (16 * s + row) * KP + 8 * swz(4 * c + grp)));
+        }
         // the accumulation chains of the two token blocks (and head blocks)
         // alternate, so no MFMA waits for the one issued just before it
-        f32x4 acc[HB][2];
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
@@ -826,38 +879,41 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
           for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
             for (int s = 0; s < 2; ++s) acc[hb][s] = mfma_16x16x32(ka[s][c], qop[hb][c], acc[hb][s]);
-        f32x4 ks[2] = {};
-        if constexpr (KV4) {
-#pragma unroll
-          for (int s = 0; s < 2; ++s) ks[s] = *reinterpret_cast<const f32x4*>(&scl[wave * 64 + 16 * s + 4 * grp]);
-        }
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int tok = t0 + 16 * s + 4 * grp + i;
-              float x = acc[hb][s][i] * a.scale_log2e;
-              if constexpr (KV4) x = (acc[hb][s][i] - 136.f * qsum[hb]) * ks[s][i] * a.scale_log2e;
-              sc[hb][s][i] = tok < c1 ? x : kNegInf;
-            }
       }
-      // the next K tile after the scores: its registers are then free (this
-      // tile is in LDS)
+      // the next K tile once this one's operands are consumed; V overwrites the
+      // K tile after its operand reads are done
       __builtin_amdgcn_sched_barrier(0);
-      f32x4 vs[2] = {};
+      if constexpr (NEXT) {
+        if constexpr (KD) load_k(kr, kp, t0 + kStep, c1);
+        else load_rows(kr, kp, t0 + kStep, c1);
+      }
+      if constexpr (!KD) wave_lds_sync();
+      if constexpr (KV4) scl[wave * 64 + lane] = sr;
+      store_rows(vr, VP);
+      if constexpr (NEXT) load_scales(sr, u, t0 + kStep, c1);
+      wave_lds_sync();
+      if constexpr (NEXT) load_rows(vr, vp, t0 + kStep, c1);
+      f32x4 ks[2] = {}, vs[2] = {};
       if constexpr (KV4) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) vs[s] = *reinterpret_cast<const f32x4*>(&scl[wave * 64 + 32 + 16 * s + 4 * grp]);
+        for (int s = 0; s < 2; ++s) {
+          ks[s] = *reinterpret_cast<const f32x4*>(&scl[wave * 64 + 16 * s + 4 * grp]);
+          vs[s] = *reinterpret_cast<const f32x4*>(&scl[wave * 64 + 32 + 16 * s + 4 * grp]);
+        }
       }
-      if constexpr (NEXT) {
-        load_rows(kr, kp, t0 + kStep, c1);
-        load_scales(sr, u, t0 + kStep, c1);
-      }
-      wave_lds_sync();
-      store_rows(vr, VP);
-      if constexpr (NEXT) load_rows(vr, vp, t0 + kStep, c1);
+      float sc[HB][2][4];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x;
+            if constexpr (KV4) x = (acc[hb][s][i] - q136[hb]) * (ks[s][i] * a.scale_log2e);
+            else x = acc[hb][s][i] * a.scale_log2e;
+            if constexpr (MASK) x = t0 + 16 * s + 4 * grp + i < c1 ? x : kNegInf;
+            sc[hb][s][i] = x;
+          }
       // Online softmax per head; P^T as the B operand of the PV product.
       bf16x8 pop[HB];
 #pragma unroll
@@ -877,15 +933,18 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
         for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            // the row sum adds the bf16-rounded probability the PV product uses
             const float p = exp2_fast(sc[hb][s][i] - mn);
-            const __bf16 pb = (__bf16)p;
-            ps += (float)pb;
             if constexpr (KV4) {
-              const __bf16 pvb = (__bf16)(p * vs[s][i]);  // the V scale of the row
+              // the PV operand is p times the row's V scale; the offset
+              // removal needs the sum of exactly those bf16 values
+              ps += p;
+              const __bf16 pvb = (__bf16)(p * vs[s][i]);
               pv += (float)pvb;
               pop[hb][4 * s + i] = pvb;
             } else {
+              // the row sum adds the bf16-rounded probability the PV product uses
+              const __bf16 pb = (__bf16)p;
+              ps += (float)pb;
               pop[hb][4 * s + i] = pb;
             }
           }
@@ -894,15 +953,14 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
 #pragma unroll
         for (int w = 0; w < DW; ++w) o[hb][w] *= alpha;
       }
-      wave_lds_sync();
       // O^T[dims 16w..][heads] += V^T[16 dims][32 tokens (permuted)] P^T; the A operand
       // (tokens 4grp..4grp+3 and 16+4grp..16+4grp+3 of dim 16w+row) comes from two
       // transposed LDS reads.
-      const u16* trbase = vt + (4 * grp + (row >> 2)) * VP + 4 * (row & 3);
 #pragma unroll
       for (int w = 0; w < DW; ++w) {
-        const u16x4 lo = lds_read_tr16(trbase + 16 * w);
-        const u16x4 hi = lds_read_tr16(trbase + 16 * VP + 16 * w);
+        const u16* tb = (w < 4 ? trbase : trbase_hi) + 16 * w;
+        const u16x4 lo = lds_read_tr16(tb);
+        const u16x4 hi = lds_read_tr16(tb + 16 * VP);
         const u16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) o[hb][w] = mfma_16x16x32(__builtin_bit_cast(bf16x8, av), pop[hb], o[hb][w]);
