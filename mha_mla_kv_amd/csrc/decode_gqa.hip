@@ -86,6 +86,11 @@ __device__ __forceinline__ float bf16_to_f32(u16 x) { return __builtin_bit_cast(
 // once per call; these loads neither displace reusable lines nor wait on them.
 constexpr int kStreamPolicy = 2;
 
+// The decode's running max moves only when a tile's max exceeds it by more than
+// this (log2 units): probabilities stay below 2^8, and most tiles skip the
+// rescale of the accumulators.
+constexpr float kLazyMax = 8.f;
+
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -603,7 +608,7 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
 // scales of a tile are read with the tile (one per lane) and staged in LDS.
 template <int D, int HB, bool QUEUE, bool KV8 = false, bool PAGED = false, bool KV4 = false>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(HB > 2 ? 1 : (HB > 1 ? 2 : (D >= 96 ? (QUEUE ? 2 : 3) : 4)))))
+__attribute__((amdgpu_waves_per_eu(HB > 2 || (HB > 1 && KV4) ? 1 : (HB > 1 ? 2 : (D >= 96 ? (QUEUE ? 2 : 3) : 4)))))
 void gqa_decode_bf16(GqaDecodeArgs a) {
   static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
   static_assert(!KV8 || D == 128, "fp8 caches: head_dim 128");
@@ -799,7 +804,8 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
 
   // Streams unit u (begin_unit(u) issued): this wave's online-softmax state.
   float m[HB], lsum[HB];
-  float psum[HB], q136[HB];  // int4: sum of the PV probabilities, 136 * sum of q (this lane's head row)
+  float q136[HB];     // int4: 136 * sum of q (this lane's head row)
+  f32x4 psum[HB];     // int4: sum of the PV operand p' per head (every element), by MFMA
   f32x4 o[HB][DW];  // O^T: lane holds dims 16w + 4grp + i of head 16hb + row
   // the transposed V reads: lane's 4-dim group of row 4grp + row / 4, for
   // dim blocks w < 4 and (chunk parity flipped by the swizzle) w >= 4
@@ -813,7 +819,7 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
     for (int hb = 0; hb < HB; ++hb) {
       m[hb] = kNegInf;
       lsum[hb] = 0.f;
-      psum[hb] = 0.f;
+      psum[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < DW; ++w) o[hb][w] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (KV4) {
@@ -888,7 +894,7 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
         else load_rows(kr, kp, t0 + kStep, c1);
       }
       if constexpr (!KD) wave_lds_sync();
-      if constexpr (KV4) scl[wave * 64 + lane] = sr;
+      if constexpr (KV4) scl[wave * 64 + lane] = lane < 32 ? sr * a.scale_log2e : sr;  // K scales: times the softmax scale
       store_rows(vr, VP);
       if constexpr (NEXT) load_scales(sr, u, t0 + kStep, c1);
       wave_lds_sync();
@@ -909,13 +915,19 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float x;
-            if constexpr (KV4) x = (acc[hb][s][i] - q136[hb]) * (ks[s][i] * a.scale_log2e);
+            if constexpr (KV4) x = (acc[hb][s][i] - q136[hb]) * ks[s][i];
             else x = acc[hb][s][i] * a.scale_log2e;
             if constexpr (MASK) x = t0 + 16 * s + 4 * grp + i < c1 ? x : kNegInf;
             sc[hb][s][i] = x;
           }
-      // Online softmax per head; P^T as the B operand of the PV product.
+      // Online softmax per head; P^T as the B operand of the PV product.  The
+      // running max moves only when a tile's max exceeds it by more than
+      // kLazyMax (log2 units), so the probabilities stay below 2^kLazyMax and
+      // the accumulators are rescaled only on such tiles (rare once the first
+      // tiles have set the max).
       bf16x8 pop[HB];
+      float alpha[HB];
+      bool up_any = false;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         float mt = kNegInf;
@@ -925,22 +937,21 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
           for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sc[hb][s][i]);
         mt = max_xor16(mt);
         mt = max_xor32(mt);
-        const float mn = fmaxf(m[hb], mt);  // finite: the tile's first token is valid
-        const float alpha = exp2_fast(m[hb] - mn);
+        const bool up = mt > m[hb] + kLazyMax;  // the tile's first token is valid: mt is finite
+        const float mn = up ? mt : m[hb];
+        alpha[hb] = exp2_fast(m[hb] - mn);  // 1 unless up (0 on the first tile)
+        up_any |= up;
         m[hb] = mn;
-        float ps = 0.f, pv = 0.f;
+        float ps = 0.f;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float p = exp2_fast(sc[hb][s][i] - mn);
             if constexpr (KV4) {
-              // the PV operand is p times the row's V scale; the offset
-              // removal needs the sum of exactly those bf16 values
+              // the PV operand is p times the row's V scale
               ps += p;
-              const __bf16 pvb = (__bf16)(p * vs[s][i]);
-              pv += (float)pvb;
-              pop[hb][4 * s + i] = pvb;
+              pop[hb][4 * s + i] = (__bf16)(p * vs[s][i]);
             } else {
               // the row sum adds the bf16-rounded probability the PV product uses
               const __bf16 pb = (__bf16)p;
@@ -948,10 +959,23 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
               pop[hb][4 * s + i] = pb;
             }
           }
-        lsum[hb] = lsum[hb] * alpha + ps;
-        if constexpr (KV4) psum[hb] = psum[hb] * alpha + pv;
+        lsum[hb] = lsum[hb] * alpha[hb] + ps;
+      }
+      if (__builtin_amdgcn_ballot_w64(up_any) != 0) {
 #pragma unroll
-        for (int w = 0; w < DW; ++w) o[hb][w] *= alpha;
+        for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+          for (int w = 0; w < DW; ++w) o[hb][w] *= alpha[hb];
+          if constexpr (KV4) psum[hb] *= alpha[hb];
+        }
+      }
+      // int4: sum p' over the tile's tokens with the PV product's own operands
+      // (an A operand of ones), for the offset removal
+      if constexpr (KV4) {
+        const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                             (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) psum[hb] = mfma_16x16x32(ones, pop[hb], psum[hb]);
       }
       // O^T[dims 16w..][heads] += V^T[16 dims][32 tokens (permuted)] P^T; the A operand
       // (tokens 4grp..4grp+3 and 16+4grp..16+4grp+3 of dim 16w+row) comes from two
@@ -977,8 +1001,9 @@ void gqa_decode_bf16(GqaDecodeArgs a) {
       lsum[hb] = sum_xor16(lsum[hb]);
       lsum[hb] = sum_xor32(lsum[hb]);
       if constexpr (KV4) {
-        // remove the codes' offset: O^T holds sum p' (136 + c)
-        const float off = 136.f * sum_xor32(sum_xor16(psum[hb]));
+        // remove the codes' offset: O^T holds sum p' (136 + c); every element
+        // of psum holds this lane's head's sum p'
+        const float off = 136.f * psum[hb][0];
 #pragma unroll
         for (int w = 0; w < DW; ++w) o[hb][w] -= off;
       }
@@ -1218,14 +1243,17 @@ hipError_t launch_one(Kernel kernel, const GqaDecodeArgs& a, dim3 grid, hipStrea
 // their units longest).  FP8 caches: two.  A tile then carries half the bytes
 // for the same LDS, MFMA and softmax work, and a lone wave per SIMD leaves the
 // chains of dependent steps bare; a second workgroup fills them (Llama-3-8B
-// shaped decode, B 32: 60.0 -> 55.4 us; three: 59.0 us).
+// shaped decode, B 32: 60.0 -> 55.4 us; three: 59.0 us, and again 59.5 against
+// 65.8 us once the LDS tiles were swizzled).  int4 caches: three (a quarter of
+// the bytes per tile and more VALU work to widen them; 49.3 -> 42.9 us).
 constexpr int kMfmaWgsPerCu = 1;
 constexpr int kMfmaWgsPerCuFp8 = 2;
+constexpr int kMfmaWgsPerCuInt4 = 3;
 
 template <int D, bool QUEUE, bool KV8 = false, bool PAGED = false, bool KV4 = false>
 hipError_t launch_bf16(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
   const int hb = (a.n_rep + 15) / 16;
-  constexpr int kNarrow = KV8 || KV4 ? kMfmaWgsPerCuFp8 : kMfmaWgsPerCu;  // workgroups per CU, one head block
+  constexpr int kNarrow = KV4 ? kMfmaWgsPerCuInt4 : (KV8 ? kMfmaWgsPerCuFp8 : kMfmaWgsPerCu);  // workgroups per CU, one head block
   if (hb == 1) return launch_one(gqa_decode_bf16<D, 1, QUEUE, KV8, PAGED, KV4>, a, grid, st, kNarrow);
   if (hb == 2) return launch_one(gqa_decode_bf16<D, 2, QUEUE, KV8, PAGED, KV4>, a, grid, st, kMfmaWgsPerCu);
   if (hb <= 4) return launch_one(gqa_decode_bf16<D, 4, QUEUE, KV8, PAGED, KV4>, a, grid, st, kMfmaWgsPerCu);
