@@ -245,6 +245,13 @@ def main():
                      kr[torch.arange(MB, device=dev), mla_last.long()].contiguous())            # [B, dR]
                     for c, kr in mla_copies]
     mla_step_out = torch.empty(MB, H, dv, dtype=torch.float32, device=dev)
+    # paged view of the same caches: 16-position pages, every sequence's pages scattered over the
+    # whole pool by a seeded permutation (each cache copy is a pool, read through the same table)
+    mpg_size = 16
+    mpg_max = MT // mpg_size
+    mpg_table = torch.randperm(MB * mpg_max, generator=torch.Generator().manual_seed(12)).to(torch.int32)
+    mpg_table = mpg_table.view(MB, mpg_max).to(dev)
+    mpg_out = torch.empty(MB, H, dv, dtype=torch.float32, device=dev)
     mla_step_ws = torch.zeros(attn.attn_decode_mla_workspace_bytes(MB, H, r, dR, MT, 0), dtype=torch.uint8,
                               device=dev)
 
@@ -310,6 +317,12 @@ def main():
         attn.attn_decode_mla_absorbed(mla["q_nope"], mla["q_rope"], mla["w_uk"], mla["w_uv"], c, kr,
                                       mla["cache_lens"], out=mla_out, workspace=mla_ws)
 
+    def run_mla_paged(i):
+        c, kr = mla_copies[i % len(mla_copies)]
+        attn.attn_decode_mla_paged(mla["q_nope"], mla["q_rope"], mla["w_uk"], mla["w_uv"],
+                                   c.view(MB * mpg_max, mpg_size, r), kr.view(MB * mpg_max, mpg_size, dR), mpg_table,
+                                   mla["cache_lens"], out=mpg_out, workspace=mla_ws)
+
     def run_prefill(i):
         attn.attn_prefill_gqa_causal(pre["q"], pre["k"], pre["v"], out=pre_out)
 
@@ -369,6 +382,7 @@ def main():
     # step takes), then the sweep settings; each part is timed on its own
     parts = [("prefill", run_prefill), ("chunked_prefill", run_chunked), ("chunked_prefill_append", run_chunked_append),
              ("mla_prefill", run_mla_prefill), ("mla_decode", run_mla), ("mla_decode_step", run_mla_step),
+             ("mla_decode_paged", run_mla_paged),
              ("kv_append", run_append), ("rope_append_decode", run_rope_decode), ("rope_append_chunk", run_rope_chunk),
              ("gqa_decode", run_decode), ("gqa_decode_paged", run_paged), ("gqa_decode_step", run_step),
              ("gqa_decode_fp8", run_fp8), ("gqa_decode_int4", run_int4)]
@@ -434,7 +448,7 @@ def main():
                          "bf16 in, fp32 out, default schedule (device-wide unit queue, library-chosen blocks)"),
             "step": ", ".join(name for name, _ in parts) + ": one call each; timed part by part, each "
                     "part's K calls back to back between one event pair, in this order",
-            "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "mla_decode_step": MB, "prefill": PB * S,
+            "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "mla_decode_step": MB, "mla_decode_paged": MB, "prefill": PB * S,
                                 "chunked_prefill": chk_tokens, "chunked_prefill_append": chk_tokens,
                                 "mla_prefill": MPB * MPS},
         },
@@ -502,6 +516,10 @@ def main():
         decode_part("mla_decode_step", mla_bytes, MB, mla_flops,
                     "minimind768_mla_decode with the newest rows as the new token (attn_decode_mla_append: "
                     "decode over cache_lens - 1 rows plus the new row, which is written at cache_lens - 1)")
+    if "mla_decode_paged" in ms:
+        decode_part("mla_decode_paged", mla_bytes, MB, mla_flops,
+                    f"minimind768_mla_decode shape and lengths over paged latent caches: {mpg_size}-position pages, "
+                    "each sequence's pages scattered over the pool by a seeded permutation (attn_decode_mla_paged)")
     if "mla_prefill" in ms:
         prefill_part("mla_prefill", mlp_flops, MPB * MPS,
                      f"minimind768_mla_prefill: B={MPB} S={MPS} H={MPH} nope={MPdn} rope={MPdR} v={MPdv} "

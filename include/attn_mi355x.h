@@ -436,6 +436,44 @@ attn_status attn_decode_mla_absorbed(const void* q_nope, const void* q_rope, con
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* MLA decode over paged latent caches.
+ *
+ *   T_max = page_size * max_pages_per_seq, L = cache_lens[b] clamped to [0, T_max];
+ *   c_kv[b,t,:]   = c_pages[block_table[b * max_pages_per_seq + t / page_size], t % page_size, :]
+ *   k_rope[b,t,:] = k_rope_pages[(the same page)], t % page_size, :]
+ *   and out is attn_decode_mla_absorbed over those rows.
+ *
+ * The latent cache of the qqstock DeepSeek MLA article (sections 1 and 3: only
+ * c_kv and the shared rotated key part are cached) held in the block-table
+ * layout that attn_decode_gqa_paged reads (the "MHA, MQA và GQA" e-book names
+ * paging only as a serving cost, with no scheme): fixed-size pages in one pool
+ * per cache, per sequence a row of page numbers in position order.  Same
+ * arithmetic and results as attn_decode_mla_absorbed on the gathered caches.
+ *
+ *   c_pages      [n_pages, page_size, kv_lora_rank]   in_dtype (16-byte aligned)
+ *   k_rope_pages [n_pages, page_size, rope_dim]       in_dtype (16-byte aligned)
+ *   block_table  [B, max_pages_per_seq] int32, device memory: entries for the
+ *                pages below ceil(L / page_size) are read, each clamped to
+ *                [0, n_pages); unused entries may hold anything
+ *   q_nope, q_rope, w_uk, w_uv, cache_lens, out: as attn_decode_mla_absorbed
+ *
+ * Supported: the shapes of attn_decode_mla_absorbed, page_size a multiple of 16
+ * (else ATTN_ERR_UNSUPPORTED); a chunk of split_tokens positions (the library's
+ * choice when 0) may span at most 128 pages (else ATTN_ERR_UNSUPPORTED, with the
+ * largest split_tokens that fits in the message).  workspace:
+ * attn_decode_mla_workspace_bytes(B, H, kv_lora_rank, rope_dim,
+ * page_size * max_pages_per_seq, split_tokens) bytes.  Errors as
+ * attn_decode_mla_absorbed, plus ATTN_ERR_NULL for a NULL block_table and
+ * ATTN_ERR_SHAPE for non-positive page counts.
+ */
+attn_status attn_decode_mla_paged(const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv,
+                                  const void* c_pages, const void* k_rope_pages, const int32_t* block_table,
+                                  const int32_t* cache_lens, void* out, int B, int H, int nope_head_dim, int rope_dim,
+                                  int v_head_dim, int kv_lora_rank, int page_size, int n_pages, int max_pages_per_seq,
+                                  float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* MLA decode step with the new token's latent row: append and attend in one call.
  *
  *   L = cache_lens[b] (positions cached before this token, clamped to [0, T_max])

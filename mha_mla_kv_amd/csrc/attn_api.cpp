@@ -611,14 +611,18 @@ int attn_decode_mla_supported(int H, int kv_lora_rank, int rope_dim, attn_dtype 
 
 namespace {
 
-// Shared checks and launch of the two MLA decode entry points.  c_new != null:
-// a decode step that also takes the new token's latent row (attn_decode_mla_append).
+// Shared checks and launch of the MLA decode entry points.  c_new != null: a
+// decode step that also takes the new token's latent row (attn_decode_mla_append);
+// block_table != null: paged caches (attn_decode_mla_paged; c_kv and k_rope are
+// page pools, T_max = page_size * table_stride).
 attn_status mla_decode_common(const char* fn, const void* q_nope, const void* q_rope, const void* c_new,
                               const void* kr_new, const void* w_uk, const void* w_uv, const void* c_kv,
                               const void* k_rope, const int32_t* cache_lens, void* out, int B, int H,
                               int nope_head_dim, int rope_dim, int v_head_dim, int kv_lora_rank, int T_max,
                               float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              const int32_t* block_table = nullptr, int page_size = 0, int n_pages = 0,
+                              int table_stride = 0) {
   const bool append = c_new != nullptr;
   if (!q_nope || !q_rope || !w_uk || !w_uv || !c_kv || !k_rope || !cache_lens || !out)
     return fail(ATTN_ERR_NULL, "%s: all tensor pointers must be non-NULL", fn);
@@ -643,6 +647,10 @@ attn_status mla_decode_common(const char* fn, const void* q_nope, const void* q_
     return fail(ATTN_ERR_UNSUPPORTED, "%s: c_kv, k_rope, w_uk, w_uv, out (and the new rows) must be 16-byte aligned",
                 fn);
   const MlaLayout lay = mla_layout(B, H, kv_lora_rank, T_max, split_tokens);
+  if (block_table && lay.split / page_size + 2 > 128)
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "%s: a chunk of %d positions spans more than 128 pages of %d; pass split_tokens of at most %d", fn,
+                lay.split, page_size, 126 * page_size / 64 * 64);
   if (!workspace || workspace_bytes < lay.total)
     return fail(ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given%s", fn, lay.total, workspace_bytes,
                 workspace ? "" : " (NULL)");
@@ -678,6 +686,10 @@ attn_status mla_decode_common(const char* fn, const void* q_nope, const void* q_
   a.kr_new = kr_new;
   a.c_cache = const_cast<void*>(c_kv);
   a.kr_cache = const_cast<void*>(k_rope);
+  a.block_table = block_table;
+  a.page_size = page_size;
+  a.n_pages = n_pages;
+  a.table_stride = table_stride;
   return hip_status(attn::launch_mla_decode(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -693,6 +705,27 @@ attn_status attn_decode_mla_absorbed(const void* q_nope, const void* q_rope, con
   return mla_decode_common("attn_decode_mla_absorbed", q_nope, q_rope, nullptr, nullptr, w_uk, w_uv, c_kv, k_rope,
                            cache_lens, out, B, H, nope_head_dim, rope_dim, v_head_dim, kv_lora_rank, T_max,
                            softmax_scale, in_dtype, out_dtype, split_tokens, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_mla_paged(const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv,
+                                  const void* c_pages, const void* k_rope_pages, const int32_t* block_table,
+                                  const int32_t* cache_lens, void* out, int B, int H, int nope_head_dim, int rope_dim,
+                                  int v_head_dim, int kv_lora_rank, int page_size, int n_pages, int max_pages_per_seq,
+                                  float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "attn_decode_mla_paged";
+  if (!block_table) return fail(ATTN_ERR_NULL, "%s: block_table must be non-NULL", fn);
+  if (page_size <= 0 || n_pages <= 0 || max_pages_per_seq <= 0)
+    return fail(ATTN_ERR_SHAPE, "%s: page_size, n_pages and max_pages_per_seq must be positive (%d, %d, %d)", fn,
+                page_size, n_pages, max_pages_per_seq);
+  if ((long long)page_size * max_pages_per_seq > 0x7fffffffLL)
+    return fail(ATTN_ERR_SHAPE, "%s: page_size * max_pages_per_seq too large", fn);
+  if (page_size % 16 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: page_size=%d must be a multiple of 16", fn, page_size);
+  return mla_decode_common(fn, q_nope, q_rope, nullptr, nullptr, w_uk, w_uv, c_pages, k_rope_pages, cache_lens, out, B,
+                           H, nope_head_dim, rope_dim, v_head_dim, kv_lora_rank, page_size * max_pages_per_seq,
+                           softmax_scale, in_dtype, out_dtype, split_tokens, workspace, workspace_bytes, stream,
+                           block_table, page_size, n_pages, max_pages_per_seq);
 }
 
 attn_status attn_decode_mla_append(const void* q_nope, const void* q_rope, const void* c_new, const void* k_rope_new,

@@ -132,6 +132,16 @@ struct MlaDecodeArgs {
   const void* kr_new;   // [B, dR]
   void* c_cache;        // the c_kv array, written at the new position
   void* kr_cache;       // the k_rope array
+  // paged caches (block_table != null, no append): c_kv and k_rope are pools of
+  // n_pages pages of page_size positions ([n_pages, page_size, r] and
+  // [n_pages, page_size, dR]); position t of sequence b sits in page
+  // block_table[b * table_stride + t / page_size] (clamped to [0, n_pages)), at
+  // row t % page_size.  page_size is a multiple of 16 and a chunk spans at most
+  // 128 pages.
+  const int32_t* block_table = nullptr;
+  int page_size = 0;
+  int table_stride = 0;
+  int n_pages = 0;
 };
 
 struct RopeAppendArgs {

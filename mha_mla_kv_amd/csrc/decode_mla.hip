@@ -189,13 +189,42 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
                                            0x00020000);
 }
 
+// Paged caches: the chunk's page numbers, read once when it starts (slot
+// p0 + i of the sequence's block-table row in lane i % 64 of pg[i / 64]).
+struct ChunkPages {
+  int p0;
+  int pg[2];
+};
+
+// Buffer resource over the 16-row slice at t0 of a paged [n_pages, page_size,
+// width] bf16 cache (page_size a multiple of 16, so the slice lies in one
+// page): its page number comes from the chunk's registers by v_readlane
+// (t0 is wave-uniform), clamped to the pool; rows at or past lim read as zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, const MlaDecodeArgs& a,
+                                                            const ChunkPages& cp, int width, int t0, int lim) {
+  const int rows = min(lim - t0, 16);
+  const int rel = min(max(t0 / a.page_size - cp.p0, 0), 127);
+  const int e = rel < 64 ? __builtin_amdgcn_readlane(cp.pg[0], rel) : __builtin_amdgcn_readlane(cp.pg[1], rel - 64);
+  const int page = min(max(e, 0), a.n_pages - 1);
+  const size_t row0 = (size_t)page * a.page_size + (size_t)(t0 - (t0 / a.page_size) * a.page_size);
+  const char* p = static_cast<const char*>(base) + row0 * width * 2;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, rows > 0 ? rows * width * 2 : 0,
+                                           0x00020000);
+}
+
 // Copies the 16-row slice at t0 (rows past lim read as zeros) into (cdst, rdst).
-template <int R, int DR>
+template <int R, int DR, bool PAGED>
 __device__ __forceinline__ void issue_slice(u16* cdst, u16* rdst, const MlaDecodeArgs& a, int b, int t0, int lim,
-                                            const Lanes<R, DR>& ln) {
+                                            const Lanes<R, DR>& ln, const ChunkPages& cp) {
   using C = Cfg<R, DR>;
-  const auto rc = rows_rsrc(a.c_kv, b, a.T_max, R, t0, lim);
-  const auto rr = rows_rsrc(a.k_rope, b, a.T_max, DR, t0, lim);
+  __amdgpu_buffer_rsrc_t rc, rr;
+  if constexpr (PAGED) {
+    rc = page_rsrc(a.c_kv, a, cp, R, t0, lim);
+    rr = page_rsrc(a.k_rope, a, cp, DR, t0, lim);
+  } else {
+    rc = rows_rsrc(a.c_kv, b, a.T_max, R, t0, lim);
+    rr = rows_rsrc(a.k_rope, b, a.T_max, DR, t0, lim);
+  }
 #pragma unroll
   for (int q = 0; q < C::kCInst; ++q)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (__attribute__((address_space(3))) void*)(cdst + 512 * q), 16,
@@ -468,7 +497,7 @@ __device__ __forceinline__ void apply_uv(const UvBatch<R>& u, const MlaDecodeArg
 }
 
 // ---------------------------------------------------------------------------
-template <int R, int DR>
+template <int R, int DR, bool PAGED>
 __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
   using C = Cfg<R, DR>;
   constexpr int RW = C::RW;
@@ -546,11 +575,22 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
   // weight reads have (a bare barrier, no wait for the loads): issued after a
   // burst of cache copies, the weight reads waited behind the whole device's
   // burst in the memory queues.
+  // paged: the chunk's page numbers (a chunk spans at most 128 pages), read by
+  // the streaming waves before their first copies
+  ChunkPages cpg = {0, {0, 0}};
+  if (PAGED && streamer) {
+    cpg.p0 = c0 / a.page_size;
+    const int np = (c1 - 1) / a.page_size - cpg.p0 + 1;
+    const int32_t* tb = a.block_table + (size_t)b * a.table_stride + cpg.p0;
+    cpg.pg[0] = lane < np ? tb[lane] : 0;
+    cpg.pg[1] = lane + 64 < np ? tb[lane + 64] : 0;
+  }
   if (streamer) {
     const Lanes<R, DR> ln(lane);
     __builtin_amdgcn_s_barrier();  // (0)
 #pragma unroll
-    for (int i = 0; i < S - 1; ++i) issue_slice<R, DR>(stage_c(i), stage_r(i), a, b, tw0 + i * kStep, c1, ln);
+    for (int i = 0; i < S - 1; ++i)
+      issue_slice<R, DR, PAGED>(stage_c(i), stage_r(i), a, b, tw0 + i * kStep, c1, ln, cpg);
   } else {
     constexpr int P = 64 / (R / 8);
     constexpr int kRound = P * kAbsorbRows;  // W_UK rows per round
@@ -631,8 +671,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < S; ++i) {
         const int kk = k + i;
-        issue_slice<R, DR>(stage_c((i + S - 1) % S), stage_r((i + S - 1) % S), a, b, tw0 + (kk + S - 1) * kStep, c1,
-                           ln);
+        issue_slice<R, DR, PAGED>(stage_c((i + S - 1) % S), stage_r((i + S - 1) % S), a, b,
+                                  tw0 + (kk + S - 1) * kStep, c1, ln, cpg);
         if (kk < n_steps) {
           wait_vmcnt<(S - 1) * C::kInstPerSlice>();
           slice_step<R, DR>(st, stage_c(i), stage_r(i), qhi, qlo, qr32, qr16, tw0 + kk * kStep, c1, c, ln);
@@ -805,7 +845,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
 
 template <int R, int DR>
 hipError_t launch_rd(const MlaDecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((mla_decode<R, DR>), dim3(a.n_splits, a.B), dim3(kThreads), 0, st, a);
+  if (a.block_table) hipLaunchKernelGGL((mla_decode<R, DR, true>), dim3(a.n_splits, a.B), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((mla_decode<R, DR, false>), dim3(a.n_splits, a.B), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -830,6 +871,9 @@ bool mla_decode_supported(int H, int r, int dR) {
 hipError_t launch_mla_decode(const MlaDecodeArgs& a, hipStream_t st) {
   if (!mla_decode_supported(a.H, a.r, a.dR)) return hipErrorInvalidValue;
   if (a.split % kStep != 0 || a.dv % 16 != 0 || a.dv > 256 || a.dn > 256 || !a.done) return hipErrorInvalidValue;
+  if (a.block_table && (a.page_size <= 0 || a.page_size % kSlice != 0 || a.n_pages <= 0 || a.append ||
+                        a.split / a.page_size + 2 > 128))
+    return hipErrorInvalidValue;
   return a.r == 64 ? launch_r<64>(a, st) : a.r == 128 ? launch_r<128>(a, st) : launch_r<256>(a, st);
 }
 

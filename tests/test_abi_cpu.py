@@ -333,6 +333,24 @@ def test_paged_decode_validation():
 
 
 @no_gpu_only
+def test_mla_paged_decode_validation():
+    lib = attn.lib()
+
+    def f(tb=FAKE, **kw):
+        return lib.attn_decode_mla_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, tb, FAKE, FAKE, 2, 8, 96, 48, 96, 128,
+                                         kw.get("ps", 16), kw.get("np", 100), kw.get("mp", 64), 0.0, BF16, F32,
+                                         kw.get("split", 0), FAKE, 1 << 30, None)
+    assert f(tb=None) == NULL
+    assert f(ps=0) == SHAPE
+    assert f(np=0) == SHAPE
+    assert f(mp=0) == SHAPE
+    assert f(ps=24) == UNSUP
+    assert f(split=4096) == UNSUP  # 4096 / 16 + 2 pages per chunk, more than 128
+    assert f(split=2048) == UNSUP  # 130
+    assert f(ps=32, split=4096) == UNSUP
+
+
+@no_gpu_only
 def test_int4_decode_validation():
     lib = attn.lib()
 
