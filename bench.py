@@ -273,6 +273,15 @@ def main():
         chk_flops += 4 * CHq * CD * (n * P + n * (n + 1) // 2)   # new token i sees P + i + 1 keys
     chk_tokens = int(chk_cpu["q_lens"].sum())
     chk_out = torch.empty_like(chk["q"])
+    # the same chunk over a paged view of the caches: 64-position pages, every sequence's pages
+    # scattered over the pool by a seeded permutation
+    cpg_size = 64
+    cpg_max = CT // cpg_size
+    cpg_table = torch.randperm(CB * cpg_max, generator=torch.Generator().manual_seed(13)).to(torch.int32)
+    cpg_table = cpg_table.view(CB, cpg_max).to(dev)
+    cpg_k = chk["k"].view(CB * cpg_max, cpg_size, chk["k"].shape[2], CD)
+    cpg_v = chk["v"].view(CB * cpg_max, cpg_size, chk["v"].shape[2], CD)
+    cpg_out = torch.empty_like(chk["q"])
     # the same chunk through the one-launch append + prefill: the new rows are the cache rows at
     # start_pos.., written back unchanged every step
     chk_sp = chk_cpu["start_pos"].clamp(0, CT)
@@ -351,6 +360,9 @@ def main():
     def run_chunked(i):
         attn.attn_prefill_gqa_cached(chk["q"], chk["k"], chk["v"], chk["start_pos"], chk["q_lens"], out=chk_out)
 
+    def run_chunked_paged(i):
+        attn.attn_prefill_gqa_paged(chk["q"], cpg_k, cpg_v, cpg_table, chk["start_pos"], chk["q_lens"], out=cpg_out)
+
     def run_chunked_append(i):
         attn.attn_prefill_gqa_cached_append(chk["q"], chk_k_new, chk_v_new, chk["k"], chk["v"], chk["start_pos"],
                                             chk["q_lens"], out=chk_app_out)
@@ -381,6 +393,7 @@ def main():
     # prefill for new requests, then the decode steps of running ones (the order a serving
     # step takes), then the sweep settings; each part is timed on its own
     parts = [("prefill", run_prefill), ("chunked_prefill", run_chunked), ("chunked_prefill_append", run_chunked_append),
+             ("chunked_prefill_paged", run_chunked_paged),
              ("mla_prefill", run_mla_prefill), ("mla_decode", run_mla), ("mla_decode_step", run_mla_step),
              ("mla_decode_paged", run_mla_paged),
              ("kv_append", run_append), ("rope_append_decode", run_rope_decode), ("rope_append_chunk", run_rope_chunk),
@@ -450,6 +463,7 @@ def main():
                     "part's K calls back to back between one event pair, in this order",
             "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "mla_decode_step": MB, "mla_decode_paged": MB, "prefill": PB * S,
                                 "chunked_prefill": chk_tokens, "chunked_prefill_append": chk_tokens,
+                                "chunked_prefill_paged": chk_tokens,
                                 "mla_prefill": MPB * MPS},
         },
         "roofline": {
@@ -512,6 +526,10 @@ def main():
         prefill_part("chunked_prefill_append", chk_flops, chk_tokens,
                      "llama3_8b_gqa_chunked_prefill through attn_prefill_gqa_cached_append: the chunk's K/V rows "
                      "come in their own arrays and are written into the caches by the same launch")
+    if "chunked_prefill_paged" in ms:
+        prefill_part("chunked_prefill_paged", chk_flops, chk_tokens,
+                     f"llama3_8b_gqa_chunked_prefill over a paged cache: {cpg_size}-position pages, each sequence's "
+                     "pages scattered over the pool by a seeded permutation (attn_prefill_gqa_paged)")
     if "mla_decode_step" in ms:
         decode_part("mla_decode_step", mla_bytes, MB, mla_flops,
                     "minimind768_mla_decode with the newest rows as the new token (attn_decode_mla_append: "

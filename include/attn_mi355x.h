@@ -333,6 +333,36 @@ attn_status attn_prefill_gqa_cached(const void* q, const void* k_cache, const vo
                                     attn_dtype in_dtype, attn_dtype out_dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Causal GQA prefill after a cached prefix, over a paged cache.
+ *
+ *   T_max = page_size * max_pages_per_seq;
+ *   K[b,t,g,:] = k_pages[block_table[b * max_pages_per_seq + t / page_size], t % page_size, g, :]
+ *   (V likewise from v_pages), and out is attn_prefill_gqa_cached over those rows.
+ *
+ * The chunked prefill of the "模型架构｜MQA & GQA 调研" page (Attention.forward
+ * with start_pos > 0, the new rows already written into the cache) when the cache
+ * is kept in the block-table layout that attn_decode_gqa_paged reads (the "MHA,
+ * MQA và GQA" e-book names paging only as a serving cost, with no scheme).  Same
+ * arithmetic and results as attn_prefill_gqa_cached on the gathered caches.
+ *
+ *   q            [B, S, Hq, head_dim]                     bf16 (the new tokens, padded to S)
+ *   k_pages, v_pages [n_pages, page_size, Hkv, head_dim]   bf16 (16-byte aligned)
+ *   block_table  [B, max_pages_per_seq] int32, device memory: entries for the
+ *                pages below ceil((P + n) / page_size) are read, each clamped to
+ *                [0, n_pages); unused entries may hold anything
+ *   start_pos, q_lens, out: as attn_prefill_gqa_cached (clamped against T_max)
+ *
+ * Supported: as attn_prefill_gqa_cached, with page_size a multiple of 64 (one
+ * 64-key tile per page; else ATTN_ERR_UNSUPPORTED).  Errors as
+ * attn_prefill_gqa_cached, plus ATTN_ERR_NULL for a NULL block_table and
+ * ATTN_ERR_SHAPE for non-positive page counts.  No workspace.
+ */
+attn_status attn_prefill_gqa_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                                   const int32_t* start_pos, const int32_t* q_lens, void* out, int B, int S, int Hq,
+                                   int Hkv, int head_dim, int page_size, int n_pages, int max_pages_per_seq,
+                                   float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Causal GQA prefill after a cached prefix that also appends the new rows.
  *
  *   P = start_pos[b], n = q_lens[b] (NULL: S), both clamped as for

@@ -74,6 +74,8 @@ def _declare(lib):
     lib.attn_prefill_mla_causal.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, P]
     lib.attn_prefill_gqa_cached.restype = I
     lib.attn_prefill_gqa_cached.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
+    lib.attn_prefill_gqa_paged.restype = I
+    lib.attn_prefill_gqa_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, P]
     lib.attn_prefill_gqa_cached_append.restype = I
     lib.attn_prefill_gqa_cached_append.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
     lib.attn_decode_mla_workspace_bytes.restype = Z
@@ -399,6 +401,37 @@ def attn_prefill_gqa_cached(q, k_cache, v_cache, start_pos, q_lens=None, out=Non
     return out
 
 
+def attn_prefill_gqa_paged(q, k_pages, v_pages, block_table, start_pos, q_lens=None, out=None,
+                           softmax_scale: float = 0.0, out_dtype=torch.bfloat16):
+    """attn_prefill_gqa_cached over a paged cache: position t of sequence b is row t % page_size
+    of page block_table[b, t // page_size] of the pools (which already hold the new rows).
+
+    q [B,S,Hq,D] bf16, k_pages/v_pages [n_pages, page_size, Hkv, D] bf16, block_table
+    [B, max_pages_per_seq] int32, start_pos, q_lens [B] int32 (q_lens None: S).  Returns out."""
+    _check(q, "q")
+    B, S, Hq, D = q.shape
+    _check(k_pages, "k_pages", dtype=q.dtype)
+    if k_pages.dim() != 4 or k_pages.shape[3] != D:
+        raise ValueError(f"k_pages must be [n_pages, page_size, Hkv, {D}] (got {tuple(k_pages.shape)})")
+    n_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    _check(v_pages, "v_pages", shape=k_pages.shape, dtype=q.dtype)
+    _check(block_table, "block_table", dtype=torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B={B}, max_pages_per_seq] (got {tuple(block_table.shape)})")
+    max_pages = block_table.shape[1]
+    _check(start_pos, "start_pos", shape=(B,), dtype=torch.int32)
+    if q_lens is not None:
+        _check(q_lens, "q_lens", shape=(B,), dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, S, Hq, D), dtype=out_dtype, device=q.device)
+    _check(out, "out", shape=(B, S, Hq, D))
+    st = lib().attn_prefill_gqa_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(start_pos),
+                                      _ptr(q_lens), _ptr(out), B, S, Hq, Hkv, D, page_size, n_pages, max_pages,
+                                      float(softmax_scale), _dt(q), _dt(out), _stream(q.device))
+    _raise_if(st, "attn_prefill_gqa_paged")
+    return out
+
+
 def attn_prefill_gqa_cached_append(q, k_new, v_new, k_cache, v_cache, start_pos, q_lens=None, out=None,
                                    softmax_scale: float = 0.0, out_dtype=torch.bfloat16):
     """Causal prefill after a cached prefix that also appends the new rows, in one launch: new token
@@ -686,7 +719,7 @@ def attn_decode_mla_append(q_nope, q_rope, c_new, k_rope_new, w_uk, w_uv, c_kv, 
     return out
 
 
-__all__ = ["attn_decode_gqa", "attn_decode_gqa_paged", "attn_decode_mla_paged", "attn_decode_gqa_int4kv", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_noalloc", "NOALLOC_SCRATCH_BYTES", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
+__all__ = ["attn_decode_gqa", "attn_decode_gqa_paged", "attn_decode_mla_paged", "attn_prefill_gqa_paged", "attn_decode_gqa_int4kv", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_noalloc", "NOALLOC_SCRATCH_BYTES", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
            "attn_decode_gqa_append_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached", "attn_prefill_gqa_cached_append",
            "attn_prefill_mla_causal", "attn_cache_append", "attn_rope_append",
            "attn_decode_mla_absorbed", "attn_decode_mla_append", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",

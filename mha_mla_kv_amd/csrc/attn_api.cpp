@@ -399,7 +399,8 @@ attn_status prefill_common(const char* fn, const void* q, const void* k, const v
                            const int32_t* start_pos, const int32_t* q_lens, void* out, int B, int S, int Hq,
                            int Hkv, int head_dim, int T_kv, float softmax_scale, attn_dtype in_dtype,
                            attn_dtype out_dtype, void* stream, const void* k_new = nullptr,
-                           const void* v_new = nullptr) {
+                           const void* v_new = nullptr, const int32_t* block_table = nullptr, int page_size = 0,
+                           int n_pages = 0, int table_stride = 0) {
   if (!q || !k || !v || !out)
     return fail(ATTN_ERR_NULL, "%s: q, k, v and out must be non-NULL", fn);
   if ((k_new != nullptr) != (v_new != nullptr))
@@ -424,6 +425,10 @@ attn_status prefill_common(const char* fn, const void* q, const void* k, const v
   attn::PrefillArgs a;
   a.k_new = k_new;
   a.v_new = v_new;
+  a.block_table = block_table;
+  a.page_size = page_size;
+  a.n_pages = n_pages;
+  a.table_stride = table_stride;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -460,6 +465,25 @@ attn_status attn_prefill_gqa_cached(const void* q, const void* k_cache, const vo
     return fail(ATTN_ERR_NULL, "attn_prefill_gqa_cached: start_pos must be non-NULL");
   return prefill_common("attn_prefill_gqa_cached", q, k_cache, v_cache, start_pos, q_lens, out, B, S, Hq, Hkv,
                         head_dim, T_max, softmax_scale, in_dtype, out_dtype, stream);
+}
+
+attn_status attn_prefill_gqa_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                                   const int32_t* start_pos, const int32_t* q_lens, void* out, int B, int S, int Hq,
+                                   int Hkv, int head_dim, int page_size, int n_pages, int max_pages_per_seq,
+                                   float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype, void* stream) {
+  static const char* fn = "attn_prefill_gqa_paged";
+  if (!start_pos) return fail(ATTN_ERR_NULL, "%s: start_pos must be non-NULL", fn);
+  if (!block_table) return fail(ATTN_ERR_NULL, "%s: block_table must be non-NULL", fn);
+  if (page_size <= 0 || n_pages <= 0 || max_pages_per_seq <= 0)
+    return fail(ATTN_ERR_SHAPE, "%s: page_size, n_pages and max_pages_per_seq must be positive (%d, %d, %d)", fn,
+                page_size, n_pages, max_pages_per_seq);
+  if ((long long)page_size * max_pages_per_seq > 0x7fffffffLL)
+    return fail(ATTN_ERR_SHAPE, "%s: page_size * max_pages_per_seq too large", fn);
+  if (page_size % 64 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: page_size=%d must be a multiple of 64", fn, page_size);
+  return prefill_common(fn, q, k_pages, v_pages, start_pos, q_lens, out, B, S, Hq, Hkv, head_dim,
+                        page_size * max_pages_per_seq, softmax_scale, in_dtype, out_dtype, stream, nullptr, nullptr,
+                        block_table, page_size, n_pages, max_pages_per_seq);
 }
 
 attn_status attn_prefill_gqa_cached_append(const void* q, const void* k_new, const void* v_new, void* k_cache,

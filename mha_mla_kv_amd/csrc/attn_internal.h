@@ -79,6 +79,14 @@ struct PrefillArgs {
   // positions P.. are read from them, and they are written into k and v at P..
   const void* k_new = nullptr;  // [B, S, Hkv, D] bf16
   const void* v_new = nullptr;  // [B, S, Hkv, D] bf16
+  // paged cache (block_table != null, start_pos required, no k_new): k and v are
+  // pools [n_pages, page_size, Hkv, D]; position t of sequence b is row
+  // t % page_size of page block_table[b * table_stride + t / page_size]
+  // (clamped to [0, n_pages)); page_size a multiple of 64; T_kv = page_size * table_stride
+  const int32_t* block_table = nullptr;
+  int page_size = 0;
+  int table_stride = 0;
+  int n_pages = 0;
 };
 
 struct MlaPrefillArgs {

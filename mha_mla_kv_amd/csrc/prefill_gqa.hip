@@ -313,16 +313,36 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, f32x16 (&sc)[2], b
 // Where the keys of a sequence come from.  Tiles 0 .. n1-1 hold positions
 // 0 .. P-1 from the cache (k, v); tiles n1 .. n_kt-1 hold positions P .. from
 // the new rows (kn, vn), one 64-key tile after another.  Without separate new
-// rows n1 = n_kt and every tile comes from the cache.
-template <int D, int DL>
+// rows n1 = n_kt and every tile comes from the cache.  PAGED: the cache is a
+// pool of pages (k and v point at the KV head's columns of the pool's first
+// row), and tile kt, which lies in one page (page_size a multiple of 64), starts
+// at row page * page_size + (64 kt mod page_size) of the pool, its page number
+// read from the sequence's block-table row trow (a scalar load per tile).
+template <int D, int DL, bool PAGED = false>
 struct KeySource {
   const u16 *k, *v, *kn, *vn;
   int row_bytes;
   int P, n1, n_kt;
   int len1, len2;  // keys in the first and in the second source
+  const int32_t* trow = nullptr;
+  int page_size = 0, n_pages = 0;
 
   __device__ __forceinline__ int kv0(int kt) const { return kt < n1 ? kt * kBN : P + (kt - n1) * kBN; }
   __device__ __forceinline__ void issue(const TileCopy<DL>& cp, u16* kl, u16* vl, int kt) const {
+    if constexpr (PAGED) {
+      const bool ok = kt >= 0 && kt < n_kt;
+      const int key0 = ok ? kt * kBN : 0;
+      const int e = ok ? __builtin_amdgcn_readfirstlane(trow[key0 / page_size]) : 0;
+      const int page = min(max(e, 0), n_pages - 1);
+      const size_t row0 = (size_t)page * page_size + (size_t)(key0 - (key0 / page_size) * page_size);
+      const int rows = min(len1 - key0, kBN);
+      const int num = ok && rows > 0 ? (rows - 1) * row_bytes + 2 * D : 0;
+      const char* kb = reinterpret_cast<const char*>(k) + row0 * row_bytes;
+      const char* vb = reinterpret_cast<const char*>(v) + row0 * row_bytes;
+      cp.issue(kl, __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kb), (short)0, num, 0x00020000));
+      cp.issue(vl, __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vb), (short)0, num, 0x00020000));
+      return;
+    }
     if (kt < n1) {
       cp.issue(kl, TileCopy<DL>::rsrc(k, kt, n1, len1, row_bytes, 2 * D));
       cp.issue(vl, TileCopy<DL>::rsrc(v, kt, n1, len1, row_bytes, 2 * D));
@@ -341,10 +361,10 @@ struct KeySource {
 // (kt < n1) when the new rows come separately are cut at the last cached
 // position P - 1 (their tail reads as zeros); the others at each row's own
 // position.
-template <int D, int DL>
+template <int D, int DL, bool PAGED>
 __device__ __forceinline__ void tile_step(RowState<D>& st, const u16* kc, const u16* vc, u16* kn, u16* vn,
                                           const bf16x8 (&qop)[D / 16], int kt, int last_kt,
-                                          const KeySource<D, DL>& src, const TileCopy<DL>& cp,
+                                          const KeySource<D, DL, PAGED>& src, const TileCopy<DL>& cp,
                                           const LdsOffsets& off, const Lane& w) {
   if (kt + 1 < src.n_kt) src.issue(cp, kn, vn, kt + 1);  // (kn, vn) were released by the last barrier
   if (kt <= last_kt) {
@@ -393,8 +413,10 @@ __device__ __forceinline__ void store_rows(void* out, size_t orow, int out_bf16,
 // MODE 0: no prefix (start_pos null); 1: a cached prefix, the new rows already
 // in the cache; 2: a cached prefix, the new rows in their own arrays (k_new,
 // v_new), read from there and written into the cache at P.. by the workgroups
-// of the first head of each KV group.  Modes 0 and 1 run the same code; the
-// separate symbols keep them apart in kernel profiles.
+// of the first head of each KV group; 3: mode 1 over a paged cache (k and v are
+// page pools, block_table maps each sequence's positions to pages).  Modes 0
+// and 1 run the same code; the separate symbols keep them apart in kernel
+// profiles.
 template <int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_causal(PrefillArgs a) {
   static_assert(D % 32 == 0 && D <= 128, "head_dim");
@@ -441,15 +463,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     return;
   }
   const u16* qp = static_cast<const u16*>(a.q) + ((size_t)b * a.S * a.Hq + h) * D;
-  const u16* kp = static_cast<const u16*>(a.k) + ((size_t)b * a.T_kv * a.Hkv + g) * D;
-  const u16* vp = static_cast<const u16*>(a.v) + ((size_t)b * a.T_kv * a.Hkv + g) * D;
+  // (paged: the KV head's columns of the pool's first row; the tiles add their page's rows)
+  const u16* kp = static_cast<const u16*>(a.k) + ((MODE == 3 ? 0 : (size_t)b * a.T_kv * a.Hkv) + g) * D;
+  const u16* vp = static_cast<const u16*>(a.v) + ((MODE == 3 ? 0 : (size_t)b * a.T_kv * a.Hkv) + g) * D;
 
   // keys of the sequence: [0, kv_len); keys needed by the workgroup:
   // [0, min(kv_len, P + q0 + BM)); tiles 0..last_kt are visible to some row of
   // this wave
   const int kv_len = P + n_q;
   const int kv_end = min(kv_len, P + q0 + kBM);
-  KeySource<D, DL> src;
+  KeySource<D, DL, MODE == 3> src;
+  if constexpr (MODE == 3) {
+    src.trow = a.block_table + (size_t)b * a.table_stride;
+    src.page_size = a.page_size;
+    src.n_pages = a.n_pages;
+  }
   src.k = kp;
   src.v = vp;
   src.row_bytes = row_bytes;
@@ -495,8 +523,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   wait_vmem();
   __syncthreads();
   for (int kt = 0; kt < n_kt; kt += 2) {
-    tile_step<D, DL>(st, k0, v0, k1, v1, qop, kt, last_kt, src, cp, off, w);
-    if (kt + 1 < n_kt) tile_step<D, DL>(st, k1, v1, k0, v0, qop, kt + 1, last_kt, src, cp, off, w);
+    tile_step<D, DL, MODE == 3>(st, k0, v0, k1, v1, qop, kt, last_kt, src, cp, off, w);
+    if (kt + 1 < n_kt) tile_step<D, DL, MODE == 3>(st, k1, v1, k0, v0, qop, kt + 1, last_kt, src, cp, off, w);
   }
 
   // normalise and store; rows past the new tokens are zeros
@@ -791,6 +819,9 @@ template __global__ void prefill_causal<64, 1>(PrefillArgs);
 template __global__ void prefill_causal<128, 2>(PrefillArgs);
 template __global__ void prefill_causal<96, 2>(PrefillArgs);
 template __global__ void prefill_causal<64, 2>(PrefillArgs);
+template __global__ void prefill_causal<128, 3>(PrefillArgs);
+template __global__ void prefill_causal<96, 3>(PrefillArgs);
+template __global__ void prefill_causal<64, 3>(PrefillArgs);
 template __global__ void prefill_mla<96, 48, 96>(MlaPrefillArgs);
 
 }  // namespace
@@ -802,11 +833,13 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const long long wgs = (long long)((a.S + kBM - 1) / kBM) * a.Hq * a.B;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)wgs);
-  const int mode = a.k_new ? 2 : a.start_pos ? 1 : 0;
-  if (mode == 2 && !a.start_pos) return hipErrorInvalidValue;
+  const int mode = a.block_table ? 3 : a.k_new ? 2 : a.start_pos ? 1 : 0;
+  if ((mode == 2 || mode == 3) && !a.start_pos) return hipErrorInvalidValue;
+  if (mode == 3 && (a.k_new || a.page_size <= 0 || a.page_size % kBN != 0 || a.n_pages <= 0)) return hipErrorInvalidValue;
 #define ATTN_PREFILL_LAUNCH(DD)                                                                                  \
   do {                                                                                                             \
-    if (mode == 2) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<DD, 2>), grid, dim3(256), 0, st, a);         \
+    if (mode == 3) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<DD, 3>), grid, dim3(256), 0, st, a);         \
+    else if (mode == 2) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<DD, 2>), grid, dim3(256), 0, st, a);    \
     else if (mode == 1) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<DD, 1>), grid, dim3(256), 0, st, a);    \
     else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_causal<DD, 0>), grid, dim3(256), 0, st, a);                   \
   } while (0)

@@ -351,6 +351,23 @@ def test_mla_paged_decode_validation():
 
 
 @no_gpu_only
+def test_paged_prefill_validation():
+    lib = attn.lib()
+
+    def f(tb=FAKE, sp=FAKE, **kw):
+        return lib.attn_prefill_gqa_paged(FAKE, FAKE, FAKE, tb, sp, None, FAKE, 2, 64, 8, 2, kw.get("D", 128),
+                                          kw.get("ps", 64), kw.get("np", 10), kw.get("mp", 8), 0.0, BF16, BF16, None)
+    assert f(tb=None) == NULL
+    assert f(sp=None) == NULL
+    assert f(ps=0) == SHAPE
+    assert f(np=0) == SHAPE
+    assert f(mp=0) == SHAPE
+    assert f(ps=32) == UNSUP
+    assert f(ps=96) == UNSUP
+    assert f(D=80) == UNSUP
+
+
+@no_gpu_only
 def test_int4_decode_validation():
     lib = attn.lib()
 
