@@ -252,6 +252,12 @@ def main():
     mpg_table = torch.randperm(MB * mpg_max, generator=torch.Generator().manual_seed(12)).to(torch.int32)
     mpg_table = mpg_table.view(MB, mpg_max).to(dev)
     mpg_out = torch.empty(MB, H, dv, dtype=torch.float32, device=dev)
+    # FP8 E4M3 latent: each copy's c_kv as codes with one scale (N(0,1) data, scale 4.5 / 448),
+    # k_rope bf16
+    mf8_scale = 4.5 / 448.0
+    mf8_copies = [((c.float() / mf8_scale).to(torch.float8_e4m3fn), kr) for c, kr in mla_copies]
+    mf8_bytes = (r + 2 * dR) * mla_len                          # one fp8 latent + bf16 rope row per position
+    mf8_out = torch.empty(MB, H, dv, dtype=torch.float32, device=dev)
     mla_step_ws = torch.zeros(attn.attn_decode_mla_workspace_bytes(MB, H, r, dR, MT, 0), dtype=torch.uint8,
                               device=dev)
 
@@ -332,6 +338,11 @@ def main():
                                    c.view(MB * mpg_max, mpg_size, r), kr.view(MB * mpg_max, mpg_size, dR), mpg_table,
                                    mla["cache_lens"], out=mpg_out, workspace=mla_ws)
 
+    def run_mla_fp8(i):
+        c8, kr = mf8_copies[i % len(mf8_copies)]
+        attn.attn_decode_mla_fp8kv(mla["q_nope"], mla["q_rope"], mla["w_uk"], mla["w_uv"], c8, mf8_scale, kr,
+                                   mla["cache_lens"], out=mf8_out, workspace=mla_ws)
+
     def run_prefill(i):
         attn.attn_prefill_gqa_causal(pre["q"], pre["k"], pre["v"], out=pre_out)
 
@@ -395,7 +406,7 @@ def main():
     parts = [("prefill", run_prefill), ("chunked_prefill", run_chunked), ("chunked_prefill_append", run_chunked_append),
              ("chunked_prefill_paged", run_chunked_paged),
              ("mla_prefill", run_mla_prefill), ("mla_decode", run_mla), ("mla_decode_step", run_mla_step),
-             ("mla_decode_paged", run_mla_paged),
+             ("mla_decode_paged", run_mla_paged), ("mla_decode_fp8", run_mla_fp8),
              ("kv_append", run_append), ("rope_append_decode", run_rope_decode), ("rope_append_chunk", run_rope_chunk),
              ("gqa_decode", run_decode), ("gqa_decode_paged", run_paged), ("gqa_decode_step", run_step),
              ("gqa_decode_fp8", run_fp8), ("gqa_decode_int4", run_int4)]
@@ -461,7 +472,7 @@ def main():
                          "bf16 in, fp32 out, default schedule (device-wide unit queue, library-chosen blocks)"),
             "step": ", ".join(name for name, _ in parts) + ": one call each; timed part by part, each "
                     "part's K calls back to back between one event pair, in this order",
-            "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "mla_decode_step": MB, "mla_decode_paged": MB, "prefill": PB * S,
+            "tokens_per_step": {"gqa_decode": B, "mla_decode": MB, "mla_decode_step": MB, "mla_decode_paged": MB, "mla_decode_fp8": MB, "prefill": PB * S,
                                 "chunked_prefill": chk_tokens, "chunked_prefill_append": chk_tokens,
                                 "chunked_prefill_paged": chk_tokens,
                                 "mla_prefill": MPB * MPS},
@@ -538,6 +549,10 @@ def main():
         decode_part("mla_decode_paged", mla_bytes, MB, mla_flops,
                     f"minimind768_mla_decode shape and lengths over paged latent caches: {mpg_size}-position pages, "
                     "each sequence's pages scattered over the pool by a seeded permutation (attn_decode_mla_paged)")
+    if "mla_decode_fp8" in ms:
+        decode_part("mla_decode_fp8", mf8_bytes, MB, mla_flops,
+                    "minimind768_mla_decode shape and lengths with the latent c_kv as FP8 E4M3 codes (one scale, "
+                    "N(0,1)/scale drawn on the device; k_rope bf16): 224 bytes per position (attn_decode_mla_fp8kv)")
     if "mla_prefill" in ms:
         prefill_part("mla_prefill", mlp_flops, MPB * MPS,
                      f"minimind768_mla_prefill: B={MPB} S={MPS} H={MPH} nope={MPdn} rope={MPdR} v={MPdv} "

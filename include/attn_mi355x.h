@@ -466,6 +466,35 @@ attn_status attn_decode_mla_absorbed(const void* q_nope, const void* q_rope, con
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* MLA decode over an FP8 latent cache.
+ *
+ *   c_kv_value[b,t,:] = c_scale * e4m3(c_kv[b,t,:]),
+ *   out is attn_decode_mla_absorbed over (c_kv_value, k_rope).
+ *
+ * The MLA decode of the qqstock DeepSeek MLA article (sections 1 and 3: only
+ * the latent c_kv and the shared rotated key part are cached) with the latent,
+ * 128 of the 176 cached numbers per token at MiniMind-768's widths, stored as
+ * OCP FP8 E4M3 codes with one fp32 scale per cache -- the fp8 number type of the
+ * "MHA, MQA và GQA" e-book's simulator, read as in attn_decode_gqa_fp8kv.
+ * k_rope stays bf16.  Encoding the cache is the caller's.  The codes are widened
+ * to bf16 exactly; c_scale multiplies the latent part of the absorbed query and
+ * the output, so the scores and the weighted sum see c_scale * code.
+ *
+ *   c_kv [B, T_max, kv_lora_rank] one byte each (16-byte aligned);
+ *   c_scale > 0 and finite (else ATTN_ERR_SHAPE);  k_rope [B, T_max, rope_dim]
+ *   bf16;  q_nope, q_rope, w_uk, w_uv bf16;  cache_lens, out, split_tokens,
+ *   workspace (attn_decode_mla_workspace_bytes): as attn_decode_mla_absorbed
+ *
+ * Supported shapes and errors as attn_decode_mla_absorbed with in_dtype
+ * ATTN_BF16.  Rows at or past cache_lens[b] are not read.
+ */
+attn_status attn_decode_mla_fp8kv(const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv,
+                                  const void* c_kv, float c_scale, const void* k_rope, const int32_t* cache_lens,
+                                  void* out, int B, int H, int nope_head_dim, int rope_dim, int v_head_dim,
+                                  int kv_lora_rank, int T_max, float softmax_scale, attn_dtype out_dtype,
+                                  int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* MLA decode over paged latent caches.
  *
  *   T_max = page_size * max_pages_per_seq, L = cache_lens[b] clamped to [0, T_max];

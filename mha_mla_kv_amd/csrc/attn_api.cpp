@@ -646,7 +646,7 @@ attn_status mla_decode_common(const char* fn, const void* q_nope, const void* q_
                               float softmax_scale, attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens,
                               void* workspace, size_t workspace_bytes, void* stream,
                               const int32_t* block_table = nullptr, int page_size = 0, int n_pages = 0,
-                              int table_stride = 0) {
+                              int table_stride = 0, bool c_fp8 = false, float c_scale = 1.f) {
   const bool append = c_new != nullptr;
   if (!q_nope || !q_rope || !w_uk || !w_uv || !c_kv || !k_rope || !cache_lens || !out)
     return fail(ATTN_ERR_NULL, "%s: all tensor pointers must be non-NULL", fn);
@@ -714,6 +714,8 @@ attn_status mla_decode_common(const char* fn, const void* q_nope, const void* q_
   a.page_size = page_size;
   a.n_pages = n_pages;
   a.table_stride = table_stride;
+  a.c_fp8 = c_fp8;
+  a.c_scale = c_scale;
   return hip_status(attn::launch_mla_decode(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -750,6 +752,20 @@ attn_status attn_decode_mla_paged(const void* q_nope, const void* q_rope, const 
                            H, nope_head_dim, rope_dim, v_head_dim, kv_lora_rank, page_size * max_pages_per_seq,
                            softmax_scale, in_dtype, out_dtype, split_tokens, workspace, workspace_bytes, stream,
                            block_table, page_size, n_pages, max_pages_per_seq);
+}
+
+attn_status attn_decode_mla_fp8kv(const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv,
+                                  const void* c_kv, float c_scale, const void* k_rope, const int32_t* cache_lens,
+                                  void* out, int B, int H, int nope_head_dim, int rope_dim, int v_head_dim,
+                                  int kv_lora_rank, int T_max, float softmax_scale, attn_dtype out_dtype,
+                                  int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "attn_decode_mla_fp8kv";
+  if (!(c_scale > 0.f) || !std::isfinite(c_scale))
+    return fail(ATTN_ERR_SHAPE, "%s: c_scale must be positive and finite (got %g)", fn, (double)c_scale);
+  return mla_decode_common(fn, q_nope, q_rope, nullptr, nullptr, w_uk, w_uv, c_kv, k_rope, cache_lens, out, B, H,
+                           nope_head_dim, rope_dim, v_head_dim, kv_lora_rank, T_max, softmax_scale, ATTN_BF16,
+                           out_dtype, split_tokens, workspace, workspace_bytes, stream, nullptr, 0, 0, 0, true,
+                           c_scale);
 }
 
 attn_status attn_decode_mla_append(const void* q_nope, const void* q_rope, const void* c_new, const void* k_rope_new,

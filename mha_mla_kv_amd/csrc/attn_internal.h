@@ -150,6 +150,10 @@ struct MlaDecodeArgs {
   int page_size = 0;
   int table_stride = 0;
   int n_pages = 0;
+  // latent cache of OCP FP8 E4M3 codes (c_fp8 != 0; not paged, no append):
+  // c_kv holds [B, T_max, r] bytes, value = c_scale * code; k_rope stays bf16
+  int c_fp8 = 0;
+  float c_scale = 1.f;
 };
 
 struct RopeAppendArgs {

@@ -55,6 +55,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kHeadsPad = 16;
@@ -136,7 +137,7 @@ __device__ __forceinline__ int swz(int r) {
   else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
 }
 
-template <int R, int DR>
+template <int R, int DR, bool F8 = false>
 struct Cfg {
   static constexpr int RW = R + DR;
   static constexpr int KC = R / 32;           // 32-wide latent chunks of the score
@@ -144,7 +145,8 @@ struct Cfg {
   static constexpr bool R16 = (DR % 32) != 0; // one trailing 16-wide rope chunk
   static constexpr int DW = R / 16;           // 16-wide latent blocks of O^T
   static constexpr int kC = kSlice * R;       // latent slice (u16)
-  static constexpr int kCInst = kC * 2 / 1024;  // copy instructions per latent slice
+  // copy instructions per latent slice (fp8 latent: R bytes per row, copied raw)
+  static constexpr int kCInst = F8 ? kSlice * R / 1024 : kC * 2 / 1024;
   static constexpr int kRInst = (kSlice * DR * 2 + 1023) / 1024;
   static constexpr int kR = kRInst * 512;     // rope slice (u16), padded to whole copies
   static constexpr int kInstPerSlice = kCInst + kRInst;
@@ -159,18 +161,24 @@ struct Cfg {
 };
 
 // Per-lane constants of the slice copies and reads.
-template <int R, int DR>
+template <int R, int DR, bool F8 = false>
 struct Lanes {
   int lane, row, grp;
-  int c_voff[Cfg<R, DR>::kCInst];  // byte offset in the global latent slice of this lane's copy
+  int c_voff[Cfg<R, DR, F8>::kCInst];  // byte offset in the global latent slice of this lane's copy
   int k_off;                       // QK operand read: element offset, XOR 32c per chunk
   int v_off;                       // transposed V read: element offset, XOR 16w per block
   __device__ __forceinline__ Lanes(int lane_) : lane(lane_), row(lane_ & 15), grp(lane_ >> 4) {
     constexpr int CPR = R / 8;  // chunks per row
 #pragma unroll
-    for (int q = 0; q < Cfg<R, DR>::kCInst; ++q) {
-      const int s = 64 * q + lane, r = s / CPR, p = s % CPR;
-      c_voff[q] = r * 2 * R + 16 * (p ^ swz<R>(r));
+    for (int q = 0; q < Cfg<R, DR, F8>::kCInst; ++q) {
+      const int s = 64 * q + lane;
+      if constexpr (F8) {
+        // raw fp8 rows, 16-byte slot s = row s / (R / 16), bytes 16 (s mod R / 16) of it
+        c_voff[q] = (s / (R / 16)) * R + 16 * (s % (R / 16));
+      } else {
+        const int r = s / CPR, p = s % CPR;
+        c_voff[q] = r * 2 * R + 16 * (p ^ swz<R>(r));
+      }
     }
     k_off = row * R + 8 * (grp ^ swz<R>(row));
     const int i = lane & 15, r = 4 * grp + (i >> 2);
@@ -213,12 +221,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, co
 }
 
 // Copies the 16-row slice at t0 (rows past lim read as zeros) into (cdst, rdst).
-template <int R, int DR, bool PAGED>
+template <int R, int DR, bool PAGED, bool F8 = false>
 __device__ __forceinline__ void issue_slice(u16* cdst, u16* rdst, const MlaDecodeArgs& a, int b, int t0, int lim,
-                                            const Lanes<R, DR>& ln, const ChunkPages& cp) {
-  using C = Cfg<R, DR>;
+                                            const Lanes<R, DR, F8>& ln, const ChunkPages& cp) {
+  using C = Cfg<R, DR, F8>;
   __amdgpu_buffer_rsrc_t rc, rr;
-  if constexpr (PAGED) {
+  if constexpr (F8) {  // rows of R one-byte codes
+    rc = rows_rsrc(a.c_kv, b, a.T_max, R / 2, t0, lim);
+    rr = rows_rsrc(a.k_rope, b, a.T_max, DR, t0, lim);
+  } else if constexpr (PAGED) {
     rc = page_rsrc(a.c_kv, a, cp, R, t0, lim);
     rr = page_rsrc(a.k_rope, a, cp, DR, t0, lim);
   } else {
@@ -242,6 +253,44 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
 }
 
+// Orders this wave's LDS accesses before its later ones: waits for its
+// outstanding LDS operations and keeps the compiler from moving LDS accesses
+// across the point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// fp8 latent: a ring stage holds the slice's raw rows (R one-byte E4M3 codes
+// each, 16-byte slot s = row s / (R / 16), bytes 16 (s mod R / 16)); each lane
+// widens the slots it copied, exactly (E4M3 values fit bf16), into the bf16
+// slice layout in place (16-byte chunk c of row r at chunk position c ^ swz(r)).
+// Every lane's raw reads complete before any lane writes.
+template <int R>
+__device__ __forceinline__ void widen_slice(u16* cs, int lane) {
+  constexpr int NS = kSlice * R / 1024;  // raw slots per lane
+  u32x4 raw[NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) raw[u] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(cs) + 16 * (64 * u + lane));
+  wave_lds_sync();
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int t = 64 * u + lane, r = t / (R / 16), j = t % (R / 16);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {  // chunk 2j + hh: codes 8hh .. 8hh+7 of the slot
+      u32x4 w;
+      w[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[u][2 * hh], 1.f, false));
+      w[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[u][2 * hh], 1.f, true));
+      w[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[u][2 * hh + 1], 1.f, false));
+      w[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[u][2 * hh + 1], 1.f, true));
+      *reinterpret_cast<u32x4*>(cs + r * R + 8 * ((2 * j + hh) ^ swz<R>(r))) = w;
+    }
+  }
+  wave_lds_sync();
+}
+
 template <int R, int DR>
 struct WaveState {
   f32x4 o[R / 16];  // O^T[16w + 4grp + i][head row]
@@ -249,11 +298,11 @@ struct WaveState {
 };
 
 // One 16-token slice from (cs, rs): scores, online softmax, O^T update.
-template <int R, int DR>
+template <int R, int DR, bool F8 = false>
 __device__ __forceinline__ void slice_step(WaveState<R, DR>& st, const u16* cs, const u16* rs, const bf16x8 (&qhi)[R / 32],
                                            const bf16x8 (&qlo)[R / 32], const bf16x8* qr32, bf16x8 qr16, int t0, int c1,
-                                           float c, const Lanes<R, DR>& ln) {
-  using C = Cfg<R, DR>;
+                                           float c, const Lanes<R, DR, F8>& ln) {
+  using C = Cfg<R, DR, F8>;
   // S^T[token 4grp + i][head row]: A = slice rows (token = row), B = q_lat^T.
   // Two accumulation chains (the hi and lo parts of q_lat) alternate, so no
   // MFMA waits for the one issued just before it; they meet at the end.
@@ -399,7 +448,8 @@ __device__ void absorb_fixed_parts(const MlaDecodeArgs& a, int j, int lane, cons
 
 // Sums the phases of the two heads' accumulators and writes their q_lat rows.
 template <int R, int DR>
-__device__ __forceinline__ void absorb_store(float (&acc)[2][8], int h0, int h1, bool two, int lane, u16* qlat) {
+__device__ __forceinline__ void absorb_store(float (&acc)[2][8], int h0, int h1, bool two, int lane, u16* qlat,
+                                             float cs) {
   constexpr int RW = R + DR;
   constexpr int OCT = R / 8;
   const int o = lane % OCT, p = lane / OCT;
@@ -417,9 +467,10 @@ __device__ __forceinline__ void absorb_store(float (&acc)[2][8], int h0, int h1,
       u16x8 vh, vl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const __bf16 x = (__bf16)acc[hh][e];
+        const float y = acc[hh][e] * cs;  // the latent cache's scale (1 for bf16 caches)
+        const __bf16 x = (__bf16)y;
         vh[e] = __builtin_bit_cast(u16, x);
-        vl[e] = f32_to_bf16(acc[hh][e] - (float)x);
+        vl[e] = f32_to_bf16(y - (float)x);
       }
       *reinterpret_cast<u16x8*>(qlat + h * RW + 8 * o) = vh;
       *reinterpret_cast<u16x8*>(qlat + (kHeadsPad + h) * RW + 8 * o) = vl;
@@ -481,6 +532,7 @@ __device__ __forceinline__ void apply_uv(const UvBatch<R>& u, const MlaDecodeArg
     const size_t o0 = ((size_t)b * a.H + h) * a.dv;
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib) {
+      acc[ib] *= a.c_scale;  // o_lat was summed over the latent cache's codes (scale 1 for bf16 caches)
       const int i = 16 * (ib0 + ib) + 4 * grp;
       if (i < a.dv) {  // dv is a multiple of 16: a block is valid as a whole
         if (a.out_bf16) {
@@ -497,9 +549,9 @@ __device__ __forceinline__ void apply_uv(const UvBatch<R>& u, const MlaDecodeArg
 }
 
 // ---------------------------------------------------------------------------
-template <int R, int DR, bool PAGED>
+template <int R, int DR, bool PAGED, bool F8 = false>
 __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
-  using C = Cfg<R, DR>;
+  using C = Cfg<R, DR, F8>;
   constexpr int RW = C::RW;
   constexpr int S = C::kStages;
   // ring stages, each a distinct LDS variable so that the compiler can tell the
@@ -586,11 +638,11 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
     cpg.pg[1] = lane + 64 < np ? tb[lane + 64] : 0;
   }
   if (streamer) {
-    const Lanes<R, DR> ln(lane);
+    const Lanes<R, DR, F8> ln(lane);
     __builtin_amdgcn_s_barrier();  // (0)
 #pragma unroll
     for (int i = 0; i < S - 1; ++i)
-      issue_slice<R, DR, PAGED>(stage_c(i), stage_r(i), a, b, tw0 + i * kStep, c1, ln, cpg);
+      issue_slice<R, DR, PAGED, F8>(stage_c(i), stage_r(i), a, b, tw0 + i * kStep, c1, ln, cpg);
   } else {
     constexpr int P = 64 / (R / 8);
     constexpr int kRound = P * kAbsorbRows;  // W_UK rows per round
@@ -620,7 +672,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
           absorb_dot<R>(acc, ld);
           if (k0 + kRound < a.dn) absorb_issue<R>(ld, a, b, h0, two ? h1 : h0, k0 + kRound, lane);
         }
-        absorb_store<R, DR>(acc, h0, h1, two, lane, qlat);
+        absorb_store<R, DR>(acc, h0, h1, two, lane, qlat, a.c_scale);
       }
     }
     // further pairs (more than 8 heads)
@@ -633,13 +685,13 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
         absorb_dot<R>(acc, ld);
         if (k0 + kRound < a.dn) absorb_issue<R>(ld, a, b, h0, two ? h1 : h0, k0 + kRound, lane);
       }
-      absorb_store<R, DR>(acc, h0, h1, two, lane, qlat);
+      absorb_store<R, DR>(acc, h0, h1, two, lane, qlat, a.c_scale);
     }
   }
   __syncthreads();  // (1) q_lat is complete
   if (streamer) {
     // ---- stream the wave's slices through the ring
-    const Lanes<R, DR> ln(lane);
+    const Lanes<R, DR, F8> ln(lane);
     const int n_steps = (c1 - c0 + kStep - 1) / kStep;
     // q_lat^T as the B operand: lane holds q_lat[head row][32k + 8grp ..+8] (hi and lo)
     bf16x8 qhi[C::KC], qlo[C::KC], qr32[C::RC > 0 ? C::RC : 1], qr16 = {};
@@ -671,11 +723,12 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < S; ++i) {
         const int kk = k + i;
-        issue_slice<R, DR, PAGED>(stage_c((i + S - 1) % S), stage_r((i + S - 1) % S), a, b,
-                                  tw0 + (kk + S - 1) * kStep, c1, ln, cpg);
+        issue_slice<R, DR, PAGED, F8>(stage_c((i + S - 1) % S), stage_r((i + S - 1) % S), a, b,
+                                      tw0 + (kk + S - 1) * kStep, c1, ln, cpg);
         if (kk < n_steps) {
           wait_vmcnt<(S - 1) * C::kInstPerSlice>();
-          slice_step<R, DR>(st, stage_c(i), stage_r(i), qhi, qlo, qr32, qr16, tw0 + kk * kStep, c1, c, ln);
+          if constexpr (F8) widen_slice<R>(stage_c(i), lane);
+          slice_step<R, DR, F8>(st, stage_c(i), stage_r(i), qhi, qlo, qr32, qr16, tw0 + kk * kStep, c1, c, ln);
         }
       }
     }
@@ -845,7 +898,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
 
 template <int R, int DR>
 hipError_t launch_rd(const MlaDecodeArgs& a, hipStream_t st) {
-  if (a.block_table) hipLaunchKernelGGL((mla_decode<R, DR, true>), dim3(a.n_splits, a.B), dim3(kThreads), 0, st, a);
+  if (a.c_fp8) hipLaunchKernelGGL((mla_decode<R, DR, false, true>), dim3(a.n_splits, a.B), dim3(kThreads), 0, st, a);
+  else if (a.block_table) hipLaunchKernelGGL((mla_decode<R, DR, true>), dim3(a.n_splits, a.B), dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL((mla_decode<R, DR, false>), dim3(a.n_splits, a.B), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
@@ -874,6 +928,7 @@ hipError_t launch_mla_decode(const MlaDecodeArgs& a, hipStream_t st) {
   if (a.block_table && (a.page_size <= 0 || a.page_size % kSlice != 0 || a.n_pages <= 0 || a.append ||
                         a.split / a.page_size + 2 > 128))
     return hipErrorInvalidValue;
+  if (a.c_fp8 && (a.block_table || a.append || !(a.c_scale > 0.f))) return hipErrorInvalidValue;
   return a.r == 64 ? launch_r<64>(a, st) : a.r == 128 ? launch_r<128>(a, st) : launch_r<256>(a, st);
 }
 

@@ -368,6 +368,22 @@ def test_paged_prefill_validation():
 
 
 @no_gpu_only
+def test_mla_fp8_decode_validation():
+    lib = attn.lib()
+
+    def f(cs=0.01, **kw):
+        return lib.attn_decode_mla_fp8kv(FAKE, FAKE, FAKE, FAKE, kw.get("c", FAKE), cs, FAKE, FAKE, FAKE, 2, 8, 96, 48,
+                                         96, kw.get("r", 128), 256, 0.0, F32, 0, FAKE, 1 << 30, None)
+    assert f(cs=0.0) == SHAPE
+    assert f(cs=-1.0) == SHAPE
+    assert f(cs=float("nan")) == SHAPE
+    assert f(cs=float("inf")) == SHAPE
+    assert f(c=None) == NULL
+    assert f(c=FAKE_MIS) == UNSUP
+    assert f(r=96) == UNSUP
+
+
+@no_gpu_only
 def test_int4_decode_validation():
     lib = attn.lib()
 
