@@ -165,8 +165,9 @@ def main():
     app_new_k, app_new_v = app_k[:, 0].contiguous(), app_v[:, 0].contiguous()  # [B, Hkv, D]
     step_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     f8_scale = 4.5 / 448.0
-    f8_k = (torch.randn(B, T_max, Hkv, D, device=dev, generator=gen) / f8_scale).to(torch.float8_e4m3fn)
-    f8_v = (torch.randn(B, T_max, Hkv, D, device=dev, generator=gen) / f8_scale).to(torch.float8_e4m3fn)
+    # (clamped to E4M3's largest finite value: torch turns values past it into NaN codes)
+    f8_k = (torch.randn(B, T_max, Hkv, D, device=dev, generator=gen) / f8_scale).clamp(-448, 448).to(torch.float8_e4m3fn)
+    f8_v = (torch.randn(B, T_max, Hkv, D, device=dev, generator=gen) / f8_scale).clamp(-448, 448).to(torch.float8_e4m3fn)
     f8_bytes = dec_bytes // 2                                 # one byte per cached element
     f8_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     # int4 caches: random code bytes and per-row scales in [0.25, 0.75), drawn on the device, three
@@ -255,7 +256,7 @@ def main():
     # FP8 E4M3 latent: each copy's c_kv as codes with one scale (N(0,1) data, scale 4.5 / 448),
     # k_rope bf16
     mf8_scale = 4.5 / 448.0
-    mf8_copies = [((c.float() / mf8_scale).to(torch.float8_e4m3fn), kr) for c, kr in mla_copies]
+    mf8_copies = [((c.float() / mf8_scale).clamp(-448, 448).to(torch.float8_e4m3fn), kr) for c, kr in mla_copies]
     mf8_bytes = (r + 2 * dR) * mla_len                          # one fp8 latent + bf16 rope row per position
     mf8_out = torch.empty(MB, H, dv, dtype=torch.float32, device=dev)
     mla_step_ws = torch.zeros(attn.attn_decode_mla_workspace_bytes(MB, H, r, dR, MT, 0), dtype=torch.uint8,

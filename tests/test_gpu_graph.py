@@ -153,3 +153,54 @@ def test_mla_step_and_cached_append_prefill_graph_replay():
         pin["q"], k_new, v_new, pin["k"], pin["v"], pin["start_pos"], pin["q_lens"], out=pout), pout)
     assert torch.isfinite(peager.float()).all()
     assert not peager[1, 111:].any()
+
+
+def test_paged_and_low_precision_paths_graph_replay():
+    """The paged GQA and MLA decodes, the FP8-latent MLA decode, the int4 GQA decode and the paged
+    chunked prefill, each captured and replayed (their queue and chunk counters go back to zero
+    inside the launch)."""
+    import mha_mla_kv_amd as attn
+    B, H, dn, dR, dv, r, T = 3, 8, 96, 48, 96, 128, 1024
+    inp = {k: v.cuda() for k, v in synth.mla_decode_inputs(B, H, dn, dR, dv, r, T, [1024, 1, 500], seed=16,
+                                                           poison=False).items()}
+    ws = torch.zeros(attn.attn_decode_mla_workspace_bytes(B, H, r, dR, T, 0), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, H, dv, device="cuda")
+    cpool = inp["c_kv"].view(B * T // 16, 16, r).flip(0).contiguous()
+    rpool = inp["k_rope"].view(B * T // 16, 16, dR).flip(0).contiguous()
+    n_pages = B * T // 16
+    table = (n_pages - 1 - torch.arange(n_pages, dtype=torch.int32, device="cuda")).view(B, T // 16).contiguous()
+    print(f"[case] paged mla graph B={B} T={T}", flush=True)
+    e1 = _graph_matches_eager(lambda: attn.attn_decode_mla_paged(
+        inp["q_nope"], inp["q_rope"], inp["w_uk"], inp["w_uv"], cpool, rpool, table, inp["cache_lens"], out=out,
+        workspace=ws), out)
+    assert torch.isfinite(e1).all() and not ws[:4 * B].any()
+    c8s = float(inp["c_kv"].float().abs().max()) / 448.0
+    c8 = (inp["c_kv"].float() / c8s).to(torch.float8_e4m3fn)
+    assert not torch.isnan(c8.float()).any()
+    print(f"[case] fp8 latent mla graph B={B} T={T}", flush=True)
+    e2 = _graph_matches_eager(lambda: attn.attn_decode_mla_fp8kv(
+        inp["q_nope"], inp["q_rope"], inp["w_uk"], inp["w_uv"], c8, c8s, inp["k_rope"], inp["cache_lens"],
+        out=out, workspace=ws), out)
+    assert torch.isfinite(e2).all() and not ws[:4 * B].any()
+
+    i4 = {k: v.cuda() for k, v in synth.gqa_decode_int4_inputs(4, 32, 8, 128, 1500, [1500, 3, 700, 0],
+                                                              seed=17).items()}
+    gws = torch.zeros(attn.attn_decode_gqa_workspace_bytes(4, 32, 8, 128, 1500, 0), dtype=torch.uint8,
+                      device="cuda")
+    gout = torch.empty(4, 32, 128, device="cuda")
+    print("[case] int4 decode graph", flush=True)
+    e3 = _graph_matches_eager(lambda: attn.attn_decode_gqa_int4kv(
+        i4["q"], i4["k"], i4["v"], i4["k_scale"], i4["v_scale"], i4["cache_lens"], out=gout, workspace=gws), gout)
+    assert torch.isfinite(e3).all() and not gws[:4].any()
+
+    Bp, S, Hq, Hkv, D, Tp = 2, 200, 16, 4, 128, 1024
+    pin = {k: v.cuda() for k, v in synth.gqa_prefill_cached_inputs(Bp, S, Hq, Hkv, D, Tp, [700, 64], [200, 111],
+                                                                   seed=18, poison=False).items()}
+    kp = pin["k"].view(Bp * Tp // 64, 64, Hkv, D)
+    vp = pin["v"].view(Bp * Tp // 64, 64, Hkv, D)
+    ptable = torch.arange(Bp * Tp // 64, dtype=torch.int32, device="cuda").view(Bp, Tp // 64).contiguous()
+    pout = torch.empty_like(pin["q"])
+    print(f"[case] paged prefill graph B={Bp} S={S}", flush=True)
+    e4 = _graph_matches_eager(lambda: attn.attn_prefill_gqa_paged(
+        pin["q"], kp, vp, ptable, pin["start_pos"], pin["q_lens"], out=pout), pout)
+    assert torch.isfinite(e4.float()).all()
