@@ -188,6 +188,12 @@ def main():
     pg_table = torch.randperm(B * pg_max, generator=torch.Generator().manual_seed(11)).to(torch.int32)
     pg_table = pg_table.view(B, pg_max).to(dev)
     pg_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    # paged decode step: the newest row of every sequence in the paged view (through its page) is the
+    # new token, written back at the same place, so every call rewrites rows with their own values
+    pgs_page = pg_table[torch.arange(B, device=dev), (app_pos // pg_size).long()].long()
+    pgs_row = (app_pos % pg_size).long()
+    pgs_new_k, pgs_new_v = pg_k[pgs_page, pgs_row].contiguous(), pg_v[pgs_page, pgs_row].contiguous()  # [B, Hkv, D]
+    pgs_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     step_ws = torch.zeros(attn.attn_decode_gqa_append_workspace_bytes(B, Hq, Hkv, D, T_max, 0), dtype=torch.uint8,
                           device=dev)
 
@@ -361,6 +367,10 @@ def main():
     def run_paged(i):
         attn.attn_decode_gqa_paged(dec["q"], pg_k, pg_v, pg_table, dec["cache_lens"], out=pg_out, workspace=dec_ws)
 
+    def run_paged_step(i):
+        attn.attn_decode_gqa_paged_append(dec["q"], pgs_new_k, pgs_new_v, pg_k, pg_v, pg_table, app_pos, out=pgs_out,
+                                          workspace=step_ws)
+
     def run_fp8(i):
         attn.attn_decode_gqa_fp8kv(dec["q"], f8_k, f8_v, f8_scale, f8_scale, dec["cache_lens"], out=f8_out,
                                    workspace=dec_ws)
@@ -410,7 +420,7 @@ def main():
              ("mla_decode_paged", run_mla_paged), ("mla_decode_fp8", run_mla_fp8),
              ("kv_append", run_append), ("rope_append_decode", run_rope_decode), ("rope_append_chunk", run_rope_chunk),
              ("gqa_decode", run_decode), ("gqa_decode_paged", run_paged), ("gqa_decode_step", run_step),
-             ("gqa_decode_fp8", run_fp8), ("gqa_decode_int4", run_int4)]
+             ("gqa_decode_paged_step", run_paged_step), ("gqa_decode_fp8", run_fp8), ("gqa_decode_int4", run_int4)]
     parts += [(name, run_sweep(name)) for name in sweep]
     parts.append(("minimind768_gqa_decode", run_minimind))
     if want:
@@ -580,6 +590,11 @@ def main():
         decode_part("gqa_decode_step", dec_bytes, B, None,
                     "llama3_8b_gqa_decode with the newest rows as the new token "
                     "(attn_decode_gqa_append: write + decode in one call)")
+    if "gqa_decode_paged_step" in ms:
+        decode_part("gqa_decode_paged_step", dec_bytes, B, None,
+                    f"llama3_8b_gqa_decode step over the paged caches of gqa_decode_paged ({pg_size}-position pages "
+                    "scattered over the pool), the newest row of each sequence as the new token "
+                    "(attn_decode_gqa_paged_append: write + decode in one call)")
     if "kv_append" in ms:
         P["kv_append"] = {"ms": round(ms["kv_append"], 5), "bytes_per_launch": app_bytes,
                           "GB/s": round(rate(app_bytes, "kv_append"), 1),

@@ -275,6 +275,42 @@ attn_status attn_decode_gqa_paged(const void* q, const void* k_pages, const void
                                   size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* GQA decode step with the new token over paged K/V caches: attn_decode_gqa_append
+ * with the caches as a page pool and a block table (attn_decode_gqa_paged).
+ *
+ *   T_max = page_size * max_pages_per_seq, L = cache_lens[b] clamped to [0, T_max];
+ *   out[b,h,:] = softmax over { K[b,t,g] (t < L), k_new[b,g] } of
+ *                scale * q[b,h,:] . key, applied to the matching V rows
+ *   when L < T_max: row L % page_size of page P = block_table[b * max_pages_per_seq + L / page_size]
+ *   (clamped to [0, n_pages)) gets k_new[b,g,:] in k_pages[P, L % page_size, g, :] and
+ *   v_new[b,g,:] in v_pages likewise
+ *
+ * One decode iteration of Attention.forward on the "模型架构｜MQA & GQA 调研" page
+ * (code section) with start_pos = L, over the block-table reading of a paged
+ * cache that attn_decode_gqa_paged states.  The caller allocates the page that
+ * holds position L (its block-table entry must name it before the call); rows
+ * below L are read, the row of position L is written after they have been read,
+ * and no other row of either pool is touched.  Bit for bit attn_decode_gqa_append
+ * over the gathered caches, with the new row landing in its page.
+ *
+ *   q [B, Hq, head_dim], k_new, v_new [B, Hkv, head_dim]   bf16
+ *   k_pages, v_pages, block_table, cache_lens, out, page sizes, split_tokens:
+ *     as attn_decode_gqa_paged (the pools are written, so not const)
+ *   workspace: attn_decode_gqa_append_workspace_bytes(B, Hq, Hkv, head_dim,
+ *     page_size * max_pages_per_seq, split_tokens) bytes, 256-byte aligned,
+ *     its first 4 bytes zero before the first call (every call leaves them zero)
+ *
+ * Supported shapes and errors as attn_decode_gqa_paged, plus ATTN_ERR_NULL for
+ * a NULL k_new or v_new and ATTN_ERR_UNSUPPORTED for rows not 16-byte aligned.
+ */
+attn_status attn_decode_gqa_paged_append(const void* q, const void* k_new, const void* v_new, void* k_pages,
+                                         void* v_pages, const int32_t* block_table, const int32_t* cache_lens,
+                                         void* out, int B, int Hq, int Hkv, int head_dim, int page_size, int n_pages,
+                                         int max_pages_per_seq, float softmax_scale, attn_dtype in_dtype,
+                                         attn_dtype out_dtype, int split_tokens, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Causal GQA prefill (no cached prefix): query i attends to keys j <= i.
  *
  *   out[b,i,h,:] = sum_{j <= i} softmax_j(scale * q[b,i,h,:] . k[b,j,g,:]) v[b,j,g,:]

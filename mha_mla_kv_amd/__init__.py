@@ -56,6 +56,8 @@ def _declare(lib):
     lib.attn_prefill_gqa_causal.argtypes = [P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.attn_decode_gqa_paged.restype = I
     lib.attn_decode_gqa_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, I, P, Z, P]
+    lib.attn_decode_gqa_paged_append.restype = I
+    lib.attn_decode_gqa_paged_append.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, I, P, Z, P]
     lib.attn_decode_gqa_noalloc.restype = I
     lib.attn_decode_gqa_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P]
     lib.attn_decode_gqa_int4kv.restype = I
@@ -266,6 +268,42 @@ def attn_decode_gqa_paged(q, k_pages, v_pages, block_table, cache_lens, out=None
                                      _dt(q), _dt(out), int(split_tokens), _ptr(workspace), workspace.numel(),
                                      _stream(q.device))
     _raise_if(st, "attn_decode_gqa_paged")
+    return out
+
+
+def attn_decode_gqa_paged_append(q, k_new, v_new, k_pages, v_pages, block_table, cache_lens, out=None,
+                                 softmax_scale: float = 0.0, out_dtype=torch.float32, split_tokens: int = 0,
+                                 workspace=None):
+    """One decode step with the new token over paged caches: writes k_new/v_new [B,Hkv,D] at
+    position cache_lens[b] (row cache_lens[b] % page_size of page block_table[b, cache_lens[b] //
+    page_size]) and attends q [B,Hq,D] to the cache_lens[b] cached positions plus the new one.
+    Pools and table as attn_decode_gqa_paged; cache_lens is not changed.  Returns out [B,Hq,D]."""
+    _check(q, "q")
+    B, Hq, D = q.shape
+    _check(k_pages, "k_pages", dtype=q.dtype)
+    if k_pages.dim() != 4 or k_pages.shape[3] != D:
+        raise ValueError(f"k_pages must be [n_pages, page_size, Hkv, {D}] (got {tuple(k_pages.shape)})")
+    n_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    _check(v_pages, "v_pages", shape=k_pages.shape, dtype=q.dtype)
+    _check(k_new, "k_new", shape=(B, Hkv, D), dtype=q.dtype)
+    _check(v_new, "v_new", shape=(B, Hkv, D), dtype=q.dtype)
+    _check(block_table, "block_table", dtype=torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B={B}, max_pages_per_seq] (got {tuple(block_table.shape)})")
+    max_pages = block_table.shape[1]
+    _check(cache_lens, "cache_lens", shape=(B,), dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    _check(out, "out", shape=(B, Hq, D))
+    need = attn_decode_gqa_append_workspace_bytes(B, Hq, Hkv, D, page_size * max_pages, split_tokens)
+    if workspace is None:
+        workspace = _workspace(need, q.device, "gqa_append")
+    _check(workspace, "workspace", dtype=torch.uint8)
+    st = lib().attn_decode_gqa_paged_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages),
+                                            _ptr(block_table), _ptr(cache_lens), _ptr(out), B, Hq, Hkv, D, page_size,
+                                            n_pages, max_pages, float(softmax_scale), _dt(q), _dt(out),
+                                            int(split_tokens), _ptr(workspace), workspace.numel(), _stream(q.device))
+    _raise_if(st, "attn_decode_gqa_paged_append")
     return out
 
 
@@ -764,7 +802,7 @@ def attn_decode_mla_append(q_nope, q_rope, c_new, k_rope_new, w_uk, w_uv, c_kv, 
     return out
 
 
-__all__ = ["attn_decode_gqa", "attn_decode_gqa_paged", "attn_decode_mla_paged", "attn_decode_mla_fp8kv", "attn_prefill_gqa_paged", "attn_decode_gqa_int4kv", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_noalloc", "NOALLOC_SCRATCH_BYTES", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
+__all__ = ["attn_decode_gqa", "attn_decode_gqa_paged", "attn_decode_gqa_paged_append", "attn_decode_mla_paged", "attn_decode_mla_fp8kv", "attn_prefill_gqa_paged", "attn_decode_gqa_int4kv", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_noalloc", "NOALLOC_SCRATCH_BYTES", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
            "attn_decode_gqa_append_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached", "attn_prefill_gqa_cached_append",
            "attn_prefill_mla_causal", "attn_cache_append", "attn_rope_append",
            "attn_decode_mla_absorbed", "attn_decode_mla_append", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",

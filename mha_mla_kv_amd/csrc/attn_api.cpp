@@ -310,12 +310,11 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
                            workspace_bytes, stream);
 }
 
-attn_status attn_decode_gqa_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
-                                  const int32_t* cache_lens, void* out, int B, int Hq, int Hkv, int head_dim,
-                                  int page_size, int n_pages, int max_pages_per_seq, float softmax_scale,
-                                  attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
-  static const char* fn = "attn_decode_gqa_paged";
+namespace {
+
+// Checks shared by the paged GQA decode entry points.
+attn_status gqa_paged_checks(const char* fn, const int32_t* block_table, int page_size, int n_pages,
+                             int max_pages_per_seq, attn_dtype in_dtype, int split_tokens) {
   if (!block_table) return fail(ATTN_ERR_NULL, "%s: block_table must be non-NULL", fn);
   if (page_size <= 0 || n_pages <= 0 || max_pages_per_seq <= 0)
     return fail(ATTN_ERR_SHAPE, "%s: page_size, n_pages and max_pages_per_seq must be positive (%d, %d, %d)", fn,
@@ -328,7 +327,39 @@ attn_status attn_decode_gqa_paged(const void* q, const void* k_pages, const void
     return fail(ATTN_ERR_UNSUPPORTED, "%s: paged caches are built for bf16 inputs only", fn);
   if (split_tokens > 1024)
     return fail(ATTN_ERR_UNSUPPORTED, "%s: split_tokens=%d: at most 1024 with paged caches", fn, split_tokens);
+  return ATTN_OK;
+}
+
+}  // namespace
+
+attn_status attn_decode_gqa_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                                  const int32_t* cache_lens, void* out, int B, int Hq, int Hkv, int head_dim,
+                                  int page_size, int n_pages, int max_pages_per_seq, float softmax_scale,
+                                  attn_dtype in_dtype, attn_dtype out_dtype, int split_tokens, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  static const char* fn = "attn_decode_gqa_paged";
+  const attn_status st = gqa_paged_checks(fn, block_table, page_size, n_pages, max_pages_per_seq, in_dtype,
+                                          split_tokens);
+  if (st != ATTN_OK) return st;
   return gqa_decode_common(fn, q, nullptr, nullptr, k_pages, v_pages, cache_lens, out, B, Hq, Hkv, head_dim,
+                           page_size * max_pages_per_seq, softmax_scale, in_dtype, out_dtype, split_tokens, workspace,
+                           workspace_bytes, stream, nullptr, false, block_table, page_size, n_pages);
+}
+
+attn_status attn_decode_gqa_paged_append(const void* q, const void* k_new, const void* v_new, void* k_pages,
+                                         void* v_pages, const int32_t* block_table, const int32_t* cache_lens,
+                                         void* out, int B, int Hq, int Hkv, int head_dim, int page_size, int n_pages,
+                                         int max_pages_per_seq, float softmax_scale, attn_dtype in_dtype,
+                                         attn_dtype out_dtype, int split_tokens, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  static const char* fn = "attn_decode_gqa_paged_append";
+  if (!k_new || !v_new) return fail(ATTN_ERR_NULL, "%s: k_new and v_new must be non-NULL", fn);
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: k_new and v_new must be 16-byte aligned", fn);
+  const attn_status st = gqa_paged_checks(fn, block_table, page_size, n_pages, max_pages_per_seq, in_dtype,
+                                          split_tokens);
+  if (st != ATTN_OK) return st;
+  return gqa_decode_common(fn, q, k_new, v_new, k_pages, v_pages, cache_lens, out, B, Hq, Hkv, head_dim,
                            page_size * max_pages_per_seq, softmax_scale, in_dtype, out_dtype, split_tokens, workspace,
                            workspace_bytes, stream, nullptr, false, block_table, page_size, n_pages);
 }

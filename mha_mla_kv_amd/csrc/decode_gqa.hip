@@ -457,6 +457,16 @@ __device__ void run_units(const GqaDecodeArgs& a, UnitShared& sh, unsigned* pre,
 // workgroup combines.
 constexpr int kMergePairs = 256;
 
+// Cache row (in [Hkv, D] rows) that holds position t of sequence b: t of the
+// contiguous cache, or row t mod page_size of the page the block table names
+// (clamped to the pool) for paged caches.
+__device__ __forceinline__ size_t cache_row(const GqaDecodeArgs& a, int b, int t) {
+  if (!a.block_table) return (size_t)b * a.T_max + t;
+  const int e = a.block_table[(size_t)b * a.table_stride + t / a.page_size];
+  const int page = min(max(e, 0), a.n_pages - 1);
+  return (size_t)page * a.page_size + (t - (t / a.page_size) * a.page_size);
+}
+
 // Combines the partials of every (sequence, KV head) with more than one chunk:
 // out = sum_j 2^(lse_j - M) o_j / sum_j 2^(lse_j - M), M = max_j lse_j.  Grid
 // (Hkv * ceil(n_rep * D / 2 / kMergePairs), B): each thread merges one pair
@@ -465,8 +475,9 @@ constexpr int kMergePairs = 256;
 // In a decode step with the new token (a.append), every (sequence, KV head) is
 // merged: the new token is one more partial, with log2 score
 // scale_log2e * q . k_new and output v_new, and the thread of query head 0 of
-// the group writes its element pair of k_new and v_new to the cache row
-// lens[b] (the decode kernel read only rows below it).
+// the group writes its element pair of k_new and v_new to the cache row of
+// position lens[b] (the decode kernel read only rows below it; for paged
+// caches the row of that position's page).
 __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
   const int tid = threadIdx.x, b = blockIdx.y;
   if (a.use_queue && blockIdx.x == 0 && b == 0 && tid == 0) *a.queue = 0u;
@@ -538,7 +549,7 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
         vx = bf16_to_f32((u16)(vw & 0xffffu));
         vy = bf16_to_f32((u16)(vw >> 16));
         if (hd == 0 && L < a.T_max) {
-          const size_t dst = ((size_t)b * a.T_max + L) * a.Hkv * a.D + (size_t)g * a.D + 2 * d2;
+          const size_t dst = cache_row(a, b, L) * a.Hkv * a.D + (size_t)g * a.D + 2 * d2;
           *reinterpret_cast<unsigned*>(static_cast<u16*>(a.k_cache) + dst) =
               *reinterpret_cast<const unsigned*>(kp + 2 * d2);
           *reinterpret_cast<unsigned*>(static_cast<u16*>(a.v_cache) + dst) = vw;
@@ -565,7 +576,7 @@ __global__ __launch_bounds__(256) void gqa_decode_merge(GqaDecodeArgs a) {
         vx = vv.x;
         vy = vv.y;
         if (hd == 0 && L < a.T_max) {
-          const size_t dst = ((size_t)b * a.T_max + L) * a.Hkv * a.D + (size_t)g * a.D + 2 * d2;
+          const size_t dst = cache_row(a, b, L) * a.Hkv * a.D + (size_t)g * a.D + 2 * d2;
           *reinterpret_cast<float2*>(static_cast<float*>(a.k_cache) + dst) =
               *reinterpret_cast<const float2*>(kp + 2 * d2);
           *reinterpret_cast<float2*>(static_cast<float*>(a.v_cache) + dst) = vv;

@@ -245,6 +245,29 @@ def gather_pages(pages, block_table, cache_lens, page_size: int | None = None) -
     return out
 
 
+def append_pages(pages, block_table, new, start_pos, n_new=None) -> np.ndarray:
+    """cache_append over a paged cache: new[b, i] goes to position P + i of sequence b, i.e. row
+    (P + i) % page_size of page block_table[b, (P + i) // page_size] (clamped to [0, n_pages)),
+    with P = start_pos[b] clamped to [0, T] and n = n_new[b] (default S) clamped to
+    [0, min(S, T - P)], T = max_pages * page_size: the block-table layout of gather_pages, read
+    in the writing direction.  Returns a new pool; the arguments are not modified.  Any dtype."""
+    out = np.array(pages, copy=True)
+    new = np.asarray(new)
+    table = np.asarray(block_table, dtype=np.int64)
+    ps = out.shape[1]
+    B, S = new.shape[0], new.shape[1]
+    T = table.shape[1] * ps
+    for b in range(B):
+        P = min(max(int(start_pos[b]), 0), T)
+        n = S if n_new is None else int(n_new[b])
+        n = max(0, min(n, S, T - P))
+        for i in range(n):
+            t = P + i
+            page = min(max(int(table[b, t // ps]), 0), out.shape[0] - 1)
+            out[page, t % ps] = new[b, i]
+    return out
+
+
 def rope(x, positions, base: float = 10000.0, lib=None) -> np.ndarray:
     """Rotary position embedding (oracle_rope in oracle.c): x [..., H, d] with d even, positions
     [...] (one absolute position per token, the leading dimensions of x) -> float64 [..., H, d].

@@ -626,6 +626,39 @@ def pin_gather_pages(lib):
            oracle.gqa_decode(q, cache, cache, lens, lib=lib), 0.0, "decode over gathered caches")
 
 
+def pin_append_pages(lib):
+    """The paged cache write against the contiguous one it stands for: appending rows into a
+    shuffled pool and gathering the pages back equals cache_append on the gathered cache (pinned
+    by pin_cache_append), over lengths that start mid-page, end a page and fill the cache; rows of
+    the pool outside the written positions, spare pages included, keep their bits; an append
+    past the cache is cut at T, as cache_append's is."""
+    rng = _rng(53)
+    B, ps, mp, Hkv, D = 3, 4, 5, 2, 8
+    T = mp * ps
+    cache = _rand(rng, B, T, Hkv, D)
+    pool = cache.reshape(B * mp, ps, Hkv, D)
+    perm = rng.permutation(B * mp)
+    shuffled = np.concatenate([np.empty_like(pool), np.full((2, ps, Hkv, D), np.nan, np.float32)])
+    shuffled[perm] = pool
+    table = perm[np.arange(B * mp).reshape(B, mp)].astype(np.int32)
+    new = _rand(rng, B, 3, Hkv, D)
+    for start, n in (([5, 8, 0], None), ([3, 19, 20], [2, 3, 1]), ([0, 0, 18], [0, 1, 3])):
+        start = np.array(start, np.int32)
+        got = oracle.append_pages(shuffled, table, new, start, None if n is None else np.array(n, np.int32))
+        full = np.full(B, T, np.int32)
+        want = oracle.cache_append(oracle.gather_pages(shuffled, table, full), new, start,
+                                   None if n is None else np.array(n, np.int32))
+        assert np.array_equal(oracle.gather_pages(got, table, full), want), ("paged append", start, n)
+        changed = ~np.all((got == shuffled) | (np.isnan(got) & np.isnan(shuffled)), axis=(2, 3))
+        written = set()
+        for b in range(B):
+            m = 3 if n is None else n[b]
+            for t in range(start[b], min(start[b] + m, T)):
+                written.add((int(table[b, t // ps]), t % ps))
+        assert {tuple(x) for x in np.argwhere(changed)} <= written, "rows outside the written positions"
+        assert np.isnan(got[B * mp:]).all(), "spare pages"
+
+
 def pin_int4_decoding(lib):
     """Every one of the 256 bytes against the two's-complement reading of each nibble computed by
     integer arithmetic (low nibble first), plus landmarks: 0x07 -> (7, 0), 0x80 -> (0, -8),
@@ -646,4 +679,4 @@ ALL_PINS = [pin_decode_vs_sdpa, pin_decode_closed_forms, pin_decode_invariants, 
             pin_prefill_vs_sdpa, pin_prefill_rows, pin_cached_vs_sdpa, pin_cached_reductions, pin_mla_vs_sdpa, pin_mla_absorbed_equals_decompressed,
             pin_mla_selection, pin_mla_prefill_vs_sdpa, pin_mla_prefill_rows_are_decodes, pin_cache_append,
             pin_e4m3_decoding, pin_rope_quarter_turns, pin_rope_invariants, pin_rope_append,
-            pin_gather_pages, pin_int4_decoding]
+            pin_gather_pages, pin_append_pages, pin_int4_decoding]

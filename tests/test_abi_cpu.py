@@ -333,6 +333,27 @@ def test_paged_decode_validation():
 
 
 @no_gpu_only
+def test_paged_decode_step_validation():
+    lib = attn.lib()
+
+    def f(tb=FAKE, kn=FAKE, vn=FAKE, **kw):
+        return lib.attn_decode_gqa_paged_append(FAKE, kn, vn, FAKE, FAKE, tb, FAKE, FAKE, 2, 32, 8, kw.get("D", 128),
+                                                kw.get("ps", 64), kw.get("np", 100), kw.get("mp", 16), 0.0,
+                                                kw.get("ind", BF16), F32, kw.get("split", 0), FAKE, 1 << 30, None)
+    assert f(tb=None) == NULL
+    assert f(kn=None) == NULL
+    assert f(vn=None) == NULL
+    assert f(kn=FAKE_MIS) == UNSUP  # new rows not 16-byte aligned
+    assert f(ps=0) == SHAPE
+    assert f(np=0) == SHAPE
+    assert f(mp=0) == SHAPE
+    assert f(ps=48) == UNSUP
+    assert f(ind=F32) == UNSUP
+    assert f(split=2048) == UNSUP
+    assert f(D=80) == UNSUP
+
+
+@no_gpu_only
 def test_mla_paged_decode_validation():
     lib = attn.lib()
 
