@@ -29,11 +29,15 @@
 //  * O^T += V^T P^T: P stays in the accumulator layout and is the B operand after
 //    a key permutation shared with the A operand; V^T comes from the row-major V
 //    tile through ds_read_b64_tr_b16.
-//  * Online softmax in base 2, scale and max folded into one FMA per score; the
-//    row sum adds the bf16-rounded probabilities the PV product uses.  The
-//    reference max only moves (and O, l are rescaled) when a tile's max exceeds
-//    it by more than 2^8: probabilities then stay below 256, far inside bf16 and
-//    fp32 range, and most tiles skip the O rescale.
+//  * Online softmax in base 2.  The query operand is scaled by scale * log2(e)
+//    once (rounded to bf16, as the query itself is), and each tile's score
+//    products accumulate onto -m, the row's reference max, held in a register
+//    block that is the first MFMA's C operand: a probability is then one
+//    v_exp_f32 of the accumulator.  The row sum adds the bf16-rounded
+//    probabilities the PV product uses.  The reference max only moves (and O, l
+//    and the tile's scores are shifted) when a tile's max exceeds it by more
+//    than 2^8: probabilities then stay below 256, far inside bf16 and fp32
+//    range, and most tiles skip the rescale.
 //  * A wave skips tiles entirely above its diagonal; only diagonal tiles mask.
 //    With a prefix the diagonal is shifted right by P; a q-tile with no new
 //    token left writes zeros and reads nothing.
@@ -75,6 +79,15 @@ __device__ __forceinline__ float sum_xor32(float x) { const float2 p = pair_xor3
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight bf16 query elements times f, rounded back to bf16 (the query operand of
+// the score products).
+__device__ __forceinline__ bf16x8 scaled_operand(u16x8 x, float f) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)(__builtin_bit_cast(float, (unsigned)x[e] << 16) * f);
+  return r;
 }
 
 // ds_read_b64_tr_b16: lane i of a 16-lane group points at row T0 + i/4, columns
@@ -209,14 +222,14 @@ __device__ __forceinline__ LdsOffsets lds_offsets(const Lane& w) {
 }
 
 // S^T of one tile from the K tile kc: lane holds S^T[key 32j + 8(i/4) + 4h2 + i%4][row ln]
-// (keys relative to the tile).  A = 32-key K block, B = the wave's Q^T.  D is
-// the head size, DL the LDS row pitch of the tile (>= D).
+// (keys relative to the tile) plus init (the row's -m).  A = 32-key K block, B =
+// the wave's scaled Q^T.  D is the head size, DL the LDS row pitch of the tile
+// (>= D).
 template <int D, int DL = D>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const u16* kc, const bf16x8 (&qop)[D / 16], int off) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[j][i] = 0.f;
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const u16* kc, const bf16x8 (&qop)[D / 16], int off,
+                                        const f32x16& init) {
+  s[0] = init;
+  s[1] = init;
   // the two 32-key blocks' chains alternate, so no MFMA waits for the one before it
 #pragma unroll
   for (int c = 0; c < D / 16; ++c)
@@ -253,22 +266,40 @@ __device__ __forceinline__ void pv_tile(f32x16 (&o)[D / 32], const u16* vc, cons
   }
 }
 
-// Running state of one wave: O^T accumulators, reference max, partial row sum.
+// Running state of one wave: O^T accumulators, reference max m (log2 units of
+// the scaled scores), -m in all 16 elements (the score products' initial
+// accumulator), partial row sum.
 template <int D>
 struct RowState {
   f32x16 o[D / 32];
+  f32x16 negm;
   float m, lsum;
 };
 
-// Online softmax of one tile's scores sc (S^T layout of qk_tile): masks the keys
-// at positions past each row's cut (its own position, or the last cached
-// position for a tile of cached keys), moves the reference max when needed
-// (rescaling O and the row sum), and returns the probabilities as the four bf16
+template <int D>
+__device__ __forceinline__ void init_rows(RowState<D>& st) {
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.o[d][i] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) st.negm[i] = 0.f;
+  st.m = 0.f;  // replaced by the first tile's max
+  st.lsum = 0.f;
+}
+
+// Online softmax of one tile's scores sc (S^T layout of qk_tile, already scaled
+// and relative to the reference max): masks the keys at positions past each
+// row's cut (its own position, or the last cached position for a tile of cached
+// keys), moves the reference max when needed (shifting the tile's scores and
+// rescaling O and the row sum), and returns the probabilities as the four bf16
 // P^T operands of PV.  kv0: position of the tile's first key; cut0: the lowest
-// cut of the wave's rows (wave-uniform), cut: this lane's row's cut.
+// cut of the wave's rows (wave-uniform), cut: this lane's row's cut; first: the
+// wave's first tile, which sets the reference (key 0 is visible to every row, so
+// its max is finite).
 template <int D>
 __device__ __forceinline__ void softmax_tile(RowState<D>& st, f32x16 (&sc)[2], bf16x8 (&pop)[4], int kv0, int cut0,
-                                             int cut, const Lane& w) {
+                                             int cut, bool first, const Lane& w) {
   if (kv0 + kBN - 1 > cut0) {  // the tile reaches past the cut of some row
     const int t = cut - kv0 - 4 * w.h2;
 #pragma unroll
@@ -276,26 +307,32 @@ __device__ __forceinline__ void softmax_tile(RowState<D>& st, f32x16 (&sc)[2], b
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[j][i] = 32 * j + 8 * (i >> 2) + (i & 3) <= t ? sc[j][i] : kNegInf;
   }
-  float mr = kNegInf;  // raw row max; the scale is positive
+  float mr = kNegInf;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int i = 0; i < 16; ++i) mr = fmaxf(mr, sc[j][i]);
-  const float mt = max_xor32(mr) * w.c;
-  // key 0 is visible to every row, so tile 0 always sets a finite reference
-  if (__builtin_amdgcn_ballot_w64(mt > st.m + kRescaleSlack) != 0) {
-    const float mn = fmaxf(st.m, mt);
-    const float alpha = exp2_fast(st.m - mn);
+  const float mt = max_xor32(mr);  // the row's max above the reference
+  if (first || __builtin_amdgcn_ballot_w64(mt > kRescaleSlack) != 0) {
+    const float mn = st.m + (first ? mt : fmaxf(mt, 0.f));
+    const float shift = mn - st.m;
+    const float alpha = first ? 0.f : exp2_fast(st.m - mn);  // O and l are still zero on the first tile
     st.m = mn;
     st.lsum *= alpha;
 #pragma unroll
     for (int d = 0; d < D / 32; ++d) st.o[d] *= alpha;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[j][i] -= shift;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.negm[i] = -mn;
   }
   // P^T operand of PV step v: S^T block v/2, values 8(v%2)..+8
 #pragma unroll
   for (int v = 0; v < 4; ++v)
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) pop[v][jj] = (__bf16)exp2_fast(fmaf(sc[v >> 1][8 * (v & 1) + jj], w.c, -st.m));
+    for (int jj = 0; jj < 8; ++jj) pop[v][jj] = (__bf16)exp2_fast(sc[v >> 1][8 * (v & 1) + jj]);
   // row sum of the bf16-rounded probabilities (the ones the PV product uses),
   // two per v_dot2_f32_bf16 against (1, 1), in four independent chains
   const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
@@ -369,11 +406,11 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, const u16* kc, const 
   if (kt + 1 < src.n_kt) src.issue(cp, kn, vn, kt + 1);  // (kn, vn) were released by the last barrier
   if (kt <= last_kt) {
     f32x16 sc[2];
-    qk_tile<D, DL>(sc, kc, qop, off.k);
+    qk_tile<D, DL>(sc, kc, qop, off.k, st.negm);
     bf16x8 pop[4];
     const bool cached_tile = kt < src.n1 && src.n1 < src.n_kt;
     softmax_tile<D>(st, sc, pop, src.kv0(kt), cached_tile ? src.P - 1 : w.pos0, cached_tile ? src.P - 1 : w.my_pos,
-                    w);
+                    kt == 0, w);
     pv_tile<D, DL>(st.o, vc, pop, off.v_lo, off.v_hi);
   }
   wait_vmem();      // this thread's copies of tile kt+1 have landed
@@ -422,7 +459,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   static_assert(D % 32 == 0 && D <= 128, "head_dim");
   static_assert(kBM == 32 * kWaves, "one 32-row slice per wave");
   constexpr int KC = D / 16;
-  constexpr int DB = D / 32;
   // LDS row pitch: head_dim 96 rows (192 bytes, which no 16-byte XOR swizzle
   // covers) sit in the head_dim-128 layout; the copies' lanes that fall past the
   // row's 12 chunks read the next bytes or zeros, and QK and PV never read those
@@ -504,21 +540,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   src.issue(cp, k0, v0, 0);
   const LdsOffsets off = lds_offsets<DL>(w);
 
-  // Q^T as the B operand: lane holds Q[row ln][16c + 8h2 ..+8]
+  // (scale * log2 e) Q^T as the B operand: lane holds Q[row ln][16c + 8h2 ..+8]
   bf16x8 qop[KC];
   {
     const u16* qr = qp + (size_t)min(w.my_row, a.S - 1) * q_row + 8 * w.h2;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) qop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qr + 16 * c));
+    for (int c = 0; c < KC; ++c) qop[c] = scaled_operand(*reinterpret_cast<const u16x8*>(qr + 16 * c), w.c);
   }
 
   RowState<D> st;
-#pragma unroll
-  for (int d = 0; d < DB; ++d)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st.o[d][i] = 0.f;
-  st.m = kNegInf;
-  st.lsum = 0.f;
+  init_rows(st);
 
   wait_vmem();
   __syncthreads();
@@ -610,11 +641,9 @@ __device__ __forceinline__ void acc_to_operands(const f32x16& acc, float f, bf16
 // from the rope tile (rows of 64 elements).
 template <int DR>
 __device__ __forceinline__ void qk_tile_mla(f32x16 (&s)[2], const u16* cc, const u16* rc, const bf16x8 (&qop)[8],
-                                            const bf16x8 (&qrop)[DR / 16], int off, int off_r) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[j][i] = 0.f;
+                                            const bf16x8 (&qrop)[DR / 16], int off, int off_r, const f32x16& init) {
+  s[0] = init;
+  s[1] = init;
 #pragma unroll
   for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -649,9 +678,9 @@ __device__ __forceinline__ void tile_step_mla(RowState<128>& st, const u16* cc, 
   }
   if (kt <= last_kt) {
     f32x16 sc[2];
-    qk_tile_mla<DR>(sc, cc, rc, qop, qrop, off.k, off_r);
+    qk_tile_mla<DR>(sc, cc, rc, qop, qrop, off.k, off_r, st.negm);
     bf16x8 pop[4];
-    softmax_tile<128>(st, sc, pop, kt * kBN, w.pos0, w.my_pos, w);
+    softmax_tile<128>(st, sc, pop, kt * kBN, w.pos0, w.my_pos, kt == 0, w);
     pv_tile<128>(st.o, cc, pop, off.v_lo, off.v_hi);  // V = the latent tile
   }
   wait_vmem();
@@ -752,10 +781,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   for (int c = 0; c < DN / 16; ++c) qnop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qn + 16 * c));
   bf16x8 qrop[DR / 16];
 #pragma unroll
-  for (int c = 0; c < DR / 16; ++c) qrop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qr + 16 * c));
+  for (int c = 0; c < DR / 16; ++c) qrop[c] = scaled_operand(*reinterpret_cast<const u16x8*>(qr + 16 * c), w.c);
   __syncthreads();  // W_UK^T staged
 
-  // q_c^T[j][row] = sum_i W_UK^T[j][i] q_nope^T[i][row], 32 j at a time
+  // q_c^T[j][row] = sum_i W_UK^T[j][i] q_nope^T[i][row], 32 j at a time, times scale * log2 e
   bf16x8 qop[8];
 #pragma unroll
   for (int jb = 0; jb < R / 32; ++jb) {
@@ -766,18 +795,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int c = 0; c < DN / 16; ++c)
       acc = mfma_32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(ar + 16 * c)), qnop[c], acc);
-    acc_to_operands(acc, 1.f, &qop[2 * jb], w.h2);
+    acc_to_operands(acc, w.c, &qop[2 * jb], w.h2);
   }
 
   const LdsOffsets off = lds_offsets<128>(w);
   const int off_r = lds_offsets<64>(w).k;
   RowState<128> st;
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st.o[d][i] = 0.f;
-  st.m = kNegInf;
-  st.lsum = 0.f;
+  init_rows(st);
 
   wait_vmem();
   __syncthreads();
