@@ -44,6 +44,7 @@ Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -106,6 +107,22 @@ def cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+def device_clock_ghz(index: int):
+    """Peak engine clock of device `index` in GHz from hipDeviceGetAttribute, or None.
+
+    torch's device properties carry no clock on ROCm.  The HIP runtime is the one torch has
+    loaded already (same soname, so dlopen returns that copy rather than a second runtime)."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+    except OSError:
+        return None
+    clock_rate_khz = 5  # hipDeviceAttributeClockRate: sixth entry of hipDeviceAttribute_t
+    v = ctypes.c_int(0)
+    if hip.hipDeviceGetAttribute(ctypes.byref(v), clock_rate_khz, index) != 0 or v.value <= 0:
+        return None
+    return v.value / 1e6
 
 
 def gqa_decode_bytes(Hkv, D, elem_bytes, sum_len):
@@ -461,7 +478,7 @@ def main():
     t_main = measured_traffic("gqa_decode_bf16<128, 1, true, false, false, false>", dec_hash)
     t_merge = measured_traffic("gqa_decode_merge", dec_hash)
     traffic = round(t_main + t_merge) if t_main is not None and t_merge is not None else None
-    clk_ghz = props.clock_rate / 1e6 if getattr(props, "clock_rate", 0) else None
+    clk_ghz = device_clock_ghz(torch.cuda.current_device())
     derived_peak = (props.multi_processor_count * BF16_FLOP_PER_CU_CLK * clk_ghz * 1e9 / 1e12) if clk_ghz else None
 
     result = {
