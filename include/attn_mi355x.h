@@ -92,10 +92,11 @@ const char* attn_last_error(void);
  * (sequence, KV head).  A workgroup reads a unit's K/V rows once for all Hq/Hkv
  * query heads of the group.  Sequences of one chunk are written directly; the
  * chunks of longer ones are combined by their log-sum-exp in a second, small
- * kernel on the same stream.  Batches of up to 1024 sequences run the units
- * through a device-wide queue taken by the resident workgroups (planned on the
- * device from cache_lens, so the host never reads the lengths); larger batches
- * launch one workgroup per unit.  split_tokens = 0 lets the library choose the
+ * kernel on the same stream.  Batches of up to 1024 sequences whose
+ * B * Hkv * ceil(T_max / chunk) blocks outnumber the 256 compute units run the
+ * units through a device-wide queue taken by the resident workgroups (planned
+ * on the device from cache_lens, so the host never reads the lengths); other
+ * batches launch one workgroup per unit.  split_tokens = 0 lets the library choose the
  * chunk from the sizes; otherwise it is a multiple of 64 in [64, 65536].  The
  * result does not depend on the chunk beyond fp32 rounding.
  *
