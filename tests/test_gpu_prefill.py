@@ -56,9 +56,9 @@ def test_prefill_first_row_is_v0_and_deterministic():
     assert np.array_equal(a, b)
     v = inp["v"].float().numpy()
     for h in range(8):
-        # query 0 sees only key 0, so its output is V[0]; the kernel's exp2(s*c - m)
-        # with m rounded gives p = 1 up to one fp32 rounding, hence the 1e-6 slack
-        # (a leak of any other key would show at the 1e-2 level)
+        # query 0 sees only key 0, so its output is V[0]: the kernel subtracts the
+        # row's max from its one visible score, p = 1; the 1e-6 slack covers the
+        # normalisation (a leak of any other key would show at the 1e-2 level)
         np.testing.assert_allclose(a[:, 0, h], v[:, 0, h // 4], rtol=1e-6, atol=1e-6)
 
 
@@ -70,3 +70,34 @@ def test_prefill_full_size_sampled_rows():
     rows = [0, 1, 127, 128, 2047, 2048, 4000, 4095]
     ref = oracle.gqa_prefill_causal(inp["q"], inp["k"], inp["v"], rows=rows)
     assert_close_rows(out[:, rows], ref[:, rows], TOL_BF16, "prefill full size sampled rows")
+
+
+def stepped_scores(q, k, n_rep, step=0.6, seed=5):
+    """Queries and keys whose scores climb by about 10 (log2 units, at head_dim 128 and the
+    default scale) from one 64-key tile to the next: every key of KV head g points along one
+    direction u_g (the group's queries too), times 1 + step * (position // 64), plus 10% noise.
+    Every later tile then lifts the running max by more than the kernel's 2^8 slack, so the
+    reference max moves (scores shifted, O and l rescaled) tile after tile, while keys of one
+    tile stay close, so the rows stay smooth averages of V.  Callers keep to about 7 tiles:
+    the scores then stay below about 75, where the bf16-rounded scaled query (relative score
+    error about 2^-9 / sqrt(head_dim)) moves the weights by well under the 2e-2 tolerance.
+    NaN entries of q and k stay NaN."""
+    g = torch.Generator().manual_seed(seed)
+    B, S, Hq, D = q.shape
+    T, Hkv = k.shape[1], k.shape[2]
+    u = torch.randn(B, 1, Hkv, D, generator=g)
+    qu = u.repeat_interleave(n_rep, dim=2)  # the contiguous head grouping: head h uses u_(h // n_rep)
+    qn = qu + 0.1 * torch.randn(B, S, Hq, D, generator=g)
+    mag = 1.0 + step * (torch.arange(T) // 64).float()
+    kn = mag[None, :, None, None] * (u + 0.1 * torch.randn(B, T, Hkv, D, generator=g))
+    return (q.float() * 0 + qn).to(q.dtype), (k.float() * 0 + kn).to(k.dtype)
+
+
+def test_prefill_moving_max_matches_oracle():
+    """Scores that climb tile after tile (stepped_scores): the path where a tile's max exceeds
+    the reference by more than the slack, on every tile after the first."""
+    inp = synth.gqa_prefill_inputs(2, 330, 8, 2, 128, seed=37)  # 6 key tiles
+    inp["q"], inp["k"] = stepped_scores(inp["q"], inp["k"], 4)
+    out = _run(inp)
+    ref = oracle.gqa_prefill_causal(inp["q"], inp["k"], inp["v"])
+    assert_close_rows(out, ref, TOL_BF16, "moving max")

@@ -97,3 +97,12 @@ def test_chunked_prefill_full_size_sampled_rows():
     ref = np.concatenate([oracle.gqa_prefill_cached(inp["q"][:, i:i + 1], inp["k"], inp["v"], inp["start_pos"] + i,
                                                     None) for i in rows], axis=1)
     assert_close_rows(out[:, rows], ref, TOL_BF16, "chunked prefill full size sampled rows")
+
+
+def test_cached_prefill_moving_max_matches_oracle():
+    """Scores that climb tile after tile over the cached prefix and the chunk (the reference max
+    moves on every tile after the first)."""
+    from tests.test_gpu_prefill import stepped_scores
+    inp = synth.gqa_prefill_cached_inputs(2, 200, 8, 2, 128, 400, [200, 64], [200, 141], seed=39)  # 7 key tiles
+    inp["q"], inp["k"] = stepped_scores(inp["q"], inp["k"], 4)
+    assert_close_rows(_run(inp), _ref(inp), TOL_BF16, "cached, moving max")

@@ -93,3 +93,25 @@ def test_mla_prefill_full_size_sampled_rows():
                                                     *(inp[k] for k in KEYS[2:]), inp["start_pos"] + i, None)
                           for i in rows], axis=1)
     assert_close_rows(out[:, rows], ref, TOL_BF16, "MLA prefill full size sampled rows")
+
+
+def test_mla_prefill_moving_max_matches_oracle():
+    """Scores that climb by about 8.4 (log2 units) from one 64-key tile to the next through the
+    shared rotated key: q_rope along one direction per sequence, k_rope along it times
+    0.5 + 1.45 * (position // 64), plus noise; the latent part scaled down to a small
+    perturbation.  The reference max moves on most tiles after the first; six key tiles keep the
+    scores below about 50, where the bf16-rounded scaled q_rope moves the weights by about 1%.
+    NaN poison stays in place."""
+    inp = synth.mla_prefill_inputs(2, 300, 8, *DIMS, 384, [0, 84], [300, 300], seed=53)
+    g = torch.Generator().manual_seed(9)
+    B, S, H, dR = inp["q_rope"].shape
+    T = inp["k_rope"].shape[1]
+    u = torch.randn(B, 1, 1, dR, generator=g)
+    qr = u + 0.1 * torch.randn(B, S, H, dR, generator=g)
+    mag = 0.5 + 1.45 * (torch.arange(T) // 64).float()
+    kr = mag[None, :, None] * (u[:, :, 0] + 0.1 * torch.randn(B, T, dR, generator=g))
+    inp["q_rope"] = (inp["q_rope"].float() * 0 + qr).to(torch.bfloat16)
+    inp["k_rope"] = (inp["k_rope"].float() * 0 + kr).to(torch.bfloat16)
+    inp["q_nope"] = (inp["q_nope"].float() * 0.3).to(torch.bfloat16)
+    inp["c_kv"] = (inp["c_kv"].float() * 0.3).to(torch.bfloat16)
+    assert_close_rows(_run(inp), _ref(inp), TOL_BF16, "mla, moving max")
