@@ -195,3 +195,27 @@ def test_four_block_units_every_row(Hq, Hkv, B, T):
     out = _run(inp, split_tokens=64)
     ref = oracle.gqa_decode(inp["q"], inp["k"], inp["v"], inp["cache_lens"])
     assert_close_rows(out, ref, TOL_BF16, f"four-block units Hkv={Hkv}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_decode_moving_max_matches_oracle(dt):
+    """Scores that climb along the cache: every key of KV head g points along the group's query
+    direction u_g, times 1 + 0.15 * (position // 32), plus 10% noise, so each wave's next
+    32-position tile (four tiles on) beats its running max by about 10 (log2 units) -- more than
+    the kernels' 2^8 slack -- and the reference moves with a rescale factor strictly between 0
+    and 1, tile after tile; the units' partials then merge across very different maxima.  Keys
+    of one tile stay close, so rows are smooth averages of V."""
+    B, Hq, Hkv, D, T = 2, 16, 4, 128, 700
+    inp = synth.gqa_decode_inputs(B, Hq, Hkv, D, T, [700, 513], dtype=dt, seed=13)
+    g = torch.Generator().manual_seed(6)
+    u = torch.randn(B, 1, Hkv, D, generator=g)
+    q = u[:, 0].repeat_interleave(Hq // Hkv, dim=1) + 0.1 * torch.randn(B, Hq, D, generator=g)
+    mag = 1.0 + 0.15 * (torch.arange(T) // 32).float()
+    k = mag[None, :, None, None] * (u + 0.1 * torch.randn(B, T, Hkv, D, generator=g))
+    dtype = inp["q"].dtype
+    inp["q"] = q.to(dtype)
+    inp["k"] = (inp["k"].float() * 0 + k).to(dtype)  # NaN poison past the lengths stays
+    ref = oracle.gqa_decode(inp["q"], inp["k"], inp["v"], inp["cache_lens"])
+    for split in (64, 256, 0):
+        out = _run(inp, split_tokens=split)
+        assert_close_rows(out, ref, TOL_FP32 if dt == "f32" else TOL_BF16, f"moving max {dt} split {split}")

@@ -104,3 +104,25 @@ def test_full_size_minimind_mla():
     bh = [0, 7, 8 * 31 + 3, 8 * 63 + 7]
     ref = _oracle(inp, bh=bh, decompressed=True).reshape(-1, 96)[bh]
     assert_close_rows(to_np(out).reshape(-1, 96)[bh], ref, TOL_BF16, "mla full vs decompressed oracle")
+
+
+def test_mla_moving_max_matches_oracle():
+    """Scores that climb along the cache through the shared rotated key: q_rope along one
+    direction per sequence, k_rope along it times 1 + 0.4 * (position // 16), plus noise, the
+    latent part scaled down to a small perturbation.  Each streaming wave's next 16-row slice
+    (four slices on) beats its running max by about 9 (log2 units), more than the 2^8 slack, so
+    the reference moves slice after slice and the chunks merge across very different maxima."""
+    B, H, dn, dR, dv, r, T = 2, 8, 96, 48, 96, 128, 300
+    inp = synth.mla_decode_inputs(B, H, dn, dR, dv, r, T, [300, 217], seed=23)
+    g = torch.Generator().manual_seed(7)
+    u = torch.randn(B, 1, dR, generator=g)
+    qr = u + 0.1 * torch.randn(B, H, dR, generator=g)
+    mag = 1.0 + 0.4 * (torch.arange(T) // 16).float()
+    kr = mag[None, :, None] * (u + 0.1 * torch.randn(B, T, dR, generator=g))
+    inp["q_rope"] = qr.to(torch.bfloat16)
+    inp["k_rope"] = (inp["k_rope"].float() * 0 + kr).to(torch.bfloat16)
+    inp["q_nope"] = (inp["q_nope"].float() * 0.3).to(torch.bfloat16)
+    inp["c_kv"] = (inp["c_kv"].float() * 0.3).to(torch.bfloat16)
+    ref = _oracle(inp, decompressed=True)
+    for split in (64, 0):
+        assert_close_rows(_run(inp, split_tokens=split), ref, TOL_BF16, f"mla moving max split {split}")
