@@ -164,6 +164,11 @@ attn_status attn_decode_gqa_noalloc(const void* q, const void* k_cache, const vo
  *   k_scale, v_scale > 0 and finite (else ATTN_ERR_SHAPE);  cache_lens, out,
  *   split_tokens, workspace (attn_decode_gqa_workspace_bytes) as attn_decode_gqa
  *
+ * split_tokens = 0 chooses a chunk a quarter longer than attn_decode_gqa's for
+ * the same sizes (at least 64 positions longer, a multiple of 64; 640 where
+ * attn_decode_gqa takes 512), so the workspace that attn_decode_gqa_workspace_bytes
+ * gives for split_tokens = 0 always suffices.
+ *
  * head_dim must be 128 (else ATTN_ERR_UNSUPPORTED); Hq/Hkv up to 64.
  */
 attn_status attn_decode_gqa_fp8kv(const void* q, const void* k_cache, const void* v_cache, float k_scale,
