@@ -73,7 +73,88 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy per step (for counter calibration)")
     ap.add_argument("--parts", default="", help="comma-separated subset of parts to run (default: all)")
+    ap.add_argument("--fixed-cost", action="store_true",
+                    help="instead of the step: time the MQA, Llama-3-head and MLA decodes over a range of cache "
+                         "lengths and fit time = fixed + bytes / stream rate (one JSON line)")
     return ap.parse_args()
+
+
+def fixed_cost(attn, torch, synth, dev, dev_normal):
+    """Per-call time of three decode families against their cache bytes, to separate a call's
+    fixed cost (launch, first loads, epilogue, merge) from its streaming rate.  Every length runs
+    over rotating cache copies of at least 512 MiB in all (twice the Infinity Cache), each time
+    the median of 5 repeats of 10 back-to-back calls; the fit is least squares over the four
+    largest lengths, where every compute unit has work."""
+    import numpy as np
+
+    def timed(fn, n_copies):
+        for i in range(2):
+            fn(i % n_copies)
+        reps = []
+        c = 0
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                fn(c % n_copies)
+                c += 1
+            e1.record()
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1) / 10 * 1000)
+        return float(np.median(reps))
+
+    def copies_for(nbytes):
+        return max(2, -(-(512 << 20) // nbytes))
+
+    res = {}
+    # GQA decode: MQA (the sweep's B 16, Hq 32, Hkv 1) and the Llama-3-8B heads (B 32, Hq 32, Hkv 8)
+    for fam, B, Hq, Hkv, lengths in (("mqa_b16", 16, 32, 1, (1024, 2048, 4096, 8192, 16384, 32768)),
+                                     ("llama3_heads_b32", 32, 32, 8, (512, 1024, 2048, 4096, 8192))):
+        D = 128
+        pts = []
+        q = dev_normal((B, Hq, D))
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+        for L in lengths:
+            nbytes = 2 * B * L * Hkv * D * 2
+            nc = copies_for(nbytes)
+            kv = [(dev_normal((B, L, Hkv, D)), dev_normal((B, L, Hkv, D))) for _ in range(nc)]
+            lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+            ws = torch.zeros(attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, L, 0), dtype=torch.uint8, device=dev)
+            us = timed(lambda i: attn.attn_decode_gqa(q, kv[i][0], kv[i][1], lens, out=out, workspace=ws), nc)
+            pts.append((L, nbytes, us))
+            del kv
+            torch.cuda.empty_cache()
+        res[fam] = pts
+    # MLA decode at the MiniMind-768 widths (B 64, H 8, r 128, dR 48)
+    mla = {k: v.to(dev) for k, v in synth.make("minimind768_mla_decode").items()}
+    MB, H, dn = mla["q_nope"].shape
+    dR, dv, r = mla["q_rope"].shape[2], mla["w_uv"].shape[1], mla["w_uv"].shape[2]
+    out = torch.empty(MB, H, dv, dtype=torch.float32, device=dev)
+    pts = []
+    for L in (512, 1024, 2048, 4096, 8192, 16384):
+        nbytes = MB * L * (r + dR) * 2
+        nc = copies_for(nbytes)
+        cc = [(dev_normal((MB, L, r)), dev_normal((MB, L, dR))) for _ in range(nc)]
+        lens = torch.full((MB,), L, dtype=torch.int32, device=dev)
+        ws = torch.zeros(attn.attn_decode_mla_workspace_bytes(MB, H, r, dR, L, 0), dtype=torch.uint8, device=dev)
+        us = timed(lambda i: attn.attn_decode_mla_absorbed(mla["q_nope"], mla["q_rope"], mla["w_uk"], mla["w_uv"],
+                                                           cc[i][0], cc[i][1], lens, out=out, workspace=ws), nc)
+        pts.append((L, nbytes, us))
+        del cc
+        torch.cuda.empty_cache()
+    res["mla_minimind768_b64"] = pts
+
+    report = {}
+    for fam, pts in res.items():
+        x = np.array([p[1] for p in pts[-4:]], dtype=np.float64)
+        y = np.array([p[2] for p in pts[-4:]], dtype=np.float64)
+        slope, icept = np.polyfit(x, y, 1)  # us per byte, us
+        report[fam] = {"points": [{"L": L, "bytes": b, "us": round(t, 2), "TB/s": round(b / t / 1e6, 3)}
+                                  for L, b, t in pts],
+                       "fit_over_L": [p[0] for p in pts[-4:]],
+                       "fixed_us": round(float(icept), 2), "stream_TB/s": round(1.0 / float(slope) / 1e6, 3)}
+    print(json.dumps({"fixed_cost": report, "hbm_peak_TB/s": 8.0,
+                      "note": "per-call time = fixed_us + bytes / stream rate, fitted over the four largest lengths"}))
 
 
 def source_hash(*names) -> str:
@@ -161,6 +242,10 @@ def main():
         if scale != 1.0:
             x *= scale
         return x.to(dtype)
+
+    if args.fixed_cost:
+        fixed_cost(attn, torch, synth, dev, dev_normal)
+        return
 
     # ---- Llama-3-8B GQA decode (the headline), its append / fused step, FP8 caches ----
     dspec = synth.WORKLOADS["llama3_8b_gqa_decode"]
