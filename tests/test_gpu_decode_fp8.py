@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from tests.parity import TOL_BF16, assert_close_rows, to_np
+from tests.parity import TOL_BF16, assert_close_rows, row_rel_err, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -71,3 +71,19 @@ def test_fp8_decode_full_size_sampled_rows():
     for b in (0, 15, 31):
         sl = slice(b, b + 1)
         assert_close_rows(out[sl], _ref(inp, sl), TOL_BF16, f"fp8 full size b={b}")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,lens", [(4, 32, 8, 1500, [0, 1, 700, 1500]), (2, 32, 1, 3000, [2999, 1234]),
+                                             (3, 8, 2, 640, [640, 639, 5]), (2, 16, 4, 8192, [8192, 4097])])
+def test_fp8_default_chunk_fits_the_decode_workspace(B, Hq, Hkv, T, lens):
+    """split_tokens = 0 picks a longer chunk for FP8 caches than attn_decode_gqa does; a workspace
+    of exactly attn_decode_gqa_workspace_bytes(..., 0) is enough for it, and the output matches the
+    oracle and the same call with 64-position chunks (up to fp32 rounding)."""
+    import mha_mla_kv_amd as attn
+    inp = synth.gqa_decode_fp8_inputs(B, Hq, Hkv, 128, T, lens, seed=19)
+    n = attn.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, 128, T, 0)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    out = _run(inp, workspace=ws)
+    assert_close_rows(out, _ref(inp), TOL_BF16, f"fp8 default chunk B={B} Hq={Hq} Hkv={Hkv} T={T}")
+    # different chunks round the bf16 probabilities against different running maxima: about 2^-9
+    assert row_rel_err(out, _run(inp, split_tokens=64)) <= 5e-3
