@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from tests.parity import TOL_BF16, assert_close_rows, to_np
+from tests.parity import TOL_BF16, assert_close_rows, stepped_scores, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -102,7 +102,6 @@ def test_chunked_prefill_full_size_sampled_rows():
 def test_cached_prefill_moving_max_matches_oracle():
     """Scores that climb tile after tile over the cached prefix and the chunk (the reference max
     moves on every tile after the first)."""
-    from tests.test_gpu_prefill import stepped_scores
     inp = synth.gqa_prefill_cached_inputs(2, 200, 8, 2, 128, 400, [200, 64], [200, 141], seed=39)  # 7 key tiles
     inp["q"], inp["k"] = stepped_scores(inp["q"], inp["k"], 4)
     assert_close_rows(_run(inp), _ref(inp), TOL_BF16, "cached, moving max")

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from tests.parity import TOL_BF16, assert_close_rows
+from tests.parity import TOL_BF16, assert_close_rows, stepped_scores
 
 pytestmark = pytest.mark.gpu
 
@@ -111,7 +111,6 @@ def test_cached_append_matches_append_then_cached_prefill():
 def test_cached_append_moving_max():
     """Scores that climb tile after tile over the cached prefix (cut at P - 1) and the chunk's
     own tiles: the reference max moves on every tile after the first."""
-    from tests.test_gpu_prefill import stepped_scores
     inp = synth.gqa_prefill_cached_inputs(2, 200, 8, 2, 128, 400, [200, 97], [200, 141], seed=67)
     inp["q"], inp["k"] = stepped_scores(inp["q"], inp["k"], 4)
     _check(inp, what="cached append, moving max")
