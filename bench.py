@@ -469,6 +469,11 @@ def main():
     def run_paged(i):
         attn.attn_decode_gqa_paged(dec["q"], pg_k, pg_v, pg_table, dec["cache_lens"], out=pg_out, workspace=dec_ws)
 
+    def run_paged_fp8(i):  # the FP8 caches seen as pools of 64-position pages, read through the same table
+        attn.attn_decode_gqa_paged_fp8kv(dec["q"], f8_k.view(B * pg_max, pg_size, Hkv, D),
+                                         f8_v.view(B * pg_max, pg_size, Hkv, D), f8_scale, f8_scale, pg_table,
+                                         dec["cache_lens"], out=f8_out, workspace=dec_ws)
+
     def run_paged_step(i):
         attn.attn_decode_gqa_paged_append(dec["q"], pgs_new_k, pgs_new_v, pg_k, pg_v, pg_table, app_pos, out=pgs_out,
                                           workspace=step_ws)
@@ -522,7 +527,8 @@ def main():
              ("mla_decode_paged", run_mla_paged), ("mla_decode_fp8", run_mla_fp8),
              ("kv_append", run_append), ("rope_append_decode", run_rope_decode), ("rope_append_chunk", run_rope_chunk),
              ("gqa_decode", run_decode), ("gqa_decode_paged", run_paged), ("gqa_decode_step", run_step),
-             ("gqa_decode_paged_step", run_paged_step), ("gqa_decode_fp8", run_fp8), ("gqa_decode_int4", run_int4)]
+             ("gqa_decode_paged_step", run_paged_step), ("gqa_decode_fp8", run_fp8),
+             ("gqa_decode_paged_fp8", run_paged_fp8), ("gqa_decode_int4", run_int4)]
     parts += [(name, run_sweep(name)) for name in sweep]
     parts.append(("minimind768_gqa_decode", run_minimind))
     if want:
@@ -680,6 +686,10 @@ def main():
         decode_part("gqa_decode_fp8", f8_bytes, B, None,
                     "llama3_8b_gqa_decode shape and lengths, K/V as FP8 E4M3 codes of N(0,1)/scale "
                     "(device-drawn, seed 8), scale 4.5/448")
+    if "gqa_decode_paged_fp8" in ms:
+        decode_part("gqa_decode_paged_fp8", f8_bytes, B, None,
+                    f"the FP8 caches of gqa_decode_fp8 as pools of {pg_size}-position pages, each sequence's pages "
+                    "scattered over the pool by the seeded permutation of gqa_decode_paged (attn_decode_gqa_paged_fp8kv)")
     if "gqa_decode_paged" in ms:
         decode_part("gqa_decode_paged", dec_bytes, B, None,
                     f"llama3_8b_gqa_decode shape and lengths over paged caches: {pg_size}-position pages, each "

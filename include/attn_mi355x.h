@@ -165,9 +165,9 @@ attn_status attn_decode_gqa_noalloc(const void* q, const void* k_cache, const vo
  *   split_tokens, workspace (attn_decode_gqa_workspace_bytes) as attn_decode_gqa
  *
  * split_tokens = 0 chooses a chunk a quarter longer than attn_decode_gqa's for
- * the same sizes (at least 64 positions longer, a multiple of 64; 640 where
- * attn_decode_gqa takes 512), so the workspace that attn_decode_gqa_workspace_bytes
- * gives for split_tokens = 0 always suffices.
+ * the same sizes (at least 64 positions longer, a multiple of 64, at most 1024;
+ * 640 where attn_decode_gqa takes 512), so the workspace that
+ * attn_decode_gqa_workspace_bytes gives for split_tokens = 0 always suffices.
  *
  * head_dim must be 128 (else ATTN_ERR_UNSUPPORTED); Hq/Hkv up to 64.
  */
@@ -315,6 +315,34 @@ attn_status attn_decode_gqa_paged_append(const void* q, const void* k_new, const
                                          int max_pages_per_seq, float softmax_scale, attn_dtype in_dtype,
                                          attn_dtype out_dtype, int split_tokens, void* workspace,
                                          size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* GQA decode over paged FP8 caches.
+ *
+ * attn_decode_gqa_fp8kv over caches kept as page pools and a block table, as
+ * attn_decode_gqa_paged keeps bf16 caches: the e-book "MHA, MQA và GQA" offers
+ * the fp8 number type, and leaves out the paging cost of serving, whose layout
+ * is the one read by attn_decode_gqa_paged (position t of sequence b is row
+ * t mod page_size of page block_table[b][t / page_size]).
+ *
+ *   q [B, Hq, 128] bf16;  k_pages, v_pages [n_pages, page_size, Hkv, 128] one
+ *   byte each (OCP FP8 E4M3 codes, K = k_scale * e4m3(code), V likewise);
+ *   block_table [B, max_pages_per_seq] int32 (entries clamped to the pool);
+ *   cache_lens [B] (clamped to page_size * max_pages_per_seq);  out [B, Hq, 128]
+ *   of out_dtype;  workspace: attn_decode_gqa_workspace_bytes(B, Hq, Hkv, 128,
+ *   page_size * max_pages_per_seq, split_tokens).
+ *
+ * The results are bit for bit those of attn_decode_gqa_fp8kv over the caches the
+ * block table gathers (same chunk).  Errors: as attn_decode_gqa_fp8kv and
+ * attn_decode_gqa_paged (NULL table ATTN_ERR_NULL, page_size not a multiple of
+ * 32 or split_tokens above 1024 ATTN_ERR_UNSUPPORTED, scales not positive and
+ * finite ATTN_ERR_SHAPE).
+ */
+attn_status attn_decode_gqa_paged_fp8kv(const void* q, const void* k_pages, const void* v_pages, float k_scale,
+                                        float v_scale, const int32_t* block_table, const int32_t* cache_lens,
+                                        void* out, int B, int Hq, int Hkv, int head_dim, int page_size, int n_pages,
+                                        int max_pages_per_seq, float softmax_scale, attn_dtype out_dtype,
+                                        int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Causal GQA prefill (no cached prefix): query i attends to keys j <= i.

@@ -62,6 +62,8 @@ def _declare(lib):
     lib.attn_decode_gqa_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P]
     lib.attn_decode_gqa_int4kv.restype = I
     lib.attn_decode_gqa_int4kv.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, Z, P]
+    lib.attn_decode_gqa_paged_fp8kv.restype = I
+    lib.attn_decode_gqa_paged_fp8kv.argtypes = [P, P, P, F, F, P, P, P, I, I, I, I, I, I, I, F, I, I, P, Z, P]
     lib.attn_decode_gqa_fp8kv.restype = I
     lib.attn_decode_gqa_fp8kv.argtypes = [P, P, P, F, F, P, P, I, I, I, I, I, F, I, I, P, ctypes.c_size_t, P]
     lib.attn_decode_gqa_append_workspace_bytes.restype = ctypes.c_size_t
@@ -356,6 +358,39 @@ def attn_decode_gqa_fp8kv(q, k_cache, v_cache, k_scale: float, v_scale: float, c
                                      _dt(out), int(split_tokens), _ptr(workspace), workspace.numel(),
                                      _stream(q.device))
     _raise_if(st, "attn_decode_gqa_fp8kv")
+    return out
+
+
+def attn_decode_gqa_paged_fp8kv(q, k_pages, v_pages, k_scale: float, v_scale: float, block_table, cache_lens,
+                                out=None, softmax_scale: float = 0.0, out_dtype=torch.float32, split_tokens: int = 0,
+                                workspace=None):
+    """attn_decode_gqa_fp8kv over paged FP8 caches: k_pages/v_pages [n_pages, page_size, Hkv, 128]
+    torch.float8_e4m3fn holding K/k_scale and V/v_scale, block_table [B, max_pages_per_seq]
+    int32 as attn_decode_gqa_paged; q [B,Hq,128] bf16.  Returns out [B,Hq,128]."""
+    _check(q, "q", dtype=torch.bfloat16)
+    B, Hq, D = q.shape
+    _check(k_pages, "k_pages", dtype=torch.float8_e4m3fn)
+    if k_pages.dim() != 4 or k_pages.shape[3] != D:
+        raise ValueError(f"k_pages must be [n_pages, page_size, Hkv, {D}] (got {tuple(k_pages.shape)})")
+    n_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    _check(v_pages, "v_pages", shape=k_pages.shape, dtype=torch.float8_e4m3fn)
+    _check(block_table, "block_table", dtype=torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B={B}, max_pages_per_seq] (got {tuple(block_table.shape)})")
+    max_pages = block_table.shape[1]
+    _check(cache_lens, "cache_lens", shape=(B,), dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    _check(out, "out", shape=(B, Hq, D))
+    need = attn_decode_gqa_workspace_bytes(B, Hq, Hkv, D, page_size * max_pages, split_tokens)
+    if workspace is None:
+        workspace = _workspace(need, q.device, "gqa")
+    _check(workspace, "workspace", dtype=torch.uint8)
+    st = lib().attn_decode_gqa_paged_fp8kv(_ptr(q), _ptr(k_pages), _ptr(v_pages), float(k_scale), float(v_scale),
+                                           _ptr(block_table), _ptr(cache_lens), _ptr(out), B, Hq, Hkv, D, page_size,
+                                           n_pages, max_pages, float(softmax_scale), _dt(out), int(split_tokens),
+                                           _ptr(workspace), workspace.numel(), _stream(q.device))
+    _raise_if(st, "attn_decode_gqa_paged_fp8kv")
     return out
 
 
@@ -802,7 +837,7 @@ def attn_decode_mla_append(q_nope, q_rope, c_new, k_rope_new, w_uk, w_uv, c_kv, 
     return out
 
 
-__all__ = ["attn_decode_gqa", "attn_decode_gqa_paged", "attn_decode_gqa_paged_append", "attn_decode_mla_paged", "attn_decode_mla_fp8kv", "attn_prefill_gqa_paged", "attn_decode_gqa_int4kv", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_noalloc", "NOALLOC_SCRATCH_BYTES", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
+__all__ = ["attn_decode_gqa", "attn_decode_gqa_paged", "attn_decode_gqa_paged_fp8kv", "attn_decode_gqa_paged_append", "attn_decode_mla_paged", "attn_decode_mla_fp8kv", "attn_prefill_gqa_paged", "attn_decode_gqa_int4kv", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_noalloc", "NOALLOC_SCRATCH_BYTES", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
            "attn_decode_gqa_append_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached", "attn_prefill_gqa_cached_append",
            "attn_prefill_mla_causal", "attn_cache_append", "attn_rope_append",
            "attn_decode_mla_absorbed", "attn_decode_mla_append", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",

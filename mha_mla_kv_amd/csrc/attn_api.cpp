@@ -81,10 +81,13 @@ constexpr long long kQueueMinBlocks = 256;
 // 512 took 58.8-59.6 us in six of ten processes and 53.7-54.8 us in the other
 // four (which one depends on the process's allocations), 640 took 54.2-55.3 us
 // in all eight that ran it.
+// Like choose_chunk it stays at most 1024 (a paged unit holds at most 128
+// page numbers: four blocks of 1024 positions at 32 per page).
 int choose_chunk_fp8(int B, int Hkv, int n_rep, int T_max) {
   const int c = choose_chunk(B, Hkv, n_rep, T_max);
   const int more = c / 4 / 64 * 64;
-  return c + (more > 64 ? more : 64);
+  const int f = c + (more > 64 ? more : 64);
+  return f < 1024 ? f : 1024;
 }
 
 bool valid_split(int split) { return split == 0 || (split >= 64 && split <= 65536 && split % 64 == 0); }
@@ -385,6 +388,24 @@ attn_status attn_decode_gqa_paged_append(const void* q, const void* k_new, const
   return gqa_decode_common(fn, q, k_new, v_new, k_pages, v_pages, cache_lens, out, B, Hq, Hkv, head_dim,
                            page_size * max_pages_per_seq, softmax_scale, in_dtype, out_dtype, split_tokens, workspace,
                            workspace_bytes, stream, nullptr, false, block_table, page_size, n_pages);
+}
+
+attn_status attn_decode_gqa_paged_fp8kv(const void* q, const void* k_pages, const void* v_pages, float k_scale,
+                                        float v_scale, const int32_t* block_table, const int32_t* cache_lens,
+                                        void* out, int B, int Hq, int Hkv, int head_dim, int page_size, int n_pages,
+                                        int max_pages_per_seq, float softmax_scale, attn_dtype out_dtype,
+                                        int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "attn_decode_gqa_paged_fp8kv";
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(ATTN_ERR_SHAPE, "%s: k_scale and v_scale must be positive and finite (got %g, %g)", fn,
+                (double)k_scale, (double)v_scale);
+  const attn_status st = gqa_paged_checks(fn, block_table, page_size, n_pages, max_pages_per_seq, ATTN_BF16,
+                                          split_tokens);
+  if (st != ATTN_OK) return st;
+  const float scales[2] = {k_scale, v_scale};
+  return gqa_decode_common(fn, q, nullptr, nullptr, k_pages, v_pages, cache_lens, out, B, Hq, Hkv, head_dim,
+                           page_size * max_pages_per_seq, softmax_scale, ATTN_BF16, out_dtype, split_tokens, workspace,
+                           workspace_bytes, stream, scales, false, block_table, page_size, n_pages);
 }
 
 attn_status attn_decode_gqa_int4kv(const void* q, const void* k_codes, const void* v_codes, const float* k_scales,

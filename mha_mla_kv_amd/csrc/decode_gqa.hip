@@ -1284,7 +1284,10 @@ hipError_t launch_f32(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
 
 template <bool QUEUE>
 hipError_t launch_mode(const GqaDecodeArgs& a, dim3 grid, hipStream_t st) {
-  if (a.kv_fp8) return a.D == 128 ? launch_bf16<128, QUEUE, true>(a, grid, st) : hipErrorInvalidValue;
+  if (a.kv_fp8) {
+    if (a.D != 128) return hipErrorInvalidValue;
+    return a.block_table ? launch_bf16<128, QUEUE, true, true>(a, grid, st) : launch_bf16<128, QUEUE, true>(a, grid, st);
+  }
   if (a.kv_int4) return a.D == 128 ? launch_bf16<128, QUEUE, false, false, true>(a, grid, st) : hipErrorInvalidValue;
   if (a.block_table) {
     if (!a.in_bf16) return hipErrorInvalidValue;

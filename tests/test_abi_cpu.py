@@ -333,6 +333,23 @@ def test_paged_decode_validation():
 
 
 @no_gpu_only
+def test_paged_fp8_decode_validation():
+    lib = attn.lib()
+
+    def f(tb=FAKE, **kw):
+        return lib.attn_decode_gqa_paged_fp8kv(FAKE, FAKE, FAKE, kw.get("ks", 0.01), kw.get("vs", 0.01), tb, FAKE, FAKE,
+                                               2, 32, 8, kw.get("D", 128), kw.get("ps", 64), kw.get("np", 100),
+                                               kw.get("mp", 16), 0.0, F32, kw.get("split", 0), FAKE, 1 << 30, None)
+    assert f(tb=None) == NULL
+    assert f(ks=0.0) == SHAPE
+    assert f(vs=float("nan")) == SHAPE
+    assert f(ps=0) == SHAPE
+    assert f(ps=48) == UNSUP
+    assert f(split=2048) == UNSUP
+    assert f(D=96) == UNSUP          # fp8 caches: head_dim 128 only
+
+
+@no_gpu_only
 def test_paged_decode_step_validation():
     lib = attn.lib()
 
