@@ -452,6 +452,13 @@ def main():
         attn.attn_decode_mla_fp8kv(mla["q_nope"], mla["q_rope"], mla["w_uk"], mla["w_uv"], c8, mf8_scale, kr,
                                    mla["cache_lens"], out=mf8_out, workspace=mla_ws)
 
+    def run_mla_paged_fp8(i):  # the FP8 latent copies as pools of 16-position pages, read through one table
+        c8, kr = mf8_copies[i % len(mf8_copies)]
+        attn.attn_decode_mla_paged_fp8kv(mla["q_nope"], mla["q_rope"], mla["w_uk"], mla["w_uv"],
+                                         c8.view(MB * mpg_max, mpg_size, r), mf8_scale,
+                                         kr.view(MB * mpg_max, mpg_size, dR), mpg_table, mla["cache_lens"],
+                                         out=mf8_out, workspace=mla_ws)
+
     def run_prefill(i):
         attn.attn_prefill_gqa_causal(pre["q"], pre["k"], pre["v"], out=pre_out)
 
@@ -525,6 +532,7 @@ def main():
              ("chunked_prefill_paged", run_chunked_paged),
              ("mla_prefill", run_mla_prefill), ("mla_decode", run_mla), ("mla_decode_step", run_mla_step),
              ("mla_decode_paged", run_mla_paged), ("mla_decode_fp8", run_mla_fp8),
+             ("mla_decode_paged_fp8", run_mla_paged_fp8),
              ("kv_append", run_append), ("rope_append_decode", run_rope_decode), ("rope_append_chunk", run_rope_chunk),
              ("gqa_decode", run_decode), ("gqa_decode_paged", run_paged), ("gqa_decode_step", run_step),
              ("gqa_decode_paged_step", run_paged_step), ("gqa_decode_fp8", run_fp8),
@@ -672,6 +680,11 @@ def main():
         decode_part("mla_decode_fp8", mf8_bytes, MB, mla_flops,
                     "minimind768_mla_decode shape and lengths with the latent c_kv as FP8 E4M3 codes (one scale, "
                     "N(0,1)/scale drawn on the device; k_rope bf16): 224 bytes per position (attn_decode_mla_fp8kv)")
+    if "mla_decode_paged_fp8" in ms:
+        decode_part("mla_decode_paged_fp8", mf8_bytes, MB, mla_flops,
+                    f"the FP8-latent caches of mla_decode_fp8 as pools of {mpg_size}-position pages, each sequence's "
+                    "pages scattered over the pool by the seeded permutation of mla_decode_paged "
+                    "(attn_decode_mla_paged_fp8kv)")
     if "mla_prefill" in ms:
         prefill_part("mla_prefill", mlp_flops, MPB * MPS,
                      f"minimind768_mla_prefill: B={MPB} S={MPS} H={MPH} nope={MPdn} rope={MPdR} v={MPdv} "

@@ -565,6 +565,37 @@ attn_status attn_decode_mla_fp8kv(const void* q_nope, const void* q_rope, const 
                                   int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* MLA decode over a paged FP8 latent cache.
+ *
+ * attn_decode_mla_fp8kv with c_kv and k_rope kept as page pools read through
+ * one block table, as attn_decode_mla_paged keeps bf16 latents: the latent
+ * cache of the qqstock DeepSeek MLA article (sections 1 and 3) in the fp8
+ * number type of the "MHA, MQA và GQA" e-book, in the paging layout that
+ * e-book leaves out of its byte counts (position t of sequence b is row
+ * t mod page_size of page block_table[b][t / page_size]).
+ *
+ *   q_nope, q_rope, w_uk, w_uv, out, cache_lens: as attn_decode_mla_fp8kv;
+ *   c_pages [n_pages, page_size, kv_lora_rank] one byte each (OCP FP8 E4M3
+ *   codes, latent = c_scale * e4m3(code)), k_rope_pages [n_pages, page_size,
+ *   rope_dim] bf16, block_table [B, max_pages_per_seq] int32 (entries clamped to
+ *   the pool); workspace: attn_decode_mla_workspace_bytes(B, H, kv_lora_rank,
+ *   rope_dim, page_size * max_pages_per_seq, split_tokens).
+ *
+ * The results are bit for bit those of attn_decode_mla_fp8kv over the caches the
+ * block table gathers (same chunk).  Errors: as attn_decode_mla_fp8kv and
+ * attn_decode_mla_paged (NULL table ATTN_ERR_NULL; page_size not a multiple of
+ * 16, or a chunk spanning more than 128 pages, ATTN_ERR_UNSUPPORTED; c_scale not
+ * positive and finite ATTN_ERR_SHAPE).
+ */
+attn_status attn_decode_mla_paged_fp8kv(const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv,
+                                        const void* c_pages, float c_scale, const void* k_rope_pages,
+                                        const int32_t* block_table, const int32_t* cache_lens, void* out, int B, int H,
+                                        int nope_head_dim, int rope_dim, int v_head_dim, int kv_lora_rank,
+                                        int page_size, int n_pages, int max_pages_per_seq, float softmax_scale,
+                                        attn_dtype out_dtype, int split_tokens, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* MLA decode over paged latent caches.
  *
  *   T_max = page_size * max_pages_per_seq, L = cache_lens[b] clamped to [0, T_max];

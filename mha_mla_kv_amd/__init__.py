@@ -93,6 +93,9 @@ def _declare(lib):
                                              P, Z, P]
     lib.attn_decode_mla_fp8kv.restype = I
     lib.attn_decode_mla_fp8kv.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, F, I, I, P, Z, P]
+    lib.attn_decode_mla_paged_fp8kv.restype = I
+    lib.attn_decode_mla_paged_fp8kv.argtypes = [P, P, P, P, P, F, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, I, P,
+                                                Z, P]
     lib.attn_decode_mla_paged.restype = I
     lib.attn_decode_mla_paged.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, I, I,
                                           P, Z, P]
@@ -747,6 +750,55 @@ def attn_decode_mla_fp8kv(q_nope, q_rope, w_uk, w_uv, c_kv, c_scale: float, k_ro
     return out
 
 
+def attn_decode_mla_paged_fp8kv(q_nope, q_rope, w_uk, w_uv, c_pages, c_scale: float, k_rope_pages, block_table,
+                                cache_lens, out=None, softmax_scale: float = 0.0, out_dtype=torch.float32,
+                                split_tokens: int = 0, workspace=None):
+    """attn_decode_mla_fp8kv over paged latent caches: c_pages [n_pages, page_size, r] of E4M3 codes
+    (torch.float8_e4m3fn or uint8) times c_scale, k_rope_pages [n_pages, page_size, dR] bf16,
+    block_table [B, max_pages_per_seq] int32 as attn_decode_mla_paged; q_nope [B,H,dn], q_rope
+    [B,H,dR], w_uk [H,dn,r], w_uv [H,dv,r] bf16; cache_lens [B] int32 -> out [B,H,dv]."""
+    _check(q_nope, "q_nope", dtype=torch.bfloat16)
+    B, H, dn = q_nope.shape
+    _check(q_rope, "q_rope", dtype=torch.bfloat16)
+    if q_rope.dim() != 3 or q_rope.shape[:2] != (B, H):
+        raise ValueError(f"q_rope must be [B={B}, H={H}, rope_dim] (got {tuple(q_rope.shape)})")
+    dR = q_rope.shape[2]
+    _check(w_uk, "w_uk", dtype=torch.bfloat16)
+    if w_uk.dim() != 3 or w_uk.shape[:2] != (H, dn):
+        raise ValueError(f"w_uk must be [H={H}, nope_head_dim={dn}, kv_lora_rank] (got {tuple(w_uk.shape)})")
+    r = w_uk.shape[2]
+    _check(w_uv, "w_uv", dtype=torch.bfloat16)
+    if w_uv.dim() != 3 or w_uv.shape[0] != H or w_uv.shape[2] != r:
+        raise ValueError(f"w_uv must be [H={H}, v_head_dim, kv_lora_rank={r}] (got {tuple(w_uv.shape)})")
+    dv = w_uv.shape[1]
+    _check(c_pages, "c_pages")
+    if c_pages.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise ValueError(f"c_pages must hold E4M3 codes (float8_e4m3fn or uint8), got {c_pages.dtype}")
+    if c_pages.dim() != 3 or c_pages.shape[2] != r:
+        raise ValueError(f"c_pages must be [n_pages, page_size, kv_lora_rank={r}] (got {tuple(c_pages.shape)})")
+    n_pages, page_size = c_pages.shape[0], c_pages.shape[1]
+    _check(k_rope_pages, "k_rope_pages", shape=(n_pages, page_size, dR), dtype=torch.bfloat16)
+    _check(block_table, "block_table", dtype=torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B={B}, max_pages_per_seq] (got {tuple(block_table.shape)})")
+    max_pages = block_table.shape[1]
+    _check(cache_lens, "cache_lens", shape=(B,), dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=out_dtype, device=q_nope.device)
+    _check(out, "out", shape=(B, H, dv))
+    need = attn_decode_mla_workspace_bytes(B, H, r, dR, page_size * max_pages, split_tokens)
+    if workspace is None:
+        workspace = _workspace(need, q_nope.device, "mla")
+    _check(workspace, "workspace", dtype=torch.uint8)
+    st = lib().attn_decode_mla_paged_fp8kv(_ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(c_pages),
+                                           float(c_scale), _ptr(k_rope_pages), _ptr(block_table), _ptr(cache_lens),
+                                           _ptr(out), B, H, dn, dR, dv, r, page_size, n_pages, max_pages,
+                                           float(softmax_scale), _dt(out), int(split_tokens), _ptr(workspace),
+                                           workspace.numel(), _stream(q_nope.device))
+    _raise_if(st, "attn_decode_mla_paged_fp8kv")
+    return out
+
+
 def attn_decode_mla_paged(q_nope, q_rope, w_uk, w_uv, c_pages, k_rope_pages, block_table, cache_lens, out=None,
                           softmax_scale: float = 0.0, out_dtype=torch.float32, split_tokens: int = 0,
                           workspace=None):
@@ -837,7 +889,7 @@ def attn_decode_mla_append(q_nope, q_rope, c_new, k_rope_new, w_uk, w_uv, c_kv, 
     return out
 
 
-__all__ = ["attn_decode_gqa", "attn_decode_gqa_paged", "attn_decode_gqa_paged_fp8kv", "attn_decode_gqa_paged_append", "attn_decode_mla_paged", "attn_decode_mla_fp8kv", "attn_prefill_gqa_paged", "attn_decode_gqa_int4kv", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_noalloc", "NOALLOC_SCRATCH_BYTES", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
+__all__ = ["attn_decode_gqa", "attn_decode_gqa_paged", "attn_decode_gqa_paged_fp8kv", "attn_decode_gqa_paged_append", "attn_decode_mla_paged", "attn_decode_mla_fp8kv", "attn_decode_mla_paged_fp8kv", "attn_prefill_gqa_paged", "attn_decode_gqa_int4kv", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa_noalloc", "NOALLOC_SCRATCH_BYTES", "attn_decode_gqa_append", "attn_decode_gqa_fp8kv",
            "attn_decode_gqa_append_workspace_bytes", "attn_prefill_gqa_causal", "attn_prefill_gqa_cached", "attn_prefill_gqa_cached_append",
            "attn_prefill_mla_causal", "attn_cache_append", "attn_rope_append",
            "attn_decode_mla_absorbed", "attn_decode_mla_append", "attn_decode_mla_workspace_bytes", "attn_decode_mla_supported",

@@ -843,6 +843,30 @@ attn_status attn_decode_mla_fp8kv(const void* q_nope, const void* q_rope, const 
                            c_scale);
 }
 
+attn_status attn_decode_mla_paged_fp8kv(const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv,
+                                        const void* c_pages, float c_scale, const void* k_rope_pages,
+                                        const int32_t* block_table, const int32_t* cache_lens, void* out, int B, int H,
+                                        int nope_head_dim, int rope_dim, int v_head_dim, int kv_lora_rank,
+                                        int page_size, int n_pages, int max_pages_per_seq, float softmax_scale,
+                                        attn_dtype out_dtype, int split_tokens, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  static const char* fn = "attn_decode_mla_paged_fp8kv";
+  if (!block_table) return fail(ATTN_ERR_NULL, "%s: block_table must be non-NULL", fn);
+  if (!(c_scale > 0.f) || !std::isfinite(c_scale))
+    return fail(ATTN_ERR_SHAPE, "%s: c_scale must be positive and finite (got %g)", fn, (double)c_scale);
+  if (page_size <= 0 || n_pages <= 0 || max_pages_per_seq <= 0)
+    return fail(ATTN_ERR_SHAPE, "%s: page_size, n_pages and max_pages_per_seq must be positive (%d, %d, %d)", fn,
+                page_size, n_pages, max_pages_per_seq);
+  if ((long long)page_size * max_pages_per_seq > 0x7fffffffLL)
+    return fail(ATTN_ERR_SHAPE, "%s: page_size * max_pages_per_seq too large", fn);
+  if (page_size % 16 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: page_size=%d must be a multiple of 16", fn, page_size);
+  return mla_decode_common(fn, q_nope, q_rope, nullptr, nullptr, w_uk, w_uv, c_pages, k_rope_pages, cache_lens, out, B,
+                           H, nope_head_dim, rope_dim, v_head_dim, kv_lora_rank, page_size * max_pages_per_seq,
+                           softmax_scale, ATTN_BF16, out_dtype, split_tokens, workspace, workspace_bytes, stream,
+                           block_table, page_size, n_pages, max_pages_per_seq, true, c_scale);
+}
+
 attn_status attn_decode_mla_append(const void* q_nope, const void* q_rope, const void* c_new, const void* k_rope_new,
                                    const void* w_uk, const void* w_uv, void* c_kv, void* k_rope,
                                    const int32_t* cache_lens, void* out, int B, int H, int nope_head_dim,

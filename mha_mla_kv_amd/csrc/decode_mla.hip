@@ -226,7 +226,10 @@ __device__ __forceinline__ void issue_slice(u16* cdst, u16* rdst, const MlaDecod
                                             const Lanes<R, DR, F8>& ln, const ChunkPages& cp) {
   using C = Cfg<R, DR, F8>;
   __amdgpu_buffer_rsrc_t rc, rr;
-  if constexpr (F8) {  // rows of R one-byte codes
+  if constexpr (F8 && PAGED) {  // pages of rows of R one-byte codes
+    rc = page_rsrc(a.c_kv, a, cp, R / 2, t0, lim);
+    rr = page_rsrc(a.k_rope, a, cp, DR, t0, lim);
+  } else if constexpr (F8) {  // rows of R one-byte codes
     rc = rows_rsrc(a.c_kv, b, a.T_max, R / 2, t0, lim);
     rr = rows_rsrc(a.k_rope, b, a.T_max, DR, t0, lim);
   } else if constexpr (PAGED) {
@@ -898,7 +901,9 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaDecodeArgs a) {
 
 template <int R, int DR>
 hipError_t launch_rd(const MlaDecodeArgs& a, hipStream_t st) {
-  if (a.c_fp8) hipLaunchKernelGGL((mla_decode<R, DR, false, true>), dim3(a.n_splits, a.B), dim3(kThreads), 0, st, a);
+  if (a.c_fp8 && a.block_table)
+    hipLaunchKernelGGL((mla_decode<R, DR, true, true>), dim3(a.n_splits, a.B), dim3(kThreads), 0, st, a);
+  else if (a.c_fp8) hipLaunchKernelGGL((mla_decode<R, DR, false, true>), dim3(a.n_splits, a.B), dim3(kThreads), 0, st, a);
   else if (a.block_table) hipLaunchKernelGGL((mla_decode<R, DR, true>), dim3(a.n_splits, a.B), dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL((mla_decode<R, DR, false>), dim3(a.n_splits, a.B), dim3(kThreads), 0, st, a);
   return hipGetLastError();
@@ -928,7 +933,7 @@ hipError_t launch_mla_decode(const MlaDecodeArgs& a, hipStream_t st) {
   if (a.block_table && (a.page_size <= 0 || a.page_size % kSlice != 0 || a.n_pages <= 0 || a.append ||
                         a.split / a.page_size + 2 > 128))
     return hipErrorInvalidValue;
-  if (a.c_fp8 && (a.block_table || a.append || !(a.c_scale > 0.f))) return hipErrorInvalidValue;
+  if (a.c_fp8 && (a.append || !(a.c_scale > 0.f))) return hipErrorInvalidValue;
   return a.r == 64 ? launch_r<64>(a, st) : a.r == 128 ? launch_r<128>(a, st) : launch_r<256>(a, st);
 }
 

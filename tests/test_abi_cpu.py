@@ -389,6 +389,22 @@ def test_mla_paged_decode_validation():
 
 
 @no_gpu_only
+def test_mla_paged_fp8_decode_validation():
+    lib = attn.lib()
+
+    def f(tb=FAKE, **kw):
+        return lib.attn_decode_mla_paged_fp8kv(FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("cs", 0.01), FAKE, tb, FAKE, FAKE,
+                                               2, 8, 96, 48, 96, 128, kw.get("ps", 16), kw.get("np", 100),
+                                               kw.get("mp", 64), 0.0, F32, kw.get("split", 0), FAKE, 1 << 30, None)
+    assert f(tb=None) == NULL
+    assert f(cs=0.0) == SHAPE
+    assert f(cs=float("inf")) == SHAPE
+    assert f(ps=0) == SHAPE
+    assert f(ps=24) == UNSUP
+    assert f(split=2048) == UNSUP  # 2048 / 16 + 2 pages per chunk, more than 128
+
+
+@no_gpu_only
 def test_paged_prefill_validation():
     lib = attn.lib()
 
